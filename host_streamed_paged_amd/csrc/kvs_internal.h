@@ -1,0 +1,84 @@
+// Internal interface between the host runtime (kvs_runtime.cpp) and the
+// kernels (kvs_kernels.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace kvs {
+
+constexpr int kPageTokens = 256;             // tokens per page
+constexpr int kHeadDim = 128;                // d
+constexpr int kQK = 32;                      // values per quant block
+constexpr int kNB = kHeadDim / kQK;          // blocks per head row (4)
+constexpr int kKBlock = 34;                  // Q8_0: f16 scale + 32 int8
+constexpr int kVBlock = 18;                  // Q4_0: f16 scale + 16 nibble bytes
+constexpr int kKRow = kNB * kKBlock;         // 136 B: one head's K for one token
+constexpr int kVRow = kNB * kVBlock;         // 72 B
+constexpr int kKTile = kPageTokens * kKRow;  // 34816 B: one head's K for one page
+constexpr int kVTile = kPageTokens * kVRow;  // 18432 B
+constexpr int kPartStride = kHeadDim + 2;    // partial record: acc[128], m (log2 units), l
+
+// One run of consecutive logical pages of one split-K group, processed in
+// page order by one workgroup. flags bit 0: page0 is the group's first page
+// (start from an empty state instead of loading the stored one).
+struct Seg {
+    int32_t group;
+    int32_t page0;
+    int32_t npages;
+    int32_t flags;
+};
+constexpr int32_t kSegFresh = 1;
+
+// Where page p's record lives: src[p] >= 0 is a resident slot index;
+// src[p] < 0 means streamed with rank -1 - src[p], found in the ring chunk of
+// the current launch at position rank - chunk_rank0.
+struct PageSource {
+    const uint8_t* slots;       // base of the resident slots
+    const uint8_t* ring_chunk;  // first ring slot of this launch's chunk (null if none)
+    const int32_t* src;         // [n_pages] device table
+    int32_t chunk_rank0;        // streamed rank of the chunk's first page
+    int64_t page_bytes;
+};
+
+__host__ __device__ inline const uint8_t* page_ptr(const PageSource& ps, int32_t page) {
+    int32_t s = ps.src[page];
+    if (s >= 0) return ps.slots + (int64_t)s * ps.page_bytes;
+    return ps.ring_chunk + (int64_t)((-1 - s) - ps.chunk_rank0) * ps.page_bytes;
+}
+
+struct AttendArgs {
+    PageSource ps;
+    const Seg* segs;      // this launch's segments
+    int32_t n_segs;
+    int32_t n_kv_heads;
+    int32_t n_q_heads;
+    int32_t G;            // query heads per kv head
+    const void* q;        // [n_q, Hq, 128]
+    int32_t q_f16;
+    int32_t n_q;
+    int64_t q_pos0;
+    int64_t n_kv;
+    float scale_log2;     // scale * log2(e): scores are kept in log2 units
+    int32_t causal;
+    float* part;          // [n_groups][n_q][Hq][kPartStride]
+};
+
+struct GatherArgs {
+    PageSource ps;
+    const Seg* segs;
+    int32_t n_segs;
+    int32_t n_kv_heads;
+    int64_t tok0;
+    int64_t n_tok;
+    float* k_out;         // [n_tok, Hkv, 128]
+    float* v_out;
+};
+
+hipError_t launch_attend(const AttendArgs& a, hipStream_t stream);
+hipError_t launch_combine(const float* part, int32_t n_groups, int32_t n_q, int32_t n_q_heads,
+                          float* out, float* lse, hipStream_t stream);
+hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
+hipError_t launch_fill_u32(void* dst, uint32_t value, uint64_t n_words, hipStream_t stream);
+
+}  // namespace kvs

@@ -1,0 +1,607 @@
+// Host runtime of libkvs: configuration checks, arena carve, page tables,
+// launch plans and the H2D ring pipeline. The C ABI is declared in
+// include/kvs.h.
+//
+// The design follows the pages' statement of the problem: authoritative KV in
+// pinned host memory, a bounded device region holding resident 256-token pages
+// and one ring shared by all layers, with flash-attention consuming both
+// (page 1, "Summary"; page 2, opening paragraph). The ring is driven from the
+// host with hipMemcpyAsync on several copy streams; HIP events order each
+// chunk's copy before its kernel and the kernel before the slot's next copy.
+#include "kvs.h"
+#include "kvs_internal.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+#define KVS_HIP(expr)                                                                      \
+    do {                                                                                   \
+        hipError_t e_ = (expr);                                                            \
+        if (e_ != hipSuccess) return fail(KVS_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(e_)); \
+    } while (0)
+
+constexpr uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+struct Layout {
+    uint64_t page_bytes = 0;
+    uint64_t ring_bytes = 0;
+    uint64_t work_bytes = 0;
+    uint64_t src_bytes = 0;    // per layer
+    uint64_t seg_bytes = 0;    // per layer
+    int32_t max_segs = 0;      // per layer
+    int32_t max_groups = 0;
+    uint64_t fixed = 0;        // ring + work + tables
+};
+
+int validate(const kvs_config* c) {
+    if (!c) return fail(KVS_ERR_INVALID_ARG, "config is NULL");
+    if (!kvs_type_pair_supported(c->type_k, c->type_v))
+        return fail(KVS_ERR_UNSUPPORTED,
+                    "K/V block types (%d, %d) have no attention kernel: only Q8_0 keys (%d) with Q4_0 values (%d) are built",
+                    c->type_k, c->type_v, KVS_TYPE_Q8_0, KVS_TYPE_Q4_0);
+    if (c->head_dim != kvs::kHeadDim)
+        return fail(KVS_ERR_UNSUPPORTED, "head_dim %d unsupported (kernels are built for %d)", c->head_dim, kvs::kHeadDim);
+    if (c->page_tokens != kvs::kPageTokens)
+        return fail(KVS_ERR_UNSUPPORTED, "page_tokens %d unsupported (pages hold %d tokens)", c->page_tokens, kvs::kPageTokens);
+    if (c->n_layers < 1 || c->n_layers > 4096) return fail(KVS_ERR_INVALID_ARG, "n_layers %d out of range [1, 4096]", c->n_layers);
+    if (c->n_kv_heads < 1 || c->n_kv_heads > 64) return fail(KVS_ERR_INVALID_ARG, "n_kv_heads %d out of range [1, 64]", c->n_kv_heads);
+    if (c->n_q_heads < c->n_kv_heads || c->n_q_heads > 1024 || c->n_q_heads % c->n_kv_heads)
+        return fail(KVS_ERR_INVALID_ARG, "n_q_heads %d must be a multiple of n_kv_heads %d (at most 1024)", c->n_q_heads, c->n_kv_heads);
+    if (c->max_pages < 1 || c->max_pages > (1 << 22)) return fail(KVS_ERR_INVALID_ARG, "max_pages %d out of range [1, 2^22]", c->max_pages);
+    if (c->max_q_tokens < 1 || c->max_q_tokens > 8192) return fail(KVS_ERR_INVALID_ARG, "max_q_tokens %d out of range [1, 8192]", c->max_q_tokens);
+    if (c->ring_pages < 1 || c->ring_pages > 4096) return fail(KVS_ERR_INVALID_ARG, "ring_pages %d out of range [1, 4096]", c->ring_pages);
+    if (c->chunk_pages < 1 || c->ring_pages % c->chunk_pages)
+        return fail(KVS_ERR_INVALID_ARG, "chunk_pages %d must be >= 1 and divide ring_pages %d", c->chunk_pages, c->ring_pages);
+    if (c->copy_streams < 1 || c->copy_streams > 8) return fail(KVS_ERR_INVALID_ARG, "copy_streams %d out of range [1, 8]", c->copy_streams);
+    if (c->group_pages < 1) return fail(KVS_ERR_INVALID_ARG, "group_pages %d must be >= 1", c->group_pages);
+    if (c->flags & ~uint32_t(KVS_FLAG_POISON_RING)) return fail(KVS_ERR_INVALID_ARG, "unknown flag bits 0x%x", c->flags);
+    return KVS_OK;
+}
+
+Layout layout_of(const kvs_config* c) {
+    Layout L;
+    L.page_bytes = (uint64_t)c->n_kv_heads * (kvs::kKTile + kvs::kVTile);
+    L.ring_bytes = align256((uint64_t)c->ring_pages * L.page_bytes);
+    L.max_groups = (c->max_pages + c->group_pages - 1) / c->group_pages;
+    // partials: one record per (group, query token, query head)
+    L.work_bytes = align256((uint64_t)L.max_groups * c->max_q_tokens * c->n_q_heads * kvs::kPartStride * sizeof(float));
+    // segments: resident groups + (chunk windows add at most one split group each)
+    L.max_segs = 2 * L.max_groups + c->max_pages + 1;
+    L.src_bytes = align256((uint64_t)c->max_pages * sizeof(int32_t));
+    L.seg_bytes = align256((uint64_t)L.max_segs * sizeof(kvs::Seg));
+    L.fixed = L.ring_bytes + L.work_bytes + (uint64_t)c->n_layers * (L.src_bytes + L.seg_bytes);
+    return L;
+}
+
+struct ChunkPlan {
+    int32_t seg0 = 0, nseg = 0;   // segments of this chunk's launch
+    int32_t rank0 = 0, npages = 0; // streamed ranks [rank0, rank0 + npages)
+    std::vector<std::pair<int32_t, int32_t>> runs;  // (first logical page, count) of consecutive streamed pages
+};
+
+struct LayerState {
+    const uint8_t* host = nullptr;
+    int32_t host_pages = 0;
+    int32_t n_pages = -1;            // -1: page table not set
+    std::vector<int32_t> src;        // per page: slot or -1 - rank
+    std::vector<int32_t> slots_held;
+    std::vector<kvs::Seg> segs;
+    int32_t res_nseg = 0;            // segments [0, res_nseg) form the resident launch
+    std::vector<ChunkPlan> chunks;
+    int32_t n_groups = 0;
+    int32_t n_streamed = 0;
+    int32_t* dev_src = nullptr;
+    kvs::Seg* dev_segs = nullptr;
+};
+
+}  // namespace
+
+struct kvs_pool {
+    kvs_config cfg{};
+    Layout L;
+    int device = 0;
+    uint8_t* arena = nullptr;
+    uint64_t budget = 0;
+    uint8_t* ring = nullptr;
+    float* work = nullptr;
+    uint8_t* slots = nullptr;
+    int64_t n_slots = 0;
+    std::vector<int32_t> slot_free;  // stack of free slot ids
+    std::vector<LayerState> layers;
+    std::vector<hipStream_t> copy;
+    int32_t n_cslots = 0;            // chunk slots in the ring
+    std::vector<hipEvent_t> filled, freed;
+    hipEvent_t last_work = nullptr;  // recorded after every attend / gather
+    int32_t ring_next = 0;           // next chunk slot the ring fills
+    int32_t pf_layer = -1;           // layer whose prefetch is outstanding
+    int32_t pf_slot0 = 0;            // chunk slot of that layer's chunk 0
+    int32_t pf_issued = 0;           // chunks of it issued so far
+    bool broken = false;             // a HIP call failed mid-sequence
+    kvs_status_info st{};
+};
+
+namespace {
+
+int check_device(const kvs_pool* p) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != p->device)
+        return fail(KVS_ERR_INVALID_ARG, "pool belongs to device %d but device %d is current", p->device, dev);
+    if (p->broken) return fail(KVS_ERR_HIP, "pool is unusable after an earlier HIP failure");
+    return KVS_OK;
+}
+
+// Build segments and chunk plans for a layer from its residency.
+int build_plan(const kvs_pool* p, LayerState& ls, int32_t n_pages, const uint8_t* resident) {
+    const int32_t G = p->cfg.group_pages, C = p->cfg.chunk_pages;
+    ls.src.assign(n_pages, 0);
+    std::vector<int32_t> streamed;
+    for (int32_t i = 0; i < n_pages; ++i)
+        if (!resident[i]) { ls.src[i] = -1 - (int32_t)streamed.size(); streamed.push_back(i); }
+    ls.n_streamed = (int32_t)streamed.size();
+    ls.n_groups = (n_pages + G - 1) / G;
+    std::vector<char> mixed(ls.n_groups, 0);
+    for (int32_t pg : streamed) mixed[pg / G] = 1;
+    ls.segs.clear();
+    ls.chunks.clear();
+    for (int32_t g = 0; g < ls.n_groups; ++g)
+        if (!mixed[g]) ls.segs.push_back({g, g * G, std::min(n_pages, (g + 1) * G) - g * G, kvs::kSegFresh});
+    ls.res_nseg = (int32_t)ls.segs.size();
+    const int32_t n_chunks = (ls.n_streamed + C - 1) / C;
+    for (int32_t c = 0; c < n_chunks; ++c) {
+        ChunkPlan cp;
+        cp.rank0 = c * C;
+        cp.npages = std::min(C, ls.n_streamed - cp.rank0);
+        for (int32_t k = 0; k < cp.npages; ++k) {
+            int32_t pg = streamed[cp.rank0 + k];
+            if (!cp.runs.empty() && cp.runs.back().first + cp.runs.back().second == pg) cp.runs.back().second++;
+            else cp.runs.push_back({pg, 1});
+        }
+        // window [w0, w1): from this chunk's first streamed page (page 0 for the
+        // first chunk) up to the next chunk's first streamed page (or the end)
+        const int32_t w0 = (c == 0) ? 0 : streamed[cp.rank0];
+        const int32_t w1 = (c + 1 < n_chunks) ? streamed[(c + 1) * C] : n_pages;
+        cp.seg0 = (int32_t)ls.segs.size();
+        for (int32_t g = w0 / G; g * G < w1; ++g) {
+            if (!mixed[g]) continue;
+            int32_t a = std::max(w0, g * G), b = std::min(w1, std::min(n_pages, (g + 1) * G));
+            if (a >= b) continue;
+            ls.segs.push_back({g, a, b - a, a == g * G ? kvs::kSegFresh : 0});
+        }
+        cp.nseg = (int32_t)ls.segs.size() - cp.seg0;
+        ls.chunks.push_back(std::move(cp));
+    }
+    // invariants the kernels rely on: every page appears in exactly one segment,
+    // pages of a group appear in ascending order, a chunk launch only touches
+    // streamed pages of its own chunk
+    std::vector<int32_t> seen(n_pages, 0);
+    std::vector<int32_t> next_in_group(ls.n_groups, -1);
+    for (int32_t g = 0; g < ls.n_groups; ++g) next_in_group[g] = g * G;
+    auto check_seg = [&](const kvs::Seg& s, int32_t rank_lo, int32_t rank_hi) -> bool {
+        if (s.npages < 1 || s.page0 < 0 || s.page0 + s.npages > n_pages) return false;
+        if (s.page0 != next_in_group[s.group]) return false;
+        if (((s.flags & kvs::kSegFresh) != 0) != (s.page0 == s.group * G)) return false;
+        for (int32_t q = s.page0; q < s.page0 + s.npages; ++q) {
+            if (q / G != s.group || seen[q]++) return false;
+            if (ls.src[q] < 0) {
+                int32_t r = -1 - ls.src[q];
+                if (r < rank_lo || r >= rank_hi) return false;
+            }
+        }
+        next_in_group[s.group] = s.page0 + s.npages;
+        return true;
+    };
+    for (int32_t i = 0; i < ls.res_nseg; ++i)
+        if (!check_seg(ls.segs[i], 0, 0)) return fail(KVS_ERR_INVALID_ARG, "internal: resident plan check failed");
+    for (const ChunkPlan& cp : ls.chunks)
+        for (int32_t i = cp.seg0; i < cp.seg0 + cp.nseg; ++i)
+            if (!check_seg(ls.segs[i], cp.rank0, cp.rank0 + cp.npages))
+                return fail(KVS_ERR_INVALID_ARG, "internal: chunk plan check failed");
+    for (int32_t q = 0; q < n_pages; ++q)
+        if (seen[q] != 1) return fail(KVS_ERR_INVALID_ARG, "internal: page %d not covered once", q);
+    if ((int32_t)ls.segs.size() > p->L.max_segs) return fail(KVS_ERR_INVALID_ARG, "internal: too many segments");
+    return KVS_OK;
+}
+
+int issue_copy(kvs_pool* p, const LayerState& ls, int32_t c, int32_t cslot) {
+    const ChunkPlan& cp = ls.chunks[c];
+    hipStream_t s = p->copy[cslot % p->copy.size()];
+    KVS_HIP(hipStreamWaitEvent(s, p->freed[cslot], 0));
+    uint8_t* dst = p->ring + (uint64_t)cslot * p->cfg.chunk_pages * p->L.page_bytes;
+    for (const auto& run : cp.runs) {
+        const uint64_t n = (uint64_t)run.second * p->L.page_bytes;
+        KVS_HIP(hipMemcpyAsync(dst, ls.host + (uint64_t)run.first * p->L.page_bytes, n, hipMemcpyHostToDevice, s));
+        dst += n;
+        p->st.copies_issued++;
+        p->st.bytes_h2d += (int64_t)n;
+        p->st.pages_streamed += run.second;
+    }
+    KVS_HIP(hipEventRecord(p->filled[cslot], s));
+    return KVS_OK;
+}
+
+int prefetch(kvs_pool* p, int32_t layer) {
+    const LayerState& ls = p->layers[layer];
+    p->pf_layer = layer;
+    p->pf_slot0 = p->ring_next;
+    p->pf_issued = 0;
+    const int32_t n = std::min<int32_t>(p->n_cslots, (int32_t)ls.chunks.size());
+    for (int32_t c = 0; c < n; ++c) {
+        int rc = issue_copy(p, ls, c, (p->pf_slot0 + c) % p->n_cslots);
+        if (rc) { p->broken = true; return rc; }
+        p->pf_issued++;
+    }
+    return KVS_OK;
+}
+
+// Run the layer's launch plan: the resident launch, then each ring chunk
+// (wait filled -> kernel -> release slot -> refill the slot with a later chunk).
+template <typename LaunchFn>
+int run_layer(kvs_pool* p, int32_t layer, hipStream_t stream, LaunchFn launch) {
+    LayerState& ls = p->layers[layer];
+    const int32_t n_chunks = (int32_t)ls.chunks.size();
+    if (n_chunks > 0 && p->pf_layer != layer) {
+        int rc = prefetch(p, layer);
+        if (rc) return rc;
+    }
+    int rc = KVS_OK;
+    auto mark = [&](int r) { if (r) p->broken = true; return r; };
+    if (ls.res_nseg > 0) {
+        if ((rc = mark(launch(0, ls.res_nseg, (const uint8_t*)nullptr, 0)))) return rc;
+        p->st.kernels_launched++;
+    }
+    for (int32_t c = 0; c < n_chunks; ++c) {
+        const int32_t cslot = (p->pf_slot0 + c) % p->n_cslots;
+        const ChunkPlan& cp = ls.chunks[c];
+        uint8_t* chunk_base = p->ring + (uint64_t)cslot * p->cfg.chunk_pages * p->L.page_bytes;
+        if (hipStreamWaitEvent(stream, p->filled[cslot], 0) != hipSuccess)
+            return mark(fail(KVS_ERR_HIP, "hipStreamWaitEvent(filled) failed"));
+        if ((rc = mark(launch(cp.seg0, cp.nseg, chunk_base, cp.rank0)))) return rc;
+        p->st.kernels_launched++;
+        if (p->cfg.flags & KVS_FLAG_POISON_RING) {
+            hipError_t e = kvs::launch_fill_u32(chunk_base, 0xA5A5A5A5u, (uint64_t)cp.npages * p->L.page_bytes / 4, stream);
+            if (e != hipSuccess) return mark(fail(KVS_ERR_HIP, "ring poison fill failed: %s", hipGetErrorString(e)));
+        }
+        if (hipEventRecord(p->freed[cslot], stream) != hipSuccess)
+            return mark(fail(KVS_ERR_HIP, "hipEventRecord(freed) failed"));
+        if (c + p->n_cslots < n_chunks) {
+            if ((rc = issue_copy(p, ls, c + p->n_cslots, cslot))) return mark(rc);
+            p->pf_issued++;
+        }
+    }
+    if (n_chunks > 0) {
+        p->ring_next = (p->pf_slot0 + n_chunks) % p->n_cslots;
+        p->pf_layer = -1;
+        p->pf_issued = 0;
+    }
+    return KVS_OK;
+}
+
+int check_layer_ready(const kvs_pool* p, int32_t layer) {
+    if (layer < 0 || layer >= p->cfg.n_layers) return fail(KVS_ERR_INVALID_ARG, "layer %d out of range [0, %d)", layer, p->cfg.n_layers);
+    const LayerState& ls = p->layers[layer];
+    if (!ls.host) return fail(KVS_ERR_NOT_READY, "layer %d has no host pages (call kvs_host_pages_set)", layer);
+    if (ls.n_pages < 0) return fail(KVS_ERR_NOT_READY, "layer %d has no page table (call kvs_page_table_set)", layer);
+    return KVS_OK;
+}
+
+int check_ring_free_for(const kvs_pool* p, int32_t layer) {
+    const LayerState& ls = p->layers[layer];
+    if (!ls.chunks.empty() && p->pf_layer >= 0 && p->pf_layer != layer)
+        return fail(KVS_ERR_STATE, "ring holds an unconsumed prefetch of layer %d; attend it before layer %d", p->pf_layer, layer);
+    return KVS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvs_type_pair_supported(int32_t type_k, int32_t type_v) {
+    return type_k == KVS_TYPE_Q8_0 && type_v == KVS_TYPE_Q4_0;
+}
+
+int kvs_config_validate(const kvs_config* cfg) { return validate(cfg); }
+
+uint64_t kvs_page_bytes(const kvs_config* cfg) {
+    if (validate(cfg)) return 0;
+    return layout_of(cfg).page_bytes;
+}
+
+int kvs_min_budget_bytes(const kvs_config* cfg, uint64_t* out) {
+    int rc = validate(cfg);
+    if (rc) return rc;
+    if (!out) return fail(KVS_ERR_INVALID_ARG, "out is NULL");
+    *out = layout_of(cfg).fixed;
+    return KVS_OK;
+}
+
+int64_t kvs_slots_for_budget(const kvs_config* cfg, uint64_t budget_bytes) {
+    if (validate(cfg)) return 0;
+    Layout L = layout_of(cfg);
+    if (budget_bytes < L.fixed) return 0;
+    return (int64_t)((budget_bytes - L.fixed) / L.page_bytes);
+}
+
+int kvs_pool_create(const kvs_config* cfg, void* dev_arena, uint64_t budget_bytes, kvs_pool** out_pool) {
+    int rc = validate(cfg);
+    if (rc) return rc;
+    if (!out_pool) return fail(KVS_ERR_INVALID_ARG, "out_pool is NULL");
+    if (!dev_arena) return fail(KVS_ERR_INVALID_ARG, "device arena is NULL");
+    if ((uintptr_t)dev_arena & 255) return fail(KVS_ERR_INVALID_ARG, "device arena must be 256-byte aligned");
+    Layout L = layout_of(cfg);
+    if (budget_bytes < L.fixed)
+        return fail(KVS_ERR_BUDGET, "budget %llu B is below the minimum %llu B (ring %llu + workspace %llu + tables)",
+                    (unsigned long long)budget_bytes, (unsigned long long)L.fixed,
+                    (unsigned long long)L.ring_bytes, (unsigned long long)L.work_bytes);
+    kvs_pool* p = new kvs_pool();
+    p->cfg = *cfg;
+    p->L = L;
+    p->arena = (uint8_t*)dev_arena;
+    p->budget = budget_bytes;
+    if (hipGetDevice(&p->device) != hipSuccess) { delete p; return fail(KVS_ERR_HIP, "hipGetDevice failed"); }
+    uint8_t* cur = p->arena;
+    p->ring = cur; cur += L.ring_bytes;
+    p->work = (float*)cur; cur += L.work_bytes;
+    p->layers.resize(cfg->n_layers);
+    for (auto& ls : p->layers) {
+        ls.dev_src = (int32_t*)cur; cur += L.src_bytes;
+        ls.dev_segs = (kvs::Seg*)cur; cur += L.seg_bytes;
+    }
+    p->slots = cur;
+    p->n_slots = (int64_t)((budget_bytes - L.fixed) / L.page_bytes);
+    for (int64_t s = p->n_slots - 1; s >= 0; --s) p->slot_free.push_back((int32_t)s);
+    p->n_cslots = cfg->ring_pages / cfg->chunk_pages;
+    auto cleanup = [&](const char* what, hipError_t e) {
+        for (auto s : p->copy) (void)hipStreamDestroy(s);
+        for (auto e2 : p->filled) (void)hipEventDestroy(e2);
+        for (auto e2 : p->freed) (void)hipEventDestroy(e2);
+        if (p->last_work) (void)hipEventDestroy(p->last_work);
+        delete p;
+        return fail(KVS_ERR_HIP, "%s failed: %s", what, hipGetErrorString(e));
+    };
+    for (int i = 0; i < cfg->copy_streams; ++i) {
+        hipStream_t s;
+        hipError_t e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+        if (e != hipSuccess) return cleanup("hipStreamCreateWithFlags", e);
+        p->copy.push_back(s);
+    }
+    for (int i = 0; i < p->n_cslots; ++i) {
+        hipEvent_t a, b;
+        hipError_t e = hipEventCreateWithFlags(&a, hipEventDisableTiming);
+        if (e != hipSuccess) return cleanup("hipEventCreateWithFlags", e);
+        p->filled.push_back(a);
+        e = hipEventCreateWithFlags(&b, hipEventDisableTiming);
+        if (e != hipSuccess) return cleanup("hipEventCreateWithFlags", e);
+        p->freed.push_back(b);
+    }
+    hipError_t e = hipEventCreateWithFlags(&p->last_work, hipEventDisableTiming);
+    if (e != hipSuccess) return cleanup("hipEventCreateWithFlags", e);
+    p->st.page_bytes = (int64_t)L.page_bytes;
+    p->st.slot_count = p->n_slots;
+    p->st.ring_pages = cfg->ring_pages;
+    p->st.workspace_bytes = (int64_t)L.work_bytes;
+    if (getenv("KVS_LOG"))
+        fprintf(stderr, "kvs: pool on device %d: budget %.2f MiB, minimum %.2f MiB, page %.4f MiB, %lld slots, ring %d pages, %d layers\n",
+                p->device, budget_bytes / 1048576.0, L.fixed / 1048576.0, L.page_bytes / 1048576.0,
+                (long long)p->n_slots, cfg->ring_pages, cfg->n_layers);
+    *out_pool = p;
+    return KVS_OK;
+}
+
+void kvs_pool_destroy(kvs_pool* p) {
+    if (!p) return;
+    for (auto s : p->copy) (void)hipStreamSynchronize(s);
+    if (p->last_work) (void)hipEventSynchronize(p->last_work);
+    for (auto s : p->copy) (void)hipStreamDestroy(s);
+    for (auto e : p->filled) (void)hipEventDestroy(e);
+    for (auto e : p->freed) (void)hipEventDestroy(e);
+    if (p->last_work) (void)hipEventDestroy(p->last_work);
+    delete p;
+}
+
+int kvs_host_pages_set(kvs_pool* p, int32_t layer, const void* pinned_records, int32_t n_pages) {
+    if (!p) return fail(KVS_ERR_INVALID_ARG, "pool is NULL");
+    if (layer < 0 || layer >= p->cfg.n_layers) return fail(KVS_ERR_INVALID_ARG, "layer %d out of range [0, %d)", layer, p->cfg.n_layers);
+    if (!pinned_records || n_pages < 1) return fail(KVS_ERR_INVALID_ARG, "host records NULL or n_pages %d < 1", n_pages);
+    if (p->pf_layer == layer) return fail(KVS_ERR_STATE, "layer %d has copies in flight from its prefetch", layer);
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, pinned_records) != hipSuccess || attr.type != hipMemoryTypeHost) {
+        (void)hipGetLastError();
+        return fail(KVS_ERR_UNSUPPORTED, "host records of layer %d are not pinned host memory", layer);
+    }
+    p->layers[layer].host = (const uint8_t*)pinned_records;
+    p->layers[layer].host_pages = n_pages;
+    return KVS_OK;
+}
+
+int kvs_page_table_set(kvs_pool* p, int32_t layer, int32_t n_pages, const uint8_t* resident, void* stream) {
+    if (!p) return fail(KVS_ERR_INVALID_ARG, "pool is NULL");
+    int rc = check_device(p);
+    if (rc) return rc;
+    if (layer < 0 || layer >= p->cfg.n_layers) return fail(KVS_ERR_INVALID_ARG, "layer %d out of range [0, %d)", layer, p->cfg.n_layers);
+    LayerState& ls = p->layers[layer];
+    if (!ls.host) return fail(KVS_ERR_NOT_READY, "layer %d has no host pages (call kvs_host_pages_set first)", layer);
+    if (n_pages < 0 || n_pages > p->cfg.max_pages || n_pages > ls.host_pages)
+        return fail(KVS_ERR_INVALID_ARG, "n_pages %d out of range [0, min(max_pages %d, host pages %d)]", n_pages, p->cfg.max_pages, ls.host_pages);
+    if (n_pages > 0 && !resident) return fail(KVS_ERR_INVALID_ARG, "resident mask is NULL");
+    if (p->pf_layer == layer) return fail(KVS_ERR_STATE, "layer %d has an unconsumed prefetch", layer);
+    int64_t need = 0;
+    for (int32_t i = 0; i < n_pages; ++i) need += resident[i] ? 1 : 0;
+    const int64_t avail = (int64_t)p->slot_free.size() + (int64_t)ls.slots_held.size();
+    if (need > avail)
+        return fail(KVS_ERR_NO_SLOTS, "layer %d wants %lld resident pages but only %lld slots are free", layer, (long long)need, (long long)avail);
+    LayerState trial;
+    trial.host = ls.host;
+    trial.host_pages = ls.host_pages;
+    trial.dev_src = ls.dev_src;
+    trial.dev_segs = ls.dev_segs;
+    rc = build_plan(p, trial, n_pages, resident);
+    if (rc) return rc;
+    // commit: release old slots, take new ones
+    for (int32_t s : ls.slots_held) p->slot_free.push_back(s);
+    for (int32_t i = 0; i < n_pages; ++i)
+        if (resident[i]) {
+            int32_t s = p->slot_free.back();
+            p->slot_free.pop_back();
+            trial.src[i] = s;
+            trial.slots_held.push_back(s);
+        }
+    ls = std::move(trial);
+    p->st.slots_used = p->n_slots - (int64_t)p->slot_free.size();
+    hipStream_t s = (hipStream_t)stream;
+    KVS_HIP(hipStreamWaitEvent(s, p->last_work, 0));
+    for (int32_t i = 0; i < n_pages; ++i)
+        if (ls.src[i] >= 0) {
+            KVS_HIP(hipMemcpyAsync(p->slots + (uint64_t)ls.src[i] * p->L.page_bytes, ls.host + (uint64_t)i * p->L.page_bytes,
+                                   p->L.page_bytes, hipMemcpyHostToDevice, s));
+            p->st.resident_upload_bytes += (int64_t)p->L.page_bytes;
+        }
+    if (n_pages > 0) KVS_HIP(hipMemcpyAsync(ls.dev_src, ls.src.data(), n_pages * sizeof(int32_t), hipMemcpyHostToDevice, s));
+    if (!ls.segs.empty())
+        KVS_HIP(hipMemcpyAsync(ls.dev_segs, ls.segs.data(), ls.segs.size() * sizeof(kvs::Seg), hipMemcpyHostToDevice, s));
+    KVS_HIP(hipStreamSynchronize(s));
+    ls.n_pages = n_pages;
+    return KVS_OK;
+}
+
+int kvs_stream_enqueue(kvs_pool* p, int32_t layer) {
+    if (!p) return fail(KVS_ERR_INVALID_ARG, "pool is NULL");
+    int rc = check_device(p);
+    if (rc) return rc;
+    if ((rc = check_layer_ready(p, layer))) return rc;
+    if (p->pf_layer == layer) return KVS_OK;  // already prefetched
+    if ((rc = check_ring_free_for(p, layer))) return rc;
+    if (p->layers[layer].chunks.empty()) return KVS_OK;
+    return prefetch(p, layer);
+}
+
+int kvs_attend(kvs_pool* p, int32_t layer, const void* q, int32_t q_dtype, int32_t n_q, int64_t q_pos0, int64_t n_kv,
+               float scale, int32_t causal, float* out, float* lse, void* stream) {
+    if (!p) return fail(KVS_ERR_INVALID_ARG, "pool is NULL");
+    int rc = check_device(p);
+    if (rc) return rc;
+    if ((rc = check_layer_ready(p, layer))) return rc;
+    const LayerState& ls = p->layers[layer];
+    if (n_q < 1) return fail(KVS_ERR_INVALID_ARG, "n_q %d < 1", n_q);
+    if (n_q > p->cfg.max_q_tokens)
+        return fail(KVS_ERR_BATCH_TOO_WIDE, "query block of %d tokens is wider than max_q_tokens %d", n_q, p->cfg.max_q_tokens);
+    if (!q || !out) return fail(KVS_ERR_INVALID_ARG, "q or out is NULL");
+    if (q_dtype != KVS_Q_F32 && q_dtype != KVS_Q_F16) return fail(KVS_ERR_INVALID_ARG, "q_dtype %d unknown", q_dtype);
+    if (!std::isfinite(scale)) return fail(KVS_ERR_INVALID_ARG, "scale is not finite");
+    if (n_kv < 0 || (n_kv + kvs::kPageTokens - 1) / kvs::kPageTokens != ls.n_pages)
+        return fail(KVS_ERR_INVALID_ARG, "n_kv %lld does not fill the layer's %d pages", (long long)n_kv, ls.n_pages);
+    if (causal && (q_pos0 < 0 || q_pos0 + n_q > n_kv))
+        return fail(KVS_ERR_INVALID_ARG, "causal queries at positions [%lld, %lld) must lie inside the cache of %lld tokens",
+                    (long long)q_pos0, (long long)(q_pos0 + n_q), (long long)n_kv);
+    if ((rc = check_ring_free_for(p, layer))) return rc;
+    hipStream_t s = (hipStream_t)stream;
+
+    kvs::AttendArgs a{};
+    a.ps.slots = p->slots;
+    a.ps.src = ls.dev_src;
+    a.ps.page_bytes = (int64_t)p->L.page_bytes;
+    a.n_kv_heads = p->cfg.n_kv_heads;
+    a.n_q_heads = p->cfg.n_q_heads;
+    a.G = p->cfg.n_q_heads / p->cfg.n_kv_heads;
+    a.q = q;
+    a.q_f16 = q_dtype == KVS_Q_F16;
+    a.n_q = n_q;
+    a.q_pos0 = q_pos0;
+    a.n_kv = n_kv;
+    a.scale_log2 = scale * 1.44269504088896340736f;
+    a.causal = causal ? 1 : 0;
+    a.part = p->work;
+    rc = run_layer(p, layer, s, [&](int32_t seg0, int32_t nseg, const uint8_t* ring_chunk, int32_t rank0) -> int {
+        kvs::AttendArgs b = a;
+        b.ps.ring_chunk = ring_chunk;
+        b.ps.chunk_rank0 = rank0;
+        b.segs = ls.dev_segs + seg0;
+        b.n_segs = nseg;
+        hipError_t e = kvs::launch_attend(b, s);
+        return e == hipSuccess ? KVS_OK : fail(KVS_ERR_HIP, "attention kernel launch failed: %s", hipGetErrorString(e));
+    });
+    if (rc) return rc;
+    hipError_t e = kvs::launch_combine(p->work, ls.n_groups, n_q, p->cfg.n_q_heads, out, lse, s);
+    if (e != hipSuccess) { p->broken = true; return fail(KVS_ERR_HIP, "combine launch failed: %s", hipGetErrorString(e)); }
+    p->st.kernels_launched++;
+    if (hipEventRecord(p->last_work, s) != hipSuccess) { p->broken = true; return fail(KVS_ERR_HIP, "hipEventRecord failed"); }
+    return KVS_OK;
+}
+
+int kvs_status(const kvs_pool* p, kvs_status_info* info) {
+    if (!p || !info) return fail(KVS_ERR_INVALID_ARG, "pool or info is NULL");
+    *info = p->st;
+    return KVS_OK;
+}
+
+int kvs_debug_gather(kvs_pool* p, int32_t layer, int64_t tok0, int64_t n_tok, float* k_out, float* v_out, void* stream) {
+    if (!p) return fail(KVS_ERR_INVALID_ARG, "pool is NULL");
+    int rc = check_device(p);
+    if (rc) return rc;
+    if ((rc = check_layer_ready(p, layer))) return rc;
+    const LayerState& ls = p->layers[layer];
+    if (tok0 < 0 || n_tok < 0 || tok0 + n_tok > (int64_t)ls.n_pages * kvs::kPageTokens)
+        return fail(KVS_ERR_INVALID_ARG, "tokens [%lld, %lld) outside the layer's %d pages", (long long)tok0, (long long)(tok0 + n_tok), ls.n_pages);
+    if (n_tok > 0 && (!k_out || !v_out)) return fail(KVS_ERR_INVALID_ARG, "k_out or v_out is NULL");
+    if ((rc = check_ring_free_for(p, layer))) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    kvs::GatherArgs a{};
+    a.ps.slots = p->slots;
+    a.ps.src = ls.dev_src;
+    a.ps.page_bytes = (int64_t)p->L.page_bytes;
+    a.n_kv_heads = p->cfg.n_kv_heads;
+    a.tok0 = tok0;
+    a.n_tok = n_tok;
+    a.k_out = k_out;
+    a.v_out = v_out;
+    rc = run_layer(p, layer, s, [&](int32_t seg0, int32_t nseg, const uint8_t* ring_chunk, int32_t rank0) -> int {
+        kvs::GatherArgs b = a;
+        b.ps.ring_chunk = ring_chunk;
+        b.ps.chunk_rank0 = rank0;
+        b.segs = ls.dev_segs + seg0;
+        b.n_segs = nseg;
+        hipError_t e = kvs::launch_gather(b, s);
+        return e == hipSuccess ? KVS_OK : fail(KVS_ERR_HIP, "gather kernel launch failed: %s", hipGetErrorString(e));
+    });
+    if (rc) return rc;
+    if (hipEventRecord(p->last_work, s) != hipSuccess) { p->broken = true; return fail(KVS_ERR_HIP, "hipEventRecord failed"); }
+    return KVS_OK;
+}
+
+int kvs_debug_read_page(kvs_pool* p, int32_t layer, int32_t page, void* dst_host) {
+    if (!p) return fail(KVS_ERR_INVALID_ARG, "pool is NULL");
+    int rc = check_device(p);
+    if (rc) return rc;
+    if ((rc = check_layer_ready(p, layer))) return rc;
+    const LayerState& ls = p->layers[layer];
+    if (page < 0 || page >= ls.n_pages) return fail(KVS_ERR_INVALID_ARG, "page %d out of range [0, %d)", page, ls.n_pages);
+    if (!dst_host) return fail(KVS_ERR_INVALID_ARG, "dst_host is NULL");
+    if (ls.src[page] < 0) return fail(KVS_ERR_NOT_RESIDENT, "page %d of layer %d is streamed, not resident", page, layer);
+    KVS_HIP(hipEventSynchronize(p->last_work));
+    KVS_HIP(hipMemcpy(dst_host, p->slots + (uint64_t)ls.src[page] * p->L.page_bytes, p->L.page_bytes, hipMemcpyDeviceToHost));
+    return KVS_OK;
+}
+
+const char* kvs_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

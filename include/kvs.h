@@ -1,0 +1,216 @@
+/*
+ * kvs.h - host-streamed, paged flash-attention over a Q8_0-K / Q4_0-V cache
+ *         (C ABI of libkvs.so, built for AMD MI355X / gfx950).
+ *
+ * The method (three pages on "Adaptive KV Streaming" for llama.cpp):
+ *   - The authoritative KV history lives in pinned host memory; the device holds
+ *     a bounded working set of resident pages plus one transfer ring shared by
+ *     all layers, and flash-attention consumes both (page 1, "Summary"; page 2,
+ *     opening paragraph).
+ *   - The unit of residency and transfer is a 256-token page of one layer
+ *     (page 2, "Dynamic draft eject": thresholds counted in 256-token pages).
+ *   - The cache types are Q8_0 for K and Q4_0 for V (page 1, "What it is useful
+ *     for"; page 2, "TLDR": the q8_0-q4_0 kernel pair).
+ *   - A byte budget sizes the device region; the smallest useful budget is one
+ *     page (page 3, "Diagnostic log": minimum_stage_bytes).
+ *   - Unsupported K/V type pairs and over-wide batches fail with an explicit
+ *     error instead of silently doing something else (page 1, "How engineers
+ *     can use it": explicit capability errors; page 2, "Phase arena:
+ *     speculative verify batches": batches wider than
+ *     max(n_seq_max, 1 + n_max_spec_draft) are rejected).
+ *
+ * Conventions for every call:
+ *   - Return 0 (KVS_OK) on success or a negative KVS_ERR_* code. Nothing
+ *     throws across this boundary. On error the pool's state is unchanged and
+ *     kvs_last_error() describes the failure (thread-local string).
+ *   - Device pointers are plain HIP device addresses; host pointers are plain
+ *     process addresses; streams are hipStream_t handles passed as void*.
+ *   - The caller owns every buffer it passes: the device arena, the pinned host
+ *     page records, q, out, lse and the compute streams. The library owns only
+ *     its metadata, its HIP events and its copy streams (created at the default
+ *     priority), and never frees caller memory.
+ *   - A pool is bound to the HIP device that is current when it is created;
+ *     later calls must be made with that device current.
+ *
+ * Page record format (one record per layer and page, page_bytes long):
+ *   [ K: for kv head g = 0..Hkv-1, token row r = 0..255, block b = 0..d/32-1:
+ *        a Q8_0 block of 34 bytes ]
+ *   [ V: same order, Q4_0 blocks of 18 bytes ]
+ *   Q8_0 block: little-endian binary16 scale d, then 32 int8 codes q;
+ *               element i = d * q[i].
+ *   Q4_0 block: little-endian binary16 scale d, then 16 bytes; byte j holds
+ *               element j in its low nibble and element j + 16 in its high
+ *               nibble; element i = d * (nibble - 8).
+ *   Token t of a layer lives in page t / 256, row t % 256. Each kv head's K tile
+ *   (256 x d/32 x 34 bytes) and V tile (256 x d/32 x 18 bytes) is contiguous,
+ *   so one workgroup reads one head of one page as two line-aligned streams.
+ *   For Hkv = 4, d = 128: K row 136 B per head, page_bytes = 212992.
+ *   Rows at or beyond the layer's token count may hold any bytes (even NaN
+ *   scales); they are never read into a result.
+ */
+#ifndef KVS_H
+#define KVS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Block types, numbered as in ggml's type enumeration. */
+#define KVS_TYPE_F16  1
+#define KVS_TYPE_Q4_0 2
+#define KVS_TYPE_Q8_0 8
+
+/* Query element types for kvs_attend. */
+#define KVS_Q_F32 0
+#define KVS_Q_F16 1
+
+/* Error codes. */
+#define KVS_OK                  0
+#define KVS_ERR_INVALID_ARG    -1  /* null pointer, out-of-range size or index        */
+#define KVS_ERR_UNSUPPORTED    -2  /* type pair, head_dim, page size, unpinned memory */
+#define KVS_ERR_BUDGET         -3  /* budget below kvs_min_budget_bytes               */
+#define KVS_ERR_NO_SLOTS       -4  /* more resident pages than free device slots      */
+#define KVS_ERR_BATCH_TOO_WIDE -5  /* n_q above max_q_tokens                          */
+#define KVS_ERR_NOT_READY      -6  /* host pages or page table of the layer unset     */
+#define KVS_ERR_STATE          -7  /* ring already lent to another layer's prefetch   */
+#define KVS_ERR_NOT_RESIDENT   -8  /* kvs_debug_read_page on a streamed page          */
+#define KVS_ERR_HIP            -9  /* a HIP runtime call failed                       */
+
+/* kvs_config.flags */
+#define KVS_FLAG_POISON_RING 1u    /* debug: fill each ring chunk with 0xA5 after its
+                                      kernel, before the slot is reused             */
+
+typedef struct kvs_config {
+    int32_t n_layers;      /* layers sharing the pool and the ring (>= 1)                 */
+    int32_t n_kv_heads;    /* Hkv (1..64)                                                 */
+    int32_t n_q_heads;     /* Hq, a multiple of Hkv; query head h reads kv head h/(Hq/Hkv) */
+    int32_t head_dim;      /* d; 128 is the only supported value                          */
+    int32_t page_tokens;   /* 256 is the only supported value                             */
+    int32_t type_k;        /* KVS_TYPE_Q8_0                                                */
+    int32_t type_v;        /* KVS_TYPE_Q4_0                                                */
+    int32_t max_pages;     /* most pages any layer will hold (sizes tables and workspace) */
+    int32_t max_q_tokens;  /* widest query block kvs_attend admits: 1 for decode,
+                              1 + n_draft for a speculative verify, the ubatch for prefill */
+    int32_t ring_pages;    /* device ring capacity in pages (>= 1)                        */
+    int32_t chunk_pages;   /* pages per ring chunk: one copy batch and one kernel launch;
+                              must divide ring_pages                                      */
+    int32_t copy_streams;  /* copy streams the chunks round-robin over (1..8)              */
+    int32_t group_pages;   /* pages per split-K partial (>= 1). Partials are keyed by this
+                              logical grouping only, so results do not depend on which
+                              pages are resident, nor on ring or chunk sizes.              */
+    uint32_t flags;        /* KVS_FLAG_*                                                   */
+} kvs_config;
+
+typedef struct kvs_status_info {
+    int64_t page_bytes;          /* bytes of one page record                         */
+    int64_t slot_count;          /* resident page slots carved from the arena        */
+    int64_t slots_used;          /* slots holding a resident page                    */
+    int64_t ring_pages;          /* ring capacity in pages                           */
+    int64_t workspace_bytes;     /* split-K partial workspace carved from the arena  */
+    int64_t bytes_h2d;           /* bytes copied host->device through the ring       */
+    int64_t pages_streamed;      /* pages copied through the ring                    */
+    int64_t copies_issued;       /* hipMemcpyAsync calls issued for the ring         */
+    int64_t kernels_launched;    /* kernel launches issued by kvs_attend/debug calls */
+    int64_t resident_upload_bytes; /* bytes copied into resident slots              */
+} kvs_status_info;
+
+typedef struct kvs_pool kvs_pool;
+
+/* 1 if the K/V block type pair has a kernel (only Q8_0 K with Q4_0 V), else 0.
+ * Pure: no HIP call. The pages compile flash-attention per K/V type pair and
+ * reject unqualified pairs (page 2, "TLDR"; page 1, "How engineers can use it"). */
+int kvs_type_pair_supported(int32_t type_k, int32_t type_v);
+
+/* Validate a configuration without touching the GPU. Returns KVS_OK,
+ * KVS_ERR_INVALID_ARG or KVS_ERR_UNSUPPORTED. Pure. */
+int kvs_config_validate(const kvs_config* cfg);
+
+/* Bytes of one page record for cfg. Pure; 0 on an invalid config. */
+uint64_t kvs_page_bytes(const kvs_config* cfg);
+
+/* Smallest budget kvs_pool_create accepts for cfg, written to *out: the ring,
+ * the split-K workspace (max_q_tokens x n_q_heads rows per page group) and the
+ * per-layer tables, each rounded up to 256 bytes. Pure. */
+int kvs_min_budget_bytes(const kvs_config* cfg, uint64_t* out);
+
+/* Number of resident page slots a budget yields for cfg (0 if below the
+ * minimum). Pure. */
+int64_t kvs_slots_for_budget(const kvs_config* cfg, uint64_t budget_bytes);
+
+/* Create a pool that carves [resident slots | ring | workspace | tables] out of
+ * the caller's device arena of budget_bytes bytes (256-byte aligned). The
+ * library never allocates device memory; the arena must outlive the pool.
+ * Creates the copy streams and the ring events on the current device. */
+int kvs_pool_create(const kvs_config* cfg, void* dev_arena, uint64_t budget_bytes,
+                    kvs_pool** out_pool);
+
+/* Wait for every copy the pool issued, then release its events, streams and
+ * metadata. Never frees caller memory. Safe on NULL. */
+void kvs_pool_destroy(kvs_pool* pool);
+
+/* Register the authoritative host records of a layer: n_pages records of
+ * page_bytes each, contiguous, in pinned host memory (hipHostMalloc or an
+ * equivalent page-locked allocation; anything else is KVS_ERR_UNSUPPORTED).
+ * The library only reads them; they must stay valid and unchanged while work
+ * that reads them is in flight. */
+int kvs_host_pages_set(kvs_pool* pool, int32_t layer, const void* pinned_records,
+                       int32_t n_pages);
+
+/* Set which pages of a layer are resident (resident[p] = 1) for a layer of
+ * n_pages pages (n_pages <= max_pages and <= the registered host pages).
+ * Assigns slots, builds the layer's launch plan (resident groups, ring chunks,
+ * copy runs), uploads the resident records and the plan on `stream`, and
+ * waits for that stream. KVS_ERR_NO_SLOTS if the pool lacks free slots. */
+int kvs_page_table_set(kvs_pool* pool, int32_t layer, int32_t n_pages,
+                       const uint8_t* resident, void* stream);
+
+/* Start copying the first ring chunks of `layer` (as many as the ring holds)
+ * on the pool's copy streams, so they overlap whatever the caller runs before
+ * kvs_attend(layer). The ring serves one layer at a time, in call order:
+ * KVS_ERR_STATE if another layer's prefetch has not been consumed yet. A layer
+ * with no streamed pages is a no-op. kvs_attend prefetches by itself when the
+ * caller did not. */
+int kvs_stream_enqueue(kvs_pool* pool, int32_t layer);
+
+/* Attention of n_q query tokens against the layer's cache of n_kv tokens.
+ *   q:    device, [n_q, n_q_heads, head_dim], f32 or f16 (q_dtype), contiguous.
+ *   out:  device, [n_q, n_q_heads, head_dim] f32; lse: device [n_q, n_q_heads]
+ *         f32 natural-log sum-exp of the scaled scores, or NULL.
+ *   Query i sits at position q_pos0 + i and reads keys t < n_kv, and with
+ *   causal != 0 only t <= q_pos0 + i (then q_pos0 >= 0 and q_pos0 + n_q <= n_kv
+ *   are required). n_kv must satisfy ceil(n_kv / 256) == the layer's n_pages.
+ *   Scores are scale * q.k. A row without any allowed key gets out = 0 and
+ *   lse = -inf.
+ * Enqueues on `stream`: the resident-group kernel, then for each ring chunk a
+ * wait for its copy, the chunk kernel and a slot release, then the split-K
+ * combine. Returns without waiting. KVS_ERR_BATCH_TOO_WIDE if n_q exceeds
+ * max_q_tokens (the pages' "decode batch too wide"). */
+int kvs_attend(kvs_pool* pool, int32_t layer, const void* q, int32_t q_dtype, int32_t n_q,
+               int64_t q_pos0, int64_t n_kv, float scale, int32_t causal, float* out,
+               float* lse, void* stream);
+
+/* Counters and sizes of the pool. */
+int kvs_status(const kvs_pool* pool, kvs_status_info* info);
+
+/* Dequantize tokens tok0 .. tok0 + n_tok - 1 of a layer into float32
+ * k_out / v_out (device, [n_tok, n_kv_heads, head_dim]) through the same page
+ * table, ring pipeline and block decode the attention kernels use. Streamed
+ * pages travel through the ring. Dequantization is exact in float32. */
+int kvs_debug_gather(kvs_pool* pool, int32_t layer, int64_t tok0, int64_t n_tok, float* k_out,
+                     float* v_out, void* stream);
+
+/* Copy the bytes of a resident page's device slot to dst_host (page_bytes).
+ * Synchronous. KVS_ERR_NOT_RESIDENT for a streamed page. */
+int kvs_debug_read_page(kvs_pool* pool, int32_t layer, int32_t page, void* dst_host);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* kvs_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVS_H */

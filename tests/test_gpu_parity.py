@@ -1,0 +1,202 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Sizes span several page tiles, split-K groups and ring chunks, with a ragged
+last page whose unused rows are NaN-poisoned. Bars: dequantization and page
+gathers bit-exact; attention within 2e-3 normwise relative error per output
+row (max_c |o - r| / max_c |r|, maximized over query token x head), lse within
+2e-3 absolute; outputs bit-identical across residency, ring and chunk sizes.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import host_streamed_paged_amd as kvs
+from kvs_case import Case, mask_all, mask_none, mask_random, normwise_error, say
+from oracle import gather_kv
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+N_KV = 5 * 256 + 77          # 6 pages, ragged tail of 77 rows
+
+
+def small_case(resident_fn, *, cid=31, n_layers=3, n_kv=N_KV, Hkv=2, Hq=12, max_q=1, ring=4, chunk=2,
+               streams=2, group=1, flags=0, slots=None):
+    say(f"case cid={cid} layers={n_layers} n_kv={n_kv} Hkv={Hkv} Hq={Hq} ring={ring} chunk={chunk} "
+        f"streams={streams} group={group} flags={flags} residency={getattr(resident_fn, '__name__', 'fn')}")
+    return Case(cid=cid, n_layers=n_layers, n_kv_heads=Hkv, n_q_heads=Hq, n_kv=n_kv, slots=slots,
+                cfg_kw=dict(max_q_tokens=max_q, ring_pages=ring, chunk_pages=chunk, copy_streams=streams,
+                            group_pages=group, flags=flags),
+                resident_fn=resident_fn)
+
+
+@pytest.mark.parametrize("resident", [mask_all, mask_none, mask_random(0.5)], ids=["all", "none", "half"])
+def test_gather_bit_exact(resident):
+    c = small_case(resident)
+    try:
+        for l in range(c.L):
+            for tok0, n_tok in [(0, c.n_pages * 256), (100, 700), (255, 2), (N_KV - 1, 1)]:
+                say(f"kvs_debug_gather layer={l} tok0={tok0} n_tok={n_tok}")
+                k = torch.empty((n_tok, c.Hkv, 128), dtype=torch.float32, device="cuda")
+                v = torch.empty_like(k)
+                c.pool.debug_gather(l, tok0, n_tok, k, v)
+                torch.cuda.synchronize()
+                rk, rv = gather_kv(c.records[l], c.Hkv, 128, tok0, n_tok)
+                valid = max(0, min(n_tok, N_KV - tok0))
+                assert np.array_equal(k.cpu().numpy()[:valid], rk[:valid].astype(np.float32))
+                assert np.array_equal(v.cpu().numpy()[:valid], rv[:valid].astype(np.float32))
+                if valid < n_tok:   # poisoned rows decode to NaN on both sides
+                    assert np.all(np.isnan(k.cpu().numpy()[valid:]))
+    finally:
+        c.close()
+
+
+def test_read_page_matches_host_records():
+    c = small_case(mask_random(0.5))
+    try:
+        for l in range(c.L):
+            for p in range(c.n_pages):
+                if c.masks[l][p]:
+                    assert np.array_equal(c.pool.debug_read_page(l, p), c.records[l][p])
+                else:
+                    with pytest.raises(kvs.KvsError) as e:
+                        c.pool.debug_read_page(l, p)
+                    assert e.value.code == kvs.ERR_NOT_RESIDENT
+    finally:
+        c.close()
+
+
+def check(c, outs, lses, qs, *, q_pos0, scale, causal):
+    worst = 0.0
+    for l in range(c.L):
+        ref, ref_lse = c.oracle(l, qs[l], q_pos0=q_pos0, scale=scale, causal=causal)
+        err = normwise_error(outs[l], ref)
+        lerr = float(np.max(np.abs(lses[l] - ref_lse)))
+        say(f"layer {l}: normwise {err:.3e} lse {lerr:.3e}")
+        assert err <= TOL, (l, err)
+        assert lerr <= TOL, (l, lerr)
+        worst = max(worst, err)
+    return worst
+
+
+@pytest.mark.parametrize("resident", [mask_all, mask_none, mask_random(0.5)], ids=["all", "none", "half"])
+def test_decode_parity(resident):
+    c = small_case(resident)
+    try:
+        qs = [c.queries(l, 1, "f32") for l in range(c.L)]
+        outs, lses = c.attend_all(qs, q_pos0=N_KV - 1, scale=1.0, causal=False)
+        check(c, outs, lses, qs, q_pos0=N_KV - 1, scale=1.0, causal=False)
+    finally:
+        c.close()
+
+
+def test_verify_parity():
+    c = small_case(mask_random(0.4, seed=2), max_q=4, group=2)
+    try:
+        qs = [c.queries(l, 4, "f32") for l in range(c.L)]
+        outs, lses = c.attend_all(qs, q_pos0=N_KV - 4, scale=1.0, causal=True)
+        check(c, outs, lses, qs, q_pos0=N_KV - 4, scale=1.0, causal=True)
+    finally:
+        c.close()
+
+
+def test_prefill_parity():
+    n_q = 300
+    c = small_case(mask_random(0.3, seed=3), n_layers=2, max_q=n_q, group=2, ring=4, chunk=2)
+    try:
+        qs = [c.queries(l, n_q, "f16") for l in range(c.L)]
+        scale = 1.0 / math.sqrt(128)
+        outs, lses = c.attend_all(qs, q_pos0=N_KV - n_q, scale=scale, causal=True)
+        check(c, outs, lses, qs, q_pos0=N_KV - n_q, scale=scale, causal=True)
+    finally:
+        c.close()
+
+
+def test_outputs_bit_identical_across_residency_ring_and_chunks():
+    variants = [
+        dict(resident=mask_all, ring=4, chunk=2, streams=2),
+        dict(resident=mask_none, ring=1, chunk=1, streams=1),
+        dict(resident=mask_none, ring=6, chunk=3, streams=3),
+        dict(resident=mask_random(0.5), ring=4, chunk=4, streams=1),
+        dict(resident=mask_random(0.3, seed=5), ring=2, chunk=1, streams=2, flags=kvs.FLAG_POISON_RING),
+    ]
+    for group in (1, 3):
+        base = None
+        for v in variants:
+            c = small_case(v["resident"], max_q=4, ring=v["ring"], chunk=v["chunk"], streams=v["streams"],
+                           group=group, flags=v.get("flags", 0))
+            try:
+                qs = [c.queries(l, 4, "f32") for l in range(c.L)]
+                outs, lses = c.attend_all(qs, q_pos0=N_KV - 4, scale=1.0, causal=True)
+                if base is None:
+                    check(c, outs, lses, qs, q_pos0=N_KV - 4, scale=1.0, causal=True)
+                    base = (outs, lses)
+                else:
+                    for l in range(c.L):
+                        assert np.array_equal(outs[l], base[0][l]), (v, group, l)
+                        assert np.array_equal(lses[l], base[1][l]), (v, group, l)
+            finally:
+                c.close()
+
+
+def test_empty_cache_returns_zero_and_minus_inf():
+    c = small_case(mask_all, n_layers=1)
+    try:
+        pool = c.pool
+        pool.page_table_set(0, np.zeros(0, np.uint8))
+        q = torch.randn(1, c.Hq, 128, device="cuda")
+        out = torch.full_like(q, 7.0)
+        lse = torch.zeros(1, c.Hq, device="cuda")
+        pool.attend(0, q, 0, 0, 1.0, False, out, lse)
+        torch.cuda.synchronize()
+        assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+    finally:
+        c.close()
+
+
+def test_errors_leave_state_usable():
+    c = small_case(mask_random(0.5), max_q=2)
+    try:
+        q = torch.from_numpy(c.queries(0, 3, "f32")).cuda()
+        out = torch.empty_like(q)
+        with pytest.raises(kvs.KvsError) as e:
+            c.pool.attend(0, q, N_KV, N_KV - 3, 1.0, True, out)
+        assert e.value.code == kvs.ERR_BATCH_TOO_WIDE
+        with pytest.raises(kvs.KvsError) as e:
+            c.pool.attend(0, q[:1], N_KV - 300, 0, 1.0, False, out[:1])
+        assert e.value.code == kvs.ERR_INVALID_ARG
+        # prefetch layer 1, then try layer 0: the ring is lent to layer 1
+        c.pool.stream_enqueue(1)
+        with pytest.raises(kvs.KvsError) as e:
+            c.pool.attend(0, q[:1], N_KV, 0, 1.0, False, out[:1])
+        assert e.value.code == kvs.ERR_STATE
+        c.pool.attend(1, q[:1], N_KV, 0, 1.0, False, out[:1])
+        # too many resident pages for the slots
+        assert c.pool.status().slot_count == sum(int(m.sum()) for m in c.masks)
+        with pytest.raises(kvs.KvsError) as e:
+            c.pool.page_table_set(0, np.ones(c.n_pages, np.uint8))
+        assert e.value.code == kvs.ERR_NO_SLOTS
+        # after all the errors, a normal pass still matches the oracle
+        qs = [c.queries(l, 1, "f32") for l in range(c.L)]
+        outs, lses = c.attend_all(qs, q_pos0=N_KV - 1, scale=1.0, causal=False)
+        check(c, outs, lses, qs, q_pos0=N_KV - 1, scale=1.0, causal=False)
+        st = c.pool.status()
+        assert st.pages_streamed > 0 and st.bytes_h2d == st.pages_streamed * kvs.page_bytes(c.cfg)
+    finally:
+        c.close()
+
+
+def test_tiny_decode_workload():
+    from kvs_synth import WORKLOADS
+    wl = WORKLOADS["tiny_decode"]
+    c = Case(cid=wl.cid, n_layers=1, n_kv_heads=1, n_q_heads=1, n_kv=wl.n_kv, resident_fn=mask_all,
+             cfg_kw=dict(max_q_tokens=1, ring_pages=4, chunk_pages=2, copy_streams=2, group_pages=1))
+    try:
+        qs = [c.queries(0, 1, wl.q_dtype)]
+        outs, lses = c.attend_all(qs, q_pos0=wl.q_pos0, scale=wl.scale, causal=wl.causal)
+        check(c, outs, lses, qs, q_pos0=wl.q_pos0, scale=wl.scale, causal=wl.causal)
+    finally:
+        c.close()
