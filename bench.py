@@ -1,0 +1,281 @@
+"""Benchmark of host-streamed paged attention on one MI355X.
+
+One step = kvs_attend over every layer of the workload (one pass of the hot
+path: ring copies, page gathers, dequantization, attention, split-K combine).
+
+Default workload: resident decode at 32 Ki context (16 layers, 24 query / 4 kv
+heads, d = 128, 128 resident pages per layer, one query token). `value` is
+the KV bytes attended per second (all 16 layers' pages, 436,207,616 B per
+step) over the timed steps. Alongside it:
+  * roofline: the attention kernel's algorithmic bytes per launch (one layer,
+    27,262,976 B) over its average launch duration (HIP events on the compute
+    stream, timed region), against 8 TB/s HBM;
+  * streamed: the same measurement at 256 Ki context with 103 resident pages
+    per layer and the rest streamed through a 16-page ring, against the host
+    link rate measured in the same run (1 GiB pinned copy, best of 5);
+  * cpu_baseline: the float64 CPU oracle on a bounded sample of layers of the
+    same workload, on this host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-streamed] [--no-cpu]
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "streamed attention KV GB/s + decode attn tok/s at 32K/256K ctx, % of HBM/link roofline"
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def gen_layers(wl, geom, threads):
+    from kvs_synth import layer_records
+    with ThreadPoolExecutor(threads) as ex:
+        return list(ex.map(lambda l: layer_records(wl.cid, l, wl.n_kv, geom), range(wl.n_layers)))
+
+
+def setup(wl, cfg_kw, threads):
+    import torch
+    import host_streamed_paged_amd as kvs
+    from kvs_synth import KVGeometry, make_q, residency_mask
+
+    geom = KVGeometry(wl.n_kv_heads, wl.head_dim)
+    t0 = time.time()
+    recs = gen_layers(wl, geom, threads)
+    host = [torch.from_numpy(r).pin_memory() for r in recs]
+    log(f"{wl.name}: generated and pinned {sum(r.nbytes for r in recs) / 2**30:.2f} GiB in {time.time() - t0:.1f}s")
+    masks = [residency_mask(wl.cid, l, wl.n_pages, wl.resident_pages, wl.own_page_resident)
+             for l in range(wl.n_layers)]
+    cfg = kvs.Config(n_layers=wl.n_layers, n_kv_heads=wl.n_kv_heads, n_q_heads=wl.n_q_heads,
+                     max_pages=wl.n_pages, max_q_tokens=wl.n_q, **cfg_kw)
+    arena = kvs.Pool.arena_for(cfg, int(sum(int(m.sum()) for m in masks)))
+    pool = kvs.Pool(cfg, arena)
+    for l in range(wl.n_layers):
+        pool.host_pages_set(l, host[l])
+        pool.page_table_set(l, masks[l])
+    qs = [torch.from_numpy(make_q(wl.cid, l, wl.n_q, wl.n_q_heads, wl.head_dim, wl.q_dtype)).cuda()
+          for l in range(wl.n_layers)]
+    outs = [torch.empty(q.shape, dtype=torch.float32, device="cuda") for q in qs]
+    return dict(recs=recs, host=host, masks=masks, cfg=cfg, arena=arena, pool=pool, qs=qs, outs=outs)
+
+
+def run_steps(wl, st, n, stream):
+    pool = st["pool"]
+    for _ in range(n):
+        for l in range(wl.n_layers):
+            pool.stream_enqueue(l)
+            pool.attend(l, st["qs"][l], wl.n_kv, wl.q_pos0, wl.scale, wl.causal, st["outs"][l], None,
+                        stream=stream)
+
+
+def timed_run(wl, st, steps, warmup):
+    import torch
+    stream = torch.cuda.current_stream()
+    pool = st["pool"]
+    run_steps(wl, st, warmup, stream)
+    torch.cuda.synchronize()
+    pool.profile_read(0, reset=True)
+    pool.profile_read(1, reset=True)
+    pool.profile_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    run_steps(wl, st, steps, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pool.profile_enable(False)
+    ms = e0.elapsed_time(e1) / steps
+    n_att, ms_att = pool.profile_read(0, reset=True)
+    n_cmb, ms_cmb = pool.profile_read(1, reset=True)
+    return dict(ms_per_step=ms, wall_ms_per_step=wall * 1e3 / steps, attn_launches=n_att,
+                attn_ms_total=ms_att, combine_launches=n_cmb, combine_ms_total=ms_cmb)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("kvs_kernels.hip", "kvs_internal.h"):
+        with open(os.path.join(ROOT, "host_streamed_paged_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload):
+    """HBM bytes per attention launch from the committed counter summary, if
+    it was taken on the current kernel source."""
+    path = os.path.join(PROFILES, f"attend_{workload}_counters.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except OSError:
+        return None
+    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def measure_link():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8).pin_memory()
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    best = math.inf
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src, non_blocking=True)
+        e1.record()
+        e1.synchronize()
+        best = min(best, e0.elapsed_time(e1) / 1e3)
+    del src, dst
+    return n / best / 1e9
+
+
+def cpu_baseline(wl, recs, qs_np, budget_s=12.0):
+    """The float64 oracle, one layer at a time, until ~budget_s of work."""
+    from oracle import attend_layer
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    t0 = time.perf_counter()
+    layers = 0
+    while layers < wl.n_layers:
+        attend_layer(recs[layers], qs_np[layers], n_kv=wl.n_kv, n_kv_heads=wl.n_kv_heads, head_dim=wl.head_dim,
+                     scale=wl.scale, causal=wl.causal, q_pos0=wl.q_pos0)
+        layers += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    layer_bytes = wl.n_pages * recs[0].shape[1]
+    return {
+        "value": round(layers * layer_bytes / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"{wl.name}: layers 0..{layers - 1} of {wl.n_layers} (float64 numpy, one layer at a time), "
+                  f"{dt:.1f}s; decode attn tok/s equivalent {layers / wl.n_layers / dt:.4f}",
+        "attn_tok_s": round(layers / wl.n_layers / dt, 5),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="resident_decode_32k")
+    ap.add_argument("--no-streamed", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--streamed-steps", type=int, default=10)
+    ap.add_argument("--threads", type=int, default=min(16, len(os.sched_getaffinity(0))))
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the streamed-attention path runs on a single device "
+              f"(--gpus {args.gpus} is not supported)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import host_streamed_paged_amd as kvs
+    from kvs_synth import WORKLOADS
+
+    kvs.lib()
+    torch.cuda.set_device(0)
+    wl = WORKLOADS[args.workload]
+    cfg_kw = dict(ring_pages=16, chunk_pages=4, copy_streams=4, group_pages=1)
+    st = setup(wl, cfg_kw, args.threads)
+    r = timed_run(wl, st, args.steps, args.warmup)
+    kv_bytes = wl.n_layers * wl.n_pages * st["recs"][0].shape[1]
+    value = kv_bytes / (r["ms_per_step"] / 1e3) / 1e9
+    layer_bytes = wl.n_pages * st["recs"][0].shape[1]
+    avg_att = r["attn_ms_total"] / max(1, r["attn_launches"])
+    achieved = layer_bytes / (avg_att / 1e3) / 1e9
+    traffic = stored_traffic(wl.name)
+    log(f"{wl.name}: {r['ms_per_step']:.4f} ms/step, {value:.1f} GB/s, attention kernel {avg_att * 1e3:.2f} us "
+        f"({achieved:.0f} GB/s), combine {r['combine_ms_total'] / max(1, r['combine_launches']) * 1e3:.2f} us")
+    qs_np = [q.cpu().numpy() for q in st["qs"]]
+    recs = st["recs"]
+    st["pool"].close()
+    del st
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "layers": wl.n_layers, "q_heads": wl.n_q_heads, "kv_heads": wl.n_kv_heads,
+            "head_dim": wl.head_dim, "context": wl.n_kv, "pages_per_layer": wl.n_pages,
+            "resident_pages_per_layer": wl.resident_pages, "query_tokens": wl.n_q, "cache": "q8_0 K / q4_0 V",
+            "kv_bytes_per_step": kv_bytes, **cfg_kw,
+        },
+        "attn_tok_s": round(wl.n_q / (r["ms_per_step"] / 1e3), 1),
+        "wall_ms_per_step": round(r["wall_ms_per_step"], 5),
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": "attend (resident launch)", "bytes_per_launch": layer_bytes,
+            "avg_launch_us": round(avg_att * 1e3, 3), "launches": r["attn_launches"],
+        },
+        "combine_avg_us": round(r["combine_ms_total"] / max(1, r["combine_launches"]) * 1e3, 3),
+    }
+
+    if not args.no_streamed:
+        link = measure_link()
+        swl = WORKLOADS["streamed_decode_256k"]
+        sst = setup(swl, cfg_kw, args.threads)
+        sr = timed_run(swl, sst, args.streamed_steps, 2)
+        st_info = sst["pool"].status()
+        pb = sst["recs"][0].shape[1]
+        streamed_bytes = sum(int((1 - m).sum()) for m in sst["masks"]) * pb
+        total_bytes = swl.n_layers * swl.n_pages * pb
+        sec = sr["ms_per_step"] / 1e3
+        res_bytes = swl.n_layers * swl.resident_pages * pb
+        result["streamed"] = {
+            "workload": swl.name, "context": swl.n_kv, "resident_pages_per_layer": swl.resident_pages,
+            "ms_per_step": round(sr["ms_per_step"], 4), "attn_tok_s": round(1 / sec, 3),
+            "kv_gbs": round(total_bytes / sec / 1e9, 2), "streamed_gbs": round(streamed_bytes / sec / 1e9, 2),
+            "link_gbs_measured": round(link, 2), "frac_of_link": round(streamed_bytes / sec / 1e9 / link, 4),
+            "streamed_bytes_per_step": streamed_bytes, "kv_bytes_per_step": total_bytes,
+            "copies_per_step": round(st_info.copies_issued / (args.streamed_steps + 2), 1),
+            "attn_launches_per_step": round(sr["attn_launches"] / args.streamed_steps, 1),
+            "attn_kernel_ms_per_step": round(sr["attn_ms_total"] / args.streamed_steps, 4),
+            "resident_bytes_per_step": res_bytes,
+        }
+        log(f"{swl.name}: {sr['ms_per_step']:.3f} ms/step, streamed {streamed_bytes / sec / 1e9:.2f} GB/s "
+            f"of link {link:.2f} GB/s")
+        sst["pool"].close()
+        del sst
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(wl, recs, qs_np)
+        log(f"cpu baseline: {result['cpu_baseline']['value']} GB/s on {result['cpu_baseline']['cores']} threads")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

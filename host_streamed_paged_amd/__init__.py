@@ -33,7 +33,7 @@ EXPORTS = [
     "kvs_type_pair_supported", "kvs_config_validate", "kvs_page_bytes", "kvs_min_budget_bytes",
     "kvs_slots_for_budget", "kvs_pool_create", "kvs_pool_destroy", "kvs_host_pages_set",
     "kvs_page_table_set", "kvs_stream_enqueue", "kvs_attend", "kvs_status", "kvs_debug_gather",
-    "kvs_debug_read_page", "kvs_last_error",
+    "kvs_debug_read_page", "kvs_last_error", "kvs_profile_enable", "kvs_profile_read",
 ]
 
 
@@ -86,6 +86,8 @@ def lib() -> ctypes.CDLL:
         "kvs_debug_gather": (ctypes.c_int, [P, I32, I64, I64, P, P, P]),
         "kvs_debug_read_page": (ctypes.c_int, [P, I32, I32, P]),
         "kvs_last_error": (ctypes.c_char_p, []),
+        "kvs_profile_enable": (ctypes.c_int, [P, I32]),
+        "kvs_profile_read": (ctypes.c_int, [P, I32, ctypes.POINTER(I64), ctypes.POINTER(ctypes.c_double), I32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -223,6 +225,15 @@ class Pool:
     def debug_gather(self, layer: int, tok0: int, n_tok: int, k_out: torch.Tensor, v_out: torch.Tensor,
                      stream=None):
         _check(lib().kvs_debug_gather(self._h, layer, tok0, n_tok, _ptr(k_out), _ptr(v_out), _stream(stream)))
+
+    def profile_enable(self, on: bool = True):
+        _check(lib().kvs_profile_enable(self._h, 1 if on else 0))
+
+    def profile_read(self, kind: int, reset: bool = True):
+        """(launches, total_ms) of attention (kind 0) or combine (kind 1) kernels."""
+        n, ms = ctypes.c_int64(0), ctypes.c_double(0.0)
+        _check(lib().kvs_profile_read(self._h, kind, ctypes.byref(n), ctypes.byref(ms), 1 if reset else 0))
+        return n.value, ms.value
 
     def debug_read_page(self, layer: int, page: int):
         import numpy as np

@@ -1,0 +1,470 @@
+// Decode attention kernel for few query rows (R = query tokens x heads per kv
+// head, R <= 6): VALU dot products on CDNA4. One workgroup per (page run of a
+// split-K group, kv head); 256 threads = 4 waves, and each wave owns a
+// 64-token slice of every page from load to weighted sum, so the waves never
+// wait on each other until the per-page merge.
+//
+// Per 64-token slice (a page is 256 tokens of one layer; page 2, "Dynamic
+// draft eject"):
+//   QK  lane = (token, 32-wide block). The lane loads its Q8_0 block straight
+//       from the page record (9 aligned dwords; odd blocks start 2 bytes into
+//       a dword and are realigned with v_perm) and forms exact integer dot
+//       products with v_dot4_i32_i8 against the query held as 16-bit fixed
+//       point (per row and block scale, split into int8 high and low bytes).
+//       The 4 blocks of a token are summed with two quad DPP adds.
+//   softmax  slice maxima per row by cross-lane reduction; p = exp2(s - m) in
+//       log2 units (the softmax scale is folded into the query scale).
+//   PV  lane = (32-wide block, byte position): its two channels are the low and
+//       high nibble of one byte. The slice's V rows are staged in the wave's
+//       LDS region; the lane builds two tokens' nibbles as exact f16 (u - 8)
+//       pairs and accumulates v_dot2_f32_f16 against p * d_v rounded to f16.
+//   The 4 slice partials of a page are merged into one page partial in a
+//   fixed order, and page partials are merged into the group state in page
+//   order: results do not depend on how pages are split into launches or
+//   which of them are resident.
+#include <hip/hip_runtime.h>
+#include <cstdint>
+#include <cmath>
+
+#include "kvs_internal.h"
+
+namespace kvs {
+namespace {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kSlice = kPageTokens / kWaves;   // 64 tokens per wave
+constexpr int kSlicePairs = kSlice / 2;        // 32 token pairs
+constexpr int kPPStride = kSlicePairs * 8 + 8; // dwords per block row of pp (padded: no bank clash across blocks)
+
+__device__ inline float f16_lo_to_float(uint32_t bits) {
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(bits & 0xFFFFu));
+}
+
+// lane i receives lane (i ^ 1) / (i ^ 2) of its quad
+__device__ inline float dpp_xor1(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+}
+__device__ inline float dpp_xor2(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+}
+// value of lane (4 * (i / 4) + SRC) of each quad
+template <int SRC>
+__device__ inline float quad_bcast(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), SRC * 0x55, 0xF, 0xF, false));
+}
+// lane i receives lane i +- 4 / 8 within its row of 16 (row rotate)
+__device__ inline float dpp_ror4(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
+}
+__device__ inline float dpp_ror8(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+}
+// max / sum over the 16 lanes of a wave that share (lane & 3)
+__device__ inline float max_over_tokens(float v) {
+    v = fmaxf(v, dpp_ror4(v));
+    v = fmaxf(v, dpp_ror8(v));
+    v = fmaxf(v, __shfl_xor(v, 16, 64));
+    v = fmaxf(v, __shfl_xor(v, 32, 64));
+    return v;
+}
+__device__ inline float sum_over_tokens(float v) {
+    v += dpp_ror4(v);
+    v += dpp_ror8(v);
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+// Workgroup barrier that orders LDS only: unlike __syncthreads() it does not
+// wait for outstanding global loads, so page data stays in flight across it.
+__device__ inline void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Uniform loads through the scalar cache (constant address space).
+template <typename T>
+__device__ inline T scalar_load(const T* p) {
+    return *(const __attribute__((address_space(4))) T*)p;
+}
+
+__device__ inline void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int R>
+struct DecodeSmem {
+    uint32_t q_hi[R][kNB][8];                     // query codes, high bytes, 4 per dword
+    uint32_t q_lo[R][kNB][8];                     // query codes, low bytes
+    float q_scale[R][kNB];                        // code -> log2-unit score scale
+    uint8_t v[kWaves][kSlice * kVRow];            // each wave's V rows (record layout)
+    uint32_t pp[kWaves][kNB][kPPStride];          // p * d_v as f16 pairs: [wave][block][pair * 8 + row]
+    float sacc[2][kWaves][R][kHeadDim];           // slice partials (double-buffered by page parity)
+    float sm_[2][kWaves][R], sl_[2][kWaves][R];
+};
+
+template <int R>
+__global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
+    __shared__ __attribute__((aligned(16))) DecodeSmem<R> sm;
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, l = tid & 63;
+    typedef int int4v __attribute__((ext_vector_type(4)));
+    const int4v segv = scalar_load((const int4v*)(a.segs + blockIdx.x));
+    const Seg seg = {segv.x, segv.y, segv.z, segv.w};
+    const int g = blockIdx.y;
+    const int G = a.G;
+
+    // QK role: block b, token u of each 16-token pass
+    const int b = l & 3, u = l >> 2;
+    const uint32_t sel = (b & 1) ? 0x07060504u : 0x05040302u;
+    const int dshift = 16 * (b & 1);
+    const int kboff = (kSlice * w + u) * kKRow + kKBlock * b - 2 * (b & 1);   // 4-aligned
+    // PV role: block bb, byte position j16 (channels 32 bb + j16 and 32 bb + 16 + j16)
+    const int j16 = l & 15, bb = l >> 4;
+
+    // Page loads are issued first so that their latency covers the query
+    // set-up. V rows go straight to the wave's LDS region with LDS DMA
+    // (global_load_lds_dwordx4, 16 bytes per lane); K blocks go to registers.
+    uint8_t* vt = sm.v[w];
+    constexpr int kVU4 = kSlice * kVRow / 16;   // 288 uint4 per slice
+    auto page_rec = [&](int page) -> const uint8_t* {
+        const int32_t sv = scalar_load(a.ps.src + page);
+        return sv >= 0 ? a.ps.slots + (int64_t)sv * a.ps.page_bytes
+                       : a.ps.ring_chunk + (int64_t)((-1 - sv) - a.ps.chunk_rank0) * a.ps.page_bytes;
+    };
+    auto issue_k = [&](const uint8_t* rec, uint32_t (&kw)[4][9]) {
+        const uint8_t* kt = rec + (int64_t)g * kKTile + kboff;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t* src = (const uint32_t*)(kt + p * 16 * kKRow);
+#pragma unroll
+            for (int k = 0; k < 9; ++k) kw[p][k] = src[k];
+        }
+    };
+    auto issue_v = [&](const uint8_t* rec) {
+        const uint4* vsrc = (const uint4*)(rec + (int64_t)a.n_kv_heads * kKTile + (int64_t)g * kVTile +
+                                           kSlice * w * kVRow);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vsrc + l + 64 * k),
+                                             (__attribute__((address_space(3))) void*)(vt + 1024 * k), 16, 0, 0);
+        if (l < kVU4 - 256)
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vsrc + l + 256),
+                                             (__attribute__((address_space(3))) void*)(vt + 4096), 16, 0, 0);
+    };
+
+    // ---- query rows -> 16-bit fixed point codes per (row, block). The query
+    // loads are issued before the page loads: vector memory counters retire in
+    // order, so the set-up below waits for the query only.
+    const bool qprep = tid < R * 16;
+    const int qr = tid >> 4, qb = (tid >> 2) & 3, qq = tid & 3;
+    uint4 qraw0 = make_uint4(0u, 0u, 0u, 0u), qraw1 = qraw0;   // raw query bits, converted once K is queued
+    if (qprep) {
+        const int i = qr / G, h = g * G + qr % G;
+        const int64_t off = ((int64_t)i * a.n_q_heads + h) * kHeadDim + qb * kQK + qq * 8;
+        if (a.q_f16) {
+            qraw0 = *(const uint4*)((const _Float16*)a.q + off);
+        } else {
+            const uint4* qp = (const uint4*)((const float*)a.q + off);
+            qraw0 = qp[0];
+            qraw1 = qp[1];
+        }
+    }
+    // memory counters retire in order: query, then K blocks, then (after the
+    // query codes are in LDS) the V rows
+    const uint8_t* rec0 = page_rec(seg.page0);
+    uint32_t kw[4][9];
+    issue_k(rec0, kw);
+    if (qprep) {
+        const int r = qr;
+        float x[8];
+        if (a.q_f16) {
+            const uint32_t wv[4] = {qraw0.x, qraw0.y, qraw0.z, qraw0.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = f16_lo_to_float(wv[e >> 1] >> (16 * (e & 1)));
+        } else {
+            const uint32_t wv[8] = {qraw0.x, qraw0.y, qraw0.z, qraw0.w, qraw1.x, qraw1.y, qraw1.z, qraw1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = __builtin_bit_cast(float, wv[e]);
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
+        amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+        // |code| <= 32639 keeps the high byte of (code + 128) >> 8 inside int8
+        const float inv = amax > 0.f ? 32639.f / amax : 0.f;
+        uint32_t hw[2] = {0u, 0u}, lw[2] = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            int c = (int)rintf(x[e] * inv);
+            c = c > 32639 ? 32639 : (c < -32639 ? -32639 : c);
+            const int hi = (c + 128) >> 8;
+            const int lo = c - hi * 256;
+            hw[e >> 2] |= (uint32_t)(hi & 0xFF) << (8 * (e & 3));
+            lw[e >> 2] |= (uint32_t)(lo & 0xFF) << (8 * (e & 3));
+        }
+        sm.q_hi[r][qb][2 * qq] = hw[0];
+        sm.q_hi[r][qb][2 * qq + 1] = hw[1];
+        sm.q_lo[r][qb][2 * qq] = lw[0];
+        sm.q_lo[r][qb][2 * qq + 1] = lw[1];
+        if (qq == 0) sm.q_scale[r][qb] = amax / 32639.f * a.scale_log2;
+    }
+    issue_v(rec0);
+    lds_barrier();
+    uint32_t qh[R][8], ql[R][8];
+    float qs[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) { qh[r][k] = sm.q_hi[r][b][k]; ql[r][k] = sm.q_lo[r][b][k]; }
+        qs[r] = sm.q_scale[r][b];
+    }
+
+    // group state, distributed for the per-page merge: thread owns channel
+    // c = tid & 127 of rows r = (tid >> 7) + 2 k
+    const int mc = tid & (kHeadDim - 1), mr0 = tid >> 7;
+    constexpr int kMR = (R + 1) / 2;
+    float acc_run[kMR], m_run[kMR], l_run[kMR];
+#pragma unroll
+    for (int k = 0; k < kMR; ++k) { acc_run[k] = 0.f; m_run[k] = -INFINITY; l_run[k] = 0.f; }
+    if (!(seg.flags & kSegFresh)) {
+#pragma unroll
+        for (int k = 0; k < kMR; ++k) {
+            const int r = mr0 + 2 * k;
+            if (r < R) {
+                const int i = r / G, h = g * G + r % G;
+                const float* pr = a.part + (((int64_t)seg.group * a.n_q + i) * a.n_q_heads + h) * kPartStride;
+                acc_run[k] = pr[mc];
+                m_run[k] = pr[kHeadDim];
+                l_run[k] = pr[kHeadDim + 1];
+            }
+        }
+    }
+
+    uint32_t* ppw = sm.pp[w][0];
+    for (int pi = 0; pi < seg.npages; ++pi) {
+        const int page = seg.page0 + pi;
+        const int par = pi & 1;
+        const int64_t rem = a.n_kv - (int64_t)page * kPageTokens - kSlice * w;
+        const int valid = (int)(rem < 0 ? 0 : (rem > kSlice ? kSlice : rem));   // valid rows of this slice
+
+        if (pi > 0) {   // this wave is done with its LDS region of the previous page
+            const uint8_t* rec = page_rec(page);
+            issue_k(rec, kw);
+            issue_v(rec);
+        }
+
+        // ---- scores. Slice row t is visible to query row r iff t <= lim[r].
+        int lim[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            int64_t l64 = (int64_t)valid - 1;
+            if (a.causal) {
+                const int64_t c = a.q_pos0 + r / G - (int64_t)page * kPageTokens - kSlice * w;
+                l64 = c < l64 ? c : l64;
+            }
+            lim[r] = (int)(l64 < -1 ? -1 : l64);
+        }
+        float s[4][R];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int t = 16 * p + u;
+            uint32_t c[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) c[k] = __builtin_amdgcn_perm(kw[p][k + 1], kw[p][k], sel);
+            const float d = f16_lo_to_float(kw[p][0] >> dshift);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                int ih = 0, il = 0;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    ih = __builtin_amdgcn_sdot4((int)c[k], (int)qh[r][k], ih, false);
+                    il = __builtin_amdgcn_sdot4((int)c[k], (int)ql[r][k], il, false);
+                }
+                float f = (float)(ih * 256 + il) * (qs[r] * d);
+                f += dpp_xor1(f);
+                f += dpp_xor2(f);
+                s[p][r] = t <= lim[r] ? f : -INFINITY;
+            }
+        }
+        // the V rows were loaded by LDS DMA before the K blocks; all K data has
+        // been consumed, and this makes the DMA writes visible to the reads below
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+        // ---- slice maxima, probabilities and row sums.
+        float m_w[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            m_w[r] = max_over_tokens(fmaxf(fmaxf(s[0][r], s[1][r]), fmaxf(s[2][r], s[3][r])));
+        // lane b of each quad exponentiates rows b and b + 4 of its 4 tokens
+        float ea[4], eb[4];
+        float la = 0.f, lb = 0.f;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            float sa = -INFINITY, sb = -INFINITY, ma = 0.f, mb = 0.f;
+#pragma unroll
+            for (int rx = 0; rx < 4; ++rx)
+                if (rx == b) {
+                    if (rx < R) { sa = s[p][rx]; ma = m_w[rx]; }
+                    if (rx + 4 < R) { sb = s[p][rx + 4]; mb = m_w[rx + 4]; }
+                }
+            ea[p] = sa == -INFINITY ? 0.f : exp2f(sa - ma);
+            eb[p] = sb == -INFINITY ? 0.f : exp2f(sb - mb);
+            la += ea[p];
+            lb += eb[p];
+        }
+        la = sum_over_tokens(la);
+        lb = sum_over_tokens(lb);
+        // p * d_v for this lane's block b, all rows (quad broadcasts share the exps)
+        {
+            float dv[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int t = 16 * p + u;
+                const float d = f16_lo_to_float(*(const uint16_t*)(vt + t * kVRow + b * kVBlock));
+                dv[p] = t < valid ? d : 0.f;   // rows past the cache may hold NaN scales
+            }
+            float pr[R][4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                if (R > 0) pr[0 % R][p] = quad_bcast<0>(ea[p]);
+                if (R > 1) pr[1 % R][p] = quad_bcast<1>(ea[p]);
+                if (R > 2) pr[2 % R][p] = quad_bcast<2>(ea[p]);
+                if (R > 3) pr[3 % R][p] = quad_bcast<3>(ea[p]);
+                if (R > 4) pr[4 % R][p] = quad_bcast<0>(eb[p]);
+                if (R > 5) pr[5 % R][p] = quad_bcast<1>(eb[p]);
+            }
+#pragma unroll
+            for (int q2 = 0; q2 < 2; ++q2) {
+                uint32_t hv[8];
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    if (r < R) {
+                        half2_t hp = {(_Float16)(pr[r][2 * q2] * dv[2 * q2]), (_Float16)(pr[r][2 * q2 + 1] * dv[2 * q2 + 1])};
+                        hv[r] = __builtin_bit_cast(uint32_t, hp);
+                    } else {
+                        hv[r] = 0u;
+                    }
+                }
+                uint4* dst = (uint4*)(ppw + b * kPPStride + (q2 * 16 + u) * 8);
+                dst[0] = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+                if (R > 4) dst[1] = make_uint4(hv[4], hv[5], hv[6], hv[7]);
+            }
+        }
+        wave_lds_sync();
+
+        // ---- P.V over the slice: 32 token pairs (t, t + 16), t = 32 q2 + u
+        float acc[R][2];
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r][0] = acc[r][1] = 0.f;
+        {
+            const uint8_t* vb = vt + bb * kVBlock + 2 + j16;
+            const uint4* ppb = (const uint4*)(ppw + bb * kPPStride);
+            const half2_t off_lo = {(_Float16)1032.f, (_Float16)1032.f};
+            const half2_t off_hi = {(_Float16)1152.f, (_Float16)1152.f};
+#pragma unroll
+            for (int n = 0; n < kSlicePairs; ++n) {
+                const int ta = 32 * (n >> 4) + (n & 15);
+                const uint32_t x = (uint32_t)vb[ta * kVRow] | ((uint32_t)vb[(ta + 16) * kVRow] << 16);
+                const half2_t lo = __builtin_bit_cast(half2_t, (x & 0x000F000Fu) | 0x64006400u) - off_lo;  // u - 8
+                const half2_t hi = __builtin_bit_cast(half2_t, (x & 0x00F000F0u) | 0x64006400u) - off_hi;  // 16 (u - 8)
+                const uint4 p0 = ppb[2 * n];
+                uint32_t prr[8] = {p0.x, p0.y, p0.z, p0.w, 0u, 0u, 0u, 0u};
+                if (R > 4) {
+                    const uint4 p1 = ppb[2 * n + 1];
+                    prr[4] = p1.x; prr[5] = p1.y; prr[6] = p1.z; prr[7] = p1.w;
+                }
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const half2_t ph = __builtin_bit_cast(half2_t, prr[r]);
+                    acc[r][0] = __builtin_amdgcn_fdot2(ph, lo, acc[r][0], false);
+                    acc[r][1] = __builtin_amdgcn_fdot2(ph, hi, acc[r][1], false);
+                }
+            }
+        }
+        // slice partial -> LDS (the next page writes the other parity)
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            sm.sacc[par][w][r][32 * bb + j16] = acc[r][0];
+            sm.sacc[par][w][r][32 * bb + 16 + j16] = acc[r][1] * 0.0625f;   // high nibbles carried 16 (u - 8)
+        }
+        if (l < 4) {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                if ((r & 3) == l) { sm.sm_[par][w][r] = m_w[r]; sm.sl_[par][w][r] = r < 4 ? la : lb; }
+        }
+        lds_barrier();
+
+        // ---- merge the 4 slices (fixed order), then the page into the group state
+#pragma unroll
+        for (int k = 0; k < kMR; ++k) {
+            const int r = mr0 + 2 * k;
+            if (r < R) {
+                float ms[kWaves], M = -INFINITY;
+#pragma unroll
+                for (int ww = 0; ww < kWaves; ++ww) { ms[ww] = sm.sm_[par][ww][r]; M = fmaxf(M, ms[ww]); }
+                float pa = 0.f, pl = 0.f;
+                if (M != -INFINITY) {
+#pragma unroll
+                    for (int ww = 0; ww < kWaves; ++ww) {
+                        const float f = ms[ww] == -INFINITY ? 0.f : exp2f(ms[ww] - M);
+                        pa = fmaf(sm.sacc[par][ww][r][mc], f, pa);
+                        pl = fmaf(sm.sl_[par][ww][r], f, pl);
+                    }
+                }
+                const float Mn = fmaxf(m_run[k], M);
+                if (Mn != -INFINITY) {
+                    const float al = m_run[k] == -INFINITY ? 0.f : exp2f(m_run[k] - Mn);
+                    const float be = M == -INFINITY ? 0.f : exp2f(M - Mn);
+                    acc_run[k] = acc_run[k] * al + pa * be;
+                    l_run[k] = l_run[k] * al + pl * be;
+                    m_run[k] = Mn;
+                }
+            }
+        }
+    }
+
+#pragma unroll
+    for (int k = 0; k < kMR; ++k) {
+        const int r = mr0 + 2 * k;
+        if (r < R) {
+            const int i = r / G, h = g * G + r % G;
+            float* pr = a.part + (((int64_t)seg.group * a.n_q + i) * a.n_q_heads + h) * kPartStride;
+            pr[mc] = acc_run[k];
+            if (mc == 0) { pr[kHeadDim] = m_run[k]; pr[kHeadDim + 1] = l_run[k]; }
+        }
+    }
+}
+
+template <int R>
+hipError_t launch_r(const AttendArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL(decode_kernel<R>, dim3(a.n_segs, a.n_kv_heads), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Up to 6 rows the query codes fit in registers (7 and 8 would spill).
+bool decode_supports(int rows) { return rows >= 1 && rows <= 6; }
+
+hipError_t launch_decode(const AttendArgs& a, hipStream_t stream) {
+    if (a.n_segs <= 0) return hipSuccess;
+    switch (a.n_q * a.G) {
+        case 1: return launch_r<1>(a, stream);
+        case 2: return launch_r<2>(a, stream);
+        case 3: return launch_r<3>(a, stream);
+        case 4: return launch_r<4>(a, stream);
+        case 5: return launch_r<5>(a, stream);
+        case 6: return launch_r<6>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace kvs

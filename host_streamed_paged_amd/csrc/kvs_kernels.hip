@@ -17,6 +17,7 @@
 #include <hip/hip_runtime.h>
 #include <cstdint>
 #include <cmath>
+#include <cstdlib>
 
 #include "kvs_internal.h"
 
@@ -198,30 +199,72 @@ __global__ __launch_bounds__(kThreads) void attend_rows_kernel(AttendArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Split-K combine: one workgroup per (query token, head), thread = channel.
-// Groups are merged in ascending order.
+// Split-K combine: one workgroup per (query token x head, 16-channel slice);
+// 256 threads = 16 channels x 16 group slices. Each thread walks groups
+// sl, sl + 16, ... in batches of 8 independent loads with an online
+// log-sum-exp merge; the 16 slices are then merged in a fixed order. The order
+// depends only on the number of groups, never on scheduling or residency.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* __restrict__ part, int32_t n_groups,
-                                                           int32_t rows, float* __restrict__ out,
-                                                           float* __restrict__ lse) {
-    const int row = blockIdx.x, c = threadIdx.x;
+constexpr int kCombSlices = 16;
+constexpr int kCombCh = 16;
+constexpr int kCombBatch = 8;
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part, int32_t n_groups,
+                                                      int32_t rows, float* __restrict__ out,
+                                                      float* __restrict__ lse) {
+    __shared__ float so[kCombSlices][kCombCh + 1];
+    __shared__ float sm_[kCombSlices], sl_[kCombSlices];
+    const int row = blockIdx.x / (kHeadDim / kCombCh), slice = blockIdx.x % (kHeadDim / kCombCh);
+    const int cl = threadIdx.x & (kCombCh - 1), sl = threadIdx.x / kCombCh;
+    const int c = slice * kCombCh + cl;
     const int64_t gstride = (int64_t)rows * kPartStride;
     const float* p = part + (int64_t)row * kPartStride;
-    float M = -INFINITY;
-    for (int gi = 0; gi < n_groups; ++gi) M = fmaxf(M, p[gi * gstride + kHeadDim]);
-    float o = 0.f, l = 0.f;
-    if (M != -INFINITY) {
-        for (int gi = 0; gi < n_groups; ++gi) {
-            const float* q = p + gi * gstride;
-            float m = q[kHeadDim];
-            float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
-            l = fmaf(q[kHeadDim + 1], w, l);
-            o = fmaf(q[c], w, o);
+    float M = -INFINITY, L = 0.f, O = 0.f;
+    for (int g0 = sl; g0 < n_groups; g0 += kCombSlices * kCombBatch) {
+        float mg[kCombBatch], lg[kCombBatch], og[kCombBatch];
+#pragma unroll
+        for (int k = 0; k < kCombBatch; ++k) {
+            const int gi = g0 + k * kCombSlices;
+            const bool ok = gi < n_groups;
+            const float* q = p + (int64_t)(ok ? gi : 0) * gstride;
+            mg[k] = ok ? q[kHeadDim] : -INFINITY;
+            lg[k] = q[kHeadDim + 1];
+            og[k] = q[c];
         }
-        o = o / l;
+        float Mb = M;
+#pragma unroll
+        for (int k = 0; k < kCombBatch; ++k) Mb = fmaxf(Mb, mg[k]);
+        if (Mb == -INFINITY) continue;
+        const float sc = (M == -INFINITY) ? 0.f : exp2f(M - Mb);
+        L *= sc;
+        O *= sc;
+#pragma unroll
+        for (int k = 0; k < kCombBatch; ++k) {
+            const float w = (mg[k] == -INFINITY) ? 0.f : exp2f(mg[k] - Mb);
+            L = fmaf(lg[k], w, L);
+            O = fmaf(og[k], w, O);
+        }
+        M = Mb;
     }
-    out[(int64_t)row * kHeadDim + c] = o;
-    if (lse && c == 0) lse[row] = (M == -INFINITY) ? -INFINITY : (M + log2f(l)) * 0.69314718055994530942f;
+    so[sl][cl] = O;
+    if (cl == 0) { sm_[sl] = M; sl_[sl] = L; }
+    __syncthreads();
+    if (sl == 0) {
+        float Mt = sm_[0];
+#pragma unroll
+        for (int k = 1; k < kCombSlices; ++k) Mt = fmaxf(Mt, sm_[k]);
+        float ot = 0.f, lt = 0.f;
+        if (Mt != -INFINITY) {
+#pragma unroll
+            for (int k = 0; k < kCombSlices; ++k) {
+                const float w = (sm_[k] == -INFINITY) ? 0.f : exp2f(sm_[k] - Mt);
+                ot = fmaf(so[k][cl], w, ot);
+                lt = fmaf(sl_[k], w, lt);
+            }
+        }
+        out[(int64_t)row * kHeadDim + c] = (Mt == -INFINITY) ? 0.f : ot / lt;
+        if (lse && slice == 0 && cl == 0)
+            lse[row] = (Mt == -INFINITY) ? -INFINITY : (Mt + log2f(lt)) * 0.69314718055994530942f;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -265,6 +308,7 @@ __global__ void fill_u32_kernel(uint32_t* __restrict__ p, uint32_t v, uint64_t n
 hipError_t launch_attend(const AttendArgs& a, hipStream_t stream) {
     if (a.n_segs <= 0) return hipSuccess;
     const int R = a.n_q * a.G;
+    if (decode_supports(R)) return launch_decode(a, stream);
     dim3 grid(a.n_segs, a.n_kv_heads, (R + kRT - 1) / kRT);
     hipLaunchKernelGGL(attend_rows_kernel, grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();
@@ -274,7 +318,7 @@ hipError_t launch_combine(const float* part, int32_t n_groups, int32_t n_q, int3
                           float* out, float* lse, hipStream_t stream) {
     const int rows = n_q * n_q_heads;
     if (rows <= 0) return hipSuccess;
-    hipLaunchKernelGGL(combine_kernel, dim3(rows), dim3(kHeadDim), 0, stream, part, n_groups, rows, out, lse);
+    hipLaunchKernelGGL(combine_kernel, dim3(rows * (kHeadDim / kCombCh)), dim3(256), 0, stream, part, n_groups, rows, out, lse);
     return hipGetLastError();
 }
 

@@ -139,9 +139,38 @@ struct kvs_pool {
     int32_t pf_issued = 0;           // chunks of it issued so far
     bool broken = false;             // a HIP call failed mid-sequence
     kvs_status_info st{};
+    // kernel timing (kvs_profile_*): per kind, event pairs in launch order
+    bool profiling = false;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> prof_ev[2];
+    size_t prof_used[2] = {0, 0};
 };
 
 namespace {
+
+constexpr size_t kMaxTimed = 65536;
+
+// Launch fn() on stream, bracketed by timing events when profiling is on.
+template <typename Fn>
+hipError_t timed(kvs_pool* p, int kind, hipStream_t s, Fn fn) {
+    if (!p->profiling || p->prof_used[kind] >= kMaxTimed) return fn();
+    auto& v = p->prof_ev[kind];
+    if (p->prof_used[kind] == v.size()) {
+        hipEvent_t a, b;
+        hipError_t e = hipEventCreate(&a);
+        if (e != hipSuccess) return e;
+        e = hipEventCreate(&b);
+        if (e != hipSuccess) { (void)hipEventDestroy(a); return e; }
+        v.push_back({a, b});
+    }
+    auto& pr = v[p->prof_used[kind]];
+    hipError_t e = hipEventRecord(pr.first, s);
+    if (e != hipSuccess) return e;
+    e = fn();
+    if (e != hipSuccess) return e;
+    e = hipEventRecord(pr.second, s);
+    if (e == hipSuccess) p->prof_used[kind]++;
+    return e;
+}
 
 int check_device(const kvs_pool* p) {
     int dev = -1;
@@ -416,6 +445,8 @@ void kvs_pool_destroy(kvs_pool* p) {
     for (auto e : p->filled) (void)hipEventDestroy(e);
     for (auto e : p->freed) (void)hipEventDestroy(e);
     if (p->last_work) (void)hipEventDestroy(p->last_work);
+    for (auto& v : p->prof_ev)
+        for (auto& pr : v) { (void)hipEventDestroy(pr.first); (void)hipEventDestroy(pr.second); }
     delete p;
 }
 
@@ -537,11 +568,11 @@ int kvs_attend(kvs_pool* p, int32_t layer, const void* q, int32_t q_dtype, int32
         b.ps.chunk_rank0 = rank0;
         b.segs = ls.dev_segs + seg0;
         b.n_segs = nseg;
-        hipError_t e = kvs::launch_attend(b, s);
+        hipError_t e = timed(p, 0, s, [&] { return kvs::launch_attend(b, s); });
         return e == hipSuccess ? KVS_OK : fail(KVS_ERR_HIP, "attention kernel launch failed: %s", hipGetErrorString(e));
     });
     if (rc) return rc;
-    hipError_t e = kvs::launch_combine(p->work, ls.n_groups, n_q, p->cfg.n_q_heads, out, lse, s);
+    hipError_t e = timed(p, 1, s, [&] { return kvs::launch_combine(p->work, ls.n_groups, n_q, p->cfg.n_q_heads, out, lse, s); });
     if (e != hipSuccess) { p->broken = true; return fail(KVS_ERR_HIP, "combine launch failed: %s", hipGetErrorString(e)); }
     p->st.kernels_launched++;
     if (hipEventRecord(p->last_work, s) != hipSuccess) { p->broken = true; return fail(KVS_ERR_HIP, "hipEventRecord failed"); }
@@ -599,6 +630,29 @@ int kvs_debug_read_page(kvs_pool* p, int32_t layer, int32_t page, void* dst_host
     if (ls.src[page] < 0) return fail(KVS_ERR_NOT_RESIDENT, "page %d of layer %d is streamed, not resident", page, layer);
     KVS_HIP(hipEventSynchronize(p->last_work));
     KVS_HIP(hipMemcpy(dst_host, p->slots + (uint64_t)ls.src[page] * p->L.page_bytes, p->L.page_bytes, hipMemcpyDeviceToHost));
+    return KVS_OK;
+}
+
+int kvs_profile_enable(kvs_pool* p, int32_t enable) {
+    if (!p) return fail(KVS_ERR_INVALID_ARG, "pool is NULL");
+    p->profiling = enable != 0;
+    return KVS_OK;
+}
+
+int kvs_profile_read(kvs_pool* p, int32_t kind, int64_t* launches, double* total_ms, int32_t reset) {
+    if (!p || !launches || !total_ms) return fail(KVS_ERR_INVALID_ARG, "NULL argument");
+    if (kind < 0 || kind > 1) return fail(KVS_ERR_INVALID_ARG, "kind %d unknown", kind);
+    double ms = 0.0;
+    for (size_t i = 0; i < p->prof_used[kind]; ++i) {
+        auto& pr = p->prof_ev[kind][i];
+        KVS_HIP(hipEventSynchronize(pr.second));
+        float t = 0.f;
+        KVS_HIP(hipEventElapsedTime(&t, pr.first, pr.second));
+        ms += t;
+    }
+    *launches = (int64_t)p->prof_used[kind];
+    *total_ms = ms;
+    if (reset) p->prof_used[kind] = 0;
     return KVS_OK;
 }
 

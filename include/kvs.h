@@ -206,6 +206,15 @@ int kvs_debug_gather(kvs_pool* pool, int32_t layer, int64_t tok0, int64_t n_tok,
  * Synchronous. KVS_ERR_NOT_RESIDENT for a streamed page. */
 int kvs_debug_read_page(kvs_pool* pool, int32_t layer, int32_t page, void* dst_host);
 
+/* Kernel timing. With enable != 0, kvs_attend brackets every attention kernel
+ * launch (kind 0) and every split-K combine launch (kind 1) with timing
+ * events recorded on the compute stream it was given. kvs_profile_read waits
+ * for the recorded events and returns the number of timed launches of that
+ * kind and their summed duration in milliseconds; reset != 0 clears the
+ * record. At most 65536 launches per kind are kept (later ones are not timed). */
+int kvs_profile_enable(kvs_pool* pool, int32_t enable);
+int kvs_profile_read(kvs_pool* pool, int32_t kind, int64_t* launches, double* total_ms, int32_t reset);
+
 /* Message of the last failing call on this thread ("" if none). */
 const char* kvs_last_error(void);
 
