@@ -45,22 +45,22 @@ __device__ inline float f16_lo_to_float(uint32_t bits) {
 
 // lane i receives lane (i ^ 1) / (i ^ 2) of its quad
 __device__ inline float dpp_xor1(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
 }
 __device__ inline float dpp_xor2(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
 }
 // value of lane (4 * (i / 4) + SRC) of each quad
 template <int SRC>
 __device__ inline float quad_bcast(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), SRC * 0x55, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), SRC * 0x55, 0xF, 0xF, true));
 }
 // lane i receives lane i +- 4 / 8 within its row of 16 (row rotate)
 __device__ inline float dpp_ror4(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, true));
 }
 __device__ inline float dpp_ror8(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, true));
 }
 // max / sum over the 16 lanes of a wave that share (lane & 3)
 __device__ inline float max_over_tokens(float v) {
@@ -76,6 +76,22 @@ __device__ inline float sum_over_tokens(float v) {
     v += __shfl_xor(v, 16, 64);
     v += __shfl_xor(v, 32, 64);
     return v;
+}
+
+// A 32-bit constant held in a VGPR the compiler cannot see through, so
+// three-operand VALU ops (v_and_or_b32) can take it: gfx9 VOP3 encodings have
+// no literal field and read at most one scalar operand.
+__device__ inline uint32_t vconst(uint32_t c) {
+    uint32_t r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
+    return r;
+}
+
+// a . b over 4 signed bytes, starting from 0
+__device__ inline int sdot4_first(uint32_t a, uint32_t b) {
+    int r;
+    asm("v_dot4_i32_i8 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
 }
 
 // Workgroup barrier that orders LDS only: unlike __syncthreads() it does not
@@ -98,14 +114,17 @@ __device__ inline void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Every array that is read or written 16 bytes at a time (LDS DMA targets,
+// uint4 reads) sits on a 16-byte boundary; misaligned 128-bit LDS accesses
+// are split and stall.
 template <int R>
 struct DecodeSmem {
-    uint32_t q_hi[R][kNB][8];                     // query codes, high bytes, 4 per dword
-    uint32_t q_lo[R][kNB][8];                     // query codes, low bytes
-    float q_scale[R][kNB];                        // code -> log2-unit score scale
-    uint8_t v[kWaves][kSlice * kVRow];            // each wave's V rows (record layout)
-    uint32_t pp[kWaves][kNB][kPPStride];          // p * d_v as f16 pairs: [wave][block][pair * 8 + row]
-    float sacc[2][kWaves][R][kHeadDim];           // slice partials (double-buffered by page parity)
+    alignas(16) uint8_t v[kWaves][kSlice * kVRow];            // each wave's V rows (record layout)
+    alignas(16) uint32_t pp[kWaves][kNB][kPPStride];          // p * d_v as f16 pairs: [wave][block][pair * 8 + row]
+    alignas(16) float sacc[2][kWaves][R][kHeadDim];           // slice partials (double-buffered by page parity)
+    alignas(16) uint32_t q_hi[R][kNB][8];                     // query codes, high bytes, 4 per dword
+    alignas(16) uint32_t q_lo[R][kNB][8];                     // query codes, low bytes
+    float q_scale[R];                                         // code -> log2-unit score scale, per row
     float sm_[2][kWaves][R], sl_[2][kWaves][R];
 };
 
@@ -196,10 +215,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
         float amax = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
-        amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-        amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-        // |code| <= 32639 keeps the high byte of (code + 128) >> 8 inside int8
-        const float inv = amax > 0.f ? 32639.f / amax : 0.f;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));   // the row's 16 threads
+        // |code| <= 32639 keeps the high byte of (code + 128) >> 8 inside int8;
+        // a negative softmax scale is folded into the codes' sign
+        const float inv = amax > 0.f ? (a.scale_log2 < 0.f ? -32639.f : 32639.f) / amax : 0.f;
         uint32_t hw[2] = {0u, 0u}, lw[2] = {0u, 0u};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -214,7 +234,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
         sm.q_hi[r][qb][2 * qq + 1] = hw[1];
         sm.q_lo[r][qb][2 * qq] = lw[0];
         sm.q_lo[r][qb][2 * qq + 1] = lw[1];
-        if (qq == 0) sm.q_scale[r][qb] = amax / 32639.f * a.scale_log2;
+        if (qb == 0 && qq == 0) sm.q_scale[r] = amax / 32639.f * fabsf(a.scale_log2);
     }
     issue_v(rec0);
     lds_barrier();
@@ -224,7 +244,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
     for (int r = 0; r < R; ++r) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) { qh[r][k] = sm.q_hi[r][b][k]; ql[r][k] = sm.q_lo[r][b][k]; }
-        qs[r] = sm.q_scale[r][b];
+        qs[r] = sm.q_scale[r];
     }
 
     // group state, distributed for the per-page merge: thread owns channel
@@ -280,15 +300,26 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) c[k] = __builtin_amdgcn_perm(kw[p][k + 1], kw[p][k], sel);
             const float d = f16_lo_to_float(kw[p][0] >> dshift);
+            // 2 R independent accumulator chains, interleaved so that no dot
+            // waits on the one before it
+            int ih[R], il[R];
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                int ih = 0, il = 0;
+                ih[r] = sdot4_first(c[0], qh[r][0]);
+                il[r] = sdot4_first(c[0], ql[r][0]);
+            }
 #pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    ih = __builtin_amdgcn_sdot4((int)c[k], (int)qh[r][k], ih, false);
-                    il = __builtin_amdgcn_sdot4((int)c[k], (int)ql[r][k], il, false);
+            for (int k = 1; k < 8; ++k) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    ih[r] = __builtin_amdgcn_sdot4((int)c[k], (int)qh[r][k], ih[r], false);
+                    il[r] = __builtin_amdgcn_sdot4((int)c[k], (int)ql[r][k], il[r], false);
                 }
-                float f = (float)(ih * 256 + il) * (qs[r] * d);
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                // score / (row scale): the row scale is applied inside the exponent
+                float f = (float)(ih[r] * 256 + il[r]) * d;
                 f += dpp_xor1(f);
                 f += dpp_xor2(f);
                 s[p][r] = t <= lim[r] ? f : -INFINITY;
@@ -308,15 +339,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
         float la = 0.f, lb = 0.f;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            float sa = -INFINITY, sb = -INFINITY, ma = 0.f, mb = 0.f;
+            float sa = -INFINITY, sb = -INFINITY, ma = 0.f, mb = 0.f, ka = 0.f, kb = 0.f;
 #pragma unroll
             for (int rx = 0; rx < 4; ++rx)
                 if (rx == b) {
-                    if (rx < R) { sa = s[p][rx]; ma = m_w[rx]; }
-                    if (rx + 4 < R) { sb = s[p][rx + 4]; mb = m_w[rx + 4]; }
+                    if (rx < R) { sa = s[p][rx]; ma = m_w[rx]; ka = qs[rx]; }
+                    if (rx + 4 < R) { sb = s[p][rx + 4]; mb = m_w[rx + 4]; kb = qs[rx + 4]; }
                 }
-            ea[p] = sa == -INFINITY ? 0.f : exp2f(sa - ma);
-            eb[p] = sb == -INFINITY ? 0.f : exp2f(sb - mb);
+            ea[p] = sa == -INFINITY ? 0.f : exp2f(ka * (sa - ma));
+            eb[p] = sb == -INFINITY ? 0.f : exp2f(kb * (sb - mb));
             la += ea[p];
             lb += eb[p];
         }
@@ -369,12 +400,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
             const uint4* ppb = (const uint4*)(ppw + bb * kPPStride);
             const half2_t off_lo = {(_Float16)1032.f, (_Float16)1032.f};
             const half2_t off_hi = {(_Float16)1152.f, (_Float16)1152.f};
+            const uint32_t m_lo = vconst(0x000F000Fu), m_hi = vconst(0x00F000F0u), magic = vconst(0x64006400u);
 #pragma unroll
             for (int n = 0; n < kSlicePairs; ++n) {
                 const int ta = 32 * (n >> 4) + (n & 15);
-                const uint32_t x = (uint32_t)vb[ta * kVRow] | ((uint32_t)vb[(ta + 16) * kVRow] << 16);
-                const half2_t lo = __builtin_bit_cast(half2_t, (x & 0x000F000Fu) | 0x64006400u) - off_lo;  // u - 8
-                const half2_t hi = __builtin_bit_cast(half2_t, (x & 0x00F000F0u) | 0x64006400u) - off_hi;  // 16 (u - 8)
+                const uint32_t x = __builtin_amdgcn_perm((uint32_t)vb[(ta + 16) * kVRow], (uint32_t)vb[ta * kVRow], 0x0c040c00u);
+                const half2_t lo = __builtin_bit_cast(half2_t, (x & m_lo) | magic) - off_lo;  // u - 8
+                const half2_t hi = __builtin_bit_cast(half2_t, (x & m_hi) | magic) - off_hi;  // 16 (u - 8)
                 const uint4 p0 = ppb[2 * n];
                 uint32_t prr[8] = {p0.x, p0.y, p0.z, p0.w, 0u, 0u, 0u, 0u};
                 if (R > 4) {
@@ -398,7 +430,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
         if (l < 4) {
 #pragma unroll
             for (int r = 0; r < R; ++r)
-                if ((r & 3) == l) { sm.sm_[par][w][r] = m_w[r]; sm.sl_[par][w][r] = r < 4 ? la : lb; }
+                if ((r & 3) == l) {
+                    sm.sm_[par][w][r] = m_w[r] == -INFINITY ? -INFINITY : qs[r] * m_w[r];
+                    sm.sl_[par][w][r] = r < 4 ? la : lb;
+                }
         }
         lds_barrier();
 
