@@ -131,6 +131,10 @@ struct DecodeSmem {
 template <int R>
 __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
     __shared__ __attribute__((aligned(16))) DecodeSmem<R> sm;
+    if ((int)blockIdx.x >= a.n_segs) {   // ring refill workgroup
+        copy_role(a.copy, ((int)blockIdx.x - a.n_segs) * (int)gridDim.y + (int)blockIdx.y);
+        return;
+    }
     const int tid = threadIdx.x;
     const int w = tid >> 6, l = tid & 63;
     typedef int int4v __attribute__((ext_vector_type(4)));
@@ -480,7 +484,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
 
 template <int R>
 hipError_t launch_r(const AttendArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL(decode_kernel<R>, dim3(a.n_segs, a.n_kv_heads), dim3(kThreads), 0, stream, a);
+    const int cx = (copy_workgroups(a.copy) + a.n_kv_heads - 1) / a.n_kv_heads;
+    hipLaunchKernelGGL(decode_kernel<R>, dim3(a.n_segs + cx, a.n_kv_heads), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -490,7 +495,7 @@ hipError_t launch_r(const AttendArgs& a, hipStream_t stream) {
 bool decode_supports(int rows) { return rows >= 1 && rows <= 6; }
 
 hipError_t launch_decode(const AttendArgs& a, hipStream_t stream) {
-    if (a.n_segs <= 0) return hipSuccess;
+    if (a.n_segs <= 0 && copy_workgroups(a.copy) == 0) return hipSuccess;
     switch (a.n_q * a.G) {
         case 1: return launch_r<1>(a, stream);
         case 2: return launch_r<2>(a, stream);

@@ -47,7 +47,52 @@ __host__ __device__ inline const uint8_t* page_ptr(const PageSource& ps, int32_t
     return ps.ring_chunk + (int64_t)((-1 - s) - ps.chunk_rank0) * ps.page_bytes;
 }
 
+// Ring refill carried by a launch: copy workgroups (blockIdx.x >= n_segs)
+// copy n_pages page records from pinned host memory into consecutive ring
+// slots at ring_dst, while the other workgroups compute on earlier slots.
+constexpr int kMaxCopyPages = 16;
+constexpr int kCopyPartBytes = 32768;   // bytes per copy workgroup
+struct CopyJob {
+    const uint8_t* host;                // the layer's host records (page-major)
+    uint8_t* ring_dst;                  // first ring slot to fill
+    int64_t page_bytes;
+    int32_t n_pages;                    // pages to copy (0: none)
+    int32_t parts_per_page;             // copy workgroups per page
+    int32_t pages[kMaxCopyPages];       // logical page of each copied slot
+};
+
+// Copy role of a workgroup: part `part` of the job's pages. Global loads of
+// the whole part are issued before any store so that many host-memory reads
+// are in flight over the link.
+__device__ inline void copy_role(const CopyJob& cj, int part) {
+    const int page_i = part / cj.parts_per_page, sub = part % cj.parts_per_page;
+    if (page_i >= cj.n_pages) return;
+    const int64_t off = (int64_t)sub * kCopyPartBytes;
+    const int64_t n = cj.page_bytes - off < kCopyPartBytes ? cj.page_bytes - off : kCopyPartBytes;
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4* src = (const u32x4*)(cj.host + (int64_t)cj.pages[page_i] * cj.page_bytes + off);
+    u32x4* dst = (u32x4*)(cj.ring_dst + (int64_t)page_i * cj.page_bytes + off);
+    const int n16 = (int)(n / 16);
+    constexpr int kPer = kCopyPartBytes / 16 / 256;   // 8 x 16 bytes per thread
+    u32x4 v[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int e = threadIdx.x + 256 * k;
+        if (e < n16) v[k] = __builtin_nontemporal_load(src + e);
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int e = threadIdx.x + 256 * k;
+        if (e < n16) dst[e] = v[k];
+    }
+}
+
+__host__ __device__ inline int copy_workgroups(const CopyJob& cj) {
+    return cj.n_pages * cj.parts_per_page;
+}
+
 struct AttendArgs {
+    CopyJob copy;         // ring refill carried by this launch
     PageSource ps;
     const Seg* segs;      // this launch's segments
     int32_t n_segs;
@@ -65,6 +110,7 @@ struct AttendArgs {
 };
 
 struct GatherArgs {
+    CopyJob copy;
     PageSource ps;
     const Seg* segs;
     int32_t n_segs;
@@ -83,5 +129,6 @@ hipError_t launch_combine(const float* part, int32_t n_groups, int32_t n_q, int3
                           float* out, float* lse, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
 hipError_t launch_fill_u32(void* dst, uint32_t value, uint64_t n_words, hipStream_t stream);
+hipError_t launch_copy(const CopyJob& cj, hipStream_t stream);   // copy-only launch
 
 }  // namespace kvs

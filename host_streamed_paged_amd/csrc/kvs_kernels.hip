@@ -56,6 +56,10 @@ __global__ __launch_bounds__(kThreads) void attend_rows_kernel(AttendArgs a) {
     __shared__ float p_s[kRT][kPageTokens];
     __shared__ float m_s[kRT], l_s[kRT];
 
+    if ((int)blockIdx.x >= a.n_segs) {   // ring refill workgroup
+        if (blockIdx.z == 0) copy_role(a.copy, ((int)blockIdx.x - a.n_segs) * (int)gridDim.y + (int)blockIdx.y);
+        return;
+    }
     const int tid = threadIdx.x;
     const Seg seg = a.segs[blockIdx.x];
     const int g = blockIdx.y;
@@ -272,6 +276,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 // One workgroup per (segment, kv head); thread = token row of the page.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kPageTokens) void gather_kernel(GatherArgs a) {
+    if ((int)blockIdx.x >= a.n_segs) {   // ring refill workgroup
+        copy_role(a.copy, ((int)blockIdx.x - a.n_segs) * (int)gridDim.y + (int)blockIdx.y);
+        return;
+    }
     const Seg seg = a.segs[blockIdx.x];
     const int g = blockIdx.y, t = threadIdx.x;
     for (int pi = 0; pi < seg.npages; ++pi) {
@@ -298,6 +306,8 @@ __global__ __launch_bounds__(kPageTokens) void gather_kernel(GatherArgs a) {
     }
 }
 
+__global__ __launch_bounds__(256) void copy_kernel(CopyJob cj) { copy_role(cj, (int)blockIdx.x); }
+
 __global__ void fill_u32_kernel(uint32_t* __restrict__ p, uint32_t v, uint64_t n) {
     for (uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; i < n; i += (uint64_t)gridDim.x * blockDim.x)
         p[i] = v;
@@ -306,10 +316,11 @@ __global__ void fill_u32_kernel(uint32_t* __restrict__ p, uint32_t v, uint64_t n
 }  // namespace
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t stream) {
-    if (a.n_segs <= 0) return hipSuccess;
+    if (a.n_segs <= 0 && copy_workgroups(a.copy) == 0) return hipSuccess;
     const int R = a.n_q * a.G;
     if (decode_supports(R)) return launch_decode(a, stream);
-    dim3 grid(a.n_segs, a.n_kv_heads, (R + kRT - 1) / kRT);
+    const int cx = (copy_workgroups(a.copy) + a.n_kv_heads - 1) / a.n_kv_heads;
+    dim3 grid(a.n_segs + cx, a.n_kv_heads, (R + kRT - 1) / kRT);
     hipLaunchKernelGGL(attend_rows_kernel, grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
@@ -323,8 +334,16 @@ hipError_t launch_combine(const float* part, int32_t n_groups, int32_t n_q, int3
 }
 
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream) {
-    if (a.n_segs <= 0) return hipSuccess;
-    hipLaunchKernelGGL(gather_kernel, dim3(a.n_segs, a.n_kv_heads), dim3(kPageTokens), 0, stream, a);
+    if (a.n_segs <= 0 && copy_workgroups(a.copy) == 0) return hipSuccess;
+    const int cx = (copy_workgroups(a.copy) + a.n_kv_heads - 1) / a.n_kv_heads;
+    hipLaunchKernelGGL(gather_kernel, dim3(a.n_segs + cx, a.n_kv_heads), dim3(kPageTokens), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy(const CopyJob& cj, hipStream_t stream) {
+    const int n = copy_workgroups(cj);
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(copy_kernel, dim3(n), dim3(256), 0, stream, cj);
     return hipGetLastError();
 }
 

@@ -71,8 +71,9 @@ int validate(const kvs_config* c) {
     if (c->max_pages < 1 || c->max_pages > (1 << 22)) return fail(KVS_ERR_INVALID_ARG, "max_pages %d out of range [1, 2^22]", c->max_pages);
     if (c->max_q_tokens < 1 || c->max_q_tokens > 8192) return fail(KVS_ERR_INVALID_ARG, "max_q_tokens %d out of range [1, 8192]", c->max_q_tokens);
     if (c->ring_pages < 1 || c->ring_pages > 4096) return fail(KVS_ERR_INVALID_ARG, "ring_pages %d out of range [1, 4096]", c->ring_pages);
-    if (c->chunk_pages < 1 || c->ring_pages % c->chunk_pages)
-        return fail(KVS_ERR_INVALID_ARG, "chunk_pages %d must be >= 1 and divide ring_pages %d", c->chunk_pages, c->ring_pages);
+    if (c->chunk_pages < 1 || c->chunk_pages > kvs::kMaxCopyPages || c->ring_pages % c->chunk_pages)
+        return fail(KVS_ERR_INVALID_ARG, "chunk_pages %d must be in [1, %d] and divide ring_pages %d", c->chunk_pages,
+                    kvs::kMaxCopyPages, c->ring_pages);
     if (c->copy_streams < 1 || c->copy_streams > 8) return fail(KVS_ERR_INVALID_ARG, "copy_streams %d out of range [1, 8]", c->copy_streams);
     if (c->group_pages < 1) return fail(KVS_ERR_INVALID_ARG, "group_pages %d must be >= 1", c->group_pages);
     if (c->flags & ~uint32_t(KVS_FLAG_POISON_RING)) return fail(KVS_ERR_INVALID_ARG, "unknown flag bits 0x%x", c->flags);
@@ -129,14 +130,16 @@ struct kvs_pool {
     int64_t n_slots = 0;
     std::vector<int32_t> slot_free;  // stack of free slot ids
     std::vector<LayerState> layers;
-    std::vector<hipStream_t> copy;
+    std::vector<hipStream_t> copy;   // stream prefetches (kvs_stream_enqueue) run on copy[0]
     int32_t n_cslots = 0;            // chunk slots in the ring
-    std::vector<hipEvent_t> filled, freed;
+    hipEvent_t pf_done = nullptr;    // recorded on copy[0] after a prefetch
+    hipEvent_t ring_free = nullptr;  // recorded on the compute stream after a layer's last ring read
+    bool ring_used = false;          // ring_free has been recorded at least once
     hipEvent_t last_work = nullptr;  // recorded after every attend / gather
-    int32_t ring_next = 0;           // next chunk slot the ring fills
-    int32_t pf_layer = -1;           // layer whose prefetch is outstanding
-    int32_t pf_slot0 = 0;            // chunk slot of that layer's chunk 0
-    int32_t pf_issued = 0;           // chunks of it issued so far
+    hipStream_t lane = nullptr;      // second compute lane for ring chunks
+    hipEvent_t fork_ev = nullptr, join_ev = nullptr;
+    int32_t ring_next = 0;           // chunk slot that receives the next layer's chunk 0
+    int32_t pf_layer = -1;           // layer whose chunk 0 was prefetched and not yet consumed
     bool broken = false;             // a HIP call failed mid-sequence
     kvs_status_info st{};
     // kernel timing (kvs_profile_*): per kind, event pairs in launch order
@@ -252,76 +255,122 @@ int build_plan(const kvs_pool* p, LayerState& ls, int32_t n_pages, const uint8_t
     return KVS_OK;
 }
 
-int issue_copy(kvs_pool* p, const LayerState& ls, int32_t c, int32_t cslot) {
+kvs::CopyJob make_copy(const kvs_pool* p, const LayerState& ls, int32_t c, int32_t cslot) {
+    kvs::CopyJob cj{};
     const ChunkPlan& cp = ls.chunks[c];
-    hipStream_t s = p->copy[cslot % p->copy.size()];
-    KVS_HIP(hipStreamWaitEvent(s, p->freed[cslot], 0));
-    uint8_t* dst = p->ring + (uint64_t)cslot * p->cfg.chunk_pages * p->L.page_bytes;
-    for (const auto& run : cp.runs) {
-        const uint64_t n = (uint64_t)run.second * p->L.page_bytes;
-        KVS_HIP(hipMemcpyAsync(dst, ls.host + (uint64_t)run.first * p->L.page_bytes, n, hipMemcpyHostToDevice, s));
-        dst += n;
-        p->st.copies_issued++;
-        p->st.bytes_h2d += (int64_t)n;
-        p->st.pages_streamed += run.second;
-    }
-    KVS_HIP(hipEventRecord(p->filled[cslot], s));
-    return KVS_OK;
+    cj.host = ls.host;
+    cj.ring_dst = p->ring + (uint64_t)cslot * p->cfg.chunk_pages * p->L.page_bytes;
+    cj.page_bytes = (int64_t)p->L.page_bytes;
+    cj.n_pages = cp.npages;
+    cj.parts_per_page = (int32_t)((p->L.page_bytes + kvs::kCopyPartBytes - 1) / kvs::kCopyPartBytes);
+    int32_t k = 0;
+    for (const auto& run : cp.runs)
+        for (int32_t j = 0; j < run.second; ++j) cj.pages[k++] = run.first + j;
+    return cj;
 }
 
+void count_copy(kvs_pool* p, const kvs::CopyJob& cj) {
+    if (cj.n_pages <= 0) return;
+    p->st.copies_issued++;
+    p->st.pages_streamed += cj.n_pages;
+    p->st.bytes_h2d += (int64_t)cj.n_pages * cj.page_bytes;
+}
+
+// Copy chunk 0 of `layer` into the ring on the pool's copy stream, after the
+// previous ring reader is done.
 int prefetch(kvs_pool* p, int32_t layer) {
     const LayerState& ls = p->layers[layer];
+    hipStream_t cs = p->copy[0];
+    if (p->ring_used) KVS_HIP(hipStreamWaitEvent(cs, p->ring_free, 0));
+    kvs::CopyJob cj = make_copy(p, ls, 0, p->ring_next);
+    hipError_t e = kvs::launch_copy(cj, cs);
+    if (e != hipSuccess) { p->broken = true; return fail(KVS_ERR_HIP, "prefetch copy launch failed: %s", hipGetErrorString(e)); }
+    count_copy(p, cj);
+    p->st.kernels_launched++;
+    KVS_HIP(hipEventRecord(p->pf_done, cs));
     p->pf_layer = layer;
-    p->pf_slot0 = p->ring_next;
-    p->pf_issued = 0;
-    const int32_t n = std::min<int32_t>(p->n_cslots, (int32_t)ls.chunks.size());
-    for (int32_t c = 0; c < n; ++c) {
-        int rc = issue_copy(p, ls, c, (p->pf_slot0 + c) % p->n_cslots);
-        if (rc) { p->broken = true; return rc; }
-        p->pf_issued++;
-    }
     return KVS_OK;
 }
 
-// Run the layer's launch plan: the resident launch, then each ring chunk
-// (wait filled -> kernel -> release slot -> refill the slot with a later chunk).
+// Run the layer's launch plan. Ring chunks are moved by copy workgroups
+// inside the compute launches; kernel boundaries on a stream order each copy
+// before its reader and each reader before its slot is refilled.
+//   Two lanes (ring of an even number >= 4 of chunk slots, one page per
+//   split-K group): the caller's stream computes even chunks and the pool's
+//   lane stream odd chunks; the launch that computes chunk c copies chunk
+//   c + 2, which belongs to the same lane, into a slot last read by that lane.
+//   The lanes' launch boundaries fall at different times, so the host link
+//   stays busy. They meet through one fork and one join event per layer.
+//   One lane (otherwise): the launch that computes chunk c copies chunk c + 1
+//   (ring of >= 2 slots), or copies and computes alternate (one slot).
+// The resident groups are computed by the first launch on the caller's
+// stream, which also copies chunk 0 unless it was prefetched.
 template <typename LaunchFn>
 int run_layer(kvs_pool* p, int32_t layer, hipStream_t stream, LaunchFn launch) {
     LayerState& ls = p->layers[layer];
-    const int32_t n_chunks = (int32_t)ls.chunks.size();
-    if (n_chunks > 0 && p->pf_layer != layer) {
-        int rc = prefetch(p, layer);
-        if (rc) return rc;
-    }
-    int rc = KVS_OK;
+    const int32_t n_ch = (int32_t)ls.chunks.size();
+    const int32_t R = p->n_cslots;
     auto mark = [&](int r) { if (r) p->broken = true; return r; };
-    if (ls.res_nseg > 0) {
-        if ((rc = mark(launch(0, ls.res_nseg, (const uint8_t*)nullptr, 0)))) return rc;
-        p->st.kernels_launched++;
+    int rc = KVS_OK;
+    const int32_t slot0 = p->ring_next;
+    bool prefetched = false;
+    if (n_ch > 0 && p->pf_layer == layer) {
+        if (hipStreamWaitEvent(stream, p->pf_done, 0) != hipSuccess) return mark(fail(KVS_ERR_HIP, "hipStreamWaitEvent(prefetch) failed"));
+        prefetched = true;
+    } else if (n_ch > 0 && p->ring_used) {
+        if (hipStreamWaitEvent(stream, p->ring_free, 0) != hipSuccess) return mark(fail(KVS_ERR_HIP, "hipStreamWaitEvent(ring) failed"));
     }
-    for (int32_t c = 0; c < n_chunks; ++c) {
-        const int32_t cslot = (p->pf_slot0 + c) % p->n_cslots;
-        const ChunkPlan& cp = ls.chunks[c];
-        uint8_t* chunk_base = p->ring + (uint64_t)cslot * p->cfg.chunk_pages * p->L.page_bytes;
-        if (hipStreamWaitEvent(stream, p->filled[cslot], 0) != hipSuccess)
-            return mark(fail(KVS_ERR_HIP, "hipStreamWaitEvent(filled) failed"));
-        if ((rc = mark(launch(cp.seg0, cp.nseg, chunk_base, cp.rank0)))) return rc;
+    p->pf_layer = -1;
+    const bool two = n_ch >= 2 && R >= 4 && (R % 2) == 0 && p->cfg.group_pages == 1;
+    auto slot_of = [&](int32_t c) { return (slot0 + c) % R; };
+    auto do_launch = [&](hipStream_t st, int32_t seg0, int32_t nseg, int32_t c_compute, int32_t c_copy) -> int {
+        kvs::CopyJob cj{};
+        if (c_copy >= 0) cj = make_copy(p, ls, c_copy, slot_of(c_copy));
+        const uint8_t* ring_chunk = c_compute >= 0 ? p->ring + (uint64_t)slot_of(c_compute) * p->cfg.chunk_pages * p->L.page_bytes : nullptr;
+        const int32_t rank0 = c_compute >= 0 ? ls.chunks[c_compute].rank0 : 0;
+        int r = launch(st, seg0, nseg, ring_chunk, rank0, cj);
+        if (r) return mark(r);
+        count_copy(p, cj);
         p->st.kernels_launched++;
-        if (p->cfg.flags & KVS_FLAG_POISON_RING) {
-            hipError_t e = kvs::launch_fill_u32(chunk_base, 0xA5A5A5A5u, (uint64_t)cp.npages * p->L.page_bytes / 4, stream);
+        if (c_compute >= 0 && (p->cfg.flags & KVS_FLAG_POISON_RING)) {
+            hipError_t e = kvs::launch_fill_u32(const_cast<uint8_t*>(ring_chunk), 0xA5A5A5A5u,
+                                                (uint64_t)ls.chunks[c_compute].npages * p->L.page_bytes / 4, st);
             if (e != hipSuccess) return mark(fail(KVS_ERR_HIP, "ring poison fill failed: %s", hipGetErrorString(e)));
         }
-        if (hipEventRecord(p->freed[cslot], stream) != hipSuccess)
-            return mark(fail(KVS_ERR_HIP, "hipEventRecord(freed) failed"));
-        if (c + p->n_cslots < n_chunks) {
-            if ((rc = issue_copy(p, ls, c + p->n_cslots, cslot))) return mark(rc);
-            p->pf_issued++;
+        return KVS_OK;
+    };
+    const int32_t c0 = (n_ch > 0 && !prefetched) ? 0 : -1;
+    if (ls.res_nseg > 0 || c0 >= 0) {
+        if ((rc = do_launch(stream, 0, ls.res_nseg, -1, c0))) return rc;
+    }
+    if (two) {
+        hipStream_t ln = p->lane;
+        if (hipEventRecord(p->fork_ev, stream) != hipSuccess || hipStreamWaitEvent(ln, p->fork_ev, 0) != hipSuccess)
+            return mark(fail(KVS_ERR_HIP, "lane fork failed"));
+        if ((rc = do_launch(ln, 0, 0, -1, 1))) return rc;   // lane 1 starts by copying chunk 1
+        for (int32_t c = 0; c < n_ch; ++c) {
+            const ChunkPlan& cp = ls.chunks[c];
+            const int32_t cc = (c + 2 < n_ch) ? c + 2 : -1;
+            if ((rc = do_launch((c & 1) ? ln : stream, cp.seg0, cp.nseg, c, cc))) return rc;
+        }
+        if (hipEventRecord(p->join_ev, ln) != hipSuccess || hipStreamWaitEvent(stream, p->join_ev, 0) != hipSuccess)
+            return mark(fail(KVS_ERR_HIP, "lane join failed"));
+    } else {
+        for (int32_t c = 0; c < n_ch; ++c) {
+            const ChunkPlan& cp = ls.chunks[c];
+            if (R >= 2) {
+                const int32_t cc = (c + 1 < n_ch) ? c + 1 : -1;
+                if ((rc = do_launch(stream, cp.seg0, cp.nseg, c, cc))) return rc;
+            } else {
+                if ((rc = do_launch(stream, cp.seg0, cp.nseg, c, -1))) return rc;
+                if (c + 1 < n_ch && (rc = do_launch(stream, 0, 0, -1, c + 1))) return rc;
+            }
         }
     }
-    if (n_chunks > 0) {
-        p->ring_next = (p->pf_slot0 + n_chunks) % p->n_cslots;
-        p->pf_layer = -1;
-        p->pf_issued = 0;
+    if (n_ch > 0) {
+        p->ring_next = slot_of(n_ch);
+        if (hipEventRecord(p->ring_free, stream) != hipSuccess) return mark(fail(KVS_ERR_HIP, "hipEventRecord(ring) failed"));
+        p->ring_used = true;
     }
     return KVS_OK;
 }
@@ -331,6 +380,20 @@ int check_layer_ready(const kvs_pool* p, int32_t layer) {
     const LayerState& ls = p->layers[layer];
     if (!ls.host) return fail(KVS_ERR_NOT_READY, "layer %d has no host pages (call kvs_host_pages_set)", layer);
     if (ls.n_pages < 0) return fail(KVS_ERR_NOT_READY, "layer %d has no page table (call kvs_page_table_set)", layer);
+    return KVS_OK;
+}
+
+// Ring chunks are ordered by events across the pool's copy streams; a graph
+// captured from the compute stream cannot replay that exchange faithfully.
+int check_capture(const kvs_pool* p, int32_t layer, hipStream_t s) {
+    if (p->layers[layer].chunks.empty()) return KVS_OK;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        return KVS_OK;
+    }
+    if (cs != hipStreamCaptureStatusNone)
+        return fail(KVS_ERR_UNSUPPORTED, "layer %d streams pages through the ring, which cannot be captured in a graph", layer);
     return KVS_OK;
 }
 
@@ -402,9 +465,8 @@ int kvs_pool_create(const kvs_config* cfg, void* dev_arena, uint64_t budget_byte
     p->n_cslots = cfg->ring_pages / cfg->chunk_pages;
     auto cleanup = [&](const char* what, hipError_t e) {
         for (auto s : p->copy) (void)hipStreamDestroy(s);
-        for (auto e2 : p->filled) (void)hipEventDestroy(e2);
-        for (auto e2 : p->freed) (void)hipEventDestroy(e2);
-        if (p->last_work) (void)hipEventDestroy(p->last_work);
+        if (p->lane) (void)hipStreamDestroy(p->lane);
+        for (hipEvent_t ev : {p->pf_done, p->ring_free, p->last_work, p->fork_ev, p->join_ev}) if (ev) (void)hipEventDestroy(ev);
         delete p;
         return fail(KVS_ERR_HIP, "%s failed: %s", what, hipGetErrorString(e));
     };
@@ -414,17 +476,14 @@ int kvs_pool_create(const kvs_config* cfg, void* dev_arena, uint64_t budget_byte
         if (e != hipSuccess) return cleanup("hipStreamCreateWithFlags", e);
         p->copy.push_back(s);
     }
-    for (int i = 0; i < p->n_cslots; ++i) {
-        hipEvent_t a, b;
-        hipError_t e = hipEventCreateWithFlags(&a, hipEventDisableTiming);
+    for (hipEvent_t* ev : {&p->pf_done, &p->ring_free, &p->last_work, &p->fork_ev, &p->join_ev}) {
+        hipError_t e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
         if (e != hipSuccess) return cleanup("hipEventCreateWithFlags", e);
-        p->filled.push_back(a);
-        e = hipEventCreateWithFlags(&b, hipEventDisableTiming);
-        if (e != hipSuccess) return cleanup("hipEventCreateWithFlags", e);
-        p->freed.push_back(b);
     }
-    hipError_t e = hipEventCreateWithFlags(&p->last_work, hipEventDisableTiming);
-    if (e != hipSuccess) return cleanup("hipEventCreateWithFlags", e);
+    {
+        hipError_t e = hipStreamCreateWithFlags(&p->lane, hipStreamNonBlocking);
+        if (e != hipSuccess) return cleanup("hipStreamCreateWithFlags", e);
+    }
     p->st.page_bytes = (int64_t)L.page_bytes;
     p->st.slot_count = p->n_slots;
     p->st.ring_pages = cfg->ring_pages;
@@ -441,10 +500,10 @@ void kvs_pool_destroy(kvs_pool* p) {
     if (!p) return;
     for (auto s : p->copy) (void)hipStreamSynchronize(s);
     if (p->last_work) (void)hipEventSynchronize(p->last_work);
+    if (p->lane) (void)hipStreamSynchronize(p->lane);
     for (auto s : p->copy) (void)hipStreamDestroy(s);
-    for (auto e : p->filled) (void)hipEventDestroy(e);
-    for (auto e : p->freed) (void)hipEventDestroy(e);
-    if (p->last_work) (void)hipEventDestroy(p->last_work);
+    if (p->lane) (void)hipStreamDestroy(p->lane);
+    for (hipEvent_t ev : {p->pf_done, p->ring_free, p->last_work, p->fork_ev, p->join_ev}) if (ev) (void)hipEventDestroy(ev);
     for (auto& v : p->prof_ev)
         for (auto& pr : v) { (void)hipEventDestroy(pr.first); (void)hipEventDestroy(pr.second); }
     delete p;
@@ -546,6 +605,7 @@ int kvs_attend(kvs_pool* p, int32_t layer, const void* q, int32_t q_dtype, int32
                     (long long)q_pos0, (long long)(q_pos0 + n_q), (long long)n_kv);
     if ((rc = check_ring_free_for(p, layer))) return rc;
     hipStream_t s = (hipStream_t)stream;
+    if ((rc = check_capture(p, layer, s))) return rc;
 
     kvs::AttendArgs a{};
     a.ps.slots = p->slots;
@@ -562,13 +622,15 @@ int kvs_attend(kvs_pool* p, int32_t layer, const void* q, int32_t q_dtype, int32
     a.scale_log2 = scale * 1.44269504088896340736f;
     a.causal = causal ? 1 : 0;
     a.part = p->work;
-    rc = run_layer(p, layer, s, [&](int32_t seg0, int32_t nseg, const uint8_t* ring_chunk, int32_t rank0) -> int {
+    rc = run_layer(p, layer, s, [&](hipStream_t st, int32_t seg0, int32_t nseg, const uint8_t* ring_chunk, int32_t rank0,
+                                    const kvs::CopyJob& cj) -> int {
         kvs::AttendArgs b = a;
+        b.copy = cj;
         b.ps.ring_chunk = ring_chunk;
         b.ps.chunk_rank0 = rank0;
         b.segs = ls.dev_segs + seg0;
         b.n_segs = nseg;
-        hipError_t e = timed(p, 0, s, [&] { return kvs::launch_attend(b, s); });
+        hipError_t e = timed(p, 0, st, [&] { return kvs::launch_attend(b, st); });
         return e == hipSuccess ? KVS_OK : fail(KVS_ERR_HIP, "attention kernel launch failed: %s", hipGetErrorString(e));
     });
     if (rc) return rc;
@@ -596,6 +658,7 @@ int kvs_debug_gather(kvs_pool* p, int32_t layer, int64_t tok0, int64_t n_tok, fl
     if (n_tok > 0 && (!k_out || !v_out)) return fail(KVS_ERR_INVALID_ARG, "k_out or v_out is NULL");
     if ((rc = check_ring_free_for(p, layer))) return rc;
     hipStream_t s = (hipStream_t)stream;
+    if ((rc = check_capture(p, layer, s))) return rc;
     kvs::GatherArgs a{};
     a.ps.slots = p->slots;
     a.ps.src = ls.dev_src;
@@ -605,13 +668,15 @@ int kvs_debug_gather(kvs_pool* p, int32_t layer, int64_t tok0, int64_t n_tok, fl
     a.n_tok = n_tok;
     a.k_out = k_out;
     a.v_out = v_out;
-    rc = run_layer(p, layer, s, [&](int32_t seg0, int32_t nseg, const uint8_t* ring_chunk, int32_t rank0) -> int {
+    rc = run_layer(p, layer, s, [&](hipStream_t st, int32_t seg0, int32_t nseg, const uint8_t* ring_chunk, int32_t rank0,
+                                    const kvs::CopyJob& cj) -> int {
         kvs::GatherArgs b = a;
+        b.copy = cj;
         b.ps.ring_chunk = ring_chunk;
         b.ps.chunk_rank0 = rank0;
         b.segs = ls.dev_segs + seg0;
         b.n_segs = nseg;
-        hipError_t e = kvs::launch_gather(b, s);
+        hipError_t e = kvs::launch_gather(b, st);
         return e == hipSuccess ? KVS_OK : fail(KVS_ERR_HIP, "gather kernel launch failed: %s", hipGetErrorString(e));
     });
     if (rc) return rc;

@@ -95,9 +95,10 @@ typedef struct kvs_config {
     int32_t max_q_tokens;  /* widest query block kvs_attend admits: 1 for decode,
                               1 + n_draft for a speculative verify, the ubatch for prefill */
     int32_t ring_pages;    /* device ring capacity in pages (>= 1)                        */
-    int32_t chunk_pages;   /* pages per ring chunk: one copy batch and one kernel launch;
-                              must divide ring_pages                                      */
-    int32_t copy_streams;  /* copy streams the chunks round-robin over (1..8)              */
+    int32_t chunk_pages;   /* pages per ring chunk (1..16), a divisor of ring_pages: one
+                              launch computes a chunk while its copy workgroups pull the
+                              next chunk from host memory into the next chunk slot       */
+    int32_t copy_streams;  /* streams the pool creates for kvs_stream_enqueue (1..8)       */
     int32_t group_pages;   /* pages per split-K partial (>= 1). Partials are keyed by this
                               logical grouping only, so results do not depend on which
                               pages are resident, nor on ring or chunk sizes.              */
@@ -167,12 +168,12 @@ int kvs_host_pages_set(kvs_pool* pool, int32_t layer, const void* pinned_records
 int kvs_page_table_set(kvs_pool* pool, int32_t layer, int32_t n_pages,
                        const uint8_t* resident, void* stream);
 
-/* Start copying the first ring chunks of `layer` (as many as the ring holds)
- * on the pool's copy streams, so they overlap whatever the caller runs before
- * kvs_attend(layer). The ring serves one layer at a time, in call order:
- * KVS_ERR_STATE if another layer's prefetch has not been consumed yet. A layer
- * with no streamed pages is a no-op. kvs_attend prefetches by itself when the
- * caller did not. */
+/* Start copying the first ring chunk of `layer` on the pool's copy stream
+ * (after the previous ring reader finished), so it overlaps whatever the
+ * caller runs before kvs_attend(layer). The ring serves one layer at a time,
+ * in call order: KVS_ERR_STATE if another layer's prefetch has not been
+ * consumed yet. A layer with no streamed pages is a no-op. Without a prefetch,
+ * kvs_attend copies the first chunk itself. */
 int kvs_stream_enqueue(kvs_pool* pool, int32_t layer);
 
 /* Attention of n_q query tokens against the layer's cache of n_kv tokens.
@@ -184,10 +185,17 @@ int kvs_stream_enqueue(kvs_pool* pool, int32_t layer);
  *   are required). n_kv must satisfy ceil(n_kv / 256) == the layer's n_pages.
  *   Scores are scale * q.k. A row without any allowed key gets out = 0 and
  *   lse = -inf.
- * Enqueues on `stream`: the resident-group kernel, then for each ring chunk a
- * wait for its copy, the chunk kernel and a slot release, then the split-K
- * combine. Returns without waiting. KVS_ERR_BATCH_TOO_WIDE if n_q exceeds
- * max_q_tokens (the pages' "decode batch too wide"). */
+ * Enqueues on `stream`: the resident-group launch, then one launch per ring
+ * chunk, then the split-K combine. Each launch computes on the chunk that the
+ * previous launch copied into the ring, while its own copy workgroups read the
+ * next chunk's pages from pinned host memory over the host link into the next
+ * ring slot; kernel boundaries on the one stream order each copy before its
+ * reader and each reader before the slot is refilled. Returns without waiting. KVS_ERR_BATCH_TOO_WIDE if n_q exceeds
+ * max_q_tokens (the pages' "decode batch too wide").
+ * A layer whose pages are all resident may be captured into a HIP graph
+ * (stream capture on `stream`) and replayed; a layer with streamed pages
+ * returns KVS_ERR_UNSUPPORTED under capture, because its ring chunks are
+ * ordered by events on the pool's own copy streams. */
 int kvs_attend(kvs_pool* pool, int32_t layer, const void* q, int32_t q_dtype, int32_t n_q,
                int64_t q_pos0, int64_t n_kv, float scale, int32_t causal, float* out,
                float* lse, void* stream);

@@ -122,6 +122,9 @@ def test_outputs_bit_identical_across_residency_ring_and_chunks():
         dict(resident=mask_none, ring=6, chunk=3, streams=3),
         dict(resident=mask_random(0.5), ring=4, chunk=4, streams=1),
         dict(resident=mask_random(0.3, seed=5), ring=2, chunk=1, streams=2, flags=kvs.FLAG_POISON_RING),
+        # four or more chunk slots: two compute lanes when groups are single pages
+        dict(resident=mask_none, ring=4, chunk=1, streams=1),
+        dict(resident=mask_random(0.5, seed=6), ring=8, chunk=2, streams=2, flags=kvs.FLAG_POISON_RING),
     ]
     for group in (1, 3):
         base = None
@@ -198,5 +201,55 @@ def test_tiny_decode_workload():
         qs = [c.queries(0, 1, wl.q_dtype)]
         outs, lses = c.attend_all(qs, q_pos0=wl.q_pos0, scale=wl.scale, causal=wl.causal)
         check(c, outs, lses, qs, q_pos0=wl.q_pos0, scale=wl.scale, causal=wl.causal)
+    finally:
+        c.close()
+
+
+def test_graph_replay_matches_eager():
+    """A resident-only step captured in a HIP graph and replayed several
+    times, with eager work and synchronizations between replays, gives the
+    eager result bit for bit each time; streamed layers refuse capture."""
+    c = small_case(mask_all, n_layers=3)
+    try:
+        dq = [torch.from_numpy(c.queries(l, 1, "f32")).cuda() for l in range(c.L)]
+        eager = [torch.empty_like(q) for q in dq]
+        for l in range(c.L):
+            c.pool.attend(l, dq[l], N_KV, N_KV - 1, 1.0, False, eager[l])
+        torch.cuda.synchronize()
+        outs = [torch.empty_like(q) for q in dq]
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for l in range(c.L):
+                c.pool.attend(l, dq[l], N_KV, N_KV - 1, 1.0, False, outs[l], stream=s)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for l in range(c.L):
+                c.pool.attend(l, dq[l], N_KV, N_KV - 1, 1.0, False, outs[l], stream=s)
+        scratch = torch.empty_like(dq[0])
+        for rep in range(4):
+            for o in outs:
+                o.fill_(float("nan"))
+            c.pool.attend(rep % c.L, dq[0], N_KV, N_KV - 1, 1.0, False, scratch)   # eager work between replays
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for l in range(c.L):
+                assert torch.equal(outs[l], eager[l]), (rep, l)
+        del g
+    finally:
+        c.close()
+    c = small_case(mask_none, n_layers=1)
+    try:
+        q = torch.from_numpy(c.queries(0, 1, "f32")).cuda()
+        out = torch.empty_like(q)
+        s = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with pytest.raises(kvs.KvsError) as e:
+            with torch.cuda.graph(g, stream=s):
+                c.pool.attend(0, q, N_KV, N_KV - 1, 1.0, False, out, stream=s)
+        assert e.value.code == kvs.ERR_UNSUPPORTED
     finally:
         c.close()
