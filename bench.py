@@ -163,9 +163,11 @@ def streamed_run(wl, st, steps, warmup):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("kvs_kernels.hip", "kvs_internal.h"):
-        with open(os.path.join(ROOT, "host_streamed_paged_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    csrc = os.path.join(ROOT, "host_streamed_paged_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(fh.read())
     return h.hexdigest()[:16]
 
 

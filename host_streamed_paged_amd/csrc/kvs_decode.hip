@@ -27,6 +27,7 @@
 #include <cmath>
 
 #include "kvs_internal.h"
+#include "kvs_device.h"
 
 namespace kvs {
 namespace {
@@ -78,34 +79,11 @@ __device__ inline float sum_over_tokens(float v) {
     return v;
 }
 
-// A 32-bit constant held in a VGPR the compiler cannot see through, so
-// three-operand VALU ops (v_and_or_b32) can take it: gfx9 VOP3 encodings have
-// no literal field and read at most one scalar operand.
-__device__ inline uint32_t vconst(uint32_t c) {
-    uint32_t r;
-    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
-    return r;
-}
-
 // a . b over 4 signed bytes, starting from 0
 __device__ inline int sdot4_first(uint32_t a, uint32_t b) {
     int r;
     asm("v_dot4_i32_i8 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
     return r;
-}
-
-// Workgroup barrier that orders LDS only: unlike __syncthreads() it does not
-// wait for outstanding global loads, so page data stays in flight across it.
-__device__ inline void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// Uniform loads through the scalar cache (constant address space).
-template <typename T>
-__device__ inline T scalar_load(const T* p) {
-    return *(const __attribute__((address_space(4))) T*)p;
 }
 
 __device__ inline void wave_lds_sync() {

@@ -1,0 +1,49 @@
+// Small device helpers shared by the attention kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "kvs_internal.h"
+
+namespace kvs {
+
+// Workgroup barrier that orders LDS only: unlike __syncthreads() it does not
+// wait for outstanding global loads, so page data stays in flight across it.
+__device__ inline void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Uniform loads through the scalar cache (constant address space).
+template <typename T>
+__device__ inline T scalar_load(const T* p) {
+    return *(const __attribute__((address_space(4))) T*)p;
+}
+
+// A 32-bit constant held in a VGPR the compiler cannot see through, so
+// three-operand VALU ops (v_and_or_b32) can take it: gfx9 VOP3 encodings have
+// no literal field and read at most one scalar operand.
+__device__ inline uint32_t vconst(uint32_t c) {
+    uint32_t r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
+    return r;
+}
+
+// LDS DMA: each lane of the wave copies 16 bytes from global memory to
+// lds_base + 16 * lane (lds_base must be the same for the whole wave).
+__device__ inline void dma16(const void* gsrc, void* lds_base) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
+                                     (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+// Page record of logical page `page` for this launch: a resident slot, or a
+// slot of the ring chunk the launch works on.
+__device__ inline const uint8_t* page_record(const PageSource& ps, int32_t page) {
+    const int32_t sv = scalar_load(ps.src + page);
+    return sv >= 0 ? ps.slots + (int64_t)sv * ps.page_bytes
+                   : ps.ring_chunk + (int64_t)((-1 - sv) - ps.chunk_rank0) * ps.page_bytes;
+}
+
+}  // namespace kvs

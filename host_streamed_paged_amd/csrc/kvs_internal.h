@@ -125,6 +125,8 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t stream);
 // few-row VALU decode kernel (kvs_decode.hip): rows = n_q * G in [1, 6]
 bool decode_supports(int rows);
 hipError_t launch_decode(const AttendArgs& a, hipStream_t stream);
+// matrix-core kernel (kvs_mfma.hip) for more rows
+hipError_t launch_mfma(const AttendArgs& a, hipStream_t stream);
 hipError_t launch_combine(const float* part, int32_t n_groups, int32_t n_q, int32_t n_q_heads,
                           float* out, float* lse, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);

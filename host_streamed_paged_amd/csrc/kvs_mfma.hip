@@ -1,0 +1,357 @@
+// Matrix-core attention kernel for query blocks with more than a few rows:
+// a speculative verify batch of 1 + draft tokens (page 2, "Phase arena:
+// speculative verify batches") and a prefill ubatch (256 tokens in page 2's
+// "TLDR - recommended setup"), on CDNA4 v_mfma_f32_16x16x32_f16.
+//
+// One workgroup = one segment (run of pages of one split-K group) x one kv
+// head x a tile of 16 RT query rows (row = query token x head of the GQA
+// group). 4 waves. Every page is staged whole in LDS by LDS DMA (K tile
+// 34816 B, V tile 18432 B, record layout), then:
+//   QK   wave w owns tokens [64 w, 64 w + 64) of the page:
+//        S^T (16 tokens x 16 rows) = K_blk (16 x 32) . Q_blk^T (32 x 16),
+//        four 32-wide quant blocks per tile. The K operand is built by the
+//        lane itself from its 8 int8 codes: exact f16 code, times the block
+//        scale d rounded once to f16. The query operand holds
+//        q * scale * log2(e) in f16 (scores in log2 units).
+//   softmax  page maxima per row across the 4 waves through LDS; the running
+//        max m, p = exp2(s - m). Each lane's scores sit exactly where the P.V
+//        product wants its P operand, so P never leaves registers on the
+//        producing wave; it is published to LDS for the channel owners.
+//   PV   wave w owns channels [32 w, 32 w + 32) (= V quant block w):
+//        O^T (16 channels x 16 rows) += V^T (16 x 32 tokens) . P^T (32 x 16).
+//        The V operand is gathered from the V tile: one nibble byte and the
+//        block scale per token, d * (u - 8) rounded once to f16.
+// The running state (m, l, O) is updated once per page in page order from
+// state and page data alone, so results do not depend on how pages are split
+// into launches or which pages are resident.
+#include <hip/hip_runtime.h>
+#include <cstdint>
+#include <cmath>
+
+#include "kvs_internal.h"
+#include "kvs_device.h"
+
+namespace kvs {
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTokW = kPageTokens / kWaves;   // tokens per wave in QK (64)
+constexpr int kChunks = kPageTokens / 32;     // 32-token MFMA chunks per page in PV
+
+template <int RT>
+struct MfmaSmem {
+    // K tile in record layout; once every wave is past QK it holds the P
+    // operands [chunk][row tile][lane] (16 bytes each)
+    alignas(16) uint8_t k[kKTile];
+    alignas(16) uint8_t v[kVTile];
+    float red_m[kWaves][16 * RT];
+    float red_l[kWaves][16 * RT];
+};
+
+__device__ inline half2_t as_h2(uint32_t x) { return __builtin_bit_cast(half2_t, x); }
+__device__ inline uint32_t as_u(half2_t x) { return __builtin_bit_cast(uint32_t, x); }
+
+// two workgroups per CU up to 3 row tiles; 4 row tiles need the whole
+// register file of a SIMD lane (256 arch + acc registers would spill)
+template <int RT>
+__global__ __launch_bounds__(kThreads, RT <= 3 ? 2 : 1) void mfma_kernel(AttendArgs a) {
+    static_assert(kChunks * RT * 64 * 16 <= kKTile, "P operands must fit in the K tile");
+    __shared__ MfmaSmem<RT> sm;
+    if ((int)blockIdx.x >= a.n_segs) {   // ring refill workgroup
+        if (blockIdx.z == 0) copy_role(a.copy, ((int)blockIdx.x - a.n_segs) * (int)gridDim.y + (int)blockIdx.y);
+        return;
+    }
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int n = lane & 15, gq = lane >> 4;   // MFMA row/column index and lane group
+    typedef int int4v __attribute__((ext_vector_type(4)));
+    const int4v segv = scalar_load((const int4v*)(a.segs + blockIdx.x));
+    const Seg seg = {segv.x, segv.y, segv.z, segv.w};
+    const int g = blockIdx.y;
+    const int G = a.G, R = a.n_q * G;
+    const int r0 = blockIdx.z * 16 * RT;
+
+    auto issue_page = [&](int page) {
+        const uint8_t* rec = page_record(a.ps, page);
+        const uint8_t* kt = rec + (int64_t)g * kKTile;
+        const uint8_t* vt = rec + (int64_t)a.n_kv_heads * kKTile + (int64_t)g * kVTile;
+        // wave-sized pieces of 1 KB: 34 for K, 18 for V
+#pragma unroll
+        for (int k = 0; k < 9; ++k) {
+            const int piece = w + 4 * k;
+            if (piece < kKTile / 1024) dma16(kt + piece * 1024 + lane * 16, sm.k + piece * 1024);
+        }
+#pragma unroll
+        for (int k = 0; k < 5; ++k) {
+            const int piece = w + 4 * k;
+            if (piece < kVTile / 1024) dma16(vt + piece * 1024 + lane * 16, sm.v + piece * 1024);
+        }
+    };
+    issue_page(seg.page0);
+
+    // ---- this lane's query rows (one per row tile) and their visible prefix
+    half8_t qop[RT][kNB];
+    int64_t lim[RT];
+    int qi_[RT], h_[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int r = r0 + 16 * rt + n;
+        qi_[rt] = r / G;
+        h_[rt] = g * G + r % G;
+        if (r < R) {
+            lim[rt] = a.n_kv;
+            if (a.causal) {
+                const int64_t c = a.q_pos0 + qi_[rt] + 1;
+                lim[rt] = c < lim[rt] ? c : lim[rt];
+            }
+            const int64_t off = ((int64_t)qi_[rt] * a.n_q_heads + h_[rt]) * kHeadDim + 8 * gq;
+#pragma unroll
+            for (int b = 0; b < kNB; ++b) {
+                float x[8];
+                if (a.q_f16) {
+                    const u32x4 raw = *(const u32x4*)((const _Float16*)a.q + off + kQK * b);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const half2_t hv = as_h2(raw[e]);
+                        x[2 * e] = (float)hv[0];
+                        x[2 * e + 1] = (float)hv[1];
+                    }
+                } else {
+                    const f32x4* qp = (const f32x4*)((const float*)a.q + off + kQK * b);
+                    const f32x4 u0 = qp[0], u1 = qp[1];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) { x[e] = u0[e]; x[4 + e] = u1[e]; }
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qop[rt][b][e] = (_Float16)(x[e] * a.scale_log2);
+            }
+        } else {
+            lim[rt] = 0;
+#pragma unroll
+            for (int b = 0; b < kNB; ++b)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qop[rt][b][e] = (_Float16)0.f;
+        }
+    }
+
+    // ---- running state: O^T tiles [ct][rt] hold channels 32 w + 16 ct + 4 gq + i
+    // of row 16 rt + n; m and l are replicated over the lanes of a row
+    f32x4 o[2][RT];
+    float m_run[RT], l_run[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        m_run[rt] = -INFINITY;
+        l_run[rt] = 0.f;
+        o[0][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        o[1][rt] = o[0][rt];
+        if (!(seg.flags & kSegFresh) && r0 + 16 * rt + n < R) {
+            const float* pr = a.part + (((int64_t)seg.group * a.n_q + qi_[rt]) * a.n_q_heads + h_[rt]) * kPartStride;
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[ct][rt][i] = pr[32 * w + 16 * ct + 4 * gq + i];
+            m_run[rt] = pr[kHeadDim];
+            l_run[rt] = pr[kHeadDim + 1];
+        }
+    }
+
+    const uint32_t c_hi64 = 0x64646464u;
+    const half2_t k_off = {(_Float16)1152.f, (_Float16)1152.f};   // 1024 + 128
+    const half2_t v_off = {(_Float16)1032.f, (_Float16)1032.f};   // 1024 + 8
+    const uint32_t m_nib = vconst(0x000F000Fu), magic = vconst(0x64006400u);
+
+    for (int pi = 0; pi < seg.npages; ++pi) {
+        const int page = seg.page0 + pi;
+        const int64_t base_tok = (int64_t)page * kPageTokens;
+        int limrel[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int64_t x = lim[rt] - base_tok;
+            limrel[rt] = (int)(x < 0 ? 0 : (x > kPageTokens ? kPageTokens : x));
+        }
+        const int64_t vx = a.n_kv - base_tok;
+        const int valid = (int)(vx < 0 ? 0 : (vx > kPageTokens ? kPageTokens : vx));   // cached rows of the page
+
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_barrier();   // the page's tiles are in LDS for every wave
+
+        // ---- QK over this wave's 64 tokens
+        f32x4 s[4][RT];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) s[tt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const uint8_t* krow = sm.k + (kTokW * w + 16 * tt + n) * kKRow;
+#pragma unroll
+            for (int b = 0; b < kNB; ++b) {
+                const uint8_t* blk = krow + b * kKBlock;
+                uint32_t x0, x1;
+                if (b & 1) {   // codes start on a dword boundary
+                    const uint32_t* p = (const uint32_t*)(blk + 2 + 8 * gq);
+                    x0 = p[0];
+                    x1 = p[1];
+                } else {       // codes start 2 bytes into a dword
+                    const uint32_t* p = (const uint32_t*)(blk + 8 * gq);
+                    const uint32_t y0 = p[0], y1 = p[1], y2 = p[2];
+                    x0 = __builtin_amdgcn_alignbyte(y1, y0, 2);
+                    x1 = __builtin_amdgcn_alignbyte(y2, y1, 2);
+                }
+                const uint32_t db = *(const uint16_t*)blk;
+                const half2_t d2 = as_h2(db | (db << 16));
+                // int8 code k -> f16 (1024 + (k + 128)) - 1152, exact; then * d
+                x0 ^= 0x80808080u;
+                x1 ^= 0x80808080u;
+                half8_t kop;
+                const half2_t e0 = (as_h2(__builtin_amdgcn_perm(c_hi64, x0, 0x04010400u)) - k_off) * d2;
+                const half2_t e1 = (as_h2(__builtin_amdgcn_perm(c_hi64, x0, 0x04030402u)) - k_off) * d2;
+                const half2_t e2 = (as_h2(__builtin_amdgcn_perm(c_hi64, x1, 0x04010400u)) - k_off) * d2;
+                const half2_t e3 = (as_h2(__builtin_amdgcn_perm(c_hi64, x1, 0x04030402u)) - k_off) * d2;
+                kop[0] = e0[0]; kop[1] = e0[1]; kop[2] = e1[0]; kop[3] = e1[1];
+                kop[4] = e2[0]; kop[5] = e2[1]; kop[6] = e3[0]; kop[7] = e3[1];
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    s[tt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[rt][b], s[tt][rt], 0, 0, 0);
+            }
+        }
+
+        // ---- mask, page maxima (lane value i is token 64 w + 16 tt + 4 gq + i)
+        float mx[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            mx[rt] = -INFINITY;
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tok = kTokW * w + 16 * tt + 4 * gq + i;
+                    const float v = tok < limrel[rt] ? s[tt][rt][i] : -INFINITY;
+                    s[tt][rt][i] = v;
+                    mx[rt] = fmaxf(mx[rt], v);
+                }
+            mx[rt] = fmaxf(mx[rt], __shfl_xor(mx[rt], 16, 64));
+            mx[rt] = fmaxf(mx[rt], __shfl_xor(mx[rt], 32, 64));
+            if (gq == 0) sm.red_m[w][16 * rt + n] = mx[rt];
+        }
+        lds_barrier();   // maxima published; every wave is done reading the K tile
+
+        float m_use[RT], alpha[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            float pm = sm.red_m[0][16 * rt + n];
+#pragma unroll
+            for (int ww = 1; ww < kWaves; ++ww) pm = fmaxf(pm, sm.red_m[ww][16 * rt + n]);
+            const float m_new = fmaxf(m_run[rt], pm);
+            m_use[rt] = m_new == -INFINITY ? 0.f : m_new;
+            alpha[rt] = exp2f(m_run[rt] - m_use[rt]);   // 0 while the state is empty
+            m_run[rt] = m_new;
+        }
+        // ---- probabilities -> P operands in LDS (slot 8 gq + j of chunk c is
+        // token 32 c + 4 gq + j for j < 4, 32 c + 12 + 4 gq + j otherwise)
+        uint8_t* pbuf = sm.k;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            float ls = 0.f;
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+                half8_t pv;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float p = exp2f(s[2 * c2 + (j >> 2)][rt][j & 3] - m_use[rt]);
+                    ls += p;
+                    pv[j] = (_Float16)p;
+                }
+                *(half8_t*)(pbuf + (((2 * w + c2) * RT + rt) * 64 + lane) * 16) = pv;
+            }
+            ls += __shfl_xor(ls, 16, 64);
+            ls += __shfl_xor(ls, 32, 64);
+            if (gq == 0) sm.red_l[w][16 * rt + n] = ls;
+        }
+        lds_barrier();   // P operands and row sums published
+
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            float lp = sm.red_l[0][16 * rt + n];
+#pragma unroll
+            for (int ww = 1; ww < kWaves; ++ww) lp += sm.red_l[ww][16 * rt + n];
+            l_run[rt] = l_run[rt] * alpha[rt] + lp;
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) o[ct][rt] *= alpha[rt];
+        }
+
+        // ---- P.V for channels 32 w .. 32 w + 31 (V quant block w)
+        const uint8_t* vcol = sm.v + w * kVBlock;
+#pragma unroll 2
+        for (int c = 0; c < kChunks; ++c) {
+            half8_t vop[2];
+#pragma unroll
+            for (int jp = 0; jp < 4; ++jp) {
+                const int j0 = 2 * jp, j1 = 2 * jp + 1;
+                const int t0 = 32 * c + (j0 < 4 ? 4 * gq + j0 : 12 + 4 * gq + j0);
+                const int t1 = 32 * c + (j1 < 4 ? 4 * gq + j1 : 12 + 4 * gq + j1);
+                const uint8_t* r0p = vcol + t0 * kVRow;
+                const uint8_t* r1p = vcol + t1 * kVRow;
+                uint32_t d0 = *(const uint16_t*)r0p, d1 = *(const uint16_t*)r1p;
+                d0 = t0 < valid ? d0 : 0u;   // rows past the cache may hold NaN scales
+                d1 = t1 < valid ? d1 : 0u;
+                const half2_t dd = as_h2(d0 | (d1 << 16));
+                const uint32_t x = __builtin_amdgcn_perm((uint32_t)r1p[2 + n], (uint32_t)r0p[2 + n], 0x0c040c00u);
+                const half2_t lo = (as_h2((x & m_nib) | magic) - v_off) * dd;          // channel n
+                const half2_t hi = (as_h2(((x >> 4) & m_nib) | magic) - v_off) * dd;   // channel 16 + n
+                vop[0][j0] = lo[0]; vop[0][j1] = lo[1];
+                vop[1][j0] = hi[0]; vop[1][j1] = hi[1];
+            }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const half8_t pop = *(const half8_t*)(pbuf + ((c * RT + rt) * 64 + lane) * 16);
+                o[0][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[0], pop, o[0][rt], 0, 0, 0);
+                o[1][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[1], pop, o[1][rt], 0, 0, 0);
+            }
+        }
+        lds_barrier();   // every wave is done with this page's tiles
+        if (pi + 1 < seg.npages) issue_page(page + 1);
+    }
+
+    // ---- group state -> partial records
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        if (r0 + 16 * rt + n >= R) continue;
+        float* pr = a.part + (((int64_t)seg.group * a.n_q + qi_[rt]) * a.n_q_heads + h_[rt]) * kPartStride;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            float2* dst = (float2*)(pr + 32 * w + 16 * ct + 4 * gq);
+            dst[0] = make_float2(o[ct][rt][0], o[ct][rt][1]);
+            dst[1] = make_float2(o[ct][rt][2], o[ct][rt][3]);
+        }
+        if (w == 0 && gq == 0) {
+            pr[kHeadDim] = m_run[rt];
+            pr[kHeadDim + 1] = l_run[rt];
+        }
+    }
+}
+
+template <int RT>
+hipError_t launch_rt(const AttendArgs& a, hipStream_t stream) {
+    const int R = a.n_q * a.G;
+    const int cx = (copy_workgroups(a.copy) + a.n_kv_heads - 1) / a.n_kv_heads;
+    const dim3 grid(a.n_segs + cx, a.n_kv_heads, (R + 16 * RT - 1) / (16 * RT));
+    hipLaunchKernelGGL(mfma_kernel<RT>, grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_mfma(const AttendArgs& a, hipStream_t stream) {
+    if (a.n_segs <= 0 && copy_workgroups(a.copy) == 0) return hipSuccess;
+    const int R = a.n_q * a.G;
+    if (R <= 16) return launch_rt<1>(a, stream);
+    if (R <= 32) return launch_rt<2>(a, stream);
+    if (R <= 48) return launch_rt<3>(a, stream);
+    return launch_rt<4>(a, stream);
+}
+
+}  // namespace kvs

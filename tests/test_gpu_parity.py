@@ -115,6 +115,52 @@ def test_prefill_parity():
         c.close()
 
 
+# Score spread: f32 queries are N(0,1)/sqrt(128), f16 queries N(0,1); the
+# scales keep the standard deviation of the scores near 1 to 2 (natural log
+# units), the range of the workloads. The matrix-core path rounds q * scale and
+# d * k to f16, so its score error grows with the spread (about 2^-12 |s|).
+@pytest.mark.parametrize("n_q,causal,qdt,scale", [(2, True, "f32", 1.0), (3, False, "f16", 0.15),
+                                                 (6, True, "f16", 1 / math.sqrt(128)), (8, False, "f32", 2.0),
+                                                 (11, True, "f32", 1.0)],
+                         ids=["rows12", "rows18-noncausal", "rows36", "rows48-noncausal", "rows66"])
+def test_multi_row_parity(n_q, causal, qdt, scale):
+    """Query blocks between decode and prefill widths: every row-tile variant
+    of the matrix-core kernel (16, 32, 48, 64 rows per workgroup), ragged row
+    tiles included."""
+    c = small_case(mask_random(0.5, seed=7), n_layers=2, max_q=n_q, group=2)
+    try:
+        qs = [c.queries(l, n_q, qdt) for l in range(c.L)]
+        q_pos0 = N_KV - n_q
+        outs, lses = c.attend_all(qs, q_pos0=q_pos0, scale=scale, causal=causal)
+        check(c, outs, lses, qs, q_pos0=q_pos0, scale=scale, causal=causal)
+    finally:
+        c.close()
+
+
+def test_prefill_bit_identical_across_residency_and_ring():
+    """Large query blocks (64-row tiles, last one ragged) give the same bits
+    whichever pages are resident and however the ring chunks the rest."""
+    n_q = 40
+    base = None
+    for v in [dict(resident=mask_all, ring=4, chunk=2, group=3),
+              dict(resident=mask_none, ring=2, chunk=1, group=3, flags=kvs.FLAG_POISON_RING),
+              dict(resident=mask_random(0.4, seed=9), ring=8, chunk=4, group=3)]:
+        c = small_case(v["resident"], n_layers=2, max_q=n_q, ring=v["ring"], chunk=v["chunk"],
+                       group=v["group"], flags=v.get("flags", 0))
+        try:
+            qs = [c.queries(l, n_q, "f16") for l in range(c.L)]
+            outs, lses = c.attend_all(qs, q_pos0=N_KV - n_q, scale=0.12, causal=True)
+            if base is None:
+                check(c, outs, lses, qs, q_pos0=N_KV - n_q, scale=0.12, causal=True)
+                base = (outs, lses)
+            else:
+                for l in range(c.L):
+                    assert np.array_equal(outs[l], base[0][l]), (v, l)
+                    assert np.array_equal(lses[l], base[1][l]), (v, l)
+        finally:
+            c.close()
+
+
 def test_outputs_bit_identical_across_residency_ring_and_chunks():
     variants = [
         dict(resident=mask_all, ring=4, chunk=2, streams=2),
@@ -145,14 +191,15 @@ def test_outputs_bit_identical_across_residency_ring_and_chunks():
                 c.close()
 
 
-def test_empty_cache_returns_zero_and_minus_inf():
-    c = small_case(mask_all, n_layers=1)
+@pytest.mark.parametrize("n_q", [1, 4], ids=["decode", "verify"])
+def test_empty_cache_returns_zero_and_minus_inf(n_q):
+    c = small_case(mask_all, n_layers=1, max_q=n_q)
     try:
         pool = c.pool
         pool.page_table_set(0, np.zeros(0, np.uint8))
-        q = torch.randn(1, c.Hq, 128, device="cuda")
+        q = torch.randn(n_q, c.Hq, 128, device="cuda")
         out = torch.full_like(q, 7.0)
-        lse = torch.zeros(1, c.Hq, device="cuda")
+        lse = torch.zeros(n_q, c.Hq, device="cuda")
         pool.attend(0, q, 0, 0, 1.0, False, out, lse)
         torch.cuda.synchronize()
         assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
