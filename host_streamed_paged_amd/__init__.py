@@ -12,6 +12,8 @@ import ctypes
 import os
 from dataclasses import dataclass
 
+import numpy as np
+
 import torch  # noqa: F401  (loads the HIP runtime the library binds to)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -31,7 +33,7 @@ _ERR_NAMES = {
 
 EXPORTS = [
     "kvs_type_pair_supported", "kvs_config_validate", "kvs_page_bytes", "kvs_min_budget_bytes",
-    "kvs_slots_for_budget", "kvs_pool_create", "kvs_pool_destroy", "kvs_host_pages_set",
+    "kvs_slots_for_budget", "kvs_plan_layer", "kvs_pool_create", "kvs_pool_destroy", "kvs_host_pages_set",
     "kvs_page_table_set", "kvs_stream_enqueue", "kvs_attend", "kvs_status", "kvs_debug_gather",
     "kvs_debug_read_page", "kvs_last_error", "kvs_profile_enable", "kvs_profile_read",
 ]
@@ -48,6 +50,11 @@ class KvsConfig(ctypes.Structure):
         "n_layers", "n_kv_heads", "n_q_heads", "head_dim", "page_tokens", "type_k", "type_v",
         "max_pages", "max_q_tokens", "ring_pages", "chunk_pages", "copy_streams", "group_pages")] + [
         ("flags", ctypes.c_uint32)]
+
+
+class KvsPlanInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "n_groups", "n_streamed", "n_segs", "n_resident_segs", "n_chunks", "whole_groups")]
 
 
 class KvsStatus(ctypes.Structure):
@@ -76,6 +83,7 @@ def lib() -> ctypes.CDLL:
         "kvs_page_bytes": (U64, [cfgp]),
         "kvs_min_budget_bytes": (ctypes.c_int, [cfgp, ctypes.POINTER(U64)]),
         "kvs_slots_for_budget": (I64, [cfgp, U64]),
+        "kvs_plan_layer": (ctypes.c_int, [cfgp, I32, P, ctypes.POINTER(KvsPlanInfo), P, I32, P, I32]),
         "kvs_pool_create": (ctypes.c_int, [cfgp, P, U64, ctypes.POINTER(P)]),
         "kvs_pool_destroy": (None, [P]),
         "kvs_host_pages_set": (ctypes.c_int, [P, I32, P, I32]),
@@ -154,6 +162,24 @@ def min_budget_bytes(cfg: Config) -> int:
 
 def slots_for_budget(cfg: Config, budget: int) -> int:
     return lib().kvs_slots_for_budget(ctypes.byref(cfg.c()), budget)
+
+
+def plan_layer(cfg: Config, resident):
+    """The launch plan for one layer (kvs_plan_layer): (info, segments, chunks)
+    with segments as rows {group, first page, pages, flags} and chunks as rows
+    {first streamed rank, pages, first segment, segments}."""
+    res = np.ascontiguousarray(np.asarray(resident, dtype=np.uint8))
+    n = int(res.shape[0])
+    info = KvsPlanInfo()
+    c = cfg.c()
+    rp = res.ctypes.data_as(ctypes.c_void_p) if n else None
+    _check(lib().kvs_plan_layer(ctypes.byref(c), n, rp, ctypes.byref(info), None, 0, None, 0))
+    segs = np.zeros((max(1, info.n_segs), 4), np.int32)
+    chunks = np.zeros((max(1, info.n_chunks), 4), np.int32)
+    _check(lib().kvs_plan_layer(ctypes.byref(c), n, rp, ctypes.byref(info),
+                                segs.ctypes.data_as(ctypes.c_void_p), segs.shape[0],
+                                chunks.ctypes.data_as(ctypes.c_void_p), chunks.shape[0]))
+    return info, segs[:info.n_segs], chunks[:info.n_chunks]
 
 
 def last_error() -> str:

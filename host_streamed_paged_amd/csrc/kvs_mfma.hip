@@ -27,6 +27,7 @@
 #include <hip/hip_runtime.h>
 #include <cstdint>
 #include <cmath>
+#include <type_traits>
 
 #include "kvs_internal.h"
 #include "kvs_device.h"
@@ -43,7 +44,12 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTokW = kPageTokens / kWaves;   // tokens per wave in QK (64)
 constexpr int kChunks = kPageTokens / 32;     // 32-token MFMA chunks per page in PV
+// The running max moves only when a page's max exceeds it by more than this
+// (log2 units), so p <= 2^8 stays well inside f16 and O is rarely rescaled.
+constexpr float kLazyMax = 8.f;
 
+// One page's tiles. (Double-buffering them measured slower: the next page's
+// LDS DMA then competes with the QK reads of the current one.)
 template <int RT>
 struct MfmaSmem {
     // K tile in record layout; once every wave is past QK it holds the P
@@ -57,10 +63,10 @@ struct MfmaSmem {
 __device__ inline half2_t as_h2(uint32_t x) { return __builtin_bit_cast(half2_t, x); }
 __device__ inline uint32_t as_u(half2_t x) { return __builtin_bit_cast(uint32_t, x); }
 
-// two workgroups per CU up to 3 row tiles; 4 row tiles need the whole
+// two workgroups per CU up to 2 row tiles; 4 row tiles need the whole
 // register file of a SIMD lane (256 arch + acc registers would spill)
 template <int RT>
-__global__ __launch_bounds__(kThreads, RT <= 3 ? 2 : 1) void mfma_kernel(AttendArgs a) {
+__global__ __launch_bounds__(kThreads, RT <= 2 ? 2 : 1) void mfma_kernel(AttendArgs a) {
     static_assert(kChunks * RT * 64 * 16 <= kKTile, "P operands must fit in the K tile");
     __shared__ MfmaSmem<RT> sm;
     if ((int)blockIdx.x >= a.n_segs) {   // ring refill workgroup
@@ -165,9 +171,19 @@ __global__ __launch_bounds__(kThreads, RT <= 3 ? 2 : 1) void mfma_kernel(AttendA
     const half2_t v_off = {(_Float16)1032.f, (_Float16)1032.f};   // 1024 + 8
     const uint32_t m_nib = vconst(0x000F000Fu), magic = vconst(0x64006400u);
 
+    // smallest visible prefix over the workgroup's rows (causal limits grow
+    // with the query index): pages below it need no mask
+    int64_t lim_min = a.n_kv;
+    if (a.causal) {
+        const int64_t c = a.q_pos0 + r0 / G + 1;
+        lim_min = c < lim_min ? c : lim_min;
+    }
+
     for (int pi = 0; pi < seg.npages; ++pi) {
         const int page = seg.page0 + pi;
         const int64_t base_tok = (int64_t)page * kPageTokens;
+        const bool mask_page = base_tok + kPageTokens > lim_min;   // uniform
+        const bool tail_page = base_tok + kPageTokens > a.n_kv;    // rows past the cache
         int limrel[RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -220,6 +236,17 @@ __global__ __launch_bounds__(kThreads, RT <= 3 ? 2 : 1) void mfma_kernel(AttendA
         }
 
         // ---- mask, page maxima (lane value i is token 64 w + 16 tt + 4 gq + i)
+        if (mask_page) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int tok = kTokW * w + 16 * tt + 4 * gq + i;
+                        s[tt][rt][i] = tok < limrel[rt] ? s[tt][rt][i] : -INFINITY;
+                    }
+        }
         float mx[RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -227,12 +254,7 @@ __global__ __launch_bounds__(kThreads, RT <= 3 ? 2 : 1) void mfma_kernel(AttendA
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int tok = kTokW * w + 16 * tt + 4 * gq + i;
-                    const float v = tok < limrel[rt] ? s[tt][rt][i] : -INFINITY;
-                    s[tt][rt][i] = v;
-                    mx[rt] = fmaxf(mx[rt], v);
-                }
+                for (int i = 0; i < 4; ++i) mx[rt] = fmaxf(mx[rt], s[tt][rt][i]);
             mx[rt] = fmaxf(mx[rt], __shfl_xor(mx[rt], 16, 64));
             mx[rt] = fmaxf(mx[rt], __shfl_xor(mx[rt], 32, 64));
             if (gq == 0) sm.red_m[w][16 * rt + n] = mx[rt];
@@ -245,10 +267,11 @@ __global__ __launch_bounds__(kThreads, RT <= 3 ? 2 : 1) void mfma_kernel(AttendA
             float pm = sm.red_m[0][16 * rt + n];
 #pragma unroll
             for (int ww = 1; ww < kWaves; ++ww) pm = fmaxf(pm, sm.red_m[ww][16 * rt + n]);
-            const float m_new = fmaxf(m_run[rt], pm);
-            m_use[rt] = m_new == -INFINITY ? 0.f : m_new;
-            alpha[rt] = exp2f(m_run[rt] - m_use[rt]);   // 0 while the state is empty
-            m_run[rt] = m_new;
+            // pm > -inf + 8 holds for any finite pm: the first visible page sets m
+            const bool grow = pm > m_run[rt] + kLazyMax;
+            alpha[rt] = grow ? __builtin_amdgcn_exp2f(m_run[rt] - pm) : 1.f;   // 0 while the state is empty
+            m_run[rt] = grow ? pm : m_run[rt];
+            m_use[rt] = m_run[rt] == -INFINITY ? 0.f : m_run[rt];
         }
         // ---- probabilities -> P operands in LDS (slot 8 gq + j of chunk c is
         // token 32 c + 4 gq + j for j < 4, 32 c + 12 + 4 gq + j otherwise)
@@ -261,7 +284,7 @@ __global__ __launch_bounds__(kThreads, RT <= 3 ? 2 : 1) void mfma_kernel(AttendA
                 half8_t pv;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const float p = exp2f(s[2 * c2 + (j >> 2)][rt][j & 3] - m_use[rt]);
+                    const float p = __builtin_amdgcn_exp2f(s[2 * c2 + (j >> 2)][rt][j & 3] - m_use[rt]);
                     ls += p;
                     pv[j] = (_Float16)p;
                 }
@@ -273,45 +296,57 @@ __global__ __launch_bounds__(kThreads, RT <= 3 ? 2 : 1) void mfma_kernel(AttendA
         }
         lds_barrier();   // P operands and row sums published
 
+        bool rescale = false;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             float lp = sm.red_l[0][16 * rt + n];
 #pragma unroll
             for (int ww = 1; ww < kWaves; ++ww) lp += sm.red_l[ww][16 * rt + n];
             l_run[rt] = l_run[rt] * alpha[rt] + lp;
+            rescale |= alpha[rt] != 1.f;
+        }
+        if (__any(rescale)) {
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) o[ct][rt] *= alpha[rt];
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) o[ct][rt] *= alpha[rt];
         }
 
-        // ---- P.V for channels 32 w .. 32 w + 31 (V quant block w)
-        const uint8_t* vcol = sm.v + w * kVBlock;
-#pragma unroll 2
-        for (int c = 0; c < kChunks; ++c) {
-            half8_t vop[2];
+        // ---- P.V for channels 32 w .. 32 w + 31 (V quant block w). The lane's
+        // V rows: tokens 32 c + 4 gq + {0..3} and 32 c + 16 + 4 gq + {0..3}.
+        const uint8_t* vlane = sm.v + w * kVBlock + 4 * gq * kVRow;
+        auto pv_page = [&](auto tail) {
 #pragma unroll
-            for (int jp = 0; jp < 4; ++jp) {
-                const int j0 = 2 * jp, j1 = 2 * jp + 1;
-                const int t0 = 32 * c + (j0 < 4 ? 4 * gq + j0 : 12 + 4 * gq + j0);
-                const int t1 = 32 * c + (j1 < 4 ? 4 * gq + j1 : 12 + 4 * gq + j1);
-                const uint8_t* r0p = vcol + t0 * kVRow;
-                const uint8_t* r1p = vcol + t1 * kVRow;
-                uint32_t d0 = *(const uint16_t*)r0p, d1 = *(const uint16_t*)r1p;
-                d0 = t0 < valid ? d0 : 0u;   // rows past the cache may hold NaN scales
-                d1 = t1 < valid ? d1 : 0u;
-                const half2_t dd = as_h2(d0 | (d1 << 16));
-                const uint32_t x = __builtin_amdgcn_perm((uint32_t)r1p[2 + n], (uint32_t)r0p[2 + n], 0x0c040c00u);
-                const half2_t lo = (as_h2((x & m_nib) | magic) - v_off) * dd;          // channel n
-                const half2_t hi = (as_h2(((x >> 4) & m_nib) | magic) - v_off) * dd;   // channel 16 + n
-                vop[0][j0] = lo[0]; vop[0][j1] = lo[1];
-                vop[1][j0] = hi[0]; vop[1][j1] = hi[1];
-            }
+            for (int c = 0; c < kChunks; ++c) {
+                half8_t vop[2];
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                const half8_t pop = *(const half8_t*)(pbuf + ((c * RT + rt) * 64 + lane) * 16);
-                o[0][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[0], pop, o[0][rt], 0, 0, 0);
-                o[1][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[1], pop, o[1][rt], 0, 0, 0);
+                for (int jp = 0; jp < 4; ++jp) {
+                    const int j0 = 2 * jp, j1 = 2 * jp + 1;
+                    const int o0 = 32 * c + (j0 < 4 ? j0 : 12 + j0), o1 = 32 * c + (j1 < 4 ? j1 : 12 + j1);
+                    const uint8_t* r0p = vlane + o0 * kVRow;
+                    const uint8_t* r1p = vlane + o1 * kVRow;
+                    uint32_t d0 = *(const uint16_t*)r0p, d1 = *(const uint16_t*)r1p;
+                    if constexpr (decltype(tail)::value) {   // rows past the cache may hold NaN scales
+                        d0 = o0 + 4 * gq < valid ? d0 : 0u;
+                        d1 = o1 + 4 * gq < valid ? d1 : 0u;
+                    }
+                    const half2_t dd = as_h2(d0 | (d1 << 16));
+                    const uint32_t x = __builtin_amdgcn_perm((uint32_t)r1p[2 + n], (uint32_t)r0p[2 + n], 0x0c040c00u);
+                    const half2_t lo = (as_h2((x & m_nib) | magic) - v_off) * dd;          // channel n
+                    const half2_t hi = (as_h2(((x >> 4) & m_nib) | magic) - v_off) * dd;   // channel 16 + n
+                    vop[0][j0] = lo[0]; vop[0][j1] = lo[1];
+                    vop[1][j0] = hi[0]; vop[1][j1] = hi[1];
+                }
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    const half8_t pop = *(const half8_t*)(pbuf + ((c * RT + rt) * 64 + lane) * 16);
+                    o[0][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[0], pop, o[0][rt], 0, 0, 0);
+                    o[1][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[1], pop, o[1][rt], 0, 0, 0);
+                }
             }
-        }
+        };
+        if (tail_page) pv_page(std::true_type{});
+        else pv_page(std::false_type{});
         lds_barrier();   // every wave is done with this page's tiles
         if (pi + 1 < seg.npages) issue_page(page + 1);
     }
@@ -345,12 +380,13 @@ hipError_t launch_rt(const AttendArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+// Row tile width by query rows per kv head: 16 (verify-sized blocks up to 16
+// rows), 32, else 64 rows per workgroup.
 hipError_t launch_mfma(const AttendArgs& a, hipStream_t stream) {
     if (a.n_segs <= 0 && copy_workgroups(a.copy) == 0) return hipSuccess;
     const int R = a.n_q * a.G;
     if (R <= 16) return launch_rt<1>(a, stream);
     if (R <= 32) return launch_rt<2>(a, stream);
-    if (R <= 48) return launch_rt<3>(a, stream);
     return launch_rt<4>(a, stream);
 }
 

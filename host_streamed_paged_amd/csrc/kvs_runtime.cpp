@@ -110,6 +110,7 @@ struct LayerState {
     std::vector<kvs::Seg> segs;
     int32_t res_nseg = 0;            // segments [0, res_nseg) form the resident launch
     std::vector<ChunkPlan> chunks;
+    bool whole_groups = true;        // no split-K group spans two chunk launches
     int32_t n_groups = 0;
     int32_t n_streamed = 0;
     int32_t* dev_src = nullptr;
@@ -184,8 +185,8 @@ int check_device(const kvs_pool* p) {
 }
 
 // Build segments and chunk plans for a layer from its residency.
-int build_plan(const kvs_pool* p, LayerState& ls, int32_t n_pages, const uint8_t* resident) {
-    const int32_t G = p->cfg.group_pages, C = p->cfg.chunk_pages;
+int build_plan(const kvs_config& cfg, int32_t max_segs, LayerState& ls, int32_t n_pages, const uint8_t* resident) {
+    const int32_t G = cfg.group_pages, C = cfg.chunk_pages;
     ls.src.assign(n_pages, 0);
     std::vector<int32_t> streamed;
     for (int32_t i = 0; i < n_pages; ++i)
@@ -196,23 +197,53 @@ int build_plan(const kvs_pool* p, LayerState& ls, int32_t n_pages, const uint8_t
     for (int32_t pg : streamed) mixed[pg / G] = 1;
     ls.segs.clear();
     ls.chunks.clear();
+    ls.whole_groups = true;
     for (int32_t g = 0; g < ls.n_groups; ++g)
         if (!mixed[g]) ls.segs.push_back({g, g * G, std::min(n_pages, (g + 1) * G) - g * G, kvs::kSegFresh});
     ls.res_nseg = (int32_t)ls.segs.size();
-    const int32_t n_chunks = (ls.n_streamed + C - 1) / C;
+    // Chunks: runs of at most C streamed pages in ascending order. A chunk
+    // boundary falls between split-K groups, so that each group is computed by
+    // one launch, unless a group alone has more than C streamed pages: its
+    // streamed pages then fill consecutive chunks and its running state is
+    // carried from one launch to the next.
+    std::vector<int32_t> gstream(ls.n_groups, 0);
+    for (int32_t pg : streamed) gstream[pg / G]++;
+    std::vector<std::pair<int32_t, int32_t>> spans;   // (rank0, npages)
+    {
+        int32_t rank0 = 0, cur = 0;
+        for (int32_t g = 0; g < ls.n_groups; ++g) {
+            int32_t sg = gstream[g];
+            if (sg == 0) continue;
+            if (cur > 0 && (cur + sg > C || sg > C)) { spans.push_back({rank0, cur}); rank0 += cur; cur = 0; }
+            if (sg > C) {
+                ls.whole_groups = false;
+                for (; sg > 0; sg -= std::min(C, sg)) { spans.push_back({rank0, std::min(C, sg)}); rank0 += std::min(C, sg); }
+                continue;
+            }
+            cur += sg;
+        }
+        if (cur > 0) spans.push_back({rank0, cur});
+    }
+    const int32_t n_chunks = (int32_t)spans.size();
+    // page windows: chunk c owns [bound[c], bound[c + 1]); a bound is the start
+    // of the group holding the chunk's first streamed page, or that page itself
+    // where a group is split
+    std::vector<int32_t> bound(n_chunks + 1, 0);
+    bound[n_chunks] = n_pages;
+    for (int32_t c = 1; c < n_chunks; ++c) {
+        const int32_t first = streamed[spans[c].first], prev_last = streamed[spans[c].first - 1];
+        bound[c] = (prev_last / G == first / G) ? first : (first / G) * G;
+    }
     for (int32_t c = 0; c < n_chunks; ++c) {
         ChunkPlan cp;
-        cp.rank0 = c * C;
-        cp.npages = std::min(C, ls.n_streamed - cp.rank0);
+        cp.rank0 = spans[c].first;
+        cp.npages = spans[c].second;
         for (int32_t k = 0; k < cp.npages; ++k) {
             int32_t pg = streamed[cp.rank0 + k];
             if (!cp.runs.empty() && cp.runs.back().first + cp.runs.back().second == pg) cp.runs.back().second++;
             else cp.runs.push_back({pg, 1});
         }
-        // window [w0, w1): from this chunk's first streamed page (page 0 for the
-        // first chunk) up to the next chunk's first streamed page (or the end)
-        const int32_t w0 = (c == 0) ? 0 : streamed[cp.rank0];
-        const int32_t w1 = (c + 1 < n_chunks) ? streamed[(c + 1) * C] : n_pages;
+        const int32_t w0 = bound[c], w1 = bound[c + 1];
         cp.seg0 = (int32_t)ls.segs.size();
         for (int32_t g = w0 / G; g * G < w1; ++g) {
             if (!mixed[g]) continue;
@@ -251,7 +282,7 @@ int build_plan(const kvs_pool* p, LayerState& ls, int32_t n_pages, const uint8_t
                 return fail(KVS_ERR_INVALID_ARG, "internal: chunk plan check failed");
     for (int32_t q = 0; q < n_pages; ++q)
         if (seen[q] != 1) return fail(KVS_ERR_INVALID_ARG, "internal: page %d not covered once", q);
-    if ((int32_t)ls.segs.size() > p->L.max_segs) return fail(KVS_ERR_INVALID_ARG, "internal: too many segments");
+    if ((int32_t)ls.segs.size() > max_segs) return fail(KVS_ERR_INVALID_ARG, "internal: too many segments");
     return KVS_OK;
 }
 
@@ -295,8 +326,10 @@ int prefetch(kvs_pool* p, int32_t layer) {
 // Run the layer's launch plan. Ring chunks are moved by copy workgroups
 // inside the compute launches; kernel boundaries on a stream order each copy
 // before its reader and each reader before its slot is refilled.
-//   Two lanes (ring of an even number >= 4 of chunk slots, one page per
-//   split-K group): the caller's stream computes even chunks and the pool's
+//   Two lanes (ring of an even number >= 4 of chunk slots, and every
+//   split-K group computed by a single chunk launch, so that concurrent
+//   launches never share a group's state): the caller's stream computes even
+//   chunks and the pool's
 //   lane stream odd chunks; the launch that computes chunk c copies chunk
 //   c + 2, which belongs to the same lane, into a slot last read by that lane.
 //   The lanes' launch boundaries fall at different times, so the host link
@@ -321,7 +354,7 @@ int run_layer(kvs_pool* p, int32_t layer, hipStream_t stream, LaunchFn launch) {
         if (hipStreamWaitEvent(stream, p->ring_free, 0) != hipSuccess) return mark(fail(KVS_ERR_HIP, "hipStreamWaitEvent(ring) failed"));
     }
     p->pf_layer = -1;
-    const bool two = n_ch >= 2 && R >= 4 && (R % 2) == 0 && p->cfg.group_pages == 1;
+    const bool two = n_ch >= 2 && R >= 4 && (R % 2) == 0 && ls.whole_groups;
     auto slot_of = [&](int32_t c) { return (slot0 + c) % R; };
     auto do_launch = [&](hipStream_t st, int32_t seg0, int32_t nseg, int32_t c_compute, int32_t c_copy) -> int {
         kvs::CopyJob cj{};
@@ -424,6 +457,43 @@ int kvs_min_budget_bytes(const kvs_config* cfg, uint64_t* out) {
     if (rc) return rc;
     if (!out) return fail(KVS_ERR_INVALID_ARG, "out is NULL");
     *out = layout_of(cfg).fixed;
+    return KVS_OK;
+}
+
+int kvs_plan_layer(const kvs_config* cfg, int32_t n_pages, const uint8_t* resident, kvs_plan_info* info,
+                   int32_t* segs, int32_t seg_cap, int32_t* chunks, int32_t chunk_cap) {
+    int rc = validate(cfg);
+    if (rc) return rc;
+    if (n_pages < 0 || n_pages > cfg->max_pages)
+        return fail(KVS_ERR_INVALID_ARG, "n_pages %d out of range [0, max_pages %d]", n_pages, cfg->max_pages);
+    if ((n_pages > 0 && !resident) || !info) return fail(KVS_ERR_INVALID_ARG, "resident or info is NULL");
+    LayerState ls;
+    rc = build_plan(*cfg, layout_of(cfg).max_segs, ls, n_pages, resident);
+    if (rc) return rc;
+    info->n_groups = ls.n_groups;
+    info->n_streamed = ls.n_streamed;
+    info->n_segs = (int32_t)ls.segs.size();
+    info->n_resident_segs = ls.res_nseg;
+    info->n_chunks = (int32_t)ls.chunks.size();
+    info->whole_groups = ls.whole_groups ? 1 : 0;
+    if (segs) {
+        if (seg_cap < info->n_segs) return fail(KVS_ERR_INVALID_ARG, "seg_cap %d < %d segments", seg_cap, info->n_segs);
+        for (int32_t i = 0; i < info->n_segs; ++i) {
+            segs[4 * i] = ls.segs[i].group;
+            segs[4 * i + 1] = ls.segs[i].page0;
+            segs[4 * i + 2] = ls.segs[i].npages;
+            segs[4 * i + 3] = ls.segs[i].flags;
+        }
+    }
+    if (chunks) {
+        if (chunk_cap < info->n_chunks) return fail(KVS_ERR_INVALID_ARG, "chunk_cap %d < %d chunks", chunk_cap, info->n_chunks);
+        for (int32_t c = 0; c < info->n_chunks; ++c) {
+            chunks[4 * c] = ls.chunks[c].rank0;
+            chunks[4 * c + 1] = ls.chunks[c].npages;
+            chunks[4 * c + 2] = ls.chunks[c].seg0;
+            chunks[4 * c + 3] = ls.chunks[c].nseg;
+        }
+    }
     return KVS_OK;
 }
 
@@ -545,7 +615,7 @@ int kvs_page_table_set(kvs_pool* p, int32_t layer, int32_t n_pages, const uint8_
     trial.host_pages = ls.host_pages;
     trial.dev_src = ls.dev_src;
     trial.dev_segs = ls.dev_segs;
-    rc = build_plan(p, trial, n_pages, resident);
+    rc = build_plan(p->cfg, p->L.max_segs, trial, n_pages, resident);
     if (rc) return rc;
     // commit: release old slots, take new ones
     for (int32_t s : ls.slots_held) p->slot_free.push_back(s);

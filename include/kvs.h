@@ -96,8 +96,11 @@ typedef struct kvs_config {
                               1 + n_draft for a speculative verify, the ubatch for prefill */
     int32_t ring_pages;    /* device ring capacity in pages (>= 1)                        */
     int32_t chunk_pages;   /* pages per ring chunk (1..16), a divisor of ring_pages: one
-                              launch computes a chunk while its copy workgroups pull the
-                              next chunk from host memory into the next chunk slot       */
+                              launch computes a chunk while its copy workgroups pull a
+                              later chunk from host memory into a free chunk slot. A
+                              chunk holds whole split-K groups when group_pages <=
+                              chunk_pages (so it may carry fewer pages); only then can
+                              two chunk launches run concurrently                      */
     int32_t copy_streams;  /* streams the pool creates for kvs_stream_enqueue (1..8)       */
     int32_t group_pages;   /* pages per split-K partial (>= 1). Partials are keyed by this
                               logical grouping only, so results do not depend on which
@@ -140,6 +143,35 @@ int kvs_min_budget_bytes(const kvs_config* cfg, uint64_t* out);
 /* Number of resident page slots a budget yields for cfg (0 if below the
  * minimum). Pure. */
 int64_t kvs_slots_for_budget(const kvs_config* cfg, uint64_t budget_bytes);
+
+/* The launch plan kvs_page_table_set would build for one layer of n_pages
+ * pages with the given residency (resident[i] != 0: page i resident). Pure
+ * host computation, no device needed; for inspection and tests.
+ *
+ * Split-K groups are runs of group_pages logical pages (page 2, "Phase arena:
+ * speculative verify batches": a verify batch attends the whole cache; the
+ * grouping is this library's, fixed by page index so results do not depend on
+ * residency). Groups with no streamed page form the resident launch; the
+ * streamed pages, in ascending order, are cut into ring chunks of at most
+ * chunk_pages pages, each chunk launch also computing the resident pages of
+ * the groups it finishes.
+ *
+ * Outputs: *info (required); if segs is not NULL, segment i is written to
+ * segs[4i .. 4i+3] = {group, first page, pages, flags (1 = starts its group)},
+ * resident launch first; if chunks is not NULL, chunk c is written to
+ * chunks[4c .. 4c+3] = {first streamed rank, pages, first segment, segments}.
+ * KVS_ERR_INVALID_ARG if a capacity is too small or an argument is invalid. */
+typedef struct kvs_plan_info {
+    int32_t n_groups;         /* split-K groups of the layer                       */
+    int32_t n_streamed;       /* pages not resident                                */
+    int32_t n_segs;           /* segments over all launches                        */
+    int32_t n_resident_segs;  /* segments of the resident launch                   */
+    int32_t n_chunks;         /* ring chunk launches                               */
+    int32_t whole_groups;     /* 1 if no group spans two launches (then chunk
+                                 launches may run on two streams at once)          */
+} kvs_plan_info;
+int kvs_plan_layer(const kvs_config* cfg, int32_t n_pages, const uint8_t* resident, kvs_plan_info* info,
+                   int32_t* segs, int32_t seg_cap, int32_t* chunks, int32_t chunk_cap);
 
 /* Create a pool that carves [resident slots | ring | workspace | tables] out of
  * the caller's device arena of budget_bytes bytes (256-byte aligned). The

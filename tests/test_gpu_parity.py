@@ -124,9 +124,9 @@ def test_prefill_parity():
                                                  (11, True, "f32", 1.0)],
                          ids=["rows12", "rows18-noncausal", "rows36", "rows48-noncausal", "rows66"])
 def test_multi_row_parity(n_q, causal, qdt, scale):
-    """Query blocks between decode and prefill widths: every row-tile variant
-    of the matrix-core kernel (16, 32, 48, 64 rows per workgroup), ragged row
-    tiles included."""
+    """Query blocks between decode and prefill widths (16- and 32-row tiles of
+    the matrix-core kernel, ragged row tiles included; the full-size tests
+    cover the 64-row tiles)."""
     c = small_case(mask_random(0.5, seed=7), n_layers=2, max_q=n_q, group=2)
     try:
         qs = [c.queries(l, n_q, qdt) for l in range(c.L)]
@@ -168,7 +168,7 @@ def test_outputs_bit_identical_across_residency_ring_and_chunks():
         dict(resident=mask_none, ring=6, chunk=3, streams=3),
         dict(resident=mask_random(0.5), ring=4, chunk=4, streams=1),
         dict(resident=mask_random(0.3, seed=5), ring=2, chunk=1, streams=2, flags=kvs.FLAG_POISON_RING),
-        # four or more chunk slots: two compute lanes when groups are single pages
+        # four or more chunk slots: two compute lanes when no group spans two chunks
         dict(resident=mask_none, ring=4, chunk=1, streams=1),
         dict(resident=mask_random(0.5, seed=6), ring=8, chunk=2, streams=2, flags=kvs.FLAG_POISON_RING),
     ]
