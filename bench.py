@@ -13,10 +13,16 @@ step) over the timed steps. Alongside it:
   * streamed: the same measurement at 256 Ki context with 103 resident pages
     per layer and the rest streamed through a 16-page ring, against the host
     link rate measured in the same run (1 GiB pinned copy, best of 5);
+  * verify / prefill: the speculative-verify block (4 query tokens at 160 Ki
+    context, 180 resident pages per layer) and the prefill ubatch (256 query
+    tokens over a 128 Ki prefix, 10 % resident), each streamed through the ring
+    against the measured link, plus the matrix-core kernel on the same shapes
+    with every page resident: KV bytes against HBM for verify, flops against
+    the dense f16 matrix peak for prefill;
   * cpu_baseline: the float64 CPU oracle on a bounded sample of layers of the
     same workload, on this host's cores.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-streamed] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-streamed] [--no-multi] [--no-cpu]
 """
 
 import argparse
@@ -35,6 +41,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "streamed attention KV GB/s + decode attn tok/s at 32K/256K ctx, % of HBM/link roofline"
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0   # dense f16 matrix peak of MI355X
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -161,6 +168,59 @@ def streamed_run(wl, st, steps, warmup):
     return dict(ms_per_step=e0.elapsed_time(e1) / steps, wall_ms_per_step=wall * 1e3 / steps)
 
 
+def allowed_keys(wl):
+    """Keys each query row may attend, summed over the block's query tokens."""
+    if not wl.causal:
+        return wl.n_q * wl.n_kv
+    return sum(min(wl.n_kv, wl.q_pos0 + i + 1) for i in range(wl.n_q))
+
+
+def multi_leg(name, cfg_kw, threads, link, steps, kind):
+    """A multi-query workload: the streamed step through the ring, then the
+    same shapes with every page resident to time the matrix-core kernel."""
+    import dataclasses
+    from kvs_synth import WORKLOADS
+    wl = WORKLOADS[name]
+    st = setup(wl, cfg_kw, threads)
+    sr = streamed_run(wl, st, steps, 2)
+    pb = st["recs"][0].shape[1]
+    streamed_bytes = sum(int((1 - m).sum()) for m in st["masks"]) * pb
+    total_bytes = wl.n_layers * wl.n_pages * pb
+    sec = sr["ms_per_step"] / 1e3
+    st["pool"].close()
+    del st
+    out = {
+        "workload": name, "context": wl.n_kv, "query_tokens": wl.n_q, "resident_pages_per_layer": wl.resident_pages,
+        "ms_per_step": round(sr["ms_per_step"], 4), "q_tok_s": round(wl.n_q / sec, 2),
+        "kv_gbs": round(total_bytes / sec / 1e9, 2), "streamed_gbs": round(streamed_bytes / sec / 1e9, 2),
+        "link_gbs_measured": round(link, 2), "frac_of_link": round(streamed_bytes / sec / 1e9 / link, 4),
+        "streamed_bytes_per_step": streamed_bytes, **cfg_kw,
+    }
+    log(f"{name}: {sr['ms_per_step']:.3f} ms/step, streamed {streamed_bytes / sec / 1e9:.2f} GB/s of link {link:.2f}")
+    rwl = dataclasses.replace(wl, resident_pages=wl.n_pages)
+    rst = setup(rwl, cfg_kw, threads)
+    r = timed_run(rwl, rst, 5, 2)
+    rst["pool"].close()
+    del rst
+    avg = r["attn_ms_total"] / max(1, r["attn_launches"])
+    layer_bytes = wl.n_pages * pb
+    flops = 4 * wl.n_q_heads * wl.head_dim * allowed_keys(wl)
+    k = {"kernel": f"mfma_kernel<{2 if kind == 'verify' else 4}> (all pages resident, one launch per layer)",
+         "avg_launch_us": round(avg * 1e3, 2), "launches": r["attn_launches"],
+         "bytes_per_launch": layer_bytes, "flops_per_launch": flops,
+         "achieved_gbs": round(layer_bytes / (avg / 1e3) / 1e9, 1),
+         "achieved_tflops": round(flops / (avg / 1e3) / 1e12, 1)}
+    if kind == "verify":
+        k.update(bound="hbm", frac=round(k["achieved_gbs"] / HBM_PEAK_GBS, 4), peak=HBM_PEAK_GBS, unit="GB/s")
+    else:
+        k.update(bound="mfma", frac=round(k["achieved_tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
+                 peak=MFMA_F16_PEAK_TFLOPS, unit="TFLOP/s")
+    out["resident_kernel"] = k
+    log(f"{name} all-resident: attention launch {avg * 1e3:.1f} us, {k['achieved_gbs']} GB/s, "
+        f"{k['achieved_tflops']} TFLOP/s")
+    return out
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "host_streamed_paged_amd", "csrc")
@@ -239,8 +299,12 @@ def main():
     ap.add_argument("--workload", default="resident_decode_32k")
     ap.add_argument("--no-streamed", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-multi", action="store_true", help="skip the verify and prefill workloads")
     ap.add_argument("--streamed-steps", type=int, default=10)
     ap.add_argument("--threads", type=int, default=min(16, len(os.sched_getaffinity(0))))
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run torch device-to-device copies of MIB MiB (the reference kernel of known "
+                         "traffic for scaling the FETCH_SIZE / WRITE_SIZE counters), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the streamed-attention path runs on a single device "
@@ -248,6 +312,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": n, "launches": 3}), flush=True)
+        return
     import host_streamed_paged_amd as kvs
     from kvs_synth import WORKLOADS
 
@@ -305,8 +378,10 @@ def main():
         "combine_avg_us": round(r["combine_ms_total"] / max(1, r["combine_launches"]) * 1e3, 3),
     }
 
-    if not args.no_streamed:
+    link = None
+    if not args.no_streamed or not args.no_multi:
         link = measure_link()
+    if not args.no_streamed:
         swl = WORKLOADS["streamed_decode_256k"]
         sst = setup(swl, cfg_kw, args.threads)
         sr = streamed_run(swl, sst, args.streamed_steps, 2)
@@ -331,6 +406,12 @@ def main():
             f"of link {link:.2f} GB/s")
         sst["pool"].close()
         del sst
+
+    if not args.no_multi:
+        result["verify"] = multi_leg("spec_verify_160k", dict(ring_pages=16, chunk_pages=4, copy_streams=1,
+                                                              group_pages=1), args.threads, link, 8, "verify")
+        result["prefill"] = multi_leg("prefill_ubatch_128k", dict(ring_pages=32, chunk_pages=8, copy_streams=1,
+                                                                  group_pages=8), args.threads, link, 6, "prefill")
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(wl, recs, qs_np)
