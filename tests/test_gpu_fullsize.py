@@ -1,0 +1,63 @@
+"""Full-size parity: every workload at its real size, in the launch
+configuration bench.py times (ring, chunk and group sizes), all 16 layers
+computed on the GPU; sampled outputs checked against the float64 oracle, which
+computes them one (layer, query token, head) at a time.
+
+Bars as in test_gpu_parity: 2e-3 normwise per output row, lse within 2e-3
+absolute. Sampled: the first and last layer, the first, middle and last query
+token, and query heads spread over all kv heads.
+"""
+
+import numpy as np
+import pytest
+
+from kvs_case import Case, normwise_error, say
+from kvs_synth import WORKLOADS, residency_mask
+from oracle import attend, gather_kv
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+TOL = 2e-3
+
+# workload -> the pool configuration bench.py runs it with
+BENCH_CFG = {
+    "resident_decode_32k": dict(ring_pages=16, chunk_pages=4, copy_streams=1, group_pages=1),
+    "streamed_decode_256k": dict(ring_pages=16, chunk_pages=4, copy_streams=1, group_pages=1),
+    "spec_verify_160k": dict(ring_pages=16, chunk_pages=4, copy_streams=1, group_pages=1),
+    "prefill_ubatch_128k": dict(ring_pages=32, chunk_pages=8, copy_streams=1, group_pages=8),
+}
+
+
+@pytest.mark.parametrize("name", list(BENCH_CFG))
+def test_full_size_sampled_parity(name):
+    wl = WORKLOADS[name]
+    say(f"full-size {name}: layers={wl.n_layers} n_kv={wl.n_kv} n_q={wl.n_q} cfg={BENCH_CFG[name]}")
+
+    def resident(l, n):
+        return residency_mask(wl.cid, l, n, wl.resident_pages, wl.own_page_resident)
+
+    c = Case(cid=wl.cid, n_layers=wl.n_layers, n_kv_heads=wl.n_kv_heads, n_q_heads=wl.n_q_heads, n_kv=wl.n_kv,
+             cfg_kw=dict(max_q_tokens=wl.n_q, **BENCH_CFG[name]), resident_fn=resident)
+    try:
+        qs = [c.queries(l, wl.n_q, wl.q_dtype) for l in range(wl.n_layers)]
+        outs, lses = c.attend_all(qs, q_pos0=wl.q_pos0, scale=wl.scale, causal=wl.causal)
+        assert all(np.isfinite(o).all() for o in outs)
+        G = wl.n_q_heads // wl.n_kv_heads
+        heads = [g * G + (g * 5) % G for g in range(wl.n_kv_heads)]   # one per kv head
+        q_idx = sorted({0, wl.n_q // 2, wl.n_q - 1})
+        worst = 0.0
+        for l in (0, wl.n_layers - 1):
+            K, V = gather_kv(c.records[l], wl.n_kv_heads, wl.head_dim, 0, wl.n_kv)
+            for i in q_idx:
+                ref, ref_lse = attend(qs[l][i:i + 1], K, V, n_kv=wl.n_kv, scale=wl.scale, causal=wl.causal,
+                                      q_pos0=wl.q_pos0 + i, heads=heads)
+                err = normwise_error(outs[l][i:i + 1, heads], ref[:, heads])
+                lerr = float(np.max(np.abs(lses[l][i:i + 1, heads] - ref_lse[:, heads])))
+                say(f"layer {l} query {i} heads {heads}: normwise {err:.3e} lse {lerr:.3e}")
+                assert err <= TOL, (l, i, err)
+                assert lerr <= TOL, (l, i, lerr)
+                worst = max(worst, err)
+            del K, V
+        say(f"{name}: worst normwise {worst:.3e}")
+    finally:
+        c.close()
