@@ -100,8 +100,8 @@ def timed_run(wl, st, steps, warmup):
     pool = st["pool"]
     run_steps(wl, st, warmup, stream)
     torch.cuda.synchronize()
-    pool.profile_read(0, reset=True)
-    pool.profile_read(1, reset=True)
+    for kind in (0, 1, 2):
+        pool.profile_read(kind, reset=True)
     pool.profile_enable(True)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -115,8 +115,10 @@ def timed_run(wl, st, steps, warmup):
     ms = e0.elapsed_time(e1) / steps
     n_att, ms_att = pool.profile_read(0, reset=True)
     n_cmb, ms_cmb = pool.profile_read(1, reset=True)
+    n_stg, ms_stg = pool.profile_read(2, reset=True)
     return dict(ms_per_step=ms, wall_ms_per_step=wall * 1e3 / steps, attn_launches=n_att,
-                attn_ms_total=ms_att, combine_launches=n_cmb, combine_ms_total=ms_cmb)
+                attn_ms_total=ms_att, combine_launches=n_cmb, combine_ms_total=ms_cmb,
+                stage_launches=n_stg, stage_ms_total=ms_stg, steps=steps)
 
 
 def graph_run(wl, st, steps, warmup):
@@ -202,12 +204,18 @@ def multi_leg(name, cfg_kw, threads, link, steps, kind):
     r = timed_run(rwl, rst, 5, 2)
     rst["pool"].close()
     del rst
-    avg = r["attn_ms_total"] / max(1, r["attn_launches"])
+    # per layer: the attention launches plus, for wide blocks, the staging
+    # launches that convert each page once into matrix-core operands
+    layers_timed = r["steps"] * wl.n_layers
+    avg = (r["attn_ms_total"] + r["stage_ms_total"]) / max(1, layers_timed)
     layer_bytes = wl.n_pages * pb
     flops = 4 * wl.n_q_heads * wl.head_dim * allowed_keys(wl)
-    k = {"kernel": f"mfma_kernel<{2 if kind == 'verify' else 4}> (all pages resident, one launch per layer)",
-         "avg_launch_us": round(avg * 1e3, 2), "launches": r["attn_launches"],
-         "bytes_per_launch": layer_bytes, "flops_per_launch": flops,
+    staged = r["stage_launches"] > 0
+    k = {"kernel": f"mfma_kernel<{2 if kind == 'verify' else 4}{', staged' if staged else ''}>"
+                   f"{' + stage_kernel' if staged else ''} (all pages resident)",
+         "avg_layer_us": round(avg * 1e3, 2), "attn_launches": r["attn_launches"],
+         "stage_launches": r["stage_launches"], "stage_us_per_layer": round(r["stage_ms_total"] / max(1, layers_timed) * 1e3, 2),
+         "bytes_per_layer": layer_bytes, "flops_per_layer": flops,
          "achieved_gbs": round(layer_bytes / (avg / 1e3) / 1e9, 1),
          "achieved_tflops": round(flops / (avg / 1e3) / 1e12, 1)}
     if kind == "verify":
@@ -216,7 +224,7 @@ def multi_leg(name, cfg_kw, threads, link, steps, kind):
         k.update(bound="mfma", frac=round(k["achieved_tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
                  peak=MFMA_F16_PEAK_TFLOPS, unit="TFLOP/s")
     out["resident_kernel"] = k
-    log(f"{name} all-resident: attention launch {avg * 1e3:.1f} us, {k['achieved_gbs']} GB/s, "
+    log(f"{name} all-resident: {avg * 1e3:.1f} us per layer, {k['achieved_gbs']} GB/s, "
         f"{k['achieved_tflops']} TFLOP/s")
     return out
 
@@ -411,7 +419,7 @@ def main():
         result["verify"] = multi_leg("spec_verify_160k", dict(ring_pages=16, chunk_pages=4, copy_streams=1,
                                                               group_pages=1), args.threads, link, 8, "verify")
         result["prefill"] = multi_leg("prefill_ubatch_128k", dict(ring_pages=32, chunk_pages=8, copy_streams=1,
-                                                                  group_pages=8), args.threads, link, 6, "prefill")
+                                                                  group_pages=4), args.threads, link, 6, "prefill")
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(wl, recs, qs_np)

@@ -18,6 +18,7 @@ constexpr int kVRow = kNB * kVBlock;         // 72 B
 constexpr int kKTile = kPageTokens * kKRow;  // 34816 B: one head's K for one page
 constexpr int kVTile = kPageTokens * kVRow;  // 18432 B
 constexpr int kPartStride = kHeadDim + 2;    // partial record: acc[128], m (log2 units), l
+constexpr int kStagedTile = 2 * kPageTokens * kHeadDim * 2;   // f16 K and V^T operands of one (page, kv head)
 
 // One run of consecutive logical pages of one split-K group, processed in
 // page order by one workgroup. flags bit 0: page0 is the group's first page
@@ -107,6 +108,17 @@ struct AttendArgs {
     float scale_log2;     // scale * log2(e): scores are kept in log2 units
     int32_t causal;
     float* part;          // [n_groups][n_q][Hq][kPartStride]
+    const uint8_t* staged; // staged operands of this launch's pages (null: convert in the kernel)
+};
+
+// Conversion of a launch's pages into staged operands (kvs_mfma.hip).
+struct StageArgs {
+    PageSource ps;
+    const Seg* segs;      // the launch's segments; their pages are staged in order
+    int32_t n_segs;
+    int32_t n_kv_heads;
+    int64_t n_kv;
+    uint8_t* staged;      // [pages][n_kv_heads][kStagedTile]
 };
 
 struct GatherArgs {
@@ -127,6 +139,8 @@ bool decode_supports(int rows);
 hipError_t launch_decode(const AttendArgs& a, hipStream_t stream);
 // matrix-core kernel (kvs_mfma.hip) for more rows
 hipError_t launch_mfma(const AttendArgs& a, hipStream_t stream);
+bool mfma_stages(int rows);   // rows per kv head for which launches stage their pages first
+hipError_t launch_stage(const StageArgs& a, int32_t n_pages, hipStream_t stream);
 hipError_t launch_combine(const float* part, int32_t n_groups, int32_t n_q, int32_t n_q_heads,
                           float* out, float* lse, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);

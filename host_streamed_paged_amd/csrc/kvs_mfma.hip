@@ -24,6 +24,14 @@
 // The running state (m, l, O) is updated once per page in page order from
 // state and page data alone, so results do not depend on how pages are split
 // into launches or which pages are resident.
+//
+// Staged mode, for blocks of more than 64 rows per kv head (a prefill
+// ubatch): every row tile would otherwise dequantize the same page again, so
+// stage_kernel first converts each (page, kv head) of the launch once into a
+// 128 KB tile of f16 MFMA operands in fragment order (K: [token tile][block]
+// [lane] x 16 B; V^T: [32-token chunk][channel tile][lane] x 16 B) with the
+// same code, and the attention kernel loads whole fragments from it. The
+// operands, and so the results, are the same bits either way.
 #include <hip/hip_runtime.h>
 #include <cstdint>
 #include <cmath>
@@ -50,7 +58,7 @@ constexpr float kLazyMax = 8.f;
 
 // One page's tiles. (Double-buffering them measured slower: the next page's
 // LDS DMA then competes with the QK reads of the current one.)
-template <int RT>
+template <int RT, bool STAGED>
 struct MfmaSmem {
     // K tile in record layout; once every wave is past QK it holds the P
     // operands [chunk][row tile][lane] (16 bytes each)
@@ -59,46 +67,184 @@ struct MfmaSmem {
     float red_m[kWaves][16 * RT];
     float red_l[kWaves][16 * RT];
 };
+template <int RT>
+struct MfmaSmem<RT, true> {
+    alignas(16) uint8_t k[kChunks * RT * 64 * 16];   // P operands only
+    float red_m[kWaves][16 * RT];
+    float red_l[kWaves][16 * RT];
+};
+
+constexpr int kStagedK = kPageTokens * kHeadDim * 2;   // f16 K operands of one (page, kv head)
+static_assert(2 * kStagedK == kStagedTile, "staged tile = K + V^T operands");
 
 __device__ inline half2_t as_h2(uint32_t x) { return __builtin_bit_cast(half2_t, x); }
 __device__ inline uint32_t as_u(half2_t x) { return __builtin_bit_cast(uint32_t, x); }
 
-// two workgroups per CU up to 2 row tiles; 4 row tiles need the whole
-// register file of a SIMD lane (256 arch + acc registers would spill)
-template <int RT>
-__global__ __launch_bounds__(kThreads, RT <= 2 ? 2 : 1) void mfma_kernel(AttendArgs a) {
+// Stage one (page, kv head) tile pair of a page record into LDS by LDS DMA:
+// wave-sized pieces of 1 KB, 34 for K and 18 for V.
+__device__ inline void dma_page_tiles(const uint8_t* rec, int g, int n_kv_heads, uint8_t* k_lds, uint8_t* v_lds,
+                                      int w, int lane) {
+    const uint8_t* kt = rec + (int64_t)g * kKTile;
+    const uint8_t* vt = rec + (int64_t)n_kv_heads * kKTile + (int64_t)g * kVTile;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+        const int piece = w + 4 * k;
+        if (piece < kKTile / 1024) dma16(kt + piece * 1024 + lane * 16, k_lds + piece * 1024);
+    }
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+        const int piece = w + 4 * k;
+        if (piece < kVTile / 1024) dma16(vt + piece * 1024 + lane * 16, v_lds + piece * 1024);
+    }
+}
+
+// K operand of v_mfma_f32_16x16x32_f16 for S^T = K . Q^T: this lane's 8 dims
+// [32 b + 8 gq, +8) of token `tok` of the K tile (record layout, in LDS),
+// each d * code rounded once to f16 (the code is converted exactly first).
+__device__ inline half8_t k_fragment(const uint8_t* k_lds, int tok, int b, int gq) {
+    const uint8_t* blk = k_lds + tok * kKRow + b * kKBlock;
+    uint32_t x0, x1;
+    if (b & 1) {   // codes start on a dword boundary
+        const uint32_t* p = (const uint32_t*)(blk + 2 + 8 * gq);
+        x0 = p[0];
+        x1 = p[1];
+    } else {       // codes start 2 bytes into a dword
+        const uint32_t* p = (const uint32_t*)(blk + 8 * gq);
+        const uint32_t y0 = p[0], y1 = p[1], y2 = p[2];
+        x0 = __builtin_amdgcn_alignbyte(y1, y0, 2);
+        x1 = __builtin_amdgcn_alignbyte(y2, y1, 2);
+    }
+    const uint32_t db = *(const uint16_t*)blk;
+    const half2_t d2 = as_h2(db | (db << 16));
+    const half2_t k_off = {(_Float16)1152.f, (_Float16)1152.f};   // 1024 + 128
+    const uint32_t c_hi64 = 0x64646464u;
+    // int8 code k -> f16 (1024 + (k + 128)) - 1152, exact; then * d
+    x0 ^= 0x80808080u;
+    x1 ^= 0x80808080u;
+    const half2_t e0 = (as_h2(__builtin_amdgcn_perm(c_hi64, x0, 0x04010400u)) - k_off) * d2;
+    const half2_t e1 = (as_h2(__builtin_amdgcn_perm(c_hi64, x0, 0x04030402u)) - k_off) * d2;
+    const half2_t e2 = (as_h2(__builtin_amdgcn_perm(c_hi64, x1, 0x04010400u)) - k_off) * d2;
+    const half2_t e3 = (as_h2(__builtin_amdgcn_perm(c_hi64, x1, 0x04030402u)) - k_off) * d2;
+    half8_t kop;
+    kop[0] = e0[0]; kop[1] = e0[1]; kop[2] = e1[0]; kop[3] = e1[1];
+    kop[4] = e2[0]; kop[5] = e2[1]; kop[6] = e3[0]; kop[7] = e3[1];
+    return kop;
+}
+
+// V^T operands of O^T += V^T . P^T for chunk c (tokens [32 c, 32 c + 32)) and
+// quant block b: vop[0] holds channel 32 b + n, vop[1] channel 32 b + 16 + n
+// (low and high nibbles of byte n), for the lane's 8 token slots: slot j of
+// lane group gq is token 32 c + 4 gq + j for j < 4, else 32 c + 12 + 4 gq + j.
+// Each value is d * (u - 8) rounded once to f16. TAIL zeroes rows at or past
+// `valid` (their scales may be NaN).
+template <bool TAIL>
+__device__ inline void v_fragments(const uint8_t* v_lds, int b, int c, int gq, int n, int valid,
+                                   uint32_t m_nib, uint32_t magic, half8_t (&vop)[2]) {
+    const half2_t v_off = {(_Float16)1032.f, (_Float16)1032.f};   // 1024 + 8
+    const uint8_t* vlane = v_lds + b * kVBlock + 4 * gq * kVRow;
+#pragma unroll
+    for (int jp = 0; jp < 4; ++jp) {
+        const int j0 = 2 * jp, j1 = 2 * jp + 1;
+        const int o0 = 32 * c + (j0 < 4 ? j0 : 12 + j0), o1 = 32 * c + (j1 < 4 ? j1 : 12 + j1);
+        const uint8_t* r0p = vlane + o0 * kVRow;
+        const uint8_t* r1p = vlane + o1 * kVRow;
+        uint32_t d0 = *(const uint16_t*)r0p, d1 = *(const uint16_t*)r1p;
+        if constexpr (TAIL) {
+            d0 = o0 + 4 * gq < valid ? d0 : 0u;
+            d1 = o1 + 4 * gq < valid ? d1 : 0u;
+        }
+        const half2_t dd = as_h2(d0 | (d1 << 16));
+        const uint32_t x = __builtin_amdgcn_perm((uint32_t)r1p[2 + n], (uint32_t)r0p[2 + n], 0x0c040c00u);
+        const half2_t lo = (as_h2((x & m_nib) | magic) - v_off) * dd;          // channel n
+        const half2_t hi = (as_h2(((x >> 4) & m_nib) | magic) - v_off) * dd;   // channel 16 + n
+        vop[0][j0] = lo[0]; vop[0][j1] = lo[1];
+        vop[1][j0] = hi[0]; vop[1][j1] = hi[1];
+    }
+}
+
+// Offsets of the staged operands of one (page, kv head) tile.
+__device__ inline int staged_k_offset(int tt16, int b, int lane) { return ((tt16 * kNB + b) * 64 + lane) * 16; }
+__device__ inline int staged_v_offset(int c, int ct, int lane) { return kStagedK + ((c * 8 + ct) * 64 + lane) * 16; }
+
+// Position of this launch's segment `seg_i` in the staged tiles: pages of the
+// launch's segments are staged in order.
+__device__ inline int staged_first_tile(const Seg* segs, int seg_i) {
+    int t = 0;
+    for (int i = 0; i < seg_i; ++i) t += scalar_load(&segs[i].npages);
+    return t;
+}
+
+// Workgroups per CU the register budget is cut for: up to 2 row tiles,
+// KVS_MFMA_OCC_NARROW; 4 row tiles need a SIMD lane's whole register file
+// (256 arch + acc registers), unless staged (no conversion temporaries).
+#ifndef KVS_MFMA_OCC_NARROW
+#define KVS_MFMA_OCC_NARROW 2
+#endif
+#ifndef KVS_MFMA_OCC_STAGED
+#define KVS_MFMA_OCC_STAGED 1
+#endif
+template <int RT, bool STAGED>
+__global__ __launch_bounds__(kThreads, RT <= 2 ? KVS_MFMA_OCC_NARROW : (STAGED ? KVS_MFMA_OCC_STAGED : 1))
+void mfma_kernel(AttendArgs a) {
     static_assert(kChunks * RT * 64 * 16 <= kKTile, "P operands must fit in the K tile");
-    __shared__ MfmaSmem<RT> sm;
-    if ((int)blockIdx.x >= a.n_segs) {   // ring refill workgroup
-        if (blockIdx.z == 0) copy_role(a.copy, ((int)blockIdx.x - a.n_segs) * (int)gridDim.y + (int)blockIdx.y);
+    __shared__ MfmaSmem<RT, STAGED> sm;
+    // 1-D grid: the ring refill workgroups first (so that they start at
+    // once), then the work items (segment, kv head, row tile) with the row tile
+    // fastest. Workgroups go to the 8 XCDs round-robin by linear index; the
+    // work is permuted so that each XCD takes a contiguous range of work items,
+    // and the row tiles of one (segment, kv head), which read the same pages,
+    // run together on one XCD and share its L2.
+    const int G = a.G, R = a.n_q * G;
+    const int n_rt = (R + 16 * RT - 1) / (16 * RT);
+    const int n_copy8 = (copy_workgroups(a.copy) + 7) & ~7;
+    const int L = (int)blockIdx.x;
+    if (L < n_copy8) {   // ring refill workgroup
+        copy_role(a.copy, L);
         return;
     }
+    const int n_work = a.n_segs * a.n_kv_heads * n_rt;
+    const int per_xcd = ((n_work + 7) & ~7) / 8;
+    const int work = ((L - n_copy8) & 7) * per_xcd + ((L - n_copy8) >> 3);
+    if (work >= n_work) return;
+    const int seg_i = work / (n_rt * a.n_kv_heads);
+    const int g = (work / n_rt) % a.n_kv_heads;
+    const int r0 = (work % n_rt) * 16 * RT;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int n = lane & 15, gq = lane >> 4;   // MFMA row/column index and lane group
     typedef int int4v __attribute__((ext_vector_type(4)));
-    const int4v segv = scalar_load((const int4v*)(a.segs + blockIdx.x));
+    const int4v segv = scalar_load((const int4v*)(a.segs + seg_i));
     const Seg seg = {segv.x, segv.y, segv.z, segv.w};
-    const int g = blockIdx.y;
-    const int G = a.G, R = a.n_q * G;
-    const int r0 = blockIdx.z * 16 * RT;
 
     auto issue_page = [&](int page) {
-        const uint8_t* rec = page_record(a.ps, page);
-        const uint8_t* kt = rec + (int64_t)g * kKTile;
-        const uint8_t* vt = rec + (int64_t)a.n_kv_heads * kKTile + (int64_t)g * kVTile;
-        // wave-sized pieces of 1 KB: 34 for K, 18 for V
-#pragma unroll
-        for (int k = 0; k < 9; ++k) {
-            const int piece = w + 4 * k;
-            if (piece < kKTile / 1024) dma16(kt + piece * 1024 + lane * 16, sm.k + piece * 1024);
-        }
-#pragma unroll
-        for (int k = 0; k < 5; ++k) {
-            const int piece = w + 4 * k;
-            if (piece < kVTile / 1024) dma16(vt + piece * 1024 + lane * 16, sm.v + piece * 1024);
-        }
+        if constexpr (!STAGED) dma_page_tiles(page_record(a.ps, page), g, a.n_kv_heads, sm.k, sm.v, w, lane);
     };
     issue_page(seg.page0);
+    // staged operands of this segment's first page, for kv head g
+    const uint8_t* stile = nullptr;
+    if constexpr (STAGED)
+        stile = a.staged + ((int64_t)staged_first_tile(a.segs, seg_i) * a.n_kv_heads + g) * kStagedTile;
+    // staged operands are software-pipelined through registers: the K
+    // fragments of page p + 1 are loaded while page p computes P.V, and the V
+    // fragments of page p run a few 32-token chunks ahead of their use
+    const int64_t tile_step = (int64_t)a.n_kv_heads * kStagedTile;
+    half8_t kf[STAGED ? 4 : 1][kNB], vf[STAGED ? kChunks : 1][2];
+    constexpr int kKAhead = 2;   // token tiles of the next page loaded during P.V
+    auto load_k = [&](const uint8_t* pt, int tt0, int tt1) {
+        if constexpr (STAGED) {
+#pragma unroll
+            for (int tt = tt0; tt < tt1; ++tt)
+#pragma unroll
+                for (int b = 0; b < kNB; ++b) kf[tt][b] = *(const half8_t*)(pt + staged_k_offset(4 * w + tt, b, lane));
+        }
+    };
+    constexpr int kVAhead = 4;   // V chunks in flight ahead of the one consumed
+    auto load_v = [&](const uint8_t* pt, int c) {
+        if constexpr (STAGED) {
+            vf[c][0] = *(const half8_t*)(pt + staged_v_offset(c, 2 * w, lane));
+            vf[c][1] = *(const half8_t*)(pt + staged_v_offset(c, 2 * w + 1, lane));
+        }
+    };
+    if constexpr (STAGED) load_k(stile, 0, kKAhead);
 
     // ---- this lane's query rows (one per row tile) and their visible prefix
     half8_t qop[RT][kNB];
@@ -166,9 +312,6 @@ __global__ __launch_bounds__(kThreads, RT <= 2 ? 2 : 1) void mfma_kernel(AttendA
         }
     }
 
-    const uint32_t c_hi64 = 0x64646464u;
-    const half2_t k_off = {(_Float16)1152.f, (_Float16)1152.f};   // 1024 + 128
-    const half2_t v_off = {(_Float16)1032.f, (_Float16)1032.f};   // 1024 + 8
     const uint32_t m_nib = vconst(0x000F000Fu), magic = vconst(0x64006400u);
 
     // smallest visible prefix over the workgroup's rows (causal limits grow
@@ -193,8 +336,15 @@ __global__ __launch_bounds__(kThreads, RT <= 2 ? 2 : 1) void mfma_kernel(AttendA
         const int64_t vx = a.n_kv - base_tok;
         const int valid = (int)(vx < 0 ? 0 : (vx > kPageTokens ? kPageTokens : vx));   // cached rows of the page
 
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        lds_barrier();   // the page's tiles are in LDS for every wave
+        if constexpr (!STAGED) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            lds_barrier();   // the page's tiles are in LDS for every wave
+        }
+        if constexpr (STAGED) {
+            load_k(stile + pi * tile_step, kKAhead, 4);
+#pragma unroll
+            for (int c = 0; c < kVAhead; ++c) load_v(stile + pi * tile_step, c);
+        }
 
         // ---- QK over this wave's 64 tokens
         f32x4 s[4][RT];
@@ -202,33 +352,13 @@ __global__ __launch_bounds__(kThreads, RT <= 2 ? 2 : 1) void mfma_kernel(AttendA
         for (int tt = 0; tt < 4; ++tt) {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) s[tt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const uint8_t* krow = sm.k + (kTokW * w + 16 * tt + n) * kKRow;
 #pragma unroll
             for (int b = 0; b < kNB; ++b) {
-                const uint8_t* blk = krow + b * kKBlock;
-                uint32_t x0, x1;
-                if (b & 1) {   // codes start on a dword boundary
-                    const uint32_t* p = (const uint32_t*)(blk + 2 + 8 * gq);
-                    x0 = p[0];
-                    x1 = p[1];
-                } else {       // codes start 2 bytes into a dword
-                    const uint32_t* p = (const uint32_t*)(blk + 8 * gq);
-                    const uint32_t y0 = p[0], y1 = p[1], y2 = p[2];
-                    x0 = __builtin_amdgcn_alignbyte(y1, y0, 2);
-                    x1 = __builtin_amdgcn_alignbyte(y2, y1, 2);
-                }
-                const uint32_t db = *(const uint16_t*)blk;
-                const half2_t d2 = as_h2(db | (db << 16));
-                // int8 code k -> f16 (1024 + (k + 128)) - 1152, exact; then * d
-                x0 ^= 0x80808080u;
-                x1 ^= 0x80808080u;
                 half8_t kop;
-                const half2_t e0 = (as_h2(__builtin_amdgcn_perm(c_hi64, x0, 0x04010400u)) - k_off) * d2;
-                const half2_t e1 = (as_h2(__builtin_amdgcn_perm(c_hi64, x0, 0x04030402u)) - k_off) * d2;
-                const half2_t e2 = (as_h2(__builtin_amdgcn_perm(c_hi64, x1, 0x04010400u)) - k_off) * d2;
-                const half2_t e3 = (as_h2(__builtin_amdgcn_perm(c_hi64, x1, 0x04030402u)) - k_off) * d2;
-                kop[0] = e0[0]; kop[1] = e0[1]; kop[2] = e1[0]; kop[3] = e1[1];
-                kop[4] = e2[0]; kop[5] = e2[1]; kop[6] = e3[0]; kop[7] = e3[1];
+                if constexpr (STAGED)
+                    kop = kf[tt][b];
+                else
+                    kop = k_fragment(sm.k, kTokW * w + 16 * tt + n, b, gq);
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
                     s[tt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[rt][b], s[tt][rt], 0, 0, 0);
@@ -312,30 +442,21 @@ __global__ __launch_bounds__(kThreads, RT <= 2 ? 2 : 1) void mfma_kernel(AttendA
                 for (int ct = 0; ct < 2; ++ct) o[ct][rt] *= alpha[rt];
         }
 
-        // ---- P.V for channels 32 w .. 32 w + 31 (V quant block w). The lane's
-        // V rows: tokens 32 c + 4 gq + {0..3} and 32 c + 16 + 4 gq + {0..3}.
-        const uint8_t* vlane = sm.v + w * kVBlock + 4 * gq * kVRow;
+        if constexpr (STAGED) {
+            if (pi + 1 < seg.npages) load_k(stile + (pi + 1) * tile_step, 0, kKAhead);
+        }
+
+        // ---- P.V for channels 32 w .. 32 w + 31 (V quant block w)
         auto pv_page = [&](auto tail) {
 #pragma unroll
             for (int c = 0; c < kChunks; ++c) {
                 half8_t vop[2];
-#pragma unroll
-                for (int jp = 0; jp < 4; ++jp) {
-                    const int j0 = 2 * jp, j1 = 2 * jp + 1;
-                    const int o0 = 32 * c + (j0 < 4 ? j0 : 12 + j0), o1 = 32 * c + (j1 < 4 ? j1 : 12 + j1);
-                    const uint8_t* r0p = vlane + o0 * kVRow;
-                    const uint8_t* r1p = vlane + o1 * kVRow;
-                    uint32_t d0 = *(const uint16_t*)r0p, d1 = *(const uint16_t*)r1p;
-                    if constexpr (decltype(tail)::value) {   // rows past the cache may hold NaN scales
-                        d0 = o0 + 4 * gq < valid ? d0 : 0u;
-                        d1 = o1 + 4 * gq < valid ? d1 : 0u;
-                    }
-                    const half2_t dd = as_h2(d0 | (d1 << 16));
-                    const uint32_t x = __builtin_amdgcn_perm((uint32_t)r1p[2 + n], (uint32_t)r0p[2 + n], 0x0c040c00u);
-                    const half2_t lo = (as_h2((x & m_nib) | magic) - v_off) * dd;          // channel n
-                    const half2_t hi = (as_h2(((x >> 4) & m_nib) | magic) - v_off) * dd;   // channel 16 + n
-                    vop[0][j0] = lo[0]; vop[0][j1] = lo[1];
-                    vop[1][j0] = hi[0]; vop[1][j1] = hi[1];
+                if constexpr (STAGED) {
+                    vop[0] = vf[c][0];
+                    vop[1] = vf[c][1];
+                    if (c + kVAhead < kChunks) load_v(stile + pi * tile_step, c + kVAhead);
+                } else {
+                    v_fragments<decltype(tail)::value>(sm.v, w, c, gq, n, valid, m_nib, magic, vop);
                 }
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
@@ -345,10 +466,12 @@ __global__ __launch_bounds__(kThreads, RT <= 2 ? 2 : 1) void mfma_kernel(AttendA
                 }
             }
         };
-        if (tail_page) pv_page(std::true_type{});
+        if (!STAGED && tail_page) pv_page(std::true_type{});
         else pv_page(std::false_type{});
-        lds_barrier();   // every wave is done with this page's tiles
-        if (pi + 1 < seg.npages) issue_page(page + 1);
+        if constexpr (!STAGED) {
+            lds_barrier();   // every wave is done with this page's tiles
+            if (pi + 1 < seg.npages) issue_page(page + 1);
+        }
     }
 
     // ---- group state -> partial records
@@ -369,12 +492,53 @@ __global__ __launch_bounds__(kThreads, RT <= 2 ? 2 : 1) void mfma_kernel(AttendA
     }
 }
 
-template <int RT>
+// Converts each (page, kv head) of a launch once into f16 MFMA operands (the
+// staged mode above). Grid: (pages of the launch, kv heads); block x stages
+// the x-th page of the launch's segments, in segment order.
+__global__ __launch_bounds__(kThreads) void stage_kernel(StageArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t k_lds[kKTile];
+    __shared__ __attribute__((aligned(16))) uint8_t v_lds[kVTile];
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int n = lane & 15, gq = lane >> 4;
+    const int slot = blockIdx.x, g = blockIdx.y;
+    int rem = slot;
+    int32_t page = -1;
+    for (int si = 0; si < a.n_segs; ++si) {
+        const int np = scalar_load(&a.segs[si].npages);
+        if (rem < np) { page = scalar_load(&a.segs[si].page0) + rem; break; }
+        rem -= np;
+    }
+    if (page < 0) return;   // past the launch's pages
+    dma_page_tiles(page_record(a.ps, page), g, a.n_kv_heads, k_lds, v_lds, w, lane);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+    uint8_t* tile = a.staged + ((int64_t)slot * a.n_kv_heads + g) * kStagedTile;
+    // K: wave w converts token tiles 4 w .. 4 w + 3, as the QK role does
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int b = 0; b < kNB; ++b)
+            *(half8_t*)(tile + staged_k_offset(4 * w + tt, b, lane)) = k_fragment(k_lds, kTokW * w + 16 * tt + n, b, gq);
+    // V: wave w converts block w (channel tiles 2 w, 2 w + 1), as the PV role does
+    const int64_t vx = a.n_kv - (int64_t)page * kPageTokens;
+    const int valid = (int)(vx < 0 ? 0 : (vx > kPageTokens ? kPageTokens : vx));
+    const uint32_t m_nib = vconst(0x000F000Fu), magic = vconst(0x64006400u);
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+        half8_t vop[2];
+        v_fragments<true>(v_lds, w, c, gq, n, valid, m_nib, magic, vop);
+        *(half8_t*)(tile + staged_v_offset(c, 2 * w, lane)) = vop[0];
+        *(half8_t*)(tile + staged_v_offset(c, 2 * w + 1, lane)) = vop[1];
+    }
+}
+
+template <int RT, bool STAGED>
 hipError_t launch_rt(const AttendArgs& a, hipStream_t stream) {
     const int R = a.n_q * a.G;
-    const int cx = (copy_workgroups(a.copy) + a.n_kv_heads - 1) / a.n_kv_heads;
-    const dim3 grid(a.n_segs + cx, a.n_kv_heads, (R + 16 * RT - 1) / (16 * RT));
-    hipLaunchKernelGGL(mfma_kernel<RT>, grid, dim3(kThreads), 0, stream, a);
+    const int64_t n_work = (int64_t)a.n_segs * a.n_kv_heads * ((R + 16 * RT - 1) / (16 * RT));
+    const int64_t blocks = ((copy_workgroups(a.copy) + 7) & ~7) + ((n_work + 7) & ~7);
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((mfma_kernel<RT, STAGED>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -382,12 +546,26 @@ hipError_t launch_rt(const AttendArgs& a, hipStream_t stream) {
 
 // Row tile width by query rows per kv head: 16 (verify-sized blocks up to 16
 // rows), 32, else 64 rows per workgroup.
+#ifndef KVS_MFMA_STAGED_RT
+#define KVS_MFMA_STAGED_RT 2   // row tiles per workgroup on staged operands
+#endif
+
+// Staged operands (a.staged) are used for blocks of more than 64 rows.
 hipError_t launch_mfma(const AttendArgs& a, hipStream_t stream) {
     if (a.n_segs <= 0 && copy_workgroups(a.copy) == 0) return hipSuccess;
     const int R = a.n_q * a.G;
-    if (R <= 16) return launch_rt<1>(a, stream);
-    if (R <= 32) return launch_rt<2>(a, stream);
-    return launch_rt<4>(a, stream);
+    if (a.staged) return launch_rt<KVS_MFMA_STAGED_RT, true>(a, stream);
+    if (R <= 16) return launch_rt<1, false>(a, stream);
+    if (R <= 32) return launch_rt<2, false>(a, stream);
+    return launch_rt<4, false>(a, stream);
+}
+
+bool mfma_stages(int rows) { return rows > 64; }
+
+hipError_t launch_stage(const StageArgs& a, int32_t n_pages, hipStream_t stream) {
+    if (n_pages <= 0) return hipSuccess;
+    hipLaunchKernelGGL(stage_kernel, dim3(n_pages, a.n_kv_heads), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
 }
 
 }  // namespace kvs

@@ -51,7 +51,9 @@ struct Layout {
     uint64_t seg_bytes = 0;    // per layer
     int32_t max_segs = 0;      // per layer
     int32_t max_groups = 0;
-    uint64_t fixed = 0;        // ring + work + tables
+    int32_t stage_pages = 0;   // pages per staging region (0: blocks never wide enough to stage)
+    uint64_t stage_bytes = 0;  // two staging regions, one per compute lane
+    uint64_t fixed = 0;        // ring + work + staging + tables
 };
 
 int validate(const kvs_config* c) {
@@ -91,7 +93,14 @@ Layout layout_of(const kvs_config* c) {
     L.max_segs = 2 * L.max_groups + c->max_pages + 1;
     L.src_bytes = align256((uint64_t)c->max_pages * sizeof(int32_t));
     L.seg_bytes = align256((uint64_t)L.max_segs * sizeof(kvs::Seg));
-    L.fixed = L.ring_bytes + L.work_bytes + (uint64_t)c->n_layers * (L.src_bytes + L.seg_bytes);
+    // staged operands for blocks wider than 64 rows per kv head: a launch's
+    // pages are staged in runs of at most stage_pages (a segment never spans
+    // more than group_pages pages)
+    if (kvs::mfma_stages(c->max_q_tokens * (c->n_q_heads / c->n_kv_heads))) {
+        L.stage_pages = std::max(64, c->group_pages);
+        L.stage_bytes = 2 * align256((uint64_t)L.stage_pages * c->n_kv_heads * kvs::kStagedTile);
+    }
+    L.fixed = L.ring_bytes + L.work_bytes + L.stage_bytes + (uint64_t)c->n_layers * (L.src_bytes + L.seg_bytes);
     return L;
 }
 
@@ -127,6 +136,7 @@ struct kvs_pool {
     uint64_t budget = 0;
     uint8_t* ring = nullptr;
     float* work = nullptr;
+    uint8_t* staged[2] = {nullptr, nullptr};   // staging regions of the caller's stream and of the lane
     uint8_t* slots = nullptr;
     int64_t n_slots = 0;
     std::vector<int32_t> slot_free;  // stack of free slot ids
@@ -145,8 +155,8 @@ struct kvs_pool {
     kvs_status_info st{};
     // kernel timing (kvs_profile_*): per kind, event pairs in launch order
     bool profiling = false;
-    std::vector<std::pair<hipEvent_t, hipEvent_t>> prof_ev[2];
-    size_t prof_used[2] = {0, 0};
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> prof_ev[3];
+    size_t prof_used[3] = {0, 0, 0};
 };
 
 namespace {
@@ -524,6 +534,11 @@ int kvs_pool_create(const kvs_config* cfg, void* dev_arena, uint64_t budget_byte
     uint8_t* cur = p->arena;
     p->ring = cur; cur += L.ring_bytes;
     p->work = (float*)cur; cur += L.work_bytes;
+    if (L.stage_bytes) {
+        p->staged[0] = cur;
+        p->staged[1] = cur + L.stage_bytes / 2;
+        cur += L.stage_bytes;
+    }
     p->layers.resize(cfg->n_layers);
     for (auto& ls : p->layers) {
         ls.dev_src = (int32_t*)cur; cur += L.src_bytes;
@@ -692,16 +707,45 @@ int kvs_attend(kvs_pool* p, int32_t layer, const void* q, int32_t q_dtype, int32
     a.scale_log2 = scale * 1.44269504088896340736f;
     a.causal = causal ? 1 : 0;
     a.part = p->work;
+    const bool staging = kvs::mfma_stages(n_q * a.G);
     rc = run_layer(p, layer, s, [&](hipStream_t st, int32_t seg0, int32_t nseg, const uint8_t* ring_chunk, int32_t rank0,
                                     const kvs::CopyJob& cj) -> int {
         kvs::AttendArgs b = a;
         b.copy = cj;
         b.ps.ring_chunk = ring_chunk;
         b.ps.chunk_rank0 = rank0;
-        b.segs = ls.dev_segs + seg0;
-        b.n_segs = nseg;
-        hipError_t e = timed(p, 0, st, [&] { return kvs::launch_attend(b, st); });
-        return e == hipSuccess ? KVS_OK : fail(KVS_ERR_HIP, "attention kernel launch failed: %s", hipGetErrorString(e));
+        if (!staging || nseg == 0) {
+            b.segs = ls.dev_segs + seg0;
+            b.n_segs = nseg;
+            hipError_t e = timed(p, 0, st, [&] { return kvs::launch_attend(b, st); });
+            return e == hipSuccess ? KVS_OK : fail(KVS_ERR_HIP, "attention kernel launch failed: %s", hipGetErrorString(e));
+        }
+        // staged: runs of segments of at most stage_pages pages; each run is
+        // converted into the lane's staging region, then attended
+        uint8_t* region = p->staged[st == p->lane ? 1 : 0];
+        for (int32_t i = seg0; i < seg0 + nseg;) {
+            int32_t j = i, pages = 0;
+            while (j < seg0 + nseg && pages + ls.segs[j].npages <= p->L.stage_pages) pages += ls.segs[j++].npages;
+            if (j == i) return fail(KVS_ERR_INVALID_ARG, "internal: segment longer than the staging region");
+            kvs::StageArgs sa{};
+            sa.ps = b.ps;
+            sa.segs = ls.dev_segs + i;
+            sa.n_segs = j - i;
+            sa.n_kv_heads = p->cfg.n_kv_heads;
+            sa.n_kv = n_kv;
+            sa.staged = region;
+            hipError_t e = timed(p, 2, st, [&] { return kvs::launch_stage(sa, pages, st); });
+            if (e != hipSuccess) return fail(KVS_ERR_HIP, "staging kernel launch failed: %s", hipGetErrorString(e));
+            kvs::AttendArgs c = b;
+            if (i != seg0) c.copy = kvs::CopyJob{};   // the ring refill rides with the first run
+            c.segs = ls.dev_segs + i;
+            c.n_segs = j - i;
+            c.staged = region;
+            e = timed(p, 0, st, [&] { return kvs::launch_attend(c, st); });
+            if (e != hipSuccess) return fail(KVS_ERR_HIP, "attention kernel launch failed: %s", hipGetErrorString(e));
+            i = j;
+        }
+        return KVS_OK;
     });
     if (rc) return rc;
     hipError_t e = timed(p, 1, s, [&] { return kvs::launch_combine(p->work, ls.n_groups, n_q, p->cfg.n_q_heads, out, lse, s); });
@@ -776,7 +820,7 @@ int kvs_profile_enable(kvs_pool* p, int32_t enable) {
 
 int kvs_profile_read(kvs_pool* p, int32_t kind, int64_t* launches, double* total_ms, int32_t reset) {
     if (!p || !launches || !total_ms) return fail(KVS_ERR_INVALID_ARG, "NULL argument");
-    if (kind < 0 || kind > 1) return fail(KVS_ERR_INVALID_ARG, "kind %d unknown", kind);
+    if (kind < 0 || kind > 2) return fail(KVS_ERR_INVALID_ARG, "kind %d unknown", kind);
     double ms = 0.0;
     for (size_t i = 0; i < p->prof_used[kind]; ++i) {
         auto& pr = p->prof_ev[kind][i];

@@ -136,8 +136,12 @@ int kvs_config_validate(const kvs_config* cfg);
 uint64_t kvs_page_bytes(const kvs_config* cfg);
 
 /* Smallest budget kvs_pool_create accepts for cfg, written to *out: the ring,
- * the split-K workspace (max_q_tokens x n_q_heads rows per page group) and the
- * per-layer tables, each rounded up to 256 bytes. Pure. */
+ * the split-K workspace (max_q_tokens x n_q_heads rows per page group), the
+ * staging regions and the per-layer tables, each rounded up to 256 bytes.
+ * Staging regions exist only when a query block can exceed 64 rows per kv
+ * head (max_q_tokens x n_q_heads / n_kv_heads > 64, a prefill ubatch): two of
+ * max(64, group_pages) pages x n_kv_heads x 128 KiB, where each launch first
+ * converts its pages once into f16 matrix-core operands. Pure. */
 int kvs_min_budget_bytes(const kvs_config* cfg, uint64_t* out);
 
 /* Number of resident page slots a budget yields for cfg (0 if below the
@@ -247,8 +251,9 @@ int kvs_debug_gather(kvs_pool* pool, int32_t layer, int64_t tok0, int64_t n_tok,
 int kvs_debug_read_page(kvs_pool* pool, int32_t layer, int32_t page, void* dst_host);
 
 /* Kernel timing. With enable != 0, kvs_attend brackets every attention kernel
- * launch (kind 0) and every split-K combine launch (kind 1) with timing
- * events recorded on the compute stream it was given. kvs_profile_read waits
+ * launch (kind 0), every split-K combine launch (kind 1) and every staging
+ * launch of a wide query block (kind 2) with timing events recorded on the
+ * stream the launch runs on. kvs_profile_read waits
  * for the recorded events and returns the number of timed launches of that
  * kind and their summed duration in milliseconds; reset != 0 clears the
  * record. At most 65536 launches per kind are kept (later ones are not timed). */
