@@ -32,36 +32,39 @@ __device__ inline float f16_bits_to_float(uint32_t bits) {
 }
 
 // ---------------------------------------------------------------------------
-// Split-K combine: one workgroup per (query token x head, 16-channel slice);
-// 256 threads = 16 channels x 16 group slices. Each thread walks groups
-// sl, sl + 16, ... in batches of 8 independent loads with an online
-// log-sum-exp merge; the 16 slices are then merged in a fixed order. The order
-// depends only on the number of groups, never on scheduling or residency.
+// Split-K combine: one workgroup per output row (query token x head), 16
+// waves. Wave s folds groups s, s + 16, s + 32, ... into a running
+// log-sum-exp state, 8 groups per step so that 8 record loads are in flight;
+// lane i owns channels 2i and 2i + 1 (one 8-byte load per record, so a wave
+// reads a 512-byte record in one coalesced access). The 16 wave states are
+// then merged in wave order. The order depends only on the number of groups,
+// never on scheduling or residency.
 // ---------------------------------------------------------------------------
-constexpr int kCombSlices = 16;
-constexpr int kCombCh = 16;
+constexpr int kCombWaves = 16;
 constexpr int kCombBatch = 8;
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part, int32_t n_groups,
-                                                      int32_t rows, float* __restrict__ out,
-                                                      float* __restrict__ lse) {
-    __shared__ float so[kCombSlices][kCombCh + 1];
-    __shared__ float sm_[kCombSlices], sl_[kCombSlices];
-    const int row = blockIdx.x / (kHeadDim / kCombCh), slice = blockIdx.x % (kHeadDim / kCombCh);
-    const int cl = threadIdx.x & (kCombCh - 1), sl = threadIdx.x / kCombCh;
-    const int c = slice * kCombCh + cl;
+__global__ __launch_bounds__(64 * kCombWaves) void combine_kernel(const float* __restrict__ part, int32_t n_groups,
+                                                                  int32_t rows, float* __restrict__ out,
+                                                                  float* __restrict__ lse) {
+    __shared__ float2 so[kCombWaves][64];
+    __shared__ float sm_[kCombWaves], sl_[kCombWaves];
+    const int row = blockIdx.x;
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t gstride = (int64_t)rows * kPartStride;
     const float* p = part + (int64_t)row * kPartStride;
-    float M = -INFINITY, L = 0.f, O = 0.f;
-    for (int g0 = sl; g0 < n_groups; g0 += kCombSlices * kCombBatch) {
-        float mg[kCombBatch], lg[kCombBatch], og[kCombBatch];
+    float M = -INFINITY, L = 0.f;
+    float2 O = make_float2(0.f, 0.f);
+    for (int g0 = wv; g0 < n_groups; g0 += kCombWaves * kCombBatch) {
+        float mg[kCombBatch], lg[kCombBatch];
+        float2 og[kCombBatch];
 #pragma unroll
         for (int k = 0; k < kCombBatch; ++k) {
-            const int gi = g0 + k * kCombSlices;
+            const int gi = g0 + k * kCombWaves;
             const bool ok = gi < n_groups;
             const float* q = p + (int64_t)(ok ? gi : 0) * gstride;
-            mg[k] = ok ? q[kHeadDim] : -INFINITY;
-            lg[k] = q[kHeadDim + 1];
-            og[k] = q[c];
+            const float2 ml = *(const float2*)(q + kHeadDim);
+            mg[k] = ok ? ml.x : -INFINITY;
+            lg[k] = ml.y;
+            og[k] = *(const float2*)(q + 2 * lane);
         }
         float Mb = M;
 #pragma unroll
@@ -69,34 +72,39 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         if (Mb == -INFINITY) continue;
         const float sc = (M == -INFINITY) ? 0.f : exp2f(M - Mb);
         L *= sc;
-        O *= sc;
+        O.x *= sc;
+        O.y *= sc;
 #pragma unroll
         for (int k = 0; k < kCombBatch; ++k) {
             const float w = (mg[k] == -INFINITY) ? 0.f : exp2f(mg[k] - Mb);
             L = fmaf(lg[k], w, L);
-            O = fmaf(og[k], w, O);
+            O.x = fmaf(og[k].x, w, O.x);
+            O.y = fmaf(og[k].y, w, O.y);
         }
         M = Mb;
     }
-    so[sl][cl] = O;
-    if (cl == 0) { sm_[sl] = M; sl_[sl] = L; }
+    so[wv][lane] = O;
+    if (lane == 0) { sm_[wv] = M; sl_[wv] = L; }
     __syncthreads();
-    if (sl == 0) {
+    if (wv == 0) {
         float Mt = sm_[0];
 #pragma unroll
-        for (int k = 1; k < kCombSlices; ++k) Mt = fmaxf(Mt, sm_[k]);
-        float ot = 0.f, lt = 0.f;
+        for (int k = 1; k < kCombWaves; ++k) Mt = fmaxf(Mt, sm_[k]);
+        float2 ot = make_float2(0.f, 0.f);
+        float lt = 0.f;
         if (Mt != -INFINITY) {
 #pragma unroll
-            for (int k = 0; k < kCombSlices; ++k) {
+            for (int k = 0; k < kCombWaves; ++k) {
                 const float w = (sm_[k] == -INFINITY) ? 0.f : exp2f(sm_[k] - Mt);
-                ot = fmaf(so[k][cl], w, ot);
+                ot.x = fmaf(so[k][lane].x, w, ot.x);
+                ot.y = fmaf(so[k][lane].y, w, ot.y);
                 lt = fmaf(sl_[k], w, lt);
             }
         }
-        out[(int64_t)row * kHeadDim + c] = (Mt == -INFINITY) ? 0.f : ot / lt;
-        if (lse && slice == 0 && cl == 0)
-            lse[row] = (Mt == -INFINITY) ? -INFINITY : (Mt + log2f(lt)) * 0.69314718055994530942f;
+        const bool empty = Mt == -INFINITY;
+        *(float2*)(out + (int64_t)row * kHeadDim + 2 * lane) = empty ? make_float2(0.f, 0.f)
+                                                                      : make_float2(ot.x / lt, ot.y / lt);
+        if (lse && lane == 0) lse[row] = empty ? -INFINITY : (Mt + log2f(lt)) * 0.69314718055994530942f;
     }
 }
 
@@ -155,7 +163,7 @@ hipError_t launch_combine(const float* part, int32_t n_groups, int32_t n_q, int3
                           float* out, float* lse, hipStream_t stream) {
     const int rows = n_q * n_q_heads;
     if (rows <= 0) return hipSuccess;
-    hipLaunchKernelGGL(combine_kernel, dim3(rows * (kHeadDim / kCombCh)), dim3(256), 0, stream, part, n_groups, rows, out, lse);
+    hipLaunchKernelGGL(combine_kernel, dim3(rows), dim3(64 * kCombWaves), 0, stream, part, n_groups, rows, out, lse);
     return hipGetLastError();
 }
 
