@@ -46,22 +46,22 @@ __device__ inline float f16_lo_to_float(uint32_t bits) {
 
 // lane i receives lane (i ^ 1) / (i ^ 2) of its quad
 __device__ inline float dpp_xor1(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
 }
 __device__ inline float dpp_xor2(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
 }
 // value of lane (4 * (i / 4) + SRC) of each quad
 template <int SRC>
 __device__ inline float quad_bcast(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), SRC * 0x55, 0xF, 0xF, true));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), SRC * 0x55, 0xF, 0xF, true));
 }
 // lane i receives lane i +- 4 / 8 within its row of 16 (row rotate)
 __device__ inline float dpp_ror4(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, true));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x124, 0xF, 0xF, true));
 }
 __device__ inline float dpp_ror8(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, true));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128, 0xF, 0xF, true));
 }
 // max / sum over the 16 lanes of a wave that share (lane & 3)
 __device__ inline float max_over_tokens(float v) {
@@ -265,6 +265,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
 
         // ---- scores. Slice row t is visible to query row r iff t <= lim[r].
         int lim[R];
+        bool need_mask = false;   // wave-uniform: some row does not see the whole slice
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             int64_t l64 = (int64_t)valid - 1;
@@ -273,6 +274,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
                 l64 = c < l64 ? c : l64;
             }
             lim[r] = (int)(l64 < -1 ? -1 : l64);
+            need_mask |= lim[r] < kSlice - 1;
         }
         float s[4][R];
 #pragma unroll
@@ -304,8 +306,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
                 float f = (float)(ih[r] * 256 + il[r]) * d;
                 f += dpp_xor1(f);
                 f += dpp_xor2(f);
-                s[p][r] = t <= lim[r] ? f : -INFINITY;
+                s[p][r] = f;
             }
+        }
+        if (need_mask) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+#pragma unroll
+                for (int r = 0; r < R; ++r) s[p][r] = 16 * p + u <= lim[r] ? s[p][r] : -INFINITY;
         }
         // the V rows were loaded by LDS DMA before the K blocks; all K data has
         // been consumed, and this makes the DMA writes visible to the reads below
@@ -316,22 +324,37 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
 #pragma unroll
         for (int r = 0; r < R; ++r)
             m_w[r] = max_over_tokens(fmaxf(fmaxf(s[0][r], s[1][r]), fmaxf(s[2][r], s[3][r])));
-        // lane b of each quad exponentiates rows b and b + 4 of its 4 tokens
+        // lane b of each quad exponentiates rows b and b + 4 of its 4 tokens.
+        // Masked scores are -inf and give exp2 = 0; a fully masked slice uses
+        // 0 as its reference, and a zero row scale is lifted to a tiny one so
+        // that 0 * -inf never arises.
         float ea[4], eb[4];
         float la = 0.f, lb = 0.f;
+        {
+            // per-lane selection of rows b and b + 4 by value selects (no
+            // divergent branches)
+            const bool b1 = (b & 1) != 0, b2 = (b & 2) != 0;
+            auto sel = [&](float x0, float x1, float x2, float x3) {
+                const float lo = b1 ? x1 : x0, hi = b1 ? x3 : x2;
+                return b2 ? hi : lo;
+            };
+            auto row = [&](const float* v, int r) { return r < R ? v[r] : -INFINITY; };
+            auto rowk = [&](const float* v, int r) { return r < R ? v[r] : 0.f; };
+            float ma = sel(row(m_w, 0), row(m_w, 1), row(m_w, 2), row(m_w, 3));
+            float mb = sel(row(m_w, 4), row(m_w, 5), row(m_w, 6), row(m_w, 7));
+            const float ka = fmaxf(sel(rowk(qs, 0), rowk(qs, 1), rowk(qs, 2), rowk(qs, 3)), 1e-30f);
+            const float kb = fmaxf(sel(rowk(qs, 4), rowk(qs, 5), rowk(qs, 6), rowk(qs, 7)), 1e-30f);
+            ma = ma == -INFINITY ? 0.f : ma;
+            mb = mb == -INFINITY ? 0.f : mb;
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            float sa = -INFINITY, sb = -INFINITY, ma = 0.f, mb = 0.f, ka = 0.f, kb = 0.f;
-#pragma unroll
-            for (int rx = 0; rx < 4; ++rx)
-                if (rx == b) {
-                    if (rx < R) { sa = s[p][rx]; ma = m_w[rx]; ka = qs[rx]; }
-                    if (rx + 4 < R) { sb = s[p][rx + 4]; mb = m_w[rx + 4]; kb = qs[rx + 4]; }
-                }
-            ea[p] = sa == -INFINITY ? 0.f : exp2f(ka * (sa - ma));
-            eb[p] = sb == -INFINITY ? 0.f : exp2f(kb * (sb - mb));
-            la += ea[p];
-            lb += eb[p];
+            for (int p = 0; p < 4; ++p) {
+                const float sa = sel(row(s[p], 0), row(s[p], 1), row(s[p], 2), row(s[p], 3));
+                const float sb = sel(row(s[p], 4), row(s[p], 5), row(s[p], 6), row(s[p], 7));
+                ea[p] = __builtin_amdgcn_exp2f(ka * (sa - ma));
+                eb[p] = __builtin_amdgcn_exp2f(kb * (sb - mb));
+                la += ea[p];
+                lb += eb[p];
+            }
         }
         la = sum_over_tokens(la);
         lb = sum_over_tokens(lb);
@@ -431,15 +454,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
                 if (M != -INFINITY) {
 #pragma unroll
                     for (int ww = 0; ww < kWaves; ++ww) {
-                        const float f = ms[ww] == -INFINITY ? 0.f : exp2f(ms[ww] - M);
+                        const float f = __builtin_amdgcn_exp2f(ms[ww] - M);   // 0 for an empty slice
                         pa = fmaf(sm.sacc[par][ww][r][mc], f, pa);
                         pl = fmaf(sm.sl_[par][ww][r], f, pl);
                     }
                 }
                 const float Mn = fmaxf(m_run[k], M);
                 if (Mn != -INFINITY) {
-                    const float al = m_run[k] == -INFINITY ? 0.f : exp2f(m_run[k] - Mn);
-                    const float be = M == -INFINITY ? 0.f : exp2f(M - Mn);
+                    const float al = __builtin_amdgcn_exp2f(m_run[k] - Mn);   // 0 from an empty state
+                    const float be = __builtin_amdgcn_exp2f(M - Mn);
                     acc_run[k] = acc_run[k] * al + pa * be;
                     l_run[k] = l_run[k] * al + pl * be;
                     m_run[k] = Mn;
