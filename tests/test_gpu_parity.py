@@ -137,6 +137,27 @@ def test_multi_row_parity(n_q, causal, qdt, scale):
         c.close()
 
 
+def test_staged_and_in_kernel_conversion_agree_bit_for_bit():
+    """A block wider than 64 rows per kv head stages every page once into f16
+    matrix-core operands; a narrower block converts in the kernel. Each row's
+    arithmetic is the same either way, so the first 10 query tokens of an
+    11-token block (66 rows, staged) equal a 10-token block (60 rows) bit for
+    bit."""
+    c = small_case(mask_random(0.5, seed=11), n_layers=2, max_q=11, group=2)
+    try:
+        qs11 = [c.queries(l, 11, "f32") for l in range(c.L)]
+        qs10 = [q[:10].copy() for q in qs11]
+        q_pos0 = N_KV - 11
+        o11, l11 = c.attend_all(qs11, q_pos0=q_pos0, scale=1.0, causal=True)
+        o10, l10 = c.attend_all(qs10, q_pos0=q_pos0, scale=1.0, causal=True)
+        check(c, o11, l11, qs11, q_pos0=q_pos0, scale=1.0, causal=True)
+        for l in range(c.L):
+            assert np.array_equal(o11[l][:10], o10[l]), l
+            assert np.array_equal(l11[l][:10], l10[l]), l
+    finally:
+        c.close()
+
+
 def test_prefill_bit_identical_across_residency_and_ring():
     """Large query blocks (64-row tiles, last one ragged) give the same bits
     whichever pages are resident and however the ring chunks the rest."""
