@@ -419,7 +419,7 @@ def main():
         result["verify"] = multi_leg("spec_verify_160k", dict(ring_pages=16, chunk_pages=4, copy_streams=1,
                                                               group_pages=1), args.threads, link, 8, "verify")
         result["prefill"] = multi_leg("prefill_ubatch_128k", dict(ring_pages=32, chunk_pages=8, copy_streams=1,
-                                                                  group_pages=4), args.threads, link, 6, "prefill")
+                                                                  group_pages=8), args.threads, link, 6, "prefill")
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(wl, recs, qs_np)

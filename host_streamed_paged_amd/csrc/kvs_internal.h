@@ -113,13 +113,29 @@ struct AttendArgs {
 
 // Conversion of a launch's pages into staged operands (kvs_mfma.hip).
 struct StageArgs {
+    CopyJob copy;         // ring refill carried by this launch
     PageSource ps;
     const Seg* segs;      // the launch's segments; their pages are staged in order
     int32_t n_segs;
     int32_t n_kv_heads;
     int64_t n_kv;
+    int32_t n_pages;      // pages of the launch's segments
     uint8_t* staged;      // [pages][n_kv_heads][kStagedTile]
 };
+
+// The first `first` pages of a copy job, or the rest (ring slots follow).
+inline CopyJob split_copy(const CopyJob& cj, int32_t first, bool head) {
+    CopyJob r = cj;
+    if (head) {
+        r.n_pages = first < cj.n_pages ? first : cj.n_pages;
+    } else {
+        const int32_t k = first < cj.n_pages ? first : cj.n_pages;
+        r.n_pages = cj.n_pages - k;
+        r.ring_dst = cj.ring_dst + (int64_t)k * cj.page_bytes;
+        for (int32_t i = 0; i < r.n_pages; ++i) r.pages[i] = cj.pages[k + i];
+    }
+    return r;
+}
 
 struct GatherArgs {
     CopyJob copy;
@@ -140,7 +156,7 @@ hipError_t launch_decode(const AttendArgs& a, hipStream_t stream);
 // matrix-core kernel (kvs_mfma.hip) for more rows
 hipError_t launch_mfma(const AttendArgs& a, hipStream_t stream);
 bool mfma_stages(int rows);   // rows per kv head for which launches stage their pages first
-hipError_t launch_stage(const StageArgs& a, int32_t n_pages, hipStream_t stream);
+hipError_t launch_stage(const StageArgs& a, hipStream_t stream);
 hipError_t launch_combine(const float* part, int32_t n_groups, int32_t n_q, int32_t n_q_heads,
                           float* out, float* lse, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);

@@ -494,10 +494,15 @@ void mfma_kernel(AttendArgs a) {
 
 // Converts each (page, kv head) of a launch once into f16 MFMA operands (the
 // staged mode above). Grid: (pages of the launch, kv heads); block x stages
-// the x-th page of the launch's segments, in segment order.
+// the x-th page of the launch's segments, in segment order; blocks past the
+// pages are ring refill workgroups.
 __global__ __launch_bounds__(kThreads) void stage_kernel(StageArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t k_lds[kKTile];
     __shared__ __attribute__((aligned(16))) uint8_t v_lds[kVTile];
+    if ((int)blockIdx.x >= a.n_pages) {   // ring refill workgroup
+        copy_role(a.copy, ((int)blockIdx.x - a.n_pages) * (int)gridDim.y + (int)blockIdx.y);
+        return;
+    }
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int n = lane & 15, gq = lane >> 4;
     const int slot = blockIdx.x, g = blockIdx.y;
@@ -562,9 +567,10 @@ hipError_t launch_mfma(const AttendArgs& a, hipStream_t stream) {
 
 bool mfma_stages(int rows) { return rows > 64; }
 
-hipError_t launch_stage(const StageArgs& a, int32_t n_pages, hipStream_t stream) {
-    if (n_pages <= 0) return hipSuccess;
-    hipLaunchKernelGGL(stage_kernel, dim3(n_pages, a.n_kv_heads), dim3(kThreads), 0, stream, a);
+hipError_t launch_stage(const StageArgs& a, hipStream_t stream) {
+    const int cx = (copy_workgroups(a.copy) + a.n_kv_heads - 1) / a.n_kv_heads;
+    if (a.n_pages <= 0 && cx == 0) return hipSuccess;
+    hipLaunchKernelGGL(stage_kernel, dim3(a.n_pages + cx, a.n_kv_heads), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -727,17 +727,24 @@ int kvs_attend(kvs_pool* p, int32_t layer, const void* q, int32_t q_dtype, int32
             int32_t j = i, pages = 0;
             while (j < seg0 + nseg && pages + ls.segs[j].npages <= p->L.stage_pages) pages += ls.segs[j++].npages;
             if (j == i) return fail(KVS_ERR_INVALID_ARG, "internal: segment longer than the staging region");
+            // the ring refill rides with the first run, half of its pages
+            // with the staging launch and half with the attention launch, so
+            // that the lane keeps pulling pages over the link through both
+            const bool first_run = i == seg0;
+            const int32_t half = (cj.n_pages + 1) / 2;
             kvs::StageArgs sa{};
+            sa.copy = first_run ? kvs::split_copy(cj, half, true) : kvs::CopyJob{};
             sa.ps = b.ps;
             sa.segs = ls.dev_segs + i;
             sa.n_segs = j - i;
             sa.n_kv_heads = p->cfg.n_kv_heads;
             sa.n_kv = n_kv;
+            sa.n_pages = pages;
             sa.staged = region;
-            hipError_t e = timed(p, 2, st, [&] { return kvs::launch_stage(sa, pages, st); });
+            hipError_t e = timed(p, 2, st, [&] { return kvs::launch_stage(sa, st); });
             if (e != hipSuccess) return fail(KVS_ERR_HIP, "staging kernel launch failed: %s", hipGetErrorString(e));
             kvs::AttendArgs c = b;
-            if (i != seg0) c.copy = kvs::CopyJob{};   // the ring refill rides with the first run
+            c.copy = first_run ? kvs::split_copy(cj, half, false) : kvs::CopyJob{};
             c.segs = ls.dev_segs + i;
             c.n_segs = j - i;
             c.staged = region;
