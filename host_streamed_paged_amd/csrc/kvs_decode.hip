@@ -279,7 +279,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
         float s[4][R];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const int t = 16 * p + u;
             uint32_t c[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) c[k] = __builtin_amdgcn_perm(kw[p][k + 1], kw[p][k], sel);

@@ -43,6 +43,8 @@ int fail(int code, const char* fmt, ...) {
 
 constexpr uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
+constexpr int kMaxLanes = 3;   // compute lanes for ring chunks (lane 0 is the caller's stream)
+
 struct Layout {
     uint64_t page_bytes = 0;
     uint64_t ring_bytes = 0;
@@ -52,7 +54,7 @@ struct Layout {
     int32_t max_segs = 0;      // per layer
     int32_t max_groups = 0;
     int32_t stage_pages = 0;   // pages per staging region (0: blocks never wide enough to stage)
-    uint64_t stage_bytes = 0;  // two staging regions, one per compute lane
+    uint64_t stage_bytes = 0;  // one staging region per compute lane
     uint64_t fixed = 0;        // ring + work + staging + tables
 };
 
@@ -98,7 +100,7 @@ Layout layout_of(const kvs_config* c) {
     // more than group_pages pages)
     if (kvs::mfma_stages(c->max_q_tokens * (c->n_q_heads / c->n_kv_heads))) {
         L.stage_pages = std::max(64, c->group_pages);
-        L.stage_bytes = 2 * align256((uint64_t)L.stage_pages * c->n_kv_heads * kvs::kStagedTile);
+        L.stage_bytes = kMaxLanes * align256((uint64_t)L.stage_pages * c->n_kv_heads * kvs::kStagedTile);
     }
     L.fixed = L.ring_bytes + L.work_bytes + L.stage_bytes + (uint64_t)c->n_layers * (L.src_bytes + L.seg_bytes);
     return L;
@@ -136,7 +138,7 @@ struct kvs_pool {
     uint64_t budget = 0;
     uint8_t* ring = nullptr;
     float* work = nullptr;
-    uint8_t* staged[2] = {nullptr, nullptr};   // staging regions of the caller's stream and of the lane
+    uint8_t* staged[kMaxLanes] = {};   // staging region of each compute lane (lane 0: the caller's stream)
     uint8_t* slots = nullptr;
     int64_t n_slots = 0;
     std::vector<int32_t> slot_free;  // stack of free slot ids
@@ -147,8 +149,9 @@ struct kvs_pool {
     hipEvent_t ring_free = nullptr;  // recorded on the compute stream after a layer's last ring read
     bool ring_used = false;          // ring_free has been recorded at least once
     hipEvent_t last_work = nullptr;  // recorded after every attend / gather
-    hipStream_t lane = nullptr;      // second compute lane for ring chunks
-    hipEvent_t fork_ev = nullptr, join_ev = nullptr;
+    hipStream_t lanes[kMaxLanes] = {};   // compute lanes 1.. for ring chunks (lane 0 is the caller's stream)
+    hipEvent_t fork_ev = nullptr;
+    hipEvent_t join_ev[kMaxLanes] = {};
     int32_t ring_next = 0;           // chunk slot that receives the next layer's chunk 0
     int32_t pf_layer = -1;           // layer whose chunk 0 was prefetched and not yet consumed
     bool broken = false;             // a HIP call failed mid-sequence
@@ -336,18 +339,27 @@ int prefetch(kvs_pool* p, int32_t layer) {
 // Run the layer's launch plan. Ring chunks are moved by copy workgroups
 // inside the compute launches; kernel boundaries on a stream order each copy
 // before its reader and each reader before its slot is refilled.
-//   Two lanes (ring of an even number >= 4 of chunk slots, and every
-//   split-K group computed by a single chunk launch, so that concurrent
-//   launches never share a group's state): the caller's stream computes even
-//   chunks and the pool's
-//   lane stream odd chunks; the launch that computes chunk c copies chunk
-//   c + 2, which belongs to the same lane, into a slot last read by that lane.
-//   The lanes' launch boundaries fall at different times, so the host link
-//   stays busy. They meet through one fork and one join event per layer.
+//   n lanes (lanes_for: 3 when the ring holds a multiple of 3 and at least 6
+//   chunk slots, else 2 when it holds an even number >= 4; and every split-K
+//   group computed by a single chunk launch, so that concurrent launches never
+//   share a group's state): chunk c is computed on lane c mod n (lane 0 is the
+//   caller's stream, the others the pool's lane streams), and the launch that
+//   computes chunk c copies chunk c + n, which belongs to the same lane, into
+//   a slot last read by that lane (slot count a multiple of n, at least 2 n).
+//   The lanes' copies overlap, so the host link stays busy. They meet through
+//   one fork event and one join event per lane per layer.
 //   One lane (otherwise): the launch that computes chunk c copies chunk c + 1
 //   (ring of >= 2 slots), or copies and computes alternate (one slot).
 // The resident groups are computed by the first launch on the caller's
 // stream, which also copies chunk 0 unless it was prefetched.
+// Compute lanes for a layer with n_ch ring chunks over R chunk slots.
+int lanes_for(int32_t R, int32_t n_ch, bool whole_groups) {
+    if (n_ch < 2 || !whole_groups) return 1;
+    if (R >= 6 && R % 3 == 0 && n_ch >= 3) return 3;
+    if (R >= 4 && R % 2 == 0) return 2;
+    return 1;
+}
+
 template <typename LaunchFn>
 int run_layer(kvs_pool* p, int32_t layer, hipStream_t stream, LaunchFn launch) {
     LayerState& ls = p->layers[layer];
@@ -364,14 +376,15 @@ int run_layer(kvs_pool* p, int32_t layer, hipStream_t stream, LaunchFn launch) {
         if (hipStreamWaitEvent(stream, p->ring_free, 0) != hipSuccess) return mark(fail(KVS_ERR_HIP, "hipStreamWaitEvent(ring) failed"));
     }
     p->pf_layer = -1;
-    const bool two = n_ch >= 2 && R >= 4 && (R % 2) == 0 && ls.whole_groups;
+    const int n_lanes = lanes_for(R, n_ch, ls.whole_groups);
     auto slot_of = [&](int32_t c) { return (slot0 + c) % R; };
-    auto do_launch = [&](hipStream_t st, int32_t seg0, int32_t nseg, int32_t c_compute, int32_t c_copy) -> int {
+    auto do_launch = [&](int lane, int32_t seg0, int32_t nseg, int32_t c_compute, int32_t c_copy) -> int {
+        hipStream_t st = lane == 0 ? stream : p->lanes[lane];
         kvs::CopyJob cj{};
         if (c_copy >= 0) cj = make_copy(p, ls, c_copy, slot_of(c_copy));
         const uint8_t* ring_chunk = c_compute >= 0 ? p->ring + (uint64_t)slot_of(c_compute) * p->cfg.chunk_pages * p->L.page_bytes : nullptr;
         const int32_t rank0 = c_compute >= 0 ? ls.chunks[c_compute].rank0 : 0;
-        int r = launch(st, seg0, nseg, ring_chunk, rank0, cj);
+        int r = launch(st, lane, seg0, nseg, ring_chunk, rank0, cj);
         if (r) return mark(r);
         count_copy(p, cj);
         p->st.kernels_launched++;
@@ -384,29 +397,31 @@ int run_layer(kvs_pool* p, int32_t layer, hipStream_t stream, LaunchFn launch) {
     };
     const int32_t c0 = (n_ch > 0 && !prefetched) ? 0 : -1;
     if (ls.res_nseg > 0 || c0 >= 0) {
-        if ((rc = do_launch(stream, 0, ls.res_nseg, -1, c0))) return rc;
+        if ((rc = do_launch(0, 0, ls.res_nseg, -1, c0))) return rc;
     }
-    if (two) {
-        hipStream_t ln = p->lane;
-        if (hipEventRecord(p->fork_ev, stream) != hipSuccess || hipStreamWaitEvent(ln, p->fork_ev, 0) != hipSuccess)
-            return mark(fail(KVS_ERR_HIP, "lane fork failed"));
-        if ((rc = do_launch(ln, 0, 0, -1, 1))) return rc;   // lane 1 starts by copying chunk 1
+    if (n_lanes > 1) {
+        if (hipEventRecord(p->fork_ev, stream) != hipSuccess) return mark(fail(KVS_ERR_HIP, "lane fork failed"));
+        for (int k = 1; k < n_lanes; ++k) {
+            if (hipStreamWaitEvent(p->lanes[k], p->fork_ev, 0) != hipSuccess) return mark(fail(KVS_ERR_HIP, "lane fork failed"));
+            if ((rc = do_launch(k, 0, 0, -1, k))) return rc;   // lane k starts by copying chunk k
+        }
         for (int32_t c = 0; c < n_ch; ++c) {
             const ChunkPlan& cp = ls.chunks[c];
-            const int32_t cc = (c + 2 < n_ch) ? c + 2 : -1;
-            if ((rc = do_launch((c & 1) ? ln : stream, cp.seg0, cp.nseg, c, cc))) return rc;
+            const int32_t cc = (c + n_lanes < n_ch) ? c + n_lanes : -1;
+            if ((rc = do_launch(c % n_lanes, cp.seg0, cp.nseg, c, cc))) return rc;
         }
-        if (hipEventRecord(p->join_ev, ln) != hipSuccess || hipStreamWaitEvent(stream, p->join_ev, 0) != hipSuccess)
-            return mark(fail(KVS_ERR_HIP, "lane join failed"));
+        for (int k = 1; k < n_lanes; ++k)
+            if (hipEventRecord(p->join_ev[k], p->lanes[k]) != hipSuccess || hipStreamWaitEvent(stream, p->join_ev[k], 0) != hipSuccess)
+                return mark(fail(KVS_ERR_HIP, "lane join failed"));
     } else {
         for (int32_t c = 0; c < n_ch; ++c) {
             const ChunkPlan& cp = ls.chunks[c];
             if (R >= 2) {
                 const int32_t cc = (c + 1 < n_ch) ? c + 1 : -1;
-                if ((rc = do_launch(stream, cp.seg0, cp.nseg, c, cc))) return rc;
+                if ((rc = do_launch(0, cp.seg0, cp.nseg, c, cc))) return rc;
             } else {
-                if ((rc = do_launch(stream, cp.seg0, cp.nseg, c, -1))) return rc;
-                if (c + 1 < n_ch && (rc = do_launch(stream, 0, 0, -1, c + 1))) return rc;
+                if ((rc = do_launch(0, cp.seg0, cp.nseg, c, -1))) return rc;
+                if (c + 1 < n_ch && (rc = do_launch(0, 0, 0, -1, c + 1))) return rc;
             }
         }
     }
@@ -535,8 +550,7 @@ int kvs_pool_create(const kvs_config* cfg, void* dev_arena, uint64_t budget_byte
     p->ring = cur; cur += L.ring_bytes;
     p->work = (float*)cur; cur += L.work_bytes;
     if (L.stage_bytes) {
-        p->staged[0] = cur;
-        p->staged[1] = cur + L.stage_bytes / 2;
+        for (int k = 0; k < kMaxLanes; ++k) p->staged[k] = cur + k * (L.stage_bytes / kMaxLanes);
         cur += L.stage_bytes;
     }
     p->layers.resize(cfg->n_layers);
@@ -550,8 +564,9 @@ int kvs_pool_create(const kvs_config* cfg, void* dev_arena, uint64_t budget_byte
     p->n_cslots = cfg->ring_pages / cfg->chunk_pages;
     auto cleanup = [&](const char* what, hipError_t e) {
         for (auto s : p->copy) (void)hipStreamDestroy(s);
-        if (p->lane) (void)hipStreamDestroy(p->lane);
-        for (hipEvent_t ev : {p->pf_done, p->ring_free, p->last_work, p->fork_ev, p->join_ev}) if (ev) (void)hipEventDestroy(ev);
+        for (auto s : p->lanes) if (s) (void)hipStreamDestroy(s);
+        for (hipEvent_t ev : {p->pf_done, p->ring_free, p->last_work, p->fork_ev}) if (ev) (void)hipEventDestroy(ev);
+        for (hipEvent_t ev : p->join_ev) if (ev) (void)hipEventDestroy(ev);
         delete p;
         return fail(KVS_ERR_HIP, "%s failed: %s", what, hipGetErrorString(e));
     };
@@ -561,12 +576,14 @@ int kvs_pool_create(const kvs_config* cfg, void* dev_arena, uint64_t budget_byte
         if (e != hipSuccess) return cleanup("hipStreamCreateWithFlags", e);
         p->copy.push_back(s);
     }
-    for (hipEvent_t* ev : {&p->pf_done, &p->ring_free, &p->last_work, &p->fork_ev, &p->join_ev}) {
+    for (hipEvent_t* ev : {&p->pf_done, &p->ring_free, &p->last_work, &p->fork_ev}) {
         hipError_t e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
         if (e != hipSuccess) return cleanup("hipEventCreateWithFlags", e);
     }
-    {
-        hipError_t e = hipStreamCreateWithFlags(&p->lane, hipStreamNonBlocking);
+    for (int k = 1; k < kMaxLanes; ++k) {
+        hipError_t e = hipEventCreateWithFlags(&p->join_ev[k], hipEventDisableTiming);
+        if (e != hipSuccess) return cleanup("hipEventCreateWithFlags", e);
+        e = hipStreamCreateWithFlags(&p->lanes[k], hipStreamNonBlocking);
         if (e != hipSuccess) return cleanup("hipStreamCreateWithFlags", e);
     }
     p->st.page_bytes = (int64_t)L.page_bytes;
@@ -585,10 +602,11 @@ void kvs_pool_destroy(kvs_pool* p) {
     if (!p) return;
     for (auto s : p->copy) (void)hipStreamSynchronize(s);
     if (p->last_work) (void)hipEventSynchronize(p->last_work);
-    if (p->lane) (void)hipStreamSynchronize(p->lane);
+    for (auto s : p->lanes) if (s) (void)hipStreamSynchronize(s);
     for (auto s : p->copy) (void)hipStreamDestroy(s);
-    if (p->lane) (void)hipStreamDestroy(p->lane);
-    for (hipEvent_t ev : {p->pf_done, p->ring_free, p->last_work, p->fork_ev, p->join_ev}) if (ev) (void)hipEventDestroy(ev);
+    for (auto s : p->lanes) if (s) (void)hipStreamDestroy(s);
+    for (hipEvent_t ev : {p->pf_done, p->ring_free, p->last_work, p->fork_ev}) if (ev) (void)hipEventDestroy(ev);
+    for (hipEvent_t ev : p->join_ev) if (ev) (void)hipEventDestroy(ev);
     for (auto& v : p->prof_ev)
         for (auto& pr : v) { (void)hipEventDestroy(pr.first); (void)hipEventDestroy(pr.second); }
     delete p;
@@ -708,8 +726,8 @@ int kvs_attend(kvs_pool* p, int32_t layer, const void* q, int32_t q_dtype, int32
     a.causal = causal ? 1 : 0;
     a.part = p->work;
     const bool staging = kvs::mfma_stages(n_q * a.G);
-    rc = run_layer(p, layer, s, [&](hipStream_t st, int32_t seg0, int32_t nseg, const uint8_t* ring_chunk, int32_t rank0,
-                                    const kvs::CopyJob& cj) -> int {
+    rc = run_layer(p, layer, s, [&](hipStream_t st, int lane, int32_t seg0, int32_t nseg, const uint8_t* ring_chunk,
+                                    int32_t rank0, const kvs::CopyJob& cj) -> int {
         kvs::AttendArgs b = a;
         b.copy = cj;
         b.ps.ring_chunk = ring_chunk;
@@ -722,7 +740,7 @@ int kvs_attend(kvs_pool* p, int32_t layer, const void* q, int32_t q_dtype, int32
         }
         // staged: runs of segments of at most stage_pages pages; each run is
         // converted into the lane's staging region, then attended
-        uint8_t* region = p->staged[st == p->lane ? 1 : 0];
+        uint8_t* region = p->staged[lane];
         for (int32_t i = seg0; i < seg0 + nseg;) {
             int32_t j = i, pages = 0;
             while (j < seg0 + nseg && pages + ls.segs[j].npages <= p->L.stage_pages) pages += ls.segs[j++].npages;
@@ -789,8 +807,8 @@ int kvs_debug_gather(kvs_pool* p, int32_t layer, int64_t tok0, int64_t n_tok, fl
     a.n_tok = n_tok;
     a.k_out = k_out;
     a.v_out = v_out;
-    rc = run_layer(p, layer, s, [&](hipStream_t st, int32_t seg0, int32_t nseg, const uint8_t* ring_chunk, int32_t rank0,
-                                    const kvs::CopyJob& cj) -> int {
+    rc = run_layer(p, layer, s, [&](hipStream_t st, int /*lane*/, int32_t seg0, int32_t nseg, const uint8_t* ring_chunk,
+                                    int32_t rank0, const kvs::CopyJob& cj) -> int {
         kvs::GatherArgs b = a;
         b.copy = cj;
         b.ps.ring_chunk = ring_chunk;

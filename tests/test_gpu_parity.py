@@ -165,7 +165,8 @@ def test_prefill_bit_identical_across_residency_and_ring():
     base = None
     for v in [dict(resident=mask_all, ring=4, chunk=2, group=3),
               dict(resident=mask_none, ring=2, chunk=1, group=3, flags=kvs.FLAG_POISON_RING),
-              dict(resident=mask_random(0.4, seed=9), ring=8, chunk=4, group=3)]:
+              dict(resident=mask_random(0.4, seed=9), ring=8, chunk=4, group=3),
+              dict(resident=mask_none, ring=18, chunk=3, group=3, flags=kvs.FLAG_POISON_RING)]:
         c = small_case(v["resident"], n_layers=2, max_q=n_q, ring=v["ring"], chunk=v["chunk"],
                        group=v["group"], flags=v.get("flags", 0))
         try:
@@ -189,9 +190,12 @@ def test_outputs_bit_identical_across_residency_ring_and_chunks():
         dict(resident=mask_none, ring=6, chunk=3, streams=3),
         dict(resident=mask_random(0.5), ring=4, chunk=4, streams=1),
         dict(resident=mask_random(0.3, seed=5), ring=2, chunk=1, streams=2, flags=kvs.FLAG_POISON_RING),
-        # four or more chunk slots: two compute lanes when no group spans two chunks
+        # four or more chunk slots: two compute lanes when no group spans two
+        # chunks; six (or a larger multiple of three): three lanes
         dict(resident=mask_none, ring=4, chunk=1, streams=1),
         dict(resident=mask_random(0.5, seed=6), ring=8, chunk=2, streams=2, flags=kvs.FLAG_POISON_RING),
+        dict(resident=mask_none, ring=6, chunk=1, streams=1, flags=kvs.FLAG_POISON_RING),
+        dict(resident=mask_random(0.3, seed=8), ring=12, chunk=2, streams=1),
     ]
     for group in (1, 3):
         base = None
