@@ -43,7 +43,7 @@ int fail(int code, const char* fmt, ...) {
 
 constexpr uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
-constexpr int kMaxLanes = 3;   // compute lanes for ring chunks (lane 0 is the caller's stream)
+constexpr int kMaxLanes = 4;   // compute lanes for ring chunks (lane 0 is the caller's stream)
 
 struct Layout {
     uint64_t page_bytes = 0;
@@ -339,10 +339,9 @@ int prefetch(kvs_pool* p, int32_t layer) {
 // Run the layer's launch plan. Ring chunks are moved by copy workgroups
 // inside the compute launches; kernel boundaries on a stream order each copy
 // before its reader and each reader before its slot is refilled.
-//   n lanes (lanes_for: 3 when the ring holds a multiple of 3 and at least 6
-//   chunk slots, else 2 when it holds an even number >= 4; and every split-K
-//   group computed by a single chunk launch, so that concurrent launches never
-//   share a group's state): chunk c is computed on lane c mod n (lane 0 is the
+//   n lanes (lanes_for: up to 4, n dividing the number of chunk slots, which
+//   is at least 2 n; and every split-K group computed by a single chunk
+//   launch, so that concurrent launches never share a group's state): chunk c is computed on lane c mod n (lane 0 is the
 //   caller's stream, the others the pool's lane streams), and the launch that
 //   computes chunk c copies chunk c + n, which belongs to the same lane, into
 //   a slot last read by that lane (slot count a multiple of n, at least 2 n).
@@ -352,11 +351,13 @@ int prefetch(kvs_pool* p, int32_t layer) {
 //   (ring of >= 2 slots), or copies and computes alternate (one slot).
 // The resident groups are computed by the first launch on the caller's
 // stream, which also copies chunk 0 unless it was prefetched.
-// Compute lanes for a layer with n_ch ring chunks over R chunk slots.
+// Compute lanes for a layer with n_ch ring chunks over R chunk slots: the
+// most lanes n (up to kMaxLanes) with R a multiple of n and at least 2 n, so
+// that a lane only ever refills slots it has read itself.
 int lanes_for(int32_t R, int32_t n_ch, bool whole_groups) {
     if (n_ch < 2 || !whole_groups) return 1;
-    if (R >= 6 && R % 3 == 0 && n_ch >= 3) return 3;
-    if (R >= 4 && R % 2 == 0) return 2;
+    for (int n = kMaxLanes; n >= 2; --n)
+        if (n_ch >= n && R >= 2 * n && R % n == 0) return n;
     return 1;
 }
 
