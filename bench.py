@@ -211,8 +211,8 @@ def multi_leg(name, cfg_kw, threads, link, steps, kind):
     layer_bytes = wl.n_pages * pb
     flops = 4 * wl.n_q_heads * wl.head_dim * allowed_keys(wl)
     staged = r["stage_launches"] > 0
-    k = {"kernel": f"mfma_kernel<{2 if kind == 'verify' else 4}{', staged' if staged else ''}>"
-                   f"{' + stage_kernel' if staged else ''} (all pages resident)",
+    k = {"kernel": ("stage_kernel + mfma_kernel<2, staged> (32-row tiles on staged operands)" if staged
+                    else "mfma_kernel<2> (32-row tiles, in-kernel conversion)") + ", all pages resident",
          "avg_layer_us": round(avg * 1e3, 2), "attn_launches": r["attn_launches"],
          "stage_launches": r["stage_launches"], "stage_us_per_layer": round(r["stage_ms_total"] / max(1, layers_timed) * 1e3, 2),
          "bytes_per_layer": layer_bytes, "flops_per_layer": flops,
