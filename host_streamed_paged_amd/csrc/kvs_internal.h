@@ -109,6 +109,7 @@ struct AttendArgs {
     int32_t causal;
     float* part;          // [n_groups][n_q][Hq][kPartStride]
     const uint8_t* staged; // staged operands of this launch's pages (null: convert in the kernel)
+    int32_t n_slices;     // matrix-core kernel: segment slices per (kv head, row tile), set at launch
 };
 
 // Conversion of a launch's pages into staged operands (kvs_mfma.hip).

@@ -101,21 +101,39 @@ __device__ inline void dma_page_tiles(const uint8_t* rec, int g, int n_kv_heads,
 // K operand of v_mfma_f32_16x16x32_f16 for S^T = K . Q^T: this lane's 8 dims
 // [32 b + 8 gq, +8) of token `tok` of the K tile (record layout, in LDS),
 // each d * code rounded once to f16 (the code is converted exactly first).
-__device__ inline half8_t k_fragment(const uint8_t* k_lds, int tok, int b, int gq) {
+// Split into the LDS reads (k_raw) and the arithmetic (k_convert) so that a
+// caller can read the next fragments while converting the current ones.
+struct KRaw {
+    uint32_t x0, x1, x2;   // 3 aligned dwords (even blocks) or 2 (odd blocks)
+    uint32_t db;           // scale bits
+};
+__device__ inline KRaw k_raw(const uint8_t* k_lds, int tok, int b, int gq) {
     const uint8_t* blk = k_lds + tok * kKRow + b * kKBlock;
-    uint32_t x0, x1;
+    KRaw r;
     if (b & 1) {   // codes start on a dword boundary
         const uint32_t* p = (const uint32_t*)(blk + 2 + 8 * gq);
-        x0 = p[0];
-        x1 = p[1];
+        r.x0 = p[0];
+        r.x1 = p[1];
+        r.x2 = 0u;
     } else {       // codes start 2 bytes into a dword
         const uint32_t* p = (const uint32_t*)(blk + 8 * gq);
-        const uint32_t y0 = p[0], y1 = p[1], y2 = p[2];
-        x0 = __builtin_amdgcn_alignbyte(y1, y0, 2);
-        x1 = __builtin_amdgcn_alignbyte(y2, y1, 2);
+        r.x0 = p[0];
+        r.x1 = p[1];
+        r.x2 = p[2];
     }
-    const uint32_t db = *(const uint16_t*)blk;
-    const half2_t d2 = as_h2(db | (db << 16));
+    r.db = *(const uint16_t*)blk;
+    return r;
+}
+__device__ inline half8_t k_convert(const KRaw& r, int b) {
+    uint32_t x0, x1;
+    if (b & 1) {
+        x0 = r.x0;
+        x1 = r.x1;
+    } else {
+        x0 = __builtin_amdgcn_alignbyte(r.x1, r.x0, 2);
+        x1 = __builtin_amdgcn_alignbyte(r.x2, r.x1, 2);
+    }
+    const half2_t d2 = as_h2(r.db | (r.db << 16));
     const half2_t k_off = {(_Float16)1152.f, (_Float16)1152.f};   // 1024 + 128
     const uint32_t c_hi64 = 0x64646464u;
     // int8 code k -> f16 (1024 + (k + 128)) - 1152, exact; then * d
@@ -130,36 +148,57 @@ __device__ inline half8_t k_fragment(const uint8_t* k_lds, int tok, int b, int g
     kop[4] = e2[0]; kop[5] = e2[1]; kop[6] = e3[0]; kop[7] = e3[1];
     return kop;
 }
+__device__ inline half8_t k_fragment(const uint8_t* k_lds, int tok, int b, int gq) {
+    return k_convert(k_raw(k_lds, tok, b, gq), b);
+}
 
 // V^T operands of O^T += V^T . P^T for chunk c (tokens [32 c, 32 c + 32)) and
 // quant block b: vop[0] holds channel 32 b + n, vop[1] channel 32 b + 16 + n
 // (low and high nibbles of byte n), for the lane's 8 token slots: slot j of
 // lane group gq is token 32 c + 4 gq + j for j < 4, else 32 c + 12 + 4 gq + j.
 // Each value is d * (u - 8) rounded once to f16. TAIL zeroes rows at or past
-// `valid` (their scales may be NaN).
-template <bool TAIL>
-__device__ inline void v_fragments(const uint8_t* v_lds, int b, int c, int gq, int n, int valid,
-                                   uint32_t m_nib, uint32_t magic, half8_t (&vop)[2]) {
-    const half2_t v_off = {(_Float16)1032.f, (_Float16)1032.f};   // 1024 + 8
+// `valid` (their scales may be NaN). Split into the LDS reads (v_raw) and the
+// arithmetic (v_convert), like the K operand.
+struct VRaw {
+    uint32_t byte[8];   // nibble byte n of the slot's token
+    uint32_t d[8];      // scale bits of the slot's token
+};
+__device__ inline VRaw v_raw(const uint8_t* v_lds, int b, int c, int gq, int n) {
     const uint8_t* vlane = v_lds + b * kVBlock + 4 * gq * kVRow;
+    VRaw r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint8_t* row = vlane + (32 * c + (j < 4 ? j : 12 + j)) * kVRow;
+        r.byte[j] = row[2 + n];
+        r.d[j] = *(const uint16_t*)row;
+    }
+    return r;
+}
+template <bool TAIL>
+__device__ inline void v_convert(const VRaw& r, int c, int gq, int valid, uint32_t m_nib, uint32_t magic,
+                                 half8_t (&vop)[2]) {
+    const half2_t v_off = {(_Float16)1032.f, (_Float16)1032.f};   // 1024 + 8
 #pragma unroll
     for (int jp = 0; jp < 4; ++jp) {
         const int j0 = 2 * jp, j1 = 2 * jp + 1;
-        const int o0 = 32 * c + (j0 < 4 ? j0 : 12 + j0), o1 = 32 * c + (j1 < 4 ? j1 : 12 + j1);
-        const uint8_t* r0p = vlane + o0 * kVRow;
-        const uint8_t* r1p = vlane + o1 * kVRow;
-        uint32_t d0 = *(const uint16_t*)r0p, d1 = *(const uint16_t*)r1p;
+        uint32_t d0 = r.d[j0], d1 = r.d[j1];
         if constexpr (TAIL) {
+            const int o0 = 32 * c + (j0 < 4 ? j0 : 12 + j0), o1 = 32 * c + (j1 < 4 ? j1 : 12 + j1);
             d0 = o0 + 4 * gq < valid ? d0 : 0u;
             d1 = o1 + 4 * gq < valid ? d1 : 0u;
         }
         const half2_t dd = as_h2(d0 | (d1 << 16));
-        const uint32_t x = __builtin_amdgcn_perm((uint32_t)r1p[2 + n], (uint32_t)r0p[2 + n], 0x0c040c00u);
+        const uint32_t x = __builtin_amdgcn_perm(r.byte[j1], r.byte[j0], 0x0c040c00u);
         const half2_t lo = (as_h2((x & m_nib) | magic) - v_off) * dd;          // channel n
         const half2_t hi = (as_h2(((x >> 4) & m_nib) | magic) - v_off) * dd;   // channel 16 + n
         vop[0][j0] = lo[0]; vop[0][j1] = lo[1];
         vop[1][j0] = hi[0]; vop[1][j1] = hi[1];
     }
+}
+template <bool TAIL>
+__device__ inline void v_fragments(const uint8_t* v_lds, int b, int c, int gq, int n, int valid,
+                                   uint32_t m_nib, uint32_t magic, half8_t (&vop)[2]) {
+    v_convert<TAIL>(v_raw(v_lds, b, c, gq, n), c, gq, valid, m_nib, magic, vop);
 }
 
 // Offsets of the staged operands of one (page, kv head) tile.
@@ -189,11 +228,13 @@ void mfma_kernel(AttendArgs a) {
     static_assert(kChunks * RT * 64 * 16 <= kKTile, "P operands must fit in the K tile");
     __shared__ MfmaSmem<RT, STAGED> sm;
     // 1-D grid: the ring refill workgroups first (so that they start at
-    // once), then the work items (segment, kv head, row tile) with the row tile
-    // fastest. Workgroups go to the 8 XCDs round-robin by linear index; the
-    // work is permuted so that each XCD takes a contiguous range of work items,
-    // and the row tiles of one (segment, kv head), which read the same pages,
-    // run together on one XCD and share its L2.
+    // once), then the workers. A worker owns one (kv head, row tile) and walks
+    // the segments slice, slice + n_slices, ...: its query operands are built
+    // once, and each segment's first page is fetched while the one before is
+    // finished. Workgroups go to the 8 XCDs round-robin by linear index; the
+    // workers are permuted so that each XCD takes a contiguous range, and the
+    // row tiles of one kv head, which read the same pages, run together on one
+    // XCD and share its L2.
     const int G = a.G, R = a.n_q * G;
     const int n_rt = (R + 16 * RT - 1) / (16 * RT);
     const int n_copy8 = (copy_workgroups(a.copy) + 7) & ~7;
@@ -202,27 +243,24 @@ void mfma_kernel(AttendArgs a) {
         copy_role(a.copy, L);
         return;
     }
-    const int n_work = a.n_segs * a.n_kv_heads * n_rt;
+    const int n_work = a.n_slices * a.n_kv_heads * n_rt;
     const int per_xcd = ((n_work + 7) & ~7) / 8;
     const int work = ((L - n_copy8) & 7) * per_xcd + ((L - n_copy8) >> 3);
     if (work >= n_work) return;
-    const int seg_i = work / (n_rt * a.n_kv_heads);
+    const int slice = work / (n_rt * a.n_kv_heads);
     const int g = (work / n_rt) % a.n_kv_heads;
     const int r0 = (work % n_rt) * 16 * RT;
+    if (slice >= a.n_segs) return;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int n = lane & 15, gq = lane >> 4;   // MFMA row/column index and lane group
     typedef int int4v __attribute__((ext_vector_type(4)));
-    const int4v segv = scalar_load((const int4v*)(a.segs + seg_i));
-    const Seg seg = {segv.x, segv.y, segv.z, segv.w};
 
     auto issue_page = [&](int page) {
         if constexpr (!STAGED) dma_page_tiles(page_record(a.ps, page), g, a.n_kv_heads, sm.k, sm.v, w, lane);
     };
-    issue_page(seg.page0);
-    // staged operands of this segment's first page, for kv head g
+    issue_page(scalar_load(&a.segs[slice].page0));
+    // staged operands of the current segment's first page, for kv head g
     const uint8_t* stile = nullptr;
-    if constexpr (STAGED)
-        stile = a.staged + ((int64_t)staged_first_tile(a.segs, seg_i) * a.n_kv_heads + g) * kStagedTile;
     // staged operands are software-pipelined through registers: the K
     // fragments of page p + 1 are loaded while page p computes P.V, and the V
     // fragments of page p run a few 32-token chunks ahead of their use
@@ -244,7 +282,13 @@ void mfma_kernel(AttendArgs a) {
             vf[c][1] = *(const half8_t*)(pt + staged_v_offset(c, 2 * w + 1, lane));
         }
     };
-    if constexpr (STAGED) load_k(stile, 0, kKAhead);
+
+    // a staged worker takes one segment: fetch its first K fragments before
+    // the query operands are built
+    if constexpr (STAGED) {
+        stile = a.staged + ((int64_t)staged_first_tile(a.segs, slice) * a.n_kv_heads + g) * kStagedTile;
+        load_k(stile, 0, kKAhead);
+    }
 
     // ---- this lane's query rows (one per row tile) and their visible prefix
     half8_t qop[RT][kNB];
@@ -291,6 +335,20 @@ void mfma_kernel(AttendArgs a) {
         }
     }
 
+    const uint32_t m_nib = vconst(0x000F000Fu), magic = vconst(0x64006400u);
+
+    // smallest visible prefix over the workgroup's rows (causal limits grow
+    // with the query index): pages below it need no mask
+    int64_t lim_min = a.n_kv;
+    if (a.causal) {
+        const int64_t c = a.q_pos0 + r0 / G + 1;
+        lim_min = c < lim_min ? c : lim_min;
+    }
+
+  for (int seg_i = slice; seg_i < a.n_segs; seg_i += a.n_slices) {
+    const int4v segv = scalar_load((const int4v*)(a.segs + seg_i));
+    const Seg seg = {segv.x, segv.y, segv.z, segv.w};
+
     // ---- running state: O^T tiles [ct][rt] hold channels 32 w + 16 ct + 4 gq + i
     // of row 16 rt + n; m and l are replicated over the lanes of a row
     f32x4 o[2][RT];
@@ -310,16 +368,6 @@ void mfma_kernel(AttendArgs a) {
             m_run[rt] = pr[kHeadDim];
             l_run[rt] = pr[kHeadDim + 1];
         }
-    }
-
-    const uint32_t m_nib = vconst(0x000F000Fu), magic = vconst(0x64006400u);
-
-    // smallest visible prefix over the workgroup's rows (causal limits grow
-    // with the query index): pages below it need no mask
-    int64_t lim_min = a.n_kv;
-    if (a.causal) {
-        const int64_t c = a.q_pos0 + r0 / G + 1;
-        lim_min = c < lim_min ? c : lim_min;
     }
 
     for (int pi = 0; pi < seg.npages; ++pi) {
@@ -346,19 +394,31 @@ void mfma_kernel(AttendArgs a) {
             for (int c = 0; c < kVAhead; ++c) load_v(stile + pi * tile_step, c);
         }
 
-        // ---- QK over this wave's 64 tokens
+        // ---- QK over this wave's 64 tokens (in-kernel conversion reads the
+        // next token tile's K bytes while converting the current one)
         f32x4 s[4][RT];
+        KRaw kr[2][STAGED ? 1 : kNB];
+        if constexpr (!STAGED) {
+#pragma unroll
+            for (int b = 0; b < kNB; ++b) kr[0][b] = k_raw(sm.k, kTokW * w + n, b, gq);
+        }
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) s[tt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (!STAGED) {
+                if (tt + 1 < 4) {
+#pragma unroll
+                    for (int b = 0; b < kNB; ++b) kr[(tt + 1) & 1][b] = k_raw(sm.k, kTokW * w + 16 * (tt + 1) + n, b, gq);
+                }
+            }
 #pragma unroll
             for (int b = 0; b < kNB; ++b) {
                 half8_t kop;
                 if constexpr (STAGED)
                     kop = kf[tt][b];
                 else
-                    kop = k_fragment(sm.k, kTokW * w + 16 * tt + n, b, gq);
+                    kop = k_convert(kr[tt & 1][b], b);
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
                     s[tt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[rt][b], s[tt][rt], 0, 0, 0);
@@ -448,6 +508,8 @@ void mfma_kernel(AttendArgs a) {
 
         // ---- P.V for channels 32 w .. 32 w + 31 (V quant block w)
         auto pv_page = [&](auto tail) {
+            VRaw vr[2];
+            if constexpr (!STAGED) vr[0] = v_raw(sm.v, w, 0, gq, n);
 #pragma unroll
             for (int c = 0; c < kChunks; ++c) {
                 half8_t vop[2];
@@ -456,7 +518,8 @@ void mfma_kernel(AttendArgs a) {
                     vop[1] = vf[c][1];
                     if (c + kVAhead < kChunks) load_v(stile + pi * tile_step, c + kVAhead);
                 } else {
-                    v_fragments<decltype(tail)::value>(sm.v, w, c, gq, n, valid, m_nib, magic, vop);
+                    if (c + 1 < kChunks) vr[(c + 1) & 1] = v_raw(sm.v, w, c + 1, gq, n);
+                    v_convert<decltype(tail)::value>(vr[c & 1], c, gq, valid, m_nib, magic, vop);
                 }
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
@@ -471,6 +534,7 @@ void mfma_kernel(AttendArgs a) {
         if constexpr (!STAGED) {
             lds_barrier();   // every wave is done with this page's tiles
             if (pi + 1 < seg.npages) issue_page(page + 1);
+            else if (seg_i + a.n_slices < a.n_segs) issue_page(scalar_load(&a.segs[seg_i + a.n_slices].page0));
         }
     }
 
@@ -490,6 +554,8 @@ void mfma_kernel(AttendArgs a) {
             pr[kHeadDim + 1] = l_run[rt];
         }
     }
+    if constexpr (STAGED) break;   // staged launches run one worker per segment
+  }
 }
 
 // Converts each (page, kv head) of a launch once into f16 MFMA operands (the
@@ -537,13 +603,35 @@ __global__ __launch_bounds__(kThreads) void stage_kernel(StageArgs a) {
     }
 }
 
+int compute_units() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
 template <int RT, bool STAGED>
 hipError_t launch_rt(const AttendArgs& a, hipStream_t stream) {
     const int R = a.n_q * a.G;
-    const int64_t n_work = (int64_t)a.n_segs * a.n_kv_heads * ((R + 16 * RT - 1) / (16 * RT));
+    const int64_t units = (int64_t)a.n_kv_heads * ((R + 16 * RT - 1) / (16 * RT));
+    // workers: one per segment, unless the launch is unstaged with few (kv
+    // head, row tile) units and many segments (a verify block over a long
+    // cache): then about as many workers as the compute units hold at once,
+    // each taking an even slice of the segments
+    const int64_t target = (int64_t)compute_units() * (RT <= 2 ? 2 : 1);
+    int64_t slices = a.n_segs;
+    if (!STAGED && units * a.n_segs > 2 * target && units * 8 <= target) slices = target / units;
+    AttendArgs b = a;
+    b.n_slices = (int32_t)slices;
+    const int64_t n_work = slices * units;
     const int64_t blocks = ((copy_workgroups(a.copy) + 7) & ~7) + ((n_work + 7) & ~7);
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((mfma_kernel<RT, STAGED>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((mfma_kernel<RT, STAGED>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, b);
     return hipGetLastError();
 }
 

@@ -218,6 +218,33 @@ def test_outputs_bit_identical_across_residency_ring_and_chunks():
                 c.close()
 
 
+def test_verify_over_many_segments_slices_them_across_workers():
+    """A verify block over many single-page groups: the matrix-core launch
+    (8 kv heads x one 32-row tile, 160 segments; more than twice the 512
+    workers that 256 compute units hold) gives each worker a slice of the
+    segments, some two and some three. All resident, checked against the
+    oracle; all streamed through the ring, whose chunk launches take one
+    worker per segment, the same bits."""
+    n_q, n_kv = 4, 160 * 256 - 45
+    base = None
+    for v in [dict(resident=mask_all, ring=8, chunk=2),
+              dict(resident=mask_none, ring=8, chunk=2, flags=kvs.FLAG_POISON_RING)]:
+        c = small_case(v["resident"], cid=41, n_layers=2, n_kv=n_kv, Hkv=8, Hq=48, max_q=n_q, ring=v["ring"],
+                       chunk=v["chunk"], streams=1, group=1, flags=v.get("flags", 0))
+        try:
+            qs = [c.queries(l, n_q, "f32") for l in range(c.L)]
+            outs, lses = c.attend_all(qs, q_pos0=n_kv - n_q, scale=1.0, causal=True)
+            if base is None:
+                check(c, outs, lses, qs, q_pos0=n_kv - n_q, scale=1.0, causal=True)
+                base = (outs, lses)
+            else:
+                for l in range(c.L):
+                    assert np.array_equal(outs[l], base[0][l]), (v, l)
+                    assert np.array_equal(lses[l], base[1][l]), (v, l)
+        finally:
+            c.close()
+
+
 @pytest.mark.parametrize("n_q", [1, 4], ids=["decode", "verify"])
 def test_empty_cache_returns_zero_and_minus_inf(n_q):
     c = small_case(mask_all, n_layers=1, max_q=n_q)
