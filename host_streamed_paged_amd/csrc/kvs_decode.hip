@@ -67,15 +67,15 @@ __device__ inline float dpp_ror8(float v) {
 __device__ inline float max_over_tokens(float v) {
     v = fmaxf(v, dpp_ror4(v));
     v = fmaxf(v, dpp_ror8(v));
-    v = fmaxf(v, __shfl_xor(v, 16, 64));
-    v = fmaxf(v, __shfl_xor(v, 32, 64));
+    v = max_xor16(v);
+    v = max_xor32(v);
     return v;
 }
 __device__ inline float sum_over_tokens(float v) {
     v += dpp_ror4(v);
     v += dpp_ror8(v);
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
+    v = add_xor16(v);
+    v = add_xor32(v);
     return v;
 }
 
@@ -197,8 +197,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
         float amax = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));   // the row's 16 threads
+        // over the row's 16 threads: quad, then rotations by 4 and 8 in the row
+        amax = fmaxf(amax, dpp_xor1(amax));
+        amax = fmaxf(amax, dpp_xor2(amax));
+        amax = fmaxf(amax, dpp_ror4(amax));
+        amax = fmaxf(amax, dpp_ror8(amax));
         // |code| <= 32639 keeps the high byte of (code + 128) >> 8 inside int8;
         // a negative softmax scale is folded into the codes' sign
         const float inv = amax > 0.f ? (a.scale_log2 < 0.f ? -32639.f : 32639.f) / amax : 0.f;

@@ -38,6 +38,29 @@ __device__ inline void dma16(const void* gsrc, void* lds_base) {
                                      (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
 
+// This lane's value combined with lane (i ^ 16) / (i ^ 32)'s by max or add.
+// v_permlane16_swap / v_permlane32_swap hand every lane both values without an
+// LDS round trip; max and add are commutative, so every lane of the pair gets
+// the same bits.
+__device__ inline float f_bits(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ inline uint32_t u_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ inline float max_xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u_bits(v), u_bits(v), false, false);
+    return fmaxf(f_bits(r[0]), f_bits(r[1]));
+}
+__device__ inline float max_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(u_bits(v), u_bits(v), false, false);
+    return fmaxf(f_bits(r[0]), f_bits(r[1]));
+}
+__device__ inline float add_xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u_bits(v), u_bits(v), false, false);
+    return f_bits(r[0]) + f_bits(r[1]);
+}
+__device__ inline float add_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(u_bits(v), u_bits(v), false, false);
+    return f_bits(r[0]) + f_bits(r[1]);
+}
+
 // Page record of logical page `page` for this launch: a resident slot, or a
 // slot of the ring chunk the launch works on.
 __device__ inline const uint8_t* page_record(const PageSource& ps, int32_t page) {

@@ -445,8 +445,8 @@ void mfma_kernel(AttendArgs a) {
             for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) mx[rt] = fmaxf(mx[rt], s[tt][rt][i]);
-            mx[rt] = fmaxf(mx[rt], __shfl_xor(mx[rt], 16, 64));
-            mx[rt] = fmaxf(mx[rt], __shfl_xor(mx[rt], 32, 64));
+            mx[rt] = max_xor16(mx[rt]);
+            mx[rt] = max_xor32(mx[rt]);
             if (gq == 0) sm.red_m[w][16 * rt + n] = mx[rt];
         }
         lds_barrier();   // maxima published; every wave is done reading the K tile
@@ -480,8 +480,8 @@ void mfma_kernel(AttendArgs a) {
                 }
                 *(half8_t*)(pbuf + (((2 * w + c2) * RT + rt) * 64 + lane) * 16) = pv;
             }
-            ls += __shfl_xor(ls, 16, 64);
-            ls += __shfl_xor(ls, 32, 64);
+            ls = add_xor16(ls);
+            ls = add_xor32(ls);
             if (gq == 0) sm.red_l[w][16 * rt + n] = ls;
         }
         lds_barrier();   // P operands and row sums published
