@@ -396,16 +396,25 @@ int run_layer(kvs_pool* p, int32_t layer, hipStream_t stream, LaunchFn launch) {
         }
         return KVS_OK;
     };
+    if (n_lanes > 1) {
+        // Lane k starts by copying chunk k into a slot of the ring, which
+        // needs only the previous layer's ring reads done: the copy overlaps
+        // that layer's combine and this layer's resident launch. Its compute
+        // launches write the split-K partials, so they also wait for the
+        // caller's stream up to here (the previous combine reads them).
+        if (hipEventRecord(p->fork_ev, stream) != hipSuccess) return mark(fail(KVS_ERR_HIP, "lane fork failed"));
+        for (int k = 1; k < n_lanes; ++k) {
+            if (p->ring_used && hipStreamWaitEvent(p->lanes[k], p->ring_free, 0) != hipSuccess)
+                return mark(fail(KVS_ERR_HIP, "lane ring wait failed"));
+            if ((rc = do_launch(k, 0, 0, -1, k))) return rc;
+            if (hipStreamWaitEvent(p->lanes[k], p->fork_ev, 0) != hipSuccess) return mark(fail(KVS_ERR_HIP, "lane fork failed"));
+        }
+    }
     const int32_t c0 = (n_ch > 0 && !prefetched) ? 0 : -1;
     if (ls.res_nseg > 0 || c0 >= 0) {
         if ((rc = do_launch(0, 0, ls.res_nseg, -1, c0))) return rc;
     }
     if (n_lanes > 1) {
-        if (hipEventRecord(p->fork_ev, stream) != hipSuccess) return mark(fail(KVS_ERR_HIP, "lane fork failed"));
-        for (int k = 1; k < n_lanes; ++k) {
-            if (hipStreamWaitEvent(p->lanes[k], p->fork_ev, 0) != hipSuccess) return mark(fail(KVS_ERR_HIP, "lane fork failed"));
-            if ((rc = do_launch(k, 0, 0, -1, k))) return rc;   // lane k starts by copying chunk k
-        }
         for (int32_t c = 0; c < n_ch; ++c) {
             const ChunkPlan& cp = ls.chunks[c];
             const int32_t cc = (c + n_lanes < n_ch) ? c + n_lanes : -1;
