@@ -19,6 +19,14 @@ Parity status of each function (how it is pinned, in tests/test_oracle_*.py):
   attend           pinned: mpmath brute force on tiny inputs, closed forms
                    (single key, zero scale, dominant key, GQA constants,
                    causal prefix means, ragged tails), LSE split invariance.
+  quantize_q8_0_block, quantize_q4_0_block
+                   pinned: dequantize-then-quantize returns the block for
+                   every block whose extreme code is +-127 (Q8_0) or nibble 0
+                   (Q4_0); hand-worked blocks (half-way codes, ties on the
+                   largest magnitude, zero blocks, both scale signs); the
+                   error bound of each rule on random blocks.
+  append_rows      pinned: rows land at (page, head, row) as gather_kv reads
+                   them back; bytes outside the appended rows are unchanged.
 """
 
 from .kvs_oracle import (  # noqa: F401
@@ -33,4 +41,7 @@ from .kvs_oracle import (  # noqa: F401
     gather_kv,
     attend,
     attend_layer,
+    quantize_q8_0_block,
+    quantize_q4_0_block,
+    append_rows,
 )

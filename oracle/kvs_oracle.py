@@ -154,3 +154,98 @@ def attend_layer(records, q, *, n_kv: int, n_kv_heads: int, head_dim: int, scale
     """Gather the whole layer from its host records, then attend."""
     K, V = gather_kv(records, n_kv_heads, head_dim, 0, n_kv, page_tokens)
     return attend(q, K, V, n_kv=n_kv, scale=scale, causal=causal, q_pos0=q_pos0, heads=heads)
+
+
+# ---------------------------------------------------------------------------
+# KV append: quantizing a step's new K and V rows into the page records.
+#
+# The rule is the ggml reference quantizer for each block type (the pages
+# name the types only; their blocks come from llama.cpp's quantizers), in
+# float32 with the scale stored as the nearest binary16:
+#   Q8_0: amax = max |x_i|; d = amax / 127; id = 1 / d (0 when d = 0);
+#         q_i = round-half-away-from-zero(x_i * id), kept within [-127, 127].
+#   Q4_0: m = the element of largest magnitude (the first one on ties; +0 for
+#         an all-zero block); d = m / -8; id = 1 / d (0 when d = 0);
+#         nibble_i = min(15, trunc(x_i * id + 8.5)).
+# Each step below is one float32 operation, rounded to nearest even, written
+# out one element at a time so that it can be read against the rule.
+# Inputs must be finite, with a block's max |x| either 0 or at least 2^-100
+# (so that 1 / d stays finite).
+# ---------------------------------------------------------------------------
+
+def _f16_bits(d32) -> int:
+    return int(np.array([d32], dtype=np.float32).astype(np.float16).view(np.uint16)[0])
+
+
+def quantize_q8_0_block(x) -> np.ndarray:
+    """32 float32 values -> one Q8_0 block (uint8 [34])."""
+    x = np.asarray(x, dtype=np.float32)
+    assert x.shape == (QK,)
+    amax = np.float32(0.0)
+    for v in x:
+        a = np.float32(abs(v))
+        if a > amax:
+            amax = a
+    d = np.float32(amax / np.float32(127.0))
+    inv = np.float32(np.float32(1.0) / d) if d != 0 else np.float32(0.0)
+    out = np.zeros(Q8_0_BYTES, dtype=np.uint8)
+    bits = _f16_bits(d)
+    out[0], out[1] = bits & 0xFF, bits >> 8
+    for i, v in enumerate(x):
+        y = float(np.float32(v * inv))            # a float32 value, exact as a Python float
+        r = math.floor(abs(y) + 0.5)              # exact: |y| + 0.5 is exact in float64
+        q = int(math.copysign(r, y)) if r else 0
+        q = max(-127, min(127, q))
+        out[2 + i] = q & 0xFF
+    return out
+
+
+def quantize_q4_0_block(x) -> np.ndarray:
+    """32 float32 values -> one Q4_0 block (uint8 [18])."""
+    x = np.asarray(x, dtype=np.float32)
+    assert x.shape == (QK,)
+    amax, m = np.float32(0.0), np.float32(0.0)
+    for v in x:
+        a = np.float32(abs(v))
+        if a > amax:
+            amax, m = a, v
+    d = np.float32(m / np.float32(-8.0))
+    inv = np.float32(np.float32(1.0) / d) if d != 0 else np.float32(0.0)
+    nib = []
+    for v in x:
+        y = np.float32(np.float32(v * inv) + np.float32(8.5))
+        nib.append(min(15, int(math.trunc(float(y)))))
+    out = np.zeros(Q4_0_BYTES, dtype=np.uint8)
+    bits = _f16_bits(d)
+    out[0], out[1] = bits & 0xFF, bits >> 8
+    for j in range(16):
+        out[2 + j] = nib[j] | (nib[j + 16] << 4)
+    return out
+
+
+def append_rows(records, k_new, v_new, *, pos0: int, n_kv_heads: int, head_dim: int,
+                page_tokens: int = 256) -> np.ndarray:
+    """Copy of the page records (uint8 [n_pages, page_bytes]) with tokens
+    pos0 .. pos0 + n - 1 replaced by the quantized rows of k_new / v_new
+    ([n, Hkv, head_dim]; float16 inputs are widened to float32 exactly).
+    Token t goes to page t // page_tokens, row t % page_tokens; every other
+    byte is kept."""
+    recs = np.array(records, dtype=np.uint8, copy=True)
+    k_new = np.asarray(k_new).astype(np.float32)
+    v_new = np.asarray(v_new).astype(np.float32)
+    n, H, T = k_new.shape[0], n_kv_heads, page_tokens
+    nb = head_dim // QK
+    assert k_new.shape == (n, H, head_dim) and v_new.shape == (n, H, head_dim)
+    assert recs.shape[1] == page_bytes(H, head_dim, T)
+    k_tile, v_tile = T * nb * Q8_0_BYTES, T * nb * Q4_0_BYTES
+    for i in range(n):
+        t = pos0 + i
+        page, r = t // T, t % T
+        assert page < recs.shape[0]
+        for g in range(H):
+            for b in range(nb):
+                ko = g * k_tile + (r * nb + b) * Q8_0_BYTES
+                recs[page, ko:ko + Q8_0_BYTES] = quantize_q8_0_block(k_new[i, g, b * QK:(b + 1) * QK])
+                vo = H * k_tile + g * v_tile + (r * nb + b) * Q4_0_BYTES
+                recs[page, vo:vo + Q4_0_BYTES] = quantize_q4_0_block(v_new[i, g, b * QK:(b + 1) * QK])
+    return recs
