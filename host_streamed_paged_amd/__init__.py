@@ -35,7 +35,7 @@ EXPORTS = [
     "kvs_type_pair_supported", "kvs_config_validate", "kvs_page_bytes", "kvs_min_budget_bytes",
     "kvs_slots_for_budget", "kvs_plan_layer", "kvs_pool_create", "kvs_pool_destroy", "kvs_host_pages_set",
     "kvs_page_table_set", "kvs_stream_enqueue", "kvs_attend", "kvs_status", "kvs_debug_gather",
-    "kvs_debug_read_page", "kvs_last_error", "kvs_profile_enable", "kvs_profile_read",
+    "kvs_debug_read_page", "kvs_last_error", "kvs_profile_enable", "kvs_profile_read", "kvs_append",
 ]
 
 
@@ -92,6 +92,7 @@ def lib() -> ctypes.CDLL:
         "kvs_attend": (ctypes.c_int, [P, I32, P, I32, I32, I64, I64, F, I32, P, P, P]),
         "kvs_status": (ctypes.c_int, [P, ctypes.POINTER(KvsStatus)]),
         "kvs_debug_gather": (ctypes.c_int, [P, I32, I64, I64, P, P, P]),
+        "kvs_append": (ctypes.c_int, [P, I32, P, P, I32, I64, I32, P]),
         "kvs_debug_read_page": (ctypes.c_int, [P, I32, I32, P]),
         "kvs_last_error": (ctypes.c_char_p, []),
         "kvs_profile_enable": (ctypes.c_int, [P, I32]),
@@ -242,6 +243,15 @@ class Pool:
             assert lse.dtype == torch.float32 and lse.is_contiguous() and lse.shape == q.shape[:2]
         _check(lib().kvs_attend(self._h, layer, _ptr(q), qd, q.shape[0], q_pos0, n_kv, float(scale),
                                 1 if causal else 0, _ptr(out), _ptr(lse), _stream(stream)))
+
+    def append(self, layer: int, k_new: torch.Tensor, v_new: torch.Tensor, pos0: int, stream=None):
+        """Quantize new K and V rows [n_tok, Hkv, head_dim] (f32 or f16, on the
+        device) into the layer's records at tokens pos0 .. pos0 + n_tok - 1."""
+        if k_new.dtype != v_new.dtype or k_new.dtype not in (torch.float32, torch.float16):
+            raise TypeError("k_new and v_new must both be float32 or both float16")
+        assert k_new.is_contiguous() and v_new.is_contiguous() and k_new.shape == v_new.shape and k_new.dim() == 3
+        dt = Q_F32 if k_new.dtype == torch.float32 else Q_F16
+        _check(lib().kvs_append(self._h, layer, _ptr(k_new), _ptr(v_new), dt, pos0, k_new.shape[0], _stream(stream)))
 
     def status(self) -> KvsStatus:
         st = KvsStatus()

@@ -150,7 +150,23 @@ struct GatherArgs {
     float* v_out;
 };
 
+// KV append: new K and V rows [n_tok, Hkv, 128] (f32 or f16) quantized into
+// the page records of tokens pos0 .. pos0 + n_tok - 1.
+struct AppendArgs {
+    const void* k;
+    const void* v;
+    int32_t f16;              // 1: inputs are f16, 0: f32
+    int64_t pos0;
+    int32_t n_tok;
+    int32_t n_kv_heads;
+    int64_t page_bytes;
+    const int32_t* src;       // the layer's device page table (slot >= 0 when resident)
+    uint8_t* slots;           // resident slots
+    uint8_t* host;            // the layer's host records (pinned, device-visible)
+};
+
 hipError_t launch_attend(const AttendArgs& a, hipStream_t stream);
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 // few-row VALU decode kernel (kvs_decode.hip): rows = n_q * G in [1, 6]
 bool decode_supports(int rows);
 hipError_t launch_decode(const AttendArgs& a, hipStream_t stream);

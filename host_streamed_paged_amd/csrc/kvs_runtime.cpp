@@ -149,6 +149,8 @@ struct kvs_pool {
     hipEvent_t ring_free = nullptr;  // recorded on the compute stream after a layer's last ring read
     bool ring_used = false;          // ring_free has been recorded at least once
     hipEvent_t last_work = nullptr;  // recorded after every attend / gather
+    hipEvent_t append_ev = nullptr;  // recorded after every kvs_append
+    bool appended = false;           // append_ev has been recorded at least once
     hipStream_t lanes[kMaxLanes] = {};   // compute lanes 1.. for ring chunks (lane 0 is the caller's stream)
     hipEvent_t fork_ev = nullptr;
     hipEvent_t join_ev[kMaxLanes] = {};
@@ -326,6 +328,7 @@ int prefetch(kvs_pool* p, int32_t layer) {
     const LayerState& ls = p->layers[layer];
     hipStream_t cs = p->copy[0];
     if (p->ring_used) KVS_HIP(hipStreamWaitEvent(cs, p->ring_free, 0));
+    if (p->appended) KVS_HIP(hipStreamWaitEvent(cs, p->append_ev, 0));   // host records it copies
     kvs::CopyJob cj = make_copy(p, ls, 0, p->ring_next);
     hipError_t e = kvs::launch_copy(cj, cs);
     if (e != hipSuccess) { p->broken = true; return fail(KVS_ERR_HIP, "prefetch copy launch failed: %s", hipGetErrorString(e)); }
@@ -377,6 +380,10 @@ int run_layer(kvs_pool* p, int32_t layer, hipStream_t stream, LaunchFn launch) {
         if (hipStreamWaitEvent(stream, p->ring_free, 0) != hipSuccess) return mark(fail(KVS_ERR_HIP, "hipStreamWaitEvent(ring) failed"));
     }
     p->pf_layer = -1;
+    // rows appended on another stream must be in the host records and slots
+    // before this layer's launches read them
+    if (p->appended && hipStreamWaitEvent(stream, p->append_ev, 0) != hipSuccess)
+        return mark(fail(KVS_ERR_HIP, "hipStreamWaitEvent(append) failed"));
     const int n_lanes = lanes_for(R, n_ch, ls.whole_groups);
     auto slot_of = [&](int32_t c) { return (slot0 + c) % R; };
     auto do_launch = [&](int lane, int32_t seg0, int32_t nseg, int32_t c_compute, int32_t c_copy) -> int {
@@ -406,6 +413,8 @@ int run_layer(kvs_pool* p, int32_t layer, hipStream_t stream, LaunchFn launch) {
         for (int k = 1; k < n_lanes; ++k) {
             if (p->ring_used && hipStreamWaitEvent(p->lanes[k], p->ring_free, 0) != hipSuccess)
                 return mark(fail(KVS_ERR_HIP, "lane ring wait failed"));
+            if (p->appended && hipStreamWaitEvent(p->lanes[k], p->append_ev, 0) != hipSuccess)
+                return mark(fail(KVS_ERR_HIP, "lane append wait failed"));
             if ((rc = do_launch(k, 0, 0, -1, k))) return rc;
             if (hipStreamWaitEvent(p->lanes[k], p->fork_ev, 0) != hipSuccess) return mark(fail(KVS_ERR_HIP, "lane fork failed"));
         }
@@ -575,7 +584,7 @@ int kvs_pool_create(const kvs_config* cfg, void* dev_arena, uint64_t budget_byte
     auto cleanup = [&](const char* what, hipError_t e) {
         for (auto s : p->copy) (void)hipStreamDestroy(s);
         for (auto s : p->lanes) if (s) (void)hipStreamDestroy(s);
-        for (hipEvent_t ev : {p->pf_done, p->ring_free, p->last_work, p->fork_ev}) if (ev) (void)hipEventDestroy(ev);
+        for (hipEvent_t ev : {p->pf_done, p->ring_free, p->last_work, p->fork_ev, p->append_ev}) if (ev) (void)hipEventDestroy(ev);
         for (hipEvent_t ev : p->join_ev) if (ev) (void)hipEventDestroy(ev);
         delete p;
         return fail(KVS_ERR_HIP, "%s failed: %s", what, hipGetErrorString(e));
@@ -586,7 +595,7 @@ int kvs_pool_create(const kvs_config* cfg, void* dev_arena, uint64_t budget_byte
         if (e != hipSuccess) return cleanup("hipStreamCreateWithFlags", e);
         p->copy.push_back(s);
     }
-    for (hipEvent_t* ev : {&p->pf_done, &p->ring_free, &p->last_work, &p->fork_ev}) {
+    for (hipEvent_t* ev : {&p->pf_done, &p->ring_free, &p->last_work, &p->fork_ev, &p->append_ev}) {
         hipError_t e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
         if (e != hipSuccess) return cleanup("hipEventCreateWithFlags", e);
     }
@@ -612,10 +621,11 @@ void kvs_pool_destroy(kvs_pool* p) {
     if (!p) return;
     for (auto s : p->copy) (void)hipStreamSynchronize(s);
     if (p->last_work) (void)hipEventSynchronize(p->last_work);
+    if (p->appended) (void)hipEventSynchronize(p->append_ev);
     for (auto s : p->lanes) if (s) (void)hipStreamSynchronize(s);
     for (auto s : p->copy) (void)hipStreamDestroy(s);
     for (auto s : p->lanes) if (s) (void)hipStreamDestroy(s);
-    for (hipEvent_t ev : {p->pf_done, p->ring_free, p->last_work, p->fork_ev}) if (ev) (void)hipEventDestroy(ev);
+    for (hipEvent_t ev : {p->pf_done, p->ring_free, p->last_work, p->fork_ev, p->append_ev}) if (ev) (void)hipEventDestroy(ev);
     for (hipEvent_t ev : p->join_ev) if (ev) (void)hipEventDestroy(ev);
     for (auto& v : p->prof_ev)
         for (auto& pr : v) { (void)hipEventDestroy(pr.first); (void)hipEventDestroy(pr.second); }
@@ -673,6 +683,7 @@ int kvs_page_table_set(kvs_pool* p, int32_t layer, int32_t n_pages, const uint8_
     p->st.slots_used = p->n_slots - (int64_t)p->slot_free.size();
     hipStream_t s = (hipStream_t)stream;
     KVS_HIP(hipStreamWaitEvent(s, p->last_work, 0));
+    if (p->appended) KVS_HIP(hipStreamWaitEvent(s, p->append_ev, 0));
     for (int32_t i = 0; i < n_pages; ++i)
         if (ls.src[i] >= 0) {
             KVS_HIP(hipMemcpyAsync(p->slots + (uint64_t)ls.src[i] * p->L.page_bytes, ls.host + (uint64_t)i * p->L.page_bytes,
@@ -830,6 +841,46 @@ int kvs_debug_gather(kvs_pool* p, int32_t layer, int64_t tok0, int64_t n_tok, fl
     });
     if (rc) return rc;
     if (hipEventRecord(p->last_work, s) != hipSuccess) { p->broken = true; return fail(KVS_ERR_HIP, "hipEventRecord failed"); }
+    return KVS_OK;
+}
+
+int kvs_append(kvs_pool* p, int32_t layer, const void* k_new, const void* v_new, int32_t dtype, int64_t pos0,
+               int32_t n_tok, void* stream) {
+    if (!p) return fail(KVS_ERR_INVALID_ARG, "pool is NULL");
+    int rc = check_device(p);
+    if (rc) return rc;
+    if ((rc = check_layer_ready(p, layer))) return rc;
+    const LayerState& ls = p->layers[layer];
+    if (dtype != KVS_Q_F32 && dtype != KVS_Q_F16) return fail(KVS_ERR_INVALID_ARG, "dtype %d unknown", dtype);
+    if (n_tok < 0 || pos0 < 0 || pos0 + n_tok > (int64_t)ls.n_pages * kvs::kPageTokens)
+        return fail(KVS_ERR_INVALID_ARG, "tokens [%lld, %lld) outside the layer's %d pages", (long long)pos0,
+                    (long long)(pos0 + n_tok), ls.n_pages);
+    if (n_tok == 0) return KVS_OK;
+    if (!k_new || !v_new) return fail(KVS_ERR_INVALID_ARG, "k_new or v_new is NULL");
+    if ((((uintptr_t)k_new) | ((uintptr_t)v_new)) & 15) return fail(KVS_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
+    if (p->pf_layer == layer) {
+        for (int64_t pg = pos0 / kvs::kPageTokens; pg <= (pos0 + n_tok - 1) / kvs::kPageTokens; ++pg)
+            if (ls.src[pg] < 0)
+                return fail(KVS_ERR_STATE, "layer %d has a pending prefetch that may read streamed page %lld; append before kvs_stream_enqueue",
+                            layer, (long long)pg);
+    }
+    kvs::AppendArgs a{};
+    a.k = k_new;
+    a.v = v_new;
+    a.f16 = dtype == KVS_Q_F16 ? 1 : 0;
+    a.pos0 = pos0;
+    a.n_tok = n_tok;
+    a.n_kv_heads = p->cfg.n_kv_heads;
+    a.page_bytes = (int64_t)p->L.page_bytes;
+    a.src = ls.dev_src;
+    a.slots = p->slots;
+    a.host = const_cast<uint8_t*>(ls.host);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = kvs::launch_append(a, s);
+    if (e != hipSuccess) return fail(KVS_ERR_HIP, "append kernel launch failed: %s", hipGetErrorString(e));
+    p->st.kernels_launched++;
+    if (hipEventRecord(p->append_ev, s) != hipSuccess) { p->broken = true; return fail(KVS_ERR_HIP, "hipEventRecord failed"); }
+    p->appended = true;
     return KVS_OK;
 }
 

@@ -191,8 +191,8 @@ void kvs_pool_destroy(kvs_pool* pool);
 /* Register the authoritative host records of a layer: n_pages records of
  * page_bytes each, contiguous, in pinned host memory (hipHostMalloc or an
  * equivalent page-locked allocation; anything else is KVS_ERR_UNSUPPORTED).
- * The library only reads them; they must stay valid and unchanged while work
- * that reads them is in flight. */
+ * The library writes them only through kvs_append; they must stay valid, and
+ * the caller must not change them, while work that reads them is in flight. */
 int kvs_host_pages_set(kvs_pool* pool, int32_t layer, const void* pinned_records,
                        int32_t n_pages);
 
@@ -235,6 +235,31 @@ int kvs_stream_enqueue(kvs_pool* pool, int32_t layer);
 int kvs_attend(kvs_pool* pool, int32_t layer, const void* q, int32_t q_dtype, int32_t n_q,
                int64_t q_pos0, int64_t n_kv, float scale, int32_t causal, float* out,
                float* lse, void* stream);
+
+/* Append a step's new K and V rows to a layer: quantize them into Q8_0 (K)
+ * and Q4_0 (V) blocks and write them at tokens pos0 .. pos0 + n_tok - 1 of
+ * the layer, into the authoritative host records and, for each resident page,
+ * into its device slot. The pages keep the whole history in pinned host
+ * memory and a working set on the device (page 1, "Summary"; page 2, opening
+ * paragraph), so every new row reaches the host record; a streamed page is
+ * read from there by the next ring copy.
+ *   k_new, v_new: device, [n_tok, n_kv_heads, head_dim], f32 or f16 (dtype
+ *     KVS_Q_F32 / KVS_Q_F16), contiguous, 16-byte aligned, finite; a block's
+ *     largest magnitude is 0 or at least 2^-100.
+ *   The tokens must lie in the layer's pages (pos0 >= 0, pos0 + n_tok <=
+ *     256 * n_pages of its page table); grow the table with
+ *     kvs_page_table_set before appending into a new page. n_tok = 0 is a
+ *     no-op.
+ *   Block rule (ggml's reference quantizers, float32, scale stored as the
+ *     nearest binary16): Q8_0 d = max|x| / 127, code = x / d rounded half away
+ *     from zero; Q4_0 d = (first element of largest magnitude) / -8,
+ *     nibble = min(15, trunc(x / d + 8.5)).
+ * Enqueues one kernel on `stream` and returns without waiting. Later
+ * attention, gathers and prefetches of any layer wait for it. KVS_ERR_STATE
+ * if a prefetch of this layer (kvs_stream_enqueue) is pending and a target
+ * page is streamed: that prefetch may be reading the record. */
+int kvs_append(kvs_pool* pool, int32_t layer, const void* k_new, const void* v_new, int32_t dtype,
+               int64_t pos0, int32_t n_tok, void* stream);
 
 /* Counters and sizes of the pool. */
 int kvs_status(const kvs_pool* pool, kvs_status_info* info);
