@@ -170,6 +170,39 @@ def streamed_run(wl, st, steps, warmup):
     return dict(ms_per_step=e0.elapsed_time(e1) / steps, wall_ms_per_step=wall * 1e3 / steps)
 
 
+def append_leg(wl, st, steps, link):
+    """kvs_append on the resident decode pool (every page resident): a step's
+    new rows quantized into Q8_0 / Q4_0 and written to each layer's host record
+    and resident slot. One row per layer (a decode step) and a 256-row ubatch
+    per layer, at the cache's last positions; eager calls over all layers,
+    HIP events around `steps` such passes."""
+    import torch
+    pool, L, H, D = st["pool"], wl.n_layers, wl.n_kv_heads, wl.head_dim
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    out = {"note": "host record and device slot both written; bytes = rows x kv heads x 208 (136 B K + 72 B V)"}
+    for name, n in (("decode_row", 1), ("ubatch_256", 256)):
+        k = torch.randn((n, H, D), device="cuda", generator=gen)
+        v = torch.randn((n, H, D), device="cuda", generator=gen)
+        pos0 = wl.n_kv - n
+        for l in range(L):
+            pool.append(l, k, v, pos0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            for l in range(L):
+                pool.append(l, k, v, pos0)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (steps * L)
+        nbytes = n * H * 208
+        out[name] = {"rows": n, "us_per_layer": round(us, 3), "bytes_per_layer": nbytes,
+                     "host_write_gbs": round(nbytes / us / 1e3, 3)}
+        if link:
+            out[name]["frac_of_link"] = round(nbytes / us / 1e3 / link, 4)
+    return out
+
+
 def allowed_keys(wl):
     """Keys each query row may attend, summed over the block's query tokens."""
     if not wl.causal:
@@ -350,6 +383,12 @@ def main():
         f"combine {r['combine_ms_total'] / max(1, r['combine_launches']) * 1e3:.2f} us")
     qs_np = [q.cpu().numpy() for q in st["qs"]]
     recs = st["recs"]
+    link = None
+    if not args.no_streamed or not args.no_multi:
+        link = measure_link()
+    appended = append_leg(wl, st, args.steps, link)
+    log(f"append: decode row {appended['decode_row']['us_per_layer']:.2f} us/layer, 256-row ubatch "
+        f"{appended['ubatch_256']['us_per_layer']:.2f} us/layer ({appended['ubatch_256']['host_write_gbs']:.2f} GB/s)")
     st["pool"].close()
     del st
 
@@ -384,11 +423,8 @@ def main():
             "avg_launch_us": round(avg_att * 1e3, 3), "launches": r["attn_launches"],
         },
         "combine_avg_us": round(r["combine_ms_total"] / max(1, r["combine_launches"]) * 1e3, 3),
+        "append": appended,
     }
-
-    link = None
-    if not args.no_streamed or not args.no_multi:
-        link = measure_link()
     if not args.no_streamed:
         swl = WORKLOADS["streamed_decode_256k"]
         sst = setup(swl, cfg_kw, args.threads)
