@@ -36,6 +36,7 @@ EXPORTS = [
     "kvs_slots_for_budget", "kvs_plan_layer", "kvs_pool_create", "kvs_pool_destroy", "kvs_host_pages_set",
     "kvs_page_table_set", "kvs_stream_enqueue", "kvs_attend", "kvs_status", "kvs_debug_gather",
     "kvs_debug_read_page", "kvs_last_error", "kvs_profile_enable", "kvs_profile_read", "kvs_append",
+    "kvs_auto_resident_pages", "kvs_auto_stage_bytes", "kvs_auto_budget_bytes", "kvs_residency_promote_newest",
 ]
 
 
@@ -93,6 +94,10 @@ def lib() -> ctypes.CDLL:
         "kvs_status": (ctypes.c_int, [P, ctypes.POINTER(KvsStatus)]),
         "kvs_debug_gather": (ctypes.c_int, [P, I32, I64, I64, P, P, P]),
         "kvs_append": (ctypes.c_int, [P, I32, P, P, I32, I64, I32, P]),
+        "kvs_auto_resident_pages": (I32, [I64]),
+        "kvs_auto_stage_bytes": (U64, [I32, I64, U64]),
+        "kvs_auto_budget_bytes": (ctypes.c_int, [cfgp, I64, ctypes.POINTER(U64)]),
+        "kvs_residency_promote_newest": (ctypes.c_int, [P, I32, I32, I32, P]),
         "kvs_debug_read_page": (ctypes.c_int, [P, I32, I32, P]),
         "kvs_last_error": (ctypes.c_char_p, []),
         "kvs_profile_enable": (ctypes.c_int, [P, I32]),
@@ -163,6 +168,34 @@ def min_budget_bytes(cfg: Config) -> int:
 
 def slots_for_budget(cfg: Config, budget: int) -> int:
     return lib().kvs_slots_for_budget(ctypes.byref(cfg.c()), budget)
+
+
+def auto_resident_pages(n_ctx: int) -> int:
+    """Resident pages per layer under automatic sizing (kvs_auto_resident_pages)."""
+    return lib().kvs_auto_resident_pages(n_ctx)
+
+
+def auto_stage_bytes(n_layers: int, n_ctx: int, bytes_per_token: int) -> int:
+    """The pages' automatic stage size (kvs_auto_stage_bytes)."""
+    return lib().kvs_auto_stage_bytes(n_layers, n_ctx, bytes_per_token)
+
+
+def auto_budget_bytes(cfg: Config, n_ctx: int) -> int:
+    """This pool's budget for automatic residency (kvs_auto_budget_bytes)."""
+    out = ctypes.c_uint64(0)
+    _check(lib().kvs_auto_budget_bytes(ctypes.byref(cfg.c()), n_ctx, ctypes.byref(out)))
+    return out.value
+
+
+def residency_promote_newest(cur, n_new: int, max_resident: int):
+    """The residency mask after the layer grows to n_new pages
+    (kvs_residency_promote_newest)."""
+    cur = np.ascontiguousarray(np.asarray(cur, dtype=np.uint8))
+    out = np.zeros(max(1, n_new), np.uint8)
+    cp = cur.ctypes.data_as(ctypes.c_void_p) if cur.size else None
+    _check(lib().kvs_residency_promote_newest(cp, int(cur.size), n_new, max_resident,
+                                              out.ctypes.data_as(ctypes.c_void_p)))
+    return out[:n_new]
 
 
 def plan_layer(cfg: Config, resident):

@@ -44,6 +44,12 @@ int fail(int code, const char* fmt, ...) {
 constexpr uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
 constexpr int kMaxLanes = 4;   // compute lanes for ring chunks (lane 0 is the caller's stream)
+// automatic sizing (page 3, description of --kv-stream auto): a 2048-token
+// floor, an 8192 MiB ceiling, and in the stage formula that reproduces its
+// logs, 4 pages per layer above the resident ones
+constexpr int64_t kAutoFloorTokens = 2048;
+constexpr uint64_t kAutoStageExtraPages = 4;
+constexpr uint64_t kAutoCeilingBytes = 8192ull << 20;
 
 struct Layout {
     uint64_t page_bytes = 0;
@@ -546,6 +552,60 @@ int64_t kvs_slots_for_budget(const kvs_config* cfg, uint64_t budget_bytes) {
     Layout L = layout_of(cfg);
     if (budget_bytes < L.fixed) return 0;
     return (int64_t)((budget_bytes - L.fixed) / L.page_bytes);
+}
+
+int32_t kvs_auto_resident_pages(int64_t n_ctx) {
+    if (n_ctx <= 0) return 0;
+    const int64_t T = kvs::kPageTokens;
+    const int64_t ctx_pages = (n_ctx + T - 1) / T;
+    const int64_t tenth = (n_ctx + 9) / 10;                 // ceil(0.1 n_ctx) tokens
+    int64_t pages = (tenth + T - 1) / T;                    // whole pages, rounded up
+    pages = std::max<int64_t>(pages, (kAutoFloorTokens + T - 1) / T);
+    pages = std::min(pages, ctx_pages);
+    return (int32_t)std::min<int64_t>(pages, INT32_MAX);
+}
+
+uint64_t kvs_auto_stage_bytes(int32_t n_layers, int64_t n_ctx, uint64_t bytes_per_token) {
+    if (n_layers <= 0 || n_ctx <= 0 || bytes_per_token == 0) return 0;
+    const uint64_t pages = (uint64_t)kvs_auto_resident_pages(n_ctx) + kAutoStageExtraPages;
+    const long double bytes = (long double)n_layers * pages * kvs::kPageTokens * bytes_per_token;
+    return bytes >= (long double)kAutoCeilingBytes ? kAutoCeilingBytes : (uint64_t)bytes;
+}
+
+int kvs_auto_budget_bytes(const kvs_config* cfg, int64_t n_ctx, uint64_t* out) {
+    int rc = validate(cfg);
+    if (rc) return rc;
+    if (!out) return fail(KVS_ERR_INVALID_ARG, "out is NULL");
+    if (n_ctx < 0) return fail(KVS_ERR_INVALID_ARG, "n_ctx %lld < 0", (long long)n_ctx);
+    const Layout L = layout_of(cfg);
+    const long double want = (long double)L.fixed +
+                             (long double)cfg->n_layers * kvs_auto_resident_pages(n_ctx) * L.page_bytes;
+    uint64_t b = want >= (long double)kAutoCeilingBytes ? kAutoCeilingBytes : (uint64_t)want;
+    *out = std::max<uint64_t>(b, L.fixed);
+    return KVS_OK;
+}
+
+int kvs_residency_promote_newest(const uint8_t* cur, int32_t n_cur, int32_t n_new, int32_t max_resident, uint8_t* out) {
+    if (n_cur < 0 || n_new < n_cur) return fail(KVS_ERR_INVALID_ARG, "page counts %d -> %d must not shrink", n_cur, n_new);
+    if (max_resident < 0) return fail(KVS_ERR_INVALID_ARG, "max_resident %d < 0", max_resident);
+    if ((n_cur > 0 && !cur) || (n_new > 0 && !out)) return fail(KVS_ERR_INVALID_ARG, "mask is NULL");
+    std::vector<uint8_t> m(n_new, 0);
+    for (int32_t i = 0; i < n_cur; ++i) m[i] = cur[i] ? 1 : 0;
+    int64_t resident = 0;
+    for (uint8_t v : m) resident += v;
+    int32_t oldest = 0;                       // scan position for the oldest resident page
+    for (int32_t i = n_cur; i < n_new; ++i) {
+        if (max_resident == 0) break;
+        m[i] = 1;
+        ++resident;
+        while (resident > max_resident) {
+            while (oldest < i && !m[oldest]) ++oldest;
+            m[oldest] = 0;                    // oldest < i: the new page itself is never evicted here
+            --resident;
+        }
+    }
+    for (int32_t i = 0; i < n_new; ++i) out[i] = m[i];
+    return KVS_OK;
 }
 
 int kvs_pool_create(const kvs_config* cfg, void* dev_arena, uint64_t budget_bytes, kvs_pool** out_pool) {

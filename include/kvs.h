@@ -139,14 +139,51 @@ uint64_t kvs_page_bytes(const kvs_config* cfg);
  * the split-K workspace (max_q_tokens x n_q_heads rows per page group), the
  * staging regions and the per-layer tables, each rounded up to 256 bytes.
  * Staging regions exist only when a query block can exceed 64 rows per kv
- * head (max_q_tokens x n_q_heads / n_kv_heads > 64, a prefill ubatch): two of
- * max(64, group_pages) pages x n_kv_heads x 128 KiB, where each launch first
- * converts its pages once into f16 matrix-core operands. Pure. */
+ * head (max_q_tokens x n_q_heads / n_kv_heads > 64, a prefill ubatch): one
+ * per compute lane (four) of max(64, group_pages) pages x n_kv_heads x
+ * 128 KiB, where each launch first converts its pages once into f16
+ * matrix-core operands. Pure. */
 int kvs_min_budget_bytes(const kvs_config* cfg, uint64_t* out);
 
 /* Number of resident page slots a budget yields for cfg (0 if below the
  * minimum). Pure. */
 int64_t kvs_slots_for_budget(const kvs_config* cfg, uint64_t budget_bytes);
+
+/* Pool policy: automatic sizing and the newest-page residency rule.
+ *
+ * The pages size the device stage from the context alone when asked for
+ * "auto" (page 3, description: 10 % of the context resident per layer, a
+ * 2048-token floor and an 8192 MiB ceiling; its diagnostic logs print the
+ * resident tokens per layer and the stage for 64 Ki and 256 Ki contexts).
+ *
+ * kvs_auto_resident_pages: resident pages per layer for a context of n_ctx
+ *   tokens: ceil(0.1 n_ctx) rounded up to whole 256-token pages (10 % of
+ *   65536 gives 26 pages = 6656 tokens, of 262144 gives 103 = 26368, as
+ *   logged), at least 2048 tokens (8 pages), at most the context's own pages.
+ *   0 for n_ctx <= 0. Pure.
+ * kvs_auto_stage_bytes: the pages' stage size for n_layers streamed layers of
+ *   bytes_per_token bytes per token and layer: n_layers x (resident pages + 4)
+ *   x 256 x bytes_per_token, capped at 8192 MiB (reproduces the logged 255 MiB
+ *   at 64 Ki and 910 MiB at 256 Ki for 2176 B q8_0/q8_0 tokens, and 1712 MiB
+ *   at 256 Ki for 4096 B f16 tokens). Pure; 0 on non-positive arguments.
+ * kvs_auto_budget_bytes: this pool's budget for the same residency: the
+ *   minimum budget of cfg plus n_layers x resident pages x page_bytes, capped
+ *   at 8192 MiB (never below the minimum). Written to *out. Pure. */
+int32_t kvs_auto_resident_pages(int64_t n_ctx);
+uint64_t kvs_auto_stage_bytes(int32_t n_layers, int64_t n_ctx, uint64_t bytes_per_token);
+int kvs_auto_budget_bytes(const kvs_config* cfg, int64_t n_ctx, uint64_t* out);
+
+/* Residency as a context grows: the device window follows the newest tokens
+ * (page 2, "Dynamic draft eject": the draft's KV slides to follow the
+ * target's decode window). Given the current mask of
+ * n_cur pages and a layer that now has n_new >= n_cur pages, write the mask
+ * of n_new pages to out. Each new page, in order, becomes resident; then,
+ * while more than max_resident pages are resident, the oldest resident page
+ * is streamed (max_resident = 0: new pages stay streamed). Pages that were
+ * streamed stay streamed; n_new == n_cur copies the mask. out may alias cur.
+ * Pure. */
+int kvs_residency_promote_newest(const uint8_t* cur, int32_t n_cur, int32_t n_new, int32_t max_resident,
+                                 uint8_t* out);
 
 /* The launch plan kvs_page_table_set would build for one layer of n_pages
  * pages with the given residency (resident[i] != 0: page i resident). Pure
