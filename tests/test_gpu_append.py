@@ -150,3 +150,48 @@ def test_append_errors_leave_the_records_unchanged():
         assert np.array_equal(c.host[1].numpy(), before[1])
     finally:
         c.close()
+
+
+def test_append_on_another_stream_orders_before_a_multi_lane_attention():
+    """Rows appended on a side stream into a streamed page, then attention on
+    the default stream with no host synchronization in between: a 4-slot ring
+    in 2-page chunks runs two compute lanes, whose ring copies must wait for
+    the append. Checked against the oracle on the updated records, over
+    several rounds."""
+    def mask(l, n):
+        m = np.zeros(n, np.uint8)
+        m[0] = 1
+        return m
+    c = Case(cid=60, n_layers=1, n_kv_heads=H, n_q_heads=HQ, n_kv=N_KV,
+             cfg_kw=dict(max_q_tokens=4, ring_pages=8, chunk_pages=2, copy_streams=1, group_pages=1),
+             resident_fn=mask)
+    try:
+        info, _, _ = kvs.plan_layer(c.cfg, c.masks[0])
+        assert info.n_chunks >= 2 and info.whole_groups == 1
+        side = torch.cuda.Stream()
+        records = c.records[0].copy()
+        q = dev(c.queries(0, 1, "f32"))
+        for rnd in range(3):
+            pos0 = N_KV - 1 - 300 * rnd                   # pages 5, 4, 3: all streamed
+            k, v = new_rows(30 + rnd, 1, "f32")
+            # the new key is aligned with the query of its group's first head,
+            # so that the new row dominates those rows' attention: a missed
+            # append would move the output far past the bar
+            qn = c.queries(0, 1, "f32")
+            for g in range(H):
+                k[0, g] = 10.0 * qn[0, g * (HQ // H)]
+            kd, vd = dev(k), dev(v)
+            torch.cuda.synchronize()
+            with torch.cuda.stream(side):
+                c.pool.append(0, kd, vd, pos0, stream=side)
+            records = append_rows(records, k, v, pos0=pos0, n_kv_heads=H, head_dim=128)
+            out = torch.empty((1, HQ, 128), dtype=torch.float32, device="cuda")
+            c.pool.attend(0, q, N_KV, N_KV - 1, 1.0, True, out)
+            torch.cuda.synchronize()
+            ref, _ = attend_layer(records, c.queries(0, 1, "f32"), n_kv=N_KV, n_kv_heads=H, head_dim=128,
+                                  scale=1.0, causal=True, q_pos0=N_KV - 1)
+            err = normwise_error(out.cpu().numpy(), ref)
+            say(f"side-stream append round {rnd}: normwise {err:.3e}")
+            assert err <= TOL
+    finally:
+        c.close()
