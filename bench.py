@@ -203,6 +203,29 @@ def append_leg(wl, st, steps, link):
     return out
 
 
+def zero_copy_leg(wl, st, cfg_kw, steps, link):
+    """The A/B against the ring (KVS_FLAG_ZERO_COPY): a second pool over the
+    same pinned host records and residency, whose attention kernels read the
+    streamed pages in place over the link instead of through the ring."""
+    import host_streamed_paged_amd as kvs
+    cfg = kvs.Config(n_layers=wl.n_layers, n_kv_heads=wl.n_kv_heads, n_q_heads=wl.n_q_heads,
+                     max_pages=wl.n_pages, max_q_tokens=wl.n_q, flags=kvs.FLAG_ZERO_COPY, **cfg_kw)
+    arena = kvs.Pool.arena_for(cfg, int(sum(int(m.sum()) for m in st["masks"])))
+    pool = kvs.Pool(cfg, arena)
+    for l in range(wl.n_layers):
+        pool.host_pages_set(l, st["host"][l])
+        pool.page_table_set(l, st["masks"][l])
+    sr = streamed_run(wl, dict(st, pool=pool, cfg=cfg, arena=arena), steps, 2)
+    pool.close()
+    pb = st["recs"][0].shape[1]
+    streamed_bytes = sum(int((1 - m).sum()) for m in st["masks"]) * pb
+    sec = sr["ms_per_step"] / 1e3
+    log(f"{wl.name} zero-copy: {sr['ms_per_step']:.3f} ms/step, streamed {streamed_bytes / sec / 1e9:.2f} GB/s")
+    return {"ms_per_step": round(sr["ms_per_step"], 4), "streamed_gbs": round(streamed_bytes / sec / 1e9, 2),
+            "frac_of_link": round(streamed_bytes / sec / 1e9 / link, 4) if link else None,
+            "how": "attention kernels read streamed pages in place from pinned host memory; no ring, no copies"}
+
+
 def allowed_keys(wl):
     """Keys each query row may attend, summed over the block's query tokens."""
     if not wl.causal:
@@ -223,6 +246,7 @@ def multi_leg(name, cfg_kw, threads, link, steps, kind):
     total_bytes = wl.n_layers * wl.n_pages * pb
     sec = sr["ms_per_step"] / 1e3
     st["pool"].close()
+    zc = zero_copy_leg(wl, st, cfg_kw, steps, link)
     del st
     out = {
         "workload": name, "context": wl.n_kv, "query_tokens": wl.n_q, "resident_pages_per_layer": wl.resident_pages,
@@ -230,6 +254,7 @@ def multi_leg(name, cfg_kw, threads, link, steps, kind):
         "kv_gbs": round(total_bytes / sec / 1e9, 2), "streamed_gbs": round(streamed_bytes / sec / 1e9, 2),
         "link_gbs_measured": round(link, 2), "frac_of_link": round(streamed_bytes / sec / 1e9 / link, 4),
         "streamed_bytes_per_step": streamed_bytes, **cfg_kw,
+        "zero_copy": zc,
     }
     log(f"{name}: {sr['ms_per_step']:.3f} ms/step, streamed {streamed_bytes / sec / 1e9:.2f} GB/s of link {link:.2f}")
     rwl = dataclasses.replace(wl, resident_pages=wl.n_pages)
@@ -449,6 +474,7 @@ def main():
         log(f"{swl.name}: {sr['ms_per_step']:.3f} ms/step, streamed {streamed_bytes / sec / 1e9:.2f} GB/s "
             f"of link {link:.2f} GB/s")
         sst["pool"].close()
+        result["streamed"]["zero_copy"] = zero_copy_leg(swl, sst, cfg_kw, args.streamed_steps, link)
         del sst
 
     if not args.no_multi:

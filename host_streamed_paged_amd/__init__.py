@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libkvs.so")
 TYPE_F16, TYPE_Q4_0, TYPE_Q8_0 = 1, 2, 8
 Q_F32, Q_F16 = 0, 1
 FLAG_POISON_RING = 1
+FLAG_ZERO_COPY = 2
 
 OK = 0
 ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_BUDGET, ERR_NO_SLOTS = -1, -2, -3, -4

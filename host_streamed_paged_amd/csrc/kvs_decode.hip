@@ -134,11 +134,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
     // (global_load_lds_dwordx4, 16 bytes per lane); K blocks go to registers.
     uint8_t* vt = sm.v[w];
     constexpr int kVU4 = kSlice * kVRow / 16;   // 288 uint4 per slice
-    auto page_rec = [&](int page) -> const uint8_t* {
-        const int32_t sv = scalar_load(a.ps.src + page);
-        return sv >= 0 ? a.ps.slots + (int64_t)sv * a.ps.page_bytes
-                       : a.ps.ring_chunk + (int64_t)((-1 - sv) - a.ps.chunk_rank0) * a.ps.page_bytes;
-    };
+    auto page_rec = [&](int page) -> const uint8_t* { return page_record(a.ps, page); };
     auto issue_k = [&](const uint8_t* rec, uint32_t (&kw)[4][9]) {
         const uint8_t* kt = rec + (int64_t)g * kKTile + kboff;
 #pragma unroll

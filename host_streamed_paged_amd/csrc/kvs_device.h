@@ -61,12 +61,14 @@ __device__ inline float add_xor32(float v) {
     return f_bits(r[0]) + f_bits(r[1]);
 }
 
-// Page record of logical page `page` for this launch: a resident slot, or a
-// slot of the ring chunk the launch works on.
+// Page record of logical page `page` for this launch: a resident slot, a
+// slot of the ring chunk the launch works on, or (zero-copy launches) the
+// pinned host record itself.
 __device__ inline const uint8_t* page_record(const PageSource& ps, int32_t page) {
     const int32_t sv = scalar_load(ps.src + page);
-    return sv >= 0 ? ps.slots + (int64_t)sv * ps.page_bytes
-                   : ps.ring_chunk + (int64_t)((-1 - sv) - ps.chunk_rank0) * ps.page_bytes;
+    if (sv >= 0) return ps.slots + (int64_t)sv * ps.page_bytes;
+    if (ps.host) return ps.host + (int64_t)page * ps.page_bytes;
+    return ps.ring_chunk + (int64_t)((-1 - sv) - ps.chunk_rank0) * ps.page_bytes;
 }
 
 }  // namespace kvs

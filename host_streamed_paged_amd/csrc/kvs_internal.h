@@ -33,18 +33,21 @@ constexpr int32_t kSegFresh = 1;
 
 // Where page p's record lives: src[p] >= 0 is a resident slot index;
 // src[p] < 0 means streamed with rank -1 - src[p], found in the ring chunk of
-// the current launch at position rank - chunk_rank0.
+// the current launch at position rank - chunk_rank0, or, in a zero-copy
+// launch (host set), read in place from the pinned host record of page p.
 struct PageSource {
     const uint8_t* slots;       // base of the resident slots
     const uint8_t* ring_chunk;  // first ring slot of this launch's chunk (null if none)
     const int32_t* src;         // [n_pages] device table
     int32_t chunk_rank0;        // streamed rank of the chunk's first page
     int64_t page_bytes;
+    const uint8_t* host;        // zero-copy launches: the layer's host records, else null
 };
 
 __host__ __device__ inline const uint8_t* page_ptr(const PageSource& ps, int32_t page) {
     int32_t s = ps.src[page];
     if (s >= 0) return ps.slots + (int64_t)s * ps.page_bytes;
+    if (ps.host) return ps.host + (int64_t)page * ps.page_bytes;
     return ps.ring_chunk + (int64_t)((-1 - s) - ps.chunk_rank0) * ps.page_bytes;
 }
 

@@ -86,7 +86,8 @@ int validate(const kvs_config* c) {
                     kvs::kMaxCopyPages, c->ring_pages);
     if (c->copy_streams < 1 || c->copy_streams > 8) return fail(KVS_ERR_INVALID_ARG, "copy_streams %d out of range [1, 8]", c->copy_streams);
     if (c->group_pages < 1) return fail(KVS_ERR_INVALID_ARG, "group_pages %d must be >= 1", c->group_pages);
-    if (c->flags & ~uint32_t(KVS_FLAG_POISON_RING)) return fail(KVS_ERR_INVALID_ARG, "unknown flag bits 0x%x", c->flags);
+    if (c->flags & ~uint32_t(KVS_FLAG_POISON_RING | KVS_FLAG_ZERO_COPY))
+        return fail(KVS_ERR_INVALID_ARG, "unknown flag bits 0x%x", c->flags);
     return KVS_OK;
 }
 
@@ -330,6 +331,15 @@ void count_copy(kvs_pool* p, const kvs::CopyJob& cj) {
 
 // Copy chunk 0 of `layer` into the ring on the pool's copy stream, after the
 // previous ring reader is done.
+bool stream_capturing(hipStream_t s) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return cs != hipStreamCaptureStatusNone;
+}
+
 int prefetch(kvs_pool* p, int32_t layer) {
     const LayerState& ls = p->layers[layer];
     hipStream_t cs = p->copy[0];
@@ -387,9 +397,30 @@ int run_layer(kvs_pool* p, int32_t layer, hipStream_t stream, LaunchFn launch) {
     }
     p->pf_layer = -1;
     // rows appended on another stream must be in the host records and slots
-    // before this layer's launches read them
-    if (p->appended && hipStreamWaitEvent(stream, p->append_ev, 0) != hipSuccess)
+    // before this layer's launches read them (under graph capture an outside
+    // event cannot be waited on; an append on the captured stream is ordered)
+    if (p->appended && !stream_capturing(stream) && hipStreamWaitEvent(stream, p->append_ev, 0) != hipSuccess)
         return mark(fail(KVS_ERR_HIP, "hipStreamWaitEvent(append) failed"));
+    if (p->cfg.flags & KVS_FLAG_ZERO_COPY) {
+        // Zero-copy: streamed pages are read in place from the host records
+        // (the launch's PageSource carries them), so there is no ring. With
+        // whole groups every group has one segment, and a single launch takes
+        // them all; otherwise each chunk's segments run in their own launch,
+        // in order, so that a group's pages still fold in page order.
+        const int32_t n_segs = (int32_t)ls.segs.size();
+        if (n_segs == 0) return KVS_OK;
+        auto run = [&](int32_t seg0, int32_t nseg) -> int {
+            if (nseg == 0) return KVS_OK;
+            int r = launch(stream, 0, seg0, nseg, nullptr, 0, kvs::CopyJob{});
+            if (r) return mark(r);
+            p->st.kernels_launched++;
+            return KVS_OK;
+        };
+        if (n_ch == 0 || ls.whole_groups) return run(0, n_segs);
+        int r = run(0, ls.res_nseg);
+        for (int32_t c = 0; c < n_ch && !r; ++c) r = run(ls.chunks[c].seg0, ls.chunks[c].nseg);
+        return r;
+    }
     const int n_lanes = lanes_for(R, n_ch, ls.whole_groups);
     auto slot_of = [&](int32_t c) { return (slot0 + c) % R; };
     auto do_launch = [&](int lane, int32_t seg0, int32_t nseg, int32_t c_compute, int32_t c_copy) -> int {
@@ -469,7 +500,7 @@ int check_layer_ready(const kvs_pool* p, int32_t layer) {
 // Ring chunks are ordered by events across the pool's copy streams; a graph
 // captured from the compute stream cannot replay that exchange faithfully.
 int check_capture(const kvs_pool* p, int32_t layer, hipStream_t s) {
-    if (p->layers[layer].chunks.empty()) return KVS_OK;
+    if (p->layers[layer].chunks.empty() || (p->cfg.flags & KVS_FLAG_ZERO_COPY)) return KVS_OK;
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
         (void)hipGetLastError();
@@ -765,7 +796,7 @@ int kvs_stream_enqueue(kvs_pool* p, int32_t layer) {
     if ((rc = check_layer_ready(p, layer))) return rc;
     if (p->pf_layer == layer) return KVS_OK;  // already prefetched
     if ((rc = check_ring_free_for(p, layer))) return rc;
-    if (p->layers[layer].chunks.empty()) return KVS_OK;
+    if (p->layers[layer].chunks.empty() || (p->cfg.flags & KVS_FLAG_ZERO_COPY)) return KVS_OK;
     return prefetch(p, layer);
 }
 
@@ -794,6 +825,7 @@ int kvs_attend(kvs_pool* p, int32_t layer, const void* q, int32_t q_dtype, int32
     kvs::AttendArgs a{};
     a.ps.slots = p->slots;
     a.ps.src = ls.dev_src;
+    a.ps.host = (p->cfg.flags & KVS_FLAG_ZERO_COPY) ? ls.host : nullptr;
     a.ps.page_bytes = (int64_t)p->L.page_bytes;
     a.n_kv_heads = p->cfg.n_kv_heads;
     a.n_q_heads = p->cfg.n_q_heads;
@@ -882,6 +914,7 @@ int kvs_debug_gather(kvs_pool* p, int32_t layer, int64_t tok0, int64_t n_tok, fl
     kvs::GatherArgs a{};
     a.ps.slots = p->slots;
     a.ps.src = ls.dev_src;
+    a.ps.host = (p->cfg.flags & KVS_FLAG_ZERO_COPY) ? ls.host : nullptr;
     a.ps.page_bytes = (int64_t)p->L.page_bytes;
     a.n_kv_heads = p->cfg.n_kv_heads;
     a.tok0 = tok0;

@@ -82,6 +82,13 @@ extern "C" {
 /* kvs_config.flags */
 #define KVS_FLAG_POISON_RING 1u    /* debug: fill each ring chunk with 0xA5 after its
                                       kernel, before the slot is reused             */
+#define KVS_FLAG_ZERO_COPY   2u    /* streamed pages are read in place from their pinned
+                                      host records by the attention kernels (mapped
+                                      host memory over the link, no ring copies): the
+                                      A/B against the ring. The ring is unused,
+                                      kvs_stream_enqueue is a no-op, and a streamed
+                                      layer may be captured in a HIP graph. Outputs
+                                      equal the ring's bit for bit. */
 
 typedef struct kvs_config {
     int32_t n_layers;      /* layers sharing the pool and the ring (>= 1)                 */

@@ -59,7 +59,9 @@ def test_type_pair_gate():
     (dict(copy_streams=0), kvs.ERR_INVALID_ARG),
     (dict(copy_streams=9), kvs.ERR_INVALID_ARG),
     (dict(group_pages=0), kvs.ERR_INVALID_ARG),
-    (dict(flags=2), kvs.ERR_INVALID_ARG),
+    (dict(flags=kvs.FLAG_ZERO_COPY), kvs.OK),
+    (dict(flags=kvs.FLAG_ZERO_COPY | kvs.FLAG_POISON_RING), kvs.OK),
+    (dict(flags=4), kvs.ERR_INVALID_ARG),
 ])
 def test_config_validation(kw, code):
     assert kvs.config_validate(base_cfg(**kw)) == code
