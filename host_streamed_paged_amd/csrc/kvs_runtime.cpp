@@ -381,7 +381,7 @@ int lanes_for(int32_t R, int32_t n_ch, bool whole_groups) {
 }
 
 template <typename LaunchFn>
-int run_layer(kvs_pool* p, int32_t layer, hipStream_t stream, LaunchFn launch) {
+int run_layer(kvs_pool* p, int32_t layer, hipStream_t stream, int32_t run_pages, LaunchFn launch) {
     LayerState& ls = p->layers[layer];
     const int32_t n_ch = (int32_t)ls.chunks.size();
     const int32_t R = p->n_cslots;
@@ -416,6 +416,38 @@ int run_layer(kvs_pool* p, int32_t layer, hipStream_t stream, LaunchFn launch) {
             p->st.kernels_launched++;
             return KVS_OK;
         };
+        if ((n_ch == 0 || ls.whole_groups) && run_pages > 0 && !stream_capturing(stream)) {
+            // Staged launches (blocks wider than 64 rows): runs of whole
+            // segments, at most run_pages pages each, go to the compute lanes
+            // in turn, so that one lane's staging reads over the link overlap
+            // another lane's matrix-core work. Each run is staged into its
+            // lane's region; groups are whole, so no two lanes share one.
+            std::vector<std::pair<int32_t, int32_t>> runs;
+            for (int32_t i = 0; i < n_segs;) {
+                int32_t j = i, pages = 0;
+                while (j < n_segs && pages + ls.segs[j].npages <= run_pages) pages += ls.segs[j++].npages;
+                if (j == i) return mark(fail(KVS_ERR_INVALID_ARG, "internal: segment longer than a staging run"));
+                runs.emplace_back(i, j - i);
+                i = j;
+            }
+            const int n_l = (int)std::min<size_t>(kMaxLanes, runs.size());
+            if (n_l > 1) {
+                if (hipEventRecord(p->fork_ev, stream) != hipSuccess) return mark(fail(KVS_ERR_HIP, "lane fork failed"));
+                for (int k = 1; k < n_l; ++k)
+                    if (hipStreamWaitEvent(p->lanes[k], p->fork_ev, 0) != hipSuccess) return mark(fail(KVS_ERR_HIP, "lane fork failed"));
+            }
+            for (size_t r = 0; r < runs.size(); ++r) {
+                const int lane = (int)(r % n_l);
+                int e = launch(lane == 0 ? stream : p->lanes[lane], lane, runs[r].first, runs[r].second, nullptr, 0,
+                               kvs::CopyJob{});
+                if (e) return mark(e);
+                p->st.kernels_launched++;
+            }
+            for (int k = 1; k < n_l; ++k)
+                if (hipEventRecord(p->join_ev[k], p->lanes[k]) != hipSuccess || hipStreamWaitEvent(stream, p->join_ev[k], 0) != hipSuccess)
+                    return mark(fail(KVS_ERR_HIP, "lane join failed"));
+            return KVS_OK;
+        }
         if (n_ch == 0 || ls.whole_groups) return run(0, n_segs);
         int r = run(0, ls.res_nseg);
         for (int32_t c = 0; c < n_ch && !r; ++c) r = run(ls.chunks[c].seg0, ls.chunks[c].nseg);
@@ -839,7 +871,8 @@ int kvs_attend(kvs_pool* p, int32_t layer, const void* q, int32_t q_dtype, int32
     a.causal = causal ? 1 : 0;
     a.part = p->work;
     const bool staging = kvs::mfma_stages(n_q * a.G);
-    rc = run_layer(p, layer, s, [&](hipStream_t st, int lane, int32_t seg0, int32_t nseg, const uint8_t* ring_chunk,
+    rc = run_layer(p, layer, s, staging ? p->L.stage_pages : 0,
+                   [&](hipStream_t st, int lane, int32_t seg0, int32_t nseg, const uint8_t* ring_chunk,
                                     int32_t rank0, const kvs::CopyJob& cj) -> int {
         kvs::AttendArgs b = a;
         b.copy = cj;
@@ -921,7 +954,7 @@ int kvs_debug_gather(kvs_pool* p, int32_t layer, int64_t tok0, int64_t n_tok, fl
     a.n_tok = n_tok;
     a.k_out = k_out;
     a.v_out = v_out;
-    rc = run_layer(p, layer, s, [&](hipStream_t st, int /*lane*/, int32_t seg0, int32_t nseg, const uint8_t* ring_chunk,
+    rc = run_layer(p, layer, s, 0, [&](hipStream_t st, int /*lane*/, int32_t seg0, int32_t nseg, const uint8_t* ring_chunk,
                                     int32_t rank0, const kvs::CopyJob& cj) -> int {
         kvs::GatherArgs b = a;
         b.copy = cj;

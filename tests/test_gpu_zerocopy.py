@@ -111,3 +111,29 @@ def test_zero_copy_streamed_layer_replays_in_a_graph():
         del g
     finally:
         c.close()
+
+
+def test_zero_copy_staged_runs_on_lanes_equal_the_ring():
+    """A layer longer than one 64-page staging run: the zero-copy launches
+    spread the runs over compute lanes (each staging into its own region),
+    and give the ring's bits."""
+    n_kv, n_q = 70 * 256 - 31, 11                     # 70 pages: runs of 64 and 6 pages; 66 rows
+    res = []
+    for flags in (0, kvs.FLAG_ZERO_COPY):
+        say(f"staged lanes case flags={flags} n_kv={n_kv}")
+        c = Case(cid=73, n_layers=1, n_kv_heads=2, n_q_heads=12, n_kv=n_kv,
+                 cfg_kw=dict(max_q_tokens=n_q, ring_pages=8, chunk_pages=4, copy_streams=1, group_pages=1,
+                             flags=flags),
+                 resident_fn=mask_random(0.3, seed=10))
+        try:
+            qs = [c.queries(0, n_q, "f16")]
+            outs, lses = c.attend_all(qs, q_pos0=n_kv - n_q, scale=0.12, causal=True)
+            if flags:
+                ref, ref_lse = c.oracle(0, qs[0], q_pos0=n_kv - n_q, scale=0.12, causal=True)
+                err = normwise_error(outs[0], ref)
+                say(f"zero-copy staged lanes: normwise {err:.3e}")
+                assert err <= TOL and float(np.max(np.abs(lses[0] - ref_lse))) <= TOL
+            res.append((outs[0], lses[0]))
+        finally:
+            c.close()
+    assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])
