@@ -233,7 +233,7 @@ def allowed_keys(wl):
     return sum(min(wl.n_kv, wl.q_pos0 + i + 1) for i in range(wl.n_q))
 
 
-def multi_leg(name, cfg_kw, threads, link, steps, kind):
+def multi_leg(name, cfg_kw, threads, link, steps, kind, zero_copy=True):
     """A multi-query workload: the streamed step through the ring, then the
     same shapes with every page resident to time the matrix-core kernel."""
     import dataclasses
@@ -246,7 +246,7 @@ def multi_leg(name, cfg_kw, threads, link, steps, kind):
     total_bytes = wl.n_layers * wl.n_pages * pb
     sec = sr["ms_per_step"] / 1e3
     st["pool"].close()
-    zc = zero_copy_leg(wl, st, cfg_kw, steps, link)
+    zc = zero_copy_leg(wl, st, cfg_kw, steps, link) if zero_copy else None
     del st
     out = {
         "workload": name, "context": wl.n_kv, "query_tokens": wl.n_q, "resident_pages_per_layer": wl.resident_pages,
@@ -254,8 +254,9 @@ def multi_leg(name, cfg_kw, threads, link, steps, kind):
         "kv_gbs": round(total_bytes / sec / 1e9, 2), "streamed_gbs": round(streamed_bytes / sec / 1e9, 2),
         "link_gbs_measured": round(link, 2), "frac_of_link": round(streamed_bytes / sec / 1e9 / link, 4),
         "streamed_bytes_per_step": streamed_bytes, **cfg_kw,
-        "zero_copy": zc,
     }
+    if zc:
+        out["zero_copy"] = zc
     log(f"{name}: {sr['ms_per_step']:.3f} ms/step, streamed {streamed_bytes / sec / 1e9:.2f} GB/s of link {link:.2f}")
     rwl = dataclasses.replace(wl, resident_pages=wl.n_pages)
     rst = setup(rwl, cfg_kw, threads)
@@ -366,6 +367,7 @@ def main():
     ap.add_argument("--no-streamed", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-multi", action="store_true", help="skip the verify and prefill workloads")
+    ap.add_argument("--no-zero-copy", action="store_true", help="skip the zero-copy A/B runs")
     ap.add_argument("--streamed-steps", type=int, default=10)
     ap.add_argument("--threads", type=int, default=min(16, len(os.sched_getaffinity(0))))
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -474,14 +476,17 @@ def main():
         log(f"{swl.name}: {sr['ms_per_step']:.3f} ms/step, streamed {streamed_bytes / sec / 1e9:.2f} GB/s "
             f"of link {link:.2f} GB/s")
         sst["pool"].close()
-        result["streamed"]["zero_copy"] = zero_copy_leg(swl, sst, cfg_kw, args.streamed_steps, link)
+        if not args.no_zero_copy:
+            result["streamed"]["zero_copy"] = zero_copy_leg(swl, sst, cfg_kw, args.streamed_steps, link)
         del sst
 
     if not args.no_multi:
         result["verify"] = multi_leg("spec_verify_160k", dict(ring_pages=32, chunk_pages=4, copy_streams=1,
-                                                              group_pages=1), args.threads, link, 8, "verify")
+                                                              group_pages=1), args.threads, link, 8, "verify",
+                                     not args.no_zero_copy)
         result["prefill"] = multi_leg("prefill_ubatch_128k", dict(ring_pages=64, chunk_pages=8, copy_streams=1,
-                                                                  group_pages=8), args.threads, link, 6, "prefill")
+                                                                  group_pages=8), args.threads, link, 6, "prefill",
+                                      not args.no_zero_copy)
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(wl, recs, qs_np)
