@@ -25,6 +25,7 @@
 #include <hip/hip_runtime.h>
 #include <cstdint>
 #include <cmath>
+#include <type_traits>
 
 #include "kvs_internal.h"
 #include "kvs_device.h"
@@ -114,10 +115,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
         return;
     }
     const int tid = threadIdx.x;
-    const int w = tid >> 6, l = tid & 63;
-    typedef int int4v __attribute__((ext_vector_type(4)));
-    const int4v segv = scalar_load((const int4v*)(a.segs + blockIdx.x));
-    const Seg seg = {segv.x, segv.y, segv.z, segv.w};
+    // the wave index is uniform: slice bounds and masks stay in scalar registers
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
     const int g = blockIdx.y;
     const int G = a.G;
 
@@ -129,11 +128,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
     // PV role: block bb, byte position j16 (channels 32 bb + j16 and 32 bb + 16 + j16)
     const int j16 = l & 15, bb = l >> 4;
 
-    // Page loads are issued first so that their latency covers the query
-    // set-up. V rows go straight to the wave's LDS region with LDS DMA
-    // (global_load_lds_dwordx4, 16 bytes per lane); K blocks go to registers.
+    // K blocks and V rows are loaded into registers; the V rows are stored to
+    // the wave's LDS region once the scores are done. Plain loads (no LDS DMA)
+    // keep every load in flight of one kind, so that each score pass waits for
+    // its own K blocks only.
     uint8_t* vt = sm.v[w];
-    constexpr int kVU4 = kSlice * kVRow / 16;   // 288 uint4 per slice
     auto page_rec = [&](int page) -> const uint8_t* { return page_record(a.ps, page); };
     auto issue_k = [&](const uint8_t* rec, uint32_t (&kw)[4][9]) {
         const uint8_t* kt = rec + (int64_t)g * kKTile + kboff;
@@ -144,40 +143,53 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
             for (int k = 0; k < 9; ++k) kw[p][k] = src[k];
         }
     };
-    auto issue_v = [&](const uint8_t* rec) {
-        const uint4* vsrc = (const uint4*)(rec + (int64_t)a.n_kv_heads * kKTile + (int64_t)g * kVTile +
-                                           kSlice * w * kVRow);
+    // 4608 bytes of V rows per slice: four coalesced 16-byte loads and one
+    // 8-byte load per lane
+    static_assert(kSlice * kVRow == 4 * 1024 + 512, "V slice size");
+    auto issue_v = [&](const uint8_t* rec, uint4 (&vr)[4], uint2& vr2) {
+        const uint8_t* vsrc = rec + (int64_t)a.n_kv_heads * kKTile + (int64_t)g * kVTile + kSlice * w * kVRow;
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vsrc + l + 64 * k),
-                                             (__attribute__((address_space(3))) void*)(vt + 1024 * k), 16, 0, 0);
-        if (l < kVU4 - 256)
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vsrc + l + 256),
-                                             (__attribute__((address_space(3))) void*)(vt + 4096), 16, 0, 0);
+        for (int k = 0; k < 4; ++k) vr[k] = *(const uint4*)(vsrc + 1024 * k + 16 * l);
+        vr2 = *(const uint2*)(vsrc + 4096 + 8 * l);
+    };
+    auto store_v = [&](const uint4 (&vr)[4], const uint2& vr2) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) *(uint4*)(vt + 1024 * k + 16 * l) = vr[k];
+        *(uint2*)(vt + 4096 + 8 * l) = vr2;
     };
 
     // ---- query rows -> 16-bit fixed point codes per (row, block). The query
-    // loads are issued before the page loads: vector memory counters retire in
-    // order, so the set-up below waits for the query only.
+    // loads are issued first, before the segment is even known: vector memory
+    // counters retire in order, so the set-up below waits for the query only,
+    // with the page's K and V loads already in flight.
     const bool qprep = tid < R * 16;
     const int qr = tid >> 4, qb = (tid >> 2) & 3, qq = tid & 3;
     uint4 qraw0 = make_uint4(0u, 0u, 0u, 0u), qraw1 = qraw0;   // raw query bits, converted once K is queued
+    const int qi = qr / G, qhd = g * G + qr % G;
+    const uint8_t* qaddr = (const uint8_t*)a.q +
+        (((int64_t)qi * a.n_q_heads + qhd) * kHeadDim + qb * kQK + qq * 8) * (a.q_f16 ? 2 : 4);
     if (qprep) {
-        const int i = qr / G, h = g * G + qr % G;
-        const int64_t off = ((int64_t)i * a.n_q_heads + h) * kHeadDim + qb * kQK + qq * 8;
         if (a.q_f16) {
-            qraw0 = *(const uint4*)((const _Float16*)a.q + off);
+            qraw0 = *(const uint4*)qaddr;
         } else {
-            const uint4* qp = (const uint4*)((const float*)a.q + off);
-            qraw0 = qp[0];
-            qraw1 = qp[1];
+            qraw0 = ((const uint4*)qaddr)[0];
+            qraw1 = ((const uint4*)qaddr)[1];
         }
     }
-    // memory counters retire in order: query, then K blocks, then (after the
-    // query codes are in LDS) the V rows
+    typedef int int4v __attribute__((ext_vector_type(4)));
+    const int4v segv = scalar_load((const int4v*)(a.segs + blockIdx.x));
+    const Seg seg = {segv.x, segv.y, segv.z, segv.w};
+    // memory counters retire in order: query, then K blocks, then V rows
     const uint8_t* rec0 = page_rec(seg.page0);
     uint32_t kw[4][9];
+    uint4 vr[4];
+    uint2 vr2;
     issue_k(rec0, kw);
+    issue_v(rec0, vr, vr2);
+    // keeps the query address registers allocated until the page loads are
+    // issued: their reuse would make the compiler wait for the query load
+    // (and everything before it) ahead of the first K load
+    asm volatile("" ::"v"(qaddr));
     if (qprep) {
         const int r = qr;
         float x[8];
@@ -217,7 +229,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
         sm.q_lo[r][qb][2 * qq + 1] = lw[1];
         if (qb == 0 && qq == 0) sm.q_scale[r] = amax / 32639.f * fabsf(a.scale_log2);
     }
-    issue_v(rec0);
     lds_barrier();
     uint32_t qh[R][8], ql[R][8];
     float qs[R];
@@ -250,17 +261,20 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
     }
 
     uint32_t* ppw = sm.pp[w][0];
-    for (int pi = 0; pi < seg.npages; ++pi) {
+    // One page of the segment, its K blocks and V rows already in flight.
+    // With PREFETCH (every page but the segment's last), the next page's K
+    // blocks are loaded into the same registers as soon as the scores are
+    // done, and its V rows as soon as this page's rows are in LDS, so that
+    // they arrive while this page is still being computed. The last page is
+    // peeled off the loop: every load site is then unconditional and each wait
+    // covers exactly the loads it needs.
+    auto page_body = [&](int pi, auto prefetch) {
+        constexpr bool kPrefetch = decltype(prefetch)::value;
         const int page = seg.page0 + pi;
+        const uint8_t* rec_next = kPrefetch ? page_rec(page + 1) : nullptr;
         const int par = pi & 1;
         const int64_t rem = a.n_kv - (int64_t)page * kPageTokens - kSlice * w;
         const int valid = (int)(rem < 0 ? 0 : (rem > kSlice ? kSlice : rem));   // valid rows of this slice
-
-        if (pi > 0) {   // this wave is done with its LDS region of the previous page
-            const uint8_t* rec = page_rec(page);
-            issue_k(rec, kw);
-            issue_v(rec);
-        }
 
         // ---- scores. Slice row t is visible to query row r iff t <= lim[r].
         int lim[R];
@@ -300,22 +314,37 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
             }
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                // score / (row scale): the row scale is applied inside the exponent
+                // score / (row scale): the row scale is applied inside the exponent.
+                // No contraction: the product and both quad sums stay one
+                // multiply and two DPP adds (a fused multiply-add here costs a
+                // separate DPP move and a second multiply).
+#pragma clang fp contract(off)
                 float f = (float)(ih[r] * 256 + il[r]) * d;
                 f += dpp_xor1(f);
                 f += dpp_xor2(f);
                 s[p][r] = f;
             }
         }
+        if constexpr (kPrefetch) issue_k(rec_next, kw);   // the scores no longer need kw
         if (need_mask) {
 #pragma unroll
             for (int p = 0; p < 4; ++p)
 #pragma unroll
                 for (int r = 0; r < R; ++r) s[p][r] = 16 * p + u <= lim[r] ? s[p][r] : -INFINITY;
         }
-        // the V rows were loaded by LDS DMA before the K blocks; all K data has
-        // been consumed, and this makes the DMA writes visible to the reads below
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // the slice's V rows to LDS (read by other lanes of this wave only).
+        // The empty asm ties the rows to the last score so that the stores,
+        // and the wait for the V loads they imply, stay after the score passes.
+        {
+            const float dep = s[3][R - 1];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                asm volatile("" : "+v"(vr[k].x), "+v"(vr[k].y), "+v"(vr[k].z), "+v"(vr[k].w) : "v"(dep));
+            asm volatile("" : "+v"(vr2.x), "+v"(vr2.y) : "v"(dep));
+        }
+        store_v(vr, vr2);
+        if constexpr (kPrefetch) issue_v(rec_next, vr, vr2);
+        wave_lds_sync();
 
         // ---- slice maxima, probabilities and row sums.
         float m_w[R];
@@ -467,7 +496,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
                 }
             }
         }
-    }
+    };
+    for (int pi = 0; pi + 1 < seg.npages; ++pi) page_body(pi, std::true_type{});
+    page_body(seg.npages - 1, std::false_type{});
 
 #pragma unroll
     for (int k = 0; k < kMR; ++k) {
