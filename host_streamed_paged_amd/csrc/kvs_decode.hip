@@ -515,8 +515,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
 template <int R>
 hipError_t launch_r(const AttendArgs& a, hipStream_t stream) {
     const int cx = (copy_workgroups(a.copy) + a.n_kv_heads - 1) / a.n_kv_heads;
-    hipLaunchKernelGGL(decode_kernel<R>, dim3(a.n_segs + cx, a.n_kv_heads), dim3(kThreads), 0, stream, a);
-    return hipGetLastError();
+    return launch_kernel(decode_kernel<R>, dim3(a.n_segs + cx, a.n_kv_heads), dim3(kThreads), stream, a);
 }
 
 }  // namespace

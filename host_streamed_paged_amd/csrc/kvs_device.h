@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <cstdint>
 
 #include "kvs_internal.h"
@@ -69,6 +70,20 @@ __device__ inline const uint8_t* page_record(const PageSource& ps, int32_t page)
     if (sv >= 0) return ps.slots + (int64_t)sv * ps.page_bytes;
     if (ps.host) return ps.host + (int64_t)page * ps.page_bytes;
     return ps.ring_chunk + (int64_t)((-1 - sv) - ps.chunk_rank0) * ps.page_bytes;
+}
+
+// Launch a kernel; a pending timing pair (launch_timing) goes with it.
+template <typename K, typename... Args>
+inline hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, hipStream_t stream, Args... args) {
+    LaunchTiming& t = launch_timing();
+    if (t.start) {
+        const LaunchTiming u = t;
+        t = LaunchTiming{};
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, u.start, u.stop, 0, args...);
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace kvs

@@ -168,6 +168,16 @@ struct AppendArgs {
     uint8_t* host;            // the layer's host records (pinned, device-visible)
 };
 
+// Kernel timing: when the host sets a start/stop event pair here, the next
+// kernel launched by this thread carries them on its dispatch
+// (hipExtLaunchKernel), so their elapsed time spans the kernel's execution
+// only, not the work of getting it onto the queue.
+struct LaunchTiming {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+LaunchTiming& launch_timing();   // this thread's pending pair (kvs_kernels.hip)
+
 hipError_t launch_attend(const AttendArgs& a, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 // few-row VALU decode kernel (kvs_decode.hip): rows = n_q * G in [1, 6]

@@ -23,6 +23,7 @@
 #include <cstdlib>
 
 #include "kvs_internal.h"
+#include "kvs_device.h"
 
 namespace kvs {
 namespace {
@@ -152,6 +153,11 @@ __global__ void fill_u32_kernel(uint32_t* __restrict__ p, uint32_t v, uint64_t n
 
 }  // namespace
 
+LaunchTiming& launch_timing() {
+    static thread_local LaunchTiming t;
+    return t;
+}
+
 hipError_t launch_attend(const AttendArgs& a, hipStream_t stream) {
     if (a.n_segs <= 0 && copy_workgroups(a.copy) == 0) return hipSuccess;
     const int R = a.n_q * a.G;
@@ -163,8 +169,7 @@ hipError_t launch_combine(const float* part, int32_t n_groups, int32_t n_q, int3
                           float* out, float* lse, hipStream_t stream) {
     const int rows = n_q * n_q_heads;
     if (rows <= 0) return hipSuccess;
-    hipLaunchKernelGGL(combine_kernel, dim3(rows), dim3(64 * kCombWaves), 0, stream, part, n_groups, rows, out, lse);
-    return hipGetLastError();
+    return launch_kernel(combine_kernel, dim3(rows), dim3(64 * kCombWaves), stream, part, n_groups, rows, out, lse);
 }
 
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream) {

@@ -631,8 +631,7 @@ hipError_t launch_rt(const AttendArgs& a, hipStream_t stream) {
     const int64_t n_work = slices * units;
     const int64_t blocks = ((copy_workgroups(a.copy) + 7) & ~7) + ((n_work + 7) & ~7);
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((mfma_kernel<RT, STAGED>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, b);
-    return hipGetLastError();
+    return launch_kernel(mfma_kernel<RT, STAGED>, dim3((unsigned)blocks), dim3(kThreads), stream, b);
 }
 
 }  // namespace
@@ -658,8 +657,7 @@ bool mfma_stages(int rows) { return rows > 64; }
 hipError_t launch_stage(const StageArgs& a, hipStream_t stream) {
     const int cx = (copy_workgroups(a.copy) + a.n_kv_heads - 1) / a.n_kv_heads;
     if (a.n_pages <= 0 && cx == 0) return hipSuccess;
-    hipLaunchKernelGGL(stage_kernel, dim3(a.n_pages + cx, a.n_kv_heads), dim3(kThreads), 0, stream, a);
-    return hipGetLastError();
+    return launch_kernel(stage_kernel, dim3(a.n_pages + cx, a.n_kv_heads), dim3(kThreads), stream, a);
 }
 
 }  // namespace kvs

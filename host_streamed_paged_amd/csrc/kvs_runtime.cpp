@@ -188,13 +188,14 @@ hipError_t timed(kvs_pool* p, int kind, hipStream_t s, Fn fn) {
         if (e != hipSuccess) { (void)hipEventDestroy(a); return e; }
         v.push_back({a, b});
     }
+    // the pair rides on the kernel's own dispatch (kvs::launch_kernel), so it
+    // times the kernel's execution; a call that launched nothing leaves it
     auto& pr = v[p->prof_used[kind]];
-    hipError_t e = hipEventRecord(pr.first, s);
-    if (e != hipSuccess) return e;
-    e = fn();
-    if (e != hipSuccess) return e;
-    e = hipEventRecord(pr.second, s);
-    if (e == hipSuccess) p->prof_used[kind]++;
+    kvs::launch_timing() = kvs::LaunchTiming{pr.first, pr.second};
+    hipError_t e = fn();
+    const bool used = kvs::launch_timing().start == nullptr;
+    kvs::launch_timing() = kvs::LaunchTiming{};
+    if (e == hipSuccess && used) p->prof_used[kind]++;
     return e;
 }
 
