@@ -8,10 +8,11 @@ heads, d = 128, 128 resident pages per layer, one query token). `value` is
 the KV bytes attended per second (all 16 layers' pages, 436,207,616 B per
 step) over the timed steps. Alongside it:
   * roofline: the attention kernel's algorithmic bytes per launch (one layer,
-    27,262,976 B) over its average launch duration (HIP events on the compute
-    stream, timed region), against 8 TB/s HBM;
+    27,262,976 B) over its average launch duration (HIP events carried by
+    each launch's dispatch on the compute stream, timed region), against
+    8 TB/s HBM;
   * streamed: the same measurement at 256 Ki context with 103 resident pages
-    per layer and the rest streamed through a 32-page ring, against the host
+    per layer and the rest streamed through a 48-page ring, against the host
     link rate measured in the same run (1 GiB pinned copy, best of 5);
   * verify / prefill: the speculative-verify block (4 query tokens at 160 Ki
     context, 180 resident pages per layer) and the prefill ubatch (256 query
@@ -395,7 +396,7 @@ def main():
     kvs.lib()
     torch.cuda.set_device(0)
     wl = WORKLOADS[args.workload]
-    cfg_kw = dict(ring_pages=32, chunk_pages=4, copy_streams=1, group_pages=1)
+    cfg_kw = dict(ring_pages=48, chunk_pages=4, copy_streams=1, group_pages=1)
     st = setup(wl, cfg_kw, args.threads)
     r = timed_run(wl, st, args.steps, args.warmup)          # eager, per-kernel events
     gr = graph_run(wl, st, args.steps, args.warmup)        # graph replay of the whole step
@@ -470,8 +471,8 @@ def main():
             "streamed_bytes_per_step": streamed_bytes, "kv_bytes_per_step": total_bytes,
             "ring_copy_launches_per_step": round(st_info.copies_issued / (args.streamed_steps + 2), 1),
             "resident_bytes_per_step": res_bytes,
-            "schedule": "ring 32 pages in 4-page chunks; copy workgroups inside the compute launches; "
-                        "four compute lanes take chunks in turn",
+            "schedule": "ring 48 pages in 4-page chunks; copy workgroups inside the compute launches; "
+                        "three compute lanes take chunks in turn",
         }
         log(f"{swl.name}: {sr['ms_per_step']:.3f} ms/step, streamed {streamed_bytes / sec / 1e9:.2f} GB/s "
             f"of link {link:.2f} GB/s")
@@ -481,10 +482,10 @@ def main():
         del sst
 
     if not args.no_multi:
-        result["verify"] = multi_leg("spec_verify_160k", dict(ring_pages=32, chunk_pages=4, copy_streams=1,
+        result["verify"] = multi_leg("spec_verify_160k", dict(ring_pages=48, chunk_pages=4, copy_streams=1,
                                                               group_pages=1), args.threads, link, 8, "verify",
                                      not args.no_zero_copy)
-        result["prefill"] = multi_leg("prefill_ubatch_128k", dict(ring_pages=64, chunk_pages=8, copy_streams=1,
+        result["prefill"] = multi_leg("prefill_ubatch_128k", dict(ring_pages=96, chunk_pages=16, copy_streams=1,
                                                                   group_pages=8), args.threads, link, 6, "prefill",
                                       not args.no_zero_copy)
 

@@ -43,7 +43,7 @@ int fail(int code, const char* fmt, ...) {
 
 constexpr uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
-constexpr int kMaxLanes = 4;   // compute lanes for ring chunks (lane 0 is the caller's stream)
+constexpr int kMaxLanes = 3;   // compute lanes for ring chunks and staged runs
 // automatic sizing (page 3, description of --kv-stream auto): a 2048-token
 // floor, an 8192 MiB ceiling, and in the stage formula that reproduces its
 // logs, 4 pages per layer above the resident ones
@@ -158,7 +158,13 @@ struct kvs_pool {
     hipEvent_t last_work = nullptr;  // recorded after every attend / gather
     hipEvent_t append_ev = nullptr;  // recorded after every kvs_append
     bool appended = false;           // append_ev has been recorded at least once
-    hipStream_t lanes[kMaxLanes] = {};   // compute lanes 1.. for ring chunks (lane 0 is the caller's stream)
+    // Compute lanes, used when a layer runs on more than one (otherwise its
+    // launches go to the caller's stream). They are created back to back,
+    // before any other stream of the pool: the runtime hands streams to its
+    // hardware queues in turn, so consecutive streams land on distinct queues
+    // and no two lanes serialize on a shared queue (the caller's stream, whose
+    // queue is unknown, only forks, joins and combines).
+    hipStream_t lanes[kMaxLanes] = {};
     hipEvent_t fork_ev = nullptr;
     hipEvent_t join_ev[kMaxLanes] = {};
     int32_t ring_next = 0;           // chunk slot that receives the next layer's chunk 0
@@ -359,18 +365,25 @@ int prefetch(kvs_pool* p, int32_t layer) {
 // Run the layer's launch plan. Ring chunks are moved by copy workgroups
 // inside the compute launches; kernel boundaries on a stream order each copy
 // before its reader and each reader before its slot is refilled.
-//   n lanes (lanes_for: up to 4, n dividing the number of chunk slots, which
-//   is at least 2 n; and every split-K group computed by a single chunk
-//   launch, so that concurrent launches never share a group's state): chunk c is computed on lane c mod n (lane 0 is the
-//   caller's stream, the others the pool's lane streams), and the launch that
-//   computes chunk c copies chunk c + n, which belongs to the same lane, into
-//   a slot last read by that lane (slot count a multiple of n, at least 2 n).
-//   The lanes' copies overlap, so the host link stays busy. They meet through
-//   one fork event and one join event per lane per layer.
-//   One lane (otherwise): the launch that computes chunk c copies chunk c + 1
-//   (ring of >= 2 slots), or copies and computes alternate (one slot).
-// The resident groups are computed by the first launch on the caller's
-// stream, which also copies chunk 0 unless it was prefetched.
+//   n lanes (lanes_for: up to kMaxLanes = 3, n dividing the number of chunk
+//   slots, which is at least 2 n; and every split-K group computed by a
+//   single chunk launch, so that concurrent launches never share a group's
+//   state): chunk c is computed on the pool's lane stream c mod n, and the
+//   launch that computes chunk c copies chunk c + n, which belongs to the
+//   same lane, into a slot last read by that lane (slot count a multiple of
+//   n, at least 2 n). The lanes' copies overlap, so the host link stays busy.
+//   They meet the caller's stream through one fork event and one join event
+//   per lane per layer. Three lanes and the caller's stream fit the four
+//   hardware queues a process gets by default: with a fourth lane two lanes
+//   could share a queue, and the rate swung between 79 % and 87 % of the
+//   link from one pool to the next in a process, against a steady 84-85 %
+//   with three.
+//   One lane (otherwise): every launch goes to the caller's stream; the
+//   launch that computes chunk c copies chunk c + 1 (ring of >= 2 slots), or
+//   copies and computes alternate (one slot).
+// The resident groups are computed by the first launch of lane 0 (the
+// caller's stream with one lane), which also copies chunk 0 unless it was
+// prefetched.
 // Compute lanes for a layer with n_ch ring chunks over R chunk slots: the
 // most lanes n (up to kMaxLanes) with R a multiple of n and at least 2 n, so
 // that a lane only ever refills slots it has read itself.
@@ -434,17 +447,17 @@ int run_layer(kvs_pool* p, int32_t layer, hipStream_t stream, int32_t run_pages,
             const int n_l = (int)std::min<size_t>(kMaxLanes, runs.size());
             if (n_l > 1) {
                 if (hipEventRecord(p->fork_ev, stream) != hipSuccess) return mark(fail(KVS_ERR_HIP, "lane fork failed"));
-                for (int k = 1; k < n_l; ++k)
+                for (int k = 0; k < n_l; ++k)
                     if (hipStreamWaitEvent(p->lanes[k], p->fork_ev, 0) != hipSuccess) return mark(fail(KVS_ERR_HIP, "lane fork failed"));
             }
             for (size_t r = 0; r < runs.size(); ++r) {
                 const int lane = (int)(r % n_l);
-                int e = launch(lane == 0 ? stream : p->lanes[lane], lane, runs[r].first, runs[r].second, nullptr, 0,
+                int e = launch(n_l > 1 ? p->lanes[lane] : stream, lane, runs[r].first, runs[r].second, nullptr, 0,
                                kvs::CopyJob{});
                 if (e) return mark(e);
                 p->st.kernels_launched++;
             }
-            for (int k = 1; k < n_l; ++k)
+            for (int k = 0; k < (n_l > 1 ? n_l : 0); ++k)
                 if (hipEventRecord(p->join_ev[k], p->lanes[k]) != hipSuccess || hipStreamWaitEvent(stream, p->join_ev[k], 0) != hipSuccess)
                     return mark(fail(KVS_ERR_HIP, "lane join failed"));
             return KVS_OK;
@@ -457,7 +470,7 @@ int run_layer(kvs_pool* p, int32_t layer, hipStream_t stream, int32_t run_pages,
     const int n_lanes = lanes_for(R, n_ch, ls.whole_groups);
     auto slot_of = [&](int32_t c) { return (slot0 + c) % R; };
     auto do_launch = [&](int lane, int32_t seg0, int32_t nseg, int32_t c_compute, int32_t c_copy) -> int {
-        hipStream_t st = lane == 0 ? stream : p->lanes[lane];
+        hipStream_t st = n_lanes > 1 ? p->lanes[lane] : stream;
         kvs::CopyJob cj{};
         if (c_copy >= 0) cj = make_copy(p, ls, c_copy, slot_of(c_copy));
         const uint8_t* ring_chunk = c_compute >= 0 ? p->ring + (uint64_t)slot_of(c_compute) * p->cfg.chunk_pages * p->L.page_bytes : nullptr;
@@ -479,6 +492,8 @@ int run_layer(kvs_pool* p, int32_t layer, hipStream_t stream, int32_t run_pages,
         // that layer's combine and this layer's resident launch. Its compute
         // launches write the split-K partials, so they also wait for the
         // caller's stream up to here (the previous combine reads them).
+        // Lane 0 takes the resident launch (and chunk 0's copy) after the
+        // fork, like the caller's stream it stands in for.
         if (hipEventRecord(p->fork_ev, stream) != hipSuccess) return mark(fail(KVS_ERR_HIP, "lane fork failed"));
         for (int k = 1; k < n_lanes; ++k) {
             if (p->ring_used && hipStreamWaitEvent(p->lanes[k], p->ring_free, 0) != hipSuccess)
@@ -488,6 +503,7 @@ int run_layer(kvs_pool* p, int32_t layer, hipStream_t stream, int32_t run_pages,
             if ((rc = do_launch(k, 0, 0, -1, k))) return rc;
             if (hipStreamWaitEvent(p->lanes[k], p->fork_ev, 0) != hipSuccess) return mark(fail(KVS_ERR_HIP, "lane fork failed"));
         }
+        if (hipStreamWaitEvent(p->lanes[0], p->fork_ev, 0) != hipSuccess) return mark(fail(KVS_ERR_HIP, "lane fork failed"));
     }
     const int32_t c0 = (n_ch > 0 && !prefetched) ? 0 : -1;
     if (ls.res_nseg > 0 || c0 >= 0) {
@@ -499,7 +515,7 @@ int run_layer(kvs_pool* p, int32_t layer, hipStream_t stream, int32_t run_pages,
             const int32_t cc = (c + n_lanes < n_ch) ? c + n_lanes : -1;
             if ((rc = do_launch(c % n_lanes, cp.seg0, cp.nseg, c, cc))) return rc;
         }
-        for (int k = 1; k < n_lanes; ++k)
+        for (int k = 0; k < n_lanes; ++k)
             if (hipEventRecord(p->join_ev[k], p->lanes[k]) != hipSuccess || hipStreamWaitEvent(stream, p->join_ev[k], 0) != hipSuccess)
                 return mark(fail(KVS_ERR_HIP, "lane join failed"));
     } else {
@@ -713,6 +729,10 @@ int kvs_pool_create(const kvs_config* cfg, void* dev_arena, uint64_t budget_byte
         delete p;
         return fail(KVS_ERR_HIP, "%s failed: %s", what, hipGetErrorString(e));
     };
+    for (int k = 0; k < kMaxLanes; ++k) {   // first and back to back: one hardware queue each
+        hipError_t e = hipStreamCreateWithFlags(&p->lanes[k], hipStreamNonBlocking);
+        if (e != hipSuccess) return cleanup("hipStreamCreateWithFlags", e);
+    }
     for (int i = 0; i < cfg->copy_streams; ++i) {
         hipStream_t s;
         hipError_t e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
@@ -723,11 +743,9 @@ int kvs_pool_create(const kvs_config* cfg, void* dev_arena, uint64_t budget_byte
         hipError_t e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
         if (e != hipSuccess) return cleanup("hipEventCreateWithFlags", e);
     }
-    for (int k = 1; k < kMaxLanes; ++k) {
+    for (int k = 0; k < kMaxLanes; ++k) {
         hipError_t e = hipEventCreateWithFlags(&p->join_ev[k], hipEventDisableTiming);
         if (e != hipSuccess) return cleanup("hipEventCreateWithFlags", e);
-        e = hipStreamCreateWithFlags(&p->lanes[k], hipStreamNonBlocking);
-        if (e != hipSuccess) return cleanup("hipStreamCreateWithFlags", e);
     }
     p->st.page_bytes = (int64_t)L.page_bytes;
     p->st.slot_count = p->n_slots;

@@ -190,9 +190,9 @@ def test_outputs_bit_identical_across_residency_ring_and_chunks():
         dict(resident=mask_none, ring=6, chunk=3, streams=3),
         dict(resident=mask_random(0.5), ring=4, chunk=4, streams=1),
         dict(resident=mask_random(0.3, seed=5), ring=2, chunk=1, streams=2, flags=kvs.FLAG_POISON_RING),
-        # four or more chunk slots: two to four compute lanes (a divisor of the
-        # slot count, which is at least twice the lanes) when no group spans
-        # two chunks
+        # four or more chunk slots: two or three compute lanes (a divisor of
+        # the slot count, which is at least twice the lanes) when no group
+        # spans two chunks
         dict(resident=mask_none, ring=4, chunk=1, streams=1),
         dict(resident=mask_random(0.5, seed=6), ring=8, chunk=2, streams=2, flags=kvs.FLAG_POISON_RING),
         dict(resident=mask_none, ring=6, chunk=1, streams=1, flags=kvs.FLAG_POISON_RING),
