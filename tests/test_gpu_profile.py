@@ -1,0 +1,78 @@
+"""Kernel timing through the C ABI (kvs_profile_enable / kvs_profile_read).
+
+The start/stop event pair of each timed launch rides on that kernel's own
+dispatch. These tests check the counts per kind (attention 0, combine 1,
+staging 2), that every timed launch took a positive time no longer than the
+whole pass, and that profiling changes no output bit.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from kvs_case import mask_all, mask_random, say
+from test_gpu_parity import small_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(c, qs, **kw):
+    return c.attend_all(qs, **kw)
+
+
+def test_profile_counts_and_times_decode():
+    c = small_case(mask_all, n_layers=2, Hkv=2, Hq=12)
+    try:
+        qs = [c.queries(l, 1, "f32") for l in range(c.L)]
+        kw = dict(q_pos0=c.n_kv - 1, scale=1.0, causal=False, prefetch=False)
+        ref, _ = _run(c, qs, **kw)
+        for kind in (0, 1, 2):
+            c.pool.profile_read(kind, reset=True)
+        c.pool.profile_enable(True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        out, _ = _run(c, qs, **kw)
+        e1.record()
+        torch.cuda.synchronize()
+        c.pool.profile_enable(False)
+        wall_ms = e0.elapsed_time(e1)
+        n_att, ms_att = c.pool.profile_read(0)
+        n_cmb, ms_cmb = c.pool.profile_read(1)
+        n_stg, _ = c.pool.profile_read(2)
+        say(f"decode profile: {n_att} attention launches {ms_att:.4f} ms, {n_cmb} combines {ms_cmb:.4f} ms, "
+            f"pass {wall_ms:.4f} ms")
+        assert n_att == c.L and n_cmb == c.L and n_stg == 0   # all resident: one attention launch per layer
+        assert 0.0 < ms_att <= wall_ms and 0.0 < ms_cmb <= wall_ms
+        for l in range(c.L):
+            assert np.array_equal(out[l], ref[l])
+        # a read with reset clears the counts
+        assert c.pool.profile_read(0) == (0, 0.0)
+    finally:
+        c.close()
+
+
+def test_profile_streamed_lanes_and_staged_prefill():
+    # streamed pages through the ring on several lanes, and a block wide
+    # enough to stage (more than 64 rows per kv head)
+    c = small_case(mask_random(0.3, seed=21), n_layers=2, Hkv=2, Hq=12, max_q=16, ring=12, chunk=2)
+    try:
+        n_q = 16   # 16 queries x 6 heads = 96 rows per kv head: staged
+        qs = [c.queries(l, n_q, "f16") for l in range(c.L)]
+        kw = dict(q_pos0=c.n_kv - n_q, scale=0.088, causal=True, prefetch=True)
+        ref, _ = _run(c, qs, **kw)
+        for kind in (0, 1, 2):
+            c.pool.profile_read(kind, reset=True)
+        c.pool.profile_enable(True)
+        out, _ = _run(c, qs, **kw)
+        c.pool.profile_enable(False)
+        n_att, ms_att = c.pool.profile_read(0)
+        n_cmb, ms_cmb = c.pool.profile_read(1)
+        n_stg, ms_stg = c.pool.profile_read(2)
+        say(f"streamed profile: {n_att} attention {ms_att:.4f} ms, {n_cmb} combines, {n_stg} stagings {ms_stg:.4f} ms")
+        assert n_cmb == c.L
+        assert n_att >= c.L and ms_att > 0.0      # resident launch plus chunk launches on the lanes
+        assert n_stg >= 1 and ms_stg > 0.0        # one staging launch per staged run
+        for l in range(c.L):
+            assert np.array_equal(out[l], ref[l])
+    finally:
+        c.close()
