@@ -40,6 +40,16 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+# The pool configuration each workload runs with (ring, chunk and split-K
+# group sizes in pages; one copy stream for kvs_stream_enqueue). The
+# full-size parity tests use the same table.
+POOL_CFG = {
+    "resident_decode_32k": dict(ring_pages=48, chunk_pages=4, copy_streams=1, group_pages=1),
+    "streamed_decode_256k": dict(ring_pages=48, chunk_pages=4, copy_streams=1, group_pages=1),
+    "spec_verify_160k": dict(ring_pages=48, chunk_pages=4, copy_streams=1, group_pages=1),
+    "prefill_ubatch_128k": dict(ring_pages=96, chunk_pages=16, copy_streams=1, group_pages=8),
+}
+
 METRIC = "streamed attention KV GB/s + decode attn tok/s at 32K/256K ctx, % of HBM/link roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0   # dense f16 matrix peak of MI355X
@@ -396,7 +406,7 @@ def main():
     kvs.lib()
     torch.cuda.set_device(0)
     wl = WORKLOADS[args.workload]
-    cfg_kw = dict(ring_pages=48, chunk_pages=4, copy_streams=1, group_pages=1)
+    cfg_kw = POOL_CFG[args.workload] if args.workload in POOL_CFG else POOL_CFG["resident_decode_32k"]
     st = setup(wl, cfg_kw, args.threads)
     r = timed_run(wl, st, args.steps, args.warmup)          # eager, per-kernel events
     gr = graph_run(wl, st, args.steps, args.warmup)        # graph replay of the whole step
@@ -455,7 +465,8 @@ def main():
     }
     if not args.no_streamed:
         swl = WORKLOADS["streamed_decode_256k"]
-        sst = setup(swl, cfg_kw, args.threads)
+        scfg = POOL_CFG["streamed_decode_256k"]
+        sst = setup(swl, scfg, args.threads)
         sr = streamed_run(swl, sst, args.streamed_steps, 2)
         st_info = sst["pool"].status()
         pb = sst["recs"][0].shape[1]
@@ -478,15 +489,13 @@ def main():
             f"of link {link:.2f} GB/s")
         sst["pool"].close()
         if not args.no_zero_copy:
-            result["streamed"]["zero_copy"] = zero_copy_leg(swl, sst, cfg_kw, args.streamed_steps, link)
+            result["streamed"]["zero_copy"] = zero_copy_leg(swl, sst, scfg, args.streamed_steps, link)
         del sst
 
     if not args.no_multi:
-        result["verify"] = multi_leg("spec_verify_160k", dict(ring_pages=48, chunk_pages=4, copy_streams=1,
-                                                              group_pages=1), args.threads, link, 8, "verify",
+        result["verify"] = multi_leg("spec_verify_160k", POOL_CFG["spec_verify_160k"], args.threads, link, 8, "verify",
                                      not args.no_zero_copy)
-        result["prefill"] = multi_leg("prefill_ubatch_128k", dict(ring_pages=96, chunk_pages=16, copy_streams=1,
-                                                                  group_pages=8), args.threads, link, 6, "prefill",
+        result["prefill"] = multi_leg("prefill_ubatch_128k", POOL_CFG["prefill_ubatch_128k"], args.threads, link, 6, "prefill",
                                       not args.no_zero_copy)
 
     if not args.no_cpu:

@@ -20,12 +20,7 @@ pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 TOL = 2e-3
 
 # workload -> the pool configuration bench.py runs it with
-BENCH_CFG = {
-    "resident_decode_32k": dict(ring_pages=32, chunk_pages=4, copy_streams=1, group_pages=1),
-    "streamed_decode_256k": dict(ring_pages=32, chunk_pages=4, copy_streams=1, group_pages=1),
-    "spec_verify_160k": dict(ring_pages=32, chunk_pages=4, copy_streams=1, group_pages=1),
-    "prefill_ubatch_128k": dict(ring_pages=64, chunk_pages=8, copy_streams=1, group_pages=8),
-}
+from bench import POOL_CFG as BENCH_CFG  # noqa: E402
 
 
 @pytest.mark.parametrize("name", list(BENCH_CFG))
