@@ -181,10 +181,14 @@ namespace {
 
 constexpr size_t kMaxTimed = 65536;
 
-// Launch fn() on stream, bracketed by timing events when profiling is on.
+bool stream_capturing(hipStream_t s);
+
+// Launch fn() on stream, with a timing pair on its kernel's dispatch when
+// profiling is on. Launches under graph capture go untimed: a replay would
+// not refill the pair.
 template <typename Fn>
 hipError_t timed(kvs_pool* p, int kind, hipStream_t s, Fn fn) {
-    if (!p->profiling || p->prof_used[kind] >= kMaxTimed) return fn();
+    if (!p->profiling || p->prof_used[kind] >= kMaxTimed || stream_capturing(s)) return fn();
     auto& v = p->prof_ev[kind];
     if (p->prof_used[kind] == v.size()) {
         hipEvent_t a, b;

@@ -76,3 +76,40 @@ def test_profile_streamed_lanes_and_staged_prefill():
             assert np.array_equal(out[l], ref[l])
     finally:
         c.close()
+
+
+def test_profiling_stays_off_graph_capture():
+    # launches captured into a graph are not timed (a replay would not refill
+    # the event pair); capture and replays work with profiling on
+    c = small_case(mask_all, n_layers=1, Hkv=2, Hq=12)
+    try:
+        q = torch.from_numpy(c.queries(0, 1, "f32")).cuda()
+        ref = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+        c.pool.attend(0, q, c.n_kv, c.n_kv - 1, 1.0, False, ref, None)
+        torch.cuda.synchronize()
+        for kind in (0, 1, 2):
+            c.pool.profile_read(kind, reset=True)
+        c.pool.profile_enable(True)
+        out = torch.empty_like(ref)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            c.pool.attend(0, q, c.n_kv, c.n_kv - 1, 1.0, False, out, None, stream=s)   # eager: timed
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            c.pool.attend(0, q, c.n_kv, c.n_kv - 1, 1.0, False, out, None, stream=s)
+        for rep in range(3):
+            out.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            say(f"graph replay {rep} with profiling on")
+            assert torch.equal(out, ref)
+        c.pool.profile_enable(False)
+        n_att, _ = c.pool.profile_read(0)
+        n_cmb, _ = c.pool.profile_read(1)
+        assert (n_att, n_cmb) == (1, 1)   # the eager call only
+    finally:
+        c.close()
