@@ -332,20 +332,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
 #pragma unroll
                 for (int r = 0; r < R; ++r) s[p][r] = 16 * p + u <= lim[r] ? s[p][r] : -INFINITY;
         }
-        // the slice's V rows to LDS (read by other lanes of this wave only).
-        // The empty asm ties the rows to the last score so that the stores,
-        // and the wait for the V loads they imply, stay after the score passes.
-        {
-            const float dep = s[3][R - 1];
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                asm volatile("" : "+v"(vr[k].x), "+v"(vr[k].y), "+v"(vr[k].z), "+v"(vr[k].w) : "v"(dep));
-            asm volatile("" : "+v"(vr2.x), "+v"(vr2.y) : "v"(dep));
-        }
-        store_v(vr, vr2);
-        if constexpr (kPrefetch) issue_v(rec_next, vr, vr2);
-        wave_lds_sync();
-
         // ---- slice maxima, probabilities and row sums.
         float m_w[R];
 #pragma unroll
@@ -385,6 +371,21 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
         }
         la = sum_over_tokens(la);
         lb = sum_over_tokens(lb);
+        // The slice's V rows to LDS (read by other lanes of this wave only).
+        // Maxima, exponentials and sums above need the scores alone, so they
+        // run while the V rows (the last loads of the page) are still in
+        // flight; the empty asm ties the rows to the row sums so that the
+        // stores, and the wait for the V loads they imply, stay after them.
+        {
+            const float dep = la + lb;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                asm volatile("" : "+v"(vr[k].x), "+v"(vr[k].y), "+v"(vr[k].z), "+v"(vr[k].w) : "v"(dep));
+            asm volatile("" : "+v"(vr2.x), "+v"(vr2.y) : "v"(dep));
+        }
+        store_v(vr, vr2);
+        if constexpr (kPrefetch) issue_v(rec_next, vr, vr2);
+        wave_lds_sync();
         // p * d_v for this lane's block b, all rows (quad broadcasts share the exps)
         {
             float dv[4];
