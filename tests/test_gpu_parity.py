@@ -354,3 +354,39 @@ def test_graph_replay_matches_eager():
         assert e.value.code == kvs.ERR_UNSUPPORTED
     finally:
         c.close()
+
+
+# (n_kv_heads, n_q_heads, query tokens, causal): every query-row count R of the
+# VALU decode kernel (R = query tokens x query heads per kv head, 1..6), with
+# causal blocks of 2 tokens among them
+DECODE_ROWS = [(2, 2, 1, False), (2, 4, 1, False), (2, 6, 1, False), (2, 4, 2, True), (1, 5, 1, False),
+               (2, 6, 2, True)]
+
+
+@pytest.mark.parametrize("Hkv,Hq,n_q,causal", DECODE_ROWS,
+                         ids=["R1", "R2", "R3", "R4-causal", "R5", "R6-causal"])
+@pytest.mark.parametrize("group", [1, 3], ids=["group1", "group3"])
+def test_decode_rows_groups_and_residency(Hkv, Hq, n_q, causal, group):
+    """The decode kernel for each row count, with one-page groups and with
+    3-page groups (runs of several pages: the next page's loads are issued
+    while the current one computes; groups split across ring chunks resume a
+    stored group state). All pages resident (one launch), then half of them
+    streamed through a ring on three compute lanes: both within 2e-3 of the
+    oracle, and the same bits."""
+    base = None
+    for resident, ring, chunk in [(mask_all, 4, 2), (mask_random(0.5, seed=17), 12, 2)]:
+        c = small_case(resident, n_layers=2, Hkv=Hkv, Hq=Hq, max_q=n_q, ring=ring, chunk=chunk, streams=1,
+                       group=group)
+        try:
+            qs = [c.queries(l, n_q, "f32") for l in range(c.L)]
+            q_pos0 = N_KV - n_q
+            outs, lses = c.attend_all(qs, q_pos0=q_pos0, scale=1.0, causal=causal)
+            check(c, outs, lses, qs, q_pos0=q_pos0, scale=1.0, causal=causal)
+            if base is None:
+                base = (outs, lses)
+            else:
+                for l in range(c.L):
+                    assert np.array_equal(outs[l], base[0][l]), l
+                    assert np.array_equal(lses[l], base[1][l]), l
+        finally:
+            c.close()
