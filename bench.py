@@ -299,13 +299,17 @@ def multi_leg(name, cfg_kw, threads, link, steps, kind, zero_copy=True):
     return out
 
 
+# Sources of the decode kernel, whose HBM traffic the stored counters record:
+# its own file and the headers it includes.
+DECODE_SOURCES = ("kvs_decode.hip", "kvs_device.h", "kvs_internal.h")
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "host_streamed_paged_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(fh.read())
+    for f in DECODE_SOURCES:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()[:16]
 
 

@@ -6,7 +6,8 @@
 // One workgroup = one segment (run of pages of one split-K group) x one kv
 // head x a tile of 16 RT query rows (row = query token x head of the GQA
 // group). 4 waves. Every page is staged whole in LDS by LDS DMA (K tile
-// 34816 B, V tile 18432 B, record layout), then:
+// 34816 B, V tile 18432 B, record layout); the next page's K tile is fetched
+// once every wave is past QK, its V tile once P.V is done. Then:
 //   QK   wave w owns tokens [64 w, 64 w + 64) of the page:
 //        S^T (16 tokens x 16 rows) = K_blk (16 x 32) . Q_blk^T (32 x 16),
 //        four 32-wide quant blocks per tile. The K operand is built by the
@@ -57,13 +58,15 @@ constexpr int kChunks = kPageTokens / 32;     // 32-token MFMA chunks per page i
 constexpr float kLazyMax = 8.f;
 
 // One page's tiles. (Double-buffering them measured slower: the next page's
-// LDS DMA then competes with the QK reads of the current one.)
+// LDS DMA then competes with the QK reads of the current one.) The P
+// operands [chunk][row tile][lane] (16 bytes each) have a region of their
+// own, so that the next page's K tile can be fetched into `k` as soon as
+// every wave is past QK, during the softmax and P.V of the current page.
 template <int RT, bool STAGED>
 struct MfmaSmem {
-    // K tile in record layout; once every wave is past QK it holds the P
-    // operands [chunk][row tile][lane] (16 bytes each)
-    alignas(16) uint8_t k[kKTile];
-    alignas(16) uint8_t v[kVTile];
+    alignas(16) uint8_t k[kKTile];   // K tile in record layout
+    alignas(16) uint8_t v[kVTile];   // V tile in record layout
+    alignas(16) uint8_t p[kChunks * RT * 64 * 16];
     float red_m[kWaves][16 * RT];
     float red_l[kWaves][16 * RT];
 };
@@ -77,20 +80,26 @@ struct MfmaSmem<RT, true> {
 constexpr int kStagedK = kPageTokens * kHeadDim * 2;   // f16 K operands of one (page, kv head)
 static_assert(2 * kStagedK == kStagedTile, "staged tile = K + V^T operands");
 
+template <int RT>
+__device__ inline uint8_t* sm_p(MfmaSmem<RT, false>& sm) { return sm.p; }
+template <int RT>
+__device__ inline uint8_t* sm_p(MfmaSmem<RT, true>& sm) { return sm.k; }
+
 __device__ inline half2_t as_h2(uint32_t x) { return __builtin_bit_cast(half2_t, x); }
 __device__ inline uint32_t as_u(half2_t x) { return __builtin_bit_cast(uint32_t, x); }
 
-// Stage one (page, kv head) tile pair of a page record into LDS by LDS DMA:
+// Stage one (page, kv head) tile of a page record into LDS by LDS DMA:
 // wave-sized pieces of 1 KB, 34 for K and 18 for V.
-__device__ inline void dma_page_tiles(const uint8_t* rec, int g, int n_kv_heads, uint8_t* k_lds, uint8_t* v_lds,
-                                      int w, int lane) {
+__device__ inline void dma_k_tile(const uint8_t* rec, int g, uint8_t* k_lds, int w, int lane) {
     const uint8_t* kt = rec + (int64_t)g * kKTile;
-    const uint8_t* vt = rec + (int64_t)n_kv_heads * kKTile + (int64_t)g * kVTile;
 #pragma unroll
     for (int k = 0; k < 9; ++k) {
         const int piece = w + 4 * k;
         if (piece < kKTile / 1024) dma16(kt + piece * 1024 + lane * 16, k_lds + piece * 1024);
     }
+}
+__device__ inline void dma_v_tile(const uint8_t* rec, int g, int n_kv_heads, uint8_t* v_lds, int w, int lane) {
+    const uint8_t* vt = rec + (int64_t)n_kv_heads * kKTile + (int64_t)g * kVTile;
 #pragma unroll
     for (int k = 0; k < 5; ++k) {
         const int piece = w + 4 * k;
@@ -256,7 +265,11 @@ void mfma_kernel(AttendArgs a) {
     typedef int int4v __attribute__((ext_vector_type(4)));
 
     auto issue_page = [&](int page) {
-        if constexpr (!STAGED) dma_page_tiles(page_record(a.ps, page), g, a.n_kv_heads, sm.k, sm.v, w, lane);
+        if constexpr (!STAGED) {
+            const uint8_t* rec = page_record(a.ps, page);
+            dma_k_tile(rec, g, sm.k, w, lane);
+            dma_v_tile(rec, g, a.n_kv_heads, sm.v, w, lane);
+        }
     };
     issue_page(scalar_load(&a.segs[slice].page0));
     // staged operands of the current segment's first page, for kv head g
@@ -383,6 +396,13 @@ void mfma_kernel(AttendArgs a) {
         }
         const int64_t vx = a.n_kv - base_tok;
         const int valid = (int)(vx < 0 ? 0 : (vx > kPageTokens ? kPageTokens : vx));   // cached rows of the page
+        // the worker's next page (this segment's next, else the first of its
+        // next segment), whose tiles are fetched while this page finishes
+        const uint8_t* next_rec = nullptr;
+        if constexpr (!STAGED) {
+            if (pi + 1 < seg.npages) next_rec = page_record(a.ps, page + 1);
+            else if (seg_i + a.n_slices < a.n_segs) next_rec = page_record(a.ps, scalar_load(&a.segs[seg_i + a.n_slices].page0));
+        }
 
         if constexpr (!STAGED) {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -450,6 +470,9 @@ void mfma_kernel(AttendArgs a) {
             if (gq == 0) sm.red_m[w][16 * rt + n] = mx[rt];
         }
         lds_barrier();   // maxima published; every wave is done reading the K tile
+        if constexpr (!STAGED) {
+            if (next_rec) dma_k_tile(next_rec, g, sm.k, w, lane);   // lands during softmax and P.V
+        }
 
         float m_use[RT], alpha[RT];
 #pragma unroll
@@ -465,7 +488,7 @@ void mfma_kernel(AttendArgs a) {
         }
         // ---- probabilities -> P operands in LDS (slot 8 gq + j of chunk c is
         // token 32 c + 4 gq + j for j < 4, 32 c + 12 + 4 gq + j otherwise)
-        uint8_t* pbuf = sm.k;
+        uint8_t* pbuf = STAGED ? sm.k : sm_p(sm);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             float ls = 0.f;
@@ -532,9 +555,8 @@ void mfma_kernel(AttendArgs a) {
         if (!STAGED && tail_page) pv_page(std::true_type{});
         else pv_page(std::false_type{});
         if constexpr (!STAGED) {
-            lds_barrier();   // every wave is done with this page's tiles
-            if (pi + 1 < seg.npages) issue_page(page + 1);
-            else if (seg_i + a.n_slices < a.n_segs) issue_page(scalar_load(&a.segs[seg_i + a.n_slices].page0));
+            lds_barrier();   // every wave is done with this page's V tile and P operands
+            if (next_rec) dma_v_tile(next_rec, g, a.n_kv_heads, sm.v, w, lane);
         }
     }
 
@@ -580,7 +602,11 @@ __global__ __launch_bounds__(kThreads) void stage_kernel(StageArgs a) {
         rem -= np;
     }
     if (page < 0) return;   // past the launch's pages
-    dma_page_tiles(page_record(a.ps, page), g, a.n_kv_heads, k_lds, v_lds, w, lane);
+    {
+        const uint8_t* rec = page_record(a.ps, page);
+        dma_k_tile(rec, g, k_lds, w, lane);
+        dma_v_tile(rec, g, a.n_kv_heads, v_lds, w, lane);
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
     uint8_t* tile = a.staged + ((int64_t)slot * a.n_kv_heads + g) * kStagedTile;
