@@ -321,8 +321,9 @@ int kvs_debug_read_page(kvs_pool* pool, int32_t layer, int32_t page, void* dst_h
 
 /* Kernel timing. With enable != 0, kvs_attend brackets every attention kernel
  * launch (kind 0), every split-K combine launch (kind 1) and every staging
- * launch of a wide query block (kind 2) with timing events recorded on the
- * stream the launch runs on. kvs_profile_read waits
+ * launch of a wide query block (kind 2) with a start/stop event pair carried
+ * by the kernel's own dispatch (so the time is the kernel's execution, not its
+ * queueing); launches under graph capture are not timed. kvs_profile_read waits
  * for the recorded events and returns the number of timed launches of that
  * kind and their summed duration in milliseconds; reset != 0 clears the
  * record. At most 65536 launches per kind are kept (later ones are not timed). */
