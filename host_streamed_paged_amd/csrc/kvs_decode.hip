@@ -7,11 +7,13 @@
 // Per 64-token slice (a page is 256 tokens of one layer; page 2, "Dynamic
 // draft eject"):
 //   QK  lane = (token, 32-wide block). The lane loads its Q8_0 block straight
-//       from the page record (9 aligned dwords; odd blocks start 2 bytes into
-//       a dword and are realigned with v_perm) and forms exact integer dot
-//       products with v_dot4_i32_i8 against the query held as 16-bit fixed
-//       point (per row and block scale, split into int8 high and low bytes).
-//       The 4 blocks of a token are summed with two quad DPP adds.
+//       from the page record as 9 aligned dwords (an even block's codes start
+//       2 bytes into a dword, an odd block's on a dword boundary; one v_perm
+//       with a per-lane selector yields the 8 code dwords either way) and forms
+//       exact integer dot products with v_dot4_i32_i8 against the query held
+//       as 16-bit fixed point (per row and block scale, split into int8 high
+//       and low bytes). The 4 blocks of a token are summed with two quad DPP
+//       adds.
 //   softmax  slice maxima per row by cross-lane reduction; p = exp2(s - m) in
 //       log2 units (the softmax scale is folded into the query scale).
 //   PV  lane = (32-wide block, byte position): its two channels are the low and
@@ -22,6 +24,8 @@
 //   fixed order, and page partials are merged into the group state in page
 //   order: results do not depend on how pages are split into launches or
 //   which of them are resident.
+// Loads are issued query first, then K blocks, then V rows, all as plain
+// register loads, so each wait covers exactly what the next step reads.
 #include <hip/hip_runtime.h>
 #include <cstdint>
 #include <cmath>
