@@ -1,8 +1,9 @@
 // Decode attention kernel for few query rows (R = query tokens x heads per kv
-// head, R <= 6): VALU dot products on CDNA4. One workgroup per (page run of a
-// split-K group, kv head); 256 threads = 4 waves, and each wave owns a
-// 64-token slice of every page from load to weighted sum, so the waves never
-// wait on each other until the per-page merge.
+// head, R <= 6) on CDNA4: integer dot products for the scores, matrix cores
+// for the weighted sum of V. One workgroup per (page run of a split-K group,
+// kv head); 256 threads = 4 waves, and each wave owns a 64-token slice of
+// every page from load to weighted sum, so the waves never wait on each other
+// until the per-page merge.
 //
 // Per 64-token slice (a page is 256 tokens of one layer; page 2, "Dynamic
 // draft eject"):
@@ -16,10 +17,11 @@
 //       adds.
 //   softmax  slice maxima per row by cross-lane reduction; p = exp2(s - m) in
 //       log2 units (the softmax scale is folded into the query scale).
-//   PV  lane = (32-wide block, byte position): its two channels are the low and
-//       high nibble of one byte. The slice's V rows are staged in the wave's
-//       LDS region; the lane builds two tokens' nibbles as exact f16 (u - 8)
-//       pairs and accumulates v_dot2_f32_f16 against p * d_v rounded to f16.
+//   PV  on the matrix cores (v_mfma_f32_16x16x32_f16): the slice's V rows are
+//       staged in the wave's LDS region, p * d_v is rounded to f16 into a
+//       per-wave buffer, and each V block's low and high nibbles form two
+//       16-channel tiles of V^T as exact f16 (u - 8), multiplied against the
+//       rows' p * d_v over two 32-token steps.
 //   The 4 slice partials of a page are merged into one page partial in a
 //   fixed order, and page partials are merged into the group state in page
 //   order: results do not depend on how pages are split into launches or
@@ -38,6 +40,9 @@ namespace kvs {
 namespace {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -129,8 +134,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
     const uint32_t sel = (b & 1) ? 0x07060504u : 0x05040302u;
     const int dshift = 16 * (b & 1);
     const int kboff = (kSlice * w + u) * kKRow + kKBlock * b - 2 * (b & 1);   // 4-aligned
-    // PV role: block bb, byte position j16 (channels 32 bb + j16 and 32 bb + 16 + j16)
-    const int j16 = l & 15, bb = l >> 4;
 
     // K blocks and V rows are loaded into registers; the V rows are stored to
     // the wave's LDS region once the scores are done. Plain loads (no LDS DMA)
@@ -428,41 +431,47 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
         }
         wave_lds_sync();
 
-        // ---- P.V over the slice: 32 token pairs (t, t + 16), t = 32 q2 + u
-        float acc[R][2];
-#pragma unroll
-        for (int r = 0; r < R; ++r) acc[r][0] = acc[r][1] = 0.f;
+        // ---- P.V over the slice on the matrix cores: O^T = V^T . P' per V
+        // block, one 16-channel tile for the low nibbles and one for the high,
+        // in two 32-token steps (v_mfma_f32_16x16x32_f16). Lane (n, kg) =
+        // (l & 15, l >> 4) holds operand slots 8 kg .. 8 kg + 7; slots 8 kg + 2 i
+        // and 8 kg + 2 i + 1 of step ks are tokens t = 32 ks + 4 kg + i and
+        // t + 16, the pair one dword of the p * d_v buffer holds. A: channel n
+        // of the tile (V nibbles as exact f16 (u - 8), high nibbles 16 (u - 8));
+        // B: query row n; C: channels 4 kg .. 4 kg + 3 of the tile, row n. B
+        // columns of rows past R hold stale buffer words and only reach output
+        // columns that are dropped.
         {
-            const uint8_t* vb = vt + bb * kVBlock + 2 + j16;
-            const uint4* ppb = (const uint4*)(ppw + bb * kPPStride);
+            const int n = l & 15, kg = l >> 4;
             const half2_t off_lo = {(_Float16)1032.f, (_Float16)1032.f};
             const half2_t off_hi = {(_Float16)1152.f, (_Float16)1152.f};
             const uint32_t m_lo = vconst(0x000F000Fu), m_hi = vconst(0x00F000F0u), magic = vconst(0x64006400u);
 #pragma unroll
-            for (int n = 0; n < kSlicePairs; ++n) {
-                const int ta = 32 * (n >> 4) + (n & 15);
-                const uint32_t x = __builtin_amdgcn_perm((uint32_t)vb[(ta + 16) * kVRow], (uint32_t)vb[ta * kVRow], 0x0c040c00u);
-                const half2_t lo = __builtin_bit_cast(half2_t, (x & m_lo) | magic) - off_lo;  // u - 8
-                const half2_t hi = __builtin_bit_cast(half2_t, (x & m_hi) | magic) - off_hi;  // 16 (u - 8)
-                const uint4 p0 = ppb[2 * n];
-                uint32_t prr[8] = {p0.x, p0.y, p0.z, p0.w, 0u, 0u, 0u, 0u};
-                if (R > 4) {
-                    const uint4 p1 = ppb[2 * n + 1];
-                    prr[4] = p1.x; prr[5] = p1.y; prr[6] = p1.z; prr[7] = p1.w;
-                }
+            for (int vb = 0; vb < kNB; ++vb) {
+                f32x4 clo = {0.f, 0.f, 0.f, 0.f}, chi = clo;
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const half2_t ph = __builtin_bit_cast(half2_t, prr[r]);
-                    acc[r][0] = __builtin_amdgcn_fdot2(ph, lo, acc[r][0], false);
-                    acc[r][1] = __builtin_amdgcn_fdot2(ph, hi, acc[r][1], false);
+                for (int ks = 0; ks < 2; ++ks) {
+                    const uint8_t* vsrc = vt + (32 * ks + 4 * kg) * kVRow + vb * kVBlock + 2 + n;
+                    const uint32_t* psrc = ppw + vb * kPPStride + (16 * ks + 4 * kg) * 8 + n;
+                    u32x4 alo, ahi, bp;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t x = __builtin_amdgcn_perm((uint32_t)vsrc[(i + 16) * kVRow], (uint32_t)vsrc[i * kVRow], 0x0c040c00u);
+                        alo[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, (x & m_lo) | magic) - off_lo);  // u - 8
+                        ahi[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, (x & m_hi) | magic) - off_hi);  // 16 (u - 8)
+                        bp[i] = psrc[8 * i];
+                    }
+                    const half8_t pb = __builtin_bit_cast(half8_t, bp);
+                    clo = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, alo), pb, clo, 0, 0, 0);
+                    chi = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ahi), pb, chi, 0, 0, 0);
+                }
+                // slice partial -> LDS (the next page writes the other parity)
+                if (n < R) {
+                    float* dst = &sm.sacc[par][w][n < R ? n : 0][32 * vb + 4 * kg];
+                    *(f32x4*)dst = clo;
+                    *(f32x4*)(dst + 16) = chi * 0.0625f;   // high nibbles carried 16 (u - 8)
                 }
             }
-        }
-        // slice partial -> LDS (the next page writes the other parity)
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            sm.sacc[par][w][r][32 * bb + j16] = acc[r][0];
-            sm.sacc[par][w][r][32 * bb + 16 + j16] = acc[r][1] * 0.0625f;   // high nibbles carried 16 (u - 8)
         }
         if (l < 4) {
 #pragma unroll
