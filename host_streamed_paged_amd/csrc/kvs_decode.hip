@@ -1,33 +1,34 @@
 // Decode attention kernel for few query rows (R = query tokens x heads per kv
-// head, R <= 6) on CDNA4: integer dot products for the scores, matrix cores
-// for the weighted sum of V. One workgroup per (page run of a split-K group,
-// kv head); 256 threads = 4 waves, and each wave owns a 64-token slice of
-// every page from load to weighted sum, so the waves never wait on each other
-// until the per-page merge.
+// head, R <= 6) on CDNA4, both products on the matrix cores. One workgroup
+// per (page run of a split-K group, kv head); 256 threads = 4 waves, and each
+// wave owns a 64-token slice of every page from load to weighted sum, so the
+// waves never wait on each other until the per-page merge.
 //
 // Per 64-token slice (a page is 256 tokens of one layer; page 2, "Dynamic
-// draft eject"):
-//   QK  lane = (token, 32-wide block). The lane loads its Q8_0 block straight
-//       from the page record as 9 aligned dwords (an even block's codes start
-//       2 bytes into a dword, an odd block's on a dword boundary; one v_perm
-//       with a per-lane selector yields the 8 code dwords either way) and forms
-//       exact integer dot products with v_dot4_i32_i8 against the query held
-//       as 16-bit fixed point (per row and block scale, split into int8 high
-//       and low bytes). The 4 blocks of a token are summed with two quad DPP
-//       adds.
-//   softmax  slice maxima per row by cross-lane reduction; p = exp2(s - m) in
+// draft eject"), in 16x16x32 tiles where lane (n, kg) = (l & 15, l >> 4)
+// holds operand slots 8 kg .. 8 kg + 7 of row or column n and output rows
+// 4 kg .. 4 kg + 3 of column n:
+//   QK  S = Q . K^T per (16-token tile, 32-wide block) on
+//       v_mfma_i32_16x16x32_i8: exact integer products of the Q8_0 codes,
+//       loaded straight from the page record into the lane of their token,
+//       with the query held as 16-bit fixed point (per row scale, split into
+//       int8 high and low bytes, one instruction each). The block scale
+//       multiplies each block's integer sum, and the 4 block terms are added
+//       in a fixed order.
+//   softmax  lanes hold query rows of one token: slice maxima and row sums
+//       are reductions over the 16 lanes of a DPP row; p = exp2(s - m) in
 //       log2 units (the softmax scale is folded into the query scale).
-//   PV  on the matrix cores (v_mfma_f32_16x16x32_f16): the slice's V rows are
-//       staged in the wave's LDS region, p * d_v is rounded to f16 into a
-//       per-wave buffer, and each V block's low and high nibbles form two
-//       16-channel tiles of V^T as exact f16 (u - 8), multiplied against the
-//       rows' p * d_v over two 32-token steps.
+//   PV  v_mfma_f32_16x16x32_f16: the slice's V rows are staged in the wave's
+//       LDS region, p * d_v is rounded to f16 into a per-wave buffer, and
+//       each V block's low and high nibbles form two 16-channel tiles of V^T
+//       as exact f16 (u - 8), multiplied against the rows' p * d_v over two
+//       32-token steps.
 //   The 4 slice partials of a page are merged into one page partial in a
 //   fixed order, and page partials are merged into the group state in page
 //   order: results do not depend on how pages are split into launches or
 //   which of them are resident.
-// Loads are issued query first, then K blocks, then V rows, all as plain
-// register loads, so each wait covers exactly what the next step reads.
+// Loads are issued query first, then K codes and scales, then V rows, all as
+// plain register loads, so each wait covers exactly what the next step reads.
 #include <hip/hip_runtime.h>
 #include <cstdint>
 #include <cmath>
@@ -43,12 +44,14 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kSlice = kPageTokens / kWaves;   // 64 tokens per wave
 constexpr int kSlicePairs = kSlice / 2;        // 32 token pairs
 constexpr int kPPStride = kSlicePairs * 8 + 8; // dwords per block row of pp (padded: no bank clash across blocks)
+constexpr int kKW = 14;                        // K dwords per lane and 16-token tile
 
 __device__ inline float f16_lo_to_float(uint32_t bits) {
     return (float)__builtin_bit_cast(_Float16, (unsigned short)(bits & 0xFFFFu));
@@ -61,39 +64,28 @@ __device__ inline float dpp_xor1(float v) {
 __device__ inline float dpp_xor2(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
 }
-// value of lane (4 * (i / 4) + SRC) of each quad
-template <int SRC>
-__device__ inline float quad_bcast(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), SRC * 0x55, 0xF, 0xF, true));
+// lane i receives lane i +- 1 / 2 / 4 / 8 within its row of 16 (row rotate)
+template <int N>
+__device__ inline float dpp_ror(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x120 + N, 0xF, 0xF, true));
 }
-// lane i receives lane i +- 4 / 8 within its row of 16 (row rotate)
-__device__ inline float dpp_ror4(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x124, 0xF, 0xF, true));
-}
-__device__ inline float dpp_ror8(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128, 0xF, 0xF, true));
-}
-// max / sum over the 16 lanes of a wave that share (lane & 3)
-__device__ inline float max_over_tokens(float v) {
-    v = fmaxf(v, dpp_ror4(v));
-    v = fmaxf(v, dpp_ror8(v));
-    v = max_xor16(v);
-    v = max_xor32(v);
+__device__ inline float dpp_ror4(float v) { return dpp_ror<4>(v); }
+__device__ inline float dpp_ror8(float v) { return dpp_ror<8>(v); }
+// max / sum over the 16 lanes of a DPP row (every lane gets the max; the sum's
+// rounding may differ from lane to lane)
+__device__ inline float max_over_row16(float v) {
+    v = fmaxf(v, dpp_ror<1>(v));
+    v = fmaxf(v, dpp_ror<2>(v));
+    v = fmaxf(v, dpp_ror<4>(v));
+    v = fmaxf(v, dpp_ror<8>(v));
     return v;
 }
-__device__ inline float sum_over_tokens(float v) {
-    v += dpp_ror4(v);
-    v += dpp_ror8(v);
-    v = add_xor16(v);
-    v = add_xor32(v);
+__device__ inline float sum_over_row16(float v) {
+    v += dpp_ror<1>(v);
+    v += dpp_ror<2>(v);
+    v += dpp_ror<4>(v);
+    v += dpp_ror<8>(v);
     return v;
-}
-
-// a . b over 4 signed bytes, starting from 0
-__device__ inline int sdot4_first(uint32_t a, uint32_t b) {
-    int r;
-    asm("v_dot4_i32_i8 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
-    return r;
 }
 
 __device__ inline void wave_lds_sync() {
@@ -129,25 +121,42 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
     const int g = blockIdx.y;
     const int G = a.G;
 
-    // QK role: block b, token u of each 16-token pass
-    const int b = l & 3, u = l >> 2;
-    const uint32_t sel = (b & 1) ? 0x07060504u : 0x05040302u;
-    const int dshift = 16 * (b & 1);
-    const int kboff = (kSlice * w + u) * kKRow + kKBlock * b - 2 * (b & 1);   // 4-aligned
+    // Matrix-core lane roles (16x16x32 tiles): lane (n, kg) = (l & 15, l >> 4)
+    // holds operand slots 8 kg .. 8 kg + 7 of row or column n and output rows
+    // 4 kg .. 4 kg + 3 of column n. Scores: token n of each 16-token tile,
+    // channels 8 kg .. 8 kg + 7 of each 32-wide block.
+    const int n = l & 15, kg = l >> 4;
+    const int krow = (kSlice * w + n) * kKRow;   // this lane's token row in the K tile
 
     // K blocks and V rows are loaded into registers; the V rows are stored to
     // the wave's LDS region once the scores are done. Plain loads (no LDS DMA)
-    // keep every load in flight of one kind, so that each score pass waits for
-    // its own K blocks only.
+    // keep every load in flight of one kind, so that each score tile waits for
+    // its own K codes only.
     uint8_t* vt = sm.v[w];
     auto page_rec = [&](int page) -> const uint8_t* { return page_record(a.ps, page); };
-    auto issue_k = [&](const uint8_t* rec, uint32_t (&kw)[4][9]) {
-        const uint8_t* kt = rec + (int64_t)g * kKTile + kboff;
+    // Per 16-token tile: this lane's 8 codes of blocks 0..3 (block b starts at
+    // byte 34 b of the token row, its codes 2 bytes later: an even block's
+    // 8-code window [34 b + 2 + 8 kg, +8) is covered by the 3 aligned dwords
+    // from 34 b + 8 kg, an odd block's is itself 2 aligned dwords), then the 4
+    // aligned dwords holding the block scales (bytes 0, 32, 68, 100; the scale
+    // is the low half for an even block, the high half for an odd one).
+    auto issue_k = [&](const uint8_t* rec, uint32_t (&kw)[4][kKW]) {
+        const uint8_t* kt = rec + (int64_t)g * kKTile + krow;
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const uint32_t* src = (const uint32_t*)(kt + p * 16 * kKRow);
-#pragma unroll
-            for (int k = 0; k < 9; ++k) kw[p][k] = src[k];
+        for (int t = 0; t < 4; ++t) {
+            const uint8_t* row = kt + t * 16 * kKRow;
+            const uint32_t* b0 = (const uint32_t*)(row + 8 * kg);
+            const uint32_t* b1 = (const uint32_t*)(row + kKBlock + 2 + 8 * kg);
+            const uint32_t* b2 = (const uint32_t*)(row + 2 * kKBlock + 8 * kg);
+            const uint32_t* b3 = (const uint32_t*)(row + 3 * kKBlock + 2 + 8 * kg);
+            kw[t][0] = b0[0]; kw[t][1] = b0[1]; kw[t][2] = b0[2];
+            kw[t][3] = b1[0]; kw[t][4] = b1[1];
+            kw[t][5] = b2[0]; kw[t][6] = b2[1]; kw[t][7] = b2[2];
+            kw[t][8] = b3[0]; kw[t][9] = b3[1];
+            kw[t][10] = *(const uint32_t*)(row);
+            kw[t][11] = *(const uint32_t*)(row + kKBlock - 2);
+            kw[t][12] = *(const uint32_t*)(row + 2 * kKBlock);
+            kw[t][13] = *(const uint32_t*)(row + 3 * kKBlock - 2);
         }
     };
     // 4608 bytes of V rows per slice: four coalesced 16-byte loads and one
@@ -188,7 +197,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
     const Seg seg = {segv.x, segv.y, segv.z, segv.w};
     // memory counters retire in order: query, then K blocks, then V rows
     const uint8_t* rec0 = page_rec(seg.page0);
-    uint32_t kw[4][9];
+    uint32_t kw[4][kKW];
     uint4 vr[4];
     uint2 vr2;
     issue_k(rec0, kw);
@@ -237,13 +246,26 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
         if (qb == 0 && qq == 0) sm.q_scale[r] = amax / 32639.f * fabsf(a.scale_log2);
     }
     lds_barrier();
-    uint32_t qh[R][8], ql[R][8];
-    float qs[R];
+    // score operands: query row n (zero past R), channels 8 kg .. 8 kg + 7 of
+    // each block, high and low bytes; the row scales of output rows 4 kg + i
+    long qa_hi[kNB], qa_lo[kNB];
+    {
+        const int qn = n < R ? n : 0;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
+        for (int blk = 0; blk < kNB; ++blk) {
+            const uint64_t h = ((uint64_t)sm.q_hi[qn][blk][2 * kg + 1] << 32) | sm.q_hi[qn][blk][2 * kg];
+            const uint64_t o = ((uint64_t)sm.q_lo[qn][blk][2 * kg + 1] << 32) | sm.q_lo[qn][blk][2 * kg];
+            qa_hi[blk] = n < R ? (long)h : 0;
+            qa_lo[blk] = n < R ? (long)o : 0;
+        }
+    }
+    float qsv[4], kav[4];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) { qh[r][k] = sm.q_hi[r][b][k]; ql[r][k] = sm.q_lo[r][b][k]; }
-        qs[r] = sm.q_scale[r];
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * kg + i;
+        qsv[i] = r < R ? sm.q_scale[r < R ? r : 0] : 0.f;
+        // a zero row scale is lifted to a tiny one so that 0 * -inf never arises
+        kav[i] = fmaxf(qsv[i], 1e-30f);
     }
 
     // group state, distributed for the per-page merge: thread owns channel
@@ -296,95 +318,79 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
             lim[r] = (int)(l64 < -1 ? -1 : l64);
             need_mask |= lim[r] < kSlice - 1;
         }
-        float s[4][R];
+        // S = Q . K^T per (16-token tile, block) on v_mfma_i32_16x16x32_i8, once
+        // for each byte of the query codes; s[t][i] is row 4 kg + i, token
+        // 16 t + n, in units of the row scale
+        float s[4][4];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            uint32_t c[8];
+        for (int t = 0; t < 4; ++t) {
+            float f[kNB][4];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) c[k] = __builtin_amdgcn_perm(kw[p][k + 1], kw[p][k], sel);
-            const float d = f16_lo_to_float(kw[p][0] >> dshift);
-            // 2 R independent accumulator chains, interleaved so that no dot
-            // waits on the one before it
-            int ih[R], il[R];
+            for (int blk = 0; blk < kNB; ++blk) {
+                const int o = blk == 0 ? 0 : blk == 1 ? 3 : blk == 2 ? 5 : 8;
+                uint32_t c0, c1;
+                if (blk & 1) {
+                    c0 = kw[t][o];
+                    c1 = kw[t][o + 1];
+                } else {
+                    c0 = __builtin_amdgcn_perm(kw[t][o + 1], kw[t][o], 0x05040302u);
+                    c1 = __builtin_amdgcn_perm(kw[t][o + 2], kw[t][o + 1], 0x05040302u);
+                }
+                const long kb = (long)(((uint64_t)c1 << 32) | c0);
+                const i32x4 zero = {0, 0, 0, 0};
+                const i32x4 ih = __builtin_amdgcn_mfma_i32_16x16x32_i8(qa_hi[blk], kb, zero, 0, 0, 0);
+                const i32x4 il = __builtin_amdgcn_mfma_i32_16x16x32_i8(qa_lo[blk], kb, zero, 0, 0, 0);
+                const float d = f16_lo_to_float(kw[t][10 + blk] >> (16 * (blk & 1)));
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                ih[r] = sdot4_first(c[0], qh[r][0]);
-                il[r] = sdot4_first(c[0], ql[r][0]);
-            }
-#pragma unroll
-            for (int k = 1; k < 8; ++k) {
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    ih[r] = __builtin_amdgcn_sdot4((int)c[k], (int)qh[r][k], ih[r], false);
-                    il[r] = __builtin_amdgcn_sdot4((int)c[k], (int)ql[r][k], il[r], false);
+                for (int i = 0; i < 4; ++i) {
+#pragma clang fp contract(off)
+                    f[blk][i] = (float)(ih[i] * 256 + il[i]) * d;
                 }
             }
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                // score / (row scale): the row scale is applied inside the exponent.
-                // No contraction: the product and both quad sums stay one
-                // multiply and two DPP adds (a fused multiply-add here costs a
-                // separate DPP move and a second multiply).
+            for (int i = 0; i < 4; ++i) {
 #pragma clang fp contract(off)
-                float f = (float)(ih[r] * 256 + il[r]) * d;
-                f += dpp_xor1(f);
-                f += dpp_xor2(f);
-                s[p][r] = f;
+                s[t][i] = (f[0][i] + f[1][i]) + (f[2][i] + f[3][i]);
             }
         }
         if constexpr (kPrefetch) issue_k(rec_next, kw);   // the scores no longer need kw
         if (need_mask) {
+            int limv[4];
 #pragma unroll
-            for (int p = 0; p < 4; ++p)
-#pragma unroll
-                for (int r = 0; r < R; ++r) s[p][r] = 16 * p + u <= lim[r] ? s[p][r] : -INFINITY;
-        }
-        // ---- slice maxima, probabilities and row sums.
-        float m_w[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-            m_w[r] = max_over_tokens(fmaxf(fmaxf(s[0][r], s[1][r]), fmaxf(s[2][r], s[3][r])));
-        // lane b of each quad exponentiates rows b and b + 4 of its 4 tokens.
-        // Masked scores are -inf and give exp2 = 0; a fully masked slice uses
-        // 0 as its reference, and a zero row scale is lifted to a tiny one so
-        // that 0 * -inf never arises.
-        float ea[4], eb[4];
-        float la = 0.f, lb = 0.f;
-        {
-            // per-lane selection of rows b and b + 4 by value selects (no
-            // divergent branches)
-            const bool b1 = (b & 1) != 0, b2 = (b & 2) != 0;
-            auto sel = [&](float x0, float x1, float x2, float x3) {
-                const float lo = b1 ? x1 : x0, hi = b1 ? x3 : x2;
-                return b2 ? hi : lo;
-            };
-            auto row = [&](const float* v, int r) { return r < R ? v[r] : -INFINITY; };
-            auto rowk = [&](const float* v, int r) { return r < R ? v[r] : 0.f; };
-            float ma = sel(row(m_w, 0), row(m_w, 1), row(m_w, 2), row(m_w, 3));
-            float mb = sel(row(m_w, 4), row(m_w, 5), row(m_w, 6), row(m_w, 7));
-            const float ka = fmaxf(sel(rowk(qs, 0), rowk(qs, 1), rowk(qs, 2), rowk(qs, 3)), 1e-30f);
-            const float kb = fmaxf(sel(rowk(qs, 4), rowk(qs, 5), rowk(qs, 6), rowk(qs, 7)), 1e-30f);
-            ma = ma == -INFINITY ? 0.f : ma;
-            mb = mb == -INFINITY ? 0.f : mb;
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const float sa = sel(row(s[p], 0), row(s[p], 1), row(s[p], 2), row(s[p], 3));
-                const float sb = sel(row(s[p], 4), row(s[p], 5), row(s[p], 6), row(s[p], 7));
-                ea[p] = __builtin_amdgcn_exp2f(ka * (sa - ma));
-                eb[p] = __builtin_amdgcn_exp2f(kb * (sb - mb));
-                la += ea[p];
-                lb += eb[p];
+            for (int i = 0; i < 4; ++i) {
+                const int r0 = i, r1 = 4 + i;
+                const int l0 = r0 < R ? lim[r0 < R ? r0 : 0] : -1;
+                const int l1 = r1 < R ? lim[r1 < R ? r1 : 0] : -1;
+                limv[i] = kg == 0 ? l0 : (kg == 1 ? l1 : -1);
             }
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s[t][i] = 16 * t + n <= limv[i] ? s[t][i] : -INFINITY;
         }
-        la = sum_over_tokens(la);
-        lb = sum_over_tokens(lb);
+        // ---- slice maxima, probabilities and row sums over the 16 lanes of
+        // each output row. Masked scores are -inf and give exp2 = 0; a fully
+        // masked slice uses 0 as its reference.
+        float m_w[4], e[4][4], lsum[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            m_w[i] = max_over_row16(fmaxf(fmaxf(s[0][i], s[1][i]), fmaxf(s[2][i], s[3][i])));
+            const float mref = m_w[i] == -INFINITY ? 0.f : m_w[i];
+            float acc = 0.f;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                e[t][i] = __builtin_amdgcn_exp2f(kav[i] * (s[t][i] - mref));
+                acc += e[t][i];
+            }
+            lsum[i] = sum_over_row16(acc);
+        }
         // The slice's V rows to LDS (read by other lanes of this wave only).
         // Maxima, exponentials and sums above need the scores alone, so they
         // run while the V rows (the last loads of the page) are still in
         // flight; the empty asm ties the rows to the row sums so that the
         // stores, and the wait for the V loads they imply, stay after them.
         {
-            const float dep = la + lb;
+            const float dep = lsum[0] + lsum[3];
 #pragma unroll
             for (int k = 0; k < 4; ++k)
                 asm volatile("" : "+v"(vr[k].x), "+v"(vr[k].y), "+v"(vr[k].z), "+v"(vr[k].w) : "v"(dep));
@@ -393,40 +399,35 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
         store_v(vr, vr2);
         if constexpr (kPrefetch) issue_v(rec_next, vr, vr2);
         wave_lds_sync();
-        // p * d_v for this lane's block b, all rows (quad broadcasts share the exps)
+        // p * d_v as f16 pairs of tokens (t, t + 16), t = 32 q2 + n: the 4 rows
+        // 4 kg .. 4 kg + 3 of a (pair, block) are one 16-byte store (rows past R
+        // are zero; lanes of rows 8..15 hold none)
         {
-            float dv[4];
+            float dv[4][kNB];
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int t = 16 * p + u;
-                const float d = f16_lo_to_float(*(const uint16_t*)(vt + t * kVRow + b * kVBlock));
-                dv[p] = t < valid ? d : 0.f;   // rows past the cache may hold NaN scales
+            for (int t = 0; t < 4; ++t) {
+                const int tok = 16 * t + n;
+#pragma unroll
+                for (int blk = 0; blk < kNB; ++blk) {
+                    const float d = f16_lo_to_float(*(const uint16_t*)(vt + tok * kVRow + blk * kVBlock));
+                    dv[t][blk] = tok < valid ? d : 0.f;   // rows past the cache may hold NaN scales
+                }
             }
-            float pr[R][4];
+            if (kg < 2) {
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                if (R > 0) pr[0 % R][p] = quad_bcast<0>(ea[p]);
-                if (R > 1) pr[1 % R][p] = quad_bcast<1>(ea[p]);
-                if (R > 2) pr[2 % R][p] = quad_bcast<2>(ea[p]);
-                if (R > 3) pr[3 % R][p] = quad_bcast<3>(ea[p]);
-                if (R > 4) pr[4 % R][p] = quad_bcast<0>(eb[p]);
-                if (R > 5) pr[5 % R][p] = quad_bcast<1>(eb[p]);
-            }
+                for (int q2 = 0; q2 < 2; ++q2) {
 #pragma unroll
-            for (int q2 = 0; q2 < 2; ++q2) {
-                uint32_t hv[8];
+                    for (int blk = 0; blk < kNB; ++blk) {
+                        uint32_t hv[4];
 #pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    if (r < R) {
-                        half2_t hp = {(_Float16)(pr[r][2 * q2] * dv[2 * q2]), (_Float16)(pr[r][2 * q2 + 1] * dv[2 * q2 + 1])};
-                        hv[r] = __builtin_bit_cast(uint32_t, hp);
-                    } else {
-                        hv[r] = 0u;
+                        for (int i = 0; i < 4; ++i) {
+                            const half2_t hp = {(_Float16)(e[2 * q2][i] * dv[2 * q2][blk]),
+                                                (_Float16)(e[2 * q2 + 1][i] * dv[2 * q2 + 1][blk])};
+                            hv[i] = 4 * kg + i < R ? __builtin_bit_cast(uint32_t, hp) : 0u;
+                        }
+                        *(uint4*)(ppw + blk * kPPStride + (16 * q2 + n) * 8 + 4 * kg) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
                     }
                 }
-                uint4* dst = (uint4*)(ppw + b * kPPStride + (q2 * 16 + u) * 8);
-                dst[0] = make_uint4(hv[0], hv[1], hv[2], hv[3]);
-                if (R > 4) dst[1] = make_uint4(hv[4], hv[5], hv[6], hv[7]);
             }
         }
         wave_lds_sync();
@@ -442,7 +443,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
         // columns of rows past R hold stale buffer words and only reach output
         // columns that are dropped.
         {
-            const int n = l & 15, kg = l >> 4;
             const half2_t off_lo = {(_Float16)1032.f, (_Float16)1032.f};
             const half2_t off_hi = {(_Float16)1152.f, (_Float16)1152.f};
             const uint32_t m_lo = vconst(0x000F000Fu), m_hi = vconst(0x00F000F0u), magic = vconst(0x64006400u);
@@ -473,13 +473,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
                 }
             }
         }
-        if (l < 4) {
+        if (n == 0 && kg < 2) {
 #pragma unroll
-            for (int r = 0; r < R; ++r)
-                if ((r & 3) == l) {
-                    sm.sm_[par][w][r] = m_w[r] == -INFINITY ? -INFINITY : qs[r] * m_w[r];
-                    sm.sl_[par][w][r] = r < 4 ? la : lb;
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * kg + i;
+                if (r < R) {
+                    sm.sm_[par][w][r] = m_w[i] == -INFINITY ? -INFINITY : qsv[i] * m_w[i];
+                    sm.sl_[par][w][r] = lsum[i];
                 }
+            }
         }
         lds_barrier();
 
