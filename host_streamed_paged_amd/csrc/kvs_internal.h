@@ -180,7 +180,7 @@ LaunchTiming& launch_timing();   // this thread's pending pair (kvs_kernels.hip)
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
-// few-row VALU decode kernel (kvs_decode.hip): rows = n_q * G in [1, 6]
+// few-row decode kernel (kvs_decode.hip): rows = n_q * G in [1, 6]
 bool decode_supports(int rows);
 hipError_t launch_decode(const AttendArgs& a, hipStream_t stream);
 // matrix-core kernel (kvs_mfma.hip) for more rows

@@ -357,7 +357,7 @@ def test_graph_replay_matches_eager():
 
 
 # (n_kv_heads, n_q_heads, query tokens, causal): every query-row count R of the
-# VALU decode kernel (R = query tokens x query heads per kv head, 1..6), with
+# decode kernel (R = query tokens x query heads per kv head, 1..6), with
 # causal blocks of 2 tokens among them
 DECODE_ROWS = [(2, 2, 1, False), (2, 4, 1, False), (2, 6, 1, False), (2, 4, 2, True), (1, 5, 1, False),
                (2, 6, 2, True)]
