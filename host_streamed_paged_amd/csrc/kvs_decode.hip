@@ -57,20 +57,11 @@ __device__ inline float f16_lo_to_float(uint32_t bits) {
     return (float)__builtin_bit_cast(_Float16, (unsigned short)(bits & 0xFFFFu));
 }
 
-// lane i receives lane (i ^ 1) / (i ^ 2) of its quad
-__device__ inline float dpp_xor1(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
-}
-__device__ inline float dpp_xor2(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
-}
 // lane i receives lane i +- 1 / 2 / 4 / 8 within its row of 16 (row rotate)
 template <int N>
 __device__ inline float dpp_ror(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x120 + N, 0xF, 0xF, true));
 }
-__device__ inline float dpp_ror4(float v) { return dpp_ror<4>(v); }
-__device__ inline float dpp_ror8(float v) { return dpp_ror<8>(v); }
 // max / sum over the 16 lanes of a DPP row (every lane gets the max; the sum's
 // rounding may differ from lane to lane)
 __device__ inline float max_over_row16(float v) {
@@ -102,9 +93,6 @@ struct DecodeSmem {
     alignas(16) uint8_t v[kWaves][kSlice * kVRow];            // each wave's V rows (record layout)
     alignas(16) uint32_t pp[kWaves][kNB][kPPStride];          // p * d_v as f16 pairs: [wave][block][pair * 8 + row]
     alignas(16) float sacc[2][kWaves][R][kHeadDim];           // slice partials (double-buffered by page parity)
-    alignas(16) uint32_t q_hi[R][kNB][8];                     // query codes, high bytes, 4 per dword
-    alignas(16) uint32_t q_lo[R][kNB][8];                     // query codes, low bytes
-    float q_scale[R];                                         // code -> log2-unit score scale, per row
     float sm_[2][kWaves][R], sl_[2][kWaves][R];
 };
 
@@ -174,98 +162,99 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
         *(uint2*)(vt + 4096 + 8 * l) = vr2;
     };
 
-    // ---- query rows -> 16-bit fixed point codes per (row, block). The query
-    // loads are issued first, before the segment is even known: vector memory
-    // counters retire in order, so the set-up below waits for the query only,
-    // with the page's K and V loads already in flight.
-    const bool qprep = tid < R * 16;
-    const int qr = tid >> 4, qb = (tid >> 2) & 3, qq = tid & 3;
-    uint4 qraw0 = make_uint4(0u, 0u, 0u, 0u), qraw1 = qraw0;   // raw query bits, converted once K is queued
-    const int qi = qr / G, qhd = g * G + qr % G;
-    const uint8_t* qaddr = (const uint8_t*)a.q +
-        (((int64_t)qi * a.n_q_heads + qhd) * kHeadDim + qb * kQK + qq * 8) * (a.q_f16 ? 2 : 4);
-    if (qprep) {
-        if (a.q_f16) {
-            qraw0 = *(const uint4*)qaddr;
-        } else {
-            qraw0 = ((const uint4*)qaddr)[0];
-            qraw1 = ((const uint4*)qaddr)[1];
+    // ---- query rows -> 16-bit fixed point codes, built by every wave in the
+    // layout of the score tiles' A operand: lane (n, kg) holds row n's
+    // channels 32 b + 8 kg .. 32 b + 8 kg + 7 of each block b. The query loads
+    // are issued first, before the segment is even known, and each wave
+    // converts its own copy, so no wave waits for another's page loads to be
+    // issued before its scores can start (vector memory counters retire in
+    // order: the conversion waits for this wave's query loads only).
+    uint4 qlo[kNB], qhi[kNB];   // raw query bits: elements 0..3 (all 8 for f16) and 4..7 of each window
+    {
+        const int qn = n < R ? n : 0;
+        const int qi = qn / G, qhd = g * G + qn % G;
+        const uint8_t* qrow = (const uint8_t*)a.q + ((int64_t)qi * a.n_q_heads + qhd) * kHeadDim * (a.q_f16 ? 2 : 4);
+#pragma unroll
+        for (int blk = 0; blk < kNB; ++blk) {
+            const int e0 = blk * kQK + 8 * kg;   // first element of this lane's window
+            qlo[blk] = qhi[blk] = make_uint4(0u, 0u, 0u, 0u);
+            if (n < R) {
+                if (a.q_f16) {
+                    qlo[blk] = *(const uint4*)(qrow + 2 * e0);
+                } else {
+                    qlo[blk] = ((const uint4*)(qrow + 4 * e0))[0];
+                    qhi[blk] = ((const uint4*)(qrow + 4 * e0))[1];
+                }
+            }
         }
     }
     typedef int int4v __attribute__((ext_vector_type(4)));
     const int4v segv = scalar_load((const int4v*)(a.segs + blockIdx.x));
     const Seg seg = {segv.x, segv.y, segv.z, segv.w};
-    // memory counters retire in order: query, then K blocks, then V rows
-    const uint8_t* rec0 = page_rec(seg.page0);
+    // memory counters retire in order: query, then K codes, then V rows. The
+    // segment carries its first page's source index, so the first record
+    // address needs no read of the page table.
+    const uint8_t* rec0 = page_record_of(a.ps, seg.page0, seg.flags >> kSegSrcShift);
     uint32_t kw[4][kKW];
     uint4 vr[4];
     uint2 vr2;
     issue_k(rec0, kw);
     issue_v(rec0, vr, vr2);
-    // keeps the query address registers allocated until the page loads are
-    // issued: their reuse would make the compiler wait for the query load
-    // (and everything before it) ahead of the first K load
-    asm volatile("" ::"v"(qaddr));
-    if (qprep) {
-        const int r = qr;
-        float x[8];
-        if (a.q_f16) {
-            const uint32_t wv[4] = {qraw0.x, qraw0.y, qraw0.z, qraw0.w};
+    // score operands: query row n (zero past R) as 16-bit fixed point with a
+    // per-row scale, split into int8 high and low bytes
+    long qa_hi[kNB], qa_lo[kNB];
+    float qsv[4], kav[4];
+    {
+        float x[kNB][8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = f16_lo_to_float(wv[e >> 1] >> (16 * (e & 1)));
-        } else {
-            const uint32_t wv[8] = {qraw0.x, qraw0.y, qraw0.z, qraw0.w, qraw1.x, qraw1.y, qraw1.z, qraw1.w};
+        for (int blk = 0; blk < kNB; ++blk) {
+            const uint32_t wv[8] = {qlo[blk].x, qlo[blk].y, qlo[blk].z, qlo[blk].w,
+                                    qhi[blk].x, qhi[blk].y, qhi[blk].z, qhi[blk].w};
+            if (a.q_f16) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = __builtin_bit_cast(float, wv[e]);
+                for (int e = 0; e < 8; ++e) x[blk][e] = f16_lo_to_float(wv[e >> 1] >> (16 * (e & 1)));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[blk][e] = __builtin_bit_cast(float, wv[e]);
+            }
         }
         float amax = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
-        // over the row's 16 threads: quad, then rotations by 4 and 8 in the row
-        amax = fmaxf(amax, dpp_xor1(amax));
-        amax = fmaxf(amax, dpp_xor2(amax));
-        amax = fmaxf(amax, dpp_ror4(amax));
-        amax = fmaxf(amax, dpp_ror8(amax));
+        for (int blk = 0; blk < kNB; ++blk)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[blk][e]));
+        // over the row's 4 lanes (n, n + 16, n + 32, n + 48)
+        amax = max_xor16(amax);
+        amax = max_xor32(amax);
         // |code| <= 32639 keeps the high byte of (code + 128) >> 8 inside int8;
         // a negative softmax scale is folded into the codes' sign
         const float inv = amax > 0.f ? (a.scale_log2 < 0.f ? -32639.f : 32639.f) / amax : 0.f;
-        uint32_t hw[2] = {0u, 0u}, lw[2] = {0u, 0u};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            int c = (int)rintf(x[e] * inv);
-            c = c > 32639 ? 32639 : (c < -32639 ? -32639 : c);
-            const int hi = (c + 128) >> 8;
-            const int lo = c - hi * 256;
-            hw[e >> 2] |= (uint32_t)(hi & 0xFF) << (8 * (e & 3));
-            lw[e >> 2] |= (uint32_t)(lo & 0xFF) << (8 * (e & 3));
-        }
-        sm.q_hi[r][qb][2 * qq] = hw[0];
-        sm.q_hi[r][qb][2 * qq + 1] = hw[1];
-        sm.q_lo[r][qb][2 * qq] = lw[0];
-        sm.q_lo[r][qb][2 * qq + 1] = lw[1];
-        if (qb == 0 && qq == 0) sm.q_scale[r] = amax / 32639.f * fabsf(a.scale_log2);
-    }
-    lds_barrier();
-    // score operands: query row n (zero past R), channels 8 kg .. 8 kg + 7 of
-    // each block, high and low bytes; the row scales of output rows 4 kg + i
-    long qa_hi[kNB], qa_lo[kNB];
-    {
-        const int qn = n < R ? n : 0;
 #pragma unroll
         for (int blk = 0; blk < kNB; ++blk) {
-            const uint64_t h = ((uint64_t)sm.q_hi[qn][blk][2 * kg + 1] << 32) | sm.q_hi[qn][blk][2 * kg];
-            const uint64_t o = ((uint64_t)sm.q_lo[qn][blk][2 * kg + 1] << 32) | sm.q_lo[qn][blk][2 * kg];
-            qa_hi[blk] = n < R ? (long)h : 0;
-            qa_lo[blk] = n < R ? (long)o : 0;
-        }
-    }
-    float qsv[4], kav[4];
+            uint32_t hw[2] = {0u, 0u}, lw[2] = {0u, 0u};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 4 * kg + i;
-        qsv[i] = r < R ? sm.q_scale[r < R ? r : 0] : 0.f;
-        // a zero row scale is lifted to a tiny one so that 0 * -inf never arises
-        kav[i] = fmaxf(qsv[i], 1e-30f);
+            for (int e = 0; e < 8; ++e) {
+                int c = (int)rintf(x[blk][e] * inv);
+                c = c > 32639 ? 32639 : (c < -32639 ? -32639 : c);
+                const int hi = (c + 128) >> 8;
+                const int lo = c - hi * 256;
+                hw[e >> 2] |= (uint32_t)(hi & 0xFF) << (8 * (e & 3));
+                lw[e >> 2] |= (uint32_t)(lo & 0xFF) << (8 * (e & 3));
+            }
+            qa_hi[blk] = (long)(((uint64_t)hw[1] << 32) | hw[0]);
+            qa_lo[blk] = (long)(((uint64_t)lw[1] << 32) | lw[0]);
+        }
+        // code -> log2-unit score scale of row n, then of output rows 4 kg + i
+        // (held by lanes 4 kg + i)
+        const float qs_n = amax / 32639.f * fabsf(a.scale_log2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * kg + i;
+            const float q = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * r, __builtin_bit_cast(int, qs_n)));
+            qsv[i] = r < R ? q : 0.f;
+            // a zero row scale is lifted to a tiny one so that 0 * -inf never arises
+            kav[i] = fmaxf(qsv[i], 1e-30f);
+        }
     }
 
     // group state, distributed for the per-page merge: thread owns channel

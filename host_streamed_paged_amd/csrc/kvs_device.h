@@ -65,11 +65,14 @@ __device__ inline float add_xor32(float v) {
 // Page record of logical page `page` for this launch: a resident slot, a
 // slot of the ring chunk the launch works on, or (zero-copy launches) the
 // pinned host record itself.
-__device__ inline const uint8_t* page_record(const PageSource& ps, int32_t page) {
-    const int32_t sv = scalar_load(ps.src + page);
+// Record of page `page` whose source index src[page] is sv.
+__device__ inline const uint8_t* page_record_of(const PageSource& ps, int32_t page, int32_t sv) {
     if (sv >= 0) return ps.slots + (int64_t)sv * ps.page_bytes;
     if (ps.host) return ps.host + (int64_t)page * ps.page_bytes;
     return ps.ring_chunk + (int64_t)((-1 - sv) - ps.chunk_rank0) * ps.page_bytes;
+}
+__device__ inline const uint8_t* page_record(const PageSource& ps, int32_t page) {
+    return page_record_of(ps, page, scalar_load(ps.src + page));
 }
 
 // Launch a kernel; a pending timing pair (launch_timing) goes with it.

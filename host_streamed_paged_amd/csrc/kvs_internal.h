@@ -30,6 +30,13 @@ struct Seg {
     int32_t flags;
 };
 constexpr int32_t kSegFresh = 1;
+// The device copy of a layer's segments carries src[page0] (see PageSource)
+// in flags bits 8..31, so that a kernel finds its first page's record without
+// a dependent read of the page table; bits 0..7 hold the flags proper. Slot
+// indices and streamed ranks therefore stay within a signed 24-bit range.
+constexpr int kSegSrcShift = 8;
+constexpr int32_t kSegFlagMask = 0xFF;
+constexpr int64_t kMaxSlots = (int64_t(1) << 23) - 1;
 
 // Where page p's record lives: src[p] >= 0 is a resident slot index;
 // src[p] < 0 means streamed with rank -1 - src[p], found in the ring chunk of

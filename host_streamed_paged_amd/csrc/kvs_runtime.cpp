@@ -635,7 +635,7 @@ int64_t kvs_slots_for_budget(const kvs_config* cfg, uint64_t budget_bytes) {
     if (validate(cfg)) return 0;
     Layout L = layout_of(cfg);
     if (budget_bytes < L.fixed) return 0;
-    return (int64_t)((budget_bytes - L.fixed) / L.page_bytes);
+    return std::min<int64_t>((int64_t)((budget_bytes - L.fixed) / L.page_bytes), kvs::kMaxSlots);
 }
 
 int32_t kvs_auto_resident_pages(int64_t n_ctx) {
@@ -722,7 +722,7 @@ int kvs_pool_create(const kvs_config* cfg, void* dev_arena, uint64_t budget_byte
         ls.dev_segs = (kvs::Seg*)cur; cur += L.seg_bytes;
     }
     p->slots = cur;
-    p->n_slots = (int64_t)((budget_bytes - L.fixed) / L.page_bytes);
+    p->n_slots = std::min<int64_t>((int64_t)((budget_bytes - L.fixed) / L.page_bytes), kvs::kMaxSlots);
     for (int64_t s = p->n_slots - 1; s >= 0; --s) p->slot_free.push_back((int32_t)s);
     p->n_cslots = cfg->ring_pages / cfg->chunk_pages;
     auto cleanup = [&](const char* what, hipError_t e) {
@@ -837,8 +837,13 @@ int kvs_page_table_set(kvs_pool* p, int32_t layer, int32_t n_pages, const uint8_
             p->st.resident_upload_bytes += (int64_t)p->L.page_bytes;
         }
     if (n_pages > 0) KVS_HIP(hipMemcpyAsync(ls.dev_src, ls.src.data(), n_pages * sizeof(int32_t), hipMemcpyHostToDevice, s));
-    if (!ls.segs.empty())
-        KVS_HIP(hipMemcpyAsync(ls.dev_segs, ls.segs.data(), ls.segs.size() * sizeof(kvs::Seg), hipMemcpyHostToDevice, s));
+    // device copy of the segments: flags bits 8.. carry src[page0] (slot
+    // indices below kMaxSlots, streamed ranks below max_pages <= 2^22)
+    std::vector<kvs::Seg> dsegs(ls.segs);
+    for (kvs::Seg& sg : dsegs)
+        sg.flags = (sg.flags & kvs::kSegFlagMask) | (int32_t)((uint32_t)ls.src[sg.page0] << kvs::kSegSrcShift);
+    if (!dsegs.empty())
+        KVS_HIP(hipMemcpyAsync(ls.dev_segs, dsegs.data(), dsegs.size() * sizeof(kvs::Seg), hipMemcpyHostToDevice, s));
     KVS_HIP(hipStreamSynchronize(s));
     ls.n_pages = n_pages;
     return KVS_OK;
