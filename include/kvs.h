@@ -153,7 +153,8 @@ uint64_t kvs_page_bytes(const kvs_config* cfg);
 int kvs_min_budget_bytes(const kvs_config* cfg, uint64_t* out);
 
 /* Number of resident page slots a budget yields for cfg (0 if below the
- * minimum). Pure. */
+ * minimum), at most 2^23 - 1 (slot indices travel in 24 bits of the launch
+ * plan). A pool created with the same budget has this many slots. Pure. */
 int64_t kvs_slots_for_budget(const kvs_config* cfg, uint64_t budget_bytes);
 
 /* Pool policy: automatic sizing and the newest-page residency rule.
