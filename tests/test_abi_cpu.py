@@ -81,6 +81,8 @@ def test_page_bytes_and_budget_math():
     assert kvs.slots_for_budget(c, mb - 1) == 0
     assert kvs.slots_for_budget(c, mb) == 0
     assert kvs.slots_for_budget(c, mb + 103 * 16 * pb) == 103 * 16
+    # slot indices travel in 24 bits of the device launch plan: the count is capped
+    assert kvs.slots_for_budget(c, mb + (1 << 24) * pb) == (1 << 23) - 1
     # the smallest useful pool holds one page of ring
     one = base_cfg(ring_pages=1, chunk_pages=1, max_pages=1, n_layers=1)
     assert kvs.min_budget_bytes(one) >= kvs.page_bytes(one)
