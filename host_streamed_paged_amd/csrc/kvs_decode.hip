@@ -257,25 +257,22 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
         }
     }
 
-    // group state, distributed for the per-page merge: thread owns channel
-    // c = tid & 127 of rows r = (tid >> 7) + 2 k
-    const int mc = tid & (kHeadDim - 1), mr0 = tid >> 7;
-    constexpr int kMR = (R + 1) / 2;
-    float acc_run[kMR], m_run[kMR], l_run[kMR];
-#pragma unroll
-    for (int k = 0; k < kMR; ++k) { acc_run[k] = 0.f; m_run[k] = -INFINITY; l_run[k] = 0.f; }
-    if (!(seg.flags & kSegFresh)) {
-#pragma unroll
-        for (int k = 0; k < kMR; ++k) {
-            const int r = mr0 + 2 * k;
-            if (r < R) {
-                const int i = r / G, h = g * G + r % G;
-                const float* pr = a.part + (((int64_t)seg.group * a.n_q + i) * a.n_q_heads + h) * kPartStride;
-                acc_run[k] = pr[mc];
-                m_run[k] = pr[kHeadDim];
-                l_run[k] = pr[kHeadDim + 1];
-            }
-        }
+    // group state, distributed for the per-page merge: thread owns channels
+    // mc4 .. mc4 + 3 of row mr (threads of rows past R take no part), so each
+    // thread's merge is one row deep
+    static_assert(R * 32 <= kThreads, "one merge row per 32 threads");
+    const int mr = tid >> 5, mc4 = 4 * (tid & 31);
+    const bool mown = mr < R;
+    const int mrr = mown ? mr : 0;
+    float acc_run[4] = {0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+    if (!(seg.flags & kSegFresh) && mown) {
+        const int i = mrr / G, h = g * G + mrr % G;
+        const float* pr = a.part + (((int64_t)seg.group * a.n_q + i) * a.n_q_heads + h) * kPartStride;
+        const float2 a0 = *(const float2*)(pr + mc4), a1 = *(const float2*)(pr + mc4 + 2);   // records are 8-byte aligned
+        acc_run[0] = a0.x; acc_run[1] = a0.y; acc_run[2] = a1.x; acc_run[3] = a1.y;
+        m_run = pr[kHeadDim];
+        l_run = pr[kHeadDim + 1];
     }
 
     uint32_t* ppw = sm.pp[w][0];
@@ -475,45 +472,41 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
         lds_barrier();
 
         // ---- merge the 4 slices (fixed order), then the page into the group state
+        if (mown) {
+            float ms[kWaves], M = -INFINITY;
 #pragma unroll
-        for (int k = 0; k < kMR; ++k) {
-            const int r = mr0 + 2 * k;
-            if (r < R) {
-                float ms[kWaves], M = -INFINITY;
+            for (int ww = 0; ww < kWaves; ++ww) { ms[ww] = sm.sm_[par][ww][mrr]; M = fmaxf(M, ms[ww]); }
+            float pa[4] = {0.f, 0.f, 0.f, 0.f}, pl = 0.f;
+            if (M != -INFINITY) {
 #pragma unroll
-                for (int ww = 0; ww < kWaves; ++ww) { ms[ww] = sm.sm_[par][ww][r]; M = fmaxf(M, ms[ww]); }
-                float pa = 0.f, pl = 0.f;
-                if (M != -INFINITY) {
+                for (int ww = 0; ww < kWaves; ++ww) {
+                    const float f = __builtin_amdgcn_exp2f(ms[ww] - M);   // 0 for an empty slice
+                    const f32x4 sv = *(const f32x4*)&sm.sacc[par][ww][mrr][mc4];
 #pragma unroll
-                    for (int ww = 0; ww < kWaves; ++ww) {
-                        const float f = __builtin_amdgcn_exp2f(ms[ww] - M);   // 0 for an empty slice
-                        pa = fmaf(sm.sacc[par][ww][r][mc], f, pa);
-                        pl = fmaf(sm.sl_[par][ww][r], f, pl);
-                    }
+                    for (int c = 0; c < 4; ++c) pa[c] = fmaf(sv[c], f, pa[c]);
+                    pl = fmaf(sm.sl_[par][ww][mrr], f, pl);
                 }
-                const float Mn = fmaxf(m_run[k], M);
-                if (Mn != -INFINITY) {
-                    const float al = __builtin_amdgcn_exp2f(m_run[k] - Mn);   // 0 from an empty state
-                    const float be = __builtin_amdgcn_exp2f(M - Mn);
-                    acc_run[k] = acc_run[k] * al + pa * be;
-                    l_run[k] = l_run[k] * al + pl * be;
-                    m_run[k] = Mn;
-                }
+            }
+            const float Mn = fmaxf(m_run, M);
+            if (Mn != -INFINITY) {
+                const float al = __builtin_amdgcn_exp2f(m_run - Mn);   // 0 from an empty state
+                const float be = __builtin_amdgcn_exp2f(M - Mn);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc_run[c] = acc_run[c] * al + pa[c] * be;
+                l_run = l_run * al + pl * be;
+                m_run = Mn;
             }
         }
     };
     for (int pi = 0; pi + 1 < seg.npages; ++pi) page_body(pi, std::true_type{});
     page_body(seg.npages - 1, std::false_type{});
 
-#pragma unroll
-    for (int k = 0; k < kMR; ++k) {
-        const int r = mr0 + 2 * k;
-        if (r < R) {
-            const int i = r / G, h = g * G + r % G;
-            float* pr = a.part + (((int64_t)seg.group * a.n_q + i) * a.n_q_heads + h) * kPartStride;
-            pr[mc] = acc_run[k];
-            if (mc == 0) { pr[kHeadDim] = m_run[k]; pr[kHeadDim + 1] = l_run[k]; }
-        }
+    if (mown) {
+        const int i = mrr / G, h = g * G + mrr % G;
+        float* pr = a.part + (((int64_t)seg.group * a.n_q + i) * a.n_q_heads + h) * kPartStride;
+        *(float2*)(pr + mc4) = make_float2(acc_run[0], acc_run[1]);
+        *(float2*)(pr + mc4 + 2) = make_float2(acc_run[2], acc_run[3]);
+        if (mc4 == 0) { pr[kHeadDim] = m_run; pr[kHeadDim + 1] = l_run; }
     }
 }
 
