@@ -92,7 +92,9 @@ template <int R>
 struct DecodeSmem {
     alignas(16) uint8_t v[kWaves][kSlice * kVRow];            // each wave's V rows (record layout)
     alignas(16) uint32_t pp[kWaves][kNB][kPPStride];          // p * d_v as f16 pairs: [wave][block][pair * 8 + row]
-    alignas(16) float sacc[2][kWaves][R][kHeadDim];           // slice partials (double-buffered by page parity)
+    // slice partials (double-buffered by page parity); rows padded to 144
+    // floats so that the rows' 16-byte stores fall on different LDS banks
+    alignas(16) float sacc[2][kWaves][R][kHeadDim + 16];
     float sm_[2][kWaves][R], sl_[2][kWaves][R];
 };
 
