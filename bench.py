@@ -44,10 +44,10 @@ sys.path.insert(0, ROOT)
 # group sizes in pages; one copy stream for kvs_stream_enqueue). The
 # full-size parity tests use the same table.
 POOL_CFG = {
-    "resident_decode_32k": dict(ring_pages=48, chunk_pages=4, copy_streams=1, group_pages=1),
-    "streamed_decode_256k": dict(ring_pages=48, chunk_pages=4, copy_streams=1, group_pages=1),
-    "spec_verify_160k": dict(ring_pages=48, chunk_pages=4, copy_streams=1, group_pages=1),
-    "prefill_ubatch_128k": dict(ring_pages=96, chunk_pages=16, copy_streams=1, group_pages=8),
+    "resident_decode_32k": dict(ring_pages=48, chunk_pages=4, group_pages=1),
+    "streamed_decode_256k": dict(ring_pages=48, chunk_pages=4, group_pages=1),
+    "spec_verify_160k": dict(ring_pages=48, chunk_pages=4, group_pages=1),
+    "prefill_ubatch_128k": dict(ring_pages=96, chunk_pages=16, group_pages=8),
 }
 
 METRIC = "streamed attention KV GB/s + decode attn tok/s at 32K/256K ctx, % of HBM/link roofline"

@@ -38,7 +38,10 @@ EXPORTS = [
     "kvs_page_table_set", "kvs_stream_enqueue", "kvs_attend", "kvs_status", "kvs_debug_gather",
     "kvs_debug_read_page", "kvs_last_error", "kvs_profile_enable", "kvs_profile_read", "kvs_append",
     "kvs_auto_resident_pages", "kvs_auto_stage_bytes", "kvs_auto_budget_bytes", "kvs_residency_promote_newest",
+    "kvs_pool_pin_layer", "kvs_pool_reset_pinned", "kvs_debug_export_pages", "kvs_debug_stage",
 ]
+
+STAGED_TILE_BYTES = 133376   # KVS_STAGED_TILE_BYTES
 
 
 class KvsError(RuntimeError):
@@ -50,7 +53,7 @@ class KvsError(RuntimeError):
 class KvsConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "n_layers", "n_kv_heads", "n_q_heads", "head_dim", "page_tokens", "type_k", "type_v",
-        "max_pages", "max_q_tokens", "ring_pages", "chunk_pages", "copy_streams", "group_pages")] + [
+        "max_pages", "max_q_tokens", "ring_pages", "chunk_pages", "group_pages")] + [
         ("flags", ctypes.c_uint32)]
 
 
@@ -62,7 +65,7 @@ class KvsPlanInfo(ctypes.Structure):
 class KvsStatus(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "page_bytes", "slot_count", "slots_used", "ring_pages", "workspace_bytes", "bytes_h2d",
-        "pages_streamed", "copies_issued", "kernels_launched", "resident_upload_bytes")]
+        "pages_streamed", "copies_issued", "kernels_launched", "resident_upload_bytes", "pinned_slots")]
 
 
 _lib = None
@@ -100,6 +103,10 @@ def lib() -> ctypes.CDLL:
         "kvs_auto_budget_bytes": (ctypes.c_int, [cfgp, I64, ctypes.POINTER(U64)]),
         "kvs_residency_promote_newest": (ctypes.c_int, [P, I32, I32, I32, P]),
         "kvs_debug_read_page": (ctypes.c_int, [P, I32, I32, P]),
+        "kvs_debug_export_pages": (ctypes.c_int, [P, I32, P, P]),
+        "kvs_debug_stage": (ctypes.c_int, [P, I32, I64, P, P]),
+        "kvs_pool_pin_layer": (ctypes.c_int, [P, I32, I32]),
+        "kvs_pool_reset_pinned": (ctypes.c_int, [P]),
         "kvs_last_error": (ctypes.c_char_p, []),
         "kvs_profile_enable": (ctypes.c_int, [P, I32]),
         "kvs_profile_read": (ctypes.c_int, [P, I32, ctypes.POINTER(I64), ctypes.POINTER(ctypes.c_double), I32]),
@@ -135,7 +142,6 @@ class Config:
     max_q_tokens: int = 1
     ring_pages: int = 16
     chunk_pages: int = 4
-    copy_streams: int = 4
     group_pages: int = 1
     head_dim: int = 128
     page_tokens: int = 256
@@ -146,7 +152,7 @@ class Config:
     def c(self) -> KvsConfig:
         return KvsConfig(self.n_layers, self.n_kv_heads, self.n_q_heads, self.head_dim, self.page_tokens,
                          self.type_k, self.type_v, self.max_pages, self.max_q_tokens, self.ring_pages,
-                         self.chunk_pages, self.copy_streams, self.group_pages, self.flags)
+                         self.chunk_pages, self.group_pages, self.flags)
 
 
 def type_pair_supported(type_k: int, type_v: int) -> bool:
@@ -304,6 +310,26 @@ class Pool:
         n, ms = ctypes.c_int64(0), ctypes.c_double(0.0)
         _check(lib().kvs_profile_read(self._h, kind, ctypes.byref(n), ctypes.byref(ms), 1 if reset else 0))
         return n.value, ms.value
+
+    def pin_layer(self, layer: int, n_slots: int):
+        """Reserve a pinned region of n_slots slots for one layer (kvs_pool_pin_layer)."""
+        _check(lib().kvs_pool_pin_layer(self._h, layer, n_slots))
+
+    def reset_pinned(self):
+        """Return every pinned region to the pool (kvs_pool_reset_pinned)."""
+        _check(lib().kvs_pool_reset_pinned(self._h))
+
+    def debug_export_pages(self, layer: int, dst: torch.Tensor, stream=None):
+        """Raw page records as the kernels read them, into dst (uint8, device,
+        [n_pages, page_bytes]) (kvs_debug_export_pages)."""
+        assert dst.is_cuda and dst.dtype == torch.uint8 and dst.is_contiguous()
+        _check(lib().kvs_debug_export_pages(self._h, layer, _ptr(dst), _stream(stream)))
+
+    def debug_stage(self, layer: int, n_kv: int, dst: torch.Tensor, stream=None):
+        """Staged matrix-core operands of every page (kvs_debug_stage) into dst
+        (uint8, device, [n_pages, n_kv_heads, STAGED_TILE_BYTES])."""
+        assert dst.is_cuda and dst.dtype == torch.uint8 and dst.is_contiguous()
+        _check(lib().kvs_debug_stage(self._h, layer, n_kv, _ptr(dst), _stream(stream)))
 
     def debug_read_page(self, layer: int, page: int):
         import numpy as np

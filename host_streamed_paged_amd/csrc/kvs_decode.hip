@@ -40,8 +40,6 @@
 namespace kvs {
 namespace {
 
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -53,9 +51,6 @@ constexpr int kSlicePairs = kSlice / 2;        // 32 token pairs
 constexpr int kPPStride = kSlicePairs * 8 + 8; // dwords per block row of pp (padded: no bank clash across blocks)
 constexpr int kKW = 14;                        // K dwords per lane and 16-token tile
 
-__device__ inline float f16_lo_to_float(uint32_t bits) {
-    return (float)__builtin_bit_cast(_Float16, (unsigned short)(bits & 0xFFFFu));
-}
 
 // lane i receives lane i +- 1 / 2 / 4 / 8 within its row of 16 (row rotate)
 template <int N>
@@ -214,7 +209,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
                                     qhi[blk].x, qhi[blk].y, qhi[blk].z, qhi[blk].w};
             if (a.q_f16) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[blk][e] = f16_lo_to_float(wv[e >> 1] >> (16 * (e & 1)));
+                for (int e = 0; e < 8; ++e) x[blk][e] = scale_f32(wv[e >> 1] >> (16 * (e & 1)));
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) x[blk][e] = __builtin_bit_cast(float, wv[e]);
@@ -328,7 +323,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
                 const i32x4 zero = {0, 0, 0, 0};
                 const i32x4 ih = __builtin_amdgcn_mfma_i32_16x16x32_i8(qa_hi[blk], kb, zero, 0, 0, 0);
                 const i32x4 il = __builtin_amdgcn_mfma_i32_16x16x32_i8(qa_lo[blk], kb, zero, 0, 0, 0);
-                const float d = f16_lo_to_float(kw[t][10 + blk] >> (16 * (blk & 1)));
+                const float d = scale_f32(kw[t][10 + blk] >> (16 * (blk & 1)));
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
 #pragma clang fp contract(off)
@@ -389,7 +384,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
         wave_lds_sync();
         // p * d_v as f16 pairs of tokens (t, t + 16), t = 32 q2 + n: the 4 rows
         // 4 kg .. 4 kg + 3 of a (pair, block) are one 16-byte store (rows past R
-        // are zero; lanes of rows 8..15 hold none)
+        // are zero; lanes of rows 8..15 hold none). Each block's scales are
+        // first divided by a power of two 2^k_b that puts the slice's largest
+        // magnitude in [0.5, 1), so that p * d_v (p <= 1) keeps its precision
+        // in f16 whatever the scales' size; the slice partial of the block is
+        // multiplied back by 2^k_b (exact).
+        float vunit[kNB];
         {
             float dv[4][kNB];
 #pragma unroll
@@ -397,9 +397,20 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
                 const int tok = 16 * t + n;
 #pragma unroll
                 for (int blk = 0; blk < kNB; ++blk) {
-                    const float d = f16_lo_to_float(*(const uint16_t*)(vt + tok * kVRow + blk * kVBlock));
+                    const float d = scale_f32(*(const uint16_t*)(vt + tok * kVRow + blk * kVBlock));
                     dv[t][blk] = tok < valid ? d : 0.f;   // rows past the cache may hold NaN scales
                 }
+            }
+#pragma unroll
+            for (int blk = 0; blk < kNB; ++blk) {
+                // largest magnitude over the slice's 64 tokens (16 t + n over a DPP row)
+                float mx = fmaxf(fmaxf(fabsf(dv[0][blk]), fabsf(dv[1][blk])), fmaxf(fabsf(dv[2][blk]), fabsf(dv[3][blk])));
+                mx = max_over_row16(mx);
+                const int kb = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx) : 0;
+                vunit[blk] = __builtin_amdgcn_ldexpf(1.f, kb);
+                const float down = __builtin_amdgcn_ldexpf(1.f, -kb);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) dv[t][blk] *= down;   // exact
             }
             if (kg < 2) {
 #pragma unroll
@@ -453,11 +464,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
                     clo = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, alo), pb, clo, 0, 0, 0);
                     chi = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ahi), pb, chi, 0, 0, 0);
                 }
-                // slice partial -> LDS (the next page writes the other parity)
+                // slice partial -> LDS (the next page writes the other parity),
+                // back in absolute units
                 if (n < R) {
                     float* dst = &sm.sacc[par][w][n < R ? n : 0][32 * vb + 4 * kg];
-                    *(f32x4*)dst = clo;
-                    *(f32x4*)(dst + 16) = chi * 0.0625f;   // high nibbles carried 16 (u - 8)
+                    *(f32x4*)dst = clo * vunit[vb];
+                    *(f32x4*)(dst + 16) = chi * (vunit[vb] * 0.0625f);   // high nibbles carried 16 (u - 8)
                 }
             }
         }

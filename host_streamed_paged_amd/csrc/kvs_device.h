@@ -62,6 +62,48 @@ __device__ inline float add_xor32(float v) {
     return f_bits(r[0]) + f_bits(r[1]);
 }
 
+// ---- Block decoding, shared by every kernel that reads page records (the
+// attention kernels, the staging kernel and the gather probe), so that a
+// probe of one checks the arithmetic of all.
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+
+__device__ inline half2_t as_h2(uint32_t x) { return __builtin_bit_cast(half2_t, x); }
+__device__ inline uint32_t as_u(half2_t x) { return __builtin_bit_cast(uint32_t, x); }
+
+// A block scale: the binary16 in the low 16 bits of `bits`, as float32 (exact).
+__device__ inline float scale_f32(uint32_t bits) {
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)(bits & 0xFFFFu));
+}
+
+// Eight Q8_0 codes, packed little-endian in two dwords, as exact binary16
+// values: each code k is biased to u = k + 128 in [0, 255], 0x6400 | u is the
+// binary16 value 1024 + u, and 1152 = 1024 + 128 is subtracted. Every step is
+// exact, code -128 included.
+__device__ inline half8_t q8_codes_f16(uint32_t x0, uint32_t x1) {
+    const half2_t k_off = {(_Float16)1152.f, (_Float16)1152.f};
+    const uint32_t c_hi64 = 0x64646464u;
+    x0 ^= 0x80808080u;
+    x1 ^= 0x80808080u;
+    const half2_t e0 = as_h2(__builtin_amdgcn_perm(c_hi64, x0, 0x04010400u)) - k_off;
+    const half2_t e1 = as_h2(__builtin_amdgcn_perm(c_hi64, x0, 0x04030402u)) - k_off;
+    const half2_t e2 = as_h2(__builtin_amdgcn_perm(c_hi64, x1, 0x04010400u)) - k_off;
+    const half2_t e3 = as_h2(__builtin_amdgcn_perm(c_hi64, x1, 0x04030402u)) - k_off;
+    half8_t r;
+    r[0] = e0[0]; r[1] = e0[1]; r[2] = e1[0]; r[3] = e1[1];
+    r[4] = e2[0]; r[5] = e2[1]; r[6] = e3[0]; r[7] = e3[1];
+    return r;
+}
+
+// Two Q4_0 nibbles u, held as the binary16 values 1024 + u (0x6400 | u in
+// each half of `biased`), as the exact binary16 values (u - 8) * c for
+// c = 1 or 1/8 passed as the pair {c, c} with minus_1032c = {-1032 c, -1032 c}:
+// (1024 + u) c - 1032 c is one fused operation whose exact result is
+// representable, so nothing is rounded.
+__device__ inline half2_t q4_nibbles_f16(uint32_t biased, half2_t c, half2_t minus_1032c) {
+    return __builtin_elementwise_fma(as_h2(biased), c, minus_1032c);
+}
+
 // Page record of logical page `page` for this launch: a resident slot, a
 // slot of the ring chunk the launch works on, or (zero-copy launches) the
 // pinned host record itself.

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
+#include "kvs.h"
+
 namespace kvs {
 
 constexpr int kPageTokens = 256;             // tokens per page
@@ -18,7 +20,13 @@ constexpr int kVRow = kNB * kVBlock;         // 72 B
 constexpr int kKTile = kPageTokens * kKRow;  // 34816 B: one head's K for one page
 constexpr int kVTile = kPageTokens * kVRow;  // 18432 B
 constexpr int kPartStride = kHeadDim + 2;    // partial record: acc[128], m (log2 units), l
-constexpr int kStagedTile = 2 * kPageTokens * kHeadDim * 2;   // f16 K and V^T operands of one (page, kv head)
+// Staged matrix-core operands of one (page, kv head): the f16 K and V^T
+// operands in fragment order, the K block scales per token, and the V scaling
+// exponent of each 32-channel block (padded to keep tiles 256-byte aligned).
+constexpr int kStagedOps = 2 * kPageTokens * kHeadDim * 2;
+constexpr int kStagedScaleBytes = kPageTokens * kNB * 2;
+constexpr int kStagedTile = kStagedOps + kStagedScaleBytes + 256;
+static_assert(kStagedTile == KVS_STAGED_TILE_BYTES, "staged tile size as documented in kvs.h");
 
 // One run of consecutive logical pages of one split-K group, processed in
 // page order by one workgroup. flags bit 0: page0 is the group's first page
@@ -132,6 +140,7 @@ struct StageArgs {
     int64_t n_kv;
     int32_t n_pages;      // pages of the launch's segments
     uint8_t* staged;      // [pages][n_kv_heads][kStagedTile]
+    int32_t by_page;      // 1: page p goes to tile p (a probe of a whole layer), 0: the x-th page to tile x
 };
 
 // The first `first` pages of a copy job, or the rest (ring slots follow).
@@ -158,6 +167,15 @@ struct GatherArgs {
     int64_t n_tok;
     float* k_out;         // [n_tok, Hkv, 128]
     float* v_out;
+};
+
+// Raw record export probe: the bytes of each page as the kernels read them.
+struct ExportArgs {
+    CopyJob copy;
+    PageSource ps;
+    const Seg* segs;
+    int32_t n_segs;
+    uint8_t* dst;         // [n_pages][page_bytes], device
 };
 
 // KV append: new K and V rows [n_tok, Hkv, 128] (f32 or f16) quantized into
@@ -197,6 +215,7 @@ hipError_t launch_stage(const StageArgs& a, hipStream_t stream);
 hipError_t launch_combine(const float* part, int32_t n_groups, int32_t n_q, int32_t n_q_heads,
                           float* out, float* lse, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
+hipError_t launch_export(const ExportArgs& a, hipStream_t stream);
 hipError_t launch_fill_u32(void* dst, uint32_t value, uint64_t n_words, hipStream_t stream);
 hipError_t launch_copy(const CopyJob& cj, hipStream_t stream);   // copy-only launch
 

@@ -28,9 +28,6 @@
 namespace kvs {
 namespace {
 
-__device__ inline float f16_bits_to_float(uint32_t bits) {
-    return (float)__builtin_bit_cast(_Float16, (unsigned short)(bits & 0xFFFFu));
-}
 
 // ---------------------------------------------------------------------------
 // Split-K combine: one workgroup per output row (query token x head), 16
@@ -110,8 +107,11 @@ __global__ __launch_bounds__(64 * kCombWaves) void combine_kernel(const float* _
 }
 
 // ---------------------------------------------------------------------------
-// Gather probe: dequantize tokens of the launch's pages into float32.
-// One workgroup per (segment, kv head); thread = token row of the page.
+// Gather probe: dequantize tokens of the launch's pages into float32 through
+// the block decoding the attention kernels use (kvs_device.h): each Q8_0 code
+// and Q4_0 nibble becomes an exact f16 value, multiplied by the float32 block
+// scale (exact: an 8-bit by 11-bit product). One workgroup per (segment, kv
+// head); thread = token row of the page.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kPageTokens) void gather_kernel(GatherArgs a) {
     if ((int)blockIdx.x >= a.n_segs) {   // ring refill workgroup
@@ -120,6 +120,7 @@ __global__ __launch_bounds__(kPageTokens) void gather_kernel(GatherArgs a) {
     }
     const Seg seg = a.segs[blockIdx.x];
     const int g = blockIdx.y, t = threadIdx.x;
+    const half2_t one = {(_Float16)1.f, (_Float16)1.f}, m1032 = {(_Float16)-1032.f, (_Float16)-1032.f};
     for (int pi = 0; pi < seg.npages; ++pi) {
         const int page = seg.page0 + pi;
         const int64_t tok = (int64_t)page * kPageTokens + t;
@@ -130,17 +131,54 @@ __global__ __launch_bounds__(kPageTokens) void gather_kernel(GatherArgs a) {
         float* ko = a.k_out + ((tok - a.tok0) * a.n_kv_heads + g) * kHeadDim;
         float* vo = a.v_out + ((tok - a.tok0) * a.n_kv_heads + g) * kHeadDim;
         for (int b = 0; b < kNB; ++b) {
-            const uint8_t* kb = kr + b * kKBlock;
-            float dk = f16_bits_to_float((uint32_t)kb[0] | ((uint32_t)kb[1] << 8));
-            for (int i = 0; i < kQK; ++i) ko[b * kQK + i] = dk * (float)(int8_t)kb[2 + i];
-            const uint8_t* vb = vr + b * kVBlock;
-            float dv = f16_bits_to_float((uint32_t)vb[0] | ((uint32_t)vb[1] << 8));
-            for (int j = 0; j < 16; ++j) {
-                uint32_t byte = vb[2 + j];
-                vo[b * kQK + j] = dv * (float)((int)(byte & 15) - 8);
-                vo[b * kQK + j + 16] = dv * (float)((int)(byte >> 4) - 8);
+            // blocks start on 2-byte boundaries: read 16-bit halves
+            const uint16_t* kb = (const uint16_t*)(kr + b * kKBlock);
+            const float dk = scale_f32(kb[0]);
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t x0 = kb[1 + 4 * j] | ((uint32_t)kb[2 + 4 * j] << 16);
+                const uint32_t x1 = kb[3 + 4 * j] | ((uint32_t)kb[4 + 4 * j] << 16);
+                const half8_t c = q8_codes_f16(x0, x1);
+                for (int e = 0; e < 8; ++e) ko[b * kQK + 8 * j + e] = (float)c[e] * dk;
+            }
+            const uint16_t* vb = (const uint16_t*)(vr + b * kVBlock);
+            const float dv = scale_f32(vb[0]);
+            for (int j = 0; j < 8; ++j) {
+                // bytes 2 j and 2 j + 1: elements 2 j, 2 j + 1 (low nibbles) and
+                // 2 j + 16, 2 j + 17 (high nibbles)
+                const uint32_t w2 = vb[1 + j];
+                const uint32_t x = (w2 & 0xFFu) | ((w2 >> 8) << 16);
+                const half2_t lo = q4_nibbles_f16((x & 0x000F000Fu) | 0x64006400u, one, m1032);
+                const half2_t hi = q4_nibbles_f16(((x >> 4) & 0x000F000Fu) | 0x64006400u, one, m1032);
+                vo[b * kQK + 2 * j] = (float)lo[0] * dv;
+                vo[b * kQK + 2 * j + 1] = (float)lo[1] * dv;
+                vo[b * kQK + 2 * j + 16] = (float)hi[0] * dv;
+                vo[b * kQK + 2 * j + 17] = (float)hi[1] * dv;
             }
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Record export probe: the raw bytes of each page of the launch's segments,
+// read from where the attention kernels read them (a resident slot, the ring
+// chunk of this launch, or the pinned host record), copied to dst[page].
+// One workgroup per (segment, 16 KB part of a page).
+// ---------------------------------------------------------------------------
+constexpr int kExportPart = 16384;
+__global__ __launch_bounds__(256) void export_kernel(ExportArgs a) {
+    if ((int)blockIdx.x >= a.n_segs) {   // ring refill workgroup
+        copy_role(a.copy, ((int)blockIdx.x - a.n_segs) * (int)gridDim.y + (int)blockIdx.y);
+        return;
+    }
+    const Seg seg = a.segs[blockIdx.x];
+    const int64_t off = (int64_t)blockIdx.y * kExportPart;
+    if (off >= a.ps.page_bytes) return;
+    const int64_t n = a.ps.page_bytes - off < kExportPart ? a.ps.page_bytes - off : kExportPart;
+    for (int pi = 0; pi < seg.npages; ++pi) {
+        const int page = seg.page0 + pi;
+        const uint4* src = (const uint4*)(page_ptr(a.ps, page) + off);
+        uint4* dst = (uint4*)(a.dst + (int64_t)page * a.ps.page_bytes + off);
+        for (int e = threadIdx.x; e < n / 16; e += 256) dst[e] = src[e];
     }
 }
 
@@ -176,6 +214,14 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t stream) {
     if (a.n_segs <= 0 && copy_workgroups(a.copy) == 0) return hipSuccess;
     const int cx = (copy_workgroups(a.copy) + a.n_kv_heads - 1) / a.n_kv_heads;
     hipLaunchKernelGGL(gather_kernel, dim3(a.n_segs + cx, a.n_kv_heads), dim3(kPageTokens), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_export(const ExportArgs& a, hipStream_t stream) {
+    const int parts = (int)((a.ps.page_bytes + kExportPart - 1) / kExportPart);
+    const int cx = (copy_workgroups(a.copy) + parts - 1) / parts;
+    if (a.n_segs <= 0 && cx == 0) return hipSuccess;
+    hipLaunchKernelGGL(export_kernel, dim3(a.n_segs + cx, parts), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -5,9 +5,13 @@
 // The design follows the pages' statement of the problem: authoritative KV in
 // pinned host memory, a bounded device region holding resident 256-token pages
 // and one ring shared by all layers, with flash-attention consuming both
-// (page 1, "Summary"; page 2, opening paragraph). The ring is driven from the
-// host with hipMemcpyAsync on several copy streams; HIP events order each
-// chunk's copy before its kernel and the kernel before the slot's next copy.
+// (page 1, "Summary"; page 2, opening paragraph). The ring is filled by copy
+// workgroups that ride inside the compute launches (or, for a prefetch, a
+// copy-only launch on the pool's prefetch stream): each launch computes on
+// the ring chunk the launch before it filled while its own copy workgroups
+// pull a later chunk over the host link, so kernel boundaries on a stream
+// order each copy before its reader and each reader before the slot's refill;
+// HIP events order the pool's streams against each other.
 #include "kvs.h"
 #include "kvs_internal.h"
 
@@ -84,7 +88,6 @@ int validate(const kvs_config* c) {
     if (c->chunk_pages < 1 || c->chunk_pages > kvs::kMaxCopyPages || c->ring_pages % c->chunk_pages)
         return fail(KVS_ERR_INVALID_ARG, "chunk_pages %d must be in [1, %d] and divide ring_pages %d", c->chunk_pages,
                     kvs::kMaxCopyPages, c->ring_pages);
-    if (c->copy_streams < 1 || c->copy_streams > 8) return fail(KVS_ERR_INVALID_ARG, "copy_streams %d out of range [1, 8]", c->copy_streams);
     if (c->group_pages < 1) return fail(KVS_ERR_INVALID_ARG, "group_pages %d must be >= 1", c->group_pages);
     if (c->flags & ~uint32_t(KVS_FLAG_POISON_RING | KVS_FLAG_ZERO_COPY))
         return fail(KVS_ERR_INVALID_ARG, "unknown flag bits 0x%x", c->flags);
@@ -122,6 +125,9 @@ struct ChunkPlan {
 struct LayerState {
     const uint8_t* host = nullptr;
     int32_t host_pages = 0;
+    bool host_new = true;            // records (re)registered since the last upload: upload every resident page
+    int32_t pin_slots = 0;           // slots of the pinned region this layer owns (0: it takes general slots)
+    std::vector<int32_t> pin_free;   // free slots of that region
     int32_t n_pages = -1;            // -1: page table not set
     std::vector<int32_t> src;        // per page: slot or -1 - rank
     std::vector<int32_t> slots_held;
@@ -150,12 +156,14 @@ struct kvs_pool {
     int64_t n_slots = 0;
     std::vector<int32_t> slot_free;  // stack of free slot ids
     std::vector<LayerState> layers;
-    std::vector<hipStream_t> copy;   // stream prefetches (kvs_stream_enqueue) run on copy[0]
+    hipStream_t pf_stream = nullptr; // prefetches (kvs_stream_enqueue) run here
+    int64_t pin_top = 0;             // slots at the top of the slot range held by pinned regions
     int32_t n_cslots = 0;            // chunk slots in the ring
-    hipEvent_t pf_done = nullptr;    // recorded on copy[0] after a prefetch
+    hipEvent_t pf_done = nullptr;    // recorded on pf_stream after a prefetch
     hipEvent_t ring_free = nullptr;  // recorded on the compute stream after a layer's last ring read
     bool ring_used = false;          // ring_free has been recorded at least once
-    hipEvent_t last_work = nullptr;  // recorded after every attend / gather
+    hipEvent_t last_work = nullptr;  // recorded after every attend and probe
+    bool worked = false;             // last_work has been recorded at least once
     hipEvent_t append_ev = nullptr;  // recorded after every kvs_append
     bool appended = false;           // append_ev has been recorded at least once
     // Compute lanes, used when a layer runs on more than one (otherwise its
@@ -353,7 +361,7 @@ bool stream_capturing(hipStream_t s) {
 
 int prefetch(kvs_pool* p, int32_t layer) {
     const LayerState& ls = p->layers[layer];
-    hipStream_t cs = p->copy[0];
+    hipStream_t cs = p->pf_stream;
     if (p->ring_used) KVS_HIP(hipStreamWaitEvent(cs, p->ring_free, 0));
     if (p->appended) KVS_HIP(hipStreamWaitEvent(cs, p->append_ev, 0));   // host records it copies
     kvs::CopyJob cj = make_copy(p, ls, 0, p->ring_next);
@@ -564,6 +572,36 @@ int check_capture(const kvs_pool* p, int32_t layer, hipStream_t s) {
     return KVS_OK;
 }
 
+// Work of this pool issued on another stream (an earlier attend's combine
+// still reading the split-K workspace, a probe, a staging region in use) must
+// be done before a new call's launches reuse that memory: the call's stream
+// waits for the pool's last recorded work. Under graph capture an outside
+// event cannot be waited on; a captured sequence runs on the capture stream,
+// which orders it.
+int order_after_last_work(kvs_pool* p, hipStream_t s) {
+    if (!p->worked || stream_capturing(s)) return KVS_OK;
+    if (hipStreamWaitEvent(s, p->last_work, 0) != hipSuccess) {
+        p->broken = true;
+        return fail(KVS_ERR_HIP, "hipStreamWaitEvent(last work) failed");
+    }
+    return KVS_OK;
+}
+
+int record_last_work(kvs_pool* p, hipStream_t s) {
+    if (hipEventRecord(p->last_work, s) != hipSuccess) {
+        p->broken = true;
+        return fail(KVS_ERR_HIP, "hipEventRecord failed");
+    }
+    p->worked = true;
+    return KVS_OK;
+}
+
+int64_t pinned_free_count(const kvs_pool* p) {
+    int64_t n = 0;
+    for (const auto& ls : p->layers) n += (int64_t)ls.pin_free.size();
+    return n;
+}
+
 int check_ring_free_for(const kvs_pool* p, int32_t layer) {
     const LayerState& ls = p->layers[layer];
     if (!ls.chunks.empty() && p->pf_layer >= 0 && p->pf_layer != layer)
@@ -726,7 +764,7 @@ int kvs_pool_create(const kvs_config* cfg, void* dev_arena, uint64_t budget_byte
     for (int64_t s = p->n_slots - 1; s >= 0; --s) p->slot_free.push_back((int32_t)s);
     p->n_cslots = cfg->ring_pages / cfg->chunk_pages;
     auto cleanup = [&](const char* what, hipError_t e) {
-        for (auto s : p->copy) (void)hipStreamDestroy(s);
+        if (p->pf_stream) (void)hipStreamDestroy(p->pf_stream);
         for (auto s : p->lanes) if (s) (void)hipStreamDestroy(s);
         for (hipEvent_t ev : {p->pf_done, p->ring_free, p->last_work, p->fork_ev, p->append_ev}) if (ev) (void)hipEventDestroy(ev);
         for (hipEvent_t ev : p->join_ev) if (ev) (void)hipEventDestroy(ev);
@@ -737,11 +775,9 @@ int kvs_pool_create(const kvs_config* cfg, void* dev_arena, uint64_t budget_byte
         hipError_t e = hipStreamCreateWithFlags(&p->lanes[k], hipStreamNonBlocking);
         if (e != hipSuccess) return cleanup("hipStreamCreateWithFlags", e);
     }
-    for (int i = 0; i < cfg->copy_streams; ++i) {
-        hipStream_t s;
-        hipError_t e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+    {
+        hipError_t e = hipStreamCreateWithFlags(&p->pf_stream, hipStreamNonBlocking);
         if (e != hipSuccess) return cleanup("hipStreamCreateWithFlags", e);
-        p->copy.push_back(s);
     }
     for (hipEvent_t* ev : {&p->pf_done, &p->ring_free, &p->last_work, &p->fork_ev, &p->append_ev}) {
         hipError_t e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
@@ -765,11 +801,11 @@ int kvs_pool_create(const kvs_config* cfg, void* dev_arena, uint64_t budget_byte
 
 void kvs_pool_destroy(kvs_pool* p) {
     if (!p) return;
-    for (auto s : p->copy) (void)hipStreamSynchronize(s);
+    if (p->pf_stream) (void)hipStreamSynchronize(p->pf_stream);
     if (p->last_work) (void)hipEventSynchronize(p->last_work);
     if (p->appended) (void)hipEventSynchronize(p->append_ev);
     for (auto s : p->lanes) if (s) (void)hipStreamSynchronize(s);
-    for (auto s : p->copy) (void)hipStreamDestroy(s);
+    if (p->pf_stream) (void)hipStreamDestroy(p->pf_stream);
     for (auto s : p->lanes) if (s) (void)hipStreamDestroy(s);
     for (hipEvent_t ev : {p->pf_done, p->ring_free, p->last_work, p->fork_ev, p->append_ev}) if (ev) (void)hipEventDestroy(ev);
     for (hipEvent_t ev : p->join_ev) if (ev) (void)hipEventDestroy(ev);
@@ -788,8 +824,11 @@ int kvs_host_pages_set(kvs_pool* p, int32_t layer, const void* pinned_records, i
         (void)hipGetLastError();
         return fail(KVS_ERR_UNSUPPORTED, "host records of layer %d are not pinned host memory", layer);
     }
-    p->layers[layer].host = (const uint8_t*)pinned_records;
-    p->layers[layer].host_pages = n_pages;
+    LayerState& ls = p->layers[layer];
+    if (ls.n_pages > n_pages) return fail(KVS_ERR_INVALID_ARG, "layer %d's page table holds %d pages, more than %d host pages", layer, ls.n_pages, n_pages);
+    ls.host = (const uint8_t*)pinned_records;
+    ls.host_pages = n_pages;
+    ls.host_new = true;   // resident slots no longer mirror the records: upload them all on the next table set
     return KVS_OK;
 }
 
@@ -804,48 +843,144 @@ int kvs_page_table_set(kvs_pool* p, int32_t layer, int32_t n_pages, const uint8_
         return fail(KVS_ERR_INVALID_ARG, "n_pages %d out of range [0, min(max_pages %d, host pages %d)]", n_pages, p->cfg.max_pages, ls.host_pages);
     if (n_pages > 0 && !resident) return fail(KVS_ERR_INVALID_ARG, "resident mask is NULL");
     if (p->pf_layer == layer) return fail(KVS_ERR_STATE, "layer %d has an unconsumed prefetch", layer);
-    int64_t need = 0;
-    for (int32_t i = 0; i < n_pages; ++i) need += resident[i] ? 1 : 0;
-    const int64_t avail = (int64_t)p->slot_free.size() + (int64_t)ls.slots_held.size();
-    if (need > avail)
-        return fail(KVS_ERR_NO_SLOTS, "layer %d wants %lld resident pages but only %lld slots are free", layer, (long long)need, (long long)avail);
+    // Pages that stay resident keep their slots (and their device copy, which
+    // kvs_append keeps in step with the host record); only newly resident
+    // pages are uploaded, unless the host records were registered again.
+    const bool keep_ok = ls.n_pages >= 0 && !ls.host_new;
+    std::vector<int32_t> keep(n_pages, -1);
+    int64_t need = 0, kept = 0;
+    for (int32_t i = 0; i < n_pages; ++i) {
+        if (!resident[i]) continue;
+        ++need;
+        if (keep_ok && i < ls.n_pages && ls.src[i] >= 0) { keep[i] = ls.src[i]; ++kept; }
+    }
+    // slots this call can hand out: the layer's slots that are not kept, then
+    // free ones (of the layer's pinned region for a pinned layer)
+    std::vector<char> kept_slot;
+    std::vector<int32_t> reuse;
+    {
+        std::vector<int32_t> kept_ids;
+        for (int32_t i = 0; i < n_pages; ++i) if (keep[i] >= 0) kept_ids.push_back(keep[i]);
+        std::sort(kept_ids.begin(), kept_ids.end());
+        for (int32_t sl : ls.slots_held)
+            if (!std::binary_search(kept_ids.begin(), kept_ids.end(), sl)) reuse.push_back(sl);
+    }
+    const std::vector<int32_t>& free_list = ls.pin_slots ? ls.pin_free : p->slot_free;
+    const int64_t avail = (int64_t)reuse.size() + (int64_t)free_list.size();
+    if (need - kept > avail)
+        return fail(KVS_ERR_NO_SLOTS, "layer %d wants %lld resident pages but only %lld slots are free%s", layer, (long long)need,
+                    (long long)(kept + avail), ls.pin_slots ? " in its pinned region" : "");
     LayerState trial;
     trial.host = ls.host;
     trial.host_pages = ls.host_pages;
+    trial.host_new = false;
+    trial.pin_slots = ls.pin_slots;
     trial.dev_src = ls.dev_src;
     trial.dev_segs = ls.dev_segs;
     rc = build_plan(p->cfg, p->L.max_segs, trial, n_pages, resident);
     if (rc) return rc;
-    // commit: release old slots, take new ones
-    for (int32_t s : ls.slots_held) p->slot_free.push_back(s);
-    for (int32_t i = 0; i < n_pages; ++i)
-        if (resident[i]) {
-            int32_t s = p->slot_free.back();
-            p->slot_free.pop_back();
-            trial.src[i] = s;
-            trial.slots_held.push_back(s);
+    // assign slots (no pool state changes yet): kept ones, then the layer's
+    // released ones, then free ones from the top of the free stack
+    std::vector<int32_t> free_after(free_list);
+    std::vector<std::pair<int32_t, int32_t>> uploads;   // (page, slot)
+    size_t ri = 0;
+    for (int32_t i = 0; i < n_pages; ++i) {
+        if (!resident[i]) continue;
+        int32_t sl = keep[i];
+        if (sl < 0) {
+            if (ri < reuse.size()) sl = reuse[ri++];
+            else { sl = free_after.back(); free_after.pop_back(); }
+            uploads.push_back({i, sl});
         }
-    ls = std::move(trial);
-    p->st.slots_used = p->n_slots - (int64_t)p->slot_free.size();
+        trial.src[i] = sl;
+        trial.slots_held.push_back(sl);
+    }
+    for (; ri < reuse.size(); ++ri) free_after.push_back(reuse[ri]);
+    // device work: the uploads go to slots nothing else reads once the pool's
+    // earlier work is done. A HIP failure from here on leaves the device
+    // tables in an unknown state, so it marks the pool unusable.
     hipStream_t s = (hipStream_t)stream;
-    KVS_HIP(hipStreamWaitEvent(s, p->last_work, 0));
-    if (p->appended) KVS_HIP(hipStreamWaitEvent(s, p->append_ev, 0));
-    for (int32_t i = 0; i < n_pages; ++i)
-        if (ls.src[i] >= 0) {
-            KVS_HIP(hipMemcpyAsync(p->slots + (uint64_t)ls.src[i] * p->L.page_bytes, ls.host + (uint64_t)i * p->L.page_bytes,
-                                   p->L.page_bytes, hipMemcpyHostToDevice, s));
-            p->st.resident_upload_bytes += (int64_t)p->L.page_bytes;
-        }
-    if (n_pages > 0) KVS_HIP(hipMemcpyAsync(ls.dev_src, ls.src.data(), n_pages * sizeof(int32_t), hipMemcpyHostToDevice, s));
+    auto hip_fail = [&](const char* what, hipError_t e) {
+        p->broken = true;
+        return fail(KVS_ERR_HIP, "%s failed: %s (the pool is unusable)", what, hipGetErrorString(e));
+    };
+    hipError_t e = hipSuccess;
+    if (p->worked && (e = hipStreamWaitEvent(s, p->last_work, 0)) != hipSuccess) return hip_fail("hipStreamWaitEvent", e);
+    if (p->appended && (e = hipStreamWaitEvent(s, p->append_ev, 0)) != hipSuccess) return hip_fail("hipStreamWaitEvent", e);
+    int64_t uploaded = 0;
+    for (const auto& u : uploads) {
+        e = hipMemcpyAsync(p->slots + (uint64_t)u.second * p->L.page_bytes, ls.host + (uint64_t)u.first * p->L.page_bytes,
+                           p->L.page_bytes, hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return hip_fail("hipMemcpyAsync(resident page)", e);
+        uploaded += (int64_t)p->L.page_bytes;
+    }
+    if (n_pages > 0 && (e = hipMemcpyAsync(trial.dev_src, trial.src.data(), n_pages * sizeof(int32_t), hipMemcpyHostToDevice, s)) != hipSuccess)
+        return hip_fail("hipMemcpyAsync(page table)", e);
     // device copy of the segments: flags bits 8.. carry src[page0] (slot
     // indices below kMaxSlots, streamed ranks below max_pages <= 2^22)
-    std::vector<kvs::Seg> dsegs(ls.segs);
+    std::vector<kvs::Seg> dsegs(trial.segs);
     for (kvs::Seg& sg : dsegs)
-        sg.flags = (sg.flags & kvs::kSegFlagMask) | (int32_t)((uint32_t)ls.src[sg.page0] << kvs::kSegSrcShift);
-    if (!dsegs.empty())
-        KVS_HIP(hipMemcpyAsync(ls.dev_segs, dsegs.data(), dsegs.size() * sizeof(kvs::Seg), hipMemcpyHostToDevice, s));
-    KVS_HIP(hipStreamSynchronize(s));
-    ls.n_pages = n_pages;
+        sg.flags = (sg.flags & kvs::kSegFlagMask) | (int32_t)((uint32_t)trial.src[sg.page0] << kvs::kSegSrcShift);
+    if (!dsegs.empty() &&
+        (e = hipMemcpyAsync(trial.dev_segs, dsegs.data(), dsegs.size() * sizeof(kvs::Seg), hipMemcpyHostToDevice, s)) != hipSuccess)
+        return hip_fail("hipMemcpyAsync(segments)", e);
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_fail("hipStreamSynchronize", e);
+    // commit
+    if (ls.pin_slots) trial.pin_free = std::move(free_after);
+    else p->slot_free = std::move(free_after);
+    trial.n_pages = n_pages;
+    ls = std::move(trial);
+    p->st.resident_upload_bytes += uploaded;
+    p->st.slots_used = p->n_slots - (int64_t)p->slot_free.size() - pinned_free_count(p);
+    return KVS_OK;
+}
+
+int kvs_pool_pin_layer(kvs_pool* p, int32_t layer, int32_t n_slots) {
+    if (!p) return fail(KVS_ERR_INVALID_ARG, "pool is NULL");
+    int rc = check_device(p);
+    if (rc) return rc;
+    if (layer < 0 || layer >= p->cfg.n_layers) return fail(KVS_ERR_INVALID_ARG, "layer %d out of range [0, %d)", layer, p->cfg.n_layers);
+    if (n_slots < 1) return fail(KVS_ERR_INVALID_ARG, "n_slots %d < 1", n_slots);
+    LayerState& ls = p->layers[layer];
+    if (ls.pin_slots) return fail(KVS_ERR_STATE, "layer %d already has a pinned region", layer);
+    if (!ls.slots_held.empty()) return fail(KVS_ERR_STATE, "layer %d holds resident slots; set an empty page table before pinning it", layer);
+    if (p->pin_top + n_slots > p->n_slots)
+        return fail(KVS_ERR_NO_SLOTS, "a pinned region of %d slots does not fit: %lld of %lld slots are pinned already", n_slots,
+                    (long long)p->pin_top, (long long)p->n_slots);
+    // bump allocation from the top: slots [top - n_slots, top) must be free
+    const int64_t hi = p->n_slots - p->pin_top, lo = hi - n_slots;
+    std::vector<char> is_free(p->n_slots, 0);
+    for (int32_t sl : p->slot_free) is_free[sl] = 1;
+    for (int64_t sl = lo; sl < hi; ++sl)
+        if (!is_free[sl])
+            return fail(KVS_ERR_NO_SLOTS, "slot %lld at the top of the pool is held by a resident page; release it before pinning %d slots",
+                        (long long)sl, n_slots);
+    std::vector<int32_t> rest;
+    for (int32_t sl : p->slot_free) if (sl < lo || sl >= hi) rest.push_back(sl);
+    p->slot_free = std::move(rest);
+    ls.pin_free.clear();
+    for (int64_t sl = hi - 1; sl >= lo; --sl) ls.pin_free.push_back((int32_t)sl);   // lowest handed out first
+    ls.pin_slots = n_slots;
+    p->pin_top += n_slots;
+    p->st.pinned_slots = p->pin_top;
+    return KVS_OK;
+}
+
+int kvs_pool_reset_pinned(kvs_pool* p) {
+    if (!p) return fail(KVS_ERR_INVALID_ARG, "pool is NULL");
+    int rc = check_device(p);
+    if (rc) return rc;
+    for (int32_t l = 0; l < p->cfg.n_layers; ++l)
+        if (p->layers[l].pin_slots && !p->layers[l].slots_held.empty())
+            return fail(KVS_ERR_STATE, "pinned layer %d still holds resident pages; set an empty page table first", l);
+    for (auto& ls : p->layers) {
+        if (!ls.pin_slots) continue;
+        for (int32_t sl : ls.pin_free) p->slot_free.push_back(sl);
+        ls.pin_free.clear();
+        ls.pin_slots = 0;
+    }
+    p->pin_top = 0;
+    p->st.pinned_slots = 0;
     return KVS_OK;
 }
 
@@ -881,6 +1016,7 @@ int kvs_attend(kvs_pool* p, int32_t layer, const void* q, int32_t q_dtype, int32
     if ((rc = check_ring_free_for(p, layer))) return rc;
     hipStream_t s = (hipStream_t)stream;
     if ((rc = check_capture(p, layer, s))) return rc;
+    if ((rc = order_after_last_work(p, s))) return rc;
 
     kvs::AttendArgs a{};
     a.ps.slots = p->slots;
@@ -950,8 +1086,7 @@ int kvs_attend(kvs_pool* p, int32_t layer, const void* q, int32_t q_dtype, int32
     hipError_t e = timed(p, 1, s, [&] { return kvs::launch_combine(p->work, ls.n_groups, n_q, p->cfg.n_q_heads, out, lse, s); });
     if (e != hipSuccess) { p->broken = true; return fail(KVS_ERR_HIP, "combine launch failed: %s", hipGetErrorString(e)); }
     p->st.kernels_launched++;
-    if (hipEventRecord(p->last_work, s) != hipSuccess) { p->broken = true; return fail(KVS_ERR_HIP, "hipEventRecord failed"); }
-    return KVS_OK;
+    return record_last_work(p, s);
 }
 
 int kvs_status(const kvs_pool* p, kvs_status_info* info) {
@@ -972,6 +1107,7 @@ int kvs_debug_gather(kvs_pool* p, int32_t layer, int64_t tok0, int64_t n_tok, fl
     if ((rc = check_ring_free_for(p, layer))) return rc;
     hipStream_t s = (hipStream_t)stream;
     if ((rc = check_capture(p, layer, s))) return rc;
+    if ((rc = order_after_last_work(p, s))) return rc;
     kvs::GatherArgs a{};
     a.ps.slots = p->slots;
     a.ps.src = ls.dev_src;
@@ -994,8 +1130,80 @@ int kvs_debug_gather(kvs_pool* p, int32_t layer, int64_t tok0, int64_t n_tok, fl
         return e == hipSuccess ? KVS_OK : fail(KVS_ERR_HIP, "gather kernel launch failed: %s", hipGetErrorString(e));
     });
     if (rc) return rc;
-    if (hipEventRecord(p->last_work, s) != hipSuccess) { p->broken = true; return fail(KVS_ERR_HIP, "hipEventRecord failed"); }
-    return KVS_OK;
+    return record_last_work(p, s);
+}
+
+int kvs_debug_stage(kvs_pool* p, int32_t layer, int64_t n_kv, void* dst, void* stream) {
+    if (!p) return fail(KVS_ERR_INVALID_ARG, "pool is NULL");
+    int rc = check_device(p);
+    if (rc) return rc;
+    if ((rc = check_layer_ready(p, layer))) return rc;
+    const LayerState& ls = p->layers[layer];
+    if (n_kv < 0 || (n_kv + kvs::kPageTokens - 1) / kvs::kPageTokens != ls.n_pages)
+        return fail(KVS_ERR_INVALID_ARG, "n_kv %lld does not fill the layer's %d pages", (long long)n_kv, ls.n_pages);
+    if (ls.n_pages > 0 && !dst) return fail(KVS_ERR_INVALID_ARG, "dst is NULL");
+    if ((uintptr_t)dst & 255) return fail(KVS_ERR_INVALID_ARG, "dst must be 256-byte aligned");
+    if ((rc = check_ring_free_for(p, layer))) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    if ((rc = check_capture(p, layer, s))) return rc;
+    if ((rc = order_after_last_work(p, s))) return rc;
+    kvs::StageArgs a{};
+    a.ps.slots = p->slots;
+    a.ps.src = ls.dev_src;
+    a.ps.host = (p->cfg.flags & KVS_FLAG_ZERO_COPY) ? ls.host : nullptr;
+    a.ps.page_bytes = (int64_t)p->L.page_bytes;
+    a.n_kv_heads = p->cfg.n_kv_heads;
+    a.n_kv = n_kv;
+    a.staged = (uint8_t*)dst;
+    a.by_page = 1;
+    rc = run_layer(p, layer, s, 0, [&](hipStream_t st, int /*lane*/, int32_t seg0, int32_t nseg, const uint8_t* ring_chunk,
+                                    int32_t rank0, const kvs::CopyJob& cj) -> int {
+        kvs::StageArgs b = a;
+        b.copy = cj;
+        b.ps.ring_chunk = ring_chunk;
+        b.ps.chunk_rank0 = rank0;
+        b.segs = ls.dev_segs + seg0;
+        b.n_segs = nseg;
+        b.n_pages = 0;
+        for (int32_t i = seg0; i < seg0 + nseg; ++i) b.n_pages += ls.segs[i].npages;
+        hipError_t e = kvs::launch_stage(b, st);
+        return e == hipSuccess ? KVS_OK : fail(KVS_ERR_HIP, "staging kernel launch failed: %s", hipGetErrorString(e));
+    });
+    if (rc) return rc;
+    return record_last_work(p, s);
+}
+
+int kvs_debug_export_pages(kvs_pool* p, int32_t layer, void* dst, void* stream) {
+    if (!p) return fail(KVS_ERR_INVALID_ARG, "pool is NULL");
+    int rc = check_device(p);
+    if (rc) return rc;
+    if ((rc = check_layer_ready(p, layer))) return rc;
+    const LayerState& ls = p->layers[layer];
+    if (ls.n_pages > 0 && !dst) return fail(KVS_ERR_INVALID_ARG, "dst is NULL");
+    if ((uintptr_t)dst & 15) return fail(KVS_ERR_INVALID_ARG, "dst must be 16-byte aligned");
+    if ((rc = check_ring_free_for(p, layer))) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    if ((rc = check_capture(p, layer, s))) return rc;
+    if ((rc = order_after_last_work(p, s))) return rc;
+    kvs::ExportArgs a{};
+    a.ps.slots = p->slots;
+    a.ps.src = ls.dev_src;
+    a.ps.host = (p->cfg.flags & KVS_FLAG_ZERO_COPY) ? ls.host : nullptr;
+    a.ps.page_bytes = (int64_t)p->L.page_bytes;
+    a.dst = (uint8_t*)dst;
+    rc = run_layer(p, layer, s, 0, [&](hipStream_t st, int /*lane*/, int32_t seg0, int32_t nseg, const uint8_t* ring_chunk,
+                                    int32_t rank0, const kvs::CopyJob& cj) -> int {
+        kvs::ExportArgs b = a;
+        b.copy = cj;
+        b.ps.ring_chunk = ring_chunk;
+        b.ps.chunk_rank0 = rank0;
+        b.segs = ls.dev_segs + seg0;
+        b.n_segs = nseg;
+        hipError_t e = kvs::launch_export(b, st);
+        return e == hipSuccess ? KVS_OK : fail(KVS_ERR_HIP, "export kernel launch failed: %s", hipGetErrorString(e));
+    });
+    if (rc) return rc;
+    return record_last_work(p, s);
 }
 
 int kvs_append(kvs_pool* p, int32_t layer, const void* k_new, const void* v_new, int32_t dtype, int64_t pos0,
@@ -1018,6 +1226,8 @@ int kvs_append(kvs_pool* p, int32_t layer, const void* k_new, const void* v_new,
                 return fail(KVS_ERR_STATE, "layer %d has a pending prefetch that may read streamed page %lld; append before kvs_stream_enqueue",
                             layer, (long long)pg);
     }
+    hipStream_t s = (hipStream_t)stream;
+    if ((rc = order_after_last_work(p, s))) return rc;   // no reader of the rows is still in flight
     kvs::AppendArgs a{};
     a.k = k_new;
     a.v = v_new;
@@ -1029,7 +1239,6 @@ int kvs_append(kvs_pool* p, int32_t layer, const void* k_new, const void* v_new,
     a.src = ls.dev_src;
     a.slots = p->slots;
     a.host = const_cast<uint8_t*>(ls.host);
-    hipStream_t s = (hipStream_t)stream;
     hipError_t e = kvs::launch_append(a, s);
     if (e != hipSuccess) return fail(KVS_ERR_HIP, "append kernel launch failed: %s", hipGetErrorString(e));
     p->st.kernels_launched++;
@@ -1047,7 +1256,7 @@ int kvs_debug_read_page(kvs_pool* p, int32_t layer, int32_t page, void* dst_host
     if (page < 0 || page >= ls.n_pages) return fail(KVS_ERR_INVALID_ARG, "page %d out of range [0, %d)", page, ls.n_pages);
     if (!dst_host) return fail(KVS_ERR_INVALID_ARG, "dst_host is NULL");
     if (ls.src[page] < 0) return fail(KVS_ERR_NOT_RESIDENT, "page %d of layer %d is streamed, not resident", page, layer);
-    KVS_HIP(hipEventSynchronize(p->last_work));
+    if (p->worked) KVS_HIP(hipEventSynchronize(p->last_work));
     KVS_HIP(hipMemcpy(dst_host, p->slots + (uint64_t)ls.src[page] * p->L.page_bytes, p->L.page_bytes, hipMemcpyDeviceToHost));
     return KVS_OK;
 }

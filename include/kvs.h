@@ -27,8 +27,16 @@
  *     process addresses; streams are hipStream_t handles passed as void*.
  *   - The caller owns every buffer it passes: the device arena, the pinned host
  *     page records, q, out, lse and the compute streams. The library owns only
- *     its metadata, its HIP events and its copy streams (created at the default
- *     priority), and never frees caller memory.
+ *     its metadata, its HIP events and its own streams (a prefetch stream and
+ *     three compute lanes, created at the default priority), and never frees
+ *     caller memory.
+ *   - Calls on one pool may use different streams: each call that launches
+ *     work first makes its stream wait for the pool's previous work (the
+ *     split-K workspace, staging regions and ring are shared by every layer).
+ *     Inside a HIP graph capture that wait is skipped, so a captured sequence
+ *     must issue all of its calls on the capture stream.
+ *   - A HIP runtime failure after a call has started device work marks the
+ *     pool unusable: that call and every later one return KVS_ERR_HIP.
  *   - A pool is bound to the HIP device that is current when it is created;
  *     later calls must be made with that device current.
  *
@@ -108,7 +116,6 @@ typedef struct kvs_config {
                               chunk holds whole split-K groups when group_pages <=
                               chunk_pages (so it may carry fewer pages); only then can
                               two chunk launches run concurrently                      */
-    int32_t copy_streams;  /* streams the pool creates for kvs_stream_enqueue (1..8)       */
     int32_t group_pages;   /* pages per split-K partial (>= 1). Partials are keyed by this
                               logical grouping only, so results do not depend on which
                               pages are resident, nor on ring or chunk sizes.              */
@@ -123,9 +130,11 @@ typedef struct kvs_status_info {
     int64_t workspace_bytes;     /* split-K partial workspace carved from the arena  */
     int64_t bytes_h2d;           /* bytes copied host->device through the ring       */
     int64_t pages_streamed;      /* pages copied through the ring                    */
-    int64_t copies_issued;       /* hipMemcpyAsync calls issued for the ring         */
+    int64_t copies_issued;       /* ring chunk refills issued (each carried by a launch's
+                                    copy workgroups, or a prefetch's copy-only launch) */
     int64_t kernels_launched;    /* kernel launches issued by kvs_attend/debug calls */
     int64_t resident_upload_bytes; /* bytes copied into resident slots              */
+    int64_t pinned_slots;        /* slots held by pinned regions (kvs_pool_pin_layer) */
 } kvs_status_info;
 
 typedef struct kvs_pool kvs_pool;
@@ -222,10 +231,15 @@ typedef struct kvs_plan_info {
 int kvs_plan_layer(const kvs_config* cfg, int32_t n_pages, const uint8_t* resident, kvs_plan_info* info,
                    int32_t* segs, int32_t seg_cap, int32_t* chunks, int32_t chunk_cap);
 
-/* Create a pool that carves [resident slots | ring | workspace | tables] out of
- * the caller's device arena of budget_bytes bytes (256-byte aligned). The
- * library never allocates device memory; the arena must outlive the pool.
- * Creates the copy streams and the ring events on the current device. */
+/* Create a pool that carves [ring | workspace | staging | tables | resident
+ * slots] out of the caller's device arena of budget_bytes bytes (256-byte
+ * aligned): one bounded device region holds the resident pages and the one
+ * transfer ring all layers share (page 1, "Summary"; page 2, opening
+ * paragraph), sized by a byte budget whose least useful value is one page
+ * (page 3, "Diagnostic log": minimum_stage_bytes). KVS_ERR_BUDGET below
+ * kvs_min_budget_bytes. The library never allocates device memory; the arena
+ * must outlive the pool. Creates the pool's streams and events on the current
+ * device. */
 int kvs_pool_create(const kvs_config* cfg, void* dev_arena, uint64_t budget_bytes,
                     kvs_pool** out_pool);
 
@@ -242,22 +256,39 @@ int kvs_host_pages_set(kvs_pool* pool, int32_t layer, const void* pinned_records
                        int32_t n_pages);
 
 /* Set which pages of a layer are resident (resident[p] = 1) for a layer of
- * n_pages pages (n_pages <= max_pages and <= the registered host pages).
- * Assigns slots, builds the layer's launch plan (resident groups, ring chunks,
- * copy runs), uploads the resident records and the plan on `stream`, and
- * waits for that stream. KVS_ERR_NO_SLOTS if the pool lacks free slots. */
+ * n_pages pages (n_pages <= max_pages and <= the registered host pages): the
+ * page table mapping each logical page to a device slot or to its host record
+ * (the pages' working set of resident pages; page 3's review notes its
+ * variant had no such table). Builds the layer's launch plan (resident
+ * groups, ring chunks, copy runs), uploads the plan and the records of newly
+ * resident pages on `stream` (after the pool's earlier work), and waits for
+ * that stream. Pages that stay resident keep their slot and its contents
+ * (kvs_append keeps slots and records in step); after kvs_host_pages_set
+ * registers the layer's records again, every resident page is uploaded.
+ * A growing layer calls this with its new page count, typically with
+ * kvs_residency_promote_newest's mask. A pinned layer (kvs_pool_pin_layer)
+ * takes slots from its own region only. KVS_ERR_NO_SLOTS if too few slots are
+ * free; every validation error leaves the pool unchanged. */
 int kvs_page_table_set(kvs_pool* pool, int32_t layer, int32_t n_pages,
                        const uint8_t* resident, void* stream);
 
-/* Start copying the first ring chunk of `layer` on the pool's copy stream
- * (after the previous ring reader finished), so it overlaps whatever the
- * caller runs before kvs_attend(layer). The ring serves one layer at a time,
+/* Start copying the first ring chunk of `layer` over the host link on the
+ * pool's prefetch stream (after the previous ring reader finished), so it
+ * overlaps whatever the caller runs before kvs_attend(layer): the pages
+ * overlap transfers of non-resident pages with compute (page 1, "Summary";
+ * page 2, opening paragraph). The ring serves one layer at a time,
  * in call order: KVS_ERR_STATE if another layer's prefetch has not been
  * consumed yet. A layer with no streamed pages is a no-op. Without a prefetch,
  * kvs_attend copies the first chunk itself. */
 int kvs_stream_enqueue(kvs_pool* pool, int32_t layer);
 
-/* Attention of n_q query tokens against the layer's cache of n_kv tokens.
+/* Attention of n_q query tokens against the layer's cache of n_kv tokens:
+ * flash-attention over the resident pages and, through the ring, the
+ * streamed ones (page 1, "Summary"), for a decode token, a speculative-verify
+ * block of 1 + draft tokens (page 2, "Phase arena: speculative verify
+ * batches") or a prefill ubatch (page 2, "TLDR - recommended setup"). The
+ * result is the plain softmax attention of the dequantized cache, whichever
+ * pages are resident (page 3, "KLD": streaming runs the same math).
  *   q:    device, [n_q, n_q_heads, head_dim], f32 or f16 (q_dtype), contiguous.
  *   out:  device, [n_q, n_q_heads, head_dim] f32; lse: device [n_q, n_q_heads]
  *         f32 natural-log sum-exp of the scaled scores, or NULL.
@@ -266,6 +297,24 @@ int kvs_stream_enqueue(kvs_pool* pool, int32_t layer);
  *   are required). n_kv must satisfy ceil(n_kv / 256) == the layer's n_pages.
  *   Scores are scale * q.k. A row without any allowed key gets out = 0 and
  *   lse = -inf.
+ * Supported inputs and accuracy (outputs within 2e-3 of float64 attention,
+ * normwise per row: max_c |o - r| / max_c |r|):
+ *   - K blocks: any finite binary16 scale (subnormals, zero, negative, up to
+ *     65504) and any codes (-128 included). Scores are float32 sums of exact
+ *     products: the codes enter the matrix cores exactly and each block's
+ *     scale multiplies its product in float32.
+ *   - q: finite f32 or f16. Decode-width blocks (n_q x Hq / Hkv <= 6) hold
+ *     each query row as 16-bit fixed point relative to its largest element;
+ *     wider blocks hold it exactly as f16 limbs (two for f32) after a
+ *     power-of-two scaling per row.
+ *   - V blocks: any finite binary16 scale and nibbles 0..15. Probabilities
+ *     and V values pass through f16 with one rounding each; a page whose
+ *     32-channel V block holds a scale magnitude above 8188 is taken divided
+ *     by 8. Within one page and one 32-channel block, V scale magnitudes
+ *     should lie within a factor of 2^14 of the block's largest: the
+ *     contribution of a token whose scale is smaller than that (relative to
+ *     the largest, in the same quarter page at decode width) carries an
+ *     absolute error up to 2^-24 of the largest scale.
  * Enqueues on `stream`: the resident-group launch, then one launch per ring
  * chunk, then the split-K combine. Each launch computes on the chunk that the
  * previous launch copied into the ring, while its own copy workgroups read the
@@ -306,6 +355,22 @@ int kvs_attend(kvs_pool* pool, int32_t layer, const void* q, int32_t q_dtype, in
 int kvs_append(kvs_pool* pool, int32_t layer, const void* k_new, const void* v_new, int32_t dtype,
                int64_t pos0, int32_t n_tok, void* stream);
 
+/* Pinned region (page 2, "New arena and context API": a pinned region
+ * bump-allocated from the top of the arena, the rest of the pool below it;
+ * page 1, "Summary": the draft head's KV is one more logical attention layer
+ * that borrows the same physical pool). kvs_pool_pin_layer reserves the
+ * n_slots highest free slots below any earlier pinned region for `layer`
+ * alone: its page table takes slots only from there (at most n_slots
+ * resident pages, e.g. a newest-page window from
+ * kvs_residency_promote_newest), and no other layer can take them. The
+ * layer must hold no resident slot (set an empty page table first), and the
+ * slots being reserved must be free: KVS_ERR_STATE or KVS_ERR_NO_SLOTS
+ * otherwise. kvs_pool_reset_pinned returns every pinned region to the pool
+ * (page 2's draft eject returns the draft's KV to the arena); each pinned
+ * layer must first hold no resident page (KVS_ERR_STATE). Host-only. */
+int kvs_pool_pin_layer(kvs_pool* pool, int32_t layer, int32_t n_slots);
+int kvs_pool_reset_pinned(kvs_pool* pool);
+
 /* Counters and sizes of the pool. */
 int kvs_status(const kvs_pool* pool, kvs_status_info* info);
 
@@ -319,6 +384,36 @@ int kvs_debug_gather(kvs_pool* pool, int32_t layer, int64_t tok0, int64_t n_tok,
 /* Copy the bytes of a resident page's device slot to dst_host (page_bytes).
  * Synchronous. KVS_ERR_NOT_RESIDENT for a streamed page. */
 int kvs_debug_read_page(kvs_pool* pool, int32_t layer, int32_t page, void* dst_host);
+
+/* Raw bytes of every page record of a layer as the attention kernels read
+ * them, copied to dst (device, n_pages x page_bytes, 16-byte aligned): a
+ * resident page from its slot, a streamed page from the ring chunk it was
+ * copied into during this call's pass over the layer (or in place from its
+ * pinned record in a zero-copy pool). Runs the layer's ring pipeline like
+ * kvs_attend; enqueued on `stream`. */
+int kvs_debug_export_pages(kvs_pool* pool, int32_t layer, void* dst, void* stream);
+
+/* The matrix-core operands of every page of a layer, converted by the same
+ * staging code the attention kernels use for query blocks wider than 64 rows
+ * per kv head, written to dst (device, 256-byte aligned) as n_pages x
+ * n_kv_heads tiles of KVS_STAGED_TILE_BYTES, tile (page, kv head) at
+ * (page x n_kv_heads + head) x KVS_STAGED_TILE_BYTES. n_kv is the layer's
+ * token count (rows at or past it are not cached). Streamed pages pass through
+ * the ring. Enqueued on `stream`. Tile layout (binary16 little-endian):
+ *   K operands, bytes [0, 65536): for token tile T = 0..15, block b = 0..3,
+ *     lane = 0..63: 8 values; lane (n, j) = (lane % 16, lane / 16) holds the
+ *     codes of token 16 T + n, elements 32 b + 8 j .. 32 b + 8 j + 7, exact.
+ *   V^T operands, bytes [65536, 131072): for chunk c = 0..7, channel tile
+ *     t = 0..7, lane = 0..63: 8 values; lane (n, j) holds channel
+ *     16 t + n (block t / 2, low nibbles for even t, high for odd t) of tokens
+ *     32 c + 4 j + s for slot s < 4 and 32 c + 12 + 4 j + s for s >= 4, each
+ *     d x (nibble - 8) / 2^shift rounded once to binary16 (0 for uncached
+ *     rows), shift = the block's V shift.
+ *   K scales, bytes [131072, 133120): token t's four block scales at 8 t.
+ *   V shifts, bytes [133120, 133136): int32 per block, 3 if a cached row's
+ *     scale magnitude exceeds 8188 (binary16 bits above 0x6FFF), else 0. */
+#define KVS_STAGED_TILE_BYTES 133376
+int kvs_debug_stage(kvs_pool* pool, int32_t layer, int64_t n_kv, void* dst, void* stream);
 
 /* Kernel timing. With enable != 0, kvs_attend brackets every attention kernel
  * launch (kind 0), every split-K combine launch (kind 1) and every staging

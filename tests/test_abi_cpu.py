@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 def base_cfg(**kw):
     c = dict(n_layers=16, n_kv_heads=4, n_q_heads=24, max_pages=1024, max_q_tokens=1, ring_pages=16,
-             chunk_pages=4, copy_streams=4, group_pages=1)
+             chunk_pages=4, group_pages=1)
     c.update(kw)
     return kvs.Config(**c)
 
@@ -56,8 +56,6 @@ def test_type_pair_gate():
     (dict(max_pages=0), kvs.ERR_INVALID_ARG),
     (dict(max_q_tokens=0), kvs.ERR_INVALID_ARG),
     (dict(ring_pages=16, chunk_pages=5), kvs.ERR_INVALID_ARG),
-    (dict(copy_streams=0), kvs.ERR_INVALID_ARG),
-    (dict(copy_streams=9), kvs.ERR_INVALID_ARG),
     (dict(group_pages=0), kvs.ERR_INVALID_ARG),
     (dict(flags=kvs.FLAG_ZERO_COPY), kvs.OK),
     (dict(flags=kvs.FLAG_ZERO_COPY | kvs.FLAG_POISON_RING), kvs.OK),

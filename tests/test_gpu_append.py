@@ -39,7 +39,7 @@ def new_rows(seed, n, dtype):
 def make_case(resident_fn, cid=57):
     say(f"append case cid={cid} n_kv={N_KV} residency={getattr(resident_fn, '__name__', 'fn')}")
     return Case(cid=cid, n_layers=2, n_kv_heads=H, n_q_heads=HQ, n_kv=N_KV,
-                cfg_kw=dict(max_q_tokens=4, ring_pages=4, chunk_pages=2, copy_streams=1, group_pages=1),
+                cfg_kw=dict(max_q_tokens=4, ring_pages=4, chunk_pages=2, group_pages=1),
                 resident_fn=resident_fn)
 
 
@@ -163,7 +163,7 @@ def test_append_on_another_stream_orders_before_a_multi_lane_attention():
         m[0] = 1
         return m
     c = Case(cid=60, n_layers=1, n_kv_heads=H, n_q_heads=HQ, n_kv=N_KV,
-             cfg_kw=dict(max_q_tokens=4, ring_pages=8, chunk_pages=2, copy_streams=1, group_pages=1),
+             cfg_kw=dict(max_q_tokens=4, ring_pages=8, chunk_pages=2, group_pages=1),
              resident_fn=mask)
     try:
         info, _, _ = kvs.plan_layer(c.cfg, c.masks[0])

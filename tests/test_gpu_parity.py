@@ -24,11 +24,11 @@ N_KV = 5 * 256 + 77          # 6 pages, ragged tail of 77 rows
 
 
 def small_case(resident_fn, *, cid=31, n_layers=3, n_kv=N_KV, Hkv=2, Hq=12, max_q=1, ring=4, chunk=2,
-               streams=2, group=1, flags=0, slots=None):
+               group=1, flags=0, slots=None):
     say(f"case cid={cid} layers={n_layers} n_kv={n_kv} Hkv={Hkv} Hq={Hq} ring={ring} chunk={chunk} "
-        f"streams={streams} group={group} flags={flags} residency={getattr(resident_fn, '__name__', 'fn')}")
+        f"group={group} flags={flags} residency={getattr(resident_fn, '__name__', 'fn')}")
     return Case(cid=cid, n_layers=n_layers, n_kv_heads=Hkv, n_q_heads=Hq, n_kv=n_kv, slots=slots,
-                cfg_kw=dict(max_q_tokens=max_q, ring_pages=ring, chunk_pages=chunk, copy_streams=streams,
+                cfg_kw=dict(max_q_tokens=max_q, ring_pages=ring, chunk_pages=chunk,
                             group_pages=group, flags=flags),
                 resident_fn=resident_fn)
 
@@ -185,24 +185,24 @@ def test_prefill_bit_identical_across_residency_and_ring():
 
 def test_outputs_bit_identical_across_residency_ring_and_chunks():
     variants = [
-        dict(resident=mask_all, ring=4, chunk=2, streams=2),
-        dict(resident=mask_none, ring=1, chunk=1, streams=1),
-        dict(resident=mask_none, ring=6, chunk=3, streams=3),
-        dict(resident=mask_random(0.5), ring=4, chunk=4, streams=1),
-        dict(resident=mask_random(0.3, seed=5), ring=2, chunk=1, streams=2, flags=kvs.FLAG_POISON_RING),
+        dict(resident=mask_all, ring=4, chunk=2),
+        dict(resident=mask_none, ring=1, chunk=1),
+        dict(resident=mask_none, ring=6, chunk=3),
+        dict(resident=mask_random(0.5), ring=4, chunk=4),
+        dict(resident=mask_random(0.3, seed=5), ring=2, chunk=1, flags=kvs.FLAG_POISON_RING),
         # four or more chunk slots: two or three compute lanes (a divisor of
         # the slot count, which is at least twice the lanes) when no group
         # spans two chunks
-        dict(resident=mask_none, ring=4, chunk=1, streams=1),
-        dict(resident=mask_random(0.5, seed=6), ring=8, chunk=2, streams=2, flags=kvs.FLAG_POISON_RING),
-        dict(resident=mask_none, ring=6, chunk=1, streams=1, flags=kvs.FLAG_POISON_RING),
-        dict(resident=mask_random(0.3, seed=8), ring=12, chunk=2, streams=1),
-        dict(resident=mask_random(0.2, seed=12), ring=16, chunk=2, streams=1),
+        dict(resident=mask_none, ring=4, chunk=1),
+        dict(resident=mask_random(0.5, seed=6), ring=8, chunk=2, flags=kvs.FLAG_POISON_RING),
+        dict(resident=mask_none, ring=6, chunk=1, flags=kvs.FLAG_POISON_RING),
+        dict(resident=mask_random(0.3, seed=8), ring=12, chunk=2),
+        dict(resident=mask_random(0.2, seed=12), ring=16, chunk=2),
     ]
     for group in (1, 3):
         base = None
         for v in variants:
-            c = small_case(v["resident"], max_q=4, ring=v["ring"], chunk=v["chunk"], streams=v["streams"],
+            c = small_case(v["resident"], max_q=4, ring=v["ring"], chunk=v["chunk"],
                            group=group, flags=v.get("flags", 0))
             try:
                 qs = [c.queries(l, 4, "f32") for l in range(c.L)]
@@ -230,7 +230,7 @@ def test_verify_over_many_segments_slices_them_across_workers():
     for v in [dict(resident=mask_all, ring=8, chunk=2),
               dict(resident=mask_none, ring=8, chunk=2, flags=kvs.FLAG_POISON_RING)]:
         c = small_case(v["resident"], cid=41, n_layers=2, n_kv=n_kv, Hkv=8, Hq=48, max_q=n_q, ring=v["ring"],
-                       chunk=v["chunk"], streams=1, group=1, flags=v.get("flags", 0))
+                       chunk=v["chunk"], group=1, flags=v.get("flags", 0))
         try:
             qs = [c.queries(l, n_q, "f32") for l in range(c.L)]
             outs, lses = c.attend_all(qs, q_pos0=n_kv - n_q, scale=1.0, causal=True)
@@ -297,7 +297,7 @@ def test_tiny_decode_workload():
     from kvs_synth import WORKLOADS
     wl = WORKLOADS["tiny_decode"]
     c = Case(cid=wl.cid, n_layers=1, n_kv_heads=1, n_q_heads=1, n_kv=wl.n_kv, resident_fn=mask_all,
-             cfg_kw=dict(max_q_tokens=1, ring_pages=4, chunk_pages=2, copy_streams=2, group_pages=1))
+             cfg_kw=dict(max_q_tokens=1, ring_pages=4, chunk_pages=2, group_pages=1))
     try:
         qs = [c.queries(0, 1, wl.q_dtype)]
         outs, lses = c.attend_all(qs, q_pos0=wl.q_pos0, scale=wl.scale, causal=wl.causal)
@@ -375,7 +375,7 @@ def test_decode_rows_groups_and_residency(Hkv, Hq, n_q, causal, group):
     oracle, and the same bits."""
     base = None
     for resident, ring, chunk in [(mask_all, 4, 2), (mask_random(0.5, seed=17), 12, 2)]:
-        c = small_case(resident, n_layers=2, Hkv=Hkv, Hq=Hq, max_q=n_q, ring=ring, chunk=chunk, streams=1,
+        c = small_case(resident, n_layers=2, Hkv=Hkv, Hq=Hq, max_q=n_q, ring=ring, chunk=chunk,
                        group=group)
         try:
             qs = [c.queries(l, n_q, "f32") for l in range(c.L)]

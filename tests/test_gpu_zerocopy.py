@@ -25,7 +25,7 @@ N_KV = 5 * 256 + 77
 def case(resident_fn, flags, *, n_q=4, ring=4, chunk=2, group=1, cid=71, n_layers=2):
     say(f"zero-copy case flags={flags} n_q={n_q} ring={ring} chunk={chunk} group={group}")
     return Case(cid=cid, n_layers=n_layers, n_kv_heads=2, n_q_heads=12, n_kv=N_KV,
-                cfg_kw=dict(max_q_tokens=n_q, ring_pages=ring, chunk_pages=chunk, copy_streams=1,
+                cfg_kw=dict(max_q_tokens=n_q, ring_pages=ring, chunk_pages=chunk,
                             group_pages=group, flags=flags),
                 resident_fn=resident_fn)
 
@@ -122,7 +122,7 @@ def test_zero_copy_staged_runs_on_lanes_equal_the_ring():
     for flags in (0, kvs.FLAG_ZERO_COPY):
         say(f"staged lanes case flags={flags} n_kv={n_kv}")
         c = Case(cid=73, n_layers=1, n_kv_heads=2, n_q_heads=12, n_kv=n_kv,
-                 cfg_kw=dict(max_q_tokens=n_q, ring_pages=8, chunk_pages=4, copy_streams=1, group_pages=1,
+                 cfg_kw=dict(max_q_tokens=n_q, ring_pages=8, chunk_pages=4, group_pages=1,
                              flags=flags),
                  resident_fn=mask_random(0.3, seed=10))
         try:

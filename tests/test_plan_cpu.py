@@ -19,7 +19,7 @@ import host_streamed_paged_amd as kvs
 def cfg_for(n_pages, G, C, ring=None):
     ring = ring if ring is not None else 4 * C
     return kvs.Config(n_layers=1, n_kv_heads=4, n_q_heads=24, max_pages=max(1, n_pages), max_q_tokens=4,
-                      ring_pages=ring, chunk_pages=C, copy_streams=1, group_pages=G)
+                      ring_pages=ring, chunk_pages=C, group_pages=G)
 
 
 def check_plan(mask, G, C):

@@ -43,14 +43,14 @@ def test_floor_ceiling_and_small_contexts():
 
 def test_budget_is_the_minimum_plus_the_resident_pages():
     cfg = kvs.Config(n_layers=16, n_kv_heads=4, n_q_heads=24, max_pages=1024, max_q_tokens=1,
-                     ring_pages=32, chunk_pages=4, copy_streams=1, group_pages=1)
+                     ring_pages=32, chunk_pages=4, group_pages=1)
     base, pb = kvs.min_budget_bytes(cfg), kvs.page_bytes(cfg)
     assert kvs.auto_budget_bytes(cfg, 0) == base
     b = kvs.auto_budget_bytes(cfg, 262144)
     assert b == base + 16 * 103 * pb
     assert kvs.slots_for_budget(cfg, b) == 16 * 103
     big = kvs.Config(n_layers=64, n_kv_heads=8, n_q_heads=64, max_pages=65536, max_q_tokens=1,
-                     ring_pages=32, chunk_pages=4, copy_streams=1, group_pages=1)
+                     ring_pages=32, chunk_pages=4, group_pages=1)
     assert kvs.auto_budget_bytes(big, 2 ** 24) == 8192 * 2 ** 20
 
 
