@@ -143,3 +143,28 @@ def test_q8_0_q4_0_page_bytes():
     # 4 kv heads x 128: K row 4 x 4 x 34 = 544 B, V row 4 x 4 x 18 = 288 B
     assert page_bytes(4, 128) == 256 * (544 + 288) == 212992
     assert page_bytes(1, 128) == 53248
+
+
+def test_numpy_binary16_encoding_rounds_to_nearest_even():
+    """The staged-operand probe compares the kernels' f16 operands with
+    numpy's float64 -> float16 conversion of the exact value; pin that
+    conversion to round-to-nearest-even on every pair of neighbouring finite
+    binary16 values (subnormals included): each value maps to itself, a point
+    just inside either half of the gap maps to the nearer neighbour, and the
+    exact midpoint maps to the neighbour with an even significand."""
+    from oracle import f16_to_f64
+    bits = np.arange(0, 0x7C00, dtype=np.uint16)          # +0 .. 65504
+    vals = f16_to_f64(bits)
+    lo, hi = vals[:-1], vals[1:]
+    assert np.array_equal(vals.astype(np.float16).view(np.uint16), bits)
+    mid = (lo + hi) / 2                                      # exact in float64
+    gap = hi - lo
+    near_lo = (mid - gap / 8).astype(np.float16).view(np.uint16)
+    near_hi = (mid + gap / 8).astype(np.float16).view(np.uint16)
+    assert np.array_equal(near_lo, bits[:-1]) and np.array_equal(near_hi, bits[1:])
+    at_mid = mid.astype(np.float16).view(np.uint16)
+    want = np.where(bits[:-1] % 2 == 0, bits[:-1], bits[1:])
+    assert np.array_equal(at_mid, want)
+    # negatives mirror, and the largest value's upper half-gap rounds to it
+    assert np.array_equal((-vals).astype(np.float16).view(np.uint16), bits | 0x8000)
+    assert np.float16(65504.0 + 15.0).view(np.uint16) == 0x7BFF
