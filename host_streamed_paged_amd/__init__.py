@@ -39,7 +39,10 @@ EXPORTS = [
     "kvs_debug_read_page", "kvs_last_error", "kvs_profile_enable", "kvs_profile_read", "kvs_append",
     "kvs_auto_resident_pages", "kvs_auto_stage_bytes", "kvs_auto_budget_bytes", "kvs_residency_promote_newest",
     "kvs_pool_pin_layer", "kvs_pool_reset_pinned", "kvs_debug_export_pages", "kvs_debug_stage",
+    "kvs_attend_noalloc",
 ]
+
+NOALLOC_SCRATCH_BYTES = 4 << 20   # KVS_NOALLOC_SCRATCH_BYTES
 
 STAGED_TILE_BYTES = 133376   # KVS_STAGED_TILE_BYTES
 
@@ -95,6 +98,7 @@ def lib() -> ctypes.CDLL:
         "kvs_page_table_set": (ctypes.c_int, [P, I32, I32, P, P]),
         "kvs_stream_enqueue": (ctypes.c_int, [P, I32]),
         "kvs_attend": (ctypes.c_int, [P, I32, P, I32, I32, I64, I64, F, I32, P, P, P]),
+        "kvs_attend_noalloc": (ctypes.c_int, [P, I32, P, I32, I32, I64, I64, F, I32, P, P, P]),
         "kvs_status": (ctypes.c_int, [P, ctypes.POINTER(KvsStatus)]),
         "kvs_debug_gather": (ctypes.c_int, [P, I32, I64, I64, P, P, P]),
         "kvs_append": (ctypes.c_int, [P, I32, P, P, I32, I64, I32, P]),
@@ -283,6 +287,23 @@ class Pool:
             assert lse.dtype == torch.float32 and lse.is_contiguous() and lse.shape == q.shape[:2]
         _check(lib().kvs_attend(self._h, layer, _ptr(q), qd, q.shape[0], q_pos0, n_kv, float(scale),
                                 1 if causal else 0, _ptr(out), _ptr(lse), _stream(stream)))
+
+    def attend_noalloc(self, layer: int, q: torch.Tensor, n_kv: int, q_pos0: int, scale: float, causal: bool,
+                       out: torch.Tensor, lse: torch.Tensor | None = None, stream=None):
+        """kvs_attend_noalloc: kvs_attend with the split-K partials in the
+        library's fixed scratch array (no allocation)."""
+        if q.dtype == torch.float32:
+            qd = Q_F32
+        elif q.dtype == torch.float16:
+            qd = Q_F16
+        else:
+            raise TypeError("q must be float32 or float16")
+        assert q.is_contiguous() and out.is_contiguous() and out.dtype == torch.float32
+        assert q.dim() == 3 and out.shape == q.shape
+        if lse is not None:
+            assert lse.dtype == torch.float32 and lse.is_contiguous() and lse.shape == q.shape[:2]
+        _check(lib().kvs_attend_noalloc(self._h, layer, _ptr(q), qd, q.shape[0], q_pos0, n_kv, float(scale),
+                                        1 if causal else 0, _ptr(out), _ptr(lse), _stream(stream)))
 
     def append(self, layer: int, k_new: torch.Tensor, v_new: torch.Tensor, pos0: int, stream=None):
         """Quantize new K and V rows [n_tok, Hkv, head_dim] (f32 or f16, on the

@@ -203,6 +203,13 @@ struct LaunchTiming {
 };
 LaunchTiming& launch_timing();   // this thread's pending pair (kvs_kernels.hip)
 
+// The library's fixed scratch array of split-K partials (kvs_attend_noalloc):
+// its size, and its device address on the current device, looked up once per
+// device with hipGetSymbolAddress (kvs_kernels.hip, beside the array).
+constexpr size_t kScratchBytes = size_t(KVS_NOALLOC_SCRATCH_BYTES);
+constexpr int kMaxDevices = 64;
+hipError_t scratch_region(float** out);
+
 hipError_t launch_attend(const AttendArgs& a, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 // few-row decode kernel (kvs_decode.hip): rows = n_q * G in [1, 6]

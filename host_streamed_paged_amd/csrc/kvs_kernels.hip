@@ -21,6 +21,7 @@
 #include <cstdint>
 #include <cmath>
 #include <cstdlib>
+#include <mutex>
 
 #include "kvs_internal.h"
 #include "kvs_device.h"
@@ -190,6 +191,31 @@ __global__ void fill_u32_kernel(uint32_t* __restrict__ p, uint32_t v, uint64_t n
 }
 
 }  // namespace
+
+// Split-K partial records for kvs_attend_noalloc, for callers that cannot
+// allocate: a fixed array in the library's own device memory (each GPU the
+// library runs on holds one until the process ends). Host code never passes
+// the array's name to a kernel: on the host it stands for the array, not for
+// its device address, which scratch_region looks up once per device.
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+hipError_t scratch_region(float** out) {
+    static std::mutex mu;
+    static float* addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = (float*)p;
+    }
+    *out = addr[dev];
+    return hipSuccess;
+}
 
 LaunchTiming& launch_timing() {
     static thread_local LaunchTiming t;

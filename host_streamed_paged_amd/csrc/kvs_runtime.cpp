@@ -178,6 +178,7 @@ struct kvs_pool {
     int32_t ring_next = 0;           // chunk slot that receives the next layer's chunk 0
     int32_t pf_layer = -1;           // layer whose chunk 0 was prefetched and not yet consumed
     bool broken = false;             // a HIP call failed mid-sequence
+    float* scratch = nullptr;        // device address of the library's scratch array on this device
     kvs_status_info st{};
     // kernel timing (kvs_profile_*): per kind, event pairs in launch order
     bool profiling = false;
@@ -787,6 +788,11 @@ int kvs_pool_create(const kvs_config* cfg, void* dev_arena, uint64_t budget_byte
         hipError_t e = hipEventCreateWithFlags(&p->join_ev[k], hipEventDisableTiming);
         if (e != hipSuccess) return cleanup("hipEventCreateWithFlags", e);
     }
+    {
+        // set-up of kvs_attend_noalloc: the scratch array's address on this device
+        hipError_t e = kvs::scratch_region(&p->scratch);
+        if (e != hipSuccess) return cleanup("hipGetSymbolAddress(scratch)", e);
+    }
     p->st.page_bytes = (int64_t)L.page_bytes;
     p->st.slot_count = p->n_slots;
     p->st.ring_pages = cfg->ring_pages;
@@ -995,8 +1001,15 @@ int kvs_stream_enqueue(kvs_pool* p, int32_t layer) {
     return prefetch(p, layer);
 }
 
-int kvs_attend(kvs_pool* p, int32_t layer, const void* q, int32_t q_dtype, int32_t n_q, int64_t q_pos0, int64_t n_kv,
-               float scale, int32_t causal, float* out, float* lse, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// kvs_attend and kvs_attend_noalloc: the split-K partials go to the pool's
+// workspace, or (noalloc) to the library's scratch array, and a noalloc call
+// creates no timing events.
+int attend_impl(kvs_pool* p, int32_t layer, const void* q, int32_t q_dtype, int32_t n_q, int64_t q_pos0, int64_t n_kv,
+                float scale, int32_t causal, float* out, float* lse, void* stream, bool noalloc) {
     if (!p) return fail(KVS_ERR_INVALID_ARG, "pool is NULL");
     int rc = check_device(p);
     if (rc) return rc;
@@ -1013,10 +1026,23 @@ int kvs_attend(kvs_pool* p, int32_t layer, const void* q, int32_t q_dtype, int32
     if (causal && (q_pos0 < 0 || q_pos0 + n_q > n_kv))
         return fail(KVS_ERR_INVALID_ARG, "causal queries at positions [%lld, %lld) must lie inside the cache of %lld tokens",
                     (long long)q_pos0, (long long)(q_pos0 + n_q), (long long)n_kv);
+    if (noalloc) {
+        const uint64_t need = (uint64_t)ls.n_groups * n_q * p->cfg.n_q_heads * kvs::kPartStride * sizeof(float);
+        if (need > kvs::kScratchBytes)
+            return fail(KVS_ERR_INVALID_ARG,
+                        "kvs_attend_noalloc needs %llu bytes of split-K scratch (%d groups x %d query tokens x %d heads), "
+                        "above its fixed %llu bytes; use kvs_attend or larger group_pages",
+                        (unsigned long long)need, ls.n_groups, n_q, p->cfg.n_q_heads, (unsigned long long)kvs::kScratchBytes);
+    }
     if ((rc = check_ring_free_for(p, layer))) return rc;
     hipStream_t s = (hipStream_t)stream;
     if ((rc = check_capture(p, layer, s))) return rc;
     if ((rc = order_after_last_work(p, s))) return rc;
+    float* part = noalloc ? p->scratch : p->work;
+    // a noalloc call creates no timing events
+    auto timed_or_not = [&](int kind, hipStream_t st, auto fn) -> hipError_t {
+        return noalloc ? fn() : timed(p, kind, st, fn);
+    };
 
     kvs::AttendArgs a{};
     a.ps.slots = p->slots;
@@ -1033,7 +1059,7 @@ int kvs_attend(kvs_pool* p, int32_t layer, const void* q, int32_t q_dtype, int32
     a.n_kv = n_kv;
     a.scale_log2 = scale * 1.44269504088896340736f;
     a.causal = causal ? 1 : 0;
-    a.part = p->work;
+    a.part = part;
     const bool staging = kvs::mfma_stages(n_q * a.G);
     rc = run_layer(p, layer, s, staging ? p->L.stage_pages : 0,
                    [&](hipStream_t st, int lane, int32_t seg0, int32_t nseg, const uint8_t* ring_chunk,
@@ -1045,7 +1071,7 @@ int kvs_attend(kvs_pool* p, int32_t layer, const void* q, int32_t q_dtype, int32
         if (!staging || nseg == 0) {
             b.segs = ls.dev_segs + seg0;
             b.n_segs = nseg;
-            hipError_t e = timed(p, 0, st, [&] { return kvs::launch_attend(b, st); });
+            hipError_t e = timed_or_not(0, st, [&] { return kvs::launch_attend(b, st); });
             return e == hipSuccess ? KVS_OK : fail(KVS_ERR_HIP, "attention kernel launch failed: %s", hipGetErrorString(e));
         }
         // staged: runs of segments of at most stage_pages pages; each run is
@@ -1069,24 +1095,38 @@ int kvs_attend(kvs_pool* p, int32_t layer, const void* q, int32_t q_dtype, int32
             sa.n_kv = n_kv;
             sa.n_pages = pages;
             sa.staged = region;
-            hipError_t e = timed(p, 2, st, [&] { return kvs::launch_stage(sa, st); });
+            hipError_t e = timed_or_not(2, st, [&] { return kvs::launch_stage(sa, st); });
             if (e != hipSuccess) return fail(KVS_ERR_HIP, "staging kernel launch failed: %s", hipGetErrorString(e));
             kvs::AttendArgs c = b;
             c.copy = first_run ? kvs::split_copy(cj, half, false) : kvs::CopyJob{};
             c.segs = ls.dev_segs + i;
             c.n_segs = j - i;
             c.staged = region;
-            e = timed(p, 0, st, [&] { return kvs::launch_attend(c, st); });
+            e = timed_or_not(0, st, [&] { return kvs::launch_attend(c, st); });
             if (e != hipSuccess) return fail(KVS_ERR_HIP, "attention kernel launch failed: %s", hipGetErrorString(e));
             i = j;
         }
         return KVS_OK;
     });
     if (rc) return rc;
-    hipError_t e = timed(p, 1, s, [&] { return kvs::launch_combine(p->work, ls.n_groups, n_q, p->cfg.n_q_heads, out, lse, s); });
+    hipError_t e = timed_or_not(1, s, [&] { return kvs::launch_combine(part, ls.n_groups, n_q, p->cfg.n_q_heads, out, lse, s); });
     if (e != hipSuccess) { p->broken = true; return fail(KVS_ERR_HIP, "combine launch failed: %s", hipGetErrorString(e)); }
     p->st.kernels_launched++;
     return record_last_work(p, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvs_attend(kvs_pool* p, int32_t layer, const void* q, int32_t q_dtype, int32_t n_q, int64_t q_pos0, int64_t n_kv,
+               float scale, int32_t causal, float* out, float* lse, void* stream) {
+    return attend_impl(p, layer, q, q_dtype, n_q, q_pos0, n_kv, scale, causal, out, lse, stream, false);
+}
+
+int kvs_attend_noalloc(kvs_pool* p, int32_t layer, const void* q, int32_t q_dtype, int32_t n_q, int64_t q_pos0,
+                       int64_t n_kv, float scale, int32_t causal, float* out, float* lse, void* stream) {
+    return attend_impl(p, layer, q, q_dtype, n_q, q_pos0, n_kv, scale, causal, out, lse, stream, true);
 }
 
 int kvs_status(const kvs_pool* p, kvs_status_info* info) {

@@ -330,6 +330,24 @@ int kvs_attend(kvs_pool* pool, int32_t layer, const void* q, int32_t q_dtype, in
                int64_t q_pos0, int64_t n_kv, float scale, int32_t causal, float* out,
                float* lse, void* stream);
 
+/* kvs_attend for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels and results (bit for bit), but the split-K partial records
+ * live in a fixed array of KVS_NOALLOC_SCRATCH_BYTES in the library's own
+ * device memory instead of the pool's workspace, and the call creates
+ * nothing (no timing events either: kvs_profile_enable does not apply). It
+ * needs n_groups x n_q x n_q_heads x 130 x 4 bytes of that array, where
+ * n_groups = ceil(n_pages / group_pages) of the layer; a call needing more
+ * returns KVS_ERR_INVALID_ARG before any device work. Every call on a GPU,
+ * from any pool, shares that GPU's one array, which keeps the last call's
+ * contents (nothing in it needs clearing: every group's first launch starts
+ * its record afresh). Calls of one pool are ordered like kvs_attend's; calls
+ * of different pools that overlap in time on one GPU race on the array. */
+#define KVS_NOALLOC_SCRATCH_BYTES (4u << 20)
+int kvs_attend_noalloc(kvs_pool* pool, int32_t layer, const void* q, int32_t q_dtype, int32_t n_q,
+                       int64_t q_pos0, int64_t n_kv, float scale, int32_t causal, float* out, float* lse,
+                       void* stream);
+
 /* Append a step's new K and V rows to a layer: quantize them into Q8_0 (K)
  * and Q4_0 (V) blocks and write them at tokens pos0 .. pos0 + n_tok - 1 of
  * the layer, into the authoritative host records and, for each resident page,
