@@ -181,8 +181,8 @@ int64_t kvs_slots_for_budget(const kvs_config* cfg, uint64_t budget_bytes);
  * kvs_auto_stage_bytes: the pages' stage size for n_layers streamed layers of
  *   bytes_per_token bytes per token and layer: n_layers x (resident pages + 4)
  *   x 256 x bytes_per_token, capped at 8192 MiB (reproduces the logged 255 MiB
- *   at 64 Ki and 910 MiB at 256 Ki for 2176 B q8_0/q8_0 tokens, and 1712 MiB
- *   at 256 Ki for 4096 B f16 tokens). Pure; 0 on non-positive arguments.
+ *   at 64 Ki and 910 MiB at 256 Ki for 2176 B q8_0/q8_0 tokens). Pure; 0 on
+ *   non-positive arguments.
  * kvs_auto_budget_bytes: this pool's budget for the same residency: the
  *   minimum budget of cfg plus n_layers x resident pages x page_bytes, capped
  *   at 8192 MiB (never below the minimum). Written to *out. Pure. */
