@@ -41,11 +41,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 # The pool configuration each workload runs with (ring, chunk and split-K
-# group sizes in pages; one copy stream for kvs_stream_enqueue). The
-# full-size parity tests use the same table.
+# group sizes in pages). The full-size parity tests use the same table. The
+# streamed decode runs through the 16-page ring its workload specifies; a
+# 48-page ring is timed beside it as a labelled variant.
+STREAMED_RING48 = dict(ring_pages=48, chunk_pages=4, group_pages=1)
+
 POOL_CFG = {
     "resident_decode_32k": dict(ring_pages=48, chunk_pages=4, group_pages=1),
-    "streamed_decode_256k": dict(ring_pages=48, chunk_pages=4, group_pages=1),
+    "streamed_decode_256k": dict(ring_pages=16, chunk_pages=4, group_pages=1),
     "spec_verify_160k": dict(ring_pages=48, chunk_pages=4, group_pages=1),
     "prefill_ubatch_128k": dict(ring_pages=96, chunk_pages=16, group_pages=8),
 }
@@ -214,13 +217,12 @@ def append_leg(wl, st, steps, link):
     return out
 
 
-def zero_copy_leg(wl, st, cfg_kw, steps, link):
-    """The A/B against the ring (KVS_FLAG_ZERO_COPY): a second pool over the
-    same pinned host records and residency, whose attention kernels read the
-    streamed pages in place over the link instead of through the ring."""
+def variant_leg(wl, st, cfg_kw, steps, link, flags, how):
+    """A second pool over the same pinned host records and residency, with
+    another ring geometry or mode, timed the same way."""
     import host_streamed_paged_amd as kvs
     cfg = kvs.Config(n_layers=wl.n_layers, n_kv_heads=wl.n_kv_heads, n_q_heads=wl.n_q_heads,
-                     max_pages=wl.n_pages, max_q_tokens=wl.n_q, flags=kvs.FLAG_ZERO_COPY, **cfg_kw)
+                     max_pages=wl.n_pages, max_q_tokens=wl.n_q, flags=flags, **cfg_kw)
     arena = kvs.Pool.arena_for(cfg, int(sum(int(m.sum()) for m in st["masks"])))
     pool = kvs.Pool(cfg, arena)
     for l in range(wl.n_layers):
@@ -231,10 +233,19 @@ def zero_copy_leg(wl, st, cfg_kw, steps, link):
     pb = st["recs"][0].shape[1]
     streamed_bytes = sum(int((1 - m).sum()) for m in st["masks"]) * pb
     sec = sr["ms_per_step"] / 1e3
-    log(f"{wl.name} zero-copy: {sr['ms_per_step']:.3f} ms/step, streamed {streamed_bytes / sec / 1e9:.2f} GB/s")
+    log(f"{wl.name} {how}: {sr['ms_per_step']:.3f} ms/step, streamed {streamed_bytes / sec / 1e9:.2f} GB/s")
     return {"ms_per_step": round(sr["ms_per_step"], 4), "streamed_gbs": round(streamed_bytes / sec / 1e9, 2),
-            "frac_of_link": round(streamed_bytes / sec / 1e9 / link, 4) if link else None,
-            "how": "attention kernels read streamed pages in place from pinned host memory; no ring, no copies"}
+            "frac_of_link": round(streamed_bytes / sec / 1e9 / link, 4) if link else None, "how": how, **cfg_kw}
+
+
+def zero_copy_leg(wl, st, cfg_kw, steps, link):
+    """The A/B against the ring (KVS_FLAG_ZERO_COPY): the attention kernels
+    read the streamed pages in place over the link instead of through the
+    ring."""
+    import host_streamed_paged_amd as kvs
+    return variant_leg(wl, st, cfg_kw, steps, link, kvs.FLAG_ZERO_COPY,
+                       "zero-copy: attention kernels read streamed pages in place from pinned host memory; "
+                       "no ring, no copies")
 
 
 def allowed_keys(wl):
@@ -344,10 +355,23 @@ def measure_link():
     return n / best / 1e9
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, recs, qs_np, min_s=10.0, max_s=30.0):
     """The float64 oracle, one layer at a time, in whole passes over the
     workload's layers until at least min_s of work (a pass that would run past
-    max_s stops at the layer where it gets there)."""
+    max_s stops at the layer where it gets there). `cores` is the number of
+    host cores this process may run on; numpy's BLAS threads are reported
+    beside it."""
     from oracle import attend_layer
     try:
         from threadpoolctl import threadpool_info
@@ -369,7 +393,9 @@ def cpu_baseline(wl, recs, qs_np, min_s=10.0, max_s=30.0):
     return {
         "value": round(layers * layer_bytes / dt / 1e9, 4),
         "unit": "GB/s",
-        "cores": int(blas_threads),
+        "cores": len(os.sched_getaffinity(0)),
+        "cpu_model": cpu_model(),
+        "blas_threads": int(blas_threads),
         "kind": "oracle",
         "sample": f"{wl.name}: {layers} layer passes ({layers / wl.n_layers:.2f} x the {wl.n_layers}-layer step; "
                   f"float64 numpy, one layer at a time), {dt:.1f}s; decode attn tok/s equivalent "
@@ -450,7 +476,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "mixed(i8,f16,f32)",
+        "dtype_note": "Q8_0 codes exact on int8 (decode, 16-bit fixed-point query limbs) or f16 (matrix-core "
+                      "paths) matrix operands; probabilities and V elements in f16; float32 block scales, "
+                      "scores, softmax and accumulation",
         "data": "synthetic",
         "config": {
             "workload": wl.name, "layers": wl.n_layers, "q_heads": wl.n_q_heads, "kv_heads": wl.n_kv_heads,
@@ -491,12 +520,15 @@ def main():
             "streamed_bytes_per_step": streamed_bytes, "kv_bytes_per_step": total_bytes,
             "ring_copy_launches_per_step": round(st_info.copies_issued / (args.streamed_steps + 2), 1),
             "resident_bytes_per_step": res_bytes,
-            "schedule": "ring 48 pages in 4-page chunks; copy workgroups inside the compute launches; "
-                        "three compute lanes take chunks in turn",
+            "schedule": f"ring {scfg['ring_pages']} pages in {scfg['chunk_pages']}-page chunks; copy workgroups "
+                        "inside the compute launches; the compute lanes take chunks in turn",
         }
         log(f"{swl.name}: {sr['ms_per_step']:.3f} ms/step, streamed {streamed_bytes / sec / 1e9:.2f} GB/s "
             f"of link {link:.2f} GB/s")
         sst["pool"].close()
+        result["streamed"]["ring48_variant"] = variant_leg(
+            swl, sst, STREAMED_RING48, args.streamed_steps, link, 0,
+            "variant: the same step through a 48-page ring in 4-page chunks (three compute lanes)")
         if not args.no_zero_copy:
             result["streamed"]["zero_copy"] = zero_copy_leg(swl, sst, scfg, args.streamed_steps, link)
         del sst
