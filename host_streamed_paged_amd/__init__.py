@@ -44,7 +44,7 @@ EXPORTS = [
 
 NOALLOC_SCRATCH_BYTES = 4 << 20   # KVS_NOALLOC_SCRATCH_BYTES
 
-STAGED_TILE_BYTES = 133376   # KVS_STAGED_TILE_BYTES
+STAGED_TILE_BYTES = 135424   # KVS_STAGED_TILE_BYTES
 
 
 class KvsError(RuntimeError):

@@ -104,6 +104,70 @@ __device__ inline half2_t q4_nibbles_f16(uint32_t biased, half2_t c, half2_t min
     return __builtin_elementwise_fma(as_h2(biased), c, minus_1032c);
 }
 
+// Query operands of the matrix-core kernels (16x16x32 f16 tiles, the query
+// as the B operand): this lane's 8 elements [32 b + 8 gq, +8) of each block b
+// of query row (token qi, head h), zero if !valid. The row is scaled by the
+// power of two that puts its largest magnitude in [2^14, 2^15), and by the
+// sign of the softmax scale (both exact), then split into f16 limbs:
+// hi = f16(q'), and for LIMBS == 2 lo = f16(q' - hi), which holds an f32
+// query to about 22 bits (an f16 query is exact in hi). cq = |scale| *
+// log2(e) / 2^shift > 0 turns the float32 products into log2-unit scores
+// (a zero scale gives zero operands and cq = 1: every score is 0). Every lane
+// of the wave must call it (the row maximum is exchanged between lanes n,
+// n + 16, n + 32, n + 48).
+template <int LIMBS>
+__device__ inline void query_operands(const AttendArgs& a, int qi, int h, bool valid, int gq,
+                                      half8_t (&qop)[LIMBS][kNB], float& cq) {
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    float x[kNB][8];
+    if (valid) {
+        const int64_t off = ((int64_t)qi * a.n_q_heads + h) * kHeadDim + 8 * gq;
+#pragma unroll
+        for (int b = 0; b < kNB; ++b) {
+            if (a.q_f16) {
+                const u32x4_t raw = *(const u32x4_t*)((const _Float16*)a.q + off + kQK * b);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const half2_t hv = as_h2(raw[e]);
+                    x[b][2 * e] = (float)hv[0];
+                    x[b][2 * e + 1] = (float)hv[1];
+                }
+            } else {
+                const f32x4_t* qp = (const f32x4_t*)((const float*)a.q + off + kQK * b);
+                const f32x4_t u0 = qp[0], u1 = qp[1];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { x[b][e] = u0[e]; x[b][4 + e] = u1[e]; }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int b = 0; b < kNB; ++b)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[b][e] = 0.f;
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int b = 0; b < kNB; ++b)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[b][e]));
+    amax = max_xor16(amax);   // over the row's four lanes
+    amax = max_xor32(amax);
+    const int ex = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) : 0;   // amax = m 2^ex, m in [0.5, 1)
+    const float sgn = a.scale_log2 < 0.f ? -1.f : (a.scale_log2 > 0.f ? 1.f : 0.f);
+    const float up = sgn * __builtin_amdgcn_ldexpf(1.f, 15 - ex);
+    cq = a.scale_log2 == 0.f ? 1.f : fabsf(a.scale_log2) * __builtin_amdgcn_ldexpf(1.f, ex - 15);
+#pragma unroll
+    for (int b = 0; b < kNB; ++b)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float y = x[b][e] * up;   // exact
+            const _Float16 hi = (_Float16)y;
+            qop[0][b][e] = hi;
+            if constexpr (LIMBS == 2) qop[LIMBS - 1][b][e] = (_Float16)(y - (float)hi);
+        }
+}
+
 // Page record of logical page `page` for this launch: a resident slot, a
 // slot of the ring chunk the launch works on, or (zero-copy launches) the
 // pinned host record itself.

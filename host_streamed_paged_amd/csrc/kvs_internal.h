@@ -21,11 +21,17 @@ constexpr int kKTile = kPageTokens * kKRow;  // 34816 B: one head's K for one pa
 constexpr int kVTile = kPageTokens * kVRow;  // 18432 B
 constexpr int kPartStride = kHeadDim + 2;    // partial record: acc[128], m (log2 units), l
 // Staged matrix-core operands of one (page, kv head): the f16 K and V^T
-// operands in fragment order, the K block scales per token, and the V scaling
-// exponent of each 32-channel block (padded to keep tiles 256-byte aligned).
-constexpr int kStagedOps = 2 * kPageTokens * kHeadDim * 2;
-constexpr int kStagedScaleBytes = kPageTokens * kNB * 2;
-constexpr int kStagedTile = kStagedOps + kStagedScaleBytes + 256;
+// operands in fragment order, the K block scales per token as float32, and
+// the V scaling exponent of each 32-channel block (padded to keep tiles
+// 256-byte aligned).
+constexpr int kStagedK = kPageTokens * kHeadDim * 2;          // K operands [16 token tiles][4 blocks][64 lanes] x 16 B
+constexpr int kStagedOps = 2 * kStagedK;                      // then V^T operands [8 chunks][8 channel tiles][64 lanes] x 16 B
+constexpr int kStagedScaleBytes = kPageTokens * kNB * 4;      // K scales [token][block] float32
+constexpr int kStagedShift = kStagedOps + kStagedScaleBytes;  // V shift per block, int32
+constexpr int kStagedTile = kStagedShift + 256;
+__host__ __device__ constexpr int staged_k_offset(int tt16, int b, int lane) { return ((tt16 * kNB + b) * 64 + lane) * 16; }
+__host__ __device__ constexpr int staged_v_offset(int c, int ct, int lane) { return kStagedK + ((c * 8 + ct) * 64 + lane) * 16; }
+__host__ __device__ constexpr int staged_scale_offset(int tok) { return kStagedOps + tok * kNB * 4; }
 static_assert(kStagedTile == KVS_STAGED_TILE_BYTES, "staged tile size as documented in kvs.h");
 
 // One run of consecutive logical pages of one split-K group, processed in
@@ -217,6 +223,9 @@ bool decode_supports(int rows);
 hipError_t launch_decode(const AttendArgs& a, hipStream_t stream);
 // matrix-core kernel (kvs_mfma.hip) for more rows
 hipError_t launch_mfma(const AttendArgs& a, hipStream_t stream);
+// prefill kernel on staged operands (kvs_prefill.hip), for blocks of more than
+// 64 rows per kv head
+hipError_t launch_prefill(const AttendArgs& a, hipStream_t stream);
 bool mfma_stages(int rows);   // rows per kv head for which launches stage their pages first
 hipError_t launch_stage(const StageArgs& a, hipStream_t stream);
 hipError_t launch_combine(const float* part, int32_t n_groups, int32_t n_q, int32_t n_q_heads,

@@ -31,14 +31,13 @@
 // state and page data alone, so results do not depend on how pages are split
 // into launches or which pages are resident.
 //
-// Staged mode, for blocks of more than 64 rows per kv head (a prefill
-// ubatch): every row tile would otherwise decode the same page again, so
-// stage_kernel first converts each (page, kv head) of the launch once into a
-// tile of f16 matrix-core operands in fragment order (K: [token tile][block]
-// [lane] x 16 B; V^T: [32-token chunk][channel tile][lane] x 16 B), the K
-// block scales per token and the V shift of each block, with the same code;
-// the attention kernel loads whole fragments from it. The operands, and so
-// the results, are the same bits either way.
+// Blocks of more than 64 rows per kv head (a prefill ubatch) would make
+// every row tile decode the same page again: stage_kernel (below) converts
+// each (page, kv head) of such a launch once into a tile of f16 matrix-core
+// operands in fragment order (K: [token tile][block][lane] x 16 B; V^T:
+// [32-token chunk][channel tile][lane] x 16 B), the K block scales per token
+// (float32) and the V shift of each block, with the conversion code used
+// here, and the prefill kernel (kvs_prefill.hip) computes on those tiles.
 #include <hip/hip_runtime.h>
 #include <cstdint>
 #include <cmath>
@@ -66,37 +65,14 @@ constexpr float kLazyMax = 8.f;
 constexpr uint32_t kVBigBits = 0x6FFFu;
 constexpr int kVShift = 3;
 
-// One page's tiles. (Double-buffering them measured slower: the next page's
-// LDS DMA then competes with the QK reads of the current one.) The P
-// operands [chunk][row tile][lane] (16 bytes each) have a region of their
-// own, so that the next page's K tile can be fetched into `k` as soon as
-// every wave is past QK, during the softmax and P.V of the current page.
-// `ksc` holds each wave's K block scales per token ([token][block] f16), the
-// layout the score lanes read them in.
-template <int RT, bool STAGED>
-struct MfmaSmem {
-    alignas(16) uint8_t k[kKTile];   // K tile in record layout
-    alignas(16) uint8_t v[kVTile];   // V tile in record layout
-    alignas(16) uint8_t p[kChunks * RT * 64 * 16];
-    alignas(16) uint32_t ksc[kWaves][kTokW * 2];
-    float red_m[kWaves][16 * RT];
-    float red_l[kWaves][16 * RT];
-};
-template <int RT>
-struct MfmaSmem<RT, true> {
-    alignas(16) uint8_t k[kChunks * RT * 64 * 16];   // P operands only
-    float red_m[kWaves][16 * RT];
-    float red_l[kWaves][16 * RT];
-};
-
-constexpr int kStagedK = kPageTokens * kHeadDim * 2;   // f16 K operands of one (page, kv head)
-static_assert(2 * kStagedK == kStagedOps, "staged operands = K + V^T");
-constexpr int kStagedShift = kStagedOps + kStagedScaleBytes;   // int32 V shift per block
-
-template <int RT>
-__device__ inline uint8_t* sm_p(MfmaSmem<RT, false>& sm) { return sm.p; }
-template <int RT>
-__device__ inline uint8_t* sm_p(MfmaSmem<RT, true>& sm) { return sm.k; }
+// LDS of the kernel (see mfma_kernel): one page's K tile and V tile in
+// record layout, the P operands [chunk][row tile][lane] (16 bytes each) in a
+// region of their own, so that the next page's K tile can be fetched into the
+// K tile as soon as every wave is past QK, during the softmax and P.V of the
+// current page, each wave's K block scales per token ([token][block] f16,
+// the layout the score lanes read them in), and the row maxima and sums of
+// the four waves. (Double-buffering the page tiles measured slower: the next
+// page's LDS DMA then competes with the QK reads of the current one.)
 
 // Stage one (page, kv head) tile of a page record into LDS by LDS DMA:
 // wave-sized pieces of 1 KB, 34 for K and 18 for V.
@@ -234,32 +210,21 @@ __device__ inline void v_convert(const VRaw& r, int c, int gq, int valid, int vs
     }
 }
 
-// Offsets of the staged operands of one (page, kv head) tile.
-__device__ inline int staged_k_offset(int tt16, int b, int lane) { return ((tt16 * kNB + b) * 64 + lane) * 16; }
-__device__ inline int staged_v_offset(int c, int ct, int lane) { return kStagedK + ((c * 8 + ct) * 64 + lane) * 16; }
-__device__ inline int staged_scale_offset(int tok) { return kStagedOps + tok * 8; }
-
-// Position of this launch's segment `seg_i` in the staged tiles: pages of the
-// launch's segments are staged in order.
-__device__ inline int staged_first_tile(const Seg* segs, int seg_i) {
-    int t = 0;
-    for (int i = 0; i < seg_i; ++i) t += scalar_load(&segs[i].npages);
-    return t;
-}
-
-// Workgroups per CU the register budget is cut for: up to 2 row tiles,
-// KVS_MFMA_OCC_NARROW; staged launches keep one workgroup per CU.
-#ifndef KVS_MFMA_OCC_NARROW
-#define KVS_MFMA_OCC_NARROW 2
+// Workgroups per CU the register budget is cut for.
+#ifndef KVS_MFMA_OCC
+#define KVS_MFMA_OCC 2
 #endif
-#ifndef KVS_MFMA_OCC_STAGED
-#define KVS_MFMA_OCC_STAGED 1
-#endif
-template <int RT, bool STAGED, int LIMBS>
-__global__ __launch_bounds__(kThreads, STAGED ? KVS_MFMA_OCC_STAGED : KVS_MFMA_OCC_NARROW)
+template <int RT, int LIMBS>
+__global__ __launch_bounds__(kThreads, KVS_MFMA_OCC)
 void mfma_kernel(AttendArgs a) {
-    static_assert(kChunks * RT * 64 * 16 <= kKTile, "P operands must fit in the K tile");
-    __shared__ MfmaSmem<RT, STAGED> sm;
+    // separate LDS arrays: a read of one is then ordered only after the LDS
+    // DMA into that one, not after the next page's DMA into another
+    __shared__ __attribute__((aligned(16))) uint8_t k_lds[kKTile];
+    __shared__ __attribute__((aligned(16))) uint8_t v_lds[kVTile];
+    __shared__ __attribute__((aligned(16))) uint8_t p_lds[kChunks * RT * 64 * 16];
+    __shared__ __attribute__((aligned(16))) uint32_t ksc[kWaves][kTokW * 2];
+    __shared__ float red_m[kWaves][16 * RT];
+    __shared__ float red_l[kWaves][16 * RT];
     // 1-D grid: the ring refill workgroups first (so that they start at
     // once), then the workers. A worker owns one (kv head, row tile) and walks
     // the segments slice, slice + n_slices, ...: its query operands are built
@@ -288,56 +253,13 @@ void mfma_kernel(AttendArgs a) {
     const int n = lane & 15, gq = lane >> 4;   // MFMA row/column index and lane group
     typedef int int4v __attribute__((ext_vector_type(4)));
 
-    auto issue_page = [&](int page) {
-        if constexpr (!STAGED) {
-            const uint8_t* rec = page_record(a.ps, page);
-            dma_k_tile(rec, g, sm.k, w, lane);
-            dma_v_tile(rec, g, a.n_kv_heads, sm.v, w, lane);
-        }
-    };
-    issue_page(scalar_load(&a.segs[slice].page0));
-    // staged operands of the current segment's first page, for kv head g
-    const uint8_t* stile = nullptr;
-    // staged operands are software-pipelined through registers: the K
-    // fragments (and block scales) of page p + 1 are loaded while page p
-    // computes P.V, and the V fragments of page p run a few 32-token chunks
-    // ahead of their use
-    const int64_t tile_step = (int64_t)a.n_kv_heads * kStagedTile;
-    half8_t kf[STAGED ? 4 : 1][kNB], vf[STAGED ? kChunks : 1][2];
-    u32x4 ks[STAGED ? 4 : 1][2];
-    constexpr int kKAhead = 2;   // token tiles of the next page loaded during P.V
-    auto load_k = [&](const uint8_t* pt, int tt0, int tt1) {
-        if constexpr (STAGED) {
-#pragma unroll
-            for (int tt = tt0; tt < tt1; ++tt) {
-#pragma unroll
-                for (int b = 0; b < kNB; ++b) kf[tt][b] = *(const half8_t*)(pt + staged_k_offset(4 * w + tt, b, lane));
-                const u32x4* sp = (const u32x4*)(pt + staged_scale_offset(kTokW * w + 16 * tt + 4 * gq));
-                ks[tt][0] = sp[0];
-                ks[tt][1] = sp[1];
-            }
-        }
-    };
-    constexpr int kVAhead = 4;   // V chunks in flight ahead of the one consumed
-    auto load_v = [&](const uint8_t* pt, int c) {
-        if constexpr (STAGED) {
-            vf[c][0] = *(const half8_t*)(pt + staged_v_offset(c, 2 * w, lane));
-            vf[c][1] = *(const half8_t*)(pt + staged_v_offset(c, 2 * w + 1, lane));
-        }
-    };
-
-    // a staged worker takes one segment: fetch its first K fragments before
-    // the query operands are built
-    if constexpr (STAGED) {
-        stile = a.staged + ((int64_t)staged_first_tile(a.segs, slice) * a.n_kv_heads + g) * kStagedTile;
-        load_k(stile, 0, kKAhead);
+    {
+        const uint8_t* rec = page_record(a.ps, scalar_load(&a.segs[slice].page0));
+        dma_k_tile(rec, g, k_lds, w, lane);
+        dma_v_tile(rec, g, a.n_kv_heads, v_lds, w, lane);
     }
 
-    // ---- this lane's query rows (one per row tile) and their visible prefix.
-    // Each row is scaled by a power of two that puts its largest magnitude in
-    // [2^14, 2^15), then split into f16 limbs: q' = hi + lo exactly enough
-    // (hi = f16(q'), lo = f16(q' - hi)); f16 queries need only hi. The row's
-    // score factor cq = scale * log2(e) / 2^shift undoes the scaling in f32.
+    // ---- this lane's query rows (one per row tile) and their visible prefix
     half8_t qop[RT][LIMBS][kNB];
     float cq[RT];
     int64_t lim[RT];
@@ -347,7 +269,6 @@ void mfma_kernel(AttendArgs a) {
         const int r = r0 + 16 * rt + n;
         qi_[rt] = r / G;
         h_[rt] = g * G + r % G;
-        float x[kNB][8];
         lim[rt] = 0;
         if (r < R) {
             lim[rt] = a.n_kv;
@@ -355,49 +276,8 @@ void mfma_kernel(AttendArgs a) {
                 const int64_t c = a.q_pos0 + qi_[rt] + 1;
                 lim[rt] = c < lim[rt] ? c : lim[rt];
             }
-            const int64_t off = ((int64_t)qi_[rt] * a.n_q_heads + h_[rt]) * kHeadDim + 8 * gq;
-#pragma unroll
-            for (int b = 0; b < kNB; ++b) {
-                if (a.q_f16) {
-                    const u32x4 raw = *(const u32x4*)((const _Float16*)a.q + off + kQK * b);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const half2_t hv = as_h2(raw[e]);
-                        x[b][2 * e] = (float)hv[0];
-                        x[b][2 * e + 1] = (float)hv[1];
-                    }
-                } else {
-                    const f32x4* qp = (const f32x4*)((const float*)a.q + off + kQK * b);
-                    const f32x4 u0 = qp[0], u1 = qp[1];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) { x[b][e] = u0[e]; x[b][4 + e] = u1[e]; }
-                }
-            }
-        } else {
-#pragma unroll
-            for (int b = 0; b < kNB; ++b)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[b][e] = 0.f;
         }
-        float amax = 0.f;
-#pragma unroll
-        for (int b = 0; b < kNB; ++b)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[b][e]));
-        amax = max_xor16(amax);   // over the row's four lanes n, n + 16, n + 32, n + 48
-        amax = max_xor32(amax);
-        const int ex = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) : 0;   // amax = m 2^ex, m in [0.5, 1)
-        const float up = __builtin_amdgcn_ldexpf(1.f, 15 - ex);
-        cq[rt] = a.scale_log2 * __builtin_amdgcn_ldexpf(1.f, ex - 15);
-#pragma unroll
-        for (int b = 0; b < kNB; ++b)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float y = x[b][e] * up;   // exact
-                const _Float16 hi = (_Float16)y;
-                qop[rt][0][b][e] = hi;
-                if constexpr (LIMBS == 2) qop[rt][LIMBS - 1][b][e] = (_Float16)(y - (float)hi);
-            }
+        query_operands<LIMBS>(a, qi_[rt], h_[rt], r < R, gq, qop[rt], cq[rt]);
     }
 
     const uint32_t m_nib = vconst(0x000F000Fu), magic = vconst(0x64006400u);
@@ -436,6 +316,10 @@ void mfma_kernel(AttendArgs a) {
             l_run[rt] = pr[kHeadDim + 1];
         }
     }
+    // the stored state is in registers before any page's LDS DMA is issued
+    // (a wait for it later would also wait for those DMAs): vmcnt(0), other
+    // counters untouched
+    __builtin_amdgcn_s_waitcnt(0x0F70);
 
     for (int pi = 0; pi < seg.npages; ++pi) {
         const int page = seg.page0 + pi;
@@ -453,77 +337,60 @@ void mfma_kernel(AttendArgs a) {
         // the worker's next page (this segment's next, else the first of its
         // next segment), whose tiles are fetched while this page finishes
         const uint8_t* next_rec = nullptr;
-        if constexpr (!STAGED) {
-            if (pi + 1 < seg.npages) next_rec = page_record(a.ps, page + 1);
-            else if (seg_i + a.n_slices < a.n_segs) next_rec = page_record(a.ps, scalar_load(&a.segs[seg_i + a.n_slices].page0));
-        }
+        if (pi + 1 < seg.npages) next_rec = page_record(a.ps, page + 1);
+        else if (seg_i + a.n_slices < a.n_segs) next_rec = page_record(a.ps, scalar_load(&a.segs[seg_i + a.n_slices].page0));
 
-        if constexpr (!STAGED) {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            lds_barrier();   // the page's tiles are in LDS for every wave
-        }
-        if constexpr (STAGED) {
-            load_k(stile + pi * tile_step, kKAhead, 4);
-#pragma unroll
-            for (int c = 0; c < kVAhead; ++c) load_v(stile + pi * tile_step, c);
-        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), known to the compiler's wait tracking
+        lds_barrier();   // the page's tiles are in LDS for every wave
 
         // ---- QK over this wave's 64 tokens, one product per quant block (the
-        // in-kernel conversion reads the next token tile's K bytes while
-        // converting the current one, and publishes each tile's block scales
-        // per token for the score lanes)
+        // conversion reads the next token tile's K bytes while converting the
+        // current one, and publishes each tile's block scales per token for
+        // the score lanes)
         f32x4 s[4][RT];
-        KRaw kr[2][STAGED ? 1 : kNB];
-        if constexpr (!STAGED) {
+        KRaw kr[2][kNB];
 #pragma unroll
-            for (int b = 0; b < kNB; ++b) kr[0][b] = k_raw(sm.k, kTokW * w + n, b, gq);
-        }
+        for (int b = 0; b < kNB; ++b) kr[0][b] = k_raw(k_lds, kTokW * w + n, b, gq);
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-            u32x4 sa, sb;
-            if constexpr (!STAGED) {
-                if (gq == 0) {
-                    const KRaw* k = kr[tt & 1];
-                    *(uint2*)&sm.ksc[w][(16 * tt + n) * 2] =
-                        make_uint2(k[0].db | (k[1].db << 16), k[2].db | (k[3].db << 16));
-                }
-                // written by this wave just above: the wave's own LDS
-                // operations complete in order
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                const u32x4* sp = (const u32x4*)&sm.ksc[w][(16 * tt + 4 * gq) * 2];
-                sa = sp[0];
-                sb = sp[1];
-                if (tt + 1 < 4) {
+            if (gq == 0) {
+                const KRaw* k = kr[tt & 1];
+                *(uint2*)&ksc[w][(16 * tt + n) * 2] = make_uint2(k[0].db | (k[1].db << 16), k[2].db | (k[3].db << 16));
+            }
+            // written by this wave just above: the wave's own LDS operations
+            // complete in order
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const u32x4* sp = (const u32x4*)&ksc[w][(16 * tt + 4 * gq) * 2];
+            const u32x4 sa = sp[0], sb = sp[1];
+            if (tt + 1 < 4) {
 #pragma unroll
-                    for (int b = 0; b < kNB; ++b) kr[(tt + 1) & 1][b] = k_raw(sm.k, kTokW * w + 16 * (tt + 1) + n, b, gq);
-                }
-            } else {
-                sa = ks[tt][0];
-                sb = ks[tt][1];
+                for (int b = 0; b < kNB; ++b) kr[(tt + 1) & 1][b] = k_raw(k_lds, kTokW * w + 16 * (tt + 1) + n, b, gq);
             }
             float dsc[4][kNB];
             tile_scales(sa, sb, dsc);
+            // all products of the tile first, so that no scaling waits on the
+            // matrix core's latency
+            f32x4 acc[RT][kNB];
 #pragma unroll
             for (int b = 0; b < kNB; ++b) {
-                half8_t kop;
-                if constexpr (STAGED)
-                    kop = kf[tt][b];
-                else
-                    kop = k_codes(kr[tt & 1][b], b);
+                const half8_t kop = k_codes(kr[tt & 1][b], b);
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
-                    f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[rt][0][b], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                    if constexpr (LIMBS == 2) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[rt][1][b], acc, 0, 0, 0);
-                    add_block(s[tt][rt], acc, dsc, b);
+                    acc[rt][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[rt][0][b], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    if constexpr (LIMBS == 2)
+                        acc[rt][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[rt][1][b], acc[rt][b], 0, 0, 0);
                 }
             }
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) s[tt][rt] *= cq[rt];
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int b = 0; b < kNB; ++b) add_block(s[tt][rt], acc[rt][b], dsc, b);
         }
 
-        // ---- mask, page maxima (lane value i is token 64 w + 16 tt + 4 gq + i)
+        // ---- mask, page maxima (lane value i is token 64 w + 16 tt + 4 gq + i);
+        // s holds the float32 products, cq * s the log2-unit scores (cq > 0)
         if (mask_page) {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
@@ -545,19 +412,16 @@ void mfma_kernel(AttendArgs a) {
                 for (int i = 0; i < 4; ++i) mx[rt] = fmaxf(mx[rt], s[tt][rt][i]);
             mx[rt] = max_xor16(mx[rt]);
             mx[rt] = max_xor32(mx[rt]);
-            if (gq == 0) sm.red_m[w][16 * rt + n] = mx[rt];
+            if (gq == 0) red_m[w][16 * rt + n] = mx[rt] * cq[rt];
         }
         lds_barrier();   // maxima published; every wave is done reading the K tile
-        if constexpr (!STAGED) {
-            if (next_rec) dma_k_tile(next_rec, g, sm.k, w, lane);   // lands during softmax and P.V
-        }
 
         float m_use[RT], alpha[RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            float pm = sm.red_m[0][16 * rt + n];
+            float pm = red_m[0][16 * rt + n];
 #pragma unroll
-            for (int ww = 1; ww < kWaves; ++ww) pm = fmaxf(pm, sm.red_m[ww][16 * rt + n]);
+            for (int ww = 1; ww < kWaves; ++ww) pm = fmaxf(pm, red_m[ww][16 * rt + n]);
             // pm > -inf + 8 holds for any finite pm: the first visible page sets m
             const bool grow = pm > m_run[rt] + kLazyMax;
             alpha[rt] = grow ? __builtin_amdgcn_exp2f(m_run[rt] - pm) : 1.f;   // 0 while the state is empty
@@ -566,7 +430,7 @@ void mfma_kernel(AttendArgs a) {
         }
         // ---- probabilities -> P operands in LDS (slot 8 gq + j of chunk c is
         // token 32 c + 4 gq + j for j < 4, 32 c + 12 + 4 gq + j otherwise)
-        uint8_t* pbuf = STAGED ? sm.k : sm_p(sm);
+        uint8_t* pbuf = p_lds;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             float ls = 0.f;
@@ -575,7 +439,7 @@ void mfma_kernel(AttendArgs a) {
                 half8_t pv;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const float p = __builtin_amdgcn_exp2f(s[2 * c2 + (j >> 2)][rt][j & 3] - m_use[rt]);
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * c2 + (j >> 2)][rt][j & 3], cq[rt], -m_use[rt]));
                     ls += p;
                     pv[j] = (_Float16)p;
                 }
@@ -583,16 +447,16 @@ void mfma_kernel(AttendArgs a) {
             }
             ls = add_xor16(ls);
             ls = add_xor32(ls);
-            if (gq == 0) sm.red_l[w][16 * rt + n] = ls;
+            if (gq == 0) red_l[w][16 * rt + n] = ls;
         }
         lds_barrier();   // P operands and row sums published
 
         bool rescale = false;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            float lp = sm.red_l[0][16 * rt + n];
+            float lp = red_l[0][16 * rt + n];
 #pragma unroll
-            for (int ww = 1; ww < kWaves; ++ww) lp += sm.red_l[ww][16 * rt + n];
+            for (int ww = 1; ww < kWaves; ++ww) lp += red_l[ww][16 * rt + n];
             l_run[rt] = l_run[rt] * alpha[rt] + lp;
             rescale |= alpha[rt] != 1.f;
         }
@@ -605,11 +469,7 @@ void mfma_kernel(AttendArgs a) {
 
         // ---- this page's V shift for block w; the accumulator moves to its
         // units when it changes (an exact power-of-two rescale)
-        int vsh;
-        if constexpr (STAGED)
-            vsh = scalar_load((const int32_t*)(stile + pi * tile_step + kStagedShift) + w);
-        else
-            vsh = v_shift_of(sm.v, w, valid, lane);
+        const int vsh = v_shift_of(v_lds, w, valid, lane);
         if (vsh != vsh_run) {
             const float f = __builtin_amdgcn_ldexpf(1.f, vsh_run - vsh);
 #pragma unroll
@@ -619,25 +479,15 @@ void mfma_kernel(AttendArgs a) {
             vsh_run = vsh;
         }
 
-        if constexpr (STAGED) {
-            if (pi + 1 < seg.npages) load_k(stile + (pi + 1) * tile_step, 0, kKAhead);
-        }
-
         // ---- P.V for channels 32 w .. 32 w + 31 (V quant block w)
         auto pv_page = [&](auto tail) {
             VRaw vr[2];
-            if constexpr (!STAGED) vr[0] = v_raw(sm.v, w, 0, gq, n);
+            vr[0] = v_raw(v_lds, w, 0, gq, n);
 #pragma unroll
             for (int c = 0; c < kChunks; ++c) {
                 half8_t vop[2];
-                if constexpr (STAGED) {
-                    vop[0] = vf[c][0];
-                    vop[1] = vf[c][1];
-                    if (c + kVAhead < kChunks) load_v(stile + pi * tile_step, c + kVAhead);
-                } else {
-                    if (c + 1 < kChunks) vr[(c + 1) & 1] = v_raw(sm.v, w, c + 1, gq, n);
-                    v_convert<decltype(tail)::value>(vr[c & 1], c, gq, valid, vsh, m_nib, magic, vop);
-                }
+                if (c + 1 < kChunks) vr[(c + 1) & 1] = v_raw(v_lds, w, c + 1, gq, n);
+                v_convert<decltype(tail)::value>(vr[c & 1], c, gq, valid, vsh, m_nib, magic, vop);
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
                     const half8_t pop = *(const half8_t*)(pbuf + ((c * RT + rt) * 64 + lane) * 16);
@@ -646,12 +496,15 @@ void mfma_kernel(AttendArgs a) {
                 }
             }
         };
-        if (!STAGED && tail_page) pv_page(std::true_type{});
+        if (tail_page) pv_page(std::true_type{});
         else pv_page(std::false_type{});
-        if constexpr (!STAGED) {
-            lds_barrier();   // every wave is done with this page's V tile and P operands
-            if (next_rec) dma_v_tile(next_rec, g, a.n_kv_heads, sm.v, w, lane);
-        }
+        // the next page's K tile (every wave is past QK) is fetched once this
+        // wave's V reads are done: the compiler orders an LDS read after any
+        // LDS DMA it cannot prove disjoint, so an earlier fetch would hold up
+        // the reads of the V tile
+        if (next_rec) dma_k_tile(next_rec, g, k_lds, w, lane);
+        lds_barrier();   // every wave is done with this page's V tile and P operands
+        if (next_rec) dma_v_tile(next_rec, g, a.n_kv_heads, v_lds, w, lane);
     }
 
     // ---- group state -> partial records (O back in absolute units)
@@ -672,7 +525,6 @@ void mfma_kernel(AttendArgs a) {
             pr[kHeadDim + 1] = l_run[rt];
         }
     }
-    if constexpr (STAGED) break;   // staged launches run one worker per segment
   }
 }
 
@@ -713,12 +565,12 @@ __global__ __launch_bounds__(kThreads) void stage_kernel(StageArgs a) {
 #pragma unroll
         for (int b = 0; b < kNB; ++b)
             *(half8_t*)(tile + staged_k_offset(4 * w + tt, b, lane)) = k_codes(k_raw(k_lds, kTokW * w + 16 * tt + n, b, gq), b);
-    // K block scales per token: thread t writes token t's four scales
+    // K block scales per token as float32 (exact): thread t writes token t's four
     {
         const uint8_t* row = k_lds + tid * kKRow;
-        const uint32_t d0 = *(const uint16_t*)row, d1 = *(const uint16_t*)(row + kKBlock);
-        const uint32_t d2 = *(const uint16_t*)(row + 2 * kKBlock), d3 = *(const uint16_t*)(row + 3 * kKBlock);
-        *(uint2*)(tile + staged_scale_offset(tid)) = make_uint2(d0 | (d1 << 16), d2 | (d3 << 16));
+        *(f32x4*)(tile + staged_scale_offset(tid)) =
+            f32x4{scale_f32(*(const uint16_t*)row), scale_f32(*(const uint16_t*)(row + kKBlock)),
+                  scale_f32(*(const uint16_t*)(row + 2 * kKBlock)), scale_f32(*(const uint16_t*)(row + 3 * kKBlock))};
     }
     // V: wave w converts block w (channel tiles 2 w, 2 w + 1), as the PV role does
     const int64_t vx = a.n_kv - (int64_t)page * kPageTokens;
@@ -747,39 +599,34 @@ int compute_units() {
     return cus[dev];
 }
 
-template <int RT, bool STAGED, int LIMBS>
+template <int RT, int LIMBS>
 hipError_t launch_rt(const AttendArgs& a, hipStream_t stream) {
     const int R = a.n_q * a.G;
     const int64_t units = (int64_t)a.n_kv_heads * ((R + 16 * RT - 1) / (16 * RT));
-    // workers: one per segment, unless the launch is unstaged with few (kv
-    // head, row tile) units and many segments (a verify block over a long
-    // cache): then about as many workers as the compute units hold at once,
-    // each taking an even slice of the segments
-    const int64_t target = (int64_t)compute_units() * 2;
+    // workers: one per segment, unless the launch has few (kv head, row tile)
+    // units and many segments (a verify block over a long cache): then about
+    // as many workers as the compute units hold at once, each taking an even
+    // slice of the segments
+    const int64_t target = (int64_t)compute_units() * KVS_MFMA_OCC;
     int64_t slices = a.n_segs;
-    if (!STAGED && units * a.n_segs > 2 * target && units * 8 <= target) slices = target / units;
+    if (units * a.n_segs > 2 * target && units * 8 <= target) slices = target / units;
     AttendArgs b = a;
     b.n_slices = (int32_t)slices;
     const int64_t n_work = slices * units;
     const int64_t blocks = ((copy_workgroups(a.copy) + 7) & ~7) + ((n_work + 7) & ~7);
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    return launch_kernel(mfma_kernel<RT, STAGED, LIMBS>, dim3((unsigned)blocks), dim3(kThreads), stream, b);
-}
-
-template <int RT, bool STAGED>
-hipError_t launch_limbs(const AttendArgs& a, hipStream_t stream) {
-    return a.q_f16 ? launch_rt<RT, STAGED, 1>(a, stream) : launch_rt<RT, STAGED, 2>(a, stream);
+    return launch_kernel(mfma_kernel<RT, LIMBS>, dim3((unsigned)blocks), dim3(kThreads), stream, b);
 }
 
 }  // namespace
 
-// Row tiles: in-kernel conversion takes 16-row tiles (with two query limbs,
-// 32-row tiles would not fit two workgroups' registers per compute unit);
-// staged launches take 32-row tiles.
+// 16-row tiles (with two query limbs, wider tiles would not fit two
+// workgroups' registers per compute unit); staged launches go to the prefill
+// kernel.
 hipError_t launch_mfma(const AttendArgs& a, hipStream_t stream) {
     if (a.n_segs <= 0 && copy_workgroups(a.copy) == 0) return hipSuccess;
-    if (a.staged) return launch_limbs<2, true>(a, stream);
-    return launch_limbs<1, false>(a, stream);
+    if (a.staged) return launch_prefill(a, stream);
+    return a.q_f16 ? launch_rt<1, 1>(a, stream) : launch_rt<1, 2>(a, stream);
 }
 
 bool mfma_stages(int rows) { return rows > 64; }

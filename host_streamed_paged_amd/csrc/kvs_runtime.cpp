@@ -428,6 +428,39 @@ int run_layer(kvs_pool* p, int32_t layer, hipStream_t stream, int32_t run_pages,
     // event cannot be waited on; an append on the captured stream is ordered)
     if (p->appended && !stream_capturing(stream) && hipStreamWaitEvent(stream, p->append_ev, 0) != hipSuccess)
         return mark(fail(KVS_ERR_HIP, "hipStreamWaitEvent(append) failed"));
+    // Staged launches (blocks wider than 64 rows) of segments [seg_b, seg_e)
+    // with no ring chunk to wait for: runs of whole segments, at most
+    // run_pages pages each, go to the compute lanes in turn, so that the runs
+    // (each staged into its lane's region, then attended) overlap one
+    // another; groups are whole, so no two lanes share one.
+    auto staged_runs_on_lanes = [&](int32_t seg_b, int32_t seg_e) -> int {
+        std::vector<std::pair<int32_t, int32_t>> runs;
+        for (int32_t i = seg_b; i < seg_e;) {
+            int32_t j = i, pages = 0;
+            while (j < seg_e && pages + ls.segs[j].npages <= run_pages) pages += ls.segs[j++].npages;
+            if (j == i) return mark(fail(KVS_ERR_INVALID_ARG, "internal: segment longer than a staging run"));
+            runs.emplace_back(i, j - i);
+            i = j;
+        }
+        const int n_l = (int)std::min<size_t>(kMaxLanes, runs.size());
+        if (n_l > 1) {
+            if (hipEventRecord(p->fork_ev, stream) != hipSuccess) return mark(fail(KVS_ERR_HIP, "lane fork failed"));
+            for (int k = 0; k < n_l; ++k)
+                if (hipStreamWaitEvent(p->lanes[k], p->fork_ev, 0) != hipSuccess) return mark(fail(KVS_ERR_HIP, "lane fork failed"));
+        }
+        for (size_t r = 0; r < runs.size(); ++r) {
+            const int lane = (int)(r % n_l);
+            int e = launch(n_l > 1 ? p->lanes[lane] : stream, lane, runs[r].first, runs[r].second, nullptr, 0,
+                           kvs::CopyJob{});
+            if (e) return mark(e);
+            p->st.kernels_launched++;
+        }
+        for (int k = 0; k < (n_l > 1 ? n_l : 0); ++k)
+            if (hipEventRecord(p->join_ev[k], p->lanes[k]) != hipSuccess || hipStreamWaitEvent(stream, p->join_ev[k], 0) != hipSuccess)
+                return mark(fail(KVS_ERR_HIP, "lane join failed"));
+        return KVS_OK;
+    };
+    const bool lanes_ok = run_pages > 0 && !stream_capturing(stream);
     if (p->cfg.flags & KVS_FLAG_ZERO_COPY) {
         // Zero-copy: streamed pages are read in place from the host records
         // (the launch's PageSource carries them), so there is no ring. With
@@ -443,43 +476,14 @@ int run_layer(kvs_pool* p, int32_t layer, hipStream_t stream, int32_t run_pages,
             p->st.kernels_launched++;
             return KVS_OK;
         };
-        if ((n_ch == 0 || ls.whole_groups) && run_pages > 0 && !stream_capturing(stream)) {
-            // Staged launches (blocks wider than 64 rows): runs of whole
-            // segments, at most run_pages pages each, go to the compute lanes
-            // in turn, so that one lane's staging reads over the link overlap
-            // another lane's matrix-core work. Each run is staged into its
-            // lane's region; groups are whole, so no two lanes share one.
-            std::vector<std::pair<int32_t, int32_t>> runs;
-            for (int32_t i = 0; i < n_segs;) {
-                int32_t j = i, pages = 0;
-                while (j < n_segs && pages + ls.segs[j].npages <= run_pages) pages += ls.segs[j++].npages;
-                if (j == i) return mark(fail(KVS_ERR_INVALID_ARG, "internal: segment longer than a staging run"));
-                runs.emplace_back(i, j - i);
-                i = j;
-            }
-            const int n_l = (int)std::min<size_t>(kMaxLanes, runs.size());
-            if (n_l > 1) {
-                if (hipEventRecord(p->fork_ev, stream) != hipSuccess) return mark(fail(KVS_ERR_HIP, "lane fork failed"));
-                for (int k = 0; k < n_l; ++k)
-                    if (hipStreamWaitEvent(p->lanes[k], p->fork_ev, 0) != hipSuccess) return mark(fail(KVS_ERR_HIP, "lane fork failed"));
-            }
-            for (size_t r = 0; r < runs.size(); ++r) {
-                const int lane = (int)(r % n_l);
-                int e = launch(n_l > 1 ? p->lanes[lane] : stream, lane, runs[r].first, runs[r].second, nullptr, 0,
-                               kvs::CopyJob{});
-                if (e) return mark(e);
-                p->st.kernels_launched++;
-            }
-            for (int k = 0; k < (n_l > 1 ? n_l : 0); ++k)
-                if (hipEventRecord(p->join_ev[k], p->lanes[k]) != hipSuccess || hipStreamWaitEvent(stream, p->join_ev[k], 0) != hipSuccess)
-                    return mark(fail(KVS_ERR_HIP, "lane join failed"));
-            return KVS_OK;
-        }
+        if ((n_ch == 0 || ls.whole_groups) && lanes_ok) return staged_runs_on_lanes(0, n_segs);
         if (n_ch == 0 || ls.whole_groups) return run(0, n_segs);
         int r = run(0, ls.res_nseg);
         for (int32_t c = 0; c < n_ch && !r; ++c) r = run(ls.chunks[c].seg0, ls.chunks[c].nseg);
         return r;
     }
+    // every page resident: staged runs on the lanes as above
+    if (n_ch == 0 && lanes_ok) return ls.res_nseg > 0 ? staged_runs_on_lanes(0, ls.res_nseg) : KVS_OK;
     const int n_lanes = lanes_for(R, n_ch, ls.whole_groups);
     auto slot_of = [&](int32_t c) { return (slot0 + c) % R; };
     auto do_launch = [&](int lane, int32_t seg0, int32_t nseg, int32_t c_compute, int32_t c_copy) -> int {
@@ -1068,7 +1072,11 @@ int attend_impl(kvs_pool* p, int32_t layer, const void* q, int32_t q_dtype, int3
         b.copy = cj;
         b.ps.ring_chunk = ring_chunk;
         b.ps.chunk_rank0 = rank0;
-        if (!staging || nseg == 0) {
+        if (nseg == 0) {   // a copy-only launch: the plain copy kernel, no compute footprint
+            hipError_t e = kvs::launch_copy(cj, st);
+            return e == hipSuccess ? KVS_OK : fail(KVS_ERR_HIP, "ring copy launch failed: %s", hipGetErrorString(e));
+        }
+        if (!staging) {
             b.segs = ls.dev_segs + seg0;
             b.n_segs = nseg;
             hipError_t e = timed_or_not(0, st, [&] { return kvs::launch_attend(b, st); });

@@ -427,10 +427,11 @@ int kvs_debug_export_pages(kvs_pool* pool, int32_t layer, void* dst, void* strea
  *     32 c + 4 j + s for slot s < 4 and 32 c + 12 + 4 j + s for s >= 4, each
  *     d x (nibble - 8) / 2^shift rounded once to binary16 (0 for uncached
  *     rows), shift = the block's V shift.
- *   K scales, bytes [131072, 133120): token t's four block scales at 8 t.
- *   V shifts, bytes [133120, 133136): int32 per block, 3 if a cached row's
+ *   K scales, bytes [131072, 135168): token t's four block scales as
+ *     float32 (exact) at 16 t.
+ *   V shifts, bytes [135168, 135184): int32 per block, 3 if a cached row's
  *     scale magnitude exceeds 8188 (binary16 bits above 0x6FFF), else 0. */
-#define KVS_STAGED_TILE_BYTES 133376
+#define KVS_STAGED_TILE_BYTES 135424
 int kvs_debug_stage(kvs_pool* pool, int32_t layer, int64_t n_kv, void* dst, void* stream);
 
 /* Kernel timing. With enable != 0, kvs_attend brackets every attention kernel

@@ -24,7 +24,7 @@ import torch
 import host_streamed_paged_amd as kvs
 from edge_records import edge_layer_records
 from kvs_case import mask_all, mask_random, normwise_error, say
-from oracle import attend, gather_kv
+from oracle import attend, f16_to_f64, gather_kv
 
 pytestmark = pytest.mark.gpu
 
@@ -179,7 +179,7 @@ _IDX = _staged_index()
 
 def decode_staged_tile(tile):
     """Staged tile bytes of one (page, kv head) -> (K codes as float [256, 128],
-    K scale bits uint16 [256, 4], V operands as float16 [256, 128], V shifts
+    K scales float32 [256, 4], V operands as float16 [256, 128], V shifts
     int32 [4]) in token-major order."""
     t = np.frombuffer(tile.tobytes(), dtype=np.uint8)
     k_tok, k_dim, v_tok, v_ch = _IDX
@@ -187,8 +187,8 @@ def decode_staged_tile(tile):
     kcodes[k_tok, k_dim] = t[:65536].view(np.float16).astype(np.float32)
     vv = np.full((256, 128), np.nan, np.float16)
     vv[v_tok, v_ch] = t[65536:131072].view(np.float16)
-    kscale = t[131072:133120].view(np.uint16).reshape(256, 4)
-    shifts = t[133120:133136].view(np.int32).copy()
+    kscale = t[131072:135168].view(np.float32).reshape(256, 4)
+    shifts = t[135168:135184].view(np.int32).copy()
     return kcodes, kscale, vv, shifts
 
 
@@ -198,10 +198,10 @@ def decode_staged_tile(tile):
 def test_staged_operands_bit_exact(k_regime, v_regime, zero_copy):
     """kvs_debug_stage converts every page with the staging code of the
     prefill path; streamed pages pass through the ring (or are read in place).
-    K operands are the codes exactly, the scales their bits; each V operand is
-    the round-to-nearest-even binary16 of d * (u - 8) / 2^shift computed
-    exactly from the oracle's float64 dequantization; the shift is 3 exactly
-    when a cached row's V scale magnitude exceeds 8188."""
+    K operands are the codes exactly, the scales their exact float32 values;
+    each V operand is the round-to-nearest-even binary16 of d * (u - 8) /
+    2^shift computed exactly from the oracle's float64 dequantization; the
+    shift is 3 exactly when a cached row's V scale magnitude exceeds 8188."""
     recs = regime_records(k_regime, v_regime, n_layers=1, seed=5)
     say(f"staged operands K={k_regime} V={v_regime} zero_copy={zero_copy}")
     c = EdgeCase(recs, max_q=1, resident_fn=mask_random(0.5, seed=8),
@@ -221,8 +221,9 @@ def test_staged_operands_bit_exact(k_regime, v_regime, zero_copy):
                 kb = rec[p, g * 256 * 136:(g + 1) * 256 * 136].reshape(256, 4, 34)
                 codes = kb[:, :, 2:].view(np.int8).reshape(256, 128).astype(np.float32)
                 sbits = kb[:, :, 0].astype(np.uint16) | (kb[:, :, 1].astype(np.uint16) << 8)
+                sval = f16_to_f64(sbits).astype(np.float32)   # exact
                 assert np.array_equal(kcodes[:valid], codes[:valid]), (p, g)
-                assert np.array_equal(kscale[:valid], sbits[:valid]), (p, g)
+                assert np.array_equal(kscale[:valid].view(np.uint32), sval[:valid].view(np.uint32)), (p, g)
                 vo = HKV * 256 * 136 + g * 256 * 72
                 vb = rec[p, vo:vo + 256 * 72].reshape(256, 4, 18)
                 vbits = (vb[:, :, 0].astype(np.uint16) | (vb[:, :, 1].astype(np.uint16) << 8)) & 0x7FFF

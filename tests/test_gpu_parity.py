@@ -137,12 +137,13 @@ def test_multi_row_parity(n_q, causal, qdt, scale):
         c.close()
 
 
-def test_staged_and_in_kernel_conversion_agree_bit_for_bit():
-    """A block wider than 64 rows per kv head stages every page once into f16
-    matrix-core operands; a narrower block converts in the kernel. Each row's
-    arithmetic is the same either way, so the first 10 query tokens of an
-    11-token block (66 rows, staged) equal a 10-token block (60 rows) bit for
-    bit."""
+def test_staged_and_in_kernel_paths_agree():
+    """A block wider than 64 rows per kv head runs the prefill kernel on
+    staged operands; a narrower one the matrix-core kernel converting each
+    page in the kernel. The first 10 query tokens of an 11-token block (66
+    rows, staged) and a 10-token block (60 rows) both match the oracle, and
+    each other to the same tolerance (their softmax runs over sub-blocks of
+    different sizes, so the bits may differ)."""
     c = small_case(mask_random(0.5, seed=11), n_layers=2, max_q=11, group=2)
     try:
         qs11 = [c.queries(l, 11, "f32") for l in range(c.L)]
@@ -151,9 +152,10 @@ def test_staged_and_in_kernel_conversion_agree_bit_for_bit():
         o11, l11 = c.attend_all(qs11, q_pos0=q_pos0, scale=1.0, causal=True)
         o10, l10 = c.attend_all(qs10, q_pos0=q_pos0, scale=1.0, causal=True)
         check(c, o11, l11, qs11, q_pos0=q_pos0, scale=1.0, causal=True)
+        check(c, o10, l10, qs10, q_pos0=q_pos0, scale=1.0, causal=True)
         for l in range(c.L):
-            assert np.array_equal(o11[l][:10], o10[l]), l
-            assert np.array_equal(l11[l][:10], l10[l]), l
+            assert normwise_error(o11[l][:10], o10[l].astype(np.float64)) <= TOL, l
+            assert float(np.max(np.abs(l11[l][:10] - l10[l]))) <= TOL, l
     finally:
         c.close()
 
