@@ -31,79 +31,74 @@ namespace {
 
 
 // ---------------------------------------------------------------------------
-// Split-K combine: one workgroup per output row (query token x head), 16
-// waves. Wave s folds groups s, s + 16, s + 32, ... into a running
-// log-sum-exp state, 8 groups per step so that 8 record loads are in flight;
-// lane i owns channels 2i and 2i + 1 (one 8-byte load per record, so a wave
-// reads a 512-byte record in one coalesced access). The 16 wave states are
-// then merged in wave order. The order depends only on the number of groups,
-// never on scheduling or residency.
+// Split-K combine: one workgroup per (output row, 16-channel slice), so that a
+// row's records are read by 8 compute units at once. Thread (gl, c) = (tid >>
+// 4, tid & 15) folds groups gl, gl + 16, gl + 32, ... of channel 16 s + c into
+// a running log-sum-exp state, 8 groups per step so that 8 record loads are in
+// flight; the 16 group lanes of a channel are then merged in lane order. The
+// order depends only on the number of groups, never on scheduling or
+// residency.
 // ---------------------------------------------------------------------------
-constexpr int kCombWaves = 16;
+constexpr int kCombSlices = kHeadDim / 16;
+constexpr int kCombLanes = 16;   // group lanes per channel
 constexpr int kCombBatch = 8;
-__global__ __launch_bounds__(64 * kCombWaves) void combine_kernel(const float* __restrict__ part, int32_t n_groups,
-                                                                  int32_t rows, float* __restrict__ out,
-                                                                  float* __restrict__ lse) {
-    __shared__ float2 so[kCombWaves][64];
-    __shared__ float sm_[kCombWaves], sl_[kCombWaves];
-    const int row = blockIdx.x;
-    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part, int32_t n_groups,
+                                                      int32_t rows, float* __restrict__ out,
+                                                      float* __restrict__ lse) {
+    __shared__ float so[kCombLanes][16];
+    __shared__ float sm_[kCombLanes], sl_[kCombLanes];
+    const int row = blockIdx.x, sl = blockIdx.y;
+    const int gl = threadIdx.x >> 4, c = threadIdx.x & 15;
     const int64_t gstride = (int64_t)rows * kPartStride;
     const float* p = part + (int64_t)row * kPartStride;
-    float M = -INFINITY, L = 0.f;
-    float2 O = make_float2(0.f, 0.f);
-    for (int g0 = wv; g0 < n_groups; g0 += kCombWaves * kCombBatch) {
-        float mg[kCombBatch], lg[kCombBatch];
-        float2 og[kCombBatch];
+    const int ch = 16 * sl + c;
+    float M = -INFINITY, L = 0.f, O = 0.f;
+    for (int g0 = gl; g0 < n_groups; g0 += kCombLanes * kCombBatch) {
+        float mg[kCombBatch], lg[kCombBatch], og[kCombBatch];
 #pragma unroll
         for (int k = 0; k < kCombBatch; ++k) {
-            const int gi = g0 + k * kCombWaves;
+            const int gi = g0 + k * kCombLanes;
             const bool ok = gi < n_groups;
             const float* q = p + (int64_t)(ok ? gi : 0) * gstride;
             const float2 ml = *(const float2*)(q + kHeadDim);
             mg[k] = ok ? ml.x : -INFINITY;
             lg[k] = ml.y;
-            og[k] = *(const float2*)(q + 2 * lane);
+            og[k] = q[ch];
         }
         float Mb = M;
 #pragma unroll
         for (int k = 0; k < kCombBatch; ++k) Mb = fmaxf(Mb, mg[k]);
         if (Mb == -INFINITY) continue;
-        const float sc = (M == -INFINITY) ? 0.f : exp2f(M - Mb);
+        const float sc = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - Mb);
         L *= sc;
-        O.x *= sc;
-        O.y *= sc;
+        O *= sc;
 #pragma unroll
         for (int k = 0; k < kCombBatch; ++k) {
-            const float w = (mg[k] == -INFINITY) ? 0.f : exp2f(mg[k] - Mb);
+            const float w = (mg[k] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mg[k] - Mb);
             L = fmaf(lg[k], w, L);
-            O.x = fmaf(og[k].x, w, O.x);
-            O.y = fmaf(og[k].y, w, O.y);
+            O = fmaf(og[k], w, O);
         }
         M = Mb;
     }
-    so[wv][lane] = O;
-    if (lane == 0) { sm_[wv] = M; sl_[wv] = L; }
+    so[gl][c] = O;
+    if (c == 0) { sm_[gl] = M; sl_[gl] = L; }
     __syncthreads();
-    if (wv == 0) {
+    if (gl == 0) {
         float Mt = sm_[0];
 #pragma unroll
-        for (int k = 1; k < kCombWaves; ++k) Mt = fmaxf(Mt, sm_[k]);
-        float2 ot = make_float2(0.f, 0.f);
-        float lt = 0.f;
+        for (int k = 1; k < kCombLanes; ++k) Mt = fmaxf(Mt, sm_[k]);
+        float ot = 0.f, lt = 0.f;
         if (Mt != -INFINITY) {
 #pragma unroll
-            for (int k = 0; k < kCombWaves; ++k) {
-                const float w = (sm_[k] == -INFINITY) ? 0.f : exp2f(sm_[k] - Mt);
-                ot.x = fmaf(so[k][lane].x, w, ot.x);
-                ot.y = fmaf(so[k][lane].y, w, ot.y);
+            for (int k = 0; k < kCombLanes; ++k) {
+                const float w = (sm_[k] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sm_[k] - Mt);
+                ot = fmaf(so[k][c], w, ot);
                 lt = fmaf(sl_[k], w, lt);
             }
         }
         const bool empty = Mt == -INFINITY;
-        *(float2*)(out + (int64_t)row * kHeadDim + 2 * lane) = empty ? make_float2(0.f, 0.f)
-                                                                      : make_float2(ot.x / lt, ot.y / lt);
-        if (lse && lane == 0) lse[row] = empty ? -INFINITY : (Mt + log2f(lt)) * 0.69314718055994530942f;
+        out[(int64_t)row * kHeadDim + ch] = empty ? 0.f : ot / lt;
+        if (lse && sl == 0 && c == 0) lse[row] = empty ? -INFINITY : (Mt + log2f(lt)) * 0.69314718055994530942f;
     }
 }
 
@@ -233,7 +228,7 @@ hipError_t launch_combine(const float* part, int32_t n_groups, int32_t n_q, int3
                           float* out, float* lse, hipStream_t stream) {
     const int rows = n_q * n_q_heads;
     if (rows <= 0) return hipSuccess;
-    return launch_kernel(combine_kernel, dim3(rows), dim3(64 * kCombWaves), stream, part, n_groups, rows, out, lse);
+    return launch_kernel(combine_kernel, dim3(rows, kCombSlices), dim3(256), stream, part, n_groups, rows, out, lse);
 }
 
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream) {
