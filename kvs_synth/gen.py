@@ -4,7 +4,8 @@ Page record format (one record per layer and 256-token page), the format the
 library documents in its public header:
 
     [ K tiles: for kv head g, for token row t, for block b: Q8_0 block (34 B) ]
-    [ V tiles: for kv head g, for token row t, for block b: Q4_0 block (18 B) ]
+    [ V tiles: for kv head g, for token row t, for block b: Q4_0 block (18 B)
+      or, for the q8_0-q8_0 pair, a Q8_0 block (34 B) ]
 
 A Q8_0 block is a little-endian binary16 scale followed by 32 two's-complement
 bytes; a Q4_0 block is a binary16 scale followed by 16 bytes whose low nibble
@@ -37,6 +38,11 @@ class KVGeometry:
     n_kv_heads: int
     head_dim: int
     page_tokens: int = 256
+    type_v: str = "q4_0"     # "q4_0" or "q8_0" (K is always Q8_0)
+
+    @property
+    def v_block(self) -> int:           # bytes of one V block
+        return Q8_0_BLOCK if self.type_v == "q8_0" else Q4_0_BLOCK
 
     @property
     def nb(self) -> int:
@@ -48,7 +54,7 @@ class KVGeometry:
 
     @property
     def v_tile_bytes(self) -> int:      # one kv head's V for one page
-        return self.page_tokens * self.nb * Q4_0_BLOCK
+        return self.page_tokens * self.nb * self.v_block
 
     @property
     def k_region_bytes(self) -> int:
@@ -105,13 +111,14 @@ def pack_page_records(kq: np.ndarray, vq: np.ndarray, geom: KVGeometry, n_pages:
                       tail: str = "poison") -> np.ndarray:
     """Pack token-major blocks into page records.
 
-    kq: uint8 [n_tok, Hkv, nb, 34]; vq: uint8 [n_tok, Hkv, nb, 18], tokens
-    starting at page `first_page`. Rows past n_tok in the last page are filled
+    kq: uint8 [n_tok, Hkv, nb, 34]; vq: uint8 [n_tok, Hkv, nb, geom.v_block],
+    tokens starting at page `first_page`. Rows past n_tok in the last page are filled
     with 0xFF ("poison": NaN scales) or zeros.
     """
     T, H, nb = geom.page_tokens, geom.n_kv_heads, geom.nb
     n_tok = kq.shape[0]
-    assert kq.shape == (n_tok, H, nb, Q8_0_BLOCK) and vq.shape == (n_tok, H, nb, Q4_0_BLOCK)
+    VB = geom.v_block
+    assert kq.shape == (n_tok, H, nb, Q8_0_BLOCK) and vq.shape == (n_tok, H, nb, VB)
     assert n_tok <= n_pages * T
     if out is None:
         out = np.empty((first_page + n_pages, geom.page_bytes), dtype=np.uint8)
@@ -119,10 +126,10 @@ def pack_page_records(kq: np.ndarray, vq: np.ndarray, geom: KVGeometry, n_pages:
     pad = n_pages * T - n_tok
     if pad:
         kq = np.concatenate([kq, np.full((pad, H, nb, Q8_0_BLOCK), fill, np.uint8)])
-        vq = np.concatenate([vq, np.full((pad, H, nb, Q4_0_BLOCK), fill, np.uint8)])
+        vq = np.concatenate([vq, np.full((pad, H, nb, VB), fill, np.uint8)])
     # [pages, T, H, nb, B] -> [pages, H, T, nb, B]
     k = kq.reshape(n_pages, T, H, nb, Q8_0_BLOCK).transpose(0, 2, 1, 3, 4).reshape(n_pages, -1)
-    v = vq.reshape(n_pages, T, H, nb, Q4_0_BLOCK).transpose(0, 2, 1, 3, 4).reshape(n_pages, -1)
+    v = vq.reshape(n_pages, T, H, nb, VB).transpose(0, 2, 1, 3, 4).reshape(n_pages, -1)
     dst = out[first_page:first_page + n_pages]
     dst[:, :geom.k_region_bytes] = k
     dst[:, geom.k_region_bytes:] = v
@@ -145,7 +152,7 @@ def layer_records(cid: int, layer: int, n_kv: int, geom: KVGeometry, tail: str =
         kx = rk.standard_normal((t1 - t0, H, d), dtype=np.float32)
         vx = rv.standard_normal((t1 - t0, H, d), dtype=np.float32)
         kq = quantize_q8_0(kx.reshape(t1 - t0, H, d // QK, QK))
-        vq = quantize_q4_0(vx.reshape(t1 - t0, H, d // QK, QK))
+        vq = (quantize_q8_0 if geom.type_v == "q8_0" else quantize_q4_0)(vx.reshape(t1 - t0, H, d // QK, QK))
         pack_page_records(kq, vq, geom, np_, out=out, first_page=p0, tail=tail)
     return out
 
@@ -159,8 +166,8 @@ def poison_tail(records: np.ndarray, n_kv: int, geom: KVGeometry) -> None:
         for g in range(geom.n_kv_heads):
             k0 = g * geom.k_tile_bytes + r * geom.nb * Q8_0_BLOCK
             records[p, k0:k0 + geom.nb * Q8_0_BLOCK] = POISON_BYTE
-            v0 = geom.k_region_bytes + g * geom.v_tile_bytes + r * geom.nb * Q4_0_BLOCK
-            records[p, v0:v0 + geom.nb * Q4_0_BLOCK] = POISON_BYTE
+            v0 = geom.k_region_bytes + g * geom.v_tile_bytes + r * geom.nb * geom.v_block
+            records[p, v0:v0 + geom.nb * geom.v_block] = POISON_BYTE
 
 
 def make_q(cid: int, layer: int, n_q: int, n_q_heads: int, head_dim: int, dtype: str) -> np.ndarray:

@@ -9,7 +9,8 @@ Definitions followed, all written out directly:
     holds element j in its low nibble and element j + 16 in its high nibble;
     element i is d * (nibble - 8). These are the ggml types the pages run
     their cache in (page 1, "What it is useful for"; page 2, "TLDR": the
-    q8_0-q4_0 pair).
+    q8_0-q4_0 pair). V may also be Q8_0 (page 3, "1. Correctness - PPL
+    parity": the q8_0-q8_0 pair); K is Q8_0 in both pairs.
   * A page is 256 consecutive token rows of one layer (page 2, "Dynamic draft
     eject": the keep threshold counts 256-token pages). Token t lives in page
     t // 256, row t % 256. Within a page record, the K tiles of every kv head
@@ -91,14 +92,19 @@ def page_bytes(n_kv_heads: int, head_dim: int, page_tokens: int = 256,
     return page_tokens * (row(type_k) + row(type_v))
 
 
+_DEQUANT_V = {"q4_0": dequant_q4_0, "q8_0": dequant_q8_0}
+
+
 def gather_kv(records: np.ndarray, n_kv_heads: int, head_dim: int, tok0: int, n_tok: int,
-              page_tokens: int = 256):
+              page_tokens: int = 256, type_v: str = "q4_0"):
     """Dequantized K and V (float64 [n_tok, Hkv, head_dim]) for tokens
-    tok0 .. tok0 + n_tok - 1, read from host page records uint8 [n_pages, page_bytes]."""
+    tok0 .. tok0 + n_tok - 1, read from host page records uint8 [n_pages, page_bytes].
+    K blocks are Q8_0; V blocks are `type_v` ("q4_0" or "q8_0")."""
     T, H = page_tokens, n_kv_heads
     nb = head_dim // QK
+    vbytes = _BLOCK[type_v][0]
     records = np.asarray(records, dtype=np.uint8)
-    assert records.shape[1] == page_bytes(H, head_dim, T)
+    assert records.shape[1] == page_bytes(H, head_dim, T, "q8_0", type_v)
     if n_tok == 0:
         z = np.zeros((0, H, head_dim))
         return z, z.copy()
@@ -107,10 +113,10 @@ def gather_kv(records: np.ndarray, n_kv_heads: int, head_dim: int, tok0: int, n_
     rec = records[p0:p1]
     kbytes = H * T * nb * Q8_0_BYTES
     kb = rec[:, :kbytes].reshape(p1 - p0, H, T, nb, Q8_0_BYTES)
-    vb = rec[:, kbytes:kbytes + H * T * nb * Q4_0_BYTES].reshape(p1 - p0, H, T, nb, Q4_0_BYTES)
+    vb = rec[:, kbytes:kbytes + H * T * nb * vbytes].reshape(p1 - p0, H, T, nb, vbytes)
     # [pages, H, T, nb, 32] -> [pages, T, H, nb*32] -> tokens
     k = dequant_q8_0(kb).transpose(0, 2, 1, 3, 4).reshape((p1 - p0) * T, H, head_dim)
-    v = dequant_q4_0(vb).transpose(0, 2, 1, 3, 4).reshape((p1 - p0) * T, H, head_dim)
+    v = _DEQUANT_V[type_v](vb).transpose(0, 2, 1, 3, 4).reshape((p1 - p0) * T, H, head_dim)
     lo = tok0 - p0 * T
     return k[lo:lo + n_tok], v[lo:lo + n_tok]
 
@@ -150,9 +156,10 @@ def attend(q, K, V, *, n_kv: int, scale: float, causal: bool, q_pos0: int,
 
 
 def attend_layer(records, q, *, n_kv: int, n_kv_heads: int, head_dim: int, scale: float,
-                 causal: bool, q_pos0: int, heads=None, page_tokens: int = 256):
+                 causal: bool, q_pos0: int, heads=None, page_tokens: int = 256,
+                 type_v: str = "q4_0"):
     """Gather the whole layer from its host records, then attend."""
-    K, V = gather_kv(records, n_kv_heads, head_dim, 0, n_kv, page_tokens)
+    K, V = gather_kv(records, n_kv_heads, head_dim, 0, n_kv, page_tokens, type_v)
     return attend(q, K, V, n_kv=n_kv, scale=scale, causal=causal, q_pos0=q_pos0, heads=heads)
 
 
@@ -224,20 +231,22 @@ def quantize_q4_0_block(x) -> np.ndarray:
 
 
 def append_rows(records, k_new, v_new, *, pos0: int, n_kv_heads: int, head_dim: int,
-                page_tokens: int = 256) -> np.ndarray:
+                page_tokens: int = 256, type_v: str = "q4_0") -> np.ndarray:
     """Copy of the page records (uint8 [n_pages, page_bytes]) with tokens
     pos0 .. pos0 + n - 1 replaced by the quantized rows of k_new / v_new
-    ([n, Hkv, head_dim]; float16 inputs are widened to float32 exactly).
-    Token t goes to page t // page_tokens, row t % page_tokens; every other
-    byte is kept."""
+    ([n, Hkv, head_dim]; float16 inputs are widened to float32 exactly), K
+    as Q8_0 and V as `type_v`. Token t goes to page t // page_tokens, row
+    t % page_tokens; every other byte is kept."""
     recs = np.array(records, dtype=np.uint8, copy=True)
     k_new = np.asarray(k_new).astype(np.float32)
     v_new = np.asarray(v_new).astype(np.float32)
     n, H, T = k_new.shape[0], n_kv_heads, page_tokens
     nb = head_dim // QK
     assert k_new.shape == (n, H, head_dim) and v_new.shape == (n, H, head_dim)
-    assert recs.shape[1] == page_bytes(H, head_dim, T)
-    k_tile, v_tile = T * nb * Q8_0_BYTES, T * nb * Q4_0_BYTES
+    assert recs.shape[1] == page_bytes(H, head_dim, T, "q8_0", type_v)
+    vbytes = _BLOCK[type_v][0]
+    quant_v = quantize_q8_0_block if type_v == "q8_0" else quantize_q4_0_block
+    k_tile, v_tile = T * nb * Q8_0_BYTES, T * nb * vbytes
     for i in range(n):
         t = pos0 + i
         page, r = t // T, t % T
@@ -246,6 +255,6 @@ def append_rows(records, k_new, v_new, *, pos0: int, n_kv_heads: int, head_dim: 
             for b in range(nb):
                 ko = g * k_tile + (r * nb + b) * Q8_0_BYTES
                 recs[page, ko:ko + Q8_0_BYTES] = quantize_q8_0_block(k_new[i, g, b * QK:(b + 1) * QK])
-                vo = H * k_tile + g * v_tile + (r * nb + b) * Q4_0_BYTES
-                recs[page, vo:vo + Q4_0_BYTES] = quantize_q4_0_block(v_new[i, g, b * QK:(b + 1) * QK])
+                vo = H * k_tile + g * v_tile + (r * nb + b) * vbytes
+                recs[page, vo:vo + vbytes] = quant_v(v_new[i, g, b * QK:(b + 1) * QK])
     return recs

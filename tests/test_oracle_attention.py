@@ -59,14 +59,58 @@ def test_gather_sentinels():
                     assert np.all(v[6:] == 8)
 
 
-def small_case(cid, H, Hq, d, n_kv, T, n_q=1, q_dtype="f32", layer=0):
-    geom = KVGeometry(H, d, T)
+def sentinel_records_q8v(n_pages, H, d, T):
+    """q8_0-q8_0 records: K blocks as in sentinel_records, V blocks Q8_0 with
+    d = -2 and codes (b, g, r - 128, p, r & 7, then 60 - j)."""
+    nb = d // 32
+    rec = np.zeros((n_pages, page_bytes(H, d, T, "q8_0", "q8_0")), np.uint8)
+    kbytes = H * T * nb * 34
+    for p in range(n_pages):
+        for g in range(H):
+            for r in range(T):
+                for b in range(nb):
+                    o = ((g * T + r) * nb + b) * 34
+                    rec[p, o:o + 2] = (0x00, 0x3C)
+                    codes = np.arange(32, dtype=np.int64) - 16
+                    codes[0], codes[1], codes[2], codes[3] = p, g, r - 128, b
+                    rec[p, o + 2:o + 34] = codes.astype(np.int8).view(np.uint8)
+                    o = kbytes + ((g * T + r) * nb + b) * 34
+                    rec[p, o:o + 2] = (0x00, 0xC0)                  # d = -2
+                    codes = 60 - np.arange(32, dtype=np.int64)
+                    codes[0], codes[1], codes[2], codes[3], codes[4] = b, g, r - 128, p, r & 7
+                    rec[p, o + 2:o + 34] = codes.astype(np.int8).view(np.uint8)
+    return rec
+
+
+def test_gather_sentinels_q8_0_v():
+    H, d, T = 3, 64, 16
+    rec = sentinel_records_q8v(4, H, d, T)
+    for tok0, n_tok in [(0, 64), (5, 30), (17, 1), (63, 1)]:
+        K, V = gather_kv(rec, H, d, tok0, n_tok, page_tokens=T, type_v="q8_0")
+        assert K.shape == (n_tok, H, d) and V.shape == (n_tok, H, d)
+        for i in range(n_tok):
+            p, r = divmod(tok0 + i, T)
+            for g in range(H):
+                for b in range(d // 32):
+                    k = K[i, g, 32 * b:32 * b + 32]
+                    assert (k[0], k[1], k[2], k[3]) == (p, g, r - 128, b)
+                    v = V[i, g, 32 * b:32 * b + 32] / -2.0
+                    assert (v[0], v[1], v[2], v[3], v[4]) == (b, g, r - 128, p, r & 7)
+                    assert np.array_equal(v[5:], 60 - np.arange(5, 32))
+    # the same bytes read with the other V type give a different layout: the
+    # record size alone already tells them apart
+    with pytest.raises(AssertionError):
+        gather_kv(rec, H, d, 0, 1, page_tokens=T, type_v="q4_0")
+
+
+def small_case(cid, H, Hq, d, n_kv, T, n_q=1, q_dtype="f32", layer=0, type_v="q4_0"):
+    geom = KVGeometry(H, d, T, type_v)
     rec = layer_records(cid, layer, n_kv, geom, tail="poison")
     q = make_q(cid, layer, n_q, Hq, d, q_dtype)
     return rec, q
 
 
-def brute_force(rec, q, n_kv, H, d, T, scale, causal, q_pos0):
+def brute_force(rec, q, n_kv, H, d, T, scale, causal, q_pos0, type_v="q4_0"):
     """50-digit attention straight from the record bytes, with explicit loops."""
     mpmath.mp.dps = 50
     nb = d // 32
@@ -85,6 +129,12 @@ def brute_force(rec, q, n_kv, H, d, T, scale, causal, q_pos0):
 
     def vval(t, g, c):
         p, r = divmod(t, T)
+        if type_v == "q8_0":
+            o = kbytes + ((g * T + r) * nb + c // 32) * 34
+            blk = rec[p, o:o + 34]
+            qv = int(blk[2 + c % 32])
+            qv = qv - 256 if qv >= 128 else qv
+            return f16(int(blk[0]), int(blk[1])) * qv
         o = kbytes + ((g * T + r) * nb + c // 32) * 18
         blk = rec[p, o:o + 18]
         j = c % 32
@@ -111,15 +161,16 @@ def brute_force(rec, q, n_kv, H, d, T, scale, causal, q_pos0):
     return out, lse
 
 
-@pytest.mark.parametrize("n_kv,causal,n_q,q_dtype", [(37, False, 1, "f32"), (40, True, 3, "f16")])
-def test_brute_force_tiny(n_kv, causal, n_q, q_dtype):
+@pytest.mark.parametrize("n_kv,causal,n_q,q_dtype,type_v", [(37, False, 1, "f32", "q4_0"), (40, True, 3, "f16", "q4_0"),
+                                                             (37, False, 1, "f32", "q8_0"), (40, True, 3, "f16", "q8_0")])
+def test_brute_force_tiny(n_kv, causal, n_q, q_dtype, type_v):
     H, Hq, d, T = 2, 6, 32, 16
-    rec, q = small_case(11, H, Hq, d, n_kv, T, n_q=n_q, q_dtype=q_dtype)
+    rec, q = small_case(11, H, Hq, d, n_kv, T, n_q=n_q, q_dtype=q_dtype, type_v=type_v)
     scale = 1.0 if q_dtype == "f32" else 1.0 / math.sqrt(d)
     q_pos0 = n_kv - n_q
     out, lse = attend_layer(rec, q, n_kv=n_kv, n_kv_heads=H, head_dim=d, scale=scale,
-                            causal=causal, q_pos0=q_pos0, page_tokens=T)
-    bo, bl = brute_force(rec, q, n_kv, H, d, T, scale, causal, q_pos0)
+                            causal=causal, q_pos0=q_pos0, page_tokens=T, type_v=type_v)
+    bo, bl = brute_force(rec, q, n_kv, H, d, T, scale, causal, q_pos0, type_v)
     assert np.max(np.abs(out - bo)) <= 1e-12 * max(1.0, np.max(np.abs(bo)))
     assert np.max(np.abs(lse - bl)) <= 1e-12 * max(1.0, np.max(np.abs(bl)))
 

@@ -165,3 +165,31 @@ def test_append_rows_lands_where_gather_reads_and_nowhere_else():
         assert pos0 <= tok < pos0 + n, (p, off, tok)
     assert page_bytes(H, D, T) == recs.shape[1]
     assert np.array_equal(out[2], recs[2])              # page 2 untouched
+
+
+def test_append_rows_q8_0_v_lands_where_gather_reads_and_nowhere_else():
+    H, D, T = 2, 64, 256
+    n_pages = 3
+    rng = np.random.default_rng(5)
+    pb = page_bytes(H, D, T, "q8_0", "q8_0")
+    assert pb == T * H * (D // 32) * (34 + 34)
+    recs = rng.integers(0, 256, (n_pages, pb), dtype=np.uint8)
+    pos0, n = 509, 6                                    # crosses from page 1 into page 2
+    k = rng.standard_normal((n, H, D)).astype(np.float32)
+    v = (8.0 * rng.standard_normal((n, H, D))).astype(np.float32)
+    out = append_rows(recs, k, v, pos0=pos0, n_kv_heads=H, head_dim=D, type_v="q8_0")
+    K, V = gather_kv(out, H, D, pos0, n, type_v="q8_0")
+    for i in range(n):
+        for g in range(H):
+            for b in range(D // 32):
+                kb = quantize_q8_0_block(k[i, g, 32 * b:32 * b + 32])
+                vb = quantize_q8_0_block(v[i, g, 32 * b:32 * b + 32])
+                assert np.array_equal(K[i, g, 32 * b:32 * b + 32], dequant_q8_0(kb))
+                assert np.array_equal(V[i, g, 32 * b:32 * b + 32], dequant_q8_0(vb))
+    blk = (D // 32) * 34                                # bytes of one token row of one head, K or V
+    kbytes = H * T * blk
+    for p, off in np.argwhere(out != recs):
+        row = ((off if off < kbytes else off - kbytes) % (T * blk)) // blk
+        tok = p * T + row
+        assert pos0 <= tok < pos0 + n, (p, off, tok)
+    assert np.array_equal(out[0], recs[0])              # page 0 untouched
