@@ -7,7 +7,8 @@
 // each new row is therefore written to the host record, and also to the
 // device copy when its page is resident. The block rule is ggml's reference
 // quantizer for Q8_0 and Q4_0 (the cache types named on page 1, "What it is
-// useful for"), in float32 with the scale stored as the nearest binary16:
+// useful for"; V is Q8_0 too in the q8_0-q8_0 pair of page 3, "1. Correctness
+// - PPL parity"), in float32 with the scale stored as the nearest binary16:
 //   Q8_0: d = max|x| / 127; code = round-half-away(x * (1 / d)), in [-127, 127];
 //   Q4_0: d = (first element of largest magnitude) / -8;
 //         nibble = min(15, trunc(x * (1 / d) + 8.5)).
@@ -19,8 +20,9 @@
 //
 // Work split: a workgroup of 256 threads takes 32 (token, kv head) rows;
 // thread 8 j + b quantizes K block b (b < 4) or V block b - 4 of row j into
-// LDS. The assembled rows (136 B of K, 72 B of V per head) then leave LDS as
-// 8-byte words: every row starts on an 8-byte boundary in the record.
+// LDS. The assembled rows (136 B of K, 72 B (Q4_0) or 136 B (Q8_0) of V per
+// head) then leave LDS as 8-byte words: every row starts on an 8-byte
+// boundary in the record.
 #include <hip/hip_runtime.h>
 #include <cstdint>
 #include <cmath>
@@ -31,8 +33,6 @@ namespace kvs {
 namespace {
 
 constexpr int kRowsPerWG = 32;
-constexpr int kRowBytes = kKRow + kVRow;     // 208 B: one head's K and V of one token
-constexpr int kRowWords = kRowBytes / 8;     // 26
 constexpr int kKWords = kKRow / 8;           // 17
 
 __device__ inline void load_block(const void* base, int f16, int64_t elem0, float (&x)[kQK]) {
@@ -113,7 +113,11 @@ __device__ inline void quant_q4_0(const float (&x)[kQK], uint8_t* dst) {
         h[1 + j / 2] = (uint16_t)((nib[j] | (nib[j + 16] << 4)) | ((nib[j + 1] | (nib[j + 17] << 4)) << 8));
 }
 
+template <typename VT>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+    constexpr int kRowBytes = kKRow + VT::kRow;   // one head's K and V of one token (208 / 272 B)
+    constexpr int kRowWords = kRowBytes / 8;
+    static_assert(kRowBytes % 8 == 0, "rows leave LDS as 8-byte words");
     __shared__ __attribute__((aligned(16))) uint8_t rows[kRowsPerWG][kRowBytes];
     const int t = threadIdx.x;
     const int64_t n_rows = (int64_t)a.n_tok * a.n_kv_heads;
@@ -128,8 +132,10 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
             load_block(part < 4 ? a.k : a.v, a.f16, row * kHeadDim + b * kQK, x);
             if (part < 4)
                 quant_q8_0(x, &rows[j][b * kKBlock]);
+            else if constexpr (VT::kQ8)
+                quant_q8_0(x, &rows[j][kKRow + b * VT::kBlock]);
             else
-                quant_q4_0(x, &rows[j][kKRow + b * kVBlock]);
+                quant_q4_0(x, &rows[j][kKRow + b * VT::kBlock]);
         }
     }
     __syncthreads();
@@ -142,7 +148,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
         const int64_t page = tok / kPageTokens;
         const int r = (int)(tok % kPageTokens);
         const int64_t off = w < kKWords ? (int64_t)g * kKTile + (int64_t)r * kKRow + 8 * w
-                                        : (int64_t)a.n_kv_heads * kKTile + (int64_t)g * kVTile + (int64_t)r * kVRow +
+                                        : (int64_t)a.n_kv_heads * kKTile + (int64_t)g * VT::kTile + (int64_t)r * VT::kRow +
                                               8 * (w - kKWords);
         const uint64_t val = *(const uint64_t*)&rows[j][8 * w];
         *(uint64_t*)(a.host + page * a.page_bytes + off) = val;
@@ -161,7 +167,8 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
     if (n_rows <= 0) return hipSuccess;
     const int64_t blocks = (n_rows + kRowsPerWG - 1) / kRowsPerWG;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    if (a.v_q8) hipLaunchKernelGGL(append_kernel<VQ8>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(append_kernel<VQ4>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -20,9 +20,10 @@
 //       log2 units (the softmax scale is folded into the query scale).
 //   PV  v_mfma_f32_16x16x32_f16: the slice's V rows are staged in the wave's
 //       LDS region, p * d_v is rounded to f16 into a per-wave buffer, and
-//       each V block's low and high nibbles form two 16-channel tiles of V^T
-//       as exact f16 (u - 8), multiplied against the rows' p * d_v over two
-//       32-token steps.
+//       each V block forms two 16-channel tiles of V^T as exact f16 (a Q4_0
+//       block's low and high nibbles, u - 8; a Q8_0 block's codes 0..15 and
+//       16..31), multiplied against the rows' p * d_v over two 32-token
+//       steps.
 //   The 4 slice partials of a page are merged into one page partial in a
 //   fixed order, and page partials are merged into the group state in page
 //   order: results do not depend on how pages are split into launches or
@@ -83,9 +84,9 @@ __device__ inline void wave_lds_sync() {
 // Every array that is read or written 16 bytes at a time (LDS DMA targets,
 // uint4 reads) sits on a 16-byte boundary; misaligned 128-bit LDS accesses
 // are split and stall.
-template <int R>
+template <int R, typename VT>
 struct DecodeSmem {
-    alignas(16) uint8_t v[kWaves][kSlice * kVRow];            // each wave's V rows (record layout)
+    alignas(16) uint8_t v[kWaves][kSlice * VT::kRow];         // each wave's V rows (record layout)
     alignas(16) uint32_t pp[kWaves][kNB][kPPStride];          // p * d_v as f16 pairs: [wave][block][pair * 8 + row]
     // slice partials (double-buffered by page parity); rows padded to 144
     // floats so that the rows' 16-byte stores fall on different LDS banks
@@ -93,9 +94,9 @@ struct DecodeSmem {
     float sm_[2][kWaves][R], sl_[2][kWaves][R];
 };
 
-template <int R>
+template <int R, typename VT>
 __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
-    __shared__ __attribute__((aligned(16))) DecodeSmem<R> sm;
+    __shared__ __attribute__((aligned(16))) DecodeSmem<R, VT> sm;
     if ((int)blockIdx.x >= a.n_segs) {   // ring refill workgroup
         copy_role(a.copy, ((int)blockIdx.x - a.n_segs) * (int)gridDim.y + (int)blockIdx.y);
         return;
@@ -144,19 +145,20 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
             kw[t][13] = *(const uint32_t*)(row + 3 * kKBlock - 2);
         }
     };
-    // 4608 bytes of V rows per slice: four coalesced 16-byte loads and one
-    // 8-byte load per lane
-    static_assert(kSlice * kVRow == 4 * 1024 + 512, "V slice size");
-    auto issue_v = [&](const uint8_t* rec, uint4 (&vr)[4], uint2& vr2) {
-        const uint8_t* vsrc = rec + (int64_t)a.n_kv_heads * kKTile + (int64_t)g * kVTile + kSlice * w * kVRow;
+    // V rows per slice, 4608 bytes (Q4_0) or 8704 (Q8_0): kVL coalesced
+    // 16-byte loads and one 8-byte load per lane
+    constexpr int kVL = kSlice * VT::kRow / 1024;
+    static_assert(kSlice * VT::kRow == kVL * 1024 + 512, "V slice size");
+    auto issue_v = [&](const uint8_t* rec, uint4 (&vr)[kVL], uint2& vr2) {
+        const uint8_t* vsrc = rec + (int64_t)a.n_kv_heads * kKTile + (int64_t)g * VT::kTile + kSlice * w * VT::kRow;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) vr[k] = *(const uint4*)(vsrc + 1024 * k + 16 * l);
-        vr2 = *(const uint2*)(vsrc + 4096 + 8 * l);
+        for (int k = 0; k < kVL; ++k) vr[k] = *(const uint4*)(vsrc + 1024 * k + 16 * l);
+        vr2 = *(const uint2*)(vsrc + 1024 * kVL + 8 * l);
     };
-    auto store_v = [&](const uint4 (&vr)[4], const uint2& vr2) {
+    auto store_v = [&](const uint4 (&vr)[kVL], const uint2& vr2) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) *(uint4*)(vt + 1024 * k + 16 * l) = vr[k];
-        *(uint2*)(vt + 4096 + 8 * l) = vr2;
+        for (int k = 0; k < kVL; ++k) *(uint4*)(vt + 1024 * k + 16 * l) = vr[k];
+        *(uint2*)(vt + 1024 * kVL + 8 * l) = vr2;
     };
 
     // ---- query rows -> 16-bit fixed point codes, built by every wave in the
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
     // address needs no read of the page table.
     const uint8_t* rec0 = page_record_of(a.ps, seg.page0, seg.flags >> kSegSrcShift);
     uint32_t kw[4][kKW];
-    uint4 vr[4];
+    uint4 vr[kVL];
     uint2 vr2;
     issue_k(rec0, kw);
     issue_v(rec0, vr, vr2);
@@ -375,7 +377,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
         {
             const float dep = lsum[0] + lsum[3];
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
+            for (int k = 0; k < kVL; ++k)
                 asm volatile("" : "+v"(vr[k].x), "+v"(vr[k].y), "+v"(vr[k].z), "+v"(vr[k].w) : "v"(dep));
             asm volatile("" : "+v"(vr2.x), "+v"(vr2.y) : "v"(dep));
         }
@@ -397,7 +399,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
                 const int tok = 16 * t + n;
 #pragma unroll
                 for (int blk = 0; blk < kNB; ++blk) {
-                    const float d = scale_f32(*(const uint16_t*)(vt + tok * kVRow + blk * kVBlock));
+                    const float d = scale_f32(*(const uint16_t*)(vt + tok * VT::kRow + blk * VT::kBlock));
                     dv[t][blk] = tok < valid ? d : 0.f;   // rows past the cache may hold NaN scales
                 }
             }
@@ -432,32 +434,41 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
         wave_lds_sync();
 
         // ---- P.V over the slice on the matrix cores: O^T = V^T . P' per V
-        // block, one 16-channel tile for the low nibbles and one for the high,
-        // in two 32-token steps (v_mfma_f32_16x16x32_f16). Lane (n, kg) =
-        // (l & 15, l >> 4) holds operand slots 8 kg .. 8 kg + 7; slots 8 kg + 2 i
-        // and 8 kg + 2 i + 1 of step ks are tokens t = 32 ks + 4 kg + i and
-        // t + 16, the pair one dword of the p * d_v buffer holds. A: channel n
-        // of the tile (V nibbles as exact f16 (u - 8), high nibbles 16 (u - 8));
-        // B: query row n; C: channels 4 kg .. 4 kg + 3 of the tile, row n. B
-        // columns of rows past R hold stale buffer words and only reach output
-        // columns that are dropped.
+        // block, two 16-channel tiles (Q4_0: the low nibbles and the high
+        // ones; Q8_0: elements 0..15 and 16..31 of the block), in two 32-token
+        // steps (v_mfma_f32_16x16x32_f16). Lane (n, kg) = (l & 15, l >> 4)
+        // holds operand slots 8 kg .. 8 kg + 7; slots 8 kg + 2 i and
+        // 8 kg + 2 i + 1 of step ks are tokens t = 32 ks + 4 kg + i and t + 16,
+        // the pair one dword of the p * d_v buffer holds. A: channel n of the
+        // tile as exact f16 (Q4_0: u - 8, high nibbles 16 (u - 8); Q8_0: the
+        // code); B: query row n; C: channels 4 kg .. 4 kg + 3 of the tile, row
+        // n. B columns of rows past R hold stale buffer words and only reach
+        // output columns that are dropped.
         {
             const half2_t off_lo = {(_Float16)1032.f, (_Float16)1032.f};
             const half2_t off_hi = {(_Float16)1152.f, (_Float16)1152.f};
+            const half2_t one = {(_Float16)1.f, (_Float16)1.f}, m1152 = {(_Float16)-1152.f, (_Float16)-1152.f};
             const uint32_t m_lo = vconst(0x000F000Fu), m_hi = vconst(0x00F000F0u), magic = vconst(0x64006400u);
 #pragma unroll
             for (int vb = 0; vb < kNB; ++vb) {
                 f32x4 clo = {0.f, 0.f, 0.f, 0.f}, chi = clo;
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
-                    const uint8_t* vsrc = vt + (32 * ks + 4 * kg) * kVRow + vb * kVBlock + 2 + n;
+                    const uint8_t* vsrc = vt + (32 * ks + 4 * kg) * VT::kRow + vb * VT::kBlock + 2 + n;
                     const uint32_t* psrc = ppw + vb * kPPStride + (16 * ks + 4 * kg) * 8 + n;
                     u32x4 alo, ahi, bp;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const uint32_t x = __builtin_amdgcn_perm((uint32_t)vsrc[(i + 16) * kVRow], (uint32_t)vsrc[i * kVRow], 0x0c040c00u);
-                        alo[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, (x & m_lo) | magic) - off_lo);  // u - 8
-                        ahi[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, (x & m_hi) | magic) - off_hi);  // 16 (u - 8)
+                        if constexpr (VT::kQ8) {
+                            const uint32_t xl = __builtin_amdgcn_perm((uint32_t)vsrc[(i + 16) * VT::kRow], (uint32_t)vsrc[i * VT::kRow], 0x0c040c00u);
+                            const uint32_t xh = __builtin_amdgcn_perm((uint32_t)vsrc[(i + 16) * VT::kRow + 16], (uint32_t)vsrc[i * VT::kRow + 16], 0x0c040c00u);
+                            alo[i] = as_u(q8_pair_f16(xl, one, m1152));   // code, element n
+                            ahi[i] = as_u(q8_pair_f16(xh, one, m1152));   // code, element 16 + n
+                        } else {
+                            const uint32_t x = __builtin_amdgcn_perm((uint32_t)vsrc[(i + 16) * VT::kRow], (uint32_t)vsrc[i * VT::kRow], 0x0c040c00u);
+                            alo[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, (x & m_lo) | magic) - off_lo);  // u - 8
+                            ahi[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, (x & m_hi) | magic) - off_hi);  // 16 (u - 8)
+                        }
                         bp[i] = psrc[8 * i];
                     }
                     const half8_t pb = __builtin_bit_cast(half8_t, bp);
@@ -469,7 +480,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
                 if (n < R) {
                     float* dst = &sm.sacc[par][w][n < R ? n : 0][32 * vb + 4 * kg];
                     *(f32x4*)dst = clo * vunit[vb];
-                    *(f32x4*)(dst + 16) = chi * (vunit[vb] * 0.0625f);   // high nibbles carried 16 (u - 8)
+                    // Q4_0 high nibbles carried 16 (u - 8)
+                    *(f32x4*)(dst + 16) = chi * (VT::kQ8 ? vunit[vb] : vunit[vb] * 0.0625f);
                 }
             }
         }
@@ -527,7 +539,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
 template <int R>
 hipError_t launch_r(const AttendArgs& a, hipStream_t stream) {
     const int cx = (copy_workgroups(a.copy) + a.n_kv_heads - 1) / a.n_kv_heads;
-    return launch_kernel(decode_kernel<R>, dim3(a.n_segs + cx, a.n_kv_heads), dim3(kThreads), stream, a);
+    if (a.v_q8) return launch_kernel(decode_kernel<R, VQ8>, dim3(a.n_segs + cx, a.n_kv_heads), dim3(kThreads), stream, a);
+    return launch_kernel(decode_kernel<R, VQ4>, dim3(a.n_segs + cx, a.n_kv_heads), dim3(kThreads), stream, a);
 }
 
 }  // namespace

@@ -104,6 +104,16 @@ __device__ inline half2_t q4_nibbles_f16(uint32_t biased, half2_t c, half2_t min
     return __builtin_elementwise_fma(as_h2(biased), c, minus_1032c);
 }
 
+// Two Q8_0 codes, the bytes of the low and high halves of `pair` (bits 0..7
+// and 16..23, the other bits zero), as the exact binary16 values code * c
+// for c = 1 or 2^-7 passed as {c, c} with minus_1152c = {-1152 c, -1152 c}:
+// the xor flips each code's sign bit (u = code + 128) and sets the 0x64
+// exponent byte, giving 1024 + u, and (1024 + u) c - 1152 c = code * c is
+// exact.
+__device__ inline half2_t q8_pair_f16(uint32_t pair, half2_t c, half2_t minus_1152c) {
+    return __builtin_elementwise_fma(as_h2(pair ^ 0x64806480u), c, minus_1152c);
+}
+
 // Query operands of the matrix-core kernels (16x16x32 f16 tiles, the query
 // as the B operand): this lane's 8 elements [32 b + 8 gq, +8) of each block b
 // of query row (token qi, head h), zero if !valid. The row is scaled by the

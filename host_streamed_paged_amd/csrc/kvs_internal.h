@@ -14,12 +14,26 @@ constexpr int kHeadDim = 128;                // d
 constexpr int kQK = 32;                      // values per quant block
 constexpr int kNB = kHeadDim / kQK;          // blocks per head row (4)
 constexpr int kKBlock = 34;                  // Q8_0: f16 scale + 32 int8
-constexpr int kVBlock = 18;                  // Q4_0: f16 scale + 16 nibble bytes
 constexpr int kKRow = kNB * kKBlock;         // 136 B: one head's K for one token
-constexpr int kVRow = kNB * kVBlock;         // 72 B
 constexpr int kKTile = kPageTokens * kKRow;  // 34816 B: one head's K for one page
-constexpr int kVTile = kPageTokens * kVRow;  // 18432 B
 constexpr int kPartStride = kHeadDim + 2;    // partial record: acc[128], m (log2 units), l
+
+// V block type of a page record. K is Q8_0 in both pairs the library builds:
+// V is Q4_0 (f16 scale + 16 nibble bytes, the q8_0-q4_0 pair of page 2,
+// "TLDR - recommended setup") or Q8_0 (the q8_0-q8_0 pair of page 3,
+// "1. Correctness - PPL parity"). Kernels that read V are instantiated per
+// type; the launch arguments carry the type as v_q8.
+template <bool Q8>
+struct VType {
+    static constexpr bool kQ8 = Q8;
+    static constexpr int kBlock = Q8 ? 34 : 18;              // bytes per 32-value block
+    static constexpr int kRow = kNB * kBlock;                 // one head's V for one token (136 / 72 B)
+    static constexpr int kTile = kPageTokens * kRow;          // one head's V for one page (34816 / 18432 B)
+};
+using VQ4 = VType<false>;
+using VQ8 = VType<true>;
+// Page record bytes per kv head.
+__host__ __device__ constexpr int head_record_bytes(bool v_q8) { return kKTile + (v_q8 ? VQ8::kTile : VQ4::kTile); }
 // Staged matrix-core operands of one (page, kv head): the f16 K and V^T
 // operands in fragment order, the K block scales per token as float32, and
 // the V scaling exponent of each 32-channel block (padded to keep tiles
@@ -134,6 +148,7 @@ struct AttendArgs {
     float* part;          // [n_groups][n_q][Hq][kPartStride]
     const uint8_t* staged; // staged operands of this launch's pages (null: convert in the kernel)
     int32_t n_slices;     // matrix-core kernel: segment slices per (kv head, row tile), set at launch
+    int32_t v_q8;         // V blocks are Q8_0 (else Q4_0)
 };
 
 // Conversion of a launch's pages into staged operands (kvs_mfma.hip).
@@ -147,6 +162,7 @@ struct StageArgs {
     int32_t n_pages;      // pages of the launch's segments
     uint8_t* staged;      // [pages][n_kv_heads][kStagedTile]
     int32_t by_page;      // 1: page p goes to tile p (a probe of a whole layer), 0: the x-th page to tile x
+    int32_t v_q8;         // V blocks are Q8_0 (else Q4_0)
 };
 
 // The first `first` pages of a copy job, or the rest (ring slots follow).
@@ -173,6 +189,7 @@ struct GatherArgs {
     int64_t n_tok;
     float* k_out;         // [n_tok, Hkv, 128]
     float* v_out;
+    int32_t v_q8;         // V blocks are Q8_0 (else Q4_0)
 };
 
 // Raw record export probe: the bytes of each page as the kernels read them.
@@ -197,6 +214,7 @@ struct AppendArgs {
     const int32_t* src;       // the layer's device page table (slot >= 0 when resident)
     uint8_t* slots;           // resident slots
     uint8_t* host;            // the layer's host records (pinned, device-visible)
+    int32_t v_q8;             // V blocks are Q8_0 (else Q4_0)
 };
 
 // Kernel timing: when the host sets a start/stop event pair here, the next

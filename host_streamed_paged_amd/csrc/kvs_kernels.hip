@@ -109,6 +109,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 // scale (exact: an 8-bit by 11-bit product). One workgroup per (segment, kv
 // head); thread = token row of the page.
 // ---------------------------------------------------------------------------
+template <typename VT>
 __global__ __launch_bounds__(kPageTokens) void gather_kernel(GatherArgs a) {
     if ((int)blockIdx.x >= a.n_segs) {   // ring refill workgroup
         copy_role(a.copy, ((int)blockIdx.x - a.n_segs) * (int)gridDim.y + (int)blockIdx.y);
@@ -117,13 +118,14 @@ __global__ __launch_bounds__(kPageTokens) void gather_kernel(GatherArgs a) {
     const Seg seg = a.segs[blockIdx.x];
     const int g = blockIdx.y, t = threadIdx.x;
     const half2_t one = {(_Float16)1.f, (_Float16)1.f}, m1032 = {(_Float16)-1032.f, (_Float16)-1032.f};
+    const half2_t m1152 = {(_Float16)-1152.f, (_Float16)-1152.f};
     for (int pi = 0; pi < seg.npages; ++pi) {
         const int page = seg.page0 + pi;
         const int64_t tok = (int64_t)page * kPageTokens + t;
         if (tok < a.tok0 || tok >= a.tok0 + a.n_tok) continue;
         const uint8_t* rec = page_ptr(a.ps, page);
         const uint8_t* kr = rec + (int64_t)g * kKTile + t * kKRow;
-        const uint8_t* vr = rec + (int64_t)a.n_kv_heads * kKTile + (int64_t)g * kVTile + t * kVRow;
+        const uint8_t* vr = rec + (int64_t)a.n_kv_heads * kKTile + (int64_t)g * VT::kTile + t * VT::kRow;
         float* ko = a.k_out + ((tok - a.tok0) * a.n_kv_heads + g) * kHeadDim;
         float* vo = a.v_out + ((tok - a.tok0) * a.n_kv_heads + g) * kHeadDim;
         for (int b = 0; b < kNB; ++b) {
@@ -136,8 +138,17 @@ __global__ __launch_bounds__(kPageTokens) void gather_kernel(GatherArgs a) {
                 const half8_t c = q8_codes_f16(x0, x1);
                 for (int e = 0; e < 8; ++e) ko[b * kQK + 8 * j + e] = (float)c[e] * dk;
             }
-            const uint16_t* vb = (const uint16_t*)(vr + b * kVBlock);
+            const uint16_t* vb = (const uint16_t*)(vr + b * VT::kBlock);
             const float dv = scale_f32(vb[0]);
+            if constexpr (VT::kQ8) {
+                for (int j = 0; j < 16; ++j) {   // bytes 2 j, 2 j + 1: elements 2 j, 2 j + 1
+                    const uint32_t w2 = vb[1 + j];
+                    const half2_t c = q8_pair_f16((w2 & 0xFFu) | ((w2 >> 8) << 16), one, m1152);
+                    vo[b * kQK + 2 * j] = (float)c[0] * dv;
+                    vo[b * kQK + 2 * j + 1] = (float)c[1] * dv;
+                }
+                continue;
+            }
             for (int j = 0; j < 8; ++j) {
                 // bytes 2 j and 2 j + 1: elements 2 j, 2 j + 1 (low nibbles) and
                 // 2 j + 16, 2 j + 17 (high nibbles)
@@ -234,7 +245,8 @@ hipError_t launch_combine(const float* part, int32_t n_groups, int32_t n_q, int3
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream) {
     if (a.n_segs <= 0 && copy_workgroups(a.copy) == 0) return hipSuccess;
     const int cx = (copy_workgroups(a.copy) + a.n_kv_heads - 1) / a.n_kv_heads;
-    hipLaunchKernelGGL(gather_kernel, dim3(a.n_segs + cx, a.n_kv_heads), dim3(kPageTokens), 0, stream, a);
+    if (a.v_q8) hipLaunchKernelGGL(gather_kernel<VQ8>, dim3(a.n_segs + cx, a.n_kv_heads), dim3(kPageTokens), 0, stream, a);
+    else hipLaunchKernelGGL(gather_kernel<VQ4>, dim3(a.n_segs + cx, a.n_kv_heads), dim3(kPageTokens), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -6,8 +6,9 @@
 // One workgroup = one segment (run of pages of one split-K group) x one kv
 // head x a tile of 16 RT query rows (row = query token x head of the GQA
 // group). 4 waves. Every page is staged whole in LDS by LDS DMA (K tile
-// 34816 B, V tile 18432 B, record layout); the next page's K tile is fetched
-// once every wave is past QK, its V tile once P.V is done. Then:
+// 34816 B, V tile 18432 B for Q4_0 V or 34816 B for Q8_0 V, record layout);
+// the next page's K and V tiles are fetched once the wave's P.V reads are
+// done. Then:
 //   QK   wave w owns tokens [64 w, 64 w + 64) of the page:
 //        A_b^T (16 tokens x 16 rows) = K_b (16 x 32) . Q_b^T (32 x 16) for each
 //        32-wide quant block b, with K_b the block's int8 codes as exact f16
@@ -23,10 +24,12 @@
 //        producing wave; it is published to LDS for the channel owners.
 //   PV   wave w owns channels [32 w, 32 w + 32) (= V quant block w):
 //        O^T (16 channels x 16 rows) += V^T (16 x 32 tokens) . P^T (32 x 16).
-//        The V operand is d * (u - 8) rounded once to f16. A page whose block
-//        w holds a scale above 8188 (where d * (u - 8) could exceed the f16
-//        range) takes d * (u - 8) / 8 instead; the wave keeps its accumulator
-//        in units of 2^shift and rescales it exactly when the shift changes.
+//        The V operand is d * (u - 8) (Q4_0) or d * code (Q8_0) rounded once
+//        to f16. A page whose block w holds a scale above 8188 (Q4_0) or
+//        511.75 (Q8_0), where the product could exceed the f16 range, takes
+//        it divided by 8 (Q4_0) or 128 (Q8_0) instead; the wave keeps its
+//        accumulator in units of 2^shift and rescales it exactly when the
+//        shift changes.
 // The running state (m, l, O) is updated once per page in page order from
 // state and page data alone, so results do not depend on how pages are split
 // into launches or which pages are resident.
@@ -75,7 +78,7 @@ constexpr int kVShift = 3;
 // page's LDS DMA then competes with the QK reads of the current one.)
 
 // Stage one (page, kv head) tile of a page record into LDS by LDS DMA:
-// wave-sized pieces of 1 KB, 34 for K and 18 for V.
+// wave-sized pieces of 1 KB, 34 for K and 18 (Q4_0) or 34 (Q8_0) for V.
 __device__ inline void dma_k_tile(const uint8_t* rec, int g, uint8_t* k_lds, int w, int lane) {
     const uint8_t* kt = rec + (int64_t)g * kKTile;
 #pragma unroll
@@ -84,12 +87,14 @@ __device__ inline void dma_k_tile(const uint8_t* rec, int g, uint8_t* k_lds, int
         if (piece < kKTile / 1024) dma16(kt + piece * 1024 + lane * 16, k_lds + piece * 1024);
     }
 }
+template <typename VT>
 __device__ inline void dma_v_tile(const uint8_t* rec, int g, int n_kv_heads, uint8_t* v_lds, int w, int lane) {
-    const uint8_t* vt = rec + (int64_t)n_kv_heads * kKTile + (int64_t)g * kVTile;
+    static_assert(VT::kTile % 1024 == 0, "V tile in 1 KB pieces");
+    const uint8_t* vt = rec + (int64_t)n_kv_heads * kKTile + (int64_t)g * VT::kTile;
 #pragma unroll
-    for (int k = 0; k < 5; ++k) {
+    for (int k = 0; k < (VT::kTile / 1024 + 3) / 4; ++k) {
         const int piece = w + 4 * k;
-        if (piece < kVTile / 1024) dma16(vt + piece * 1024 + lane * 16, v_lds + piece * 1024);
+        if (piece < VT::kTile / 1024) dma16(vt + piece * 1024 + lane * 16, v_lds + piece * 1024);
     }
 }
 
@@ -149,49 +154,62 @@ __device__ inline void add_block(f32x4& s, const f32x4& a, const float (&d)[4][k
     }
 }
 
-// V shift of quant block b of a page (V tile in LDS, record layout): kVShift
-// if a cached row's scale magnitude exceeds 8188, else 0. Rows at or past
-// `valid` are not cached and may hold any bytes. Wave-uniform.
+// V shift of quant block b of a page (V tile in LDS, record layout): for
+// Q4_0, kVShift if a cached row's scale magnitude exceeds 8188, else 0; for
+// Q8_0 (|code| <= 128), kVShift8 if one exceeds 511.75 (bits 0x5FFF), so
+// that d * code / 2^shift stays within 65504. Rows at or past `valid` are not
+// cached and may hold any bytes. Wave-uniform.
+constexpr uint32_t kVBigBits8 = 0x5FFFu;
+constexpr int kVShift8 = 7;
+template <typename VT>
 __device__ inline int v_shift_of(const uint8_t* v_lds, int b, int valid, int lane) {
     uint32_t mx = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int t = lane + 64 * j;
-        const uint32_t bits = *(const uint16_t*)(v_lds + t * kVRow + b * kVBlock) & 0x7FFFu;
+        const uint32_t bits = *(const uint16_t*)(v_lds + t * VT::kRow + b * VT::kBlock) & 0x7FFFu;
         mx = (t < valid && bits > mx) ? bits : mx;
     }
+    if constexpr (VT::kQ8) return __any(mx > kVBigBits8) ? kVShift8 : 0;
     return __any(mx > kVBigBits) ? kVShift : 0;
 }
 
 // V^T operands of O^T += V^T . P^T for chunk c (tokens [32 c, 32 c + 32)) and
 // quant block b: vop[0] holds channel 32 b + n, vop[1] channel 32 b + 16 + n
-// (low and high nibbles of byte n), for the lane's 8 token slots: slot j of
-// lane group gq is token 32 c + 4 gq + j for j < 4, else 32 c + 12 + 4 gq + j.
-// Each value is d * (u - 8) / 2^vshift rounded once to f16 ((u - 8) / 2^vshift
-// is exact, and the product of two f16 values is rounded once). TAIL zeroes
-// rows at or past `valid` (their scales may be NaN). Split into the LDS reads
-// (v_raw) and the arithmetic (v_convert), like the K operand.
+// (Q4_0: low and high nibbles of byte n; Q8_0: codes n and 16 + n), for the
+// lane's 8 token slots: slot j of lane group gq is token 32 c + 4 gq + j for
+// j < 4, else 32 c + 12 + 4 gq + j. Each value is d * (u - 8) / 2^vshift or
+// d * code / 2^vshift rounded once to f16 ((u - 8) / 2^vshift and
+// code / 2^vshift are exact, and the product of two f16 values is rounded
+// once). TAIL zeroes rows at or past `valid` (their scales may be NaN). Split
+// into the LDS reads (v_raw) and the arithmetic (v_convert), like the K
+// operand.
+template <typename VT>
 struct VRaw {
-    uint32_t byte[8];   // nibble byte n of the slot's token
-    uint32_t d[8];      // scale bits of the slot's token
+    uint32_t byte[8];                   // byte n of the slot's token (Q4_0 nibbles, Q8_0 code n)
+    uint32_t hbyte[VT::kQ8 ? 8 : 1];    // Q8_0: code 16 + n
+    uint32_t d[8];                      // scale bits of the slot's token
 };
-__device__ inline VRaw v_raw(const uint8_t* v_lds, int b, int c, int gq, int n) {
-    const uint8_t* vlane = v_lds + b * kVBlock + 4 * gq * kVRow;
-    VRaw r;
+template <typename VT>
+__device__ inline VRaw<VT> v_raw(const uint8_t* v_lds, int b, int c, int gq, int n) {
+    const uint8_t* vlane = v_lds + b * VT::kBlock + 4 * gq * VT::kRow;
+    VRaw<VT> r;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const uint8_t* row = vlane + (32 * c + (j < 4 ? j : 12 + j)) * kVRow;
+        const uint8_t* row = vlane + (32 * c + (j < 4 ? j : 12 + j)) * VT::kRow;
         r.byte[j] = row[2 + n];
+        if constexpr (VT::kQ8) r.hbyte[j] = row[18 + n];
         r.d[j] = *(const uint16_t*)row;
     }
     return r;
 }
-template <bool TAIL>
-__device__ inline void v_convert(const VRaw& r, int c, int gq, int valid, int vshift, uint32_t m_nib, uint32_t magic,
+template <bool TAIL, typename VT>
+__device__ inline void v_convert(const VRaw<VT>& r, int c, int gq, int valid, int vshift, uint32_t m_nib, uint32_t magic,
                                  half8_t (&vop)[2]) {
-    const _Float16 cs = vshift ? (_Float16)0.125f : (_Float16)1.f;
+    const _Float16 cs = vshift ? (VT::kQ8 ? (_Float16)0.0078125f : (_Float16)0.125f) : (_Float16)1.f;
     const half2_t cc = {cs, cs};
     const half2_t off = {(_Float16)-1032.f * cs, (_Float16)-1032.f * cs};
+    const half2_t off8 = {(_Float16)-1152.f * cs, (_Float16)-1152.f * cs};
 #pragma unroll
     for (int jp = 0; jp < 4; ++jp) {
         const int j0 = 2 * jp, j1 = 2 * jp + 1;
@@ -203,8 +221,15 @@ __device__ inline void v_convert(const VRaw& r, int c, int gq, int valid, int vs
         }
         const half2_t dd = as_h2(d0 | (d1 << 16));
         const uint32_t x = __builtin_amdgcn_perm(r.byte[j1], r.byte[j0], 0x0c040c00u);
-        const half2_t lo = q4_nibbles_f16((x & m_nib) | magic, cc, off) * dd;          // channel n
-        const half2_t hi = q4_nibbles_f16(((x >> 4) & m_nib) | magic, cc, off) * dd;   // channel 16 + n
+        half2_t lo, hi;
+        if constexpr (VT::kQ8) {
+            const uint32_t xh = __builtin_amdgcn_perm(r.hbyte[j1], r.hbyte[j0], 0x0c040c00u);
+            lo = q8_pair_f16(x, cc, off8) * dd;                  // channel n
+            hi = q8_pair_f16(xh, cc, off8) * dd;                 // channel 16 + n
+        } else {
+            lo = q4_nibbles_f16((x & m_nib) | magic, cc, off) * dd;          // channel n
+            hi = q4_nibbles_f16(((x >> 4) & m_nib) | magic, cc, off) * dd;   // channel 16 + n
+        }
         vop[0][j0] = lo[0]; vop[0][j1] = lo[1];
         vop[1][j0] = hi[0]; vop[1][j1] = hi[1];
     }
@@ -214,13 +239,13 @@ __device__ inline void v_convert(const VRaw& r, int c, int gq, int valid, int vs
 #ifndef KVS_MFMA_OCC
 #define KVS_MFMA_OCC 2
 #endif
-template <int RT, int LIMBS>
+template <int RT, int LIMBS, typename VT>
 __global__ __launch_bounds__(kThreads, KVS_MFMA_OCC)
 void mfma_kernel(AttendArgs a) {
     // separate LDS arrays: a read of one is then ordered only after the LDS
     // DMA into that one, not after the next page's DMA into another
     __shared__ __attribute__((aligned(16))) uint8_t k_lds[kKTile];
-    __shared__ __attribute__((aligned(16))) uint8_t v_lds[kVTile];
+    __shared__ __attribute__((aligned(16))) uint8_t v_lds[VT::kTile];
     __shared__ __attribute__((aligned(16))) uint8_t p_lds[kChunks * RT * 64 * 16];
     __shared__ __attribute__((aligned(16))) uint32_t ksc[kWaves][kTokW * 2];
     __shared__ float red_m[kWaves][16 * RT];
@@ -256,7 +281,7 @@ void mfma_kernel(AttendArgs a) {
     {
         const uint8_t* rec = page_record(a.ps, scalar_load(&a.segs[slice].page0));
         dma_k_tile(rec, g, k_lds, w, lane);
-        dma_v_tile(rec, g, a.n_kv_heads, v_lds, w, lane);
+        dma_v_tile<VT>(rec, g, a.n_kv_heads, v_lds, w, lane);
     }
 
     // ---- this lane's query rows (one per row tile) and their visible prefix
@@ -469,7 +494,7 @@ void mfma_kernel(AttendArgs a) {
 
         // ---- this page's V shift for block w; the accumulator moves to its
         // units when it changes (an exact power-of-two rescale)
-        const int vsh = v_shift_of(v_lds, w, valid, lane);
+        const int vsh = v_shift_of<VT>(v_lds, w, valid, lane);
         if (vsh != vsh_run) {
             const float f = __builtin_amdgcn_ldexpf(1.f, vsh_run - vsh);
 #pragma unroll
@@ -481,13 +506,13 @@ void mfma_kernel(AttendArgs a) {
 
         // ---- P.V for channels 32 w .. 32 w + 31 (V quant block w)
         auto pv_page = [&](auto tail) {
-            VRaw vr[2];
-            vr[0] = v_raw(v_lds, w, 0, gq, n);
+            VRaw<VT> vr[2];
+            vr[0] = v_raw<VT>(v_lds, w, 0, gq, n);
 #pragma unroll
             for (int c = 0; c < kChunks; ++c) {
                 half8_t vop[2];
-                if (c + 1 < kChunks) vr[(c + 1) & 1] = v_raw(v_lds, w, c + 1, gq, n);
-                v_convert<decltype(tail)::value>(vr[c & 1], c, gq, valid, vsh, m_nib, magic, vop);
+                if (c + 1 < kChunks) vr[(c + 1) & 1] = v_raw<VT>(v_lds, w, c + 1, gq, n);
+                v_convert<decltype(tail)::value, VT>(vr[c & 1], c, gq, valid, vsh, m_nib, magic, vop);
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
                     const half8_t pop = *(const half8_t*)(pbuf + ((c * RT + rt) * 64 + lane) * 16);
@@ -504,7 +529,7 @@ void mfma_kernel(AttendArgs a) {
         // the reads of the V tile
         if (next_rec) dma_k_tile(next_rec, g, k_lds, w, lane);
         lds_barrier();   // every wave is done with this page's V tile and P operands
-        if (next_rec) dma_v_tile(next_rec, g, a.n_kv_heads, v_lds, w, lane);
+        if (next_rec) dma_v_tile<VT>(next_rec, g, a.n_kv_heads, v_lds, w, lane);
     }
 
     // ---- group state -> partial records (O back in absolute units)
@@ -533,9 +558,10 @@ void mfma_kernel(AttendArgs a) {
 // of the launch, kv heads); block x stages the x-th page of the launch's
 // segments, in segment order, into staged tile x (or, with by_page, into
 // tile `page`); blocks past the pages are ring refill workgroups.
+template <typename VT>
 __global__ __launch_bounds__(kThreads) void stage_kernel(StageArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t k_lds[kKTile];
-    __shared__ __attribute__((aligned(16))) uint8_t v_lds[kVTile];
+    __shared__ __attribute__((aligned(16))) uint8_t v_lds[VT::kTile];
     if ((int)blockIdx.x >= a.n_pages) {   // ring refill workgroup
         copy_role(a.copy, ((int)blockIdx.x - a.n_pages) * (int)gridDim.y + (int)blockIdx.y);
         return;
@@ -554,7 +580,7 @@ __global__ __launch_bounds__(kThreads) void stage_kernel(StageArgs a) {
     {
         const uint8_t* rec = page_record(a.ps, page);
         dma_k_tile(rec, g, k_lds, w, lane);
-        dma_v_tile(rec, g, a.n_kv_heads, v_lds, w, lane);
+        dma_v_tile<VT>(rec, g, a.n_kv_heads, v_lds, w, lane);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
@@ -575,13 +601,13 @@ __global__ __launch_bounds__(kThreads) void stage_kernel(StageArgs a) {
     // V: wave w converts block w (channel tiles 2 w, 2 w + 1), as the PV role does
     const int64_t vx = a.n_kv - (int64_t)page * kPageTokens;
     const int valid = (int)(vx < 0 ? 0 : (vx > kPageTokens ? kPageTokens : vx));
-    const int vsh = v_shift_of(v_lds, w, valid, lane);
+    const int vsh = v_shift_of<VT>(v_lds, w, valid, lane);
     if (lane == 0) *((int32_t*)(tile + kStagedShift) + w) = vsh;
     const uint32_t m_nib = vconst(0x000F000Fu), magic = vconst(0x64006400u);
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
         half8_t vop[2];
-        v_convert<true>(v_raw(v_lds, w, c, gq, n), c, gq, valid, vsh, m_nib, magic, vop);
+        v_convert<true, VT>(v_raw<VT>(v_lds, w, c, gq, n), c, gq, valid, vsh, m_nib, magic, vop);
         *(half8_t*)(tile + staged_v_offset(c, 2 * w, lane)) = vop[0];
         *(half8_t*)(tile + staged_v_offset(c, 2 * w + 1, lane)) = vop[1];
     }
@@ -615,7 +641,8 @@ hipError_t launch_rt(const AttendArgs& a, hipStream_t stream) {
     const int64_t n_work = slices * units;
     const int64_t blocks = ((copy_workgroups(a.copy) + 7) & ~7) + ((n_work + 7) & ~7);
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    return launch_kernel(mfma_kernel<RT, LIMBS>, dim3((unsigned)blocks), dim3(kThreads), stream, b);
+    if (a.v_q8) return launch_kernel(mfma_kernel<RT, LIMBS, VQ8>, dim3((unsigned)blocks), dim3(kThreads), stream, b);
+    return launch_kernel(mfma_kernel<RT, LIMBS, VQ4>, dim3((unsigned)blocks), dim3(kThreads), stream, b);
 }
 
 }  // namespace
@@ -634,7 +661,8 @@ bool mfma_stages(int rows) { return rows > 64; }
 hipError_t launch_stage(const StageArgs& a, hipStream_t stream) {
     const int cx = (copy_workgroups(a.copy) + a.n_kv_heads - 1) / a.n_kv_heads;
     if (a.n_pages <= 0 && cx == 0) return hipSuccess;
-    return launch_kernel(stage_kernel, dim3(a.n_pages + cx, a.n_kv_heads), dim3(kThreads), stream, a);
+    if (a.v_q8) return launch_kernel(stage_kernel<VQ8>, dim3(a.n_pages + cx, a.n_kv_heads), dim3(kThreads), stream, a);
+    return launch_kernel(stage_kernel<VQ4>, dim3(a.n_pages + cx, a.n_kv_heads), dim3(kThreads), stream, a);
 }
 
 }  // namespace kvs

@@ -72,7 +72,7 @@ int validate(const kvs_config* c) {
     if (!c) return fail(KVS_ERR_INVALID_ARG, "config is NULL");
     if (!kvs_type_pair_supported(c->type_k, c->type_v))
         return fail(KVS_ERR_UNSUPPORTED,
-                    "K/V block types (%d, %d) have no attention kernel: only Q8_0 keys (%d) with Q4_0 values (%d) are built",
+                    "K/V block types (%d, %d) have no attention kernel: only Q8_0 keys (%d) with Q4_0 (%d) or Q8_0 values are built",
                     c->type_k, c->type_v, KVS_TYPE_Q8_0, KVS_TYPE_Q4_0);
     if (c->head_dim != kvs::kHeadDim)
         return fail(KVS_ERR_UNSUPPORTED, "head_dim %d unsupported (kernels are built for %d)", c->head_dim, kvs::kHeadDim);
@@ -96,7 +96,7 @@ int validate(const kvs_config* c) {
 
 Layout layout_of(const kvs_config* c) {
     Layout L;
-    L.page_bytes = (uint64_t)c->n_kv_heads * (kvs::kKTile + kvs::kVTile);
+    L.page_bytes = (uint64_t)c->n_kv_heads * kvs::head_record_bytes(c->type_v == KVS_TYPE_Q8_0);
     L.ring_bytes = align256((uint64_t)c->ring_pages * L.page_bytes);
     L.max_groups = (c->max_pages + c->group_pages - 1) / c->group_pages;
     // partials: one record per (group, query token, query head)
@@ -619,7 +619,7 @@ int check_ring_free_for(const kvs_pool* p, int32_t layer) {
 extern "C" {
 
 int kvs_type_pair_supported(int32_t type_k, int32_t type_v) {
-    return type_k == KVS_TYPE_Q8_0 && type_v == KVS_TYPE_Q4_0;
+    return type_k == KVS_TYPE_Q8_0 && (type_v == KVS_TYPE_Q4_0 || type_v == KVS_TYPE_Q8_0);
 }
 
 int kvs_config_validate(const kvs_config* cfg) { return validate(cfg); }
@@ -1058,6 +1058,7 @@ int attend_impl(kvs_pool* p, int32_t layer, const void* q, int32_t q_dtype, int3
     a.G = p->cfg.n_q_heads / p->cfg.n_kv_heads;
     a.q = q;
     a.q_f16 = q_dtype == KVS_Q_F16;
+    a.v_q8 = p->cfg.type_v == KVS_TYPE_Q8_0;
     a.n_q = n_q;
     a.q_pos0 = q_pos0;
     a.n_kv = n_kv;
@@ -1103,6 +1104,7 @@ int attend_impl(kvs_pool* p, int32_t layer, const void* q, int32_t q_dtype, int3
             sa.n_kv = n_kv;
             sa.n_pages = pages;
             sa.staged = region;
+            sa.v_q8 = b.v_q8;
             hipError_t e = timed_or_not(2, st, [&] { return kvs::launch_stage(sa, st); });
             if (e != hipSuccess) return fail(KVS_ERR_HIP, "staging kernel launch failed: %s", hipGetErrorString(e));
             kvs::AttendArgs c = b;
@@ -1166,6 +1168,7 @@ int kvs_debug_gather(kvs_pool* p, int32_t layer, int64_t tok0, int64_t n_tok, fl
     a.n_tok = n_tok;
     a.k_out = k_out;
     a.v_out = v_out;
+    a.v_q8 = p->cfg.type_v == KVS_TYPE_Q8_0;
     rc = run_layer(p, layer, s, 0, [&](hipStream_t st, int /*lane*/, int32_t seg0, int32_t nseg, const uint8_t* ring_chunk,
                                     int32_t rank0, const kvs::CopyJob& cj) -> int {
         kvs::GatherArgs b = a;
@@ -1203,6 +1206,7 @@ int kvs_debug_stage(kvs_pool* p, int32_t layer, int64_t n_kv, void* dst, void* s
     a.n_kv_heads = p->cfg.n_kv_heads;
     a.n_kv = n_kv;
     a.staged = (uint8_t*)dst;
+    a.v_q8 = p->cfg.type_v == KVS_TYPE_Q8_0;
     a.by_page = 1;
     rc = run_layer(p, layer, s, 0, [&](hipStream_t st, int /*lane*/, int32_t seg0, int32_t nseg, const uint8_t* ring_chunk,
                                     int32_t rank0, const kvs::CopyJob& cj) -> int {
@@ -1287,6 +1291,7 @@ int kvs_append(kvs_pool* p, int32_t layer, const void* k_new, const void* v_new,
     a.src = ls.dev_src;
     a.slots = p->slots;
     a.host = const_cast<uint8_t*>(ls.host);
+    a.v_q8 = p->cfg.type_v == KVS_TYPE_Q8_0;
     hipError_t e = kvs::launch_append(a, s);
     if (e != hipSuccess) return fail(KVS_ERR_HIP, "append kernel launch failed: %s", hipGetErrorString(e));
     p->st.kernels_launched++;

@@ -1,5 +1,5 @@
 /*
- * kvs.h - host-streamed, paged flash-attention over a Q8_0-K / Q4_0-V cache
+ * kvs.h - host-streamed, paged flash-attention over a Q8_0-K / Q4_0-V (or Q8_0-V) cache
  *         (C ABI of libkvs.so, built for AMD MI355X / gfx950).
  *
  * The method (three pages on "Adaptive KV Streaming" for llama.cpp):
@@ -10,7 +10,8 @@
  *   - The unit of residency and transfer is a 256-token page of one layer
  *     (page 2, "Dynamic draft eject": thresholds counted in 256-token pages).
  *   - The cache types are Q8_0 for K and Q4_0 for V (page 1, "What it is useful
- *     for"; page 2, "TLDR": the q8_0-q4_0 kernel pair).
+ *     for"; page 2, "TLDR": the q8_0-q4_0 kernel pair), or Q8_0 for both
+ *     (page 3, "1. Correctness - PPL parity" runs -ctk q8_0 -ctv q8_0).
  *   - A byte budget sizes the device region; the smallest useful budget is one
  *     page (page 3, "Diagnostic log": minimum_stage_bytes).
  *   - Unsupported K/V type pairs and over-wide batches fail with an explicit
@@ -43,16 +44,18 @@
  * Page record format (one record per layer and page, page_bytes long):
  *   [ K: for kv head g = 0..Hkv-1, token row r = 0..255, block b = 0..d/32-1:
  *        a Q8_0 block of 34 bytes ]
- *   [ V: same order, Q4_0 blocks of 18 bytes ]
+ *   [ V: same order, Q4_0 blocks of 18 bytes (type_v KVS_TYPE_Q4_0) or Q8_0
+ *        blocks of 34 bytes (type_v KVS_TYPE_Q8_0) ]
  *   Q8_0 block: little-endian binary16 scale d, then 32 int8 codes q;
  *               element i = d * q[i].
  *   Q4_0 block: little-endian binary16 scale d, then 16 bytes; byte j holds
  *               element j in its low nibble and element j + 16 in its high
  *               nibble; element i = d * (nibble - 8).
  *   Token t of a layer lives in page t / 256, row t % 256. Each kv head's K tile
- *   (256 x d/32 x 34 bytes) and V tile (256 x d/32 x 18 bytes) is contiguous,
- *   so one workgroup reads one head of one page as two line-aligned streams.
- *   For Hkv = 4, d = 128: K row 136 B per head, page_bytes = 212992.
+ *   (256 x d/32 x 34 bytes) and V tile (256 x d/32 x 18 or 34 bytes) is
+ *   contiguous, so one workgroup reads one head of one page as two line-aligned
+ *   streams. For Hkv = 4, d = 128: K row 136 B per head, page_bytes = 212992
+ *   (Q4_0 V) or 278528 (Q8_0 V).
  *   Rows at or beyond the layer's token count may hold any bytes (even NaN
  *   scales); they are never read into a result.
  */
@@ -105,7 +108,7 @@ typedef struct kvs_config {
     int32_t head_dim;      /* d; 128 is the only supported value                          */
     int32_t page_tokens;   /* 256 is the only supported value                             */
     int32_t type_k;        /* KVS_TYPE_Q8_0                                                */
-    int32_t type_v;        /* KVS_TYPE_Q4_0                                                */
+    int32_t type_v;        /* KVS_TYPE_Q4_0 or KVS_TYPE_Q8_0                               */
     int32_t max_pages;     /* most pages any layer will hold (sizes tables and workspace) */
     int32_t max_q_tokens;  /* widest query block kvs_attend admits: 1 for decode,
                               1 + n_draft for a speculative verify, the ubatch for prefill */
@@ -139,7 +142,7 @@ typedef struct kvs_status_info {
 
 typedef struct kvs_pool kvs_pool;
 
-/* 1 if the K/V block type pair has a kernel (only Q8_0 K with Q4_0 V), else 0.
+/* 1 if the K/V block type pair has a kernel (Q8_0 K with Q4_0 or Q8_0 V), else 0.
  * Pure: no HIP call. The pages compile flash-attention per K/V type pair and
  * reject unqualified pairs (page 2, "TLDR"; page 1, "How engineers can use it"). */
 int kvs_type_pair_supported(int32_t type_k, int32_t type_v);
@@ -307,10 +310,12 @@ int kvs_stream_enqueue(kvs_pool* pool, int32_t layer);
  *     each query row as 16-bit fixed point relative to its largest element;
  *     wider blocks hold it exactly as f16 limbs (two for f32) after a
  *     power-of-two scaling per row.
- *   - V blocks: any finite binary16 scale and nibbles 0..15. Probabilities
- *     and V values pass through f16 with one rounding each; a page whose
- *     32-channel V block holds a scale magnitude above 8188 is taken divided
- *     by 8. Within one page and one 32-channel block, V scale magnitudes
+ *   - V blocks: any finite binary16 scale, nibbles 0..15 (Q4_0) or any codes
+ *     (Q8_0, -128 included). Probabilities and V values pass through f16 with
+ *     one rounding each; at widths above decode, a page whose 32-channel V
+ *     block holds a scale magnitude above 8188 (Q4_0) or 511.75 (Q8_0) is
+ *     taken divided by 8 (Q4_0) or 128 (Q8_0), so that no V operand
+ *     overflows f16. Within one page and one 32-channel block, V scale magnitudes
  *     should lie within a factor of 2^14 of the block's largest: the
  *     contribution of a token whose scale is smaller than that (relative to
  *     the largest, in the same quarter page at decode width) carries an
@@ -349,7 +354,7 @@ int kvs_attend_noalloc(kvs_pool* pool, int32_t layer, const void* q, int32_t q_d
                        void* stream);
 
 /* Append a step's new K and V rows to a layer: quantize them into Q8_0 (K)
- * and Q4_0 (V) blocks and write them at tokens pos0 .. pos0 + n_tok - 1 of
+ * and Q4_0 or Q8_0 (V, the pool's type_v) blocks and write them at tokens pos0 .. pos0 + n_tok - 1 of
  * the layer, into the authoritative host records and, for each resident page,
  * into its device slot. The pages keep the whole history in pinned host
  * memory and a working set on the device (page 1, "Summary"; page 2, opening
@@ -423,14 +428,17 @@ int kvs_debug_export_pages(kvs_pool* pool, int32_t layer, void* dst, void* strea
  *     codes of token 16 T + n, elements 32 b + 8 j .. 32 b + 8 j + 7, exact.
  *   V^T operands, bytes [65536, 131072): for chunk c = 0..7, channel tile
  *     t = 0..7, lane = 0..63: 8 values; lane (n, j) holds channel
- *     16 t + n (block t / 2, low nibbles for even t, high for odd t) of tokens
+ *     16 t + n (element 16 (t % 2) + n of block t / 2: the low nibbles of a
+ *     Q4_0 block for even t, its high nibbles for odd t) of tokens
  *     32 c + 4 j + s for slot s < 4 and 32 c + 12 + 4 j + s for s >= 4, each
- *     d x (nibble - 8) / 2^shift rounded once to binary16 (0 for uncached
- *     rows), shift = the block's V shift.
+ *     d x (nibble - 8) (Q4_0) or d x code (Q8_0), divided by 2^shift and
+ *     rounded once to binary16 (0 for uncached rows), shift = the block's V
+ *     shift.
  *   K scales, bytes [131072, 135168): token t's four block scales as
  *     float32 (exact) at 16 t.
- *   V shifts, bytes [135168, 135184): int32 per block, 3 if a cached row's
- *     scale magnitude exceeds 8188 (binary16 bits above 0x6FFF), else 0. */
+ *   V shifts, bytes [135168, 135184): int32 per block: 0, or, if a cached
+ *     row's scale magnitude exceeds 8188 (binary16 bits above 0x6FFF) for
+ *     Q4_0 V or 511.75 (bits above 0x5FFF) for Q8_0 V, 3 (Q4_0) or 7 (Q8_0). */
 #define KVS_STAGED_TILE_BYTES 135424
 int kvs_debug_stage(kvs_pool* pool, int32_t layer, int64_t n_kv, void* dst, void* stream);
 

@@ -29,15 +29,17 @@ class Case:
     """L layers of seeded pages, registered with a fresh pool."""
 
     def __init__(self, *, cid, n_layers, n_kv_heads, n_q_heads, n_kv, cfg_kw, resident_fn, slots=None,
-                 tail="poison", threads=8):
+                 tail="poison", threads=8, type_v="q4_0"):
         self.cid, self.L, self.Hkv, self.Hq, self.n_kv = cid, n_layers, n_kv_heads, n_q_heads, n_kv
-        self.geom = KVGeometry(n_kv_heads, 128)
+        self.type_v = type_v
+        self.geom = KVGeometry(n_kv_heads, 128, type_v=type_v)
         self.n_pages = -(-n_kv // 256)
         with ThreadPoolExecutor(threads) as ex:
             self.records = list(ex.map(lambda l: layer_records(cid, l, n_kv, self.geom, tail=tail), range(n_layers)))
         self.host = [torch.from_numpy(r).pin_memory() for r in self.records]
         self.masks = [np.asarray(resident_fn(l, self.n_pages), np.uint8) for l in range(n_layers)]
-        cfg = dict(n_layers=n_layers, n_kv_heads=n_kv_heads, n_q_heads=n_q_heads, max_pages=max(1, self.n_pages))
+        cfg = dict(n_layers=n_layers, n_kv_heads=n_kv_heads, n_q_heads=n_q_heads, max_pages=max(1, self.n_pages),
+                   type_v=kvs.TYPE_Q8_0 if type_v == "q8_0" else kvs.TYPE_Q4_0)
         cfg.update(cfg_kw)
         self.cfg = kvs.Config(**cfg)
         need = int(sum(m.sum() for m in self.masks))
@@ -73,7 +75,7 @@ class Case:
 
     def oracle(self, layer, q, *, q_pos0, scale, causal, heads=None):
         return attend_layer(self.records[layer], q, n_kv=self.n_kv, n_kv_heads=self.Hkv, head_dim=128,
-                            scale=scale, causal=causal, q_pos0=q_pos0, heads=heads)
+                            scale=scale, causal=causal, q_pos0=q_pos0, heads=heads, type_v=self.type_v)
 
 
 def mask_all(l, n):

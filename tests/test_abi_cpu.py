@@ -38,12 +38,24 @@ def base_cfg(**kw):
 
 def test_type_pair_gate():
     assert kvs.type_pair_supported(kvs.TYPE_Q8_0, kvs.TYPE_Q4_0)
-    for tk, tv in [(kvs.TYPE_Q8_0, kvs.TYPE_Q8_0), (kvs.TYPE_F16, kvs.TYPE_F16), (kvs.TYPE_Q4_0, kvs.TYPE_Q4_0),
-                   (kvs.TYPE_Q4_0, kvs.TYPE_Q8_0)]:
+    assert kvs.type_pair_supported(kvs.TYPE_Q8_0, kvs.TYPE_Q8_0)
+    for tk, tv in [(kvs.TYPE_F16, kvs.TYPE_F16), (kvs.TYPE_Q4_0, kvs.TYPE_Q4_0), (kvs.TYPE_Q4_0, kvs.TYPE_Q8_0),
+                   (kvs.TYPE_Q8_0, kvs.TYPE_F16)]:
         assert not kvs.type_pair_supported(tk, tv)
-    rc = kvs.config_validate(base_cfg(type_k=kvs.TYPE_Q8_0, type_v=kvs.TYPE_Q8_0))
+    assert kvs.config_validate(base_cfg(type_k=kvs.TYPE_Q8_0, type_v=kvs.TYPE_Q8_0)) == kvs.OK
+    rc = kvs.config_validate(base_cfg(type_k=kvs.TYPE_F16, type_v=kvs.TYPE_F16))
     assert rc == kvs.ERR_UNSUPPORTED
     assert "Q8_0" in kvs.last_error() and "Q4_0" in kvs.last_error()
+
+
+def test_page_bytes_per_type_pair():
+    """The record sizes of both pairs: 256 tokens x Hkv x (136 B of Q8_0 K +
+    72 B of Q4_0 V or 136 B of Q8_0 V), as the oracle computes them."""
+    from oracle import page_bytes as oracle_page_bytes
+    for tv, name in [(kvs.TYPE_Q4_0, "q4_0"), (kvs.TYPE_Q8_0, "q8_0")]:
+        for hkv in (1, 4, 8):
+            cfg = base_cfg(n_kv_heads=hkv, n_q_heads=6 * hkv, type_v=tv)
+            assert kvs.page_bytes(cfg) == oracle_page_bytes(hkv, 128, 256, "q8_0", name)
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -1,6 +1,7 @@
 """KV append on the GPU (kvs_append, through the C ABI) against the oracle.
 
-Bars: the appended bytes are bit-exact with the oracle's quantizer, in the
+Both V block types (Q4_0 and Q8_0) are covered. Bars: the appended bytes are
+bit-exact with the oracle's quantizer, in the
 authoritative host records and in every resident device slot, and no other
 byte changes; attention over the appended cache is within 2e-3 (normwise per
 row, lse absolute) of the oracle on the updated records, and bit-identical
@@ -36,20 +37,21 @@ def new_rows(seed, n, dtype):
     return k, v
 
 
-def make_case(resident_fn, cid=57):
-    say(f"append case cid={cid} n_kv={N_KV} residency={getattr(resident_fn, '__name__', 'fn')}")
+def make_case(resident_fn, cid=57, type_v="q4_0"):
+    say(f"append case cid={cid} n_kv={N_KV} {type_v} residency={getattr(resident_fn, '__name__', 'fn')}")
     return Case(cid=cid, n_layers=2, n_kv_heads=H, n_q_heads=HQ, n_kv=N_KV,
                 cfg_kw=dict(max_q_tokens=4, ring_pages=4, chunk_pages=2, group_pages=1),
-                resident_fn=resident_fn)
+                resident_fn=resident_fn, type_v=type_v)
 
 
 def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
+@pytest.mark.parametrize("type_v", ["q4_0", "q8_0"])
 @pytest.mark.parametrize("resident", [mask_all, mask_none, mask_random(0.5, seed=3)], ids=["all", "none", "half"])
-def test_append_writes_quantized_rows_bit_exact(resident):
-    c = make_case(resident)
+def test_append_writes_quantized_rows_bit_exact(resident, type_v):
+    c = make_case(resident, type_v=type_v)
     try:
         # (layer, input dtype, pos0, rows): the tail of the last page; rows
         # across a page boundary, over existing ones; a single decode row; a
@@ -61,7 +63,7 @@ def test_append_writes_quantized_rows_bit_exact(resident):
             before = c.host[l].numpy().copy()
             c.pool.append(l, dev(k), dev(v), pos0)
             torch.cuda.synchronize()
-            expect = append_rows(before, k, v, pos0=pos0, n_kv_heads=H, head_dim=128)
+            expect = append_rows(before, k, v, pos0=pos0, n_kv_heads=H, head_dim=128, type_v=type_v)
             got = c.host[l].numpy()
             assert np.array_equal(got, expect), (l, pos0)
             for p in range(c.n_pages):
@@ -71,7 +73,8 @@ def test_append_writes_quantized_rows_bit_exact(resident):
         c.close()
 
 
-def test_attention_after_append_matches_oracle_and_ignores_residency():
+@pytest.mark.parametrize("type_v", ["q4_0", "q8_0"])
+def test_attention_after_append_matches_oracle_and_ignores_residency(type_v):
     """Decode: one new row at the last position, then attention over it.
     Verify: four new rows (the draft), then a causal 4-token block. The page
     that takes the rows is resident in one pool and streamed in the other."""
@@ -81,7 +84,7 @@ def test_attention_after_append_matches_oracle_and_ignores_residency():
             m = np.array(mask_random(0.5, seed=4)(l, n), np.uint8)
             m[n - 1] = 1 if tail_resident else 0
             return m
-        c = make_case(mask, cid=58)
+        c = make_case(mask, cid=58, type_v=type_v)
         try:
             records = [r.copy() for r in c.records]
             outs = []
@@ -90,7 +93,7 @@ def test_attention_after_append_matches_oracle_and_ignores_residency():
                 pos0 = N_KV - n_new
                 k, v = new_rows(20 + l, n_new, dt)
                 c.pool.append(l, dev(k), dev(v), pos0)
-                records[l] = append_rows(records[l], k, v, pos0=pos0, n_kv_heads=H, head_dim=128)
+                records[l] = append_rows(records[l], k, v, pos0=pos0, n_kv_heads=H, head_dim=128, type_v=type_v)
                 q = c.queries(l, n_new, "f32")
                 out = torch.empty((n_new, HQ, 128), dtype=torch.float32, device="cuda")
                 lse = torch.empty((n_new, HQ), dtype=torch.float32, device="cuda")
@@ -98,7 +101,7 @@ def test_attention_after_append_matches_oracle_and_ignores_residency():
                 torch.cuda.synchronize()
                 o, s = out.cpu().numpy(), lse.cpu().numpy()
                 ref, ref_lse = attend_layer(records[l], q, n_kv=N_KV, n_kv_heads=H, head_dim=128, scale=1.0,
-                                            causal=True, q_pos0=pos0)
+                                            causal=True, q_pos0=pos0, type_v=type_v)
                 err = normwise_error(o, ref)
                 lerr = float(np.max(np.abs(s - ref_lse)))
                 say(f"tail resident={tail_resident} layer {l}: normwise {err:.3e} lse {lerr:.3e}")
