@@ -69,12 +69,12 @@ def gen_layers(wl, geom, threads):
         return list(ex.map(lambda l: layer_records(wl.cid, l, wl.n_kv, geom), range(wl.n_layers)))
 
 
-def setup(wl, cfg_kw, threads):
+def setup(wl, cfg_kw, threads, type_v="q4_0"):
     import torch
     import host_streamed_paged_amd as kvs
     from kvs_synth import KVGeometry, make_q, residency_mask
 
-    geom = KVGeometry(wl.n_kv_heads, wl.head_dim)
+    geom = KVGeometry(wl.n_kv_heads, wl.head_dim, type_v=type_v)
     t0 = time.time()
     recs = gen_layers(wl, geom, threads)
     host = [torch.from_numpy(r).pin_memory() for r in recs]
@@ -82,7 +82,8 @@ def setup(wl, cfg_kw, threads):
     masks = [residency_mask(wl.cid, l, wl.n_pages, wl.resident_pages, wl.own_page_resident)
              for l in range(wl.n_layers)]
     cfg = kvs.Config(n_layers=wl.n_layers, n_kv_heads=wl.n_kv_heads, n_q_heads=wl.n_q_heads,
-                     max_pages=wl.n_pages, max_q_tokens=wl.n_q, **cfg_kw)
+                     max_pages=wl.n_pages, max_q_tokens=wl.n_q,
+                     type_v=kvs.TYPE_Q8_0 if type_v == "q8_0" else kvs.TYPE_Q4_0, **cfg_kw)
     arena = kvs.Pool.arena_for(cfg, int(sum(int(m.sum()) for m in masks)))
     pool = kvs.Pool(cfg, arena)
     for l in range(wl.n_layers):
@@ -182,6 +183,45 @@ def streamed_run(wl, st, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return dict(ms_per_step=e0.elapsed_time(e1) / steps, wall_ms_per_step=wall * 1e3 / steps)
+
+
+def q8_leg(args, link):
+    """The q8_0 K / q8_0 V pair on the two decode shapes: resident 32 Ki
+    (graph replay of the 16-layer step, plus the eager per-kernel time) and,
+    unless streamed legs are off, streamed 256 Ki through its 16-page ring."""
+    from kvs_synth import WORKLOADS
+    wl = WORKLOADS["resident_decode_32k"]
+    st = setup(wl, POOL_CFG[wl.name], args.threads, type_v="q8_0")
+    r = timed_run(wl, st, args.steps, args.warmup)
+    gr = graph_run(wl, st, args.steps, args.warmup)
+    pb = st["recs"][0].shape[1]
+    kv_bytes = wl.n_layers * wl.n_pages * pb
+    avg_att = r["attn_ms_total"] / max(1, r["attn_launches"])
+    out = {"cache": "q8_0 K / q8_0 V", "page_bytes": pb,
+           "resident": {"workload": wl.name, "ms_per_step": round(gr["ms_per_step"], 5),
+                        "kv_gbs": round(kv_bytes / (gr["ms_per_step"] / 1e3) / 1e9, 2),
+                        "attn_tok_s": round(1 / (gr["ms_per_step"] / 1e3), 1),
+                        "attention_kernel_us": round(avg_att * 1e3, 3),
+                        "kernel_frac_of_hbm": round(wl.n_pages * pb / (avg_att / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "combine_avg_us": round(r["combine_ms_total"] / max(1, r["combine_launches"]) * 1e3, 3)}}
+    log(f"q8_0/q8_0 {wl.name}: graph {gr['ms_per_step']:.4f} ms/step, attention kernel {avg_att * 1e3:.2f} us")
+    st["pool"].close()
+    del st
+    if not args.no_streamed and link:
+        swl = WORKLOADS["streamed_decode_256k"]
+        sst = setup(swl, POOL_CFG[swl.name], args.threads, type_v="q8_0")
+        sr = streamed_run(swl, sst, args.streamed_steps, 2)
+        spb = sst["recs"][0].shape[1]
+        streamed_bytes = sum(int((1 - m).sum()) for m in sst["masks"]) * spb
+        sec = sr["ms_per_step"] / 1e3
+        out["streamed"] = {"workload": swl.name, "ms_per_step": round(sr["ms_per_step"], 4),
+                           "streamed_gbs": round(streamed_bytes / sec / 1e9, 2),
+                           "frac_of_link": round(streamed_bytes / sec / 1e9 / link, 4),
+                           "attn_tok_s": round(1 / sec, 3)}
+        log(f"q8_0/q8_0 {swl.name}: {sr['ms_per_step']:.3f} ms/step, streamed {streamed_bytes / sec / 1e9:.2f} GB/s")
+        sst["pool"].close()
+        del sst
+    return out
 
 
 def append_leg(wl, st, steps, link):
@@ -414,6 +454,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-multi", action="store_true", help="skip the verify and prefill workloads")
     ap.add_argument("--no-zero-copy", action="store_true", help="skip the zero-copy A/B runs")
+    ap.add_argument("--no-q8", action="store_true", help="skip the q8_0 K / q8_0 V decode legs")
     ap.add_argument("--streamed-steps", type=int, default=10)
     ap.add_argument("--threads", type=int, default=min(16, len(os.sched_getaffinity(0))))
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -532,6 +573,9 @@ def main():
         if not args.no_zero_copy:
             result["streamed"]["zero_copy"] = zero_copy_leg(swl, sst, scfg, args.streamed_steps, link)
         del sst
+
+    if not args.no_q8:
+        result["q8_0_v"] = q8_leg(args, link)
 
     if not args.no_multi:
         result["verify"] = multi_leg("spec_verify_160k", POOL_CFG["spec_verify_160k"], args.threads, link, 8, "verify",

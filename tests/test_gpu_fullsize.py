@@ -23,16 +23,21 @@ TOL = 2e-3
 from bench import POOL_CFG as BENCH_CFG  # noqa: E402
 
 
-@pytest.mark.parametrize("name", list(BENCH_CFG))
-def test_full_size_sampled_parity(name):
+# every workload with Q4_0 V; the two decode shapes (resident 32 Ki and
+# streamed 256 Ki through the 16-page ring) also with Q8_0 V
+CASES = [(n, "q4_0") for n in BENCH_CFG] + [("resident_decode_32k", "q8_0"), ("streamed_decode_256k", "q8_0")]
+
+
+@pytest.mark.parametrize("name,type_v", CASES, ids=[f"{n}-{t}" for n, t in CASES])
+def test_full_size_sampled_parity(name, type_v):
     wl = WORKLOADS[name]
-    say(f"full-size {name}: layers={wl.n_layers} n_kv={wl.n_kv} n_q={wl.n_q} cfg={BENCH_CFG[name]}")
+    say(f"full-size {name} {type_v}: layers={wl.n_layers} n_kv={wl.n_kv} n_q={wl.n_q} cfg={BENCH_CFG[name]}")
 
     def resident(l, n):
         return residency_mask(wl.cid, l, n, wl.resident_pages, wl.own_page_resident)
 
     c = Case(cid=wl.cid, n_layers=wl.n_layers, n_kv_heads=wl.n_kv_heads, n_q_heads=wl.n_q_heads, n_kv=wl.n_kv,
-             cfg_kw=dict(max_q_tokens=wl.n_q, **BENCH_CFG[name]), resident_fn=resident)
+             cfg_kw=dict(max_q_tokens=wl.n_q, **BENCH_CFG[name]), resident_fn=resident, type_v=type_v)
     try:
         qs = [c.queries(l, wl.n_q, wl.q_dtype) for l in range(wl.n_layers)]
         outs, lses = c.attend_all(qs, q_pos0=wl.q_pos0, scale=wl.scale, causal=wl.causal)
@@ -42,7 +47,7 @@ def test_full_size_sampled_parity(name):
         q_idx = sorted({0, wl.n_q // 2, wl.n_q - 1})
         worst = 0.0
         for l in (0, wl.n_layers - 1):
-            K, V = gather_kv(c.records[l], wl.n_kv_heads, wl.head_dim, 0, wl.n_kv)
+            K, V = gather_kv(c.records[l], wl.n_kv_heads, wl.head_dim, 0, wl.n_kv, type_v=type_v)
             for i in q_idx:
                 ref, ref_lse = attend(qs[l][i:i + 1], K, V, n_kv=wl.n_kv, scale=wl.scale, causal=wl.causal,
                                       q_pos0=wl.q_pos0 + i, heads=heads)
@@ -53,6 +58,6 @@ def test_full_size_sampled_parity(name):
                 assert lerr <= TOL, (l, i, lerr)
                 worst = max(worst, err)
             del K, V
-        say(f"{name}: worst normwise {worst:.3e}")
+        say(f"{name} {type_v}: worst normwise {worst:.3e}")
     finally:
         c.close()
