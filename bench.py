@@ -115,7 +115,7 @@ def timed_run(wl, st, steps, warmup):
     pool = st["pool"]
     run_steps(wl, st, warmup, stream)
     torch.cuda.synchronize()
-    for kind in (0, 1, 2):
+    for kind in (0, 1):
         pool.profile_read(kind, reset=True)
     pool.profile_enable(True)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -130,10 +130,8 @@ def timed_run(wl, st, steps, warmup):
     ms = e0.elapsed_time(e1) / steps
     n_att, ms_att = pool.profile_read(0, reset=True)
     n_cmb, ms_cmb = pool.profile_read(1, reset=True)
-    n_stg, ms_stg = pool.profile_read(2, reset=True)
     return dict(ms_per_step=ms, wall_ms_per_step=wall * 1e3 / steps, attn_launches=n_att,
-                attn_ms_total=ms_att, combine_launches=n_cmb, combine_ms_total=ms_cmb,
-                stage_launches=n_stg, stage_ms_total=ms_stg, steps=steps)
+                attn_ms_total=ms_att, combine_launches=n_cmb, combine_ms_total=ms_cmb, steps=steps)
 
 
 def graph_run(wl, st, steps, warmup):
@@ -325,28 +323,34 @@ def multi_leg(name, cfg_kw, threads, link, steps, kind, zero_copy=True):
     r = timed_run(rwl, rst, 5, 2)
     rst["pool"].close()
     del rst
-    # per layer: the attention launches plus, for wide blocks, the staging
-    # launches that convert each page once into matrix-core operands
+    # per layer: the wall time of the whole kvs_attend call (every attention
+    # launch and the combine, timed by events around the steps), and the
+    # attention launches' own durations
     layers_timed = r["steps"] * wl.n_layers
-    avg = (r["attn_ms_total"] + r["stage_ms_total"]) / max(1, layers_timed)
+    layer_ms = r["ms_per_step"] / wl.n_layers
+    att_ms = r["attn_ms_total"] / max(1, layers_timed)
     layer_bytes = wl.n_pages * pb
     flops = 4 * wl.n_q_heads * wl.head_dim * allowed_keys(wl)
-    staged = r["stage_launches"] > 0
-    k = {"kernel": ("stage_kernel + mfma_kernel<2, staged> (32-row tiles on staged operands)" if staged
-                    else "mfma_kernel<2> (32-row tiles, in-kernel conversion)") + ", all pages resident",
-         "avg_layer_us": round(avg * 1e3, 2), "attn_launches": r["attn_launches"],
-         "stage_launches": r["stage_launches"], "stage_us_per_layer": round(r["stage_ms_total"] / max(1, layers_timed) * 1e3, 2),
+    kname = "prefill_kernel (256-row workgroups, pages converted in the workgroup)" if kind == "prefill" \
+        else "mfma_kernel (16-row tiles, in-kernel conversion)"
+    k = {"kernel": kname + ", all pages resident", "layer_us": round(layer_ms * 1e3, 2),
+         "attn_us_per_layer": round(att_ms * 1e3, 2), "attn_launches": r["attn_launches"],
+         "combine_us_per_layer": round(r["combine_ms_total"] / max(1, layers_timed) * 1e3, 2),
          "bytes_per_layer": layer_bytes, "flops_per_layer": flops,
-         "achieved_gbs": round(layer_bytes / (avg / 1e3) / 1e9, 1),
-         "achieved_tflops": round(flops / (avg / 1e3) / 1e12, 1)}
+         "achieved_gbs": round(layer_bytes / (layer_ms / 1e3) / 1e9, 1),
+         "achieved_tflops": round(flops / (layer_ms / 1e3) / 1e12, 1),
+         "kernel_gbs": round(layer_bytes / (att_ms / 1e3) / 1e9, 1),
+         "kernel_tflops": round(flops / (att_ms / 1e3) / 1e12, 1),
+         "timing": "achieved_*: whole layer (attention and combine launches, wall time by events around "
+                   "the steps); kernel_*: the attention launches' summed durations"}
     if kind == "verify":
         k.update(bound="hbm", frac=round(k["achieved_gbs"] / HBM_PEAK_GBS, 4), peak=HBM_PEAK_GBS, unit="GB/s")
     else:
         k.update(bound="mfma", frac=round(k["achieved_tflops"] / MFMA_F16_PEAK_TFLOPS, 4),
                  peak=MFMA_F16_PEAK_TFLOPS, unit="TFLOP/s")
     out["resident_kernel"] = k
-    log(f"{name} all-resident: {avg * 1e3:.1f} us per layer, {k['achieved_gbs']} GB/s, "
-        f"{k['achieved_tflops']} TFLOP/s")
+    log(f"{name} all-resident: {layer_ms * 1e3:.1f} us per layer ({att_ms * 1e3:.1f} us attention), "
+        f"{k['achieved_gbs']} GB/s, {k['achieved_tflops']} TFLOP/s")
     return out
 
 
@@ -444,6 +448,29 @@ def cpu_baseline(wl, recs, qs_np, min_s=10.0, max_s=30.0):
     }
 
 
+KERNEL_ONLY = {"decode": "resident_decode_32k", "verify": "spec_verify_160k", "prefill": "prefill_ubatch_128k"}
+
+
+def kernels_only(name, args):
+    """The kernels of one workload with every page resident: `steps` eager
+    passes over its layers after `warmup`, per-launch HIP events."""
+    import dataclasses
+    from kvs_synth import WORKLOADS
+    wl = WORKLOADS[name]
+    rwl = dataclasses.replace(wl, resident_pages=wl.n_pages)
+    st = setup(rwl, POOL_CFG[name], args.threads)
+    r = timed_run(rwl, st, args.steps, args.warmup)
+    st["pool"].close()
+    layers = r["steps"] * wl.n_layers
+    per = {k: round(r[f"{k}_ms_total"] / max(1, layers) * 1e3, 3) for k in ("attn", "combine")}
+    print(json.dumps({"workload": name, "all_resident": True, "layers_timed": layers,
+                      "attn_launches": r["attn_launches"],
+                      "combine_launches": r["combine_launches"], "us_per_layer": per,
+                      "layer_us": round(r["ms_per_step"] / wl.n_layers * 1e3, 3),
+                      "flops_per_layer": 4 * wl.n_q_heads * wl.head_dim * allowed_keys(wl),
+                      "bytes_per_layer": wl.n_pages * st["recs"][0].shape[1]}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -457,6 +484,9 @@ def main():
     ap.add_argument("--no-q8", action="store_true", help="skip the q8_0 K / q8_0 V decode legs")
     ap.add_argument("--streamed-steps", type=int, default=10)
     ap.add_argument("--threads", type=int, default=min(16, len(os.sched_getaffinity(0))))
+    ap.add_argument("--kernels-only", choices=sorted(KERNEL_ONLY), default=None,
+                    help="only time the attention (and staging, combine) launches of one workload with every page "
+                         "resident, eager with HIP events, and print one JSON line: the run profilers wrap")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run torch device-to-device copies of MIB MiB (the reference kernel of known "
                          "traffic for scaling the FETCH_SIZE / WRITE_SIZE counters), then exit")
@@ -481,6 +511,9 @@ def main():
 
     kvs.lib()
     torch.cuda.set_device(0)
+    if args.kernels_only:
+        kernels_only(KERNEL_ONLY[args.kernels_only], args)
+        return
     wl = WORKLOADS[args.workload]
     cfg_kw = POOL_CFG[args.workload] if args.workload in POOL_CFG else POOL_CFG["resident_decode_32k"]
     st = setup(wl, cfg_kw, args.threads)

@@ -34,14 +34,15 @@ using VQ4 = VType<false>;
 using VQ8 = VType<true>;
 // Page record bytes per kv head.
 __host__ __device__ constexpr int head_record_bytes(bool v_q8) { return kKTile + (v_q8 ? VQ8::kTile : VQ4::kTile); }
-// Staged matrix-core operands of one (page, kv head): the f16 K and V^T
-// operands in fragment order, the K block scales per token as float32, and
-// the V scaling exponent of each 32-channel block (padded to keep tiles
-// 256-byte aligned).
+// Matrix-core operands of one (page, kv head) as the operand probe writes
+// them (kvs_debug_stage): the f16 K and V^T operands in fragment order, the K
+// block scales per token as float32, and the V scaling exponent of each
+// (64-token sub-block, 32-channel block) (padded to keep tiles 256-byte
+// aligned).
 constexpr int kStagedK = kPageTokens * kHeadDim * 2;          // K operands [16 token tiles][4 blocks][64 lanes] x 16 B
 constexpr int kStagedOps = 2 * kStagedK;                      // then V^T operands [8 chunks][8 channel tiles][64 lanes] x 16 B
 constexpr int kStagedScaleBytes = kPageTokens * kNB * 4;      // K scales [token][block] float32
-constexpr int kStagedShift = kStagedOps + kStagedScaleBytes;  // V shift per block, int32
+constexpr int kStagedShift = kStagedOps + kStagedScaleBytes;  // V shift per (sub-block, block), int32
 constexpr int kStagedTile = kStagedShift + 256;
 __host__ __device__ constexpr int staged_k_offset(int tt16, int b, int lane) { return ((tt16 * kNB + b) * 64 + lane) * 16; }
 __host__ __device__ constexpr int staged_v_offset(int c, int ct, int lane) { return kStagedK + ((c * 8 + ct) * 64 + lane) * 16; }
@@ -90,40 +91,53 @@ __host__ __device__ inline const uint8_t* page_ptr(const PageSource& ps, int32_t
 // copy n_pages page records from pinned host memory into consecutive ring
 // slots at ring_dst, while the other workgroups compute on earlier slots.
 constexpr int kMaxCopyPages = 16;
-constexpr int kCopyPartBytes = 32768;   // bytes per copy workgroup
+constexpr int kCopyPartBytes = 32768;   // bytes a copy workgroup moves per round
 struct CopyJob {
     const uint8_t* host;                // the layer's host records (page-major)
     uint8_t* ring_dst;                  // first ring slot to fill
     int64_t page_bytes;
+    int64_t part_bytes;                 // bytes per copy workgroup (a multiple of kCopyPartBytes)
     int32_t n_pages;                    // pages to copy (0: none)
     int32_t parts_per_page;             // copy workgroups per page
     int32_t pages[kMaxCopyPages];       // logical page of each copied slot
 };
 
-// Copy role of a workgroup: part `part` of the job's pages. Global loads of
-// the whole part are issued before any store so that many host-memory reads
-// are in flight over the link.
+// Copy role of a workgroup (its first 256 threads): part `part` of the job's
+// pages, in rounds of kCopyPartBytes. Each round's global loads are all
+// issued before any of its stores, so that many host-memory reads are in
+// flight over the link.
 __device__ inline void copy_role(const CopyJob& cj, int part) {
     const int page_i = part / cj.parts_per_page, sub = part % cj.parts_per_page;
     if (page_i >= cj.n_pages) return;
-    const int64_t off = (int64_t)sub * kCopyPartBytes;
-    const int64_t n = cj.page_bytes - off < kCopyPartBytes ? cj.page_bytes - off : kCopyPartBytes;
+    const int64_t off0 = (int64_t)sub * cj.part_bytes;
+    const int64_t end = cj.page_bytes - off0 < cj.part_bytes ? cj.page_bytes : off0 + cj.part_bytes;
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4* src = (const u32x4*)(cj.host + (int64_t)cj.pages[page_i] * cj.page_bytes + off);
-    u32x4* dst = (u32x4*)(cj.ring_dst + (int64_t)page_i * cj.page_bytes + off);
-    const int n16 = (int)(n / 16);
     constexpr int kPer = kCopyPartBytes / 16 / 256;   // 8 x 16 bytes per thread
-    u32x4 v[kPer];
+    for (int64_t off = off0; off < end; off += kCopyPartBytes) {
+        const int64_t n = end - off < kCopyPartBytes ? end - off : kCopyPartBytes;
+        const u32x4* src = (const u32x4*)(cj.host + (int64_t)cj.pages[page_i] * cj.page_bytes + off);
+        u32x4* dst = (u32x4*)(cj.ring_dst + (int64_t)page_i * cj.page_bytes + off);
+        const int n16 = (int)(n / 16);
+        u32x4 v[kPer];
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-        const int e = threadIdx.x + 256 * k;
-        if (e < n16) v[k] = __builtin_nontemporal_load(src + e);
-    }
+        for (int k = 0; k < kPer; ++k) {
+            const int e = threadIdx.x + 256 * k;
+            if (e < n16) v[k] = __builtin_nontemporal_load(src + e);
+        }
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-        const int e = threadIdx.x + 256 * k;
-        if (e < n16) dst[e] = v[k];
+        for (int k = 0; k < kPer; ++k) {
+            const int e = threadIdx.x + 256 * k;
+            if (e < n16) dst[e] = v[k];
+        }
     }
+}
+// The same job cut into parts of part_bytes (a multiple of kCopyPartBytes):
+// fewer, longer-running copy workgroups.
+inline CopyJob with_part_bytes(const CopyJob& cj, int64_t part_bytes) {
+    CopyJob r = cj;
+    r.part_bytes = part_bytes;
+    r.parts_per_page = (int32_t)((cj.page_bytes + part_bytes - 1) / part_bytes);
+    return r;
 }
 
 __host__ __device__ inline int copy_workgroups(const CopyJob& cj) {
@@ -146,7 +160,6 @@ struct AttendArgs {
     float scale_log2;     // scale * log2(e): scores are kept in log2 units
     int32_t causal;
     float* part;          // [n_groups][n_q][Hq][kPartStride]
-    const uint8_t* staged; // staged operands of this launch's pages (null: convert in the kernel)
     int32_t n_slices;     // matrix-core kernel: segment slices per (kv head, row tile), set at launch
     int32_t v_q8;         // V blocks are Q8_0 (else Q4_0)
 };
@@ -164,20 +177,6 @@ struct StageArgs {
     int32_t by_page;      // 1: page p goes to tile p (a probe of a whole layer), 0: the x-th page to tile x
     int32_t v_q8;         // V blocks are Q8_0 (else Q4_0)
 };
-
-// The first `first` pages of a copy job, or the rest (ring slots follow).
-inline CopyJob split_copy(const CopyJob& cj, int32_t first, bool head) {
-    CopyJob r = cj;
-    if (head) {
-        r.n_pages = first < cj.n_pages ? first : cj.n_pages;
-    } else {
-        const int32_t k = first < cj.n_pages ? first : cj.n_pages;
-        r.n_pages = cj.n_pages - k;
-        r.ring_dst = cj.ring_dst + (int64_t)k * cj.page_bytes;
-        for (int32_t i = 0; i < r.n_pages; ++i) r.pages[i] = cj.pages[k + i];
-    }
-    return r;
-}
 
 struct GatherArgs {
     CopyJob copy;
@@ -241,10 +240,10 @@ bool decode_supports(int rows);
 hipError_t launch_decode(const AttendArgs& a, hipStream_t stream);
 // matrix-core kernel (kvs_mfma.hip) for more rows
 hipError_t launch_mfma(const AttendArgs& a, hipStream_t stream);
-// prefill kernel on staged operands (kvs_prefill.hip), for blocks of more than
-// 64 rows per kv head
+// prefill kernel (kvs_prefill.hip), for blocks of more than 64 rows per kv head
 hipError_t launch_prefill(const AttendArgs& a, hipStream_t stream);
-bool mfma_stages(int rows);   // rows per kv head for which launches stage their pages first
+bool prefill_rows(int rows);   // rows per kv head that the prefill kernel takes
+// staging probe: each page's matrix-core operands written out (kvs_mfma.hip)
 hipError_t launch_stage(const StageArgs& a, hipStream_t stream);
 hipError_t launch_combine(const float* part, int32_t n_groups, int32_t n_q, int32_t n_q_heads,
                           float* out, float* lse, hipStream_t stream);

@@ -103,6 +103,56 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
+// Split-K combine for blocks with many rows (a prefill ubatch): one wave per
+// output row. Lane l holds channels 2 l and 2 l + 1 and folds the groups in
+// ascending order, 8 records per step so that 8 coalesced 512-byte record
+// loads are in flight; the row's m and l are uniform loads. The order depends
+// only on the number of groups.
+// ---------------------------------------------------------------------------
+constexpr int kCombRowsMin = 512;   // rows from which a launch takes this kernel
+__global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restrict__ part, int32_t n_groups,
+                                                           int32_t rows, float* __restrict__ out,
+                                                           float* __restrict__ lse) {
+    const int row = __builtin_amdgcn_readfirstlane((int)blockIdx.x * 4 + ((int)threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    const int64_t gstride = (int64_t)rows * kPartStride;
+    const float* p = part + (int64_t)row * kPartStride;
+    float M = -INFINITY, L = 0.f, O0 = 0.f, O1 = 0.f;
+    for (int g0 = 0; g0 < n_groups; g0 += kCombBatch) {
+        float2 ml[kCombBatch], og[kCombBatch];
+#pragma unroll
+        for (int k = 0; k < kCombBatch; ++k) {
+            const int gi = g0 + k;
+            const bool ok = gi < n_groups;   // uniform
+            const float* q = p + (int64_t)(ok ? gi : 0) * gstride;
+            ml[k] = *(const float2*)(q + kHeadDim);
+            og[k] = *(const float2*)(q + 2 * lane);
+            if (!ok) ml[k].x = -INFINITY;
+        }
+        float Mb = M;
+#pragma unroll
+        for (int k = 0; k < kCombBatch; ++k) Mb = fmaxf(Mb, ml[k].x);
+        if (Mb == -INFINITY) continue;
+        const float sc = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - Mb);
+        L *= sc;
+        O0 *= sc;
+        O1 *= sc;
+#pragma unroll
+        for (int k = 0; k < kCombBatch; ++k) {
+            const float wk = (ml[k].x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml[k].x - Mb);
+            L = fmaf(ml[k].y, wk, L);
+            O0 = fmaf(og[k].x, wk, O0);
+            O1 = fmaf(og[k].y, wk, O1);
+        }
+        M = Mb;
+    }
+    const bool empty = M == -INFINITY;
+    *(float2*)(out + (int64_t)row * kHeadDim + 2 * lane) = empty ? make_float2(0.f, 0.f) : make_float2(O0 / L, O1 / L);
+    if (lse && lane == 0) lse[row] = empty ? -INFINITY : (M + log2f(L)) * 0.69314718055994530942f;
+}
+
+// ---------------------------------------------------------------------------
 // Gather probe: dequantize tokens of the launch's pages into float32 through
 // the block decoding the attention kernels use (kvs_device.h): each Q8_0 code
 // and Q4_0 nibble becomes an exact f16 value, multiplied by the float32 block
@@ -239,6 +289,8 @@ hipError_t launch_combine(const float* part, int32_t n_groups, int32_t n_q, int3
                           float* out, float* lse, hipStream_t stream) {
     const int rows = n_q * n_q_heads;
     if (rows <= 0) return hipSuccess;
+    if (rows >= kCombRowsMin)
+        return launch_kernel(combine_rows_kernel, dim3((rows + 3) / 4), dim3(256), stream, part, n_groups, rows, out, lse);
     return launch_kernel(combine_kernel, dim3(rows, kCombSlices), dim3(256), stream, part, n_groups, rows, out, lse);
 }
 

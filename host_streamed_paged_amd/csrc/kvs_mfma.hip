@@ -48,6 +48,7 @@
 
 #include "kvs_internal.h"
 #include "kvs_device.h"
+#include "kvs_convert.h"
 
 namespace kvs {
 namespace {
@@ -62,11 +63,6 @@ constexpr int kChunks = kPageTokens / 32;     // 32-token MFMA chunks per page i
 // The running max moves only when a page's max exceeds it by more than this
 // (log2 units), so p <= 2^8 stays well inside f16 and O is rarely rescaled.
 constexpr float kLazyMax = 8.f;
-// A V block scale of magnitude above 8188 (binary16 bits 0x6FFF) can make
-// d * (u - 8) exceed the largest f16, 65504; such pages take the V operand
-// divided by 2^kVShift.
-constexpr uint32_t kVBigBits = 0x6FFFu;
-constexpr int kVShift = 3;
 
 // LDS of the kernel (see mfma_kernel): one page's K tile and V tile in
 // record layout, the P operands [chunk][row tile][lane] (16 bytes each) in a
@@ -98,36 +94,6 @@ __device__ inline void dma_v_tile(const uint8_t* rec, int g, int n_kv_heads, uin
     }
 }
 
-// K operand of v_mfma_f32_16x16x32_f16 for A_b^T = K_b . Q_b^T: this lane's 8
-// codes [32 b + 8 gq, +8) of token `tok` of the K tile (record layout, in
-// LDS) as exact f16, and the block's scale bits. Split into the LDS reads
-// (k_raw) and the conversion (k_codes) so that a caller can read the next
-// fragments while converting the current ones.
-struct KRaw {
-    uint32_t x0, x1, x2;   // 3 aligned dwords (even blocks) or 2 (odd blocks)
-    uint32_t db;           // scale bits
-};
-__device__ inline KRaw k_raw(const uint8_t* k_lds, int tok, int b, int gq) {
-    const uint8_t* blk = k_lds + tok * kKRow + b * kKBlock;
-    KRaw r;
-    if (b & 1) {   // codes start on a dword boundary
-        const uint32_t* p = (const uint32_t*)(blk + 2 + 8 * gq);
-        r.x0 = p[0];
-        r.x1 = p[1];
-        r.x2 = 0u;
-    } else {       // codes start 2 bytes into a dword
-        const uint32_t* p = (const uint32_t*)(blk + 8 * gq);
-        r.x0 = p[0];
-        r.x1 = p[1];
-        r.x2 = p[2];
-    }
-    r.db = *(const uint16_t*)blk;
-    return r;
-}
-__device__ inline half8_t k_codes(const KRaw& r, int b) {
-    if (b & 1) return q8_codes_f16(r.x0, r.x1);
-    return q8_codes_f16(__builtin_amdgcn_alignbyte(r.x1, r.x0, 2), __builtin_amdgcn_alignbyte(r.x2, r.x1, 2));
-}
 
 // Block scales of this lane's four score tokens of a tile (token 4 gq + i of
 // the tile), from the 16 binary16 values [i][b] in two 16-byte words (sa:
@@ -154,86 +120,6 @@ __device__ inline void add_block(f32x4& s, const f32x4& a, const float (&d)[4][k
     }
 }
 
-// V shift of quant block b of a page (V tile in LDS, record layout): for
-// Q4_0, kVShift if a cached row's scale magnitude exceeds 8188, else 0; for
-// Q8_0 (|code| <= 128), kVShift8 if one exceeds 511.75 (bits 0x5FFF), so
-// that d * code / 2^shift stays within 65504. Rows at or past `valid` are not
-// cached and may hold any bytes. Wave-uniform.
-constexpr uint32_t kVBigBits8 = 0x5FFFu;
-constexpr int kVShift8 = 7;
-template <typename VT>
-__device__ inline int v_shift_of(const uint8_t* v_lds, int b, int valid, int lane) {
-    uint32_t mx = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int t = lane + 64 * j;
-        const uint32_t bits = *(const uint16_t*)(v_lds + t * VT::kRow + b * VT::kBlock) & 0x7FFFu;
-        mx = (t < valid && bits > mx) ? bits : mx;
-    }
-    if constexpr (VT::kQ8) return __any(mx > kVBigBits8) ? kVShift8 : 0;
-    return __any(mx > kVBigBits) ? kVShift : 0;
-}
-
-// V^T operands of O^T += V^T . P^T for chunk c (tokens [32 c, 32 c + 32)) and
-// quant block b: vop[0] holds channel 32 b + n, vop[1] channel 32 b + 16 + n
-// (Q4_0: low and high nibbles of byte n; Q8_0: codes n and 16 + n), for the
-// lane's 8 token slots: slot j of lane group gq is token 32 c + 4 gq + j for
-// j < 4, else 32 c + 12 + 4 gq + j. Each value is d * (u - 8) / 2^vshift or
-// d * code / 2^vshift rounded once to f16 ((u - 8) / 2^vshift and
-// code / 2^vshift are exact, and the product of two f16 values is rounded
-// once). TAIL zeroes rows at or past `valid` (their scales may be NaN). Split
-// into the LDS reads (v_raw) and the arithmetic (v_convert), like the K
-// operand.
-template <typename VT>
-struct VRaw {
-    uint32_t byte[8];                   // byte n of the slot's token (Q4_0 nibbles, Q8_0 code n)
-    uint32_t hbyte[VT::kQ8 ? 8 : 1];    // Q8_0: code 16 + n
-    uint32_t d[8];                      // scale bits of the slot's token
-};
-template <typename VT>
-__device__ inline VRaw<VT> v_raw(const uint8_t* v_lds, int b, int c, int gq, int n) {
-    const uint8_t* vlane = v_lds + b * VT::kBlock + 4 * gq * VT::kRow;
-    VRaw<VT> r;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const uint8_t* row = vlane + (32 * c + (j < 4 ? j : 12 + j)) * VT::kRow;
-        r.byte[j] = row[2 + n];
-        if constexpr (VT::kQ8) r.hbyte[j] = row[18 + n];
-        r.d[j] = *(const uint16_t*)row;
-    }
-    return r;
-}
-template <bool TAIL, typename VT>
-__device__ inline void v_convert(const VRaw<VT>& r, int c, int gq, int valid, int vshift, uint32_t m_nib, uint32_t magic,
-                                 half8_t (&vop)[2]) {
-    const _Float16 cs = vshift ? (VT::kQ8 ? (_Float16)0.0078125f : (_Float16)0.125f) : (_Float16)1.f;
-    const half2_t cc = {cs, cs};
-    const half2_t off = {(_Float16)-1032.f * cs, (_Float16)-1032.f * cs};
-    const half2_t off8 = {(_Float16)-1152.f * cs, (_Float16)-1152.f * cs};
-#pragma unroll
-    for (int jp = 0; jp < 4; ++jp) {
-        const int j0 = 2 * jp, j1 = 2 * jp + 1;
-        uint32_t d0 = r.d[j0], d1 = r.d[j1];
-        if constexpr (TAIL) {
-            const int o0 = 32 * c + (j0 < 4 ? j0 : 12 + j0), o1 = 32 * c + (j1 < 4 ? j1 : 12 + j1);
-            d0 = o0 + 4 * gq < valid ? d0 : 0u;
-            d1 = o1 + 4 * gq < valid ? d1 : 0u;
-        }
-        const half2_t dd = as_h2(d0 | (d1 << 16));
-        const uint32_t x = __builtin_amdgcn_perm(r.byte[j1], r.byte[j0], 0x0c040c00u);
-        half2_t lo, hi;
-        if constexpr (VT::kQ8) {
-            const uint32_t xh = __builtin_amdgcn_perm(r.hbyte[j1], r.hbyte[j0], 0x0c040c00u);
-            lo = q8_pair_f16(x, cc, off8) * dd;                  // channel n
-            hi = q8_pair_f16(xh, cc, off8) * dd;                 // channel 16 + n
-        } else {
-            lo = q4_nibbles_f16((x & m_nib) | magic, cc, off) * dd;          // channel n
-            hi = q4_nibbles_f16(((x >> 4) & m_nib) | magic, cc, off) * dd;   // channel 16 + n
-        }
-        vop[0][j0] = lo[0]; vop[0][j1] = lo[1];
-        vop[1][j0] = hi[0]; vop[1][j1] = hi[1];
-    }
-}
 
 // Workgroups per CU the register budget is cut for.
 #ifndef KVS_MFMA_OCC
@@ -553,66 +439,6 @@ void mfma_kernel(AttendArgs a) {
   }
 }
 
-// Converts each (page, kv head) of a launch once into f16 matrix-core
-// operands, block scales and V shifts (the staged mode above). Grid: (pages
-// of the launch, kv heads); block x stages the x-th page of the launch's
-// segments, in segment order, into staged tile x (or, with by_page, into
-// tile `page`); blocks past the pages are ring refill workgroups.
-template <typename VT>
-__global__ __launch_bounds__(kThreads) void stage_kernel(StageArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t k_lds[kKTile];
-    __shared__ __attribute__((aligned(16))) uint8_t v_lds[VT::kTile];
-    if ((int)blockIdx.x >= a.n_pages) {   // ring refill workgroup
-        copy_role(a.copy, ((int)blockIdx.x - a.n_pages) * (int)gridDim.y + (int)blockIdx.y);
-        return;
-    }
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    const int n = lane & 15, gq = lane >> 4;
-    const int slot = blockIdx.x, g = blockIdx.y;
-    int rem = slot;
-    int32_t page = -1;
-    for (int si = 0; si < a.n_segs; ++si) {
-        const int np = scalar_load(&a.segs[si].npages);
-        if (rem < np) { page = scalar_load(&a.segs[si].page0) + rem; break; }
-        rem -= np;
-    }
-    if (page < 0) return;   // past the launch's pages
-    {
-        const uint8_t* rec = page_record(a.ps, page);
-        dma_k_tile(rec, g, k_lds, w, lane);
-        dma_v_tile<VT>(rec, g, a.n_kv_heads, v_lds, w, lane);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    lds_barrier();
-    uint8_t* tile = a.staged + ((int64_t)(a.by_page ? page : slot) * a.n_kv_heads + g) * kStagedTile;
-    // K: wave w converts token tiles 4 w .. 4 w + 3, as the QK role does
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int b = 0; b < kNB; ++b)
-            *(half8_t*)(tile + staged_k_offset(4 * w + tt, b, lane)) = k_codes(k_raw(k_lds, kTokW * w + 16 * tt + n, b, gq), b);
-    // K block scales per token as float32 (exact): thread t writes token t's four
-    {
-        const uint8_t* row = k_lds + tid * kKRow;
-        *(f32x4*)(tile + staged_scale_offset(tid)) =
-            f32x4{scale_f32(*(const uint16_t*)row), scale_f32(*(const uint16_t*)(row + kKBlock)),
-                  scale_f32(*(const uint16_t*)(row + 2 * kKBlock)), scale_f32(*(const uint16_t*)(row + 3 * kKBlock))};
-    }
-    // V: wave w converts block w (channel tiles 2 w, 2 w + 1), as the PV role does
-    const int64_t vx = a.n_kv - (int64_t)page * kPageTokens;
-    const int valid = (int)(vx < 0 ? 0 : (vx > kPageTokens ? kPageTokens : vx));
-    const int vsh = v_shift_of<VT>(v_lds, w, valid, lane);
-    if (lane == 0) *((int32_t*)(tile + kStagedShift) + w) = vsh;
-    const uint32_t m_nib = vconst(0x000F000Fu), magic = vconst(0x64006400u);
-#pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-        half8_t vop[2];
-        v_convert<true, VT>(v_raw<VT>(v_lds, w, c, gq, n), c, gq, valid, vsh, m_nib, magic, vop);
-        *(half8_t*)(tile + staged_v_offset(c, 2 * w, lane)) = vop[0];
-        *(half8_t*)(tile + staged_v_offset(c, 2 * w + 1, lane)) = vop[1];
-    }
-}
-
 int compute_units() {
     static int cus[64] = {0};
     int dev = 0;
@@ -648,21 +474,15 @@ hipError_t launch_rt(const AttendArgs& a, hipStream_t stream) {
 }  // namespace
 
 // 16-row tiles (with two query limbs, wider tiles would not fit two
-// workgroups' registers per compute unit); staged launches go to the prefill
-// kernel.
+// workgroups' registers per compute unit); blocks of more than 64 rows per
+// kv head go to the prefill kernel.
 hipError_t launch_mfma(const AttendArgs& a, hipStream_t stream) {
     if (a.n_segs <= 0 && copy_workgroups(a.copy) == 0) return hipSuccess;
-    if (a.staged) return launch_prefill(a, stream);
+    if (prefill_rows(a.n_q * a.G)) return launch_prefill(a, stream);
     return a.q_f16 ? launch_rt<1, 1>(a, stream) : launch_rt<1, 2>(a, stream);
 }
 
-bool mfma_stages(int rows) { return rows > 64; }
+bool prefill_rows(int rows) { return rows > 64; }
 
-hipError_t launch_stage(const StageArgs& a, hipStream_t stream) {
-    const int cx = (copy_workgroups(a.copy) + a.n_kv_heads - 1) / a.n_kv_heads;
-    if (a.n_pages <= 0 && cx == 0) return hipSuccess;
-    if (a.v_q8) return launch_kernel(stage_kernel<VQ8>, dim3(a.n_pages + cx, a.n_kv_heads), dim3(kThreads), stream, a);
-    return launch_kernel(stage_kernel<VQ4>, dim3(a.n_pages + cx, a.n_kv_heads), dim3(kThreads), stream, a);
-}
 
 }  // namespace kvs

@@ -37,65 +37,163 @@
 
 #include "kvs_internal.h"
 #include "kvs_device.h"
+#include "kvs_convert.h"
 
 namespace kvs {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int int4v __attribute__((ext_vector_type(4)));
 
-#ifndef KVS_PF_WAVES
-#define KVS_PF_WAVES 8
-#endif
-#ifndef KVS_PF_RTW
-#define KVS_PF_RTW 2
-#endif
-constexpr int kPWaves = KVS_PF_WAVES;
+constexpr int kPWaves = 8;
 constexpr int kPThreads = 64 * kPWaves;
-constexpr int kRTW = KVS_PF_RTW;             // 16-row tiles per wave
+constexpr int kRTW = 2;                      // 16-row tiles per wave
 constexpr int kRowsWG = 16 * kRTW * kPWaves; // rows per workgroup (256)
 constexpr int kSub = 64;                     // tokens per sub-block
 constexpr int kSubs = kPageTokens / kSub;    // sub-blocks per page
-constexpr int kSubK = 4 * kNB * 64 * 16;     // K fragments of a sub-block (16 KB)
-constexpr int kSubV = 2 * 8 * 64 * 16;       // V^T fragments of a sub-block (two 32-token chunks, 16 KB)
-constexpr int kSubS = kSub * kNB * 4;        // float32 K scales of a sub-block (1 KB)
-constexpr int kSubBytes = kSubK + kSubV + kSubS;
-constexpr int kSubPieces = kSubBytes / 1024; // 1 KB LDS DMA pieces (one wave instruction each)
-static_assert(kSubBytes % 1024 == 0, "sub-block is whole 1 KB pieces");
+// Operands of a sub-block in LDS: K fragments [4 token tiles][4 blocks][64
+// lanes] x 16 B, V^T fragments [2 chunks][8 channel tiles][64 lanes] x 16 B,
+// the K block scales [token][block] float32, the V shift of each block.
+constexpr int kSubK = 4 * kNB * 64 * 16;       // 16 KB
+constexpr int kSubV = 2 * 8 * 64 * 16;         // 16 KB
+constexpr int kSubS = kSub * kNB * 4;          // 1 KB
+constexpr int kConvShift = kSubK + kSubV + kSubS;   // 16 B per block: its shift, 4 times
+constexpr int kConvBytes = kConvShift + 16 * kNB;
+// A sub-block's raw rows for one kv head as the record holds them: 64 K rows
+// (136 B each) then 64 V rows, moved by 1 KB LDS DMA pieces.
+template <typename VT>
+struct RawSub {
+    static constexpr int kK = kSub * kKRow;                  // 8704 B
+    static constexpr int kBytes = kK + kSub * VT::kRow;      // 13312 (Q4_0 V) / 17408 (Q8_0 V)
+    static constexpr int kPieces = kBytes / 1024;
+    static constexpr int kWavePieces = (kPieces + kPWaves - 1) / kPWaves;   // DMA instructions per wave
+    static_assert(kBytes % 1024 == 0 && kK % 16 == 0, "raw sub-block is whole 1 KB pieces");
+};
 constexpr float kLazyMax = 8.f;
-#ifndef KVS_PF_OCC
-#define KVS_PF_OCC 1
-#endif
 
-// Three sub-block buffers (the one in use and two in flight), each its own
-// LDS array: the compiler then orders a read of one buffer only after the
-// DMA into that buffer, not after the DMAs still in flight into the others.
+// s_waitcnt immediate: vmcnt(n) (6 bits, split over bits 3:0 and 15:14), the
+// other counters not waited on
+constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
-// Issue this wave's share of the LDS DMA of sub-block sb of a staged tile:
-// piece p (1 KB) of [K | V^T | scales] goes to dst + 1024 p.
-__device__ inline void dma_sub(const uint8_t* tile, int sb, uint8_t* dst, int w, int lane) {
+// Issue this wave's share of the LDS DMA of raw sub-block sb of kv head g of
+// page record rec into dst: byte o of [K rows | V rows] comes from the K tile
+// (o < 8704) or the V tile, in 16-byte lane pieces.
+// Every wave issues exactly kWavePieces instructions (a wave past the last
+// piece copies the last piece again, the same bytes to the same place), so
+// the code has no branch and the count of DMAs in flight is fixed. The
+// source addresses are returned so that the caller can keep their registers
+// from being rewritten while the DMAs are in flight (the compiler would
+// otherwise wait for the DMAs before reusing them).
+template <typename VT>
+struct DmaAddr {
+    const uint8_t* src[RawSub<VT>::kWavePieces];
+};
+template <typename VT>
+__device__ inline DmaAddr<VT> dma_raw(const uint8_t* rec, int g, int n_kv_heads, int sb, uint8_t* dst, int w, int lane) {
+    const uint8_t* kt = rec + (int64_t)g * kKTile + sb * RawSub<VT>::kK;
+    const uint8_t* vt = rec + (int64_t)n_kv_heads * kKTile + (int64_t)g * VT::kTile + sb * kSub * VT::kRow;
+    DmaAddr<VT> ad;
 #pragma unroll
-    for (int k = 0; k < (kSubPieces + kPWaves - 1) / kPWaves; ++k) {
-        const int p = w + kPWaves * k;
-        if (p >= kSubPieces) break;
-        const uint8_t* src;
-        if (p < kSubK / 1024) src = tile + sb * kSubK + p * 1024;
-        else if (p < (kSubK + kSubV) / 1024) src = tile + kStagedK + sb * kSubV + (p - kSubK / 1024) * 1024;
-        else src = tile + kStagedOps + sb * kSubS + (p - (kSubK + kSubV) / 1024) * 1024;
-        dma16(src + 16 * lane, dst + 1024 * p);
+    for (int k = 0; k < RawSub<VT>::kWavePieces; ++k) {
+        const int p = min(w + kPWaves * k, RawSub<VT>::kPieces - 1);
+        const int o = 1024 * p + 16 * lane;
+        ad.src[k] = o < RawSub<VT>::kK ? kt + o : vt + (o - RawSub<VT>::kK);
+        dma16(ad.src[k], dst + 1024 * p);
     }
+    return ad;
+}
+template <typename VT>
+__device__ inline void keep(const DmaAddr<VT>& ad) {
+#pragma unroll
+    for (int k = 0; k < RawSub<VT>::kWavePieces; ++k) asm volatile("" ::"v"(ad.src[k]));
 }
 
-template <int LIMBS>
-__global__ __launch_bounds__(kPThreads, KVS_PF_OCC) void prefill_kernel(AttendArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t buf0[kSubBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t buf1[kSubBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t buf2[kSubBytes];
+// Convert a raw sub-block (LDS rw) into its operands (LDS cv), with the
+// conversion code of the other matrix-core paths (kvs_convert.h); `valid`
+// rows of the sub-block are cached. Wave w converts K fragments (tile, block)
+// = (w >> 2, w & 3) and (2 + (w >> 2), w & 3), their block scales, and V^T
+// chunk w >> 2 of block w & 3. The code has no branch.
+template <typename VT>
+__device__ inline void convert_sub(const uint8_t* rw, uint8_t* cv, int valid, int tid, int w, int lane,
+                                   uint32_t m_nib, uint32_t magic) {
+    const int n = lane & 15, gq = lane >> 4, b = w & 3, c = w >> 2;
+    // The lane's 8 codes start at byte 34 b + 2 + 8 gq of its token's row:
+    // three dwords from the dword holding that byte, shifted by 2 bytes for
+    // an even block (the same codes k_codes takes; for the last block the
+    // third dword lies past the row, inside the buffer, and is not used).
+    // Lane offsets are made opaque so that the compiler forms each address
+    // here instead of holding one per buffer across the caller's loop.
+    const int kofs = kKBlock * b + 2 + 8 * gq, ksh = kofs & 3;
+    // Scales: lane l of wave w takes the four block scales of token
+    // 8 w + (l & 7) (eight lanes write the same 16 bytes, so the code has no
+    // branch). Every LDS access here is a whole dword or wider.
+    const int stok = 8 * w + (lane & 7);
+    uint32_t ko = n * kKRow + (kofs - ksh), so = stok * kKRow, oo = lane * 16;
+    const int vsh_b = (VT::kBlock * b) & 3;   // block b starts 0 or 2 bytes into a dword
+    uint32_t vo = RawSub<VT>::kK + b * VT::kBlock - vsh_b + 4 * gq * VT::kRow, st16 = 16 * stok;
+    asm volatile("" : "+v"(ko), "+v"(so), "+v"(oo), "+v"(vo), "+v"(st16));
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int f = w + 8 * k;   // (tile, block) = (f >> 2, b)
+        const uint32_t* p = (const uint32_t*)(rw + 16 * (f >> 2) * kKRow + ko);
+        const uint32_t x0 = p[0], x1 = p[1], x2 = p[2];
+        *(half8_t*)(cv + f * 1024 + oo) =
+            q8_codes_f16(__builtin_amdgcn_alignbyte(x1, x0, ksh), __builtin_amdgcn_alignbyte(x2, x1, ksh));
+    }
+    {
+        // the row's block scales: blocks 0, 1 in dword 0 and dword 8 (byte
+        // 34 = 32 + 2), blocks 2, 3 in dword 17 and dword 25 (byte 102)
+        const uint32_t* rp = (const uint32_t*)(rw + so);
+        const uint32_t d0 = rp[0], d1 = rp[8], d2 = rp[17], d3 = rp[25];
+        *(f32x4*)(cv + kSubK + kSubV + st16) = f32x4{scale_f32(d0), scale_f32(d1 >> 16), scale_f32(d2), scale_f32(d3 >> 16)};
+    }
+    // Block b's V rows as whole dwords: an even block starts on a dword
+    // boundary (its scale is the dword's low half), an odd one 2 bytes into
+    // one (the high half); byte n of the codes follows 2 bytes after the
+    // scale.
+    // the sub-block's V shift of block b (v_shift_of over 64 rows, on the
+    // same scale bits); every lane of the two waves of block b writes it
+    uint32_t vs = RawSub<VT>::kK + lane * VT::kRow + VT::kBlock * b - vsh_b;
+    asm volatile("" : "+v"(vs));
+    const uint32_t w0 = *(const uint32_t*)(rw + vs);
+    const uint32_t sbits = (vsh_b ? w0 >> 16 : w0) & 0x7FFFu;
+    const int vsh = __any(lane < valid && sbits > (VT::kQ8 ? kVBigBits8 : kVBigBits)) ? (VT::kQ8 ? kVShift8 : kVShift) : 0;
+    *(int4v*)(cv + kConvShift + 16 * b) = int4v{vsh, vsh, vsh, vsh};
+    // the V rows of v_raw (kvs_convert.h), through the opaque lane offset
+    VRaw<VT> vr;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t* rd = (const uint32_t*)(rw + vo + (32 * c + (j < 4 ? j : 12 + j)) * VT::kRow);
+        vr.d[j] = vsh_b ? rd[0] >> 16 : rd[0] & 0xFFFFu;
+        const uint32_t cb = (uint32_t)(2 + vsh_b + n);                     // byte of code n from rd
+        vr.byte[j] = (rd[cb >> 2] >> (8 * (cb & 3))) & 0xFFu;
+        if constexpr (VT::kQ8) vr.hbyte[j] = (rd[(cb + 16) >> 2] >> (8 * ((cb + 16) & 3))) & 0xFFu;
+    }
+    half8_t vop[2];
+    v_convert<true, VT>(vr, c, gq, valid, vsh, m_nib, magic, vop);
+    *(half8_t*)(cv + kSubK + (c * 8 + 2 * b) * 1024 + oo) = vop[0];
+    *(half8_t*)(cv + kSubK + (c * 8 + 2 * b + 1) * 1024 + oo) = vop[1];
+}
+
+template <int LIMBS, typename VT>
+__global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(AttendArgs a) {
+    // Two operand buffers (the sub-block being computed and the next one
+    // being converted) and four raw buffers (the one being converted and
+    // DMAs in flight), each its own LDS array: the compiler then orders a
+    // read of one array only after the DMA into that array, not after DMAs
+    // still in flight into the others.
+    __shared__ __attribute__((aligned(16))) uint8_t cv0[kConvBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t cv1[kConvBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t rw0[RawSub<VT>::kBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t rw1[RawSub<VT>::kBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t rw2[RawSub<VT>::kBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t rw3[RawSub<VT>::kBytes];
     // 1-D grid: ring refill workgroups first, then one worker per (segment,
     // kv head, row block), row blocks of one (segment, kv head) consecutive.
     // Workgroups go to the 8 XCDs round-robin by linear index; workers are
     // permuted so that each XCD takes a contiguous range, and the row blocks
-    // of one (segment, kv head), which read the same staged tiles, share an
-    // XCD's L2.
+    // of one (segment, kv head), which read the same pages, share an XCD's
+    // L2.
     const int G = a.G, R = a.n_q * G;
     const int n_rb = (R + kRowsWG - 1) / kRowsWG;
     const int n_copy8 = (copy_workgroups(a.copy) + 7) & ~7;
@@ -111,27 +209,39 @@ __global__ __launch_bounds__(kPThreads, KVS_PF_OCC) void prefill_kernel(AttendAr
     const int seg_i = work / (n_rb * a.n_kv_heads);
     const int g = (work / n_rb) % a.n_kv_heads;
     const int rb = work % n_rb;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int n = lane & 15, gq = lane >> 4;
     const int r0 = rb * kRowsWG + 16 * kRTW * w;   // this wave's first row
 
-    typedef int int4v __attribute__((ext_vector_type(4)));
     const int4v segv = scalar_load((const int4v*)(a.segs + seg_i));
     const Seg seg = {segv.x, segv.y, segv.z, segv.w};
-    // staged tiles of the segment's first page for kv head g: pages of the
-    // launch's segments are staged in order
-    int first = 0;
-    for (int i = 0; i < seg_i; ++i) first += scalar_load(&a.segs[i].npages);
-    const int64_t tile_step = (int64_t)a.n_kv_heads * kStagedTile;
-    const uint8_t* tile0 = a.staged + ((int64_t)first * a.n_kv_heads + g) * kStagedTile;
     const int n_steps = seg.npages * kSubs;
-    dma_sub(tile0, 0, buf0, w, lane);
-    if (n_steps > 1) dma_sub(tile0, 1, buf1, w, lane);
+    // the record of the segment's page pi, by selects (no branch)
+    auto record = [&](int pi) {
+        const int32_t page = seg.page0 + pi;
+        const int32_t sv = scalar_load(a.ps.src + page);
+        const uint8_t* res = a.ps.slots + (int64_t)sv * a.ps.page_bytes;
+        const uint8_t* str = a.ps.host ? a.ps.host + (int64_t)page * a.ps.page_bytes
+                                       : a.ps.ring_chunk + (int64_t)((-1 - sv) - a.ps.chunk_rank0) * a.ps.page_bytes;
+        return sv >= 0 ? res : str;
+    };
+    auto dma_step = [&](int st, uint8_t* dst) {
+        return dma_raw<VT>(record(st / kSubs), g, a.n_kv_heads, st % kSubs, dst, w, lane);
+    };
+    // cached rows of sub-block st
+    auto valid_of = [&](int st) {
+        const int64_t x = a.n_kv - ((int64_t)(seg.page0 + st / kSubs) * kPageTokens + kSub * (st % kSubs));
+        return (int)(x < 0 ? 0 : (x > kSub ? kSub : x));
+    };
 
-    // ---- this lane's query rows and their visible prefix
+    // ---- this lane's query rows and their visible prefix, counted from the
+    // segment's first token (clamped to the segment)
+    const int64_t seg_tok = (int64_t)seg.page0 * kPageTokens;
+    const int seg_len = n_steps * kSub;
+    auto rel = [&](int64_t t) { const int64_t x = t - seg_tok; return (int)(x < 0 ? 0 : (x > seg_len ? seg_len : x)); };
     half8_t qop[kRTW][LIMBS][kNB];
     float cq[kRTW];
-    int64_t lim[kRTW];
+    int lim[kRTW];
     int qi_[kRTW], h_[kRTW];
 #pragma unroll
     for (int rt = 0; rt < kRTW; ++rt) {
@@ -140,11 +250,12 @@ __global__ __launch_bounds__(kPThreads, KVS_PF_OCC) void prefill_kernel(AttendAr
         h_[rt] = g * G + r % G;
         lim[rt] = 0;
         if (r < R) {
-            lim[rt] = a.n_kv;
+            int64_t l = a.n_kv;
             if (a.causal) {
                 const int64_t c = a.q_pos0 + qi_[rt] + 1;
-                lim[rt] = c < lim[rt] ? c : lim[rt];
+                l = c < l ? c : l;
             }
+            lim[rt] = rel(l);
         }
         query_operands<LIMBS>(a, qi_[rt], h_[rt], r < R, gq, qop[rt], cq[rt]);
     }
@@ -154,6 +265,7 @@ __global__ __launch_bounds__(kPThreads, KVS_PF_OCC) void prefill_kernel(AttendAr
         const int64_t c = a.q_pos0 + r0 / G + 1;
         lim_min = c < lim_min ? c : lim_min;
     }
+    const int lim_min_rel = rel(lim_min);
 
     // ---- running state: O^T tiles [ct][rt] hold channels 16 ct + 4 gq + i of
     // row 16 rt + n, block b's in units of 2^vsh_run[b]; lsum[rt] holds the
@@ -183,26 +295,19 @@ __global__ __launch_bounds__(kPThreads, KVS_PF_OCC) void prefill_kernel(AttendAr
     half8_t ones;
 #pragma unroll
     for (int j = 0; j < 8; ++j) ones[j] = (_Float16)1.f;
+    const uint32_t m_nib = vconst(0x000F000Fu), magic = vconst(0x64006400u);
+    // The first raw sub-blocks' DMAs go out after the query and state loads,
+    // so that the wait for the first sub-block also covers every load into
+    // registers (loads complete in order): no register of the loop below then
+    // waits on a load.
+    dma_step(0, rw0);
+    dma_step(min(1, n_steps - 1), rw1);
+    dma_step(min(2, n_steps - 1), rw2);
 
-    // one step: compute sub-block `step` from B, the DMA of step + 2 goes to D
-    auto do_step = [&](int step, const uint8_t* B, uint8_t* D) {
-        const int pi = step / kSubs, sb = step % kSubs;
-        const int page = seg.page0 + pi;
-        const uint8_t* tile = tile0 + pi * tile_step;
-        // this sub-block is in LDS for every wave (a wave has at most one later
-        // sub-block's DMA in flight: 4 or 5 instructions), and every wave is
-        // done with the buffer two sub-blocks ahead goes into
-        // (the builtin, unlike inline asm, is known to the compiler's wait
-        // tracking: it then needs no wait of its own before the reads)
-        if (step + 1 < n_steps) __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4)
-        else __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0)
-        lds_barrier();
-        if (step + 2 < n_steps) {
-            const int pn = (step + 2) / kSubs, sn = (step + 2) % kSubs;
-            dma_sub(tile0 + pn * tile_step, sn, D, w, lane);
-        }
-        const int64_t base_tok = (int64_t)page * kPageTokens + kSub * sb;
-        const bool mask_sub = base_tok + kSub > lim_min;   // wave-uniform
+    // ---- one sub-block from its operands in B
+    auto compute = [&](int st, const uint8_t* B) {
+        const int base_tok = kSub * st;                     // from the segment's first token
+        const bool mask_sub = base_tok + kSub > lim_min_rel;   // wave-uniform
 
         // ---- QK (float32 products; cq * s is the log2-unit score)
         f32x4 s[4][kRTW];
@@ -221,25 +326,27 @@ __global__ __launch_bounds__(kPThreads, KVS_PF_OCC) void prefill_kernel(AttendAr
             }
             // scales of the lane's four tokens 16 tt + 4 gq + i: [i][b] float32
             const f32x4* sc = (const f32x4*)(B + kSubK + kSubV + (16 * tt + 4 * gq) * kNB * 4);
-            f32x4 d[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) d[i] = sc[i];
+            for (int i = 0; i < 4; ++i) {
+                const f32x4 d = sc[i];
 #pragma unroll
-            for (int rt = 0; rt < kRTW; ++rt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int rt = 0; rt < kRTW; ++rt) {
 #pragma clang fp contract(off)
-                    float t = acc[rt][0][i] * d[i][0];
-                    t = __builtin_fmaf(acc[rt][1][i], d[i][1], t);
-                    t = __builtin_fmaf(acc[rt][2][i], d[i][2], t);
-                    s[tt][rt][i] = __builtin_fmaf(acc[rt][3][i], d[i][3], t);
+                    float t = acc[rt][0][i] * d[0];
+                    t = __builtin_fmaf(acc[rt][1][i], d[1], t);
+                    t = __builtin_fmaf(acc[rt][2][i], d[2], t);
+                    s[tt][rt][i] = __builtin_fmaf(acc[rt][3][i], d[3], t);
                 }
+            }
+            // one token tile's products at a time (bounds the registers the
+            // scheduler may spend on products in flight)
+            __builtin_amdgcn_sched_barrier(0);
         }
         if (mask_sub) {
 #pragma unroll
             for (int rt = 0; rt < kRTW; ++rt) {
-                const int64_t x = lim[rt] - base_tok;
-                const int lr = (int)(x < 0 ? 0 : (x > kSub ? kSub : x));
+                const int x = lim[rt] - base_tok;
+                const int lr = x < 0 ? 0 : (x > kSub ? kSub : x);
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
@@ -285,21 +392,19 @@ __global__ __launch_bounds__(kPThreads, KVS_PF_OCC) void prefill_kernel(AttendAr
                 for (int ct = 0; ct < 8; ++ct) o[ct][rt] *= alpha[rt];
             }
         }
-        // ---- the page's V shifts (read at its first sub-block); an exact
-        // rescale of a block's accumulators when its shift changes
-        if (sb == 0) {
+        // ---- the sub-block's V shifts; an exact rescale of a block's
+        // accumulators when its shift changes
 #pragma unroll
-            for (int b = 0; b < kNB; ++b) {
-                const int vsh = scalar_load((const int32_t*)(tile + kStagedShift) + b);
-                if (vsh != vsh_run[b]) {
-                    const float f = __builtin_amdgcn_ldexpf(1.f, vsh_run[b] - vsh);
+        for (int b = 0; b < kNB; ++b) {
+            const int vsh = __builtin_amdgcn_readfirstlane(*(const int32_t*)(B + kConvShift + 16 * b));
+            if (vsh != vsh_run[b]) {
+                const float f = __builtin_amdgcn_ldexpf(1.f, vsh_run[b] - vsh);
 #pragma unroll
-                    for (int rt = 0; rt < kRTW; ++rt) {
-                        o[2 * b][rt] *= f;
-                        o[2 * b + 1][rt] *= f;
-                    }
-                    vsh_run[b] = vsh;
+                for (int rt = 0; rt < kRTW; ++rt) {
+                    o[2 * b][rt] *= f;
+                    o[2 * b + 1][rt] *= f;
                 }
+                vsh_run[b] = vsh;
             }
         }
 
@@ -318,11 +423,39 @@ __global__ __launch_bounds__(kPThreads, KVS_PF_OCC) void prefill_kernel(AttendAr
                 lsum[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pop[c][rt], lsum[rt], 0, 0, 0);
         }
     };
-    // steps three at a time, so that each names its buffers statically
-    for (int step = 0; step < n_steps; step += 3) {
-        do_step(step, buf0, buf2);
-        if (step + 1 < n_steps) do_step(step + 1, buf1, buf0);
-        if (step + 2 < n_steps) do_step(step + 2, buf2, buf1);
+
+    // ---- pipeline over sub-blocks: in step st every wave converts sub-block
+    // st + 1 (raw rows DMA'd two steps earlier) while it computes sub-block
+    // st, and issues the DMA of st + 3. Past the last sub-block, the DMA and
+    // the conversion repeat the last one into free buffers (no branch, so the
+    // compiler counts the DMAs in flight exactly); nothing reads them.
+    constexpr int kWP = RawSub<VT>::kWavePieces;
+    __builtin_amdgcn_s_waitcnt(vm_wait(2 * kWP));   // raw 0 landed, 1 and 2 may be in flight
+    lds_barrier();
+    convert_sub<VT>(rw0, cv0, valid_of(0), tid, w, lane, m_nib, magic);
+
+    auto do_step = [&](int st, const uint8_t* C, uint8_t* Cn, const uint8_t* Rn, uint8_t* D) {
+        // raw sub-block st + 1 is in LDS for every wave (a wave may still have
+        // the DMA of st + 2 in flight), the operands of st are published, and
+        // every wave is done with the operands of st - 1 and the raw rows of
+        // st - 1, whose buffers take st + 1 and st + 3. The DMA of st + 3 is
+        // issued after the conversion's LDS accesses: the compiler cannot tell
+        // every one of them apart from the DMA's target and would wait for
+        // the DMA there; after it, the step reads only the operand buffer.
+        __builtin_amdgcn_s_waitcnt(vm_wait(kWP));
+        lds_barrier();
+        convert_sub<VT>(Rn, Cn, valid_of(min(st + 1, n_steps - 1)), tid, w, lane, m_nib, magic);
+        const DmaAddr<VT> ad = dma_step(min(st + 3, n_steps - 1), D);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(st, C);
+        keep<VT>(ad);
+    };
+    // steps four at a time, so that each names its buffers statically
+    for (int st = 0; st < n_steps; st += 4) {
+        do_step(st, cv0, cv1, rw1, rw3);
+        if (st + 1 < n_steps) do_step(st + 1, cv1, cv0, rw2, rw0);
+        if (st + 2 < n_steps) do_step(st + 2, cv0, cv1, rw3, rw1);
+        if (st + 3 < n_steps) do_step(st + 3, cv1, cv0, rw0, rw2);
     }
 
     // ---- group state -> partial records (O back in absolute units)
@@ -344,13 +477,59 @@ __global__ __launch_bounds__(kPThreads, KVS_PF_OCC) void prefill_kernel(AttendAr
     }
 }
 
+// Operand probe: every (page, kv head) of a launch converted by convert_sub,
+// sub-block by sub-block, and written out as one staged tile (the operands
+// the prefill kernel computes on, in the layout kvs.h documents). Grid:
+// (pages of the launch, kv heads); block x takes the x-th page of the
+// launch's segments, in segment order, into tile x (with by_page, into tile
+// `page`); blocks past the pages are ring refill workgroups.
+template <typename VT>
+__global__ __launch_bounds__(kPThreads) void stage_kernel(StageArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t cv[kConvBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t rw[RawSub<VT>::kBytes];
+    if ((int)blockIdx.x >= a.n_pages) {   // ring refill workgroup: its first 256 threads copy
+        if (threadIdx.x < 256) copy_role(a.copy, ((int)blockIdx.x - a.n_pages) * (int)gridDim.y + (int)blockIdx.y);
+        return;
+    }
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int slot = blockIdx.x, g = blockIdx.y;
+    int rem = slot;
+    int32_t page = -1;
+    for (int si = 0; si < a.n_segs; ++si) {
+        const int np = scalar_load(&a.segs[si].npages);
+        if (rem < np) { page = scalar_load(&a.segs[si].page0) + rem; break; }
+        rem -= np;
+    }
+    if (page < 0) return;   // past the launch's pages
+    const uint8_t* rec = page_record(a.ps, page);
+    uint8_t* tile = a.staged + ((int64_t)(a.by_page ? page : slot) * a.n_kv_heads + g) * kStagedTile;
+    const uint32_t m_nib = vconst(0x000F000Fu), magic = vconst(0x64006400u);
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    for (int sb = 0; sb < kSubs; ++sb) {
+        dma_raw<VT>(rec, g, a.n_kv_heads, sb, rw, w, lane);
+        __builtin_amdgcn_s_waitcnt(vm_wait(0));
+        lds_barrier();   // the raw rows are in LDS for every wave
+        const int64_t x = a.n_kv - ((int64_t)page * kPageTokens + kSub * sb);
+        convert_sub<VT>(rw, cv, (int)(x < 0 ? 0 : (x > kSub ? kSub : x)), tid, w, lane, m_nib, magic);
+        lds_barrier();   // the operands are in LDS for every wave
+        for (int o = 16 * tid; o < kSubK; o += 16 * kPThreads) {
+            *(u32x4*)(tile + sb * kSubK + o) = *(const u32x4*)(cv + o);
+            *(u32x4*)(tile + kStagedK + sb * kSubV + o) = *(const u32x4*)(cv + kSubK + o);
+        }
+        if (16 * tid < kSubS) *(u32x4*)(tile + kStagedOps + sb * kSubS + 16 * tid) = *(const u32x4*)(cv + kSubK + kSubV + 16 * tid);
+        if (tid < kNB) *(int32_t*)(tile + kStagedShift + 4 * (kNB * sb + tid)) = *(const int32_t*)(cv + kConvShift + 16 * tid);
+        lds_barrier();   // every wave is done with both buffers
+    }
+}
+
 template <int LIMBS>
 hipError_t launch_limbs(const AttendArgs& a, hipStream_t stream) {
     const int R = a.n_q * a.G;
     const int64_t n_work = (int64_t)a.n_segs * a.n_kv_heads * ((R + kRowsWG - 1) / kRowsWG);
     const int64_t blocks = ((copy_workgroups(a.copy) + 7) & ~7) + ((n_work + 7) & ~7);
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    return launch_kernel(prefill_kernel<LIMBS>, dim3((unsigned)blocks), dim3(kPThreads), stream, a);
+    if (a.v_q8) return launch_kernel(prefill_kernel<LIMBS, VQ8>, dim3((unsigned)blocks), dim3(kPThreads), stream, a);
+    return launch_kernel(prefill_kernel<LIMBS, VQ4>, dim3((unsigned)blocks), dim3(kPThreads), stream, a);
 }
 
 }  // namespace
@@ -358,6 +537,13 @@ hipError_t launch_limbs(const AttendArgs& a, hipStream_t stream) {
 hipError_t launch_prefill(const AttendArgs& a, hipStream_t stream) {
     if (a.n_segs <= 0 && copy_workgroups(a.copy) == 0) return hipSuccess;
     return a.q_f16 ? launch_limbs<1>(a, stream) : launch_limbs<2>(a, stream);
+}
+
+hipError_t launch_stage(const StageArgs& a, hipStream_t stream) {
+    const int cx = (copy_workgroups(a.copy) + a.n_kv_heads - 1) / a.n_kv_heads;
+    if (a.n_pages <= 0 && cx == 0) return hipSuccess;
+    if (a.v_q8) return launch_kernel(stage_kernel<VQ8>, dim3(a.n_pages + cx, a.n_kv_heads), dim3(kPThreads), stream, a);
+    return launch_kernel(stage_kernel<VQ4>, dim3(a.n_pages + cx, a.n_kv_heads), dim3(kPThreads), stream, a);
 }
 
 }  // namespace kvs

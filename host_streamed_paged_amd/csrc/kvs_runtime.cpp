@@ -47,7 +47,8 @@ int fail(int code, const char* fmt, ...) {
 
 constexpr uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
-constexpr int kMaxLanes = 3;   // compute lanes for ring chunks and staged runs
+constexpr int kMaxLanes = 3;   // compute lanes for ring chunks
+constexpr int kWideCopyRounds = 7;   // 32 KB rounds per copy workgroup of a prefill-width launch
 // automatic sizing (page 3, description of --kv-stream auto): a 2048-token
 // floor, an 8192 MiB ceiling, and in the stage formula that reproduces its
 // logs, 4 pages per layer above the resident ones
@@ -63,9 +64,7 @@ struct Layout {
     uint64_t seg_bytes = 0;    // per layer
     int32_t max_segs = 0;      // per layer
     int32_t max_groups = 0;
-    int32_t stage_pages = 0;   // pages per staging region (0: blocks never wide enough to stage)
-    uint64_t stage_bytes = 0;  // one staging region per compute lane
-    uint64_t fixed = 0;        // ring + work + staging + tables
+    uint64_t fixed = 0;        // ring + work + tables
 };
 
 int validate(const kvs_config* c) {
@@ -105,14 +104,7 @@ Layout layout_of(const kvs_config* c) {
     L.max_segs = 2 * L.max_groups + c->max_pages + 1;
     L.src_bytes = align256((uint64_t)c->max_pages * sizeof(int32_t));
     L.seg_bytes = align256((uint64_t)L.max_segs * sizeof(kvs::Seg));
-    // staged operands for blocks wider than 64 rows per kv head: a launch's
-    // pages are staged in runs of at most stage_pages (a segment never spans
-    // more than group_pages pages)
-    if (kvs::mfma_stages(c->max_q_tokens * (c->n_q_heads / c->n_kv_heads))) {
-        L.stage_pages = std::max(64, c->group_pages);
-        L.stage_bytes = kMaxLanes * align256((uint64_t)L.stage_pages * c->n_kv_heads * kvs::kStagedTile);
-    }
-    L.fixed = L.ring_bytes + L.work_bytes + L.stage_bytes + (uint64_t)c->n_layers * (L.src_bytes + L.seg_bytes);
+    L.fixed = L.ring_bytes + L.work_bytes + (uint64_t)c->n_layers * (L.src_bytes + L.seg_bytes);
     return L;
 }
 
@@ -151,7 +143,6 @@ struct kvs_pool {
     uint64_t budget = 0;
     uint8_t* ring = nullptr;
     float* work = nullptr;
-    uint8_t* staged[kMaxLanes] = {};   // staging region of each compute lane (lane 0: the caller's stream)
     uint8_t* slots = nullptr;
     int64_t n_slots = 0;
     std::vector<int32_t> slot_free;  // stack of free slot ids
@@ -182,8 +173,8 @@ struct kvs_pool {
     kvs_status_info st{};
     // kernel timing (kvs_profile_*): per kind, event pairs in launch order
     bool profiling = false;
-    std::vector<std::pair<hipEvent_t, hipEvent_t>> prof_ev[3];
-    size_t prof_used[3] = {0, 0, 0};
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> prof_ev[2];
+    size_t prof_used[2] = {0, 0};
 };
 
 namespace {
@@ -335,6 +326,7 @@ kvs::CopyJob make_copy(const kvs_pool* p, const LayerState& ls, int32_t c, int32
     cj.ring_dst = p->ring + (uint64_t)cslot * p->cfg.chunk_pages * p->L.page_bytes;
     cj.page_bytes = (int64_t)p->L.page_bytes;
     cj.n_pages = cp.npages;
+    cj.part_bytes = kvs::kCopyPartBytes;
     cj.parts_per_page = (int32_t)((p->L.page_bytes + kvs::kCopyPartBytes - 1) / kvs::kCopyPartBytes);
     int32_t k = 0;
     for (const auto& run : cp.runs)
@@ -408,7 +400,7 @@ int lanes_for(int32_t R, int32_t n_ch, bool whole_groups) {
 }
 
 template <typename LaunchFn>
-int run_layer(kvs_pool* p, int32_t layer, hipStream_t stream, int32_t run_pages, LaunchFn launch) {
+int run_layer(kvs_pool* p, int32_t layer, hipStream_t stream, LaunchFn launch) {
     LayerState& ls = p->layers[layer];
     const int32_t n_ch = (int32_t)ls.chunks.size();
     const int32_t R = p->n_cslots;
@@ -428,39 +420,6 @@ int run_layer(kvs_pool* p, int32_t layer, hipStream_t stream, int32_t run_pages,
     // event cannot be waited on; an append on the captured stream is ordered)
     if (p->appended && !stream_capturing(stream) && hipStreamWaitEvent(stream, p->append_ev, 0) != hipSuccess)
         return mark(fail(KVS_ERR_HIP, "hipStreamWaitEvent(append) failed"));
-    // Staged launches (blocks wider than 64 rows) of segments [seg_b, seg_e)
-    // with no ring chunk to wait for: runs of whole segments, at most
-    // run_pages pages each, go to the compute lanes in turn, so that the runs
-    // (each staged into its lane's region, then attended) overlap one
-    // another; groups are whole, so no two lanes share one.
-    auto staged_runs_on_lanes = [&](int32_t seg_b, int32_t seg_e) -> int {
-        std::vector<std::pair<int32_t, int32_t>> runs;
-        for (int32_t i = seg_b; i < seg_e;) {
-            int32_t j = i, pages = 0;
-            while (j < seg_e && pages + ls.segs[j].npages <= run_pages) pages += ls.segs[j++].npages;
-            if (j == i) return mark(fail(KVS_ERR_INVALID_ARG, "internal: segment longer than a staging run"));
-            runs.emplace_back(i, j - i);
-            i = j;
-        }
-        const int n_l = (int)std::min<size_t>(kMaxLanes, runs.size());
-        if (n_l > 1) {
-            if (hipEventRecord(p->fork_ev, stream) != hipSuccess) return mark(fail(KVS_ERR_HIP, "lane fork failed"));
-            for (int k = 0; k < n_l; ++k)
-                if (hipStreamWaitEvent(p->lanes[k], p->fork_ev, 0) != hipSuccess) return mark(fail(KVS_ERR_HIP, "lane fork failed"));
-        }
-        for (size_t r = 0; r < runs.size(); ++r) {
-            const int lane = (int)(r % n_l);
-            int e = launch(n_l > 1 ? p->lanes[lane] : stream, lane, runs[r].first, runs[r].second, nullptr, 0,
-                           kvs::CopyJob{});
-            if (e) return mark(e);
-            p->st.kernels_launched++;
-        }
-        for (int k = 0; k < (n_l > 1 ? n_l : 0); ++k)
-            if (hipEventRecord(p->join_ev[k], p->lanes[k]) != hipSuccess || hipStreamWaitEvent(stream, p->join_ev[k], 0) != hipSuccess)
-                return mark(fail(KVS_ERR_HIP, "lane join failed"));
-        return KVS_OK;
-    };
-    const bool lanes_ok = run_pages > 0 && !stream_capturing(stream);
     if (p->cfg.flags & KVS_FLAG_ZERO_COPY) {
         // Zero-copy: streamed pages are read in place from the host records
         // (the launch's PageSource carries them), so there is no ring. With
@@ -476,14 +435,11 @@ int run_layer(kvs_pool* p, int32_t layer, hipStream_t stream, int32_t run_pages,
             p->st.kernels_launched++;
             return KVS_OK;
         };
-        if ((n_ch == 0 || ls.whole_groups) && lanes_ok) return staged_runs_on_lanes(0, n_segs);
         if (n_ch == 0 || ls.whole_groups) return run(0, n_segs);
         int r = run(0, ls.res_nseg);
         for (int32_t c = 0; c < n_ch && !r; ++c) r = run(ls.chunks[c].seg0, ls.chunks[c].nseg);
         return r;
     }
-    // every page resident: staged runs on the lanes as above
-    if (n_ch == 0 && lanes_ok) return ls.res_nseg > 0 ? staged_runs_on_lanes(0, ls.res_nseg) : KVS_OK;
     const int n_lanes = lanes_for(R, n_ch, ls.whole_groups);
     auto slot_of = [&](int32_t c) { return (slot0 + c) % R; };
     auto do_launch = [&](int lane, int32_t seg0, int32_t nseg, int32_t c_compute, int32_t c_copy) -> int {
@@ -578,8 +534,8 @@ int check_capture(const kvs_pool* p, int32_t layer, hipStream_t s) {
 }
 
 // Work of this pool issued on another stream (an earlier attend's combine
-// still reading the split-K workspace, a probe, a staging region in use) must
-// be done before a new call's launches reuse that memory: the call's stream
+// still reading the split-K workspace, or a probe) must be done before a new
+// call's launches reuse that memory: the call's stream
 // waits for the pool's last recorded work. Under graph capture an outside
 // event cannot be waited on; a captured sequence runs on the capture stream,
 // which orders it.
@@ -755,10 +711,6 @@ int kvs_pool_create(const kvs_config* cfg, void* dev_arena, uint64_t budget_byte
     uint8_t* cur = p->arena;
     p->ring = cur; cur += L.ring_bytes;
     p->work = (float*)cur; cur += L.work_bytes;
-    if (L.stage_bytes) {
-        for (int k = 0; k < kMaxLanes; ++k) p->staged[k] = cur + k * (L.stage_bytes / kMaxLanes);
-        cur += L.stage_bytes;
-    }
     p->layers.resize(cfg->n_layers);
     for (auto& ls : p->layers) {
         ls.dev_src = (int32_t*)cur; cur += L.src_bytes;
@@ -1065,9 +1017,8 @@ int attend_impl(kvs_pool* p, int32_t layer, const void* q, int32_t q_dtype, int3
     a.scale_log2 = scale * 1.44269504088896340736f;
     a.causal = causal ? 1 : 0;
     a.part = part;
-    const bool staging = kvs::mfma_stages(n_q * a.G);
-    rc = run_layer(p, layer, s, staging ? p->L.stage_pages : 0,
-                   [&](hipStream_t st, int lane, int32_t seg0, int32_t nseg, const uint8_t* ring_chunk,
+    const bool wide = kvs::prefill_rows(n_q * a.G);
+    rc = run_layer(p, layer, s, [&](hipStream_t st, int /*lane*/, int32_t seg0, int32_t nseg, const uint8_t* ring_chunk,
                                     int32_t rank0, const kvs::CopyJob& cj) -> int {
         kvs::AttendArgs b = a;
         b.copy = cj;
@@ -1077,46 +1028,15 @@ int attend_impl(kvs_pool* p, int32_t layer, const void* q, int32_t q_dtype, int3
             hipError_t e = kvs::launch_copy(cj, st);
             return e == hipSuccess ? KVS_OK : fail(KVS_ERR_HIP, "ring copy launch failed: %s", hipGetErrorString(e));
         }
-        if (!staging) {
-            b.segs = ls.dev_segs + seg0;
-            b.n_segs = nseg;
-            hipError_t e = timed_or_not(0, st, [&] { return kvs::launch_attend(b, st); });
-            return e == hipSuccess ? KVS_OK : fail(KVS_ERR_HIP, "attention kernel launch failed: %s", hipGetErrorString(e));
-        }
-        // staged: runs of segments of at most stage_pages pages; each run is
-        // converted into the lane's staging region, then attended
-        uint8_t* region = p->staged[lane];
-        for (int32_t i = seg0; i < seg0 + nseg;) {
-            int32_t j = i, pages = 0;
-            while (j < seg0 + nseg && pages + ls.segs[j].npages <= p->L.stage_pages) pages += ls.segs[j++].npages;
-            if (j == i) return fail(KVS_ERR_INVALID_ARG, "internal: segment longer than the staging region");
-            // the ring refill rides with the first run, half of its pages
-            // with the staging launch and half with the attention launch, so
-            // that the lane keeps pulling pages over the link through both
-            const bool first_run = i == seg0;
-            const int32_t half = (cj.n_pages + 1) / 2;
-            kvs::StageArgs sa{};
-            sa.copy = first_run ? kvs::split_copy(cj, half, true) : kvs::CopyJob{};
-            sa.ps = b.ps;
-            sa.segs = ls.dev_segs + i;
-            sa.n_segs = j - i;
-            sa.n_kv_heads = p->cfg.n_kv_heads;
-            sa.n_kv = n_kv;
-            sa.n_pages = pages;
-            sa.staged = region;
-            sa.v_q8 = b.v_q8;
-            hipError_t e = timed_or_not(2, st, [&] { return kvs::launch_stage(sa, st); });
-            if (e != hipSuccess) return fail(KVS_ERR_HIP, "staging kernel launch failed: %s", hipGetErrorString(e));
-            kvs::AttendArgs c = b;
-            c.copy = first_run ? kvs::split_copy(cj, half, false) : kvs::CopyJob{};
-            c.segs = ls.dev_segs + i;
-            c.n_segs = j - i;
-            c.staged = region;
-            e = timed_or_not(0, st, [&] { return kvs::launch_attend(c, st); });
-            if (e != hipSuccess) return fail(KVS_ERR_HIP, "attention kernel launch failed: %s", hipGetErrorString(e));
-            i = j;
-        }
-        return KVS_OK;
+        b.segs = ls.dev_segs + seg0;
+        b.n_segs = nseg;
+        // A prefill-width launch's workgroups hold most of a compute unit's
+        // LDS, and so does each of its copy workgroups: a few copy workgroups
+        // of whole pages keep the link as busy as many small ones and take
+        // fewer compute units from the attention.
+        if (wide && cj.n_pages > 0) b.copy = kvs::with_part_bytes(cj, (int64_t)kvs::kCopyPartBytes * kWideCopyRounds);
+        hipError_t e = timed_or_not(0, st, [&] { return kvs::launch_attend(b, st); });
+        return e == hipSuccess ? KVS_OK : fail(KVS_ERR_HIP, "attention kernel launch failed: %s", hipGetErrorString(e));
     });
     if (rc) return rc;
     hipError_t e = timed_or_not(1, s, [&] { return kvs::launch_combine(part, ls.n_groups, n_q, p->cfg.n_q_heads, out, lse, s); });
@@ -1169,7 +1089,7 @@ int kvs_debug_gather(kvs_pool* p, int32_t layer, int64_t tok0, int64_t n_tok, fl
     a.k_out = k_out;
     a.v_out = v_out;
     a.v_q8 = p->cfg.type_v == KVS_TYPE_Q8_0;
-    rc = run_layer(p, layer, s, 0, [&](hipStream_t st, int /*lane*/, int32_t seg0, int32_t nseg, const uint8_t* ring_chunk,
+    rc = run_layer(p, layer, s, [&](hipStream_t st, int /*lane*/, int32_t seg0, int32_t nseg, const uint8_t* ring_chunk,
                                     int32_t rank0, const kvs::CopyJob& cj) -> int {
         kvs::GatherArgs b = a;
         b.copy = cj;
@@ -1208,7 +1128,7 @@ int kvs_debug_stage(kvs_pool* p, int32_t layer, int64_t n_kv, void* dst, void* s
     a.staged = (uint8_t*)dst;
     a.v_q8 = p->cfg.type_v == KVS_TYPE_Q8_0;
     a.by_page = 1;
-    rc = run_layer(p, layer, s, 0, [&](hipStream_t st, int /*lane*/, int32_t seg0, int32_t nseg, const uint8_t* ring_chunk,
+    rc = run_layer(p, layer, s, [&](hipStream_t st, int /*lane*/, int32_t seg0, int32_t nseg, const uint8_t* ring_chunk,
                                     int32_t rank0, const kvs::CopyJob& cj) -> int {
         kvs::StageArgs b = a;
         b.copy = cj;
@@ -1243,7 +1163,7 @@ int kvs_debug_export_pages(kvs_pool* p, int32_t layer, void* dst, void* stream) 
     a.ps.host = (p->cfg.flags & KVS_FLAG_ZERO_COPY) ? ls.host : nullptr;
     a.ps.page_bytes = (int64_t)p->L.page_bytes;
     a.dst = (uint8_t*)dst;
-    rc = run_layer(p, layer, s, 0, [&](hipStream_t st, int /*lane*/, int32_t seg0, int32_t nseg, const uint8_t* ring_chunk,
+    rc = run_layer(p, layer, s, [&](hipStream_t st, int /*lane*/, int32_t seg0, int32_t nseg, const uint8_t* ring_chunk,
                                     int32_t rank0, const kvs::CopyJob& cj) -> int {
         kvs::ExportArgs b = a;
         b.copy = cj;
@@ -1322,7 +1242,7 @@ int kvs_profile_enable(kvs_pool* p, int32_t enable) {
 
 int kvs_profile_read(kvs_pool* p, int32_t kind, int64_t* launches, double* total_ms, int32_t reset) {
     if (!p || !launches || !total_ms) return fail(KVS_ERR_INVALID_ARG, "NULL argument");
-    if (kind < 0 || kind > 2) return fail(KVS_ERR_INVALID_ARG, "kind %d unknown", kind);
+    if (kind < 0 || kind > 1) return fail(KVS_ERR_INVALID_ARG, "kind %d unknown", kind);
     double ms = 0.0;
     for (size_t i = 0; i < p->prof_used[kind]; ++i) {
         auto& pr = p->prof_ev[kind][i];

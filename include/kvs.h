@@ -33,7 +33,7 @@
  *     caller memory.
  *   - Calls on one pool may use different streams: each call that launches
  *     work first makes its stream wait for the pool's previous work (the
- *     split-K workspace, staging regions and ring are shared by every layer).
+ *     split-K workspace and ring are shared by every layer).
  *     Inside a HIP graph capture that wait is skipped, so a captured sequence
  *     must issue all of its calls on the capture stream.
  *   - A HIP runtime failure after a call has started device work marks the
@@ -155,13 +155,8 @@ int kvs_config_validate(const kvs_config* cfg);
 uint64_t kvs_page_bytes(const kvs_config* cfg);
 
 /* Smallest budget kvs_pool_create accepts for cfg, written to *out: the ring,
- * the split-K workspace (max_q_tokens x n_q_heads rows per page group), the
- * staging regions and the per-layer tables, each rounded up to 256 bytes.
- * Staging regions exist only when a query block can exceed 64 rows per kv
- * head (max_q_tokens x n_q_heads / n_kv_heads > 64, a prefill ubatch): one
- * per compute lane (four) of max(64, group_pages) pages x n_kv_heads x
- * 128 KiB, where each launch first converts its pages once into f16
- * matrix-core operands. Pure. */
+ * the split-K workspace (max_q_tokens x n_q_heads rows per page group) and
+ * the per-layer tables, each rounded up to 256 bytes. Pure. */
 int kvs_min_budget_bytes(const kvs_config* cfg, uint64_t* out);
 
 /* Number of resident page slots a budget yields for cfg (0 if below the
@@ -234,9 +229,9 @@ typedef struct kvs_plan_info {
 int kvs_plan_layer(const kvs_config* cfg, int32_t n_pages, const uint8_t* resident, kvs_plan_info* info,
                    int32_t* segs, int32_t seg_cap, int32_t* chunks, int32_t chunk_cap);
 
-/* Create a pool that carves [ring | workspace | staging | tables | resident
- * slots] out of the caller's device arena of budget_bytes bytes (256-byte
- * aligned): one bounded device region holds the resident pages and the one
+/* Create a pool that carves [ring | workspace | tables | resident slots] out
+ * of the caller's device arena of budget_bytes bytes (256-byte aligned): one
+ * bounded device region holds the resident pages and the one
  * transfer ring all layers share (page 1, "Summary"; page 2, opening
  * paragraph), sized by a byte budget whose least useful value is one page
  * (page 3, "Diagnostic log": minimum_stage_bytes). KVS_ERR_BUDGET below
@@ -417,10 +412,10 @@ int kvs_debug_read_page(kvs_pool* pool, int32_t layer, int32_t page, void* dst_h
 int kvs_debug_export_pages(kvs_pool* pool, int32_t layer, void* dst, void* stream);
 
 /* The matrix-core operands of every page of a layer, converted by the same
- * staging code the attention kernels use for query blocks wider than 64 rows
- * per kv head, written to dst (device, 256-byte aligned) as n_pages x
- * n_kv_heads tiles of KVS_STAGED_TILE_BYTES, tile (page, kv head) at
- * (page x n_kv_heads + head) x KVS_STAGED_TILE_BYTES. n_kv is the layer's
+ * code the prefill kernel runs on each 64-token sub-block (query blocks wider
+ * than 64 rows per kv head), written to dst (device, 256-byte aligned) as
+ * n_pages x n_kv_heads tiles of KVS_STAGED_TILE_BYTES, tile (page, kv head)
+ * at (page x n_kv_heads + head) x KVS_STAGED_TILE_BYTES. n_kv is the layer's
  * token count (rows at or past it are not cached). Streamed pages pass through
  * the ring. Enqueued on `stream`. Tile layout (binary16 little-endian):
  *   K operands, bytes [0, 65536): for token tile T = 0..15, block b = 0..3,
@@ -432,21 +427,24 @@ int kvs_debug_export_pages(kvs_pool* pool, int32_t layer, void* dst, void* strea
  *     Q4_0 block for even t, its high nibbles for odd t) of tokens
  *     32 c + 4 j + s for slot s < 4 and 32 c + 12 + 4 j + s for s >= 4, each
  *     d x (nibble - 8) (Q4_0) or d x code (Q8_0), divided by 2^shift and
- *     rounded once to binary16 (0 for uncached rows), shift = the block's V
- *     shift.
+ *     rounded once to binary16 (0 for uncached rows), shift = the V shift of
+ *     the token's 64-token sub-block (c / 2) and the channel's block.
  *   K scales, bytes [131072, 135168): token t's four block scales as
  *     float32 (exact) at 16 t.
- *   V shifts, bytes [135168, 135184): int32 per block: 0, or, if a cached
- *     row's scale magnitude exceeds 8188 (binary16 bits above 0x6FFF) for
- *     Q4_0 V or 511.75 (bits above 0x5FFF) for Q8_0 V, 3 (Q4_0) or 7 (Q8_0). */
+ *   V shifts, bytes [135168, 135232): int32 at 4 (4 s + b) for sub-block
+ *     s = 0..3 (tokens 64 s .. 64 s + 63) and block b: 0, or, if a cached row
+ *     of the sub-block has a block b scale magnitude above 8188 (binary16 bits
+ *     above 0x6FFF) for Q4_0 V or 511.75 (bits above 0x5FFF) for Q8_0 V, 3
+ *     (Q4_0) or 7 (Q8_0). */
 #define KVS_STAGED_TILE_BYTES 135424
 int kvs_debug_stage(kvs_pool* pool, int32_t layer, int64_t n_kv, void* dst, void* stream);
 
 /* Kernel timing. With enable != 0, kvs_attend brackets every attention kernel
- * launch (kind 0), every split-K combine launch (kind 1) and every staging
- * launch of a wide query block (kind 2) with a start/stop event pair carried
- * by the kernel's own dispatch (so the time is the kernel's execution, not its
- * queueing); launches under graph capture are not timed. kvs_profile_read waits
+ * launch (kind 0) and every split-K combine launch (kind 1) with a start/stop
+ * event pair carried by the kernel's own dispatch (so the time is the
+ * kernel's execution, not its queueing); launches under graph capture are not
+ * timed. Attention launches on several compute lanes overlap, so their summed
+ * time can exceed the wall time of a call. kvs_profile_read waits
  * for the recorded events and returns the number of timed launches of that
  * kind and their summed duration in milliseconds; reset != 0 clears the
  * record. At most 65536 launches per kind are kept (later ones are not timed). */

@@ -188,7 +188,7 @@ _IDX = _staged_index()
 def decode_staged_tile(tile):
     """Staged tile bytes of one (page, kv head) -> (K codes as float [256, 128],
     K scales float32 [256, 4], V operands as float16 [256, 128], V shifts
-    int32 [4]) in token-major order."""
+    int32 [4 sub-blocks, 4 blocks]) in token-major order."""
     t = np.frombuffer(tile.tobytes(), dtype=np.uint8)
     k_tok, k_dim, v_tok, v_ch = _IDX
     kcodes = np.full((256, 128), np.nan, np.float32)
@@ -196,7 +196,7 @@ def decode_staged_tile(tile):
     vv = np.full((256, 128), np.nan, np.float16)
     vv[v_tok, v_ch] = t[65536:131072].view(np.float16)
     kscale = t[131072:135168].view(np.float32).reshape(256, 4)
-    shifts = t[135168:135184].view(np.int32).copy()
+    shifts = t[135168:135232].view(np.int32).reshape(4, 4).copy()
     return kcodes, kscale, vv, shifts
 
 
@@ -212,9 +212,9 @@ def test_staged_operands_bit_exact(type_v, k_regime, v_regime, zero_copy):
     K operands are the codes exactly, the scales their exact float32 values;
     each V operand is the round-to-nearest-even binary16 of d * (u - 8) /
     2^shift (Q4_0) or d * code / 2^shift (Q8_0) computed exactly from the
-    oracle's float64 dequantization; the shift is 3 exactly when a cached
-    row's Q4_0 V scale magnitude exceeds 8188, 7 exactly when a Q8_0 one
-    exceeds 511.75."""
+    oracle's float64 dequantization; the shift of a 64-token sub-block and
+    block is 3 exactly when a cached row of it has a Q4_0 V scale magnitude
+    above 8188, 7 exactly when a Q8_0 one exceeds 511.75."""
     recs = regime_records(k_regime, v_regime, n_layers=1, seed=5, type_v=type_v)
     say(f"staged operands {type_v} K={k_regime} V={v_regime} zero_copy={zero_copy}")
     c = EdgeCase(recs, max_q=1, resident_fn=mask_random(0.5, seed=8),
@@ -242,9 +242,15 @@ def test_staged_operands_bit_exact(type_v, k_regime, v_regime, zero_copy):
                 vo = HKV * 256 * 136 + g * 256 * 4 * vblk
                 vb = rec[p, vo:vo + 256 * 4 * vblk].reshape(256, 4, vblk)
                 vbits = (vb[:, :, 0].astype(np.uint16) | (vb[:, :, 1].astype(np.uint16) << 8)) & 0x7FFF
-                want_shift = np.where(vbits[:valid].max(axis=0) > big_bits, big_shift, 0)
+                cached = np.arange(256) < valid
+                want_shift = np.zeros((4, 4), np.int64)
+                for sb in range(4):
+                    rows = vbits[64 * sb:64 * sb + 64][cached[64 * sb:64 * sb + 64]]
+                    if len(rows):
+                        want_shift[sb] = np.where(rows.max(axis=0) > big_bits, big_shift, 0)
                 assert np.array_equal(shifts, want_shift), (p, g, shifts, want_shift)
-                exact = V[256 * p:256 * p + 256, g, :] / np.repeat(2.0 ** want_shift, 32)[None, :]
+                div = np.repeat(np.repeat(2.0 ** want_shift, 64, axis=0), 32, axis=1)   # [token, channel]
+                exact = V[256 * p:256 * p + 256, g, :] / div
                 want = exact[:valid].astype(np.float16)
                 assert np.array_equal(vv[:valid].view(np.uint16) & 0x7FFF, want.view(np.uint16) & 0x7FFF) and \
                     np.array_equal(np.signbit(vv[:valid]) | (want == 0), np.signbit(want) | (want == 0)), (p, g)

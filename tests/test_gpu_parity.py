@@ -137,11 +137,11 @@ def test_multi_row_parity(n_q, causal, qdt, scale):
         c.close()
 
 
-def test_staged_and_in_kernel_paths_agree():
-    """A block wider than 64 rows per kv head runs the prefill kernel on
-    staged operands; a narrower one the matrix-core kernel converting each
-    page in the kernel. The first 10 query tokens of an 11-token block (66
-    rows, staged) and a 10-token block (60 rows) both match the oracle, and
+def test_prefill_and_matrix_core_paths_agree():
+    """A block wider than 64 rows per kv head runs the prefill kernel; a
+    narrower one the matrix-core kernel. The first 10 query tokens of an
+    11-token block (66 rows, prefill) and a 10-token block (60 rows) both match
+    the oracle, and
     each other to the same tolerance (their softmax runs over sub-blocks of
     different sizes, so the bits may differ)."""
     c = small_case(mask_random(0.5, seed=11), n_layers=2, max_q=11, group=2)

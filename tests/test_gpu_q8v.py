@@ -68,7 +68,7 @@ def check(c, outs, lses, qs, *, q_pos0, scale, causal):
 
 # (query tokens, dtype, causal, scale): decode rows 6 and 3 per kv head (the
 # decode kernel), 24 and 36 rows (the matrix-core kernel), 300 tokens (the
-# prefill kernel on staged operands)
+# prefill kernel)
 WIDTHS = [(1, "f32", False, 1.0, 12), (1, "f32", False, 1.0, 6), (4, "f32", True, 1.0, 12),
           (6, "f16", True, 1 / math.sqrt(128), 12), (300, "f16", True, 1 / math.sqrt(128), 12)]
 

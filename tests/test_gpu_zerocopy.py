@@ -2,8 +2,9 @@
 pinned host records by the attention kernels, with no ring.
 
 Bars: the same kernels fold the same pages in the same order, so outputs are
-bit-identical to the ring path (decode, verify, and a staged block wider than
-64 rows, with whole groups and with groups split across chunks); gathers are
+bit-identical to the ring path (decode, verify, and a prefill-width block of
+more than 64 rows per kv head, with whole groups and with groups split across
+chunks); gathers are
 bit-exact with the oracle; a streamed zero-copy layer can be captured in a HIP
 graph and replayed.
 """
@@ -33,7 +34,7 @@ def case(resident_fn, flags, *, n_q=4, ring=4, chunk=2, group=1, cid=71, n_layer
 @pytest.mark.parametrize("n_q,qdt,scale,group,chunk", [
     (1, "f32", 1.0, 1, 2),        # decode
     (4, "f32", 1.0, 2, 2),        # verify (matrix cores, 24 rows)
-    (11, "f16", 0.12, 3, 1),      # 66 rows: staged; groups of 3 split across 1-page chunks
+    (11, "f16", 0.12, 3, 1),      # 66 rows: prefill kernel; groups of 3 split across 1-page chunks
 ])
 def test_zero_copy_equals_the_ring_bit_for_bit(n_q, qdt, scale, group, chunk):
     resident = mask_random(0.4, seed=8)
@@ -113,14 +114,13 @@ def test_zero_copy_streamed_layer_replays_in_a_graph():
         c.close()
 
 
-def test_zero_copy_staged_runs_on_lanes_equal_the_ring():
-    """A layer longer than one 64-page staging run: the zero-copy launches
-    spread the runs over compute lanes (each staging into its own region),
-    and give the ring's bits."""
-    n_kv, n_q = 70 * 256 - 31, 11                     # 70 pages: runs of 64 and 6 pages; 66 rows
+def test_zero_copy_long_prefill_layer_equals_the_ring():
+    """A 70-page layer at prefill width (66 rows per kv head): the zero-copy
+    launch gives the ring's bits."""
+    n_kv, n_q = 70 * 256 - 31, 11                     # 70 pages, ragged tail; 66 rows
     res = []
     for flags in (0, kvs.FLAG_ZERO_COPY):
-        say(f"staged lanes case flags={flags} n_kv={n_kv}")
+        say(f"long prefill layer flags={flags} n_kv={n_kv}")
         c = Case(cid=73, n_layers=1, n_kv_heads=2, n_q_heads=12, n_kv=n_kv,
                  cfg_kw=dict(max_q_tokens=n_q, ring_pages=8, chunk_pages=4, group_pages=1,
                              flags=flags),
@@ -131,7 +131,7 @@ def test_zero_copy_staged_runs_on_lanes_equal_the_ring():
             if flags:
                 ref, ref_lse = c.oracle(0, qs[0], q_pos0=n_kv - n_q, scale=0.12, causal=True)
                 err = normwise_error(outs[0], ref)
-                say(f"zero-copy staged lanes: normwise {err:.3e}")
+                say(f"zero-copy long prefill layer: normwise {err:.3e}")
                 assert err <= TOL and float(np.max(np.abs(lses[0] - ref_lse))) <= TOL
             res.append((outs[0], lses[0]))
         finally:

@@ -25,7 +25,7 @@ def run(pool, fn, layer, q, n_kv, q_pos0, causal):
     return out.cpu().numpy(), lse.cpu().numpy()
 
 
-@pytest.mark.parametrize("widths", [(4, 2), (12, 1)], ids=["verify-then-smaller", "staged-then-decode"])
+@pytest.mark.parametrize("widths", [(4, 2), (12, 1)], ids=["verify-then-smaller", "prefill-then-decode"])
 def test_noalloc_equals_attend_on_consecutive_calls(widths):
     say(f"noalloc widths={widths}")
     c_long = Case(cid=121, n_layers=1, n_kv_heads=2, n_q_heads=12, n_kv=N_KV_LONG,
