@@ -321,13 +321,14 @@ def multi_leg(name, cfg_kw, threads, link, steps, kind, zero_copy=True):
     rwl = dataclasses.replace(wl, resident_pages=wl.n_pages)
     rst = setup(rwl, cfg_kw, threads)
     r = timed_run(rwl, rst, 5, 2)
+    gr = graph_run(rwl, rst, 10, 2)
     rst["pool"].close()
     del rst
-    # per layer: the wall time of the whole kvs_attend call (every attention
-    # launch and the combine, timed by events around the steps), and the
-    # attention launches' own durations
+    # per layer: the whole kvs_attend call (attention and combine launches)
+    # replayed as a HIP graph of the 16-layer step, as for decode, and the
+    # attention launches' own durations (eager, events on their dispatches)
     layers_timed = r["steps"] * wl.n_layers
-    layer_ms = r["ms_per_step"] / wl.n_layers
+    layer_ms = gr["ms_per_step"] / wl.n_layers
     att_ms = r["attn_ms_total"] / max(1, layers_timed)
     layer_bytes = wl.n_pages * pb
     flops = 4 * wl.n_q_heads * wl.head_dim * allowed_keys(wl)
@@ -341,8 +342,8 @@ def multi_leg(name, cfg_kw, threads, link, steps, kind, zero_copy=True):
          "achieved_tflops": round(flops / (layer_ms / 1e3) / 1e12, 1),
          "kernel_gbs": round(layer_bytes / (att_ms / 1e3) / 1e9, 1),
          "kernel_tflops": round(flops / (att_ms / 1e3) / 1e12, 1),
-         "timing": "achieved_*: whole layer (attention and combine launches, wall time by events around "
-                   "the steps); kernel_*: the attention launches' summed durations"}
+         "timing": "achieved_*: whole layer (attention and combine launches, HIP-graph replay of the "
+                   "16-layer step); kernel_*: the attention launches' summed durations"}
     if kind == "verify":
         k.update(bound="hbm", frac=round(k["achieved_gbs"] / HBM_PEAK_GBS, 4), peak=HBM_PEAK_GBS, unit="GB/s")
     else:
@@ -460,6 +461,7 @@ def kernels_only(name, args):
     rwl = dataclasses.replace(wl, resident_pages=wl.n_pages)
     st = setup(rwl, POOL_CFG[name], args.threads)
     r = timed_run(rwl, st, args.steps, args.warmup)
+    gr = graph_run(rwl, st, args.steps, args.warmup)
     st["pool"].close()
     layers = r["steps"] * wl.n_layers
     per = {k: round(r[f"{k}_ms_total"] / max(1, layers) * 1e3, 3) for k in ("attn", "combine")}
@@ -467,6 +469,7 @@ def kernels_only(name, args):
                       "attn_launches": r["attn_launches"],
                       "combine_launches": r["combine_launches"], "us_per_layer": per,
                       "layer_us": round(r["ms_per_step"] / wl.n_layers * 1e3, 3),
+                      "graph_layer_us": round(gr["ms_per_step"] / wl.n_layers * 1e3, 3),
                       "flops_per_layer": 4 * wl.n_q_heads * wl.head_dim * allowed_keys(wl),
                       "bytes_per_layer": wl.n_pages * st["recs"][0].shape[1]}), flush=True)
 

@@ -39,19 +39,23 @@ namespace {
 // order depends only on the number of groups, never on scheduling or
 // residency.
 // ---------------------------------------------------------------------------
-constexpr int kCombSlices = kHeadDim / 16;
-constexpr int kCombLanes = 16;   // group lanes per channel
+#ifndef KVS_COMB_CH
+#define KVS_COMB_CH 16
+#endif
+constexpr int kCombCh = KVS_COMB_CH;            // channels per workgroup
+constexpr int kCombSlices = kHeadDim / kCombCh;
+constexpr int kCombLanes = 256 / kCombCh;       // group lanes per channel
 constexpr int kCombBatch = 8;
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part, int32_t n_groups,
                                                       int32_t rows, float* __restrict__ out,
                                                       float* __restrict__ lse) {
-    __shared__ float so[kCombLanes][16];
+    __shared__ float so[kCombLanes][kCombCh];
     __shared__ float sm_[kCombLanes], sl_[kCombLanes];
     const int row = blockIdx.x, sl = blockIdx.y;
-    const int gl = threadIdx.x >> 4, c = threadIdx.x & 15;
+    const int gl = threadIdx.x / kCombCh, c = threadIdx.x % kCombCh;
     const int64_t gstride = (int64_t)rows * kPartStride;
     const float* p = part + (int64_t)row * kPartStride;
-    const int ch = 16 * sl + c;
+    const int ch = kCombCh * sl + c;
     float M = -INFINITY, L = 0.f, O = 0.f;
     for (int g0 = gl; g0 < n_groups; g0 += kCombLanes * kCombBatch) {
         float mg[kCombBatch], lg[kCombBatch], og[kCombBatch];

@@ -1,7 +1,6 @@
-// Matrix-core attention kernel for query blocks with more than a few rows:
+// Matrix-core attention kernel for query blocks of 7 to 64 rows per kv head:
 // a speculative verify batch of 1 + draft tokens (page 2, "Phase arena:
-// speculative verify batches") and a prefill ubatch (256 tokens in page 2's
-// "TLDR - recommended setup"), on CDNA4 v_mfma_f32_16x16x32_f16.
+// speculative verify batches"), on CDNA4 v_mfma_f32_16x16x32_f16.
 //
 // One workgroup = one segment (run of pages of one split-K group) x one kv
 // head x a tile of 16 RT query rows (row = query token x head of the GQA
@@ -34,13 +33,9 @@
 // state and page data alone, so results do not depend on how pages are split
 // into launches or which pages are resident.
 //
-// Blocks of more than 64 rows per kv head (a prefill ubatch) would make
-// every row tile decode the same page again: stage_kernel (below) converts
-// each (page, kv head) of such a launch once into a tile of f16 matrix-core
-// operands in fragment order (K: [token tile][block][lane] x 16 B; V^T:
-// [32-token chunk][channel tile][lane] x 16 B), the K block scales per token
-// (float32) and the V shift of each block, with the conversion code used
-// here, and the prefill kernel (kvs_prefill.hip) computes on those tiles.
+// Blocks of more than 64 rows per kv head (a prefill ubatch) go to the
+// prefill kernel (kvs_prefill.hip), which converts each page once per
+// 256-row block. The page conversion code of both is in kvs_convert.h.
 #include <hip/hip_runtime.h>
 #include <cstdint>
 #include <cmath>

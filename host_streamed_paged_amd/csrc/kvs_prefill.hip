@@ -1,17 +1,21 @@
 // Prefill attention kernel: query blocks of more than 64 rows per kv head (a
-// prefill ubatch, 256 tokens in page 2's "TLDR - recommended setup") on the
-// staged matrix-core operands stage_kernel writes (kvs_mfma.hip), on CDNA4
-// v_mfma_f32_16x16x32_f16.
+// prefill ubatch, 256 tokens in page 2's "TLDR - recommended setup"), on
+// CDNA4 v_mfma_f32_16x16x32_f16, and the operand probe that writes out what
+// it computes on.
 //
 // One workgroup = one segment (run of pages of one split-K group) x one kv
 // head x a block of 256 query rows (row = query token x head of the GQA
 // group); 8 waves, each owning 32 rows (two 16-row tiles) from scores to
-// output, so no wave ever waits on another's results. The workgroup walks
-// its pages in 64-token sub-blocks: the sub-block's staged operands (K
-// fragments 16 KB, V^T fragments 16 KB, float32 K scales 1 KB) are brought
-// into LDS once by LDS DMA, two sub-blocks ahead of their use (three
-// buffers), and every wave reads them there, so each staged byte leaves L2
-// once per workgroup instead of once per 16-row tile. Per sub-block and wave:
+// output. The workgroup walks its pages in 64-token sub-blocks, as a
+// pipeline: the raw K and V rows of a sub-block (13 KB, or 17 KB with Q8_0
+// V) are brought into LDS by LDS DMA three steps ahead (four raw buffers);
+// in step st all 8 waves convert sub-block st + 1 into f16 matrix-core
+// operands in one of two operand buffers (K codes exact, K block scales as
+// float32, V^T as d * (u - 8) or d * code rounded once to f16, divided by a
+// power of two when the sub-block's scales could overflow), then compute
+// sub-block st from the other. Each page is converted once per row block,
+// inside the workgroup: no staging launch, no staging memory. Per sub-block
+// and wave:
 //   QK   A_b^T (16 tokens x 16 rows) = K_b . Q_b^T per 16-token tile and quant
 //        block, with K_b the exact f16 codes and Q_b the query's exact f16
 //        limbs (all products of a tile are issued before any is scaled); each
@@ -26,8 +30,8 @@
 //   PV   O^T (16 channels x 16 rows) += V^T (16 x 32 tokens) . P^T (32 x 16)
 //        for the 8 channel tiles and 2 chunks of the sub-block, plus a ninth
 //        tile of ones whose product is the row sum of the same f16 p that
-//        weight V; a block whose page takes V divided by 8 keeps its
-//        accumulator in units of 8 (an exact rescale when that changes).
+//        weight V; a block whose sub-block takes V divided by 2^shift keeps
+//        its accumulator in those units (an exact rescale when that changes).
 // The running state (m, l, O) is updated in a fixed order of pages and
 // sub-blocks from state and page data alone, so results do not depend on how
 // pages are split into launches or which pages are resident.

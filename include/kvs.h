@@ -307,25 +307,30 @@ int kvs_stream_enqueue(kvs_pool* pool, int32_t layer);
  *     power-of-two scaling per row.
  *   - V blocks: any finite binary16 scale, nibbles 0..15 (Q4_0) or any codes
  *     (Q8_0, -128 included). Probabilities and V values pass through f16 with
- *     one rounding each; at widths above decode, a page whose 32-channel V
- *     block holds a scale magnitude above 8188 (Q4_0) or 511.75 (Q8_0) is
- *     taken divided by 8 (Q4_0) or 128 (Q8_0), so that no V operand
- *     overflows f16. Within one page and one 32-channel block, V scale magnitudes
- *     should lie within a factor of 2^14 of the block's largest: the
- *     contribution of a token whose scale is smaller than that (relative to
- *     the largest, in the same quarter page at decode width) carries an
- *     absolute error up to 2^-24 of the largest scale.
- * Enqueues on `stream`: the resident-group launch, then one launch per ring
- * chunk, then the split-K combine. Each launch computes on the chunk that the
- * previous launch copied into the ring, while its own copy workgroups read the
- * next chunk's pages from pinned host memory over the host link into the next
- * ring slot; kernel boundaries on the one stream order each copy before its
- * reader and each reader before the slot is refilled. Returns without waiting. KVS_ERR_BATCH_TOO_WIDE if n_q exceeds
+ *     one rounding each; at widths above decode, a page (verify widths) or
+ *     a 64-token sub-block (prefill widths, more than 64 rows per kv head)
+ *     whose 32-channel V block holds a scale magnitude above 8188 (Q4_0) or
+ *     511.75 (Q8_0) is taken divided by 8 (Q4_0) or 128 (Q8_0), so that no V
+ *     operand overflows f16. Within one such range and one 32-channel block,
+ *     V scale magnitudes should lie within a factor of 2^14 of the block's
+ *     largest: the contribution of a token whose scale is smaller than that
+ *     (relative to the largest, in the same quarter page at decode width)
+ *     carries an absolute error up to 2^-24 of the largest scale.
+ * Enqueues the resident-group launch, then one launch per ring chunk, then
+ * the split-K combine on `stream`; with several ring chunks the chunk
+ * launches go to up to three compute lanes (the pool's own streams, forked
+ * from and joined back to `stream` by events). Each chunk launch computes on
+ * a chunk an earlier launch of its lane copied into the ring, while its own
+ * copy workgroups read a later chunk's pages from pinned host memory over the
+ * host link into a ring slot of the same lane; kernel boundaries on a lane
+ * order each copy before its reader and each reader before the slot is
+ * refilled. Returns without waiting. KVS_ERR_BATCH_TOO_WIDE if n_q exceeds
  * max_q_tokens (the pages' "decode batch too wide").
- * A layer whose pages are all resident may be captured into a HIP graph
- * (stream capture on `stream`) and replayed; a layer with streamed pages
- * returns KVS_ERR_UNSUPPORTED under capture, because its ring chunks are
- * ordered by events on the pool's own copy streams. */
+ * A layer whose pages are all resident, or any layer of a zero-copy pool,
+ * may be captured into a HIP graph (stream capture on `stream`) and
+ * replayed; a layer that streams pages through the ring returns
+ * KVS_ERR_UNSUPPORTED under capture, because its ring chunks are ordered by
+ * events on the pool's lanes. */
 int kvs_attend(kvs_pool* pool, int32_t layer, const void* q, int32_t q_dtype, int32_t n_q,
                int64_t q_pos0, int64_t n_kv, float scale, int32_t causal, float* out,
                float* lse, void* stream);
