@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvs.so")
 
-SOURCES = ["kvs_runtime.cpp", "kvs_kernels.hip", "kvs_decode.hip", "kvs_mfma.hip", "kvs_prefill.hip", "kvs_append.hip"]
+SOURCES = ["kvs_runtime.cpp", "kvs_kernels.hip", "kvs_decode.hip", "kvs_mfma.hip", "kvs_verify.hip", "kvs_prefill.hip", "kvs_append.hip"]
 
 # Packed FP32 math is disabled for every HIP source: hipcc -O3 would otherwise
 # form v_pk_* fp32 instructions on its own.

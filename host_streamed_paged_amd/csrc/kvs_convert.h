@@ -133,4 +133,95 @@ __device__ inline void v_convert(const VRaw<VT>& r, int c, int gq, int valid, in
     }
 }
 
+// One of the two V^T operands above, for a caller that owns one 16-channel
+// half of block b: half h = 0 gives vop[0] (channel 32 b + n), h = 1 gives
+// vop[1] (channel 32 b + 16 + n), with the same token slots and the same
+// values. For Q4_0 the high nibble is taken in place: bits 0x6400 | (u << 4)
+// are the f16 value 1024 + 16 u, and (1024 + 16 u) / 16 - 72 = u - 8 exactly.
+template <typename VT>
+struct VRaw1 {
+    uint32_t byte[8];   // Q4_0: byte n of the slot's token; Q8_0: code 16 h + n
+    uint32_t d[8];      // scale bits of the slot's token
+};
+// The lane's byte offsets into the V tile for v_raw1: `ob` of its byte in
+// token row 4 gq of block b (byte n, or code 16 h + n), `od` of that row's
+// scale. Made opaque so that every read below is one constant offset from
+// them (short address chains keep the reads attributable to their LDS array).
+struct VLane {
+    uint32_t ob, od;
+};
+template <typename VT>
+__device__ inline VLane v_lane(int b, int gq, int n, int h) {
+    VLane r;
+    r.od = b * VT::kBlock + 4 * gq * VT::kRow;
+    r.ob = r.od + 2 + (VT::kQ8 ? 16 * h : 0) + n;
+    asm volatile("" : "+v"(r.ob), "+v"(r.od));
+    return r;
+}
+// v_raw with the lane's offsets from v_lane (h = 0): every read one constant
+// offset from them.
+template <typename VT>
+__device__ inline VRaw<VT> v_raw_o(const uint8_t* v_lds, const VLane& vl, int c) {
+    VRaw<VT> r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int ro = (32 * c + (j < 4 ? j : 12 + j)) * VT::kRow;
+        r.byte[j] = v_lds[vl.ob + ro];
+        if constexpr (VT::kQ8) r.hbyte[j] = v_lds[vl.ob + 16 + ro];
+        r.d[j] = *(const uint16_t*)(v_lds + (vl.od + ro));
+    }
+    return r;
+}
+template <typename VT>
+__device__ inline VRaw1<VT> v_raw1(const uint8_t* v_lds, const VLane& vl, int c) {
+    VRaw1<VT> r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int ro = (32 * c + (j < 4 ? j : 12 + j)) * VT::kRow;
+        r.byte[j] = v_lds[vl.ob + ro];
+        r.d[j] = *(const uint16_t*)(v_lds + (vl.od + ro));
+    }
+    return r;
+}
+// Per-wave constants of v_convert1 for half h: the nibble mask and the f16
+// factor and offset pairs (Q4_0), or the factor and offset (Q8_0).
+struct VHalf {
+    uint32_t mask;
+    half2_t cc, off;
+};
+template <typename VT>
+__device__ inline VHalf v_half(int h, int vshift) {
+    const _Float16 cs = vshift ? (VT::kQ8 ? (_Float16)0.0078125f : (_Float16)0.125f) : (_Float16)1.f;
+    VHalf r;
+    if constexpr (VT::kQ8) {
+        r.mask = 0u;
+        r.cc = half2_t{cs, cs};
+        r.off = half2_t{(_Float16)-1152.f * cs, (_Float16)-1152.f * cs};
+    } else {
+        const _Float16 c = h ? cs * (_Float16)0.0625f : cs;
+        const _Float16 o = h ? (_Float16)-72.f * cs : (_Float16)-1032.f * cs;
+        r.mask = h ? 0x00F000F0u : 0x000F000Fu;
+        r.cc = half2_t{c, c};
+        r.off = half2_t{o, o};
+    }
+    return r;
+}
+// The caller zeroes the scales of rows past the cache beforehand.
+template <typename VT>
+__device__ inline half8_t v_convert1(const VRaw1<VT>& r, const VHalf& vh, uint32_t magic) {
+    half8_t vop;
+#pragma unroll
+    for (int jp = 0; jp < 4; ++jp) {
+        const int j0 = 2 * jp, j1 = 2 * jp + 1;
+        const half2_t dd = as_h2(r.d[j0] | (r.d[j1] << 16));
+        const uint32_t x = __builtin_amdgcn_perm(r.byte[j1], r.byte[j0], 0x0c040c00u);
+        half2_t v;
+        if constexpr (VT::kQ8) v = q8_pair_f16(x, vh.cc, vh.off) * dd;
+        else v = q4_nibbles_f16((x & vh.mask) | magic, vh.cc, vh.off) * dd;
+        vop[j0] = v[0];
+        vop[j1] = v[1];
+    }
+    return vop;
+}
+
 }  // namespace kvs

@@ -191,6 +191,19 @@ __device__ inline const uint8_t* page_record(const PageSource& ps, int32_t page)
     return page_record_of(ps, page, scalar_load(ps.src + page));
 }
 
+// Compute units of the current device (cached per device).
+inline int compute_units() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
 // Launch a kernel; a pending timing pair (launch_timing) goes with it.
 template <typename K, typename... Args>
 inline hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, hipStream_t stream, Args... args) {

@@ -162,6 +162,8 @@ struct AttendArgs {
     float* part;          // [n_groups][n_q][Hq][kPartStride]
     int32_t n_slices;     // matrix-core kernel: segment slices per (kv head, row tile), set at launch
     int32_t v_q8;         // V blocks are Q8_0 (else Q4_0)
+    const uint8_t* spare; // device memory of at least one page record (the ring's first slot) that a
+                          // kernel may read and ignore
 };
 
 // Conversion of a launch's pages into staged operands (kvs_mfma.hip).
@@ -238,8 +240,11 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 // few-row decode kernel (kvs_decode.hip): rows = n_q * G in [1, 6]
 bool decode_supports(int rows);
 hipError_t launch_decode(const AttendArgs& a, hipStream_t stream);
-// matrix-core kernel (kvs_mfma.hip) for more rows
+// matrix-core kernels (kvs_mfma.hip) for more rows: routes to the verify
+// kernel (kvs_verify.hip, 7 to 32 rows per kv head) and the prefill kernel
 hipError_t launch_mfma(const AttendArgs& a, hipStream_t stream);
+hipError_t launch_verify(const AttendArgs& a, hipStream_t stream);
+bool verify_rows(int rows);    // rows per kv head that the verify kernel takes
 // prefill kernel (kvs_prefill.hip), for blocks of more than 64 rows per kv head
 hipError_t launch_prefill(const AttendArgs& a, hipStream_t stream);
 bool prefill_rows(int rows);   // rows per kv head that the prefill kernel takes

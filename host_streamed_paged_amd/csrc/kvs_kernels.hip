@@ -31,37 +31,32 @@ namespace {
 
 
 // ---------------------------------------------------------------------------
-// Split-K combine: one workgroup per (output row, 16-channel slice), so that a
-// row's records are read by 8 compute units at once. Thread (gl, c) = (tid >>
-// 4, tid & 15) folds groups gl, gl + 16, gl + 32, ... of channel 16 s + c into
-// a running log-sum-exp state, 8 groups per step so that 8 record loads are in
-// flight; the 16 group lanes of a channel are then merged in lane order. The
-// order depends only on the number of groups, never on scheduling or
-// residency.
+// Split-K combine: one workgroup per (output row, CH-channel slice), so that
+// a row's records are read by several compute units at once. Thread (gl, c) =
+// (tid / CH, tid % CH) folds groups gl, gl + L, gl + 2 L, ... (L = THREADS /
+// CH group lanes) of channel CH s + c into a running log-sum-exp state, BATCH
+// groups per step so that BATCH record loads are in flight; the L group
+// lanes of a channel are then merged in lane order. The order depends only
+// on the number of groups, never on scheduling or residency.
 // ---------------------------------------------------------------------------
-#ifndef KVS_COMB_CH
-#define KVS_COMB_CH 16
-#endif
-constexpr int kCombCh = KVS_COMB_CH;            // channels per workgroup
-constexpr int kCombSlices = kHeadDim / kCombCh;
-constexpr int kCombLanes = 256 / kCombCh;       // group lanes per channel
-constexpr int kCombBatch = 8;
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part, int32_t n_groups,
-                                                      int32_t rows, float* __restrict__ out,
-                                                      float* __restrict__ lse) {
-    __shared__ float so[kCombLanes][kCombCh];
-    __shared__ float sm_[kCombLanes], sl_[kCombLanes];
+template <int CH, int BATCH, int THREADS>
+__global__ __launch_bounds__(THREADS) void combine_kernel(const float* __restrict__ part, int32_t n_groups,
+                                                          int32_t rows, float* __restrict__ out,
+                                                          float* __restrict__ lse) {
+    constexpr int kLanes = THREADS / CH;   // group lanes per channel
+    __shared__ float so[kLanes][CH];
+    __shared__ float sm_[kLanes], sl_[kLanes];
     const int row = blockIdx.x, sl = blockIdx.y;
-    const int gl = threadIdx.x / kCombCh, c = threadIdx.x % kCombCh;
+    const int gl = threadIdx.x / CH, c = threadIdx.x % CH;
     const int64_t gstride = (int64_t)rows * kPartStride;
     const float* p = part + (int64_t)row * kPartStride;
-    const int ch = kCombCh * sl + c;
+    const int ch = CH * sl + c;
     float M = -INFINITY, L = 0.f, O = 0.f;
-    for (int g0 = gl; g0 < n_groups; g0 += kCombLanes * kCombBatch) {
-        float mg[kCombBatch], lg[kCombBatch], og[kCombBatch];
+    for (int g0 = gl; g0 < n_groups; g0 += kLanes * BATCH) {
+        float mg[BATCH], lg[BATCH], og[BATCH];
 #pragma unroll
-        for (int k = 0; k < kCombBatch; ++k) {
-            const int gi = g0 + k * kCombLanes;
+        for (int k = 0; k < BATCH; ++k) {
+            const int gi = g0 + k * kLanes;
             const bool ok = gi < n_groups;
             const float* q = p + (int64_t)(ok ? gi : 0) * gstride;
             const float2 ml = *(const float2*)(q + kHeadDim);
@@ -71,13 +66,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         }
         float Mb = M;
 #pragma unroll
-        for (int k = 0; k < kCombBatch; ++k) Mb = fmaxf(Mb, mg[k]);
+        for (int k = 0; k < BATCH; ++k) Mb = fmaxf(Mb, mg[k]);
         if (Mb == -INFINITY) continue;
         const float sc = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - Mb);
         L *= sc;
         O *= sc;
 #pragma unroll
-        for (int k = 0; k < kCombBatch; ++k) {
+        for (int k = 0; k < BATCH; ++k) {
             const float w = (mg[k] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mg[k] - Mb);
             L = fmaf(lg[k], w, L);
             O = fmaf(og[k], w, O);
@@ -90,11 +85,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     if (gl == 0) {
         float Mt = sm_[0];
 #pragma unroll
-        for (int k = 1; k < kCombLanes; ++k) Mt = fmaxf(Mt, sm_[k]);
+        for (int k = 1; k < kLanes; ++k) Mt = fmaxf(Mt, sm_[k]);
         float ot = 0.f, lt = 0.f;
         if (Mt != -INFINITY) {
 #pragma unroll
-            for (int k = 0; k < kCombLanes; ++k) {
+            for (int k = 0; k < kLanes; ++k) {
                 const float w = (sm_[k] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sm_[k] - Mt);
                 ot = fmaf(so[k][c], w, ot);
                 lt = fmaf(sl_[k], w, lt);
@@ -105,6 +100,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         if (lse && sl == 0 && c == 0) lse[row] = empty ? -INFINITY : (Mt + log2f(lt)) * 0.69314718055994530942f;
     }
 }
+// Launches with many groups (a long cache in single-page groups) take
+// 32-channel slices with 512 threads: fewer workgroups read each record
+// (the launch is bound by the number of record reads), 16 group lanes per
+// channel as before.
+constexpr int kCombWideGroups = 256;   // groups from which a launch takes the wide shape
 
 // ---------------------------------------------------------------------------
 // Split-K combine for blocks with many rows (a prefill ubatch): one wave per
@@ -114,6 +114,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 // only on the number of groups.
 // ---------------------------------------------------------------------------
 constexpr int kCombRowsMin = 512;   // rows from which a launch takes this kernel
+constexpr int kCombBatch = 8;
 __global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restrict__ part, int32_t n_groups,
                                                            int32_t rows, float* __restrict__ out,
                                                            float* __restrict__ lse) {
@@ -295,7 +296,12 @@ hipError_t launch_combine(const float* part, int32_t n_groups, int32_t n_q, int3
     if (rows <= 0) return hipSuccess;
     if (rows >= kCombRowsMin)
         return launch_kernel(combine_rows_kernel, dim3((rows + 3) / 4), dim3(256), stream, part, n_groups, rows, out, lse);
-    return launch_kernel(combine_kernel, dim3(rows, kCombSlices), dim3(256), stream, part, n_groups, rows, out, lse);
+    if (n_groups >= kCombWideGroups) {
+        return launch_kernel(combine_kernel<32, 8, 512>, dim3(rows, kHeadDim / 32), dim3(512), stream, part, n_groups,
+                             rows, out, lse);
+    }
+    return launch_kernel(combine_kernel<16, 8, 256>, dim3(rows, kHeadDim / 16), dim3(256), stream, part, n_groups, rows,
+                         out, lse);
 }
 
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream) {

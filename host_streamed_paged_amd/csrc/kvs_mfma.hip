@@ -1,6 +1,8 @@
-// Matrix-core attention kernel for query blocks of 7 to 64 rows per kv head:
-// a speculative verify batch of 1 + draft tokens (page 2, "Phase arena:
-// speculative verify batches"), on CDNA4 v_mfma_f32_16x16x32_f16.
+// Matrix-core attention kernel for query blocks of 33 to 64 rows per kv head
+// (a speculative verify batch of 1 + draft tokens with a long draft; page 2,
+// "Phase arena: speculative verify batches"), on CDNA4
+// v_mfma_f32_16x16x32_f16. Blocks of 7 to 32 rows take the verify kernel
+// (kvs_verify.hip), which holds every row of a kv head in one workgroup.
 //
 // One workgroup = one segment (run of pages of one split-K group) x one kv
 // head x a tile of 16 RT query rows (row = query token x head of the GQA
@@ -168,32 +170,34 @@ void mfma_kernel(AttendArgs a) {
     // ---- this lane's query rows (one per row tile) and their visible prefix
     half8_t qop[RT][LIMBS][kNB];
     float cq[RT];
-    int64_t lim[RT];
     int qi_[RT], h_[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const int r = r0 + 16 * rt + n;
         qi_[rt] = r / G;
         h_[rt] = g * G + r % G;
-        lim[rt] = 0;
-        if (r < R) {
-            lim[rt] = a.n_kv;
-            if (a.causal) {
-                const int64_t c = a.q_pos0 + qi_[rt] + 1;
-                lim[rt] = c < lim[rt] ? c : lim[rt];
-            }
-        }
         query_operands<LIMBS>(a, qi_[rt], h_[rt], r < R, gq, qop[rt], cq[rt]);
     }
 
     const uint32_t m_nib = vconst(0x000F000Fu), magic = vconst(0x64006400u);
 
-    // smallest visible prefix over the workgroup's rows (causal limits grow
-    // with the query index): pages below it need no mask
+    // visible prefix: the smallest over the workgroup's rows, lim_min (causal
+    // limits grow with the query index; pages below it need no mask), and
+    // each row's excess over it, below 2^24 (rows past R have zero queries
+    // and any limit)
     int64_t lim_min = a.n_kv;
     if (a.causal) {
         const int64_t c = a.q_pos0 + r0 / G + 1;
         lim_min = c < lim_min ? c : lim_min;
+    }
+    int dlim[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        dlim[rt] = 0;
+        if (a.causal) {
+            const int64_t c = a.q_pos0 + qi_[rt] + 1;
+            dlim[rt] = (int)((c < a.n_kv ? c : a.n_kv) - lim_min);
+        }
     }
 
   for (int seg_i = slice; seg_i < a.n_segs; seg_i += a.n_slices) {
@@ -232,12 +236,10 @@ void mfma_kernel(AttendArgs a) {
         const int64_t base_tok = (int64_t)page * kPageTokens;
         const bool mask_page = base_tok + kPageTokens > lim_min;   // uniform
         const bool tail_page = base_tok + kPageTokens > a.n_kv;    // rows past the cache
-        int limrel[RT];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const int64_t x = lim[rt] - base_tok;
-            limrel[rt] = (int)(x < 0 ? 0 : (x > kPageTokens ? kPageTokens : x));
-        }
+        // lim_min - base_tok, clamped to a range where adding the row
+        // excesses cannot overflow
+        const int64_t lx = lim_min - base_tok;
+        const int lrel = (int)(lx < -kPageTokens ? -kPageTokens : (lx > kPageTokens ? kPageTokens : lx));
         const int64_t vx = a.n_kv - base_tok;
         const int valid = (int)(vx < 0 ? 0 : (vx > kPageTokens ? kPageTokens : vx));   // cached rows of the page
         // the worker's next page (this segment's next, else the first of its
@@ -248,19 +250,27 @@ void mfma_kernel(AttendArgs a) {
 
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), known to the compiler's wait tracking
         lds_barrier();   // the page's tiles are in LDS for every wave
+        if (tail_page) {
+            // rows past the cache may hold any bytes (NaN scales): their V
+            // scales are zeroed here, before the barriers that precede every
+            // read of the V tile, so that their V values are 0 (their scores
+            // are masked)
+            for (int e = tid; e < (kPageTokens - valid) * kNB; e += kThreads)
+                *(uint16_t*)(v_lds + (valid + e / kNB) * VT::kRow + (e % kNB) * VT::kBlock) = 0;
+        }
 
         // ---- QK over this wave's 64 tokens, one product per quant block (the
         // conversion reads the next token tile's K bytes while converting the
         // current one, and publishes each tile's block scales per token for
         // the score lanes)
         f32x4 s[4][RT];
-        KRaw kr[2][kNB];
-#pragma unroll
-        for (int b = 0; b < kNB; ++b) kr[0][b] = k_raw(k_lds, kTokW * w + n, b, gq);
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
+            KRaw kr[kNB];
+#pragma unroll
+            for (int b = 0; b < kNB; ++b) kr[b] = k_raw(k_lds, kTokW * w + 16 * tt + n, b, gq);
             if (gq == 0) {
-                const KRaw* k = kr[tt & 1];
+                const KRaw* k = kr;
                 *(uint2*)&ksc[w][(16 * tt + n) * 2] = make_uint2(k[0].db | (k[1].db << 16), k[2].db | (k[3].db << 16));
             }
             // written by this wave just above: the wave's own LDS operations
@@ -270,10 +280,6 @@ void mfma_kernel(AttendArgs a) {
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             const u32x4* sp = (const u32x4*)&ksc[w][(16 * tt + 4 * gq) * 2];
             const u32x4 sa = sp[0], sb = sp[1];
-            if (tt + 1 < 4) {
-#pragma unroll
-                for (int b = 0; b < kNB; ++b) kr[(tt + 1) & 1][b] = k_raw(k_lds, kTokW * w + 16 * (tt + 1) + n, b, gq);
-            }
             float dsc[4][kNB];
             tile_scales(sa, sb, dsc);
             // all products of the tile first, so that no scaling waits on the
@@ -281,7 +287,7 @@ void mfma_kernel(AttendArgs a) {
             f32x4 acc[RT][kNB];
 #pragma unroll
             for (int b = 0; b < kNB; ++b) {
-                const half8_t kop = k_codes(kr[tt & 1][b], b);
+                const half8_t kop = k_codes(kr[b], b);
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
                     acc[rt][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[rt][0][b], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
@@ -299,14 +305,15 @@ void mfma_kernel(AttendArgs a) {
         // s holds the float32 products, cq * s the log2-unit scores (cq > 0)
         if (mask_page) {
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
+            for (int rt = 0; rt < RT; ++rt) {
+                // token 64 w + 16 tt + 4 gq + i is visible to the row when
+                // 16 tt + i < its limit minus 64 w + 4 gq
+                const int lr = lrel + dlim[rt] - kTokW * w - 4 * gq;
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int tok = kTokW * w + 16 * tt + 4 * gq + i;
-                        s[tt][rt][i] = tok < limrel[rt] ? s[tt][rt][i] : -INFINITY;
-                    }
+                    for (int i = 0; i < 4; ++i) s[tt][rt][i] = 16 * tt + i < lr ? s[tt][rt][i] : -INFINITY;
+            }
         }
         float mx[RT];
 #pragma unroll
@@ -386,14 +393,15 @@ void mfma_kernel(AttendArgs a) {
         }
 
         // ---- P.V for channels 32 w .. 32 w + 31 (V quant block w)
-        auto pv_page = [&](auto tail) {
+        {
+            const VLane vl = v_lane<VT>(w, gq, n, 0);
             VRaw<VT> vr[2];
-            vr[0] = v_raw<VT>(v_lds, w, 0, gq, n);
+            vr[0] = v_raw_o<VT>(v_lds, vl, 0);
 #pragma unroll
             for (int c = 0; c < kChunks; ++c) {
                 half8_t vop[2];
-                if (c + 1 < kChunks) vr[(c + 1) & 1] = v_raw<VT>(v_lds, w, c + 1, gq, n);
-                v_convert<decltype(tail)::value, VT>(vr[c & 1], c, gq, valid, vsh, m_nib, magic, vop);
+                if (c + 1 < kChunks) vr[(c + 1) & 1] = v_raw_o<VT>(v_lds, vl, c + 1);
+                v_convert<false, VT>(vr[c & 1], c, gq, valid, vsh, m_nib, magic, vop);
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
                     const half8_t pop = *(const half8_t*)(pbuf + ((c * RT + rt) * 64 + lane) * 16);
@@ -401,9 +409,7 @@ void mfma_kernel(AttendArgs a) {
                     o[1][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop[1], pop, o[1][rt], 0, 0, 0);
                 }
             }
-        };
-        if (tail_page) pv_page(std::true_type{});
-        else pv_page(std::false_type{});
+        }
         // the next page's K tile (every wave is past QK) is fetched once this
         // wave's V reads are done: the compiler orders an LDS read after any
         // LDS DMA it cannot prove disjoint, so an earlier fetch would hold up
@@ -434,18 +440,6 @@ void mfma_kernel(AttendArgs a) {
   }
 }
 
-int compute_units() {
-    static int cus[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cus[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cus[dev] = n;
-    }
-    return cus[dev];
-}
-
 template <int RT, int LIMBS>
 hipError_t launch_rt(const AttendArgs& a, hipStream_t stream) {
     const int R = a.n_q * a.G;
@@ -469,11 +463,13 @@ hipError_t launch_rt(const AttendArgs& a, hipStream_t stream) {
 }  // namespace
 
 // 16-row tiles (with two query limbs, wider tiles would not fit two
-// workgroups' registers per compute unit); blocks of more than 64 rows per
-// kv head go to the prefill kernel.
+// workgroups' registers per compute unit), for 33 to 64 rows per kv head;
+// blocks of up to 32 rows go to the verify kernel, blocks of more than 64 to
+// the prefill kernel.
 hipError_t launch_mfma(const AttendArgs& a, hipStream_t stream) {
     if (a.n_segs <= 0 && copy_workgroups(a.copy) == 0) return hipSuccess;
     if (prefill_rows(a.n_q * a.G)) return launch_prefill(a, stream);
+    if (verify_rows(a.n_q * a.G)) return launch_verify(a, stream);
     return a.q_f16 ? launch_rt<1, 1>(a, stream) : launch_rt<1, 2>(a, stream);
 }
 

@@ -1017,6 +1017,7 @@ int attend_impl(kvs_pool* p, int32_t layer, const void* q, int32_t q_dtype, int3
     a.scale_log2 = scale * 1.44269504088896340736f;
     a.causal = causal ? 1 : 0;
     a.part = part;
+    a.spare = p->ring;
     const bool wide = kvs::prefill_rows(n_q * a.G);
     rc = run_layer(p, layer, s, [&](hipStream_t st, int /*lane*/, int32_t seg0, int32_t nseg, const uint8_t* ring_chunk,
                                     int32_t rank0, const kvs::CopyJob& cj) -> int {
