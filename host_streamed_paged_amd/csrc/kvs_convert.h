@@ -141,7 +141,7 @@ __device__ inline void v_convert(const VRaw<VT>& r, int c, int gq, int valid, in
 template <typename VT>
 struct VRaw1 {
     uint32_t byte[8];   // Q4_0: byte n of the slot's token; Q8_0: code 16 h + n
-    uint32_t d[8];      // scale bits of the slot's token
+    uint32_t dd[4];     // scale bits of slots 2 i (low half) and 2 i + 1 (high half)
 };
 // The lane's byte offsets into the V tile for v_raw1: `ob` of its byte in
 // token row 4 gq of block b (byte n, or code 16 h + n), `od` of that row's
@@ -172,15 +172,21 @@ __device__ inline VRaw<VT> v_raw_o(const uint8_t* v_lds, const VLane& vl, int c)
     }
     return r;
 }
+// v_raw1's reads: the slots' bytes through the lane's offsets from v_lane,
+// and their scales from a table of the tile's V scales, [block][token] as
+// binary16 bits (vsc), with two 8-byte reads: slots 0..3 are tokens
+// 32 c + 4 gq + 0..3, slots 4..7 tokens 32 c + 16 + 4 gq + 0..3.
 template <typename VT>
-__device__ inline VRaw1<VT> v_raw1(const uint8_t* v_lds, const VLane& vl, int c) {
+__device__ inline VRaw1<VT> v_raw1(const uint8_t* v_lds, const VLane& vl, const uint16_t* vsc_b, int c, int gq) {
     VRaw1<VT> r;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int ro = (32 * c + (j < 4 ? j : 12 + j)) * VT::kRow;
         r.byte[j] = v_lds[vl.ob + ro];
-        r.d[j] = *(const uint16_t*)(v_lds + (vl.od + ro));
     }
+    const uint2 lo = *(const uint2*)(vsc_b + 32 * c + 4 * gq);
+    const uint2 hi = *(const uint2*)(vsc_b + 32 * c + 16 + 4 * gq);
+    r.dd[0] = lo.x; r.dd[1] = lo.y; r.dd[2] = hi.x; r.dd[3] = hi.y;
     return r;
 }
 // Per-wave constants of v_convert1 for half h: the nibble mask and the f16
@@ -206,14 +212,14 @@ __device__ inline VHalf v_half(int h, int vshift) {
     }
     return r;
 }
-// The caller zeroes the scales of rows past the cache beforehand.
+// The caller's scale table holds 0 for rows past the cache.
 template <typename VT>
 __device__ inline half8_t v_convert1(const VRaw1<VT>& r, const VHalf& vh, uint32_t magic) {
     half8_t vop;
 #pragma unroll
     for (int jp = 0; jp < 4; ++jp) {
         const int j0 = 2 * jp, j1 = 2 * jp + 1;
-        const half2_t dd = as_h2(r.d[j0] | (r.d[j1] << 16));
+        const half2_t dd = as_h2(r.dd[jp]);
         const uint32_t x = __builtin_amdgcn_perm(r.byte[j1], r.byte[j0], 0x0c040c00u);
         half2_t v;
         if constexpr (VT::kQ8) v = q8_pair_f16(x, vh.cc, vh.off) * dd;

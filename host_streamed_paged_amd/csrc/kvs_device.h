@@ -11,8 +11,13 @@ namespace kvs {
 
 // Workgroup barrier that orders LDS only: unlike __syncthreads() it does not
 // wait for outstanding global loads, so page data stays in flight across it.
+// The wait is the builtin (lgkmcnt(0), the other counters untouched), not
+// inline asm: the compiler's wait tracking then knows that every LDS and
+// scalar load has completed here. A scalar load it still counts as pending
+// would make each later wait for an LDS result a full lgkmcnt(0).
 __device__ inline void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }

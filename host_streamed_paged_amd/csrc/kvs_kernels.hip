@@ -100,11 +100,13 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(const float* __restric
         if (lse && sl == 0 && c == 0) lse[row] = empty ? -INFINITY : (Mt + log2f(lt)) * 0.69314718055994530942f;
     }
 }
-// Launches with many groups (a long cache in single-page groups) take
-// 32-channel slices with 512 threads: fewer workgroups read each record
-// (the launch is bound by the number of record reads), 16 group lanes per
-// channel as before.
-constexpr int kCombWideGroups = 256;   // groups from which a launch takes the wide shape
+// Launches with many rows and many groups (a verify block over a long cache
+// in single-page groups) take 32-channel slices with 512 threads: fewer
+// workgroups read each record (such a launch is bound by the number of
+// record reads), 16 group lanes per channel as before. With few rows the
+// 16-channel slices keep more workgroups in flight.
+constexpr int kCombWideGroups = 256;   // groups and rows from which a launch takes the wide shape
+constexpr int kCombWideRows = 64;
 
 // ---------------------------------------------------------------------------
 // Split-K combine for blocks with many rows (a prefill ubatch): one wave per
@@ -296,7 +298,7 @@ hipError_t launch_combine(const float* part, int32_t n_groups, int32_t n_q, int3
     if (rows <= 0) return hipSuccess;
     if (rows >= kCombRowsMin)
         return launch_kernel(combine_rows_kernel, dim3((rows + 3) / 4), dim3(256), stream, part, n_groups, rows, out, lse);
-    if (n_groups >= kCombWideGroups) {
+    if (n_groups >= kCombWideGroups && rows >= kCombWideRows) {
         return launch_kernel(combine_kernel<32, 8, 512>, dim3(rows, kHeadDim / 32), dim3(512), stream, part, n_groups,
                              rows, out, lse);
     }

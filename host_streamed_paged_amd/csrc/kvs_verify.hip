@@ -75,14 +75,14 @@ __device__ inline PageDma<VT> dma_page(const uint8_t* rec, int g, int n_kv_heads
     D ad;
 #pragma unroll
     for (int k = 0; k < D::kKW; ++k) {
-        const int p = min(w + kVW * k, D::kKP - 1);
-        ad.src[k] = kt + p * 1024 + lane * 16;
+        const uint32_t p = (uint32_t)min(w + kVW * k, D::kKP - 1);
+        ad.src[k] = kt + (p * 1024u + (uint32_t)lane * 16u);
         dma16(ad.src[k], k_lds + p * 1024);
     }
 #pragma unroll
     for (int k = 0; k < D::kVWv; ++k) {
-        const int p = min(w + kVW * k, D::kVP - 1);
-        ad.src[D::kKW + k] = vt + p * 1024 + lane * 16;
+        const uint32_t p = (uint32_t)min(w + kVW * k, D::kVP - 1);
+        ad.src[D::kKW + k] = vt + (p * 1024u + (uint32_t)lane * 16u);
         dma16(ad.src[D::kKW + k], v_lds + p * 1024);
     }
     return ad;
@@ -130,6 +130,7 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(AttendArgs a) {
     __shared__ __attribute__((aligned(16))) uint32_t ksc[kVW][kVTok * 2];               // K scales [token][block] f16
     __shared__ float red_m[kVW][16 * RT];
     __shared__ float red_l[kVW][16 * RT];
+    __shared__ __attribute__((aligned(16))) uint16_t vsc[kNB][kPageTokens];   // the page's V scales, 0 past the cache
     // 1-D grid: the ring refill workgroups first, then the workers, permuted
     // so that each of the 8 XCDs takes a contiguous range of them.
     const int G = a.G, R = a.n_q * G;
@@ -227,7 +228,6 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(AttendArgs a) {
         const int page = segv.y + pi;
         const int64_t base_tok = (int64_t)page * kPageTokens;
         const bool mask_page = base_tok + kPageTokens > lim_min;   // uniform
-        const bool tail_page = base_tok + kPageTokens > a.n_kv;    // rows past the cache
         // lim_min - base_tok, clamped to a range where the row excesses
         // (below 2^24) cannot overflow
         const int64_t lx = lim_min - base_tok;
@@ -247,13 +247,15 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(AttendArgs a) {
 
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this page's DMAs (and any loaded state)
         lds_barrier();   // the page's tiles are in LDS; every wave is done with the other buffer
-        if (tail_page) {
-            // rows past the cache may hold any bytes (NaN scales): their V
-            // scales are zeroed here, before the barriers that precede every
-            // read of the V tile, so that their V values are 0 (their scores
-            // are masked). No LDS DMA is in flight yet.
-            for (int e = tid; e < (kPageTokens - valid) * kNB; e += kVThreads)
-                *(uint16_t*)(vc + (valid + e / kNB) * VT::kRow + (e % kNB) * VT::kBlock) = 0;
+        // the page's V scales as a [block][token] table, read after the
+        // barriers below: rows past the cache may hold any bytes (NaN
+        // scales) and get 0, so that their V values are 0 (their scores are
+        // masked). No LDS DMA is in flight yet.
+#pragma unroll
+        for (int k = 0; k < kNB * kPageTokens / kVThreads; ++k) {
+            const int e = tid + kVThreads * k, t = e % kPageTokens, b = e / kPageTokens;
+            const uint16_t bits = *(const uint16_t*)(vc + t * VT::kRow + b * VT::kBlock);
+            vsc[b][t] = t < valid ? bits : (uint16_t)0;
         }
         const PageDma<VT> ad = dma_page<VT>(next_rec, g, a.n_kv_heads, kn, vn, w, lane);
 
@@ -265,10 +267,8 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(AttendArgs a) {
             KRaw kr[kNB];
 #pragma unroll
             for (int b = 0; b < kNB; ++b) kr[b] = k_raw(kc, kVTok * w + 16 * tt + n, b, gq);
-            if (gq == 0) {
-                const KRaw* k = kr;
-                *(uint2*)&ksc[w][(16 * tt + n) * 2] = make_uint2(k[0].db | (k[1].db << 16), k[2].db | (k[3].db << 16));
-            }
+            // the four lanes of a token hold the same scales: all write them
+            *(uint2*)&ksc[w][(16 * tt + n) * 2] = make_uint2(kr[0].db | (kr[1].db << 16), kr[2].db | (kr[3].db << 16));
             // written by this wave just above: the wave's own LDS operations
             // complete in order
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -320,7 +320,7 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(AttendArgs a) {
                 for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[tt][rt][i]);
             mx = max_xor16(mx);
             mx = max_xor32(mx);
-            if (gq == 0) red_m[w][16 * rt + n] = mx * cq[rt];
+            red_m[w][16 * rt + n] = mx * cq[rt];   // the same bits in the row's four lanes
         }
         lds_barrier();   // maxima published
 
@@ -352,7 +352,7 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(AttendArgs a) {
             *(half8_t*)(p_lds + ((w * RT + rt) * 64 + lane) * 16) = pv;
             ls = add_xor16(ls);
             ls = add_xor32(ls);
-            if (gq == 0) red_l[w][16 * rt + n] = ls;
+            red_l[w][16 * rt + n] = ls;   // the same bits in the row's four lanes
         }
         lds_barrier();   // P operands and row sums published
 
@@ -383,18 +383,34 @@ __global__ __launch_bounds__(kVThreads) void verify_kernel(AttendArgs a) {
 
         // ---- P.V for channels 16 w .. 16 w + 15
         {
+            // each chunk's LDS reads (V bytes, scales, P operands) are issued
+            // two chunks ahead, after the current chunk's conversion (which
+            // waits for its own reads), and scheduling barriers keep the
+            // three parts of an iteration apart: a wait then never includes
+            // reads issued after the ones it needs
             const VLane vl = v_lane<VT>(vb, gq, n, vh);
-            VRaw1<VT> vr[2];
-            vr[0] = v_raw1<VT>(vc, vl, 0);
+            VRaw1<VT> vr[3];
+            half8_t pp[3][RT];
+            auto read_chunk = [&](int c) {
+                vr[c % 3] = v_raw1<VT>(vc, vl, vsc[vb], c, gq);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) pp[c % 3][rt] = *(const half8_t*)(p_lds + ((c * RT + rt) * 64 + lane) * 16);
+            };
+            read_chunk(0);
+            read_chunk(1);
 #pragma unroll
             for (int c = 0; c < kVChunks; ++c) {
-                if (c + 1 < kVChunks) vr[(c + 1) & 1] = v_raw1<VT>(vc, vl, c + 1);
-                const half8_t vop = v_convert1<VT>(vr[c & 1], hc, magic);
+                const half8_t vop = v_convert1<VT>(vr[c % 3], hc, magic);
+                half8_t pc[RT];
 #pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    const half8_t pop = *(const half8_t*)(p_lds + ((c * RT + rt) * 64 + lane) * 16);
-                    o[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop, o[rt], 0, 0, 0);
-                }
+                for (int rt = 0; rt < RT; ++rt) pc[rt] = pp[c % 3][rt];
+                asm volatile("" : "+v"(pc[0]));   // the P operands are waited for here too
+                __builtin_amdgcn_sched_barrier(0);
+                if (c + 2 < kVChunks) read_chunk(c + 2);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) o[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pc[rt], o[rt], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
 
