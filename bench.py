@@ -49,7 +49,7 @@ STREAMED_RING48 = dict(ring_pages=48, chunk_pages=4, group_pages=1)
 POOL_CFG = {
     "resident_decode_32k": dict(ring_pages=48, chunk_pages=4, group_pages=1),
     "streamed_decode_256k": dict(ring_pages=16, chunk_pages=4, group_pages=1),
-    "spec_verify_160k": dict(ring_pages=48, chunk_pages=4, group_pages=1),
+    "spec_verify_160k": dict(ring_pages=48, chunk_pages=4, group_pages=2),
     "prefill_ubatch_128k": dict(ring_pages=96, chunk_pages=16, group_pages=8),
 }
 
