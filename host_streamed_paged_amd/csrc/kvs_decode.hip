@@ -12,9 +12,9 @@
 //       v_mfma_i32_16x16x32_i8: exact integer products of the Q8_0 codes,
 //       loaded straight from the page record into the lane of their token,
 //       with the query held as 16-bit fixed point (per row scale, split into
-//       int8 high and low bytes, one instruction each). The block scale
-//       multiplies each block's integer sum, and the 4 block terms are added
-//       in a fixed order.
+//       int8 high and low bytes, one instruction each). Each block's
+//       integer sum times its scale is accumulated in float32, block 0
+//       first, in a fixed order.
 //   softmax  lanes hold query rows of one token: slice maxima and row sums
 //       are reductions over the 16 lanes of a DPP row; p = exp2(s - m) in
 //       log2 units (the softmax scale is folded into the query scale).
@@ -309,7 +309,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
         float s[4][4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            float f[kNB][4];
 #pragma unroll
             for (int blk = 0; blk < kNB; ++blk) {
                 const int o = blk == 0 ? 0 : blk == 1 ? 3 : blk == 2 ? 5 : 8;
@@ -329,13 +328,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
 #pragma clang fp contract(off)
-                    f[blk][i] = (float)(ih[i] * 256 + il[i]) * d;
+                    const float x = (float)(ih[i] * 256 + il[i]);
+                    s[t][i] = blk == 0 ? x * d : __builtin_fmaf(x, d, s[t][i]);
                 }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-#pragma clang fp contract(off)
-                s[t][i] = (f[0][i] + f[1][i]) + (f[2][i] + f[3][i]);
             }
         }
         if constexpr (kPrefetch) issue_k(rec_next, kw);   // the scores no longer need kw
@@ -361,10 +356,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttendArgs a) {
         for (int i = 0; i < 4; ++i) {
             m_w[i] = max_over_row16(fmaxf(fmaxf(s[0][i], s[1][i]), fmaxf(s[2][i], s[3][i])));
             const float mref = m_w[i] == -INFINITY ? 0.f : m_w[i];
+            const float moff = -(kav[i] * mref);
             float acc = 0.f;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                e[t][i] = __builtin_amdgcn_exp2f(kav[i] * (s[t][i] - mref));
+                e[t][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(kav[i], s[t][i], moff));
                 acc += e[t][i];
             }
             lsum[i] = sum_over_row16(acc);
