@@ -10,10 +10,15 @@
 // pipeline: the raw K and V rows of a sub-block (13 KB, or 17 KB with Q8_0
 // V) are brought into LDS by LDS DMA three steps ahead (four raw buffers);
 // in step st all 8 waves convert sub-block st + 1 into f16 matrix-core
-// operands in one of two operand buffers (K codes exact, K block scales as
-// float32, V^T as d * (u - 8) or d * code rounded once to f16, divided by a
-// power of two when the sub-block's scales could overflow), then compute
-// sub-block st from the other. Each page is converted once per row block,
+// operands (K codes exact, K block scales as float32, V^T as d * (u - 8) or
+// d * code rounded once to f16, divided by a power of two when the
+// sub-block's scales could overflow; K operands in one of two K buffers, V^T
+// in one of three V buffers), then compute the scores and probabilities of
+// sub-block st and the P.V of sub-block st - 1. That P.V does not depend on
+// st's scores, so its matrix instructions are issued in chunks between st's
+// exponentials and run while the vector unit computes them; the state still
+// sees every operation in the order of a sub-block-at-a-time walk, so the
+// results are the same bits. Each page is converted once per row block,
 // inside the workgroup: no staging launch, no staging memory. Per sub-block
 // and wave:
 //   QK   A_b^T (16 tokens x 16 rows) = K_b . Q_b^T per 16-token tile and quant
@@ -55,14 +60,17 @@ constexpr int kRTW = 2;                      // 16-row tiles per wave
 constexpr int kRowsWG = 16 * kRTW * kPWaves; // rows per workgroup (256)
 constexpr int kSub = 64;                     // tokens per sub-block
 constexpr int kSubs = kPageTokens / kSub;    // sub-blocks per page
-// Operands of a sub-block in LDS: K fragments [4 token tiles][4 blocks][64
-// lanes] x 16 B, V^T fragments [2 chunks][8 channel tiles][64 lanes] x 16 B,
-// the K block scales [token][block] float32, the V shift of each block.
+// Operands of a sub-block in LDS, in two buffers: the K buffer holds the K
+// fragments [4 token tiles][4 blocks][64 lanes] x 16 B and then the K block
+// scales [token][block] float32; the V buffer holds the V^T fragments
+// [2 chunks][8 channel tiles][64 lanes] x 16 B and then the V shift of each
+// block (16 B per block, the shift 4 times).
 constexpr int kSubK = 4 * kNB * 64 * 16;       // 16 KB
 constexpr int kSubV = 2 * 8 * 64 * 16;         // 16 KB
 constexpr int kSubS = kSub * kNB * 4;          // 1 KB
-constexpr int kConvShift = kSubK + kSubV + kSubS;   // 16 B per block: its shift, 4 times
-constexpr int kConvBytes = kConvShift + 16 * kNB;
+constexpr int kKBytes = kSubK + kSubS;         // K buffer
+constexpr int kVShiftOfs = kSubV;              // shifts in the V buffer
+constexpr int kVBytes = kVShiftOfs + 16 * kNB; // V buffer
 // A sub-block's raw rows for one kv head as the record holds them: 64 K rows
 // (136 B each) then 64 V rows, moved by 1 KB LDS DMA pieces.
 template <typename VT>
@@ -112,13 +120,13 @@ __device__ inline void keep(const DmaAddr<VT>& ad) {
     for (int k = 0; k < RawSub<VT>::kWavePieces; ++k) asm volatile("" ::"v"(ad.src[k]));
 }
 
-// Convert a raw sub-block (LDS rw) into its operands (LDS cv), with the
+// Convert a raw sub-block (LDS rw) into its operands (LDS kc, vc), with the
 // conversion code of the other matrix-core paths (kvs_convert.h); `valid`
 // rows of the sub-block are cached. Wave w converts K fragments (tile, block)
 // = (w >> 2, w & 3) and (2 + (w >> 2), w & 3), their block scales, and V^T
 // chunk w >> 2 of block w & 3. The code has no branch.
 template <typename VT>
-__device__ inline void convert_sub(const uint8_t* rw, uint8_t* cv, int valid, int tid, int w, int lane,
+__device__ inline void convert_sub(const uint8_t* rw, uint8_t* kc, uint8_t* vc, int valid, int tid, int w, int lane,
                                    uint32_t m_nib, uint32_t magic) {
     const int n = lane & 15, gq = lane >> 4, b = w & 3, c = w >> 2;
     // The lane's 8 codes start at byte 34 b + 2 + 8 gq of its token's row:
@@ -141,7 +149,7 @@ __device__ inline void convert_sub(const uint8_t* rw, uint8_t* cv, int valid, in
         const int f = w + 8 * k;   // (tile, block) = (f >> 2, b)
         const uint32_t* p = (const uint32_t*)(rw + 16 * (f >> 2) * kKRow + ko);
         const uint32_t x0 = p[0], x1 = p[1], x2 = p[2];
-        *(half8_t*)(cv + f * 1024 + oo) =
+        *(half8_t*)(kc + f * 1024 + oo) =
             q8_codes_f16(__builtin_amdgcn_alignbyte(x1, x0, ksh), __builtin_amdgcn_alignbyte(x2, x1, ksh));
     }
     {
@@ -149,7 +157,7 @@ __device__ inline void convert_sub(const uint8_t* rw, uint8_t* cv, int valid, in
         // 34 = 32 + 2), blocks 2, 3 in dword 17 and dword 25 (byte 102)
         const uint32_t* rp = (const uint32_t*)(rw + so);
         const uint32_t d0 = rp[0], d1 = rp[8], d2 = rp[17], d3 = rp[25];
-        *(f32x4*)(cv + kSubK + kSubV + st16) = f32x4{scale_f32(d0), scale_f32(d1 >> 16), scale_f32(d2), scale_f32(d3 >> 16)};
+        *(f32x4*)(kc + kSubK + st16) = f32x4{scale_f32(d0), scale_f32(d1 >> 16), scale_f32(d2), scale_f32(d3 >> 16)};
     }
     // Block b's V rows as whole dwords: an even block starts on a dword
     // boundary (its scale is the dword's low half), an odd one 2 bytes into
@@ -162,7 +170,7 @@ __device__ inline void convert_sub(const uint8_t* rw, uint8_t* cv, int valid, in
     const uint32_t w0 = *(const uint32_t*)(rw + vs);
     const uint32_t sbits = (vsh_b ? w0 >> 16 : w0) & 0x7FFFu;
     const int vsh = __any(lane < valid && sbits > (VT::kQ8 ? kVBigBits8 : kVBigBits)) ? (VT::kQ8 ? kVShift8 : kVShift) : 0;
-    *(int4v*)(cv + kConvShift + 16 * b) = int4v{vsh, vsh, vsh, vsh};
+    *(int4v*)(vc + kVShiftOfs + 16 * b) = int4v{vsh, vsh, vsh, vsh};
     // the V rows of v_raw (kvs_convert.h), through the opaque lane offset
     VRaw<VT> vr;
 #pragma unroll
@@ -175,19 +183,22 @@ __device__ inline void convert_sub(const uint8_t* rw, uint8_t* cv, int valid, in
     }
     half8_t vop[2];
     v_convert<true, VT>(vr, c, gq, valid, vsh, m_nib, magic, vop);
-    *(half8_t*)(cv + kSubK + (c * 8 + 2 * b) * 1024 + oo) = vop[0];
-    *(half8_t*)(cv + kSubK + (c * 8 + 2 * b + 1) * 1024 + oo) = vop[1];
+    *(half8_t*)(vc + (c * 8 + 2 * b) * 1024 + oo) = vop[0];
+    *(half8_t*)(vc + (c * 8 + 2 * b + 1) * 1024 + oo) = vop[1];
 }
 
 template <int LIMBS, typename VT>
 __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(AttendArgs a) {
-    // Two operand buffers (the sub-block being computed and the next one
-    // being converted) and four raw buffers (the one being converted and
-    // DMAs in flight), each its own LDS array: the compiler then orders a
-    // read of one array only after the DMA into that array, not after DMAs
-    // still in flight into the others.
-    __shared__ __attribute__((aligned(16))) uint8_t cv0[kConvBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t cv1[kConvBytes];
+    // Two K operand buffers (the sub-block whose scores are computed and the
+    // next one being converted), three V operand buffers (those two and the
+    // previous sub-block, whose P.V is computed in the same step) and four
+    // raw buffers (the one being converted and DMAs in flight). Each raw
+    // buffer is its own LDS array: the compiler then orders a read of one
+    // array only after the DMA into that array, not after DMAs still in
+    // flight into the others.
+    __shared__ __attribute__((aligned(16))) uint8_t kc0[kKBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t kc1[kKBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t vcs[3 * kVBytes];
     __shared__ __attribute__((aligned(16))) uint8_t rw0[RawSub<VT>::kBytes];
     __shared__ __attribute__((aligned(16))) uint8_t rw1[RawSub<VT>::kBytes];
     __shared__ __attribute__((aligned(16))) uint8_t rw2[RawSub<VT>::kBytes];
@@ -308,19 +319,22 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(AttendArgs a) {
     dma_step(min(1, n_steps - 1), rw1);
     dma_step(min(2, n_steps - 1), rw2);
 
-    // ---- one sub-block from its operands in B
-    auto compute = [&](int st, const uint8_t* B) {
+    // ---- scores of sub-block st from its K operands in KB, and from them
+    // the P^T operands pp (relative to the running max after the sub-block)
+    // and the factor alpha by which the state is to be rescaled when the
+    // running max moved (rescale)
+    auto scores = [&](int st, const uint8_t* KB, f32x4 (&s)[4][kRTW], float (&m_use)[kRTW], float (&alpha)[kRTW],
+                      bool& rescale) {
         const int base_tok = kSub * st;                     // from the segment's first token
         const bool mask_sub = base_tok + kSub > lim_min_rel;   // wave-uniform
 
         // ---- QK (float32 products; cq * s is the log2-unit score)
-        f32x4 s[4][kRTW];
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
             f32x4 acc[kRTW][kNB];
 #pragma unroll
             for (int b = 0; b < kNB; ++b) {
-                const half8_t kop = *(const half8_t*)(B + ((tt * kNB + b) * 64 + lane) * 16);
+                const half8_t kop = *(const half8_t*)(KB + ((tt * kNB + b) * 64 + lane) * 16);
 #pragma unroll
                 for (int rt = 0; rt < kRTW; ++rt) {
                     acc[rt][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[rt][0][b], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
@@ -329,7 +343,7 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(AttendArgs a) {
                 }
             }
             // scales of the lane's four tokens 16 tt + 4 gq + i: [i][b] float32
-            const f32x4* sc = (const f32x4*)(B + kSubK + kSubV + (16 * tt + 4 * gq) * kNB * 4);
+            const f32x4* sc = (const f32x4*)(KB + kSubK + (16 * tt + 4 * gq) * kNB * 4);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const f32x4 d = sc[i];
@@ -349,18 +363,18 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(AttendArgs a) {
         if (mask_sub) {
 #pragma unroll
             for (int rt = 0; rt < kRTW; ++rt) {
+                // token 16 tt + 4 gq + i is visible when 16 tt + i < lg
+                // (compared with immediates: no per-token index registers)
                 const int x = lim[rt] - base_tok;
-                const int lr = x < 0 ? 0 : (x > kSub ? kSub : x);
+                const int lg = (x < 0 ? 0 : (x > kSub ? kSub : x)) - 4 * gq;
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) s[tt][rt][i] = 16 * tt + 4 * gq + i < lr ? s[tt][rt][i] : -INFINITY;
+                    for (int i = 0; i < 4; ++i) s[tt][rt][i] = 16 * tt + i < lg ? s[tt][rt][i] : -INFINITY;
             }
         }
 
         // ---- softmax over the sub-block
-        float alpha[kRTW], m_use[kRTW];
-        bool rescale = false;
 #pragma unroll
         for (int rt = 0; rt < kRTW; ++rt) {
             float mx = -INFINITY;
@@ -377,17 +391,27 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(AttendArgs a) {
             m_use[rt] = m_run[rt] == -INFINITY ? 0.f : m_run[rt];
             rescale |= grow;
         }
-        // P^T operands: chunk c's slot j of lane group gq is token 32 c + 4 gq + j
-        // (j < 4, tile 2 c) or 32 c + 12 + 4 gq + j (j >= 4, tile 2 c + 1)
-        half8_t pop[2][kRTW];
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // P^T operands from the scores: chunk c's slot j of lane group gq is
+    // token 32 c + 4 gq + j (j < 4, tile 2 c) or 32 c + 12 + 4 gq + j (j >= 4,
+    // tile 2 c + 1); exps(k) gives slots 2 (k & 3) and 2 (k & 3) + 1 of chunk
+    // (k >> 2) & 1 of row tile k >> 3
+    // (the pair is pinned where it is computed: an empty volatile asm takes
+    // it, so the compiler cannot sink the arithmetic to the pair's use)
+    auto exps = [&](int k, const f32x4 (&s)[4][kRTW], const float (&m_use)[kRTW], half8_t (&pp)[2][kRTW]) {
+        const int rt = k >> 3, c = (k >> 2) & 1, j0 = 2 * (k & 3);
+        half2_t h;
 #pragma unroll
-        for (int rt = 0; rt < kRTW; ++rt)
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    pop[c][rt][j] = (_Float16)__builtin_amdgcn_exp2f(
-                        __builtin_fmaf(s[2 * c + (j >> 2)][rt][j & 3], cq[rt], -m_use[rt]));
+        for (int j = 0; j < 2; ++j)
+            h[j] = (_Float16)__builtin_amdgcn_exp2f(
+                __builtin_fmaf(s[2 * c + ((j0 + j) >> 2)][rt][(j0 + j) & 3], cq[rt], -m_use[rt]));
+        asm volatile("" : "+v"(h));
+        pp[c][rt][j0] = h[0];
+        pp[c][rt][j0 + 1] = h[1];
+    };
+    // ---- the state rescaled when the running max moved
+    auto apply_alpha = [&](const float (&alpha)[kRTW], bool rescale) {
         if (__any(rescale)) {
 #pragma unroll
             for (int rt = 0; rt < kRTW; ++rt) {
@@ -396,11 +420,13 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(AttendArgs a) {
                 for (int ct = 0; ct < 8; ++ct) o[ct][rt] *= alpha[rt];
             }
         }
-        // ---- the sub-block's V shifts; an exact rescale of a block's
-        // accumulators when its shift changes
+    };
+    // ---- the V shifts of the sub-block in VB: an exact rescale of a
+    // block's accumulators when its shift changes
+    auto v_shifts = [&](const uint8_t* VB) {
 #pragma unroll
         for (int b = 0; b < kNB; ++b) {
-            const int vsh = __builtin_amdgcn_readfirstlane(*(const int32_t*)(B + kConvShift + 16 * b));
+            const int vsh = __builtin_amdgcn_readfirstlane(*(const int32_t*)(VB + kVShiftOfs + 16 * b));
             if (vsh != vsh_run[b]) {
                 const float f = __builtin_amdgcn_ldexpf(1.f, vsh_run[b] - vsh);
 #pragma unroll
@@ -411,56 +437,123 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(AttendArgs a) {
                 vsh_run[b] = vsh;
             }
         }
-
-        // ---- P.V, and the row sums on a tile of ones
+    };
+    // ---- P.V of the sub-block in VB with its P^T operands pp, and the row
+    // sums on a tile of ones
+    auto pv = [&](const uint8_t* VB, const half8_t (&pp)[2][kRTW]) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
 #pragma unroll
             for (int ct = 0; ct < 8; ++ct) {
-                const half8_t vop = *(const half8_t*)(B + kSubK + ((c * 8 + ct) * 64 + lane) * 16);
+                const half8_t vop = *(const half8_t*)(VB + ((c * 8 + ct) * 64 + lane) * 16);
 #pragma unroll
                 for (int rt = 0; rt < kRTW; ++rt)
-                    o[ct][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop[c][rt], o[ct][rt], 0, 0, 0);
+                    o[ct][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pp[c][rt], o[ct][rt], 0, 0, 0);
             }
 #pragma unroll
             for (int rt = 0; rt < kRTW; ++rt)
-                lsum[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pop[c][rt], lsum[rt], 0, 0, 0);
+                lsum[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pp[c][rt], lsum[rt], 0, 0, 0);
         }
     };
 
-    // ---- pipeline over sub-blocks: in step st every wave converts sub-block
-    // st + 1 (raw rows DMA'd two steps earlier) while it computes sub-block
-    // st, and issues the DMA of st + 3. Past the last sub-block, the DMA and
-    // the conversion repeat the last one into free buffers (no branch, so the
-    // compiler counts the DMAs in flight exactly); nothing reads them.
+    // ---- pipeline over sub-blocks. Step st: every wave converts sub-block
+    // st + 1 (raw rows DMA'd two steps earlier), issues the DMA of st + 3,
+    // computes the scores and probabilities of sub-block st and then the P.V
+    // of sub-block st - 1, whose matrix instructions do not depend on the
+    // scores and so can issue while they are computed. The state sees the
+    // same operations in the same order as when each sub-block's P.V follows
+    // its own scores: the rescale for st's max comes after st - 1's P.V, the
+    // V shift rescale for st just before st's P.V. Past the last sub-block,
+    // the DMA and the conversion repeat the last one into free buffers (no
+    // branch, so the compiler counts the DMAs in flight exactly); nothing
+    // reads them.
     constexpr int kWP = RawSub<VT>::kWavePieces;
+    auto vbuf = [&](int i) { return vcs + i * kVBytes; };   // V buffer of sub-block st: st % 3
     __builtin_amdgcn_s_waitcnt(vm_wait(2 * kWP));   // raw 0 landed, 1 and 2 may be in flight
     lds_barrier();
-    convert_sub<VT>(rw0, cv0, valid_of(0), tid, w, lane, m_nib, magic);
+    convert_sub<VT>(rw0, kc0, vbuf(0), valid_of(0), tid, w, lane, m_nib, magic);
 
-    auto do_step = [&](int st, const uint8_t* C, uint8_t* Cn, const uint8_t* Rn, uint8_t* D) {
-        // raw sub-block st + 1 is in LDS for every wave (a wave may still have
-        // the DMA of st + 2 in flight), the operands of st are published, and
-        // every wave is done with the operands of st - 1 and the raw rows of
-        // st - 1, whose buffers take st + 1 and st + 3. The DMA of st + 3 is
-        // issued after the conversion's LDS accesses: the compiler cannot tell
-        // every one of them apart from the DMA's target and would wait for
-        // the DMA there; after it, the step reads only the operand buffer.
+    // the step's front: raw sub-block st + 1 is in LDS for every wave (a wave
+    // may still have the DMA of st + 2 in flight), the operands of st are
+    // published, and every wave is done with step st - 1, whose buffers take
+    // st + 1 (K and V operands) and st + 3 (raw rows). The DMA of st + 3 is
+    // issued after the conversion's LDS accesses: the compiler cannot tell
+    // every one of them apart from the DMA's target and would wait for the
+    // DMA there; after it, the step reads only operand buffers.
+    auto front = [&](int st, int vi, uint8_t* KN, const uint8_t* Rn, uint8_t* D, bool prev) {
         __builtin_amdgcn_s_waitcnt(vm_wait(kWP));
         lds_barrier();
-        convert_sub<VT>(Rn, Cn, valid_of(min(st + 1, n_steps - 1)), tid, w, lane, m_nib, magic);
+        if (prev) v_shifts(vbuf(vi == 0 ? 2 : vi - 1));
+        convert_sub<VT>(Rn, KN, vbuf(vi == 2 ? 0 : vi + 1), valid_of(min(st + 1, n_steps - 1)), tid, w, lane, m_nib, magic);
         const DmaAddr<VT> ad = dma_step(min(st + 3, n_steps - 1), D);
         __builtin_amdgcn_sched_barrier(0);
-        compute(st, C);
+        return ad;
+    };
+    half8_t pprev[2][kRTW];
+    // step 0: no previous sub-block
+    {
+        const DmaAddr<VT> ad = front(0, 0, kc1, rw1, rw3, false);
+        f32x4 sc[4][kRTW];
+        float m_use[kRTW], alpha[kRTW];
+        bool rescale = false;
+        scores(0, kc0, sc, m_use, alpha, rescale);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) exps(k, sc, m_use, pprev);
+        apply_alpha(alpha, rescale);
+        keep<VT>(ad);
+    }
+    auto do_step = [&](int st, int vi, const uint8_t* KC, uint8_t* KN, const uint8_t* Rn, uint8_t* D) {
+        const DmaAddr<VT> ad = front(st, vi, KN, Rn, D, true);
+        half8_t pc[2][kRTW];
+        f32x4 sc[4][kRTW];
+        float m_use[kRTW], alpha[kRTW];
+        bool rescale = false;
+        scores(st, KC, sc, m_use, alpha, rescale);
+        // P.V of sub-block st - 1 (independent of st's scores) in 16 chunks of
+        // one channel tile, each followed by two of st's exponentials per row
+        // tile, so that the vector unit works while the matrix products run;
+        // the V operands are read two chunks ahead
+        const uint8_t* VP = vbuf(vi == 0 ? 2 : vi - 1);
+        auto vread = [&](int k) { return *(const half8_t*)(VP + (((k >> 3) * 8 + (k & 7)) * 64 + lane) * 16); };
+        half8_t vq[3];
+        vq[0] = vread(0);
+        vq[1] = vread(1);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int c = k >> 3, ct = k & 7;
+            if (k + 2 < 16) vq[(k + 2) % 3] = vread(k + 2);
+#pragma unroll
+            for (int rt = 0; rt < kRTW; ++rt)
+                o[ct][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vq[k % 3], pprev[c][rt], o[ct][rt], 0, 0, 0);
+            exps(k, sc, m_use, pc);
+            if (ct == 7) {
+#pragma unroll
+                for (int rt = 0; rt < kRTW; ++rt)
+                    lsum[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pprev[c][rt], lsum[rt], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        apply_alpha(alpha, rescale);
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int rt = 0; rt < kRTW; ++rt) pprev[c][rt] = pc[c][rt];
         keep<VT>(ad);
     };
-    // steps four at a time, so that each names its buffers statically
-    for (int st = 0; st < n_steps; st += 4) {
-        do_step(st, cv0, cv1, rw1, rw3);
-        if (st + 1 < n_steps) do_step(st + 1, cv1, cv0, rw2, rw0);
-        if (st + 2 < n_steps) do_step(st + 2, cv0, cv1, rw3, rw1);
-        if (st + 3 < n_steps) do_step(st + 3, cv1, cv0, rw0, rw2);
+    // steps four at a time from step 1, so that each names its raw and K
+    // buffers statically; the V buffer index st % 3 is carried along
+    int vi = 1;
+    auto nx = [](int i) { return i == 2 ? 0 : i + 1; };
+    for (int st = 1; st < n_steps; st += 4) {
+        do_step(st, vi, kc1, kc0, rw2, rw0);
+        vi = nx(vi);
+        if (st + 1 < n_steps) { do_step(st + 1, vi, kc0, kc1, rw3, rw1); vi = nx(vi); }
+        if (st + 2 < n_steps) { do_step(st + 2, vi, kc1, kc0, rw0, rw2); vi = nx(vi); }
+        if (st + 3 < n_steps) { do_step(st + 3, vi, kc0, kc1, rw1, rw3); vi = nx(vi); }
     }
+    // the last sub-block's P.V (its operands were published before the last step)
+    v_shifts(vbuf(vi == 0 ? 2 : vi - 1));
+    pv(vbuf(vi == 0 ? 2 : vi - 1), pprev);
 
     // ---- group state -> partial records (O back in absolute units)
 #pragma unroll
@@ -489,7 +582,8 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(AttendArgs a) {
 // `page`); blocks past the pages are ring refill workgroups.
 template <typename VT>
 __global__ __launch_bounds__(kPThreads) void stage_kernel(StageArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t cv[kConvBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t kc[kKBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t vc[kVBytes];
     __shared__ __attribute__((aligned(16))) uint8_t rw[RawSub<VT>::kBytes];
     if ((int)blockIdx.x >= a.n_pages) {   // ring refill workgroup: its first 256 threads copy
         if (threadIdx.x < 256) copy_role(a.copy, ((int)blockIdx.x - a.n_pages) * (int)gridDim.y + (int)blockIdx.y);
@@ -514,14 +608,14 @@ __global__ __launch_bounds__(kPThreads) void stage_kernel(StageArgs a) {
         __builtin_amdgcn_s_waitcnt(vm_wait(0));
         lds_barrier();   // the raw rows are in LDS for every wave
         const int64_t x = a.n_kv - ((int64_t)page * kPageTokens + kSub * sb);
-        convert_sub<VT>(rw, cv, (int)(x < 0 ? 0 : (x > kSub ? kSub : x)), tid, w, lane, m_nib, magic);
+        convert_sub<VT>(rw, kc, vc, (int)(x < 0 ? 0 : (x > kSub ? kSub : x)), tid, w, lane, m_nib, magic);
         lds_barrier();   // the operands are in LDS for every wave
         for (int o = 16 * tid; o < kSubK; o += 16 * kPThreads) {
-            *(u32x4*)(tile + sb * kSubK + o) = *(const u32x4*)(cv + o);
-            *(u32x4*)(tile + kStagedK + sb * kSubV + o) = *(const u32x4*)(cv + kSubK + o);
+            *(u32x4*)(tile + sb * kSubK + o) = *(const u32x4*)(kc + o);
+            *(u32x4*)(tile + kStagedK + sb * kSubV + o) = *(const u32x4*)(vc + o);
         }
-        if (16 * tid < kSubS) *(u32x4*)(tile + kStagedOps + sb * kSubS + 16 * tid) = *(const u32x4*)(cv + kSubK + kSubV + 16 * tid);
-        if (tid < kNB) *(int32_t*)(tile + kStagedShift + 4 * (kNB * sb + tid)) = *(const int32_t*)(cv + kConvShift + 16 * tid);
+        if (16 * tid < kSubS) *(u32x4*)(tile + kStagedOps + sb * kSubS + 16 * tid) = *(const u32x4*)(kc + kSubK + 16 * tid);
+        if (tid < kNB) *(int32_t*)(tile + kStagedShift + 4 * (kNB * sb + tid)) = *(const int32_t*)(vc + kVShiftOfs + 16 * tid);
         lds_barrier();   // every wave is done with both buffers
     }
 }
