@@ -333,7 +333,7 @@ def multi_leg(name, cfg_kw, threads, link, steps, kind, zero_copy=True):
     layer_bytes = wl.n_pages * pb
     flops = 4 * wl.n_q_heads * wl.head_dim * allowed_keys(wl)
     kname = "prefill_kernel (256-row workgroups, pages converted in the workgroup)" if kind == "prefill" \
-        else "mfma_kernel (16-row tiles, in-kernel conversion)"
+        else "verify_kernel (one 8-wave workgroup per kv head with every row, pages converted in the kernel)"
     k = {"kernel": kname + ", all pages resident", "layer_us": round(layer_ms * 1e3, 2),
          "attn_us_per_layer": round(att_ms * 1e3, 2), "attn_launches": r["attn_launches"],
          "combine_us_per_layer": round(r["combine_ms_total"] / max(1, layers_timed) * 1e3, 2),
