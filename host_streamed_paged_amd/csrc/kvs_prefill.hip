@@ -143,48 +143,68 @@ __device__ inline void convert_sub(const uint8_t* rw, uint8_t* kc, uint8_t* vc, 
     uint32_t ko = n * kKRow + (kofs - ksh), so = stok * kKRow, oo = lane * 16;
     const int vsh_b = (VT::kBlock * b) & 3;   // block b starts 0 or 2 bytes into a dword
     uint32_t vo = RawSub<VT>::kK + b * VT::kBlock - vsh_b + 4 * gq * VT::kRow, st16 = 16 * stok;
-    asm volatile("" : "+v"(ko), "+v"(so), "+v"(oo), "+v"(vo), "+v"(st16));
+    uint32_t vdo = (c * 8 + 2 * b) * 1024 + lane * 16;   // the lane's two V^T fragment stores
+    asm volatile("" : "+v"(ko), "+v"(so), "+v"(oo), "+v"(vo), "+v"(st16), "+v"(vdo));
+    // Every LDS read of the conversion is issued first, so that one wait
+    // covers them all (a read, its wait and its use per piece would make the
+    // conversion a chain of LDS round trips). The K codes: three dwords per
+    // fragment. The row's block scales: blocks 0, 1 in dword 0 and dword 8
+    // (byte 34 = 32 + 2), blocks 2, 3 in dword 17 and dword 25 (byte 102).
+    // Block b's V rows as whole dwords: an even block starts on a dword
+    // boundary (its scale is the dword's low half), an odd one 2 bytes into
+    // one (the high half); byte n of the codes follows 2 bytes after the
+    // scale. The V shift of block b (v_shift_of over 64 rows, on the same
+    // scale bits) takes the scale of row `lane`.
+    uint32_t kx[2][3];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         const int f = w + 8 * k;   // (tile, block) = (f >> 2, b)
         const uint32_t* p = (const uint32_t*)(rw + 16 * (f >> 2) * kKRow + ko);
-        const uint32_t x0 = p[0], x1 = p[1], x2 = p[2];
-        *(half8_t*)(kc + f * 1024 + oo) =
-            q8_codes_f16(__builtin_amdgcn_alignbyte(x1, x0, ksh), __builtin_amdgcn_alignbyte(x2, x1, ksh));
+        kx[k][0] = p[0];
+        kx[k][1] = p[1];
+        kx[k][2] = p[2];
     }
-    {
-        // the row's block scales: blocks 0, 1 in dword 0 and dword 8 (byte
-        // 34 = 32 + 2), blocks 2, 3 in dword 17 and dword 25 (byte 102)
-        const uint32_t* rp = (const uint32_t*)(rw + so);
-        const uint32_t d0 = rp[0], d1 = rp[8], d2 = rp[17], d3 = rp[25];
-        *(f32x4*)(kc + kSubK + st16) = f32x4{scale_f32(d0), scale_f32(d1 >> 16), scale_f32(d2), scale_f32(d3 >> 16)};
-    }
-    // Block b's V rows as whole dwords: an even block starts on a dword
-    // boundary (its scale is the dword's low half), an odd one 2 bytes into
-    // one (the high half); byte n of the codes follows 2 bytes after the
-    // scale.
-    // the sub-block's V shift of block b (v_shift_of over 64 rows, on the
-    // same scale bits); every lane of the two waves of block b writes it
+    const uint32_t* rp = (const uint32_t*)(rw + so);
+    const uint32_t d0 = rp[0], d1 = rp[8], d2 = rp[17], d3 = rp[25];
     uint32_t vs = RawSub<VT>::kK + lane * VT::kRow + VT::kBlock * b - vsh_b;
     asm volatile("" : "+v"(vs));
     const uint32_t w0 = *(const uint32_t*)(rw + vs);
-    const uint32_t sbits = (vsh_b ? w0 >> 16 : w0) & 0x7FFFu;
-    const int vsh = __any(lane < valid && sbits > (VT::kQ8 ? kVBigBits8 : kVBigBits)) ? (VT::kQ8 ? kVShift8 : kVShift) : 0;
-    *(int4v*)(vc + kVShiftOfs + 16 * b) = int4v{vsh, vsh, vsh, vsh};
-    // the V rows of v_raw (kvs_convert.h), through the opaque lane offset
-    VRaw<VT> vr;
+    const uint32_t cb = (uint32_t)(2 + vsh_b + n);   // byte of code n from a row's first dword
+    uint32_t rs[8], rb[8], rh[VT::kQ8 ? 8 : 1];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const uint32_t* rd = (const uint32_t*)(rw + vo + (32 * c + (j < 4 ? j : 12 + j)) * VT::kRow);
-        vr.d[j] = vsh_b ? rd[0] >> 16 : rd[0] & 0xFFFFu;
-        const uint32_t cb = (uint32_t)(2 + vsh_b + n);                     // byte of code n from rd
-        vr.byte[j] = (rd[cb >> 2] >> (8 * (cb & 3))) & 0xFFu;
-        if constexpr (VT::kQ8) vr.hbyte[j] = (rd[(cb + 16) >> 2] >> (8 * ((cb + 16) & 3))) & 0xFFu;
+        rs[j] = rd[0];
+        rb[j] = rd[cb >> 2];
+        if constexpr (VT::kQ8) rh[j] = rd[(cb + 16) >> 2];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- the operands
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+        *(half8_t*)(kc + (w + 8 * k) * 1024 + oo) = q8_codes_f16(__builtin_amdgcn_alignbyte(kx[k][1], kx[k][0], ksh),
+                                                                  __builtin_amdgcn_alignbyte(kx[k][2], kx[k][1], ksh));
+    *(f32x4*)(kc + kSubK + st16) = f32x4{scale_f32(d0), scale_f32(d1 >> 16), scale_f32(d2), scale_f32(d3 >> 16)};
+    // every lane of the two waves of block b writes the shift
+    const uint32_t sbits = (vsh_b ? w0 >> 16 : w0) & 0x7FFFu;
+    const int vsh = __any(lane < valid && sbits > (VT::kQ8 ? kVBigBits8 : kVBigBits)) ? (VT::kQ8 ? kVShift8 : kVShift) : 0;
+    *(int4v*)(vc + kVShiftOfs + 16 * b) = int4v{vsh, vsh, vsh, vsh};
+    // the V rows as v_raw (kvs_convert.h) gives them
+    VRaw<VT> vr;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        vr.d[j] = vsh_b ? rs[j] >> 16 : rs[j] & 0xFFFFu;
+        vr.byte[j] = (rb[j] >> (8 * (cb & 3))) & 0xFFu;
+        if constexpr (VT::kQ8) vr.hbyte[j] = (rh[j] >> (8 * ((cb + 16) & 3))) & 0xFFu;
     }
     half8_t vop[2];
-    v_convert<true, VT>(vr, c, gq, valid, vsh, m_nib, magic, vop);
-    *(half8_t*)(vc + (c * 8 + 2 * b) * 1024 + oo) = vop[0];
-    *(half8_t*)(vc + (c * 8 + 2 * b + 1) * 1024 + oo) = vop[1];
+    if (valid >= kSub)   // every row cached (all but the cache's last sub-block): no row mask
+        v_convert<false, VT>(vr, c, gq, valid, vsh, m_nib, magic, vop);
+    else
+        v_convert<true, VT>(vr, c, gq, valid, vsh, m_nib, magic, vop);
+    *(half8_t*)(vc + vdo) = vop[0];
+    *(half8_t*)(vc + vdo + 1024) = vop[1];
 }
 
 template <int LIMBS, typename VT>
@@ -424,9 +444,12 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(AttendArgs a) {
     // ---- the V shifts of the sub-block in VB: an exact rescale of a
     // block's accumulators when its shift changes
     auto v_shifts = [&](const uint8_t* VB) {
+        int vshs[kNB];   // all four reads before the first use
+#pragma unroll
+        for (int b = 0; b < kNB; ++b) vshs[b] = *(const int32_t*)(VB + kVShiftOfs + 16 * b);
 #pragma unroll
         for (int b = 0; b < kNB; ++b) {
-            const int vsh = __builtin_amdgcn_readfirstlane(*(const int32_t*)(VB + kVShiftOfs + 16 * b));
+            const int vsh = __builtin_amdgcn_readfirstlane(vshs[b]);
             if (vsh != vsh_run[b]) {
                 const float f = __builtin_amdgcn_ldexpf(1.f, vsh_run[b] - vsh);
 #pragma unroll
