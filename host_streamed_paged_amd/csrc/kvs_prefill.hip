@@ -491,8 +491,14 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(AttendArgs a) {
     // branch, so the compiler counts the DMAs in flight exactly); nothing
     // reads them.
     constexpr int kWP = RawSub<VT>::kWavePieces;
+    // The waits before the step barriers count this wave's DMAs still allowed
+    // in flight. With two query limbs the kernel spills registers, and scratch
+    // stores between the DMAs could retire ahead of them: then every vector
+    // memory operation is waited for instead.
+    constexpr int kWaitOne = LIMBS == 1 ? vm_wait(kWP) : vm_wait(0);
+    constexpr int kWaitTwo = LIMBS == 1 ? vm_wait(2 * kWP) : vm_wait(0);
     auto vbuf = [&](int i) { return vcs + i * kVBytes; };   // V buffer of sub-block st: st % 3
-    __builtin_amdgcn_s_waitcnt(vm_wait(2 * kWP));   // raw 0 landed, 1 and 2 may be in flight
+    __builtin_amdgcn_s_waitcnt(kWaitTwo);   // raw 0 landed, 1 and 2 may be in flight
     lds_barrier();
     convert_sub<VT>(rw0, kc0, vbuf(0), valid_of(0), tid, w, lane, m_nib, magic);
 
@@ -504,7 +510,7 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(AttendArgs a) {
     // every one of them apart from the DMA's target and would wait for the
     // DMA there; after it, the step reads only operand buffers.
     auto front = [&](int st, int vi, uint8_t* KN, const uint8_t* Rn, uint8_t* D, bool prev) {
-        __builtin_amdgcn_s_waitcnt(vm_wait(kWP));
+        __builtin_amdgcn_s_waitcnt(kWaitOne);
         lds_barrier();
         if (prev) v_shifts(vbuf(vi == 0 ? 2 : vi - 1));
         convert_sub<VT>(Rn, KN, vbuf(vi == 2 ? 0 : vi + 1), valid_of(min(st + 1, n_steps - 1)), tid, w, lane, m_nib, magic);
