@@ -518,7 +518,10 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(AttendArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         return ad;
     };
-    half8_t pprev[2][kRTW];
+    // P^T operands of the sub-blocks of even and of odd index: a step reads
+    // the previous sub-block's from one and writes its own into the other
+    // (the unrolled steps name them statically, so nothing is copied)
+    half8_t pb0[2][kRTW], pb1[2][kRTW];
     // step 0: no previous sub-block
     {
         const DmaAddr<VT> ad = front(0, 0, kc1, rw1, rw3, false);
@@ -527,13 +530,13 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(AttendArgs a) {
         bool rescale = false;
         scores(0, kc0, sc, m_use, alpha, rescale);
 #pragma unroll
-        for (int k = 0; k < 16; ++k) exps(k, sc, m_use, pprev);
+        for (int k = 0; k < 16; ++k) exps(k, sc, m_use, pb0);
         apply_alpha(alpha, rescale);
         keep<VT>(ad);
     }
-    auto do_step = [&](int st, int vi, const uint8_t* KC, uint8_t* KN, const uint8_t* Rn, uint8_t* D) {
+    auto do_step = [&](int st, int vi, const uint8_t* KC, uint8_t* KN, const uint8_t* Rn, uint8_t* D,
+                       const half8_t (&pprev)[2][kRTW], half8_t (&pc)[2][kRTW]) {
         const DmaAddr<VT> ad = front(st, vi, KN, Rn, D, true);
-        half8_t pc[2][kRTW];
         f32x4 sc[4][kRTW];
         float m_use[kRTW], alpha[kRTW];
         bool rescale = false;
@@ -563,10 +566,6 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(AttendArgs a) {
             __builtin_amdgcn_sched_barrier(0);
         }
         apply_alpha(alpha, rescale);
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-            for (int rt = 0; rt < kRTW; ++rt) pprev[c][rt] = pc[c][rt];
         keep<VT>(ad);
     };
     // steps four at a time from step 1, so that each names its raw and K
@@ -574,15 +573,22 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(AttendArgs a) {
     int vi = 1;
     auto nx = [](int i) { return i == 2 ? 0 : i + 1; };
     for (int st = 1; st < n_steps; st += 4) {
-        do_step(st, vi, kc1, kc0, rw2, rw0);
+        do_step(st, vi, kc1, kc0, rw2, rw0, pb0, pb1);
         vi = nx(vi);
-        if (st + 1 < n_steps) { do_step(st + 1, vi, kc0, kc1, rw3, rw1); vi = nx(vi); }
-        if (st + 2 < n_steps) { do_step(st + 2, vi, kc1, kc0, rw0, rw2); vi = nx(vi); }
-        if (st + 3 < n_steps) { do_step(st + 3, vi, kc0, kc1, rw1, rw3); vi = nx(vi); }
+        if (st + 1 < n_steps) { do_step(st + 1, vi, kc0, kc1, rw3, rw1, pb1, pb0); vi = nx(vi); }
+        if (st + 2 < n_steps) { do_step(st + 2, vi, kc1, kc0, rw0, rw2, pb0, pb1); vi = nx(vi); }
+        if (st + 3 < n_steps) { do_step(st + 3, vi, kc0, kc1, rw1, rw3, pb1, pb0); vi = nx(vi); }
     }
-    // the last sub-block's P.V (its operands were published before the last step)
+    // the last sub-block's P.V (its operands were published before the last
+    // step; its P^T operands are in the buffer of its index's parity)
+    half8_t plast[2][kRTW];
+    const bool last_odd = ((n_steps - 1) & 1) != 0;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int rt = 0; rt < kRTW; ++rt) plast[c][rt] = last_odd ? pb1[c][rt] : pb0[c][rt];
     v_shifts(vbuf(vi == 0 ? 2 : vi - 1));
-    pv(vbuf(vi == 0 ? 2 : vi - 1), pprev);
+    pv(vbuf(vi == 0 ? 2 : vi - 1), plast);
 
     // ---- group state -> partial records (O back in absolute units)
 #pragma unroll
