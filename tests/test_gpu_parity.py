@@ -160,9 +160,12 @@ def test_prefill_and_matrix_core_paths_agree():
         c.close()
 
 
-def test_prefill_bit_identical_across_residency_and_ring():
+@pytest.mark.parametrize("qdt", ["f16", "f32"])
+def test_prefill_bit_identical_across_residency_and_ring(qdt):
     """Large query blocks (64-row tiles, last one ragged) give the same bits
-    whichever pages are resident and however the ring chunks the rest."""
+    whichever pages are resident and however the ring chunks the rest, for
+    f16 queries and for f32 queries (two f16 limbs: the prefill kernel's
+    variant that waits for every memory operation before its barriers)."""
     n_q = 40
     base = None
     for v in [dict(resident=mask_all, ring=4, chunk=2, group=3),
@@ -172,10 +175,12 @@ def test_prefill_bit_identical_across_residency_and_ring():
         c = small_case(v["resident"], n_layers=2, max_q=n_q, ring=v["ring"], chunk=v["chunk"],
                        group=v["group"], flags=v.get("flags", 0))
         try:
-            qs = [c.queries(l, n_q, "f16") for l in range(c.L)]
-            outs, lses = c.attend_all(qs, q_pos0=N_KV - n_q, scale=0.12, causal=True)
+            qs = [c.queries(l, n_q, qdt) for l in range(c.L)]
+            outs, lses = c.attend_all(qs, q_pos0=N_KV - n_q, scale=0.12 if qdt == "f16" else 0.12 * math.sqrt(128),
+                                      causal=True)
             if base is None:
-                check(c, outs, lses, qs, q_pos0=N_KV - n_q, scale=0.12, causal=True)
+                check(c, outs, lses, qs, q_pos0=N_KV - n_q, scale=0.12 if qdt == "f16" else 0.12 * math.sqrt(128),
+                      causal=True)
                 base = (outs, lses)
             else:
                 for l in range(c.L):
